@@ -1,0 +1,194 @@
+"""CPU oracle for the INT8-input Mamba-2 SSD scan -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may use
+this package.  It wraps liboracle.so (built from ssd_oracle.c with gcc) and
+shares nothing with the HIP library.  See ssd_oracle.c for what each function
+computes and which passage of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so with gcc (strict IEEE: no fast-math, no contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           "-Wall", "-Wextra", _SRC, "-o", _LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    lib.oracle_quantize_f16.argtypes = [P, P, P, i64, i32, i32]
+    lib.oracle_quantize_f16.restype = None
+    lib.oracle_ssd_sequential.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, i32, P]
+    lib.oracle_ssd_sequential.restype = None
+    lib.oracle_chunk_cumsum.argtypes = [P, P, i64, i32, i32, i32, i32, P]
+    lib.oracle_chunk_cumsum.restype = None
+    lib.oracle_chunk_state.argtypes = [P] * 6 + [i64, i32, i32, i32, i32, i32, i32, i32, P]
+    lib.oracle_chunk_state.restype = None
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ----------------------------------------------------------------------------------------------
+# quantizer
+
+
+def quantize(x16: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Codes of an fp16 tensor whose second-to-last axis indexes `scale`
+    (heads for x (..., H, P); groups for B/C (..., G, N))."""
+    lib = _load()
+    x16 = np.ascontiguousarray(x16, dtype=np.float16)
+    scale = _c(scale, np.float32)
+    nscale, inner = x16.shape[-2], x16.shape[-1]
+    assert scale.shape == (nscale,)
+    rows = x16.size // (nscale * inner) if x16.size else 0
+    q = np.empty(x16.shape, dtype=np.int8)
+    if x16.size:
+        lib.oracle_quantize_f16(_ptr(x16.view(np.uint16)), _ptr(q), _ptr(scale), rows, nscale, inner)
+    return q
+
+
+def quantize_values(v16: np.ndarray, scale: float) -> np.ndarray:
+    """Codes of a flat fp16 array under one scale."""
+    v16 = np.ascontiguousarray(v16, dtype=np.float16).reshape(-1, 1, 1)
+    return quantize(v16, np.array([scale], dtype=np.float32)).reshape(-1)
+
+
+# ----------------------------------------------------------------------------------------------
+# recurrence
+
+
+class Codes:
+    """Quantized prefill inputs in the scan's layout."""
+
+    def __init__(self, qx, sx, qB, sB, qC, sC, dt, A, D=None, h0=None):
+        self.qx = _c(qx, np.int8)
+        self.qB = _c(qB, np.int8)
+        self.qC = _c(qC, np.int8)
+        self.sx, self.sB, self.sC = _c(sx, np.float32), _c(sB, np.float32), _c(sC, np.float32)
+        self.dt, self.A = _c(dt, np.float32), _c(A, np.float32)
+        self.D, self.h0 = _c(D, np.float32), _c(h0, np.float32)
+        self.batch, self.L, self.H, self.P = self.qx.shape
+        self.G, self.N = self.qB.shape[2], self.qB.shape[3]
+        assert self.qB.shape == (self.batch, self.L, self.G, self.N) == self.qC.shape
+        assert self.dt.shape == (self.batch, self.L, self.H)
+        assert self.H % self.G == 0
+
+
+def codes_from_inputs(inp: dict) -> Codes:
+    """Quantize a workload draw with the oracle's quantizer."""
+    return Codes(quantize(inp["x16"], inp["x_scale"]), inp["x_scale"],
+                 quantize(inp["B16"], inp["B_scale"]), inp["B_scale"],
+                 quantize(inp["C16"], inp["C_scale"]), inp["C_scale"],
+                 inp["dt"], inp["A"], inp.get("D"), inp.get("h0"))
+
+
+def ssd_one(c: Codes, b: int, h: int, chunk: int = 0):
+    """(y (L,P), h_final (P,N), bounds (nc,P,N) or None) for one (b, h) in float64."""
+    lib = _load()
+    y = np.empty((c.L, c.P), np.float64)
+    hf = np.empty((c.P, c.N), np.float64)
+    bounds = None
+    if chunk > 0:
+        bounds = np.empty(((c.L + chunk - 1) // chunk, c.P, c.N), np.float64)
+    lib.oracle_ssd_sequential(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
+                              _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
+                              c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
+                              chunk, _ptr(bounds))
+    return y, hf, bounds
+
+
+def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None):
+    """Run the recurrence for the given (b, h) pairs (default: all) on `threads` host threads.
+    Returns (y, h_final, bounds) as full-size float64 arrays (NaN where not computed),
+    bounds only when chunk > 0."""
+    if pairs is None:
+        pairs = [(b, h) for b in range(c.batch) for h in range(c.H)]
+    y = np.full((c.batch, c.L, c.H, c.P), np.nan)
+    hf = np.full((c.batch, c.H, c.P, c.N), np.nan)
+    bounds = None
+    if chunk > 0:
+        bounds = np.full((c.batch, (c.L + chunk - 1) // chunk, c.H, c.P, c.N), np.nan)
+    threads = threads or default_threads()
+
+    def one(bh):
+        b, h = bh
+        yy, hh, bb = ssd_one(c, b, h, chunk)
+        y[b, :, h, :] = yy
+        hf[b, h] = hh
+        if bb is not None:
+            bounds[b, :, h] = bb
+
+    if threads <= 1:
+        for bh in pairs:
+            one(bh)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, pairs))
+    return y, hf, bounds
+
+
+def chunk_cumsum(c: Codes, b: int, h: int, chunk: int) -> np.ndarray:
+    lib = _load()
+    nc = (c.L + chunk - 1) // chunk
+    out = np.full(nc * chunk, np.nan)
+    lib.oracle_chunk_cumsum(_ptr(c.dt), _ptr(c.A), c.L, c.H, b, h, chunk, _ptr(out))
+    return out.reshape(nc, chunk)
+
+
+def chunk_state(c: Codes, b: int, h: int, chunk: int) -> np.ndarray:
+    lib = _load()
+    nc = (c.L + chunk - 1) // chunk
+    out = np.empty((nc, c.P, c.N))
+    lib.oracle_chunk_state(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.dt), _ptr(c.A),
+                           c.L, c.H, c.P, c.N, c.G, b, h, chunk, _ptr(out))
+    return out
+
+
+def decode_as_prefill(dec: dict) -> Codes:
+    """The decode workload as one prefill over its steps: the recurrence is the
+    same, with the decode state as h0.  Codes come from the oracle quantizer."""
+    qx = quantize(dec["x16"], dec["x_scale"])      # (T, b, H, P)
+    qB = quantize(dec["B16"], dec["B_scale"])      # (T, b, G, N)
+    qC = quantize(dec["C16"], dec["C_scale"])
+    tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))
+    return Codes(tr(qx), dec["x_scale"], tr(qB), dec["B_scale"], tr(qC), dec["C_scale"],
+                 tr(dec["dt"]), dec["A"], dec["D"], dec["state"])

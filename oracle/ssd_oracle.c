@@ -1,0 +1,170 @@
+/*
+ * ssd_oracle.c -- CPU oracle for the INT8-input Mamba-2 SSD scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that the
+ * HIP path is checked against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg load it; the product library never does, and it
+ * shares no code, header or constant with the HIP sources.
+ *
+ * What it computes (all state arithmetic in IEEE double):
+ *
+ *  - oracle_quantize_f16: the static INT8 quantizer.  The 8-bit SSD inputs
+ *    x, B, C (Quamba2 rebuttal, "impact of SSD quantization") use one static
+ *    scale per head for x and one per state group for B and C (SSDi8,
+ *    Table 10, per-H(G); Quamba project page, static quantization).  A code is
+ *    rint(v / s) with the fp32 quotient correctly rounded, rounding to nearest
+ *    with ties to even, then saturated to [-127, 127]; NaN quotients give 0.
+ *
+ *  - oracle_ssd_sequential: the selective-SSM recurrence written out token by
+ *    token (Ternary Mamba, Section 1: h_t = Abar_t h_{t-1} + Bbar_t x_t), with
+ *    the zero-order-hold decay Abar_t = exp(dt_t * A_h) and Bbar_t = dt_t * B_t,
+ *    and the readout y_t = C_t . h_t + D_h x_t, over the DEQUANTIZED codes
+ *    x = s_x[h] q_x, B = s_B[g] q_B, C = s_C[g] q_C (exact in double).
+ *    Head h reads group g = h / (H / G).  Optionally records the state at every
+ *    chunk boundary (the state entering chunk c, i.e. after token cQ - 1).
+ *
+ *  - oracle_chunk_cumsum / oracle_chunk_state: the two per-chunk quantities of
+ *    the chunked (state-space-duality) evaluation, each from its definition:
+ *    Acs[c, j] = sum_{i <= j} dt_{cQ+i} A_h  and
+ *    S_c[p, n] = sum_j exp(Acs[c, last] - Acs[c, j]) dt_j x[j, p] B[j, n]
+ *    (the decay-times-dt factor is SSDi8's LUT_state, Figure 3a).
+ *
+ * Parity pins that make this trustworthy live in tests/ (closed forms,
+ * brute force, an independent numpy chunked evaluation, invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* IEEE binary16 -> double, by the format's definition:
+ * normal: (-1)^s 2^(e-15) (1 + m/1024); subnormal: (-1)^s 2^-14 (m/1024). */
+static double half_bits_to_double(uint16_t bits) {
+  int s = bits >> 15;
+  int e = (bits >> 10) & 0x1f;
+  int m = bits & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24);
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25);
+  }
+  return s ? -v : v;
+}
+
+static int8_t quantize_one(uint16_t bits, float scale) {
+  float v = (float)half_bits_to_double(bits); /* exact: binary16 is a subset of binary32 */
+  volatile float t = v / scale;               /* one IEEE binary32 division */
+  if (isnan(t)) return 0;
+  float r = rintf(t); /* default rounding mode: nearest, ties to even */
+  if (r > 127.0f) r = 127.0f;
+  if (r < -127.0f) r = -127.0f;
+  return (int8_t)r;
+}
+
+/* q[r, k, i] = quantize(x[r, k, i], scale[k]) for a tensor viewed as (rows, nscale, inner). */
+void oracle_quantize_f16(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
+                         int32_t inner) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t k = 0; k < nscale; ++k)
+      for (int32_t i = 0; i < inner; ++i) {
+        int64_t e = (r * nscale + k) * (int64_t)inner + i;
+        q[e] = quantize_one(x[e], scale[k]);
+      }
+}
+
+/* One (b, h) sequence of the recurrence.
+ *  qx (batch, L, H, P) int8, qB/qC (batch, L, G, N) int8, dt (batch, L, H),
+ *  A[H], D[H] (NULL = 0), h0 (batch, H, P, N) float (NULL = 0).
+ *  y_out: L x P doubles; h_out: P x N doubles (final state).
+ *  bound_out (optional, chunk > 0): ceil(L/chunk) x P x N doubles, the state
+ *  entering each chunk. */
+void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
+                           const int8_t* qC, const float* sC, const float* dt, const float* A,
+                           const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
+                           int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
+                           double* h_out, int32_t chunk, double* bound_out) {
+  (void)batch;
+  const int32_t g = h / (H / G);
+  double* S = (double*)calloc((size_t)P * N, sizeof(double));
+  double* xv = (double*)malloc(sizeof(double) * P);
+  double* Bv = (double*)malloc(sizeof(double) * N);
+  double* Cv = (double*)malloc(sizeof(double) * N);
+  if (h0) {
+    const float* src = h0 + ((int64_t)b * H + h) * P * N;
+    for (int64_t i = 0; i < (int64_t)P * N; ++i) S[i] = (double)src[i];
+  }
+  const double Ah = (double)A[h];
+  const double Dh = D ? (double)D[h] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    if (chunk > 0 && bound_out && t % chunk == 0)
+      memcpy(bound_out + (t / chunk) * (int64_t)P * N, S, sizeof(double) * P * N);
+    const int64_t row = (int64_t)b * L + t;
+    const double d = (double)dt[row * H + h];
+    const double a = exp(d * Ah);
+    for (int32_t p = 0; p < P; ++p) xv[p] = (double)sx[h] * (double)qx[(row * H + h) * P + p];
+    for (int32_t n = 0; n < N; ++n) {
+      Bv[n] = (double)sB[g] * (double)qB[(row * G + g) * N + n];
+      Cv[n] = (double)sC[g] * (double)qC[(row * G + g) * N + n];
+    }
+    for (int32_t p = 0; p < P; ++p) {
+      double* Sp = S + (int64_t)p * N;
+      const double u = d * xv[p];
+      double acc = 0.0;
+      for (int32_t n = 0; n < N; ++n) {
+        Sp[n] = a * Sp[n] + u * Bv[n];
+        acc += Cv[n] * Sp[n];
+      }
+      y_out[t * P + p] = acc + Dh * xv[p];
+    }
+  }
+  memcpy(h_out, S, sizeof(double) * P * N);
+  free(S);
+  free(xv);
+  free(Bv);
+  free(Cv);
+}
+
+/* Acs for one (b, h): out[c * chunk + j] = sum_{i <= j} dt[cQ + i] * A[h] within chunk c,
+ * for every token of the (possibly ragged) last chunk; entries past L are left untouched. */
+void oracle_chunk_cumsum(const float* dt, const float* A, int64_t L, int32_t H, int32_t b, int32_t h,
+                         int32_t chunk, double* out) {
+  const int64_t nc = (L + chunk - 1) / chunk;
+  for (int64_t c = 0; c < nc; ++c) {
+    double acc = 0.0;
+    for (int32_t j = 0; j < chunk && c * chunk + j < L; ++j) {
+      acc += (double)dt[((int64_t)b * L + c * chunk + j) * H + h] * (double)A[h];
+      out[c * chunk + j] = acc;
+    }
+  }
+}
+
+/* S_c for one (b, h): out[c][p][n] = sum_{j in chunk c} exp(Acs[c,last] - Acs[c,j]) dt_j x[j,p] B[j,n],
+ * where `last` is the chunk's last valid token. */
+void oracle_chunk_state(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
+                        const float* dt, const float* A, int64_t L, int32_t H, int32_t P, int32_t N,
+                        int32_t G, int32_t b, int32_t h, int32_t chunk, double* out) {
+  const int32_t g = h / (H / G);
+  const int64_t nc = (L + chunk - 1) / chunk;
+  double* acs = (double*)malloc(sizeof(double) * nc * chunk);
+  oracle_chunk_cumsum(dt, A, L, H, b, h, chunk, acs);
+  for (int64_t c = 0; c < nc; ++c) {
+    double* Sc = out + c * (int64_t)P * N;
+    for (int64_t i = 0; i < (int64_t)P * N; ++i) Sc[i] = 0.0;
+    int64_t len = L - c * chunk;
+    if (len > chunk) len = chunk;
+    const double last = acs[c * chunk + len - 1];
+    for (int64_t j = 0; j < len; ++j) {
+      const int64_t row = (int64_t)b * L + c * chunk + j;
+      const double w = exp(last - acs[c * chunk + j]) * (double)dt[row * H + h];
+      for (int32_t p = 0; p < P; ++p) {
+        const double xw = w * (double)sx[h] * (double)qx[(row * H + h) * P + p];
+        for (int32_t n = 0; n < N; ++n)
+          Sc[(int64_t)p * N + n] += xw * (double)sB[g] * (double)qB[(row * G + g) * N + n];
+      }
+    }
+  }
+  free(acs);
+}

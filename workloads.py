@@ -1,0 +1,210 @@
+"""Seeded synthetic workloads for the INT8-input Mamba-2 SSD scan.
+
+This module only draws random inputs and derives the static calibration
+scales from a separate calibration draw.  It holds none of the scan's
+arithmetic (no quantizer, no recurrence), so that both the HIP path and the
+CPU oracle can consume the same inputs without sharing any computation.
+
+Shapes follow the Mamba-2 SSD layout (batch, length, heads, headdim) in which
+the SSDi8 page shows the head axis carrying distinct activation patterns
+(SSDi8, Figure 2).  The scale granularity is the one the pages use: one static
+scale per head for x and one per state group for B and C (Quamba2 rebuttal,
+"per-state-group quantization"; SSDi8, Table 10 "per-H(G)"), calibrated once
+offline as absmax/127 over a separate calibration draw (Quamba project page,
+"static per-tensor quantization" generalised per head / per group).
+
+The pages measure on real Mamba-2 activations (LAMBADA, Wikitext2, Pile, ...);
+none of those datasets or checkpoints is available, so these seeded draws stand
+in for them with the model shapes the pages name (Mamba-2 1.3B: d_inner 4096 =
+64 heads x 64; 2.7B: 80 heads, one B/C group; 8B: 128 heads, 8 groups).
+
+Random-number recipe (seeds per workload k): model seed 100+k, data seed 200+k,
+calibration seed 300+k; numpy PCG64.  Large arrays are drawn directly in
+float32 (numpy's float32 normal sampler) and then cast to float16.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class PrefillShape:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    chunk: int
+    x_dist: str          # "normal" | "outlier_heads" | "lognormal_heads"
+    dt_dist: str         # "fixed_bias" (softplus(N(-2,0.5))) | "head_bias" (softplus(N(0,0.5)+b_h))
+    h0_std: float = 0.0  # 0 -> no initial state
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeShape:
+    name: str
+    batch: int
+    steps: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    state_std: float
+    x_dist: str = "lognormal_heads"
+    dt_dist: str = "head_bias"
+
+
+# The five workloads: a tiny one, three prefill shapes, one decode shape.
+WORKLOADS = {
+    "tiny": PrefillShape("tiny", 1, 256, 4, 16, 16, 1, 64, "normal", "fixed_bias"),
+    "mamba2-1.3b-prefill": PrefillShape("mamba2-1.3b-prefill", 4, 2048, 64, 64, 128, 1, 256,
+                                        "outlier_heads", "fixed_bias"),
+    "mamba2-2.7b-long-prefill": PrefillShape("mamba2-2.7b-long-prefill", 1, 16384, 80, 64, 128, 1, 256,
+                                             "outlier_heads", "fixed_bias", h0_std=0.1),
+    "mamba2-8b-prefill": PrefillShape("mamba2-8b-prefill", 8, 4096, 128, 64, 128, 8, 256,
+                                      "lognormal_heads", "head_bias"),
+    "mamba2-8b-decode": DecodeShape("mamba2-8b-decode", 256, 128, 128, 64, 128, 8, 0.5),
+}
+WORKLOAD_ORDER = ["tiny", "mamba2-1.3b-prefill", "mamba2-2.7b-long-prefill",
+                  "mamba2-8b-prefill", "mamba2-8b-decode"]
+SEED_INDEX = {name: k for k, name in enumerate(WORKLOAD_ORDER)}
+
+
+def _rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _softplus(z: np.ndarray) -> np.ndarray:
+    # numerically safe log(1 + exp(z)); dt is handed to the scan already softplus'd
+    return np.logaddexp(0.0, z)
+
+
+@dataclasses.dataclass
+class ModelParams:
+    A: np.ndarray          # [H] float32, <= 0
+    D: np.ndarray          # [H] float32
+    x_mag: np.ndarray      # [H] float64 per-head magnitude of x
+    dt_bias: np.ndarray    # [H] float64 (zeros for the fixed-bias recipe)
+
+
+def model_params(nheads: int, x_dist: str, dt_dist: str, seed: int) -> ModelParams:
+    """Per-head properties shared by the calibration and the test draw."""
+    rng = _rng(seed)
+    A = (-np.exp(rng.uniform(0.0, math.log(16.0), size=nheads))).astype(np.float32)
+    D = rng.uniform(0.5, 1.5, size=nheads).astype(np.float32)
+    x_mag = np.ones(nheads)
+    if x_dist == "outlier_heads":
+        n_out = int(round(0.1 * nheads))
+        heads = rng.choice(nheads, size=n_out, replace=False)
+        x_mag[heads] = 20.0
+    elif x_dist == "lognormal_heads":
+        x_mag = np.exp(rng.normal(0.0, 1.0, size=nheads))
+    elif x_dist != "normal":
+        raise ValueError(x_dist)
+    dt_bias = np.zeros(nheads)
+    if dt_dist == "head_bias":
+        dt_bias = rng.uniform(-4.0, -1.0, size=nheads)
+    elif dt_dist != "fixed_bias":
+        raise ValueError(dt_dist)
+    return ModelParams(A, D, x_mag, dt_bias)
+
+
+def _draw_activations(rng, lead: tuple, nheads, headdim, ngroups, dstate, params: ModelParams):
+    x = rng.standard_normal(size=lead + (nheads, headdim), dtype=np.float32)
+    x *= params.x_mag.astype(np.float32)[:, None]
+    B = rng.standard_normal(size=lead + (ngroups, dstate), dtype=np.float32)
+    C = rng.standard_normal(size=lead + (ngroups, dstate), dtype=np.float32)
+    return x.astype(np.float16), B.astype(np.float16), C.astype(np.float16)
+
+
+def _draw_dt(rng, lead: tuple, nheads, params: ModelParams, dt_dist: str) -> np.ndarray:
+    if dt_dist == "fixed_bias":
+        z = rng.normal(-2.0, 0.5, size=lead + (nheads,))
+    else:
+        z = rng.normal(0.0, 0.5, size=lead + (nheads,)) + params.dt_bias
+    return _softplus(z).astype(np.float32)
+
+
+def absmax_scale(t16: np.ndarray, axis_keep: int) -> np.ndarray:
+    """Static scale per index of `axis_keep` (heads for x, groups for B/C):
+    fp32(absmax over the calibration tensor) / 127, or 1 where the absmax is 0."""
+    t = np.abs(t16.astype(np.float32))
+    axes = tuple(i for i in range(t.ndim) if i != (axis_keep % t.ndim))
+    amax = t.max(axis=axes).astype(np.float32)
+    s = amax / np.float32(127.0)
+    s[amax == 0] = np.float32(1.0)
+    return s.astype(np.float32)
+
+
+def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch: int | None = None,
+                 seqlen: int | None = None) -> dict:
+    """Seeded prefill inputs.  `batch`/`seqlen` may shrink the test draw (the
+    calibration draw keeps the workload's shape unless it is larger than the
+    test draw would be, in which case it is shrunk the same way)."""
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    k = SEED_INDEX.get(shape.name, 0) if seed_index is None else seed_index
+    b = shape.batch if batch is None else batch
+    L = shape.seqlen if seqlen is None else seqlen
+    H, P, N, G = shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    params = model_params(H, shape.x_dist, shape.dt_dist, 100 + k)
+
+    cal = _rng(300 + k)
+    xc, Bc, Cc = _draw_activations(cal, (b, L), H, P, G, N, params)
+    sx, sB, sC = absmax_scale(xc, -2), absmax_scale(Bc, -2), absmax_scale(Cc, -2)
+    del xc, Bc, Cc
+
+    rng = _rng(200 + k)
+    x, B, C = _draw_activations(rng, (b, L), H, P, G, N, params)
+    dt = _draw_dt(rng, (b, L), H, params, shape.dt_dist)
+    h0 = None
+    if shape.h0_std > 0:
+        h0 = (rng.standard_normal(size=(b, H, P, N), dtype=np.float32) * np.float32(shape.h0_std))
+    return dict(x16=x, B16=B, C16=C, dt=dt, A=params.A, D=params.D, h0=h0,
+                x_scale=sx, B_scale=sB, C_scale=sC,
+                batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=shape.chunk)
+
+
+def make_decode(shape: DecodeShape | str, seed_index: int | None = None, batch: int | None = None,
+                steps: int | None = None) -> dict:
+    """Seeded decode inputs: an fp32 state (b,H,P,N) and `steps` tokens per sequence.
+    Per-step activations are stacked on a leading step axis: x16 (steps,b,H,P),
+    B16/C16 (steps,b,G,N), dt (steps,b,H)."""
+    if isinstance(shape, str):
+        shape = WORKLOADS[shape]
+    k = SEED_INDEX.get(shape.name, 4) if seed_index is None else seed_index
+    b = shape.batch if batch is None else batch
+    T = shape.steps if steps is None else steps
+    H, P, N, G = shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    params = model_params(H, shape.x_dist, shape.dt_dist, 100 + k)
+
+    cal = _rng(300 + k)
+    xc, Bc, Cc = _draw_activations(cal, (T, b), H, P, G, N, params)
+    sx, sB, sC = absmax_scale(xc, -2), absmax_scale(Bc, -2), absmax_scale(Cc, -2)
+    del xc, Bc, Cc
+
+    rng = _rng(200 + k)
+    state = rng.standard_normal(size=(b, H, P, N), dtype=np.float32) * np.float32(shape.state_std)
+    x, B, C = _draw_activations(rng, (T, b), H, P, G, N, params)
+    dt = _draw_dt(rng, (T, b), H, params, shape.dt_dist)
+    return dict(state=state, x16=x, B16=B, C16=C, dt=dt, A=params.A, D=params.D,
+                x_scale=sx, B_scale=sB, C_scale=sC,
+                batch=b, steps=T, nheads=H, headdim=P, dstate=N, ngroups=G)
+
+
+def make_custom_prefill(seed: int, batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                        ngroups: int, chunk: int, x_dist: str = "normal", dt_dist: str = "fixed_bias",
+                        h0_std: float = 0.0) -> dict:
+    """A prefill draw of any shape (used for ragged and edge-case tests)."""
+    shape = PrefillShape(f"custom{seed}", batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                         x_dist, dt_dist, h0_std)
+    return make_prefill(shape, seed_index=seed)
