@@ -1,0 +1,258 @@
+"""Benchmark of the INT8-input Mamba-2 SSD scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the prefill hot path over the Mamba-2 1.3B-shaped layer
+(batch 4, L 2048, 64 heads x 64, d_state 128, 1 group, chunk 256): static INT8
+quantize of x, B and C, then the chunked scan (chunk cumsum, chunk state, state
+passing, chunk output).  Inputs are seeded synthetic fp16 activations resident
+in HBM before timing starts.  The decode update is measured in the same run on
+the 8B-shaped decode workload (batch 256, 128 heads, 8 groups, 128 steps, 1 GiB
+fp32 state), one launch per step.  The CPU oracle is timed on the host cores on
+the same prefill workload.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_PEAK_OPS = 5.0e15         # MI355X dense INT8 MFMA
+METRIC = "SSD scan tokens/s + % INT8 MFMA peak (prefill); decode HBM GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (for scaling HBM counter readings)")
+    return ap.parse_args()
+
+
+def kernel_bytes(b, L, H, P, N, G, Q):
+    """Algorithmic HBM bytes per launch of each prefill kernel: every input read once,
+    every output written once."""
+    nc = -(-L // Q)
+    tok = b * L
+    x = tok * H * P
+    bc = tok * G * N
+    dt = tok * H * 4
+    acs = b * H * nc * Q * 4
+    st = b * nc * H * P * N * 4
+    hfin = b * H * P * N * 4
+    return {
+        "quantize_x": 3 * x,
+        "quantize_B": 3 * bc,
+        "quantize_C": 3 * bc,
+        "chunk_cumsum": dt + acs,
+        "chunk_state": x + bc + dt + acs + st,
+        "state_passing": 2 * st + hfin,
+        "chunk_output": x + 2 * bc + dt + acs + st + 2 * tok * H * P,
+    }
+
+
+def scan_ops(b, L, H, P, N, G, Q):
+    """Algorithmic contraction ops (2 per multiply-add) of the chunked scan: chunk
+    states, causal C.B^T once per group, causal M.x and C.Hprev per head."""
+    nc = -(-L // Q)
+    pairs = 0
+    for c in range(nc):
+        q = min(Q, L - c * Q)
+        pairs += q * (q + 1) // 2
+    state = 2 * b * L * H * P * N
+    cb = 2 * b * G * pairs * N
+    mx = 2 * b * H * pairs * P
+    ch = 2 * b * L * H * P * N
+    return {"chunk_state": state, "chunk_output": cb + mx + ch, "cb_int8": cb}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import quantized_selective_state_amd as ssdq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    T = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    name = "mamba2-1.3b-prefill"
+    shape = workloads.WORKLOADS[name]
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    inp = workloads.make_prefill(name)
+    b, L, H, P, N, G, Q = (inp[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"))
+    x16, B16, C16 = T(inp["x16"]), T(inp["B16"]), T(inp["C16"])
+    sx, sB, sC = T(inp["x_scale"]), T(inp["B_scale"]), T(inp["C_scale"])
+    dt, A, D = T(inp["dt"]), T(inp["A"]), T(inp["D"])
+    qx = torch.empty(x16.shape, dtype=torch.int8, device=dev)
+    qB = torch.empty(B16.shape, dtype=torch.int8, device=dev)
+    qC = torch.empty(C16.shape, dtype=torch.int8, device=dev)
+    buf = ssdq.ScanBuffers(qx, sx, qB, sB, qC, sC, dt, A, D, None, chunk=Q)
+
+    names = ["quantize_x", "quantize_B", "quantize_C"] + list(ssdq.STAGE_NAMES)
+
+    quant = [ssdq.QuantizeCall(x16, sx, qx), ssdq.QuantizeCall(B16, sB, qB), ssdq.QuantizeCall(C16, sC, qC)]
+    fns = [q.run for q in quant] + [(lambda s=s: buf.run_stage(s)) for s in range(ssdq.CHUNK_SCAN_STAGES)]
+
+    def step(events=None):
+        for i, f in enumerate(fns):
+            if events is not None:
+                events[i].record()
+            f()
+        if events is not None:
+            events[len(fns)].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, per-kernel events on the launch stream (torch's current stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_kernel_ms = {n: 0.0 for n in names}
+    step_ms = []
+    for k in range(args.steps):
+        for i, n in enumerate(names):
+            per_kernel_ms[n] += evs[k][i].elapsed_time(evs[k][i + 1]) / args.steps
+        step_ms.append(evs[k][0].elapsed_time(evs[k][len(fns)]))
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = b * L
+    value = tokens / (ms_per_step / 1e3)
+    scan_ms = sum(per_kernel_ms[n] for n in ssdq.STAGE_NAMES)
+
+    kb = kernel_bytes(b, L, H, P, N, G, Q)
+    ops = scan_ops(b, L, H, P, N, G, Q)
+    dominant = max(names, key=lambda n: per_kernel_ms[n])
+    ach = kb[dominant] / (per_kernel_ms[dominant] / 1e3) / 1e9
+    kernels = {n: {"us": round(per_kernel_ms[n] * 1e3, 2),
+                   "alg_bytes": kb[n],
+                   "alg_GBs": round(kb[n] / (per_kernel_ms[n] / 1e3) / 1e9, 1),
+                   "hbm_frac": round(kb[n] / (per_kernel_ms[n] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)} for n in names}
+    total_ops = ops["chunk_state"] + ops["chunk_output"]
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded; fp16 activations quantized in the timed step)",
+        "config": {"workload": name, "batch": b, "seqlen": L, "nheads": H, "headdim": P, "dstate": N,
+                   "ngroups": G, "chunk": Q},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "scan_tokens_per_s": round(tokens / (scan_ms / 1e3), 1),
+        "event_ms_per_step_median": round(float(np.median(step_ms)), 5),
+        "mfma_pct_of_int8_peak": round(100 * total_ops / (scan_ms / 1e3) / INT8_PEAK_OPS, 3),
+        "chunk_output_mfma_pct_of_int8_peak": round(
+            100 * ops["chunk_output"] / (per_kernel_ms["chunk_output"] / 1e3) / INT8_PEAK_OPS, 3),
+        "kernels": kernels,
+    }
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, torch, ssdq, workloads, dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_decode(args, torch, ssdq, workloads, dev):
+    name = "mamba2-8b-decode"
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    dec = workloads.make_decode(name, steps=args.decode_steps)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    sx, sB, sC = T(dec["x_scale"]), T(dec["B_scale"]), T(dec["C_scale"])
+    qx, qB, qC = ssdq.quantize(T(dec["x16"]), sx), ssdq.quantize(T(dec["B16"]), sB), ssdq.quantize(T(dec["C16"]), sC)
+    dt, A, D = T(dec["dt"]), T(dec["A"]), T(dec["D"])
+    state = T(dec["state"])
+    steps = qx.shape[0]
+    b, H, P, N = state.shape
+    G = qB.shape[2]
+    ys = torch.empty((steps, b, H, P), dtype=torch.float16, device=dev)
+    for t in range(min(8, steps)):     # warmup (the state keeps evolving; values stay bounded)
+        ssdq.state_update(state, qx[t], sx, qB[t], sB, qC[t], sC, dt[t], A, D, y=ys[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(steps):
+        ssdq.state_update(state, qx[t], sx, qB[t], sB, qC[t], sC, dt[t], A, D, y=ys[t])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    state_bytes = b * H * P * N * 4
+    per_step = 2 * state_bytes + b * H * P + 2 * b * G * N + b * H * 4 + b * H * P * 2
+    gbs = per_step / (ms / 1e3) / 1e9
+    return {"workload": name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "ngroups": G, "steps": steps,
+            "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms / 1e3), 1),
+            "alg_bytes_per_step": per_step, "achieved_GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def cpu_baseline(inp):
+    """The oracle as it stands (quantizer + fp64 sequential recurrence) on the host cores,
+    on the whole prefill workload (every (batch, head) sequence)."""
+    import oracle
+    threads = oracle.default_threads()
+    print(f"[bench] cpu oracle on {threads} threads", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    codes = oracle.codes_from_inputs(inp)
+    oracle.ssd(codes, threads=threads)
+    sec = time.perf_counter() - t0
+    tokens = inp["batch"] * inp["seqlen"]
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload: quantize x,B,C + all {inp['batch'] * inp['nheads']} (batch, head) "
+                      f"sequences of {inp['seqlen']} tokens, fp64, one run ({sec:.2f} s)",
+            "cpu": cpu}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,153 @@
+/*
+ * ssdq.h -- C ABI of the INT8-input Mamba-2 SSD scan for AMD MI355X (gfx950).
+ *
+ * The library evaluates the selective state-space recurrence of Mamba-2
+ * (stated in Ternary Mamba, Section 1, as h_t = Abar_t h_{t-1} + Bbar_t x_t)
+ * with the zero-order-hold decay Abar_t = exp(dt_t A_h), Bbar_t = dt_t B_t and
+ * the readout y_t = C_t . h_t + D_h x_t, where x, B and C arrive as INT8 codes
+ * with static scales: one fp32 scale per head for x and one per state group
+ * for B and C (Quamba2 rebuttal: 8-bit SSD inputs B, C, x and per-state-group
+ * quantization; SSDi8 Table 10: per-H(G) scales; Quamba project page: static
+ * scales).  Prefill uses the chunked state-space-duality evaluation (SSDi8
+ * abstract and Figure 1b: chunk state, chunk-level C.B^T on INT8, state
+ * passing); decode is one recurrence step per call (Quamba2 rebuttal: the SSD
+ * update is the decode-time latency and memory bottleneck).
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless stated otherwise, must be 16-byte
+ *    aligned, and address contiguous row-major tensors in the layouts given.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates or frees device memory, never synchronizes the device, keeps no
+ *    global state and is safe to call from several host threads.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream) of the
+ *    current HIP device.
+ *  - Arguments are validated on the host before anything is enqueued; any
+ *    status other than SSDQ_SUCCESS means nothing was enqueued.  Validation
+ *    cannot read device memory, so NaN/Inf or out-of-range VALUES in device
+ *    buffers are not detected (see each call for what they produce).
+ *  - y (fp16) never aliases an input.  The only aliases allowed are the ones
+ *    each call names.
+ */
+#ifndef SSDQ_H_
+#define SSDQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSDQ_SUCCESS = 0,
+  SSDQ_ERROR_INVALID_VALUE = 1,       /* null / misaligned pointer, non-positive size, H % G != 0 */
+  SSDQ_ERROR_UNSUPPORTED = 2,         /* a shape the kernels do not handle (see each call) */
+  SSDQ_ERROR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below ssdq_chunk_scan_workspace_size() */
+  SSDQ_ERROR_LAUNCH = 4               /* the HIP runtime rejected a kernel launch */
+} ssdq_status;
+
+/* Human-readable name of a status (host; static storage; never NULL). */
+const char* ssdq_status_string(ssdq_status status);
+
+/*
+ * Static INT8 quantizer (the 8-bit SSD inputs of the Quamba2 rebuttal; static
+ * per-head / per-group scales of SSDi8 Table 10).
+ *
+ *   q[r, k, i] = clamp(round_half_even(float(x[r, k, i]) / scale[k]), -127, 127)
+ *
+ * with the fp32 quotient correctly rounded (not a reciprocal multiply).
+ * A NaN quotient gives 0 and +-Inf gives +-127; -128 is never produced.
+ *   x_f16 : (rows, nscale, inner) IEEE binary16, device
+ *   q     : (rows, nscale, inner) int8, device, written
+ *   scale : [nscale] fp32, device (positive finite for meaningful codes)
+ * Use for x (b, L, H, P): rows = b*L, nscale = H, inner = P; for B or C
+ * (b, L, G, N): rows = b*L, nscale = G, inner = N.  Any rows >= 0 (0 = no-op),
+ * nscale >= 1, inner >= 1.  q must not overlap x_f16.
+ */
+ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
+                          int32_t inner, hipStream_t stream);
+
+/* Bytes of workspace ssdq_chunk_scan needs for this shape (host; 0 on invalid shapes).
+ * Layout (stable, used by the stage-level tests):
+ *   [0, acs_bytes)           Acs   fp32 (batch, nheads, nchunks, chunk): within-chunk
+ *                            inclusive cumsum of dt * A (padded past the sequence end)
+ *   [acs_bytes, total)       states fp32 (batch, nchunks, nheads, headdim, dstate):
+ *                            chunk states S_c after stage 1, overwritten by stage 2 with
+ *                            the state ENTERING each chunk
+ * where nchunks = ceil(seqlen / chunk) and acs_bytes is rounded up to 256 bytes. */
+size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
+                                      int32_t dstate, int32_t chunk);
+
+/*
+ * Prefill: the chunked SSD scan over INT8 inputs (SSDi8 Figure 1b pipeline).
+ *
+ *   for every (b, h):  h_{-1} = h0[b, h] (or 0),
+ *     h_t = exp(dt[b,t,h] A[h]) h_{t-1} + dt[b,t,h] * xhat[b,t,h,:] (x) Bhat[b,t,g,:]
+ *     y[b,t,h,:] = h_t . Chat[b,t,g,:] + D[h] * xhat[b,t,h,:]
+ *   with xhat = x_scale[h] * x, Bhat = B_scale[g] * B, Chat = C_scale[g] * C and
+ *   g = h / (nheads / ngroups).
+ *
+ *   x  : (batch, seqlen, nheads, headdim) int8      x_scale : [nheads] fp32
+ *   B  : (batch, seqlen, ngroups, dstate) int8      B_scale : [ngroups] fp32
+ *   C  : (batch, seqlen, ngroups, dstate) int8      C_scale : [ngroups] fp32
+ *   dt : (batch, seqlen, nheads) fp32, > 0, already passed through softplus
+ *   A  : [nheads] fp32, finite, <= 0          D : [nheads] fp32 or NULL (= 0)
+ *   h0 : (batch, nheads, headdim, dstate) fp32 or NULL (= 0)
+ *   y  : (batch, seqlen, nheads, headdim) fp16, written
+ *   h_final : (batch, nheads, headdim, dstate) fp32 or NULL; may alias h0
+ *   workspace : device scratch of at least ssdq_chunk_scan_workspace_size() bytes,
+ *               owned by the caller, not shared with a concurrent call
+ * Supported shapes: headdim % 16 == 0 and headdim <= 64; dstate % 64 == 0 and
+ * dstate <= 128; chunk in {64, 128, 256}; any seqlen >= 1 (a ragged last chunk
+ * is masked); nheads % ngroups == 0.  Others return SSDQ_ERROR_UNSUPPORTED.
+ * Accuracy: y within 2e-3 * max|y| and h_final within 1e-4 * max|h| of the exact
+ * recurrence over the same codes (fp32 accumulation, fp16 y).
+ */
+ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                            const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                            const float* D, const float* h0, void* y, float* h_final, int32_t batch,
+                            int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                            int32_t chunk, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Number of stages ssdq_chunk_scan runs, in order: 0 chunk cumsum, 1 chunk state,
+ * 2 state passing, 3 chunk output. */
+#define SSDQ_CHUNK_SCAN_STAGES 4
+
+/*
+ * One stage of ssdq_chunk_scan, with the same arguments and validation.
+ * Running stages 0..3 in order on one stream is exactly ssdq_chunk_scan; the
+ * intermediate results are in the workspace layout documented above.  This
+ * lets a caller time each kernel with its own events and lets tests inspect
+ * the intermediates.  stage outside [0, SSDQ_CHUNK_SCAN_STAGES) is INVALID_VALUE.
+ */
+ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,
+                                  const float* B_scale, const int8_t* C, const float* C_scale,
+                                  const float* dt, const float* A, const float* D, const float* h0, void* y,
+                                  float* h_final, int32_t batch, int64_t seqlen, int32_t nheads,
+                                  int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Decode: one recurrence step per sequence, state updated IN PLACE (the
+ * decode-time SSD update of the Quamba2 rebuttal, Tables R7/R8).
+ *
+ *   state[b,h,p,n] <- exp(dt[b,h] A[h]) state[b,h,p,n] + dt[b,h] xhat[b,h,p] Bhat[b,g,n]
+ *   y[b,h,p] = sum_n Chat[b,g,n] state[b,h,p,n] (updated) + D[h] xhat[b,h,p]
+ *
+ *   state : (batch, nheads, headdim, dstate) fp32, read and written
+ *   x : (batch, nheads, headdim) int8     B, C : (batch, ngroups, dstate) int8
+ *   dt : (batch, nheads) fp32   A : [nheads]   D : [nheads] or NULL   y : (batch, nheads, headdim) fp16
+ * Supported: dstate == 128 or dstate == 64, headdim % 8 == 0, nheads % ngroups == 0.
+ */
+ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                              const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                              const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
+                              int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSDQ_H_ */

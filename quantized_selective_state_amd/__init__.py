@@ -1,0 +1,235 @@
+"""Python binding of libssdq, the INT8-input Mamba-2 SSD scan for MI355X (gfx950).
+
+The functions below only marshal arguments: they check device, dtype, shape and
+contiguity of torch tensors, pass their device pointers and the current HIP
+stream to the C ABI declared in include/ssdq.h, and raise on a non-success
+status.  Every step of the computation runs in the library's HIP kernels;
+torch only provides device memory and the stream.  There is no fallback: if
+libssdq.so is missing, importing this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssdq.so")
+
+SSDQ_SUCCESS = 0
+SSDQ_ERROR_INVALID_VALUE = 1
+SSDQ_ERROR_UNSUPPORTED = 2
+SSDQ_ERROR_WORKSPACE_TOO_SMALL = 3
+SSDQ_ERROR_LAUNCH = 4
+CHUNK_SCAN_STAGES = 4
+STAGE_NAMES = ("chunk_cumsum", "chunk_state", "state_passing", "chunk_output")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_selective_state_amd.build`")
+
+lib = ctypes.CDLL(LIB_PATH)
+_P, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+lib.ssdq_status_string.argtypes = [ctypes.c_int]
+lib.ssdq_status_string.restype = ctypes.c_char_p
+lib.ssdq_quantize.argtypes = [_P, _P, _P, _i64, _i32, _i32, _P]
+lib.ssdq_quantize.restype = ctypes.c_int
+lib.ssdq_chunk_scan_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32]
+lib.ssdq_chunk_scan_workspace_size.restype = _sz
+_SCAN_ARGS = [_P] * 12 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
+lib.ssdq_chunk_scan.argtypes = _SCAN_ARGS
+lib.ssdq_chunk_scan.restype = ctypes.c_int
+lib.ssdq_chunk_scan_stage.argtypes = [_i32] + _SCAN_ARGS
+lib.ssdq_chunk_scan_stage.restype = ctypes.c_int
+lib.ssdq_state_update.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, _P]
+lib.ssdq_state_update.restype = ctypes.c_int
+
+
+class SSDQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def status_string(status: int) -> str:
+    return lib.ssdq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SSDQ_SUCCESS:
+        raise SSDQError(status, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor | None, name: str, dtype: torch.dtype, shape: tuple | None, device, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------------------------
+# quantize
+
+
+class QuantizeCall:
+    """A validated quantize call with its arguments marshalled once (for launch loops)."""
+
+    def __init__(self, x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None):
+        if x.dim() < 2:
+            raise ValueError("x must have at least 2 dimensions (..., nscale, inner)")
+        nscale, inner = x.shape[-2], x.shape[-1]
+        _need(x, "x", torch.float16, None, None)
+        _need(scale, "scale", torch.float32, (nscale,), x.device)
+        if out is None:
+            out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+        _need(out, "out", torch.int8, tuple(x.shape), x.device)
+        rows = x.numel() // (nscale * inner) if x.numel() else 0
+        self.out = out
+        self.device = x.device
+        self._args = (_ptr(x), _ptr(out), _ptr(scale), rows, nscale, inner)
+        self._keep = (x, scale, out)
+
+    def run(self) -> torch.Tensor:
+        _check(lib.ssdq_quantize(*self._args, _stream(self.device)), "ssdq_quantize")
+        return self.out
+
+
+def quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """INT8 codes of an fp16 tensor (..., S, I) with one fp32 scale per index of the
+    second-to-last axis (heads for x, groups for B and C)."""
+    return QuantizeCall(x, scale, out).run()
+
+
+# ---------------------------------------------------------------------------------------------
+# prefill
+
+
+def chunk_scan_workspace_size(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, chunk: int) -> int:
+    return int(lib.ssdq_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, chunk))
+
+
+def workspace_layout(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, chunk: int) -> dict:
+    """Offsets of the documented workspace regions (for stage-level inspection)."""
+    nc = -(-seqlen // chunk)
+    acs_bytes = ((4 * batch * nheads * nc * chunk) + 255) // 256 * 256
+    return dict(nchunks=nc, acs_offset=0, acs_shape=(batch, nheads, nc, chunk), states_offset=acs_bytes,
+                states_shape=(batch, nc, nheads, headdim, dstate))
+
+
+class ScanBuffers:
+    """Validated arguments of one prefill call, reusable across calls (no allocation per call)."""
+
+    def __init__(self, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk=256, y=None,
+                 h_final=None, workspace=None, want_final_state=True):
+        if x.dim() != 4 or B.dim() != 4:
+            raise ValueError("x must be (batch, seqlen, nheads, headdim) and B, C (batch, seqlen, ngroups, dstate)")
+        b, L, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        dev = x.device
+        _need(x, "x", torch.int8, (b, L, H, P), dev)
+        _need(x_scale, "x_scale", torch.float32, (H,), dev)
+        _need(B, "B", torch.int8, (b, L, G, N), dev)
+        _need(B_scale, "B_scale", torch.float32, (G,), dev)
+        _need(C, "C", torch.int8, (b, L, G, N), dev)
+        _need(C_scale, "C_scale", torch.float32, (G,), dev)
+        _need(dt, "dt", torch.float32, (b, L, H), dev)
+        _need(A, "A", torch.float32, (H,), dev)
+        _need(D, "D", torch.float32, (H,), dev, optional=True)
+        _need(h0, "h0", torch.float32, (b, H, P, N), dev, optional=True)
+        if y is None:
+            y = torch.empty((b, L, H, P), dtype=torch.float16, device=dev)
+        _need(y, "y", torch.float16, (b, L, H, P), dev)
+        if h_final is None and want_final_state:
+            h_final = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+        _need(h_final, "h_final", torch.float32, (b, H, P, N), dev, optional=True)
+        ws = chunk_scan_workspace_size(b, L, H, P, N, chunk)
+        if ws == 0:
+            raise SSDQError(SSDQ_ERROR_UNSUPPORTED, "ssdq_chunk_scan_workspace_size")
+        if workspace is None:
+            workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        _need(workspace, "workspace", torch.uint8, None, dev)
+        self.tensors = (x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final)
+        self.dims = (b, L, H, P, N, G, chunk)
+        self.workspace = workspace
+        self.device = dev
+        self.y, self.h_final = y, h_final
+        self._args = [_ptr(t) for t in self.tensors] + list(self.dims) + [
+            _ptr(workspace), workspace.numel()]
+
+    def run(self) -> None:
+        _check(lib.ssdq_chunk_scan(*self._args, _stream(self.device)), "ssdq_chunk_scan")
+
+    def run_stage(self, stage: int) -> None:
+        _check(lib.ssdq_chunk_scan_stage(stage, *self._args, _stream(self.device)), "ssdq_chunk_scan_stage")
+
+    def workspace_views(self) -> dict:
+        b, L, H, P, N, G, Q = self.dims
+        lay = workspace_layout(b, L, H, P, N, Q)
+        acs_n = 1
+        for d in lay["acs_shape"]:
+            acs_n *= d
+        st_n = 1
+        for d in lay["states_shape"]:
+            st_n *= d
+        ws = self.workspace
+        acs = ws[lay["acs_offset"]:lay["acs_offset"] + 4 * acs_n].view(torch.float32).view(lay["acs_shape"])
+        st = ws[lay["states_offset"]:lay["states_offset"] + 4 * st_n].view(torch.float32).view(lay["states_shape"])
+        return dict(acs=acs, states=st)
+
+
+def chunk_scan(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk=256, y=None, h_final=None,
+               workspace=None, want_final_state=True):
+    """Prefill over INT8 inputs; returns (y fp16 (b,L,H,P), h_final fp32 (b,H,P,N) or None)."""
+    buf = ScanBuffers(x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, chunk, y, h_final, workspace,
+                      want_final_state)
+    buf.run()
+    return buf.y, buf.h_final
+
+
+# ---------------------------------------------------------------------------------------------
+# decode
+
+
+def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=None) -> torch.Tensor:
+    """One decode step; `state` (b,H,P,N) fp32 is updated in place; returns y fp16 (b,H,P)."""
+    if state.dim() != 4:
+        raise ValueError("state must be (batch, nheads, headdim, dstate)")
+    b, H, P, N = state.shape
+    G = B.shape[1] if B.dim() == 3 else -1
+    dev = state.device
+    _need(state, "state", torch.float32, (b, H, P, N), dev)
+    _need(x, "x", torch.int8, (b, H, P), dev)
+    _need(x_scale, "x_scale", torch.float32, (H,), dev)
+    _need(B, "B", torch.int8, (b, G, N), dev)
+    _need(B_scale, "B_scale", torch.float32, (G,), dev)
+    _need(C, "C", torch.int8, (b, G, N), dev)
+    _need(C_scale, "C_scale", torch.float32, (G,), dev)
+    _need(dt, "dt", torch.float32, (b, H), dev)
+    _need(A, "A", torch.float32, (H,), dev)
+    _need(D, "D", torch.float32, (H,), dev, optional=True)
+    if y is None:
+        y = torch.empty((b, H, P), dtype=torch.float16, device=dev)
+    _need(y, "y", torch.float16, (b, H, P), dev)
+    _check(lib.ssdq_state_update(_ptr(state), _ptr(x), _ptr(x_scale), _ptr(B), _ptr(B_scale), _ptr(C),
+                                 _ptr(C_scale), _ptr(dt), _ptr(A), _ptr(D), _ptr(y), b, H, P, N, G,
+                                 _stream(dev)), "ssdq_state_update")
+    return y

@@ -1,0 +1,171 @@
+// C ABI of libssdq: host-side validation, workspace carving and the launch sequence.
+// No HIP runtime call is made before every argument has been validated, so the error
+// paths can be exercised on a machine without a GPU.
+#include <stdint.h>
+
+#include "ssdq_internal.h"
+
+using namespace ssdq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Shape validation for the prefill scan; fills `s` on success.
+ssdq_status check_scan_shape(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                             int32_t ngroups, int32_t chunk, ScanShape* s) {
+  if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 || chunk <= 0)
+    return SSDQ_ERROR_INVALID_VALUE;
+  if (nheads % ngroups != 0) return SSDQ_ERROR_INVALID_VALUE;
+  if (headdim % 16 != 0 || headdim > 64) return SSDQ_ERROR_UNSUPPORTED;
+  if (dstate % 16 != 0 || dstate > 128) return SSDQ_ERROR_UNSUPPORTED;
+  if (chunk != 64 && chunk != 128 && chunk != 256) return SSDQ_ERROR_UNSUPPORTED;
+  const int64_t nchunks = (seqlen + chunk - 1) / chunk;
+  // grid sizes and 32-bit block indices
+  if (int64_t(batch) * nchunks * nheads > (int64_t(1) << 30)) return SSDQ_ERROR_UNSUPPORTED;
+  if (nchunks > 65535) return SSDQ_ERROR_UNSUPPORTED;
+  s->batch = batch;
+  s->seqlen = seqlen;
+  s->nheads = nheads;
+  s->headdim = headdim;
+  s->dstate = dstate;
+  s->ngroups = ngroups;
+  s->chunk = chunk;
+  s->nchunks = int32_t(nchunks);
+  s->acs_bytes = round256(sizeof(float) * size_t(batch) * nheads * nchunks * chunk);
+  s->state_bytes = sizeof(float) * size_t(batch) * nchunks * nheads * headdim * dstate;
+  return SSDQ_SUCCESS;
+}
+
+ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,
+                            const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                            const float* A, const float* D, const float* h0, void* y, float* h_final,
+                            int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                            int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
+                            ScanShape* s, ScanArgs* a) {
+  (void)stage;
+  if (!ok_ptr(x) || !ok_ptr(x_scale) || !ok_ptr(B) || !ok_ptr(B_scale) || !ok_ptr(C) || !ok_ptr(C_scale) ||
+      !ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(y) || !ok_ptr(workspace) || !ok_opt(D) || !ok_opt(h0) ||
+      !ok_opt(h_final))
+    return SSDQ_ERROR_INVALID_VALUE;
+  const ssdq_status st = check_scan_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, s);
+  if (st != SSDQ_SUCCESS) return st;
+  if (workspace_bytes < s->acs_bytes + s->state_bytes) return SSDQ_ERROR_WORKSPACE_TOO_SMALL;
+  a->x = x;
+  a->x_scale = x_scale;
+  a->B = B;
+  a->B_scale = B_scale;
+  a->C = C;
+  a->C_scale = C_scale;
+  a->dt = dt;
+  a->A = A;
+  a->D = D;
+  a->h0 = h0;
+  a->y = static_cast<_Float16*>(y);
+  a->h_final = h_final;
+  a->acs = static_cast<float*>(workspace);
+  a->states = reinterpret_cast<float*>(static_cast<char*>(workspace) + s->acs_bytes);
+  return SSDQ_SUCCESS;
+}
+
+ssdq_status run_stage(int32_t stage, const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  switch (stage) {
+    case 0: e = launch_chunk_cumsum(s, a, stream); break;
+    case 1: e = launch_chunk_state(s, a, stream); break;
+    case 2: e = launch_state_passing(s, a, stream); break;
+    case 3: e = launch_chunk_output(s, a, stream); break;
+    default: return SSDQ_ERROR_INVALID_VALUE;
+  }
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssdq_status_string(ssdq_status status) {
+  switch (status) {
+    case SSDQ_SUCCESS: return "SSDQ_SUCCESS";
+    case SSDQ_ERROR_INVALID_VALUE: return "SSDQ_ERROR_INVALID_VALUE";
+    case SSDQ_ERROR_UNSUPPORTED: return "SSDQ_ERROR_UNSUPPORTED";
+    case SSDQ_ERROR_WORKSPACE_TOO_SMALL: return "SSDQ_ERROR_WORKSPACE_TOO_SMALL";
+    case SSDQ_ERROR_LAUNCH: return "SSDQ_ERROR_LAUNCH";
+  }
+  return "SSDQ_UNKNOWN_STATUS";
+}
+
+ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
+                          int32_t inner, hipStream_t stream) {
+  if (rows < 0 || nscale <= 0 || inner <= 0) return SSDQ_ERROR_INVALID_VALUE;
+  if (rows == 0) return SSDQ_SUCCESS;
+  if (!ok_ptr(x_f16) || !ok_ptr(q) || !ok_ptr(scale)) return SSDQ_ERROR_INVALID_VALUE;
+  const hipError_t e =
+      launch_quantize(static_cast<const uint16_t*>(x_f16), q, scale, rows, nscale, inner, stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
+size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
+                                      int32_t dstate, int32_t chunk) {
+  ScanShape s;
+  // ngroups does not change the workspace; 1 always divides nheads
+  if (check_scan_shape(batch, seqlen, nheads, headdim, dstate, 1, chunk, &s) != SSDQ_SUCCESS) return 0;
+  return s.acs_bytes + s.state_bytes;
+}
+
+ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,
+                                  const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                                  const float* A, const float* D, const float* h0, void* y, float* h_final,
+                                  int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                  int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  if (stage < 0 || stage >= SSDQ_CHUNK_SCAN_STAGES) return SSDQ_ERROR_INVALID_VALUE;
+  ScanShape s;
+  ScanArgs a;
+  const ssdq_status st = check_scan_args(stage, x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final,
+                                         batch, seqlen, nheads, headdim, dstate, ngroups, chunk, workspace,
+                                         workspace_bytes, &s, &a);
+  if (st != SSDQ_SUCCESS) return st;
+  return run_stage(stage, s, a, stream);
+}
+
+ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                            const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
+                            const float* h0, void* y, float* h_final, int32_t batch, int64_t seqlen,
+                            int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ScanShape s;
+  ScanArgs a;
+  const ssdq_status st = check_scan_args(0, x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final, batch,
+                                         seqlen, nheads, headdim, dstate, ngroups, chunk, workspace,
+                                         workspace_bytes, &s, &a);
+  if (st != SSDQ_SUCCESS) return st;
+  for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
+    const ssdq_status r = run_stage(stage, s, a, stream);
+    if (r != SSDQ_SUCCESS) return r;
+  }
+  return SSDQ_SUCCESS;
+}
+
+ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                              const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                              const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
+                              int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  if (!ok_ptr(state) || !ok_ptr(x) || !ok_ptr(x_scale) || !ok_ptr(B) || !ok_ptr(B_scale) || !ok_ptr(C) ||
+      !ok_ptr(C_scale) || !ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(y) || !ok_opt(D))
+    return SSDQ_ERROR_INVALID_VALUE;
+  if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0) return SSDQ_ERROR_INVALID_VALUE;
+  if (nheads % ngroups != 0) return SSDQ_ERROR_INVALID_VALUE;
+  if ((dstate != 64 && dstate != 128) || headdim > 64) return SSDQ_ERROR_UNSUPPORTED;
+  if (int64_t(batch) * nheads > (int64_t(1) << 30)) return SSDQ_ERROR_UNSUPPORTED;
+  const hipError_t e = launch_state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
+                                           static_cast<_Float16*>(y), batch, nheads, headdim, dstate, ngroups,
+                                           stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Internal declarations shared by the HIP translation units of libssdq.
+// Everything here is CDNA4 (gfx950, wave64) specific.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssdq.h"
+
+namespace ssdq {
+
+constexpr int kWave = 64;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Shape of one prefill call after validation.
+struct ScanShape {
+  int32_t batch;
+  int64_t seqlen;
+  int32_t nheads, headdim, dstate, ngroups, chunk;
+  int32_t nchunks;
+  size_t acs_bytes;    // Acs region, rounded up to 256 bytes
+  size_t state_bytes;  // chunk-state region
+};
+
+struct ScanArgs {
+  const int8_t* x;
+  const float* x_scale;
+  const int8_t* B;
+  const float* B_scale;
+  const int8_t* C;
+  const float* C_scale;
+  const float* dt;
+  const float* A;
+  const float* D;
+  const float* h0;
+  _Float16* y;
+  float* h_final;
+  float* acs;     // workspace: (batch, nheads, nchunks, chunk)
+  float* states;  // workspace: (batch, nchunks, nheads, headdim, dstate)
+};
+
+// Kernel launchers (one per translation unit).  They return hipGetLastError().
+hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
+                           int32_t inner, hipStream_t stream);
+hipError_t launch_chunk_cumsum(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                               const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                               const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
+                               int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------------
+// device helpers
+
+// Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8).  Remap the
+// linear block index so that consecutive *logical* tiles land on the same XCD and share
+// its L2 (neighbouring heads read the same 128-byte lines of x and the same B/C rows).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int per = nblocks / kXcd;            // full rounds
+  const int full = per * kXcd;
+  if (bid >= full) return bid;               // tail blocks keep their index
+  return (bid % kXcd) * per + bid / kXcd;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ceil(log2(v)) for finite v > 0 as an exponent e with v <= 2^e, from the fp32 bits
+// (exact; no libm).  v == 0 gives -126.
+__device__ __forceinline__ int ceil_log2_pos(float v) {
+  if (!(v > 0.f)) return -126;
+  const uint32_t bits = __float_as_uint(v);
+  int e = int((bits >> 23) & 0xff) - 127;
+  const uint32_t mant = bits & 0x7fffff;
+  if (e == -127) {  // subnormal
+    return -126;
+  }
+  return mant ? e + 1 : e;
+}
+
+// 2^e as a float for e in [-126, 127] (exact).
+__device__ __forceinline__ float exp2i(int e) {
+  e = e < -126 ? -126 : (e > 127 ? 127 : e);
+  return __uint_as_float(uint32_t(e + 127) << 23);
+}
+
+}  // namespace ssdq

@@ -1,0 +1,108 @@
+// Decode: one step of the recurrence per sequence, state updated in place
+// (the SSD update that the Quamba2 rebuttal names as the decode-time latency and
+// memory bottleneck as batch grows, Tables R7/R8):
+//
+//   h[p, n] <- exp(dt A) h[p, n] + (dt xhat[p]) Bhat[n];    y[p] = sum_n Chat[n] h[p, n] + D xhat[p]
+//
+// HBM-bound: every state element is read once and written once (8 bytes) for ~6 flops.
+// One block per (batch, head); thread t owns the 4 consecutive state columns 4 (t % (N/4))
+// of rows t / (N/4) + R k (R = 1024 / N rows per pass), so each pass of the block reads a
+// contiguous 4 KiB stretch with 16-byte loads.  All passes are loaded before any is
+// computed (8 x 16 bytes in flight per thread at N = 128).  y[p] is reduced across the N/4
+// lanes that share row p with xor-shuffles.
+#include "ssdq_internal.h"
+
+namespace ssdq {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float sbyte(uint32_t w, int i) {
+  return float(int32_t(w << (24 - 8 * i)) >> 24);
+}
+
+template <int N, int MAXP>
+__global__ void __launch_bounds__(kThreads) state_update_kernel(
+    float* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
+    const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
+    const float* __restrict__ C_scale, const float* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads, int32_t headdim, int32_t ngroups) {
+  constexpr int kLanesPerRow = N / 4;
+  constexpr int kRows = kThreads / kLanesPerRow;   // rows per pass
+  constexpr int kPasses = (MAXP + kRows - 1) / kRows;
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = bh % nheads;
+  const int b = bh / nheads;
+  const int g = h / (nheads / ngroups);
+  const int tid = threadIdx.x;
+  const int nq = tid % kLanesPerRow;
+  const int r0 = tid / kLanesPerRow;
+  const int P = headdim;
+
+  float* st = state + int64_t(bh) * P * N;
+  v4f hv[kPasses];
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = r0 + kRows * k;
+    if (p < P) hv[k] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(st + int64_t(p) * N + 4 * nq));
+  }
+
+  const float d = dt[bh];
+  const float a = __expf(d * A[h]);
+  const float sx = x_scale[h];
+  const float dx = d * sx;
+  const float Dh = D ? D[h] : 0.f;
+  const uint32_t bw = *reinterpret_cast<const uint32_t*>(Bm + (int64_t(b) * ngroups + g) * N + 4 * nq);
+  const uint32_t cw = *reinterpret_cast<const uint32_t*>(Cm + (int64_t(b) * ngroups + g) * N + 4 * nq);
+  const float sB = B_scale[g], sC = C_scale[g];
+  float bh4[4], ch4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bh4[i] = sB * sbyte(bw, i);
+    ch4[i] = sC * sbyte(cw, i);
+  }
+  const int8_t* xr = x + int64_t(bh) * P;
+
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = r0 + kRows * k;
+    if (p < P) {   // uniform across the lanes of one row
+      const float xp = float(xr[p]);
+      const float u = dx * xp;
+      v4f v = hv[k];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = a * v[i] + u * bh4[i];
+      __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(st + int64_t(p) * N + 4 * nq));
+      float part = ch4[0] * v[0] + ch4[1] * v[1] + ch4[2] * v[2] + ch4[3] * v[3];
+#pragma unroll
+      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
+      if (nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dh * sx * xp);
+    }
+  }
+}
+
+template <int N>
+hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                    const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
+                    _Float16* y, int32_t batch, int32_t nheads, int32_t headdim, int32_t ngroups,
+                    hipStream_t stream) {
+  const int nblocks = batch * nheads;
+  hipLaunchKernelGGL((state_update_kernel<N, 64>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
+                     B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                               const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                               const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
+                               int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  if (dstate == 128)
+    return launch_n<128>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, ngroups,
+                         stream);
+  return launch_n<64>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, ngroups,
+                      stream);
+}
+
+}  // namespace ssdq

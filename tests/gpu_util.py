@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+HIP path through the C ABI binding, and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+Y_TOL = 2e-3      # max|y - y_ref| <= Y_TOL * max|y_ref|
+H_TOL = 1e-4      # max|h - h_ref| <= H_TOL * max|h_ref|
+
+
+def dev() -> torch.device:
+    return torch.device("cuda:0")
+
+
+def to_dev(a):
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    mask = np.isfinite(ref)
+    if not np.all(np.isfinite(got[mask])):
+        return float("inf")
+    scale = np.max(np.abs(ref[mask])) if mask.any() else 0.0
+    return float(np.max(np.abs(got[mask] - ref[mask])) / max(scale, 1e-300))
+
+
+def gpu_quantize_inputs(inp: dict):
+    """Quantize x, B, C on the GPU; returns device codes and scales."""
+    import quantized_selective_state_amd as ssdq
+    sx, sB, sC = to_dev(inp["x_scale"]), to_dev(inp["B_scale"]), to_dev(inp["C_scale"])
+    qx = ssdq.quantize(to_dev(inp["x16"]), sx)
+    qB = ssdq.quantize(to_dev(inp["B16"]), sB)
+    qC = ssdq.quantize(to_dev(inp["C16"]), sC)
+    return qx, sx, qB, sB, qC, sC
+
+
+def gpu_prefill(inp: dict, chunk: int | None = None, with_D=True, with_h0=True):
+    """GPU quantize + chunk scan.  Returns (codes dict (numpy), y (numpy f32), h_final (numpy))."""
+    import quantized_selective_state_amd as ssdq
+    qx, sx, qB, sB, qC, sC = gpu_quantize_inputs(inp)
+    h0 = to_dev(inp["h0"]) if with_h0 else None
+    D = to_dev(inp["D"]) if with_D else None
+    y, hf = ssdq.chunk_scan(qx, sx, qB, sB, qC, sC, to_dev(inp["dt"]), to_dev(inp["A"]), D, h0,
+                            chunk=chunk or inp["chunk"])
+    torch.cuda.synchronize()
+    codes = dict(qx=qx.cpu().numpy(), qB=qB.cpu().numpy(), qC=qC.cpu().numpy())
+    return codes, y.float().cpu().numpy(), hf.cpu().numpy()
+
+
+def oracle_codes(inp: dict, with_D=True, with_h0=True) -> oracle.Codes:
+    c = oracle.codes_from_inputs(inp)
+    if not with_D:
+        c.D = None
+    if not with_h0:
+        c.h0 = None
+    return c
+
+
+def sample_pairs(batch: int, nheads: int, n: int, seed: int, must_heads=()):
+    rng = np.random.default_rng(seed)
+    pairs = {(int(rng.integers(batch)), int(h)) for h in must_heads}
+    while len(pairs) < min(n, batch * nheads):
+        pairs.add((int(rng.integers(batch)), int(rng.integers(nheads))))
+    return sorted(pairs)

@@ -1,0 +1,140 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch.
+
+Pointers passed here are fake (aligned or misaligned integers); every call is
+made with at least one invalid argument, so validation returns before the
+library touches the HIP runtime or any memory.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssdq.h")
+LIB = os.path.join(ROOT, "quantized_selective_state_amd", "libssdq.so")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+A16 = 0x100000  # a fake, 16-byte aligned address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libssdq.so not built")
+    lib = ctypes.CDLL(LIB)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    scan = [P] * 12 + [i32, i64, i32, i32, i32, i32, i32, P, sz, P]
+    lib.ssdq_chunk_scan.argtypes = scan
+    lib.ssdq_chunk_scan_stage.argtypes = [i32] + scan
+    lib.ssdq_quantize.argtypes = [P, P, P, i64, i32, i32, P]
+    lib.ssdq_chunk_scan_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.ssdq_chunk_scan_workspace_size.restype = sz
+    lib.ssdq_state_update.argtypes = [P] * 11 + [i32] * 5 + [P]
+    lib.ssdq_status_string.argtypes = [ctypes.c_int]
+    lib.ssdq_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssdq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("ssdq_quantize", "ssdq_chunk_scan", "ssdq_state_update"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.ssdq_status_string(0) == b"SSDQ_SUCCESS"
+    assert lib.ssdq_status_string(3) == b"SSDQ_ERROR_WORKSPACE_TOO_SMALL"
+    assert lib.ssdq_status_string(99) == b"SSDQ_UNKNOWN_STATUS"
+
+
+def test_workspace_size(lib):
+    # Acs: 4 * b*H*nc*Q rounded to 256; states: 4 * b*nc*H*P*N
+    b, L, H, P, N, Q = 4, 2048, 64, 64, 128, 256
+    nc = L // Q
+    acs = 4 * b * H * nc * Q
+    assert lib.ssdq_chunk_scan_workspace_size(b, L, H, P, N, Q) == acs + 4 * b * nc * H * P * N
+    # ragged: L = 250, Q = 64 -> 4 chunks
+    assert lib.ssdq_chunk_scan_workspace_size(1, 250, 2, 16, 16, 64) == 2048 + 4 * 4 * 2 * 16 * 16
+    assert lib.ssdq_chunk_scan_workspace_size(1, 256, 4, 16, 16, 48) == 0     # unsupported chunk
+    assert lib.ssdq_chunk_scan_workspace_size(0, 256, 4, 16, 16, 64) == 0
+
+
+def _scan(lib, **kw):
+    args = dict(x=A16, xs=A16, B=A16, Bs=A16, C=A16, Cs=A16, dt=A16, A=A16, D=None, h0=None, y=A16, hf=None,
+                b=1, L=256, H=4, P=16, N=16, G=1, Q=64, ws=A16, wsb=1 << 30, stream=None, stage=None)
+    args.update(kw)
+    vals = [args[k] for k in ("x", "xs", "B", "Bs", "C", "Cs", "dt", "A", "D", "h0", "y", "hf", "b", "L", "H",
+                              "P", "N", "G", "Q", "ws", "wsb", "stream")]
+    if args["stage"] is None:
+        return lib.ssdq_chunk_scan(*vals)
+    return lib.ssdq_chunk_scan_stage(args["stage"], *vals)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), INVALID),
+    (dict(y=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(dt=A16 + 4), INVALID),          # misaligned
+    (dict(h0=A16 + 8), INVALID),
+    (dict(b=0), INVALID),
+    (dict(L=0), INVALID),
+    (dict(Q=0), INVALID),
+    (dict(H=6, G=4), INVALID),            # H % G != 0
+    (dict(P=24), UNSUPPORTED),
+    (dict(P=128), UNSUPPORTED),
+    (dict(N=8), UNSUPPORTED),
+    (dict(N=256), UNSUPPORTED),
+    (dict(Q=32), UNSUPPORTED),
+    (dict(Q=100), UNSUPPORTED),
+    (dict(wsb=100), WS_SMALL),
+    (dict(stage=4, wsb=100), INVALID),
+    (dict(stage=-1), INVALID),
+    (dict(stage=2, wsb=100), WS_SMALL),
+])
+def test_chunk_scan_validation(lib, kw, status):
+    assert _scan(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, A16, A16, 10, 4, 16), INVALID),
+    ((A16, A16, A16, -1, 4, 16), INVALID),
+    ((A16, A16, A16, 10, 0, 16), INVALID),
+    ((A16, A16, A16, 10, 4, 0), INVALID),
+    ((A16 + 2, A16, A16, 10, 4, 16), INVALID),
+    ((None, None, None, 0, 4, 16), OK),    # rows == 0: nothing to do
+])
+def test_quantize_validation(lib, args, status):
+    assert lib.ssdq_quantize(*args, None) == status
+
+
+def _upd(lib, **kw):
+    a = dict(state=A16, x=A16, xs=A16, B=A16, Bs=A16, C=A16, Cs=A16, dt=A16, A=A16, D=None, y=A16,
+             b=2, H=8, P=64, N=128, G=2)
+    a.update(kw)
+    return lib.ssdq_state_update(*[a[k] for k in ("state", "x", "xs", "B", "Bs", "C", "Cs", "dt", "A", "D", "y",
+                                                 "b", "H", "P", "N", "G")], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(state=None), INVALID),
+    (dict(y=A16 + 1), INVALID),
+    (dict(b=0), INVALID),
+    (dict(H=8, G=3), INVALID),
+    (dict(N=96), UNSUPPORTED),
+    (dict(P=128), UNSUPPORTED),
+])
+def test_state_update_validation(lib, kw, status):
+    assert _upd(lib, **kw) == status

@@ -1,0 +1,170 @@
+"""GPU parity of ssdq_chunk_scan (prefill) against the fp64 oracle.
+
+Bar (stated for the scan): codes bit-exact; max|y - y_ref| <= 2e-3 max|y_ref| and
+max|h_final - h_ref| <= 1e-4 max|h_ref| over the compared outputs.  Full-size
+workloads run the whole GPU path at their real shape and compare the (batch,
+head) sequences the oracle can afford, always including the outlier heads.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import (H_TOL, Y_TOL, dev, gpu_prefill, gpu_quantize_inputs, note, oracle_codes, rel_err,
+                      sample_pairs, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(inp, chunk=None, with_D=True, with_h0=True, tag=""):
+    codes, y, hf = gpu_prefill(inp, chunk, with_D, with_h0)
+    c = oracle_codes(inp, with_D, with_h0)
+    assert np.array_equal(codes["qx"], c.qx) and np.array_equal(codes["qB"], c.qB) \
+        and np.array_equal(codes["qC"], c.qC)
+    y_ref, h_ref, _ = oracle.ssd(c)
+    ey, eh = rel_err(y, y_ref), rel_err(hf, h_ref)
+    note(f"{tag} y_err={ey:.3e} h_err={eh:.3e}")
+    assert ey <= Y_TOL, ey
+    assert eh <= H_TOL, eh
+    return ey, eh
+
+
+def test_tiny_workload():
+    _check_full(workloads.make_prefill("tiny"), tag="tiny")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_chunk_size_invariance(chunk):
+    inp = workloads.make_custom_prefill(11, batch=2, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=2,
+                                        chunk=chunk, x_dist="outlier_heads", h0_std=0.1)
+    _check_full(inp, tag=f"chunk={chunk}")
+
+
+@pytest.mark.parametrize("L,Q", [(250, 64), (1, 64), (65, 64), (300, 256), (129, 128)])
+def test_ragged_lengths(L, Q):
+    inp = workloads.make_custom_prefill(12, batch=2, seqlen=L, nheads=4, headdim=32, dstate=32, ngroups=2, chunk=Q,
+                                        h0_std=0.2)
+    _check_full(inp, tag=f"L={L} Q={Q}")
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (48, 48), (64, 64), (32, 128), (64, 80)])
+def test_head_and_state_dims(P, N):
+    inp = workloads.make_custom_prefill(13, batch=1, seqlen=320, nheads=3, headdim=P, dstate=N, ngroups=1,
+                                        chunk=64, h0_std=0.1)
+    _check_full(inp, tag=f"P={P} N={N}")
+
+
+def test_without_D_and_h0():
+    inp = workloads.make_custom_prefill(14, batch=2, seqlen=200, nheads=4, headdim=16, dstate=32, ngroups=4,
+                                        chunk=64, h0_std=0.3)
+    _check_full(inp, with_D=False, with_h0=False, tag="no D, no h0")
+    _check_full(inp, with_D=False, with_h0=True, tag="no D, h0")
+
+
+def test_large_dt_and_strong_decay():
+    # dt up to ~8 and A down to -16: the decay mask spans many orders of magnitude
+    inp = workloads.make_custom_prefill(15, batch=1, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=1,
+                                        chunk=256)
+    inp["dt"] = (inp["dt"] * 30).astype(np.float32)
+    _check_full(inp, tag="large dt")
+
+
+def test_no_decay_and_decay_to_zero():
+    inp = workloads.make_custom_prefill(16, batch=1, seqlen=384, nheads=2, headdim=32, dstate=64, ngroups=1,
+                                        chunk=128, h0_std=0.1)
+    inp["A"] = np.zeros_like(inp["A"])
+    _check_full(inp, tag="A=0")
+    inp["A"] = np.full_like(inp["A"], -1e5)
+    _check_full(inp, tag="A=-1e5")
+
+
+def test_h_final_may_alias_h0():
+    import quantized_selective_state_amd as ssdq
+    inp = workloads.make_custom_prefill(17, batch=1, seqlen=256, nheads=2, headdim=32, dstate=32, ngroups=1,
+                                        chunk=64, h0_std=0.2)
+    qx, sx, qB, sB, qC, sC = gpu_quantize_inputs(inp)
+    h = to_dev(inp["h0"])
+    y, hf = ssdq.chunk_scan(qx, sx, qB, sB, qC, sC, to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]), h,
+                            chunk=64, h_final=h)
+    c = oracle_codes(inp)
+    y_ref, h_ref, _ = oracle.ssd(c)
+    assert rel_err(h.cpu().numpy(), h_ref) <= H_TOL
+    assert rel_err(y.float().cpu().numpy(), y_ref) <= Y_TOL
+
+
+def test_stage_intermediates():
+    """Acs, chunk states and the states entering each chunk against their oracle definitions."""
+    import quantized_selective_state_amd as ssdq
+    inp = workloads.make_custom_prefill(18, batch=2, seqlen=600, nheads=4, headdim=64, dstate=128, ngroups=2,
+                                        chunk=256, x_dist="outlier_heads", h0_std=0.1)
+    qx, sx, qB, sB, qC, sC = gpu_quantize_inputs(inp)
+    buf = ssdq.ScanBuffers(qx, sx, qB, sB, qC, sC, to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["D"]),
+                           to_dev(inp["h0"]), chunk=256)
+    c = oracle_codes(inp)
+    views = buf.workspace_views()
+    buf.run_stage(0)
+    acs = views["acs"].cpu().numpy()
+    buf.run_stage(1)
+    S = views["states"].cpu().numpy().copy()
+    buf.run_stage(2)
+    Hprev = views["states"].cpu().numpy().copy()
+    buf.run_stage(3)
+    torch.cuda.synchronize()
+    nc = acs.shape[2]
+    _, h_ref, bounds = oracle.ssd(c, chunk=256)
+    for b in range(c.batch):
+        for h in range(c.H):
+            a_ref = oracle.chunk_cumsum(c, b, h, 256)
+            valid = np.isfinite(a_ref)
+            # fp32 accumulation of up to 256 terms
+            assert np.max(np.abs(acs[b, h][valid] - a_ref[valid])) <= 2e-5 * max(1.0, np.max(np.abs(a_ref[valid])))
+            S_ref = oracle.chunk_state(c, b, h, 256)
+            # three INT8 limbs (~2^-21) plus fp32 cumsum/exp of the decay
+            assert rel_err(S[b, :, h], S_ref) <= 5e-5
+            assert rel_err(Hprev[b, :, h], bounds[b, :, h]) <= H_TOL
+    assert nc == 3
+    y_ref, _, _ = oracle.ssd(c)
+    assert rel_err(buf.y.float().cpu().numpy(), y_ref) <= Y_TOL
+    assert rel_err(buf.h_final.cpu().numpy(), h_ref) <= H_TOL
+
+
+def test_deterministic():
+    inp = workloads.make_custom_prefill(19, batch=2, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=1,
+                                        chunk=256, h0_std=0.1)
+    _, y1, h1 = gpu_prefill(inp)
+    _, y2, h2 = gpu_prefill(inp)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+@pytest.mark.parametrize("name,npairs", [("mamba2-1.3b-prefill", 24), ("mamba2-2.7b-long-prefill", 10),
+                                         ("mamba2-8b-prefill", 12)])
+def test_full_workload_sampled(name, npairs):
+    """Whole GPU path at the workload's real size; oracle on sampled (batch, head) sequences."""
+    note(f"generating {name}")
+    inp = workloads.make_prefill(name)
+    shape = workloads.WORKLOADS[name]
+    note(f"gpu {name}")
+    codes, y, hf = gpu_prefill(inp)
+    c = oracle_codes(inp)
+    assert np.array_equal(codes["qx"], c.qx), "x codes differ"
+    assert np.array_equal(codes["qB"], c.qB) and np.array_equal(codes["qC"], c.qC)
+    # always include the heads with the largest and smallest x scale (outliers / small heads)
+    order = np.argsort(inp["x_scale"])
+    must = list(order[-3:]) + list(order[:2])
+    pairs = sample_pairs(shape.batch, shape.nheads, npairs, 7, must)
+    note(f"oracle {name} on {len(pairs)} sequences")
+    y_ref, h_ref, _ = oracle.ssd(c, pairs=pairs)
+    worst_y = worst_h = 0.0
+    for (b, h) in pairs:
+        worst_y = max(worst_y, rel_err(y[b, :, h], y_ref[b, :, h]) * np.max(np.abs(y_ref[b, :, h])))
+        worst_h = max(worst_h, rel_err(hf[b, h], h_ref[b, h]) * np.max(np.abs(h_ref[b, h])))
+    ymax = max(np.max(np.abs(y_ref[b, :, h])) for b, h in pairs)
+    hmax = max(np.max(np.abs(h_ref[b, h])) for b, h in pairs)
+    ey, eh = worst_y / ymax, worst_h / hmax
+    per_seq = max(rel_err(y[b, :, h], y_ref[b, :, h]) for b, h in pairs)
+    note(f"{name}: y_err={ey:.3e} h_err={eh:.3e} (worst single-sequence y ratio {per_seq:.3e})")
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(hf))
+    assert ey <= Y_TOL and eh <= H_TOL
