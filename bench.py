@@ -52,16 +52,16 @@ def kernel_bytes(b, L, H, P, N, G, Q):
     bc = tok * G * N
     dt = tok * H * 4
     acs = b * H * nc * Q * 4
-    st = b * nc * H * P * N * 4
+    st32 = b * nc * H * P * N * 4          # chunk states, fp32
+    st16 = b * nc * H * P * N * 2 + b * nc * H * P * 4   # fp16 carried state + row scales
     hfin = b * H * P * N * 4
     return {
         "quantize_x": 3 * x,
         "quantize_B": 3 * bc,
         "quantize_C": 3 * bc,
-        "chunk_cumsum": dt + acs,
-        "chunk_state": x + bc + dt + acs + st,
-        "state_passing": 2 * st + hfin,
-        "chunk_output": x + 2 * bc + dt + acs + st + 2 * tok * H * P,
+        "chunk_state": x + bc + dt + acs + st32,            # also writes Acs
+        "state_passing": st32 + acs // Q * 1 + st16 + hfin,
+        "chunk_output": x + 2 * bc + dt + acs + st16 + 2 * tok * H * P,
     }
 
 

@@ -70,13 +70,14 @@ ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int6
                           int32_t inner, hipStream_t stream);
 
 /* Bytes of workspace ssdq_chunk_scan needs for this shape (host; 0 on invalid shapes).
- * Layout (stable, used by the stage-level tests):
- *   [0, acs_bytes)           Acs   fp32 (batch, nheads, nchunks, chunk): within-chunk
- *                            inclusive cumsum of dt * A (padded past the sequence end)
- *   [acs_bytes, total)       states fp32 (batch, nchunks, nheads, headdim, dstate):
- *                            chunk states S_c after stage 1, overwritten by stage 2 with
- *                            the state ENTERING each chunk
- * where nchunks = ceil(seqlen / chunk) and acs_bytes is rounded up to 256 bytes. */
+ * Layout (stable, used by the stage-level tests), with nchunks = ceil(seqlen / chunk) and
+ * each region starting at a 256-byte boundary:
+ *   Acs     fp32 (batch, nheads, nchunks, chunk): within-chunk inclusive cumsum of dt * A
+ *           (padded past the sequence end with the last value)           -- written by stage 0
+ *   S       fp32 (batch, nchunks, nheads, headdim, dstate): chunk states  -- written by stage 0
+ *   Hprev   fp16 (batch, nchunks, nheads, headdim, dstate) and
+ *   Hscale  fp32 (batch, nchunks, nheads, headdim): the state entering each chunk is
+ *           Hprev[..., p, n] * Hscale[..., p] (a power of two per state row) -- stage 1 */
 size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                       int32_t dstate, int32_t chunk);
 
@@ -99,7 +100,7 @@ size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nhe
  *   h_final : (batch, nheads, headdim, dstate) fp32 or NULL; may alias h0
  *   workspace : device scratch of at least ssdq_chunk_scan_workspace_size() bytes,
  *               owned by the caller, not shared with a concurrent call
- * Supported shapes: headdim % 16 == 0 and headdim <= 64; dstate % 64 == 0 and
+ * Supported shapes: headdim % 16 == 0 and headdim <= 64; dstate % 16 == 0 and
  * dstate <= 128; chunk in {64, 128, 256}; any seqlen >= 1 (a ragged last chunk
  * is masked); nheads % ngroups == 0.  Others return SSDQ_ERROR_UNSUPPORTED.
  * Accuracy: y within 2e-3 * max|y| and h_final within 1e-4 * max|h| of the exact
@@ -111,13 +112,13 @@ ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t*
                             int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                             int32_t chunk, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Number of stages ssdq_chunk_scan runs, in order: 0 chunk cumsum, 1 chunk state,
- * 2 state passing, 3 chunk output. */
-#define SSDQ_CHUNK_SCAN_STAGES 4
+/* Number of stages ssdq_chunk_scan runs, in order: 0 chunk cumsum + chunk state,
+ * 1 state passing, 2 chunk output. */
+#define SSDQ_CHUNK_SCAN_STAGES 3
 
 /*
  * One stage of ssdq_chunk_scan, with the same arguments and validation.
- * Running stages 0..3 in order on one stream is exactly ssdq_chunk_scan; the
+ * Running stages 0..2 in order on one stream is exactly ssdq_chunk_scan; the
  * intermediate results are in the workspace layout documented above.  This
  * lets a caller time each kernel with its own events and lets tests inspect
  * the intermediates.  stage outside [0, SSDQ_CHUNK_SCAN_STAGES) is INVALID_VALUE.
@@ -139,7 +140,7 @@ ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x
  *   state : (batch, nheads, headdim, dstate) fp32, read and written
  *   x : (batch, nheads, headdim) int8     B, C : (batch, ngroups, dstate) int8
  *   dt : (batch, nheads) fp32   A : [nheads]   D : [nheads] or NULL   y : (batch, nheads, headdim) fp16
- * Supported: dstate == 128 or dstate == 64, headdim % 8 == 0, nheads % ngroups == 0.
+ * Supported: dstate == 128 or dstate == 64, headdim <= 64, nheads % ngroups == 0.
  */
 ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                               const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,

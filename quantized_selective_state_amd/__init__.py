@@ -22,8 +22,8 @@ SSDQ_ERROR_INVALID_VALUE = 1
 SSDQ_ERROR_UNSUPPORTED = 2
 SSDQ_ERROR_WORKSPACE_TOO_SMALL = 3
 SSDQ_ERROR_LAUNCH = 4
-CHUNK_SCAN_STAGES = 4
-STAGE_NAMES = ("chunk_cumsum", "chunk_state", "state_passing", "chunk_output")
+CHUNK_SCAN_STAGES = 3
+STAGE_NAMES = ("chunk_state", "state_passing", "chunk_output")   # stage 0 also runs the chunk cumsum
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_selective_state_amd.build`")
@@ -128,11 +128,17 @@ def chunk_scan_workspace_size(batch: int, seqlen: int, nheads: int, headdim: int
 
 
 def workspace_layout(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, chunk: int) -> dict:
-    """Offsets of the documented workspace regions (for stage-level inspection)."""
+    """Offsets (bytes) and shapes of the documented workspace regions (see include/ssdq.h)."""
+    r256 = lambda v: (v + 255) // 256 * 256
     nc = -(-seqlen // chunk)
-    acs_bytes = ((4 * batch * nheads * nc * chunk) + 255) // 256 * 256
-    return dict(nchunks=nc, acs_offset=0, acs_shape=(batch, nheads, nc, chunk), states_offset=acs_bytes,
-                states_shape=(batch, nc, nheads, headdim, dstate))
+    acs = r256(4 * batch * nheads * nc * chunk)
+    st = 4 * batch * nc * nheads * headdim * dstate
+    hp = r256(2 * batch * nc * nheads * headdim * dstate)
+    return dict(nchunks=nc,
+                acs=(0, "float32", (batch, nheads, nc, chunk)),
+                states=(acs, "float32", (batch, nc, nheads, headdim, dstate)),
+                hprev=(acs + st, "float16", (batch, nc, nheads, headdim, dstate)),
+                hscale=(acs + st + hp, "float32", (batch, nc, nheads, headdim)))
 
 
 class ScanBuffers:
@@ -182,18 +188,19 @@ class ScanBuffers:
         _check(lib.ssdq_chunk_scan_stage(stage, *self._args, _stream(self.device)), "ssdq_chunk_scan_stage")
 
     def workspace_views(self) -> dict:
+        """Typed views of the workspace regions (for inspecting stage results)."""
         b, L, H, P, N, G, Q = self.dims
         lay = workspace_layout(b, L, H, P, N, Q)
-        acs_n = 1
-        for d in lay["acs_shape"]:
-            acs_n *= d
-        st_n = 1
-        for d in lay["states_shape"]:
-            st_n *= d
-        ws = self.workspace
-        acs = ws[lay["acs_offset"]:lay["acs_offset"] + 4 * acs_n].view(torch.float32).view(lay["acs_shape"])
-        st = ws[lay["states_offset"]:lay["states_offset"] + 4 * st_n].view(torch.float32).view(lay["states_shape"])
-        return dict(acs=acs, states=st)
+        out = {}
+        for key in ("acs", "states", "hprev", "hscale"):
+            off, dtype, shape = lay[key]
+            dt = getattr(torch, dtype)
+            n = 1
+            for d in shape:
+                n *= d
+            nbytes = n * torch.empty((), dtype=dt).element_size()
+            out[key] = self.workspace[off:off + nbytes].view(dt).view(shape)
+        return out
 
 
 def chunk_scan(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk=256, y=None, h_final=None,

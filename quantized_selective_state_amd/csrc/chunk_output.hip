@@ -1,4 +1,4 @@
-// Stage 3 of the chunked SSD scan: the output of chunk c,
+// Stage 2 of the chunked SSD scan: the output of chunk c,
 //
 //   y[l, p] = sum_{j <= l} M[l, j] xhat[j, p]  +  exp(Acs_l) Chat_l . Hprev_c[p, :]  +  D xhat[l, p]
 //   M[l, j] = (Chat_l . Bhat_j) exp(Acs_l - Acs_j) dt_j
@@ -6,16 +6,21 @@
 // (the state-space-duality form: the masked "attention" C B^T inside a chunk plus the
 // carried state read out by C; SSDi8 Figure 1b / Table 5: ChunkBMM C.B^T on INT8).
 //
-// Per block (8 waves) = one (batch, chunk, head); each wave owns 16-row output blocks.
-//  - G^T[j, l] = sum_n q_B[j, n] q_C[l, n]: v_mfma_i32_16x16x64_i8, exact int32.
-//  - The decay mask and dt are applied to the accumulator fragment in registers and the
-//    result, converted to fp16 with a power-of-two guard against overflow, is fed straight
-//    into the next product as its B operand (no LDS round trip): the K slots of the fp16
-//    MFMA are matched to the rows the int32 fragment holds, and the x operand is read from
-//    LDS in the same slot order.
-//  - y^T += x^T M^T and y_off^T = Hprev C^T: v_mfma_f32_16x16x32_f16 (fp32 accumulation),
-//    x codes exact in fp16, Hprev scaled by a power of two and rounded to fp16.
-//  - fp32 epilogue applies the scales, adds D x, rounds to fp16, stores 8-byte rows.
+// One block (8 waves) per (batch, chunk, head); each wave owns 16-row output blocks.
+//  - G^T[j, l] = sum_n q_B[j, n] q_C[l, n] on v_mfma_i32_16x16x64_i8 (exact int32).
+//  - Decay mask, SSDi8-style decoupled from the matrix products: for a 32-token block that
+//    lies entirely before the 16 output rows l0..l0+15, exp(Acs_l - Acs_j) =
+//    exp(Acs_l - Acs_l0) exp(Acs_l0 - Acs_j), both factors <= 1, so the per-element work is
+//    G * w_j (w_j = exp(Acs_l0 - Acs_j) dt_j, once per token) and the row factor
+//    u_l = exp(Acs_l - Acs_l0) is applied in the epilogue.  The block holding the diagonal
+//    uses the exact per-element exp with the causal mask.
+//  - The masked fragment, rounded to fp16 under a power-of-two guard, feeds the next product
+//    as its B operand straight from registers: the fp16 MFMA's K slots are matched to the
+//    rows the int32 fragment holds, and x^T is read from LDS in the same slot order.
+//  - y^T += x^T M^T and y_off^T = Hprev C^T on v_mfma_f32_16x16x32_f16 (fp32 accumulation):
+//    x codes are exact in fp16; Hprev arrives as fp16 with one power-of-two scale per row.
+//  - LDS matrices use 16-byte-chunk XOR swizzles so that the transposing writes and the
+//    MFMA operand reads are free of bank conflicts.
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -26,26 +31,67 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxQ = 256;
 constexpr int kMaxP = 64;
 constexpr int kMaxN = 128;
-constexpr int kBStride = kMaxN + 16;      // bytes per token row of B codes in LDS
-constexpr int kXStride = kMaxQ + 8;       // halves per channel row of x^T in LDS
-constexpr int kHStride = kMaxN + 8;       // halves per channel row of Hprev in LDS
+constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float sbyte(uint32_t w, int i) {
-  return float(int32_t(w << (24 - 8 * i)) >> 24);
+// x^T: [p][j] fp16, 512-byte rows, 16-byte chunk c stored at c ^ xswz(p)
+__device__ __forceinline__ int xswz(int p) { return (p & 15) ^ ((p >> 4) & 3); }
+__device__ __forceinline__ int xpos(int p, int j) { return p * kMaxQ + ((((j >> 3) ^ xswz(p)) << 3) | (j & 7)); }
+// B codes: [j][n] int8, 128-byte rows, chunk c stored at c ^ ((j >> 1) & 7)
+__device__ __forceinline__ int bpos(int j, int byte) {
+  return j * kMaxN + ((((byte >> 4) ^ ((j >> 1) & 7)) << 4) | (byte & 15));
+}
+// Hprev: [p][n] fp16, 256-byte rows, chunk c stored at c ^ (p & 15)
+__device__ __forceinline__ int hpos(int p, int n) { return p * kMaxN + ((((n >> 3) ^ (p & 15)) << 3) | (n & 7)); }
+
+__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
+  const uint32_t t01lo = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+  const uint32_t t01hi = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+  const uint32_t t23lo = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+  const uint32_t t23hi = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+  out[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);
+  out[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+  out[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+  out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
+}
+
+// Four int8 codes (biased by 128, i.e. XORed with 0x80 per byte) -> four exact fp16 values:
+// the fp16 with bits 0x64XX is 1024 + XX, so subtracting 1152 leaves the signed code.
+__device__ __forceinline__ v4h codes_to_f16(uint32_t biased) {
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, biased, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, biased, 0x04030402u);
+  const v2h off = {_Float16(-1152.f), _Float16(-1152.f)};
+  const v2h a = __builtin_bit_cast(v2h, lo) + off;
+  const v2h b = __builtin_bit_cast(v2h, hi) + off;
+  return v4h{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ void task_coords(int task, int xq_n, int& xq, int& jq) {
+  if ((xq_n & 15) == 0) {
+    const int hi_n = xq_n >> 4;
+    const int rest = task >> 6;
+    xq = (task & 15) + 16 * (rest % hi_n);
+    jq = ((task >> 4) & 3) + 4 * (rest / hi_n);
+  } else {
+    xq = task % xq_n;
+    jq = task / xq_n;
+  }
 }
 
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
     const float* __restrict__ B_scale, const int8_t* __restrict__ Cm, const float* __restrict__ C_scale,
     const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ acs,
-    const float* __restrict__ hprev, _Float16* __restrict__ y, int64_t seqlen, int32_t nheads, int32_t headdim,
-    int32_t dstate, int32_t ngroups, int32_t chunk, int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) int8_t Bs[kMaxQ][kBStride];
-  __shared__ __attribute__((aligned(16))) _Float16 xT[kMaxP][kXStride];
-  __shared__ __attribute__((aligned(16))) _Float16 Hh[kMaxP][kHStride];
-  __shared__ __attribute__((aligned(16))) float acs_s[kMaxQ];
-  __shared__ __attribute__((aligned(16))) float dts_s[kMaxQ];
-  __shared__ float red[2][kWaves];
+    const _Float16* __restrict__ hprev, const float* __restrict__ hscale, _Float16* __restrict__ y,
+    int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk,
+    int32_t nchunks) {
+  __shared__ __attribute__((aligned(16))) _Float16 xT[kMaxP * kMaxQ];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[kMaxQ * kMaxN];
+  __shared__ __attribute__((aligned(16))) _Float16 Hh[kMaxP * kMaxN];
+  __shared__ __attribute__((aligned(16))) float hsc[kMaxP];
+  __shared__ __attribute__((aligned(16))) float acs2[kMaxQ];   // Acs * log2(e)
+  __shared__ __attribute__((aligned(16))) float dts[kMaxQ];    // dt * 2^-kM
+  __shared__ __attribute__((aligned(16))) float wl[kWaves][kMaxQ];
+  __shared__ float red[kWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -61,101 +107,67 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
   const int NP = (N + 63) & ~63;   // K extent of the int8 product (zero padded)
   const int NH = (N + 31) & ~31;   // K extent of the fp16 product (zero padded)
 
-  // ---- per-token decay log and dt; dt max -> power-of-two guard for M in fp16
+  // ---- per-token decay log and dt
   const float* acs_c = acs + ((int64_t(b) * nheads + h) * nchunks + c) * chunk;
   float dtv = 0.f;
   if (tid < Q) {
-    acs_s[tid] = acs_c[tid];
+    acs2[tid] = acs_c[tid] * kLog2e;
     if (tid < len) dtv = dt[(int64_t(b) * seqlen + t0 + tid) * nheads + h];
-  }
-  // Hprev tile (P x N fp32) into registers: 16 floats per thread at most
-  const float* Hsrc = hprev + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N;
-  const int pn4 = P * N / 4;
-  float4 hv[4];
-  float hmax = 0.f;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = tid + k * kThreads;
-    hv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (idx < pn4) hv[k] = *reinterpret_cast<const float4*>(Hsrc + 4 * idx);
-    hmax = fmaxf(hmax, fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)), fmaxf(fabsf(hv[k].z), fabsf(hv[k].w))));
   }
   {
     const float dm = wave_max(dtv);
-    const float hm = wave_max(hmax);
-    if (lane == 0) {
-      red[0][wave] = dm;
-      red[1][wave] = hm;
-    }
+    if (lane == 0) red[wave] = dm;
   }
-
-  // ---- B codes of the chunk, row-major, zero padded to NP columns and Q rows
+  // ---- B codes (row-major, zero padded to NP columns and Q rows)
   {
     const int segs = NP / 16;
     const int8_t* Bb = Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N;
     for (int task = tid; task < Q * segs; task += kThreads) {
       const int j = task / segs, sg = task % segs;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (j < len && 16 * sg < N) v = *reinterpret_cast<const uint4*>(Bb + int64_t(j) * ngroups * N + 16 * sg);
-      *reinterpret_cast<uint4*>(&Bs[j][16 * sg]) = v;
+      v4u v = {0u, 0u, 0u, 0u};
+      if (j < len && 16 * sg < N) v = *reinterpret_cast<const v4u*>(Bb + int64_t(j) * ngroups * N + 16 * sg);
+      *reinterpret_cast<v4u*>(Bs + bpos(j, 16 * sg)) = v;
     }
   }
-  // ---- x codes of the chunk as fp16, transposed: xT[p][j]
+  // ---- Hprev (fp16, zero padded to NH columns) and its per-row scales
+  {
+    const int segs = NH / 8;
+    const _Float16* Hb = hprev + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N;
+    for (int task = tid; task < P * segs; task += kThreads) {
+      const int p = task / segs, sg = task % segs;
+      v4u v = {0u, 0u, 0u, 0u};
+      if (8 * sg < N) v = *reinterpret_cast<const v4u*>(Hb + int64_t(p) * N + 8 * sg);
+      *reinterpret_cast<v4u*>(Hh + hpos(p, 8 * sg)) = v;
+    }
+    if (tid < P) hsc[tid] = hscale[((int64_t(b) * nchunks + c) * nheads + h) * P + tid];
+  }
+  // ---- x codes as exact fp16, token-contiguous: xT[p][j]
   {
     const int pq_n = P / 4, jq_n = Q / 4;
     const int8_t* xb = x + ((int64_t(b) * seqlen + t0) * nheads + h) * P;
     for (int task = tid; task < pq_n * jq_n; task += kThreads) {
-      const int pq = task % pq_n, jq = task / pq_n;
-      uint32_t wv[4];
+      int pq, jq;
+      task_coords(task, pq_n, pq, jq);
+      uint32_t in[4], out[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * jq + r;
-        wv[r] = (j < len) ? *reinterpret_cast<const uint32_t*>(xb + int64_t(j) * nheads * P + 4 * pq) : 0u;
+        in[r] = ((j < len) ? *reinterpret_cast<const uint32_t*>(xb + int64_t(j) * nheads * P + 4 * pq) : 0u) ^
+                0x80808080u;
       }
+      transpose4x4(in, out);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v4h col;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) col[r] = _Float16(sbyte(wv[r], i));
-        *reinterpret_cast<v4h*>(&xT[4 * pq + i][4 * jq]) = col;
-      }
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + xpos(4 * pq + i, 4 * jq)) = codes_to_f16(out[i]);
     }
   }
   __syncthreads();
 
-  float dtmax = red[0][0], hmx = red[1][0];
+  float dtmax = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) {
-    dtmax = fmaxf(dtmax, red[0][i]);
-    hmx = fmaxf(hmx, red[1][i]);
-  }
-  // |M'| <= N * 127^2 * dtmax * 2^-kM <= 2^15 ;  |Hprev| * 2^-eh <= 2^14
-  // exponents clamped so that both 2^e and 2^-e are exact normal floats
+  for (int i = 1; i < kWaves; ++i) dtmax = fmaxf(dtmax, red[i]);
+  // |M'| <= N 127^2 dtmax 2^-kM <= 2^15; clamped so that 2^kM and 2^-kM are exact
   const int kM = min(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, -120), 120);
-  const int eh = min(max(ceil_log2_pos(hmx) - 14, -120), 120);
-  const float mscale = exp2i(-kM);
-  const float hscale = exp2i(-eh);
-  if (tid < Q) dts_s[tid] = dtv * mscale;
-  // Hprev -> fp16 in LDS, zero padded to NH columns
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = tid + k * kThreads;
-    if (idx < pn4) {
-      const int p = (4 * idx) / N, n = (4 * idx) % N;
-      v4h hh;
-      hh[0] = _Float16(hv[k].x * hscale);
-      hh[1] = _Float16(hv[k].y * hscale);
-      hh[2] = _Float16(hv[k].z * hscale);
-      hh[3] = _Float16(hv[k].w * hscale);
-      *reinterpret_cast<v4h*>(&Hh[p][n]) = hh;
-    }
-  }
-  if (NH > N) {
-    for (int idx = tid; idx < P * (NH - N); idx += kThreads) {
-      const int p = idx / (NH - N), n = N + idx % (NH - N);
-      Hh[p][n] = _Float16(0.f);
-    }
-  }
+  if (tid < Q) dts[tid] = dtv * exp2i(-kM);
   __syncthreads();
 
   // ---- per-wave 16-row output blocks
@@ -164,7 +176,9 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
   const int ptn = P / 16;
   const float sx = x_scale[h], sB = B_scale[g], sC = C_scale[g];
   const float Dh = D ? D[h] : 0.f;
+  const float s_in = sx * sC * sB * exp2i(kM);
   const int8_t* Cb = Cm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N;
+  float* wlw = wl[wave];
 
   for (int pass = 0; pass < 2; ++pass) {
     const int lb = (pass == 0) ? wave : (2 * kWaves - 1 - wave);
@@ -173,8 +187,15 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
     const int l = l0 + lcol;
     const bool lvalid = l < len;
     const int8_t* Crow = Cb + int64_t(l) * ngroups * N;
+    const int jdiag = l0 & ~31;          // the 32-token block that holds the diagonal
+    const float a_l = acs2[l];
+    const float a_0 = acs2[l0];
 
-    // C row of this lane's output token as int8 K-slices (for C.B^T) ...
+    // weights of the blocks before the diagonal, relative to row l0
+    for (int j = lane; j < jdiag; j += kWave) wlw[j] = exp2f(a_0 - acs2[j]) * dts[j];
+    __builtin_amdgcn_wave_barrier();
+    const float u_l = exp2f(a_l - a_0);
+
     v4i cq[kMaxN / 64];
 #pragma unroll
     for (int s = 0; s < kMaxN / 64; ++s) {
@@ -183,36 +204,34 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
       if (64 * s < NP && lvalid && off < N) cq[s] = *reinterpret_cast<const v4i*>(Crow + off);
     }
 
-    v4f yin[kMaxP / 16], yoff[kMaxP / 16];
+    v4f yf[kMaxP / 16], yd[kMaxP / 16], yo[kMaxP / 16];
 #pragma unroll
     for (int pt = 0; pt < kMaxP / 16; ++pt) {
-      yin[pt] = v4f{0.f, 0.f, 0.f, 0.f};
-      yoff[pt] = v4f{0.f, 0.f, 0.f, 0.f};
+      yf[pt] = v4f{0.f, 0.f, 0.f, 0.f};
+      yd[pt] = v4f{0.f, 0.f, 0.f, 0.f};
+      yo[pt] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ... and as fp16 K-slices (for Hprev.C^T)
+    // carried state read out by C: y_off^T[p][l] = sum_n Hprev[p][n] q_C[l][n]
     for (int kb = 0; kb < NH; kb += 32) {
       const int off = kb + 8 * kg;
-      uint2 raw = make_uint2(0u, 0u);
-      if (lvalid && off < N) raw = *reinterpret_cast<const uint2*>(Crow + off);
-      v8h cop;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cop[i] = _Float16(sbyte(raw.x, i));
-        cop[4 + i] = _Float16(sbyte(raw.y, i));
-      }
+      v2u raw = {0u, 0u};
+      if (lvalid && off < N) raw = *reinterpret_cast<const v2u*>(Crow + off);
+      const v4h c0 = codes_to_f16(raw[0] ^ 0x80808080u);
+      const v4h c1 = codes_to_f16(raw[1] ^ 0x80808080u);
+      const v8h cop = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
 #pragma unroll
       for (int pt = 0; pt < kMaxP / 16; ++pt) {
         if (pt < ptn) {
-          const v8h hop = *reinterpret_cast<const v8h*>(&Hh[16 * pt + lcol][off]);
-          yoff[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hop, cop, yoff[pt], 0, 0, 0);
+          const v8h hop = *reinterpret_cast<const v8h*>(Hh + hpos(16 * pt + lcol, off));
+          yo[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hop, cop, yo[pt], 0, 0, 0);
         }
       }
     }
 
-    const float acs_l = acs_s[l < Q ? l : Q - 1];
-    for (int jb = 0; jb <= l0 + 15; jb += 32) {
-      // G^T for the two 16-token sub-blocks of this 32-token K block
+    // intra-chunk part, 32 tokens per step
+    for (int jb = 0; jb <= jdiag; jb += 32) {
+      const bool diag = (jb == jdiag);
       v4i gm[2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
@@ -222,54 +241,68 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
 #pragma unroll
           for (int s = 0; s < kMaxN / 64; ++s) {
             if (64 * s < NP) {
-              const v4i bop = *reinterpret_cast<const v4i*>(&Bs[js + lcol][64 * s + 16 * kg]);
+              const v4i bop = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 64 * s + 16 * kg));
               gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, cq[s], gm[sb], 0, 0, 0);
             }
           }
         }
       }
-      // decay mask + dt -> fp16 B operand; slot s holds token j(kg, s)
-      v8h mop;
+      float mv[8];
+      if (!diag) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int jq = jb + 16 * sb + 4 * kg;
-        const float4 aj = *reinterpret_cast<const float4*>(&acs_s[jq < Q ? jq : 0]);
-        const float4 dj = *reinterpret_cast<const float4*>(&dts_s[jq < Q ? jq : 0]);
-        const float av[4] = {aj.x, aj.y, aj.z, aj.w};
-        const float dv[4] = {dj.x, dj.y, dj.z, dj.w};
+        for (int sb = 0; sb < 2; ++sb) {
+          const float4 w4 = *reinterpret_cast<const float4*>(&wlw[jb + 16 * sb + 4 * kg]);
+          mv[4 * sb + 0] = float(gm[sb][0]) * w4.x;
+          mv[4 * sb + 1] = float(gm[sb][1]) * w4.y;
+          mv[4 * sb + 2] = float(gm[sb][2]) * w4.z;
+          mv[4 * sb + 3] = float(gm[sb][3]) * w4.w;
+        }
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = jq + i;
-          float m = 0.f;
-          if (j <= l && jq < Q) m = float(gm[sb][i]) * __expf(acs_l - av[i]) * dv[i];
-          mop[4 * sb + i] = _Float16(m);
+        for (int sb = 0; sb < 2; ++sb) {
+          const int jq = jb + 16 * sb + 4 * kg;
+          const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float m = float(gm[sb][i]) * exp2f(a_l - av[i]) * dv[i];
+            mv[4 * sb + i] = (jq + i <= l) ? m : 0.f;
+          }
         }
       }
+      v8h mop;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mop[k] = _Float16(mv[k]);
 #pragma unroll
       for (int pt = 0; pt < kMaxP / 16; ++pt) {
         if (pt < ptn) {
-          const v4h lo = *reinterpret_cast<const v4h*>(&xT[16 * pt + lcol][jb + 4 * kg]);
-          const v4h hi = *reinterpret_cast<const v4h*>(&xT[16 * pt + lcol][jb + 16 + 4 * kg]);
+          const int p = 16 * pt + lcol;
+          const v4h lo = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 4 * kg));
+          const v4h hi = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 16 + 4 * kg));
           const v8h xop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          yin[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yin[pt], 0, 0, 0);
+          if (diag) yd[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yd[pt], 0, 0, 0);
+          else yf[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yf[pt], 0, 0, 0);
         }
       }
     }
 
     // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
     if (lvalid) {
-      const float s_in = sx * sC * sB * exp2i(kM);
-      const float s_off = __expf(acs_l) * sC * exp2i(eh);
+      const float s_off = exp2f(a_l) * sC;
       _Float16* yrow = y + ((int64_t(b) * seqlen + t0 + l) * nheads + h) * P;
 #pragma unroll
       for (int pt = 0; pt < kMaxP / 16; ++pt) {
         if (pt < ptn) {
+          const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
+          const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
           v4h out;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int p = 16 * pt + 4 * kg + i;
-            const float xd = float(xT[p][l]) * sx * Dh;
-            out[i] = _Float16(yin[pt][i] * s_in + yoff[pt][i] * s_off + xd);
+            const float xd = float(xT[xpos(p, l)]) * sx * Dh;
+            out[i] = _Float16((u_l * yf[pt][i] + yd[pt][i]) * s_in + yo[pt][i] * (s_off * hv[i]) + xd);
           }
           *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg) = out;
         }
@@ -283,8 +316,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   const int nblocks = s.batch * s.nchunks * s.nheads;
   hipLaunchKernelGGL(chunk_output_kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
-                     a.C, a.C_scale, a.dt, a.D, a.acs, a.states, a.y, s.seqlen, s.nheads, s.headdim, s.dstate,
-                     s.ngroups, s.chunk, s.nchunks);
+                     a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.y, s.seqlen, s.nheads, s.headdim,
+                     s.dstate, s.ngroups, s.chunk, s.nchunks);
   return hipGetLastError();
 }
 

@@ -1,40 +1,46 @@
-// Stage 1 of the chunked SSD scan: the state each chunk contributes on its own,
+// Stage 0 of the chunked SSD scan, one block (8 waves) per (batch, chunk, head):
 //
-//   S_c[p, n] = sum_{j in chunk c} w_j * xhat[j, p] * Bhat[j, n],
-//   w_j = exp(Acs[c, last] - Acs[c, j]) * dt_j          (SSDi8's LUT_state, Figure 3a)
+//  (a) chunk cumsum: Acs[j] = sum_{i <= j} dt_i A_h inside the chunk (tokens past the end
+//      of the sequence add 0), written to the workspace for the later stages;
+//  (b) chunk state: the state the chunk contributes on its own,
 //
-// computed as SSDi8 reformulates it (abstract; Figure 3a): first the element-wise
-// X_scaled[j, p] = w_j * q_x[j, p], then a plain matrix product with the INT8 codes of B
-// on the INT8 matrix cores.  A single INT8 copy of X_scaled loses too much precision for a
-// 1e-4 state bound, so X_scaled is split into three exact INT8 limbs (the multi-component
-// idea of the Multi-Scale Dequant abstract):
+//        S_c[p, n] = sum_j w_j xhat[j, p] Bhat[j, n],   w_j = exp(Acs_last - Acs_j) dt_j
 //
-//   t = X_scaled / 2^e  with 2^e >= max_j w_j, so |t| <= 127;
-//   t = l1 + l2 / 128 + l3 / 128^2 + r,   l1 in [-127, 127], l2, l3 in [-64, 64], |r| <= 2^-15
+//      (w_j is SSDi8's LUT_state, Figure 3a), computed the way SSDi8 reformulates it
+//      (abstract; Figure 3a): the element-wise X_scaled[j, p] = w_j q_x[j, p] first, then a
+//      plain product with the INT8 codes of B on the INT8 matrix cores.
 //
-// Each limb is contracted with q_B on v_mfma_i32_16x16x64_i8 with exact int32 accumulation
-// (|sum| <= Q * 127 * 127 < 2^24), and the fp32 epilogue recombines the limbs.
+// One INT8 copy of X_scaled is too coarse for a 1e-4 state bound, so X_scaled is carried
+// as three INT8 limbs (the multi-component idea of the Multi-Scale Dequant abstract):
+// with 2^e >= max_j w_j and t = X_scaled 2^-e (|t| <= 127), the integer
+// V = trunc(65536 t + 32896) has the base-256 digits  V = l1 65536 + (l2+128) 256 + (l3+128),
+// so t = l1 + l2/256 + l3/65536 to within 2^-16, with l1, l2, l3 signed bytes.  The bytes
+// of V are the limbs, so a 4x4 byte transpose of four tokens' V yields the MFMA operand
+// words directly.  Each limb goes through v_mfma_i32_16x16x64_i8 with exact int32 sums
+// (|sum| <= Q 128 127 < 2^23) and an fp32 epilogue recombines them.
 //
-// One block (8 waves) per (batch, chunk, head).  Both MFMA operands contract over the token
-// axis, which is the slow axis in memory, so the block writes the limbs and B to LDS
-// token-contiguous ("transposed"): limbT[limb][p][j], BT[n][j].
+// Both operands contract over tokens, the slow axis in memory, so x and B are transposed
+// into LDS (token-contiguous 256-byte rows).  Rows use a 16-byte-chunk XOR swizzle that
+// keeps both the transposing writes (rows 4q+i of 16 consecutive q) and the MFMA operand
+// reads (16 consecutive rows) free of bank conflicts.  The limbs are built in registers
+// from the x^T rows right before the MFMAs.
 #include "ssdq_internal.h"
 
 namespace ssdq {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxQ = 256;
 constexpr int kMaxP = 64;
 constexpr int kMaxN = 128;
-constexpr int kRowPad = 16;                 // bytes; keeps 16-row b128 reads conflict-free
-constexpr int kStride = kMaxQ + kRowPad;    // LDS row stride (bytes) for token-contiguous rows
-constexpr float kMagic = 12582912.0f;       // 1.5 * 2^23: x + kMagic rounds x to an integer (ties to even)
+constexpr int kRow = kMaxQ;          // bytes per token-contiguous LDS row
+constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ uint32_t pack_low_bytes(float a0, float a1, float a2, float a3) {
-  const uint32_t p01 = __builtin_amdgcn_perm(__float_as_uint(a1), __float_as_uint(a0), 0x0c0c0400u);
-  const uint32_t p23 = __builtin_amdgcn_perm(__float_as_uint(a3), __float_as_uint(a2), 0x0c0c0400u);
-  return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+__device__ __forceinline__ int swz(int row) { return (row & 15) ^ ((row >> 4) & 3); }
+// byte offset of (row, token byte) in a swizzled [rows][256] int8 matrix
+__device__ __forceinline__ int tpos(int row, int byte) {
+  return row * kRow + ((((byte >> 4) ^ swz(row)) << 4) | (byte & 15));
 }
 
 // 4x4 byte transpose: out[i] byte r = in[r] byte i.
@@ -49,19 +55,52 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
   out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-__device__ __forceinline__ float sbyte(uint32_t w, int i) {
-  return float(int32_t(w << (24 - 8 * i)) >> 24);
+// Transposition task -> (channel quad, token quad).  When there are 16k channel quads,
+// a wave's 64 lanes take 16 consecutive channel quads x 4 consecutive token quads, which
+// makes the swizzled LDS writes conflict-free; other shapes use a plain mapping.
+__device__ __forceinline__ void task_coords(int task, int xq_n, int& xq, int& jq) {
+  if ((xq_n & 15) == 0) {
+    const int hi_n = xq_n >> 4;
+    const int rest = task >> 6;
+    xq = (task & 15) + 16 * (rest % hi_n);
+    jq = ((task >> 4) & 3) + 4 * (rest / hi_n);
+  } else {
+    xq = task % xq_n;
+    jq = task / xq_n;
+  }
+}
+
+// Load `rows`-channel codes of the chunk (row stride `stride` bytes in global memory)
+// and store them token-contiguous into the swizzled LDS matrix.
+__device__ __forceinline__ void transpose_into(uint8_t* lds, const int8_t* src, int64_t stride, int channels,
+                                               int Q, int len, int tid) {
+  const int xq_n = channels / 4, jq_n = Q / 4;
+  for (int task = tid; task < xq_n * jq_n; task += kThreads) {
+    int xq, jq;
+    task_coords(task, xq_n, xq, jq);
+    uint32_t in[4], out[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 4 * jq + r;
+      in[r] = (j < len) ? *reinterpret_cast<const uint32_t*>(src + int64_t(j) * stride + 4 * xq) : 0u;
+    }
+    transpose4x4(in, out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(lds + tpos(4 * xq + i, 4 * jq)) = out[i];
+  }
 }
 
 __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
-    const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ acs,
-    float* __restrict__ states, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
-    int32_t ngroups, int32_t chunk, int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) uint8_t limbT[3][kMaxP][kStride];
-  __shared__ __attribute__((aligned(16))) uint8_t BT[kMaxN][kStride];
-  __shared__ float omega[kMaxQ];
-  __shared__ float red[kThreads / kWave];
+    const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ A,
+    float* __restrict__ acs, float* __restrict__ states, int64_t seqlen, int32_t nheads, int32_t headdim,
+    int32_t dstate, int32_t ngroups, int32_t chunk, int32_t nchunks) {
+  __shared__ __attribute__((aligned(16))) uint8_t xT[kMaxP * kRow];
+  __shared__ __attribute__((aligned(16))) uint8_t BT[kMaxN * kRow];
+  __shared__ __attribute__((aligned(16))) float om[kMaxQ];   // w_j 2^-e 65536
+  __shared__ __attribute__((aligned(16))) float cb[kMaxQ];   // 32896 - 128 om_j
+  __shared__ float red[kWaves];
+  __shared__ float acs_last_s;
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -75,105 +114,105 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
   const int len = int(seqlen - t0 < chunk ? seqlen - t0 : chunk);
   const int Q = chunk, P = headdim, N = dstate;
 
-  // ---- per-token weights w_j = exp(Acs_last - Acs_j) dt_j and their power-of-two scale
-  const float* acs_c = acs + ((int64_t(b) * nheads + h) * nchunks + c) * chunk;
-  const float acs_last = acs_c[len - 1];
-  float w = 0.f;
-  if (tid < Q && tid < len) {
-    const float d = dt[(int64_t(b) * seqlen + t0 + tid) * nheads + h];
-    w = __expf(acs_last - acs_c[tid]) * d;
+  // ---- (a) chunk cumsum of dt A, one token per thread of waves 0..Q/64-1
+  float d = 0.f, v = 0.f;
+  if (tid < len) {
+    d = dt[(int64_t(b) * seqlen + t0 + tid) * nheads + h];
+    v = d * A[h];
   }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float up = __shfl_up(v, o, kWave);
+    if (lane >= o) v += up;
+  }
+  if (lane == kWave - 1) red[wave] = v;
+  __syncthreads();
+  float pre = 0.f;
+  for (int w2 = 0; w2 < wave; ++w2) pre += red[w2];
+  const float acs_t = v + pre;
+  if (tid < Q) acs[((int64_t(b) * nheads + h) * nchunks + c) * chunk + tid] = acs_t;
+  if (tid == len - 1) acs_last_s = acs_t;
+  __syncthreads();
+
+  // ---- LUT_state weights and their power-of-two range
+  float w = 0.f;
+  if (tid < len) w = exp2f((acs_last_s - acs_t) * kLog2e) * d;
   const float wm = wave_max(w);
+  __syncthreads();   // red[] reuse
   if (lane == 0) red[wave] = wm;
   __syncthreads();
   float wmax = red[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / kWave; ++i) wmax = fmaxf(wmax, red[i]);
-  const int e = ceil_log2_pos(wmax);
-  if (tid < Q) omega[tid] = w * exp2i(-e);
-  __syncthreads();
-
-  // ---- limbs of X_scaled / 2^e, written token-contiguous: limbT[k][p][j]
-  // task = (4 tokens) x (4 channels); channels fastest so a wave's loads cover whole x rows
-  const int pq_n = P / 4, jq_n = Q / 4;
-  const int8_t* xb = x + ((int64_t(b) * seqlen + t0) * nheads + h) * P;
-  const int64_t xrow = int64_t(nheads) * P;
-  for (int task = tid; task < pq_n * jq_n; task += kThreads) {
-    const int pq = task % pq_n, jq = task / pq_n;
-    float t[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 4 * jq + r;
-      uint32_t wx = 0;
-      if (j < len) wx = *reinterpret_cast<const uint32_t*>(xb + int64_t(j) * xrow + 4 * pq);
-      const float om = omega[j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t[r][i] = om * sbyte(wx, i);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a1[4], a2[4], a3[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float tt = t[r][i];
-        a1[r] = tt + kMagic;                       // l1 in the low mantissa bits
-        const float l1 = a1[r] - kMagic;
-        const float d1 = (tt - l1) * 128.f;        // exact
-        a2[r] = d1 + kMagic;
-        const float l2 = a2[r] - kMagic;
-        const float d2 = (d1 - l2) * 128.f;        // exact
-        a3[r] = d2 + kMagic;
-      }
-      const int p = 4 * pq + i;
-      *reinterpret_cast<uint32_t*>(&limbT[0][p][4 * jq]) = pack_low_bytes(a1[0], a1[1], a1[2], a1[3]);
-      *reinterpret_cast<uint32_t*>(&limbT[1][p][4 * jq]) = pack_low_bytes(a2[0], a2[1], a2[2], a2[3]);
-      *reinterpret_cast<uint32_t*>(&limbT[2][p][4 * jq]) = pack_low_bytes(a3[0], a3[1], a3[2], a3[3]);
-    }
+  for (int i = 1; i < kWaves; ++i) wmax = fmaxf(wmax, red[i]);
+  const int e = min(max(ceil_log2_pos(wmax), -110), 110);
+  if (tid < Q) {
+    const float o = w * exp2i(16 - e);
+    om[tid] = o;
+    cb[tid] = 32896.f - 128.f * o;
   }
 
-  // ---- B codes of the chunk, token-contiguous: BT[n][j]
-  const int nq_n = N / 4;
-  const int8_t* Bb = Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N;
-  const int64_t brow = int64_t(ngroups) * N;
-  for (int task = tid; task < nq_n * jq_n; task += kThreads) {
-    const int nq = task % nq_n, jq = task / nq_n;
-    uint32_t in[4], out[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int j = 4 * jq + r;
-      in[r] = (j < len) ? *reinterpret_cast<const uint32_t*>(Bb + int64_t(j) * brow + 4 * nq) : 0u;
-    }
-    transpose4x4(in, out);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(&BT[4 * nq + i][4 * jq]) = out[i];
-  }
+  // ---- x and B codes of the chunk, token-contiguous in LDS
+  transpose_into(xT, x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, int64_t(nheads) * P, P, Q, len, tid);
+  transpose_into(BT, Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, int64_t(ngroups) * N, N, Q, len, tid);
   __syncthreads();
 
-  // ---- S[p, n] tiles of 16 x 16: 3 limb accumulators each, K = tokens in steps of 64
+  // ---- S tiles: a work unit is one 16-channel tile x up to four 16-state tiles
   const float post = x_scale[h] * B_scale[g] * exp2i(e);
   float* Sc = states + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N;
-  const int ptn = P / 16, ntn = N / 16;
-  const int row = lane % 16, kg = lane / 16;
-  for (int tile = wave; tile < ptn * ntn; tile += kThreads / kWave) {
-    const int pt = tile % ptn, nt = tile / ptn;
-    v4i acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0}, acc3 = {0, 0, 0, 0};
-    for (int kb = 0; kb < Q; kb += 64) {
-      const int col = kb + 16 * kg;
-      const v4i bop = *reinterpret_cast<const v4i*>(&BT[nt * 16 + row][col]);
-      const v4i a1 = *reinterpret_cast<const v4i*>(&limbT[0][pt * 16 + row][col]);
-      const v4i a2 = *reinterpret_cast<const v4i*>(&limbT[1][pt * 16 + row][col]);
-      const v4i a3 = *reinterpret_cast<const v4i*>(&limbT[2][pt * 16 + row][col]);
-      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bop, acc1, 0, 0, 0);
-      acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a2, bop, acc2, 0, 0, 0);
-      acc3 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a3, bop, acc3, 0, 0, 0);
-    }
-    // D layout of a 16x16 MFMA: lane holds rows 4*(lane/16) + i, column lane % 16
+  const int ptn = P / 16, ntn = N / 16, ngn = (ntn + 3) / 4;
+  const int lcol = lane % 16, kg = lane / 16;
+  for (int unit = wave; unit < ptn * ngn; unit += kWaves) {
+    const int pt = unit % ptn, ng = unit / ptn;
+    const int nt0 = 4 * ng;
+    const int nts = min(4, ntn - nt0);
+    v4i acc[4][3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = pt * 16 + 4 * kg + i;
-      const int n = nt * 16 + row;
-      const float v = (float(acc1[i]) + float(acc2[i]) * (1.f / 128.f) + float(acc3[i]) * (1.f / 16384.f)) * post;
-      Sc[int64_t(p) * N + n] = v;
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
+    const int p = 16 * pt + lcol;
+    for (int kb = 0; kb < Q; kb += 64) {
+      const int j0 = kb + 16 * kg;
+      const v4u xw = *reinterpret_cast<const v4u*>(xT + tpos(p, j0));
+      v4i l1, l2, l3;
+#pragma unroll
+      for (int dw = 0; dw < 4; ++dw) {
+        const float4 o4 = *reinterpret_cast<const float4*>(&om[j0 + 4 * dw]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&cb[j0 + 4 * dw]);
+        const uint32_t u = xw[dw] ^ 0x80808080u;   // biased codes q + 128
+        uint32_t V[4], pl[4];
+        V[0] = uint32_t(int32_t(fmaf(float(u & 0xffu), o4.x, c4.x)));
+        V[1] = uint32_t(int32_t(fmaf(float((u >> 8) & 0xffu), o4.y, c4.y)));
+        V[2] = uint32_t(int32_t(fmaf(float((u >> 16) & 0xffu), o4.z, c4.z)));
+        V[3] = uint32_t(int32_t(fmaf(float(u >> 24), o4.w, c4.w)));
+        transpose4x4(V, pl);
+        l1[dw] = int(pl[2]);
+        l2[dw] = int(pl[1] ^ 0x80808080u);
+        l3[dw] = int(pl[0] ^ 0x80808080u);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < nts) {
+          const v4i bop = *reinterpret_cast<const v4i*>(BT + tpos(16 * (nt0 + t) + lcol, j0));
+          acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, bop, acc[t][0], 0, 0, 0);
+          acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l2, bop, acc[t][1], 0, 0, 0);
+          acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l3, bop, acc[t][2], 0, 0, 0);
+        }
+      }
+    }
+    // D layout of a 16x16 MFMA: lane holds rows 4 (lane/16) + i, column lane % 16
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (t < nts) {
+        const int n = 16 * (nt0 + t) + lcol;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pr = 16 * pt + 4 * kg + i;
+          const float s = float(acc[t][0][i]) + float(acc[t][1][i]) * (1.f / 256.f) +
+                          float(acc[t][2][i]) * (1.f / 65536.f);
+          Sc[int64_t(pr) * N + n] = s * post;
+        }
+      }
     }
   }
 }
@@ -183,7 +222,7 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   const int nblocks = s.batch * s.nchunks * s.nheads;
   hipLaunchKernelGGL(chunk_state_kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
-                     a.dt, a.acs, a.states, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk,
+                     a.dt, a.A, a.acs, a.states, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk,
                      s.nchunks);
   return hipGetLastError();
 }

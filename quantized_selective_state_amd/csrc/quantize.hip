@@ -3,40 +3,81 @@
 // for B and C).  code = clamp(rint(float(v) / s), -127, 127), the quotient
 // correctly rounded, NaN -> 0.
 //
-// HBM-bound elementwise pass: 2 bytes in, 1 byte out per element.  Each thread
-// handles 8 consecutive elements: one 16-byte load and one 8-byte store.
+// HBM-bound elementwise pass: 2 bytes in, 1 byte out per element; each thread handles
+// 8 consecutive elements with one 16-byte load and one 8-byte store.
+//
+// Exactness without a division per element: with r = fl(1/s) (one correctly rounded
+// division per thread) and y = fl(v r), |y - v/s| <= 2^-23 |v/s| and
+// |fl(v/s) - v/s| <= 2^-24 |v/s|, so for |y| < 256 the two are within 1.5 * 2^-15.
+// rint(y) and rint(fl(v/s)) can only differ when a half-integer lies in between, i.e.
+// when y is within 2^-13 of one; those (rare) elements take the exact division.  Beyond
+// |y| >= 256 both saturate.  The int conversion maps NaN to 0 and the integer clamp
+// gives +-127 for infinities.
 #include "ssdq_internal.h"
 
 namespace ssdq {
 namespace {
 
-__device__ __forceinline__ uint32_t code_of(float v, float s) {
-  const float t = __fdiv_rn(v, s);   // IEEE-correct fp32 division, no reciprocal shortcut
+__device__ __forceinline__ uint32_t code_exact(float v, float s) {
+  const float t = __fdiv_rn(v, s);   // IEEE-correct fp32 division
   if (t != t) return 0u;             // NaN
   float r = rintf(t);                // round to nearest, ties to even
   r = fminf(fmaxf(r, -127.f), 127.f);
   return uint32_t(int32_t(r)) & 0xffu;
 }
 
-// inner % 8 == 0: the 8 elements of a thread share one scale.
+// fast code and a flag that is set when the exact division must decide
+__device__ __forceinline__ uint32_t code_fast(float v, float rcp, bool& slow) {
+  const float y = v * rcp;
+  const float k = rintf(y);
+  slow |= (fabsf(y - k) > 0.5f - 1.0f / 8192.f) && (fabsf(y) < 256.f);
+  const float kc = fminf(fmaxf(k, -127.f), 127.f);   // a NaN y is replaced below
+  return (y == y ? uint32_t(int32_t(kc)) : 0u) & 0xffu;
+}
+
+// Division by an invariant divisor d for n < 2^31 (round-up multiplier):
+// l = ceil(log2 d), m = ceil(2^(32+l) / d) - 2^32, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << (32 + l)) + d - 1) / d - (uint64_t(1) << 32);
+  return FastDiv{d, uint32_t(m), l};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
+
+// inner % 8 == 0: the 8 elements of a thread share one scale index.
+// Vector indices i < 2^31 (host-checked), so the scale index uses 32-bit invariant division.
 __global__ void __launch_bounds__(256) quantize_vec8(const v4u* __restrict__ x, v2u* __restrict__ q,
-                                                     const float* __restrict__ scale, int64_t nvec,
-                                                     int32_t nscale, int32_t inner_vec) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    const int k = int((i / inner_vec) % nscale);
+                                                     const float* __restrict__ scale, uint32_t nvec,
+                                                     FastDiv by_inner, FastDiv by_nscale) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    const uint32_t row = fdiv(i, by_inner);
+    const int k = int(row - fdiv(row, by_nscale) * by_nscale.d);
     const float s = scale[k];
+    const float rcp = __fdiv_rn(1.f, s);
     const v4u raw = __builtin_nontemporal_load(x + i);
-    const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
-    uint32_t lo = 0, hi = 0;
+    float v[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const _Float16 h0 = __builtin_bit_cast(_Float16, uint16_t(w[e] & 0xffffu));
-      const _Float16 h1 = __builtin_bit_cast(_Float16, uint16_t(w[e] >> 16));
-      const uint32_t c = code_of(float(h0), s) | (code_of(float(h1), s) << 8);
-      if (e < 2) lo |= c << (16 * e);
-      else hi |= c << (16 * (e - 2));
+      v[2 * e] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] & 0xffffu)));
+      v[2 * e + 1] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] >> 16)));
     }
+    bool slow = false;
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = code_fast(v[e], rcp, slow);
+    if (slow) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[e] = code_exact(v[e], s);
+    }
+    const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
     __builtin_nontemporal_store(v2u{lo, hi}, q + i);
   }
 }
@@ -50,7 +91,7 @@ __global__ void __launch_bounds__(256) quantize_scalar(const uint16_t* __restric
   for (int64_t e = begin + int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
     const int k = int((e / inner) % nscale);
     const _Float16 h = __builtin_bit_cast(_Float16, x[e]);
-    q[e] = int8_t(code_of(float(h), scale[k]));
+    q[e] = int8_t(code_exact(float(h), scale[k]));
   }
 }
 
@@ -68,11 +109,11 @@ hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int
   const int64_t n = rows * int64_t(nscale) * inner;
   if (n == 0) return hipSuccess;
   int64_t done = 0;
-  if (inner % 8 == 0) {
+  if (inner % 8 == 0 && n / 8 < (int64_t(1) << 31)) {
     const int64_t nvec = n / 8;
     hipLaunchKernelGGL(quantize_vec8, dim3(grid_for(nvec, 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const v4u*>(x), reinterpret_cast<v2u*>(q), scale, nvec, nscale,
-                       inner / 8);
+                       reinterpret_cast<const v4u*>(x), reinterpret_cast<v2u*>(q), scale, uint32_t(nvec),
+                       make_fastdiv(uint32_t(inner / 8)), make_fastdiv(uint32_t(nscale)));
     done = nvec * 8;
   }
   if (done < n) {

@@ -38,6 +38,8 @@ ssdq_status check_scan_shape(int32_t batch, int64_t seqlen, int32_t nheads, int3
   s->nchunks = int32_t(nchunks);
   s->acs_bytes = round256(sizeof(float) * size_t(batch) * nheads * nchunks * chunk);
   s->state_bytes = sizeof(float) * size_t(batch) * nchunks * nheads * headdim * dstate;
+  s->hprev_bytes = round256(2 * size_t(batch) * nchunks * nheads * headdim * dstate);
+  s->hscale_bytes = round256(sizeof(float) * size_t(batch) * nchunks * nheads * headdim);
   return SSDQ_SUCCESS;
 }
 
@@ -54,7 +56,7 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
     return SSDQ_ERROR_INVALID_VALUE;
   const ssdq_status st = check_scan_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, s);
   if (st != SSDQ_SUCCESS) return st;
-  if (workspace_bytes < s->acs_bytes + s->state_bytes) return SSDQ_ERROR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < s->total_bytes()) return SSDQ_ERROR_WORKSPACE_TOO_SMALL;
   a->x = x;
   a->x_scale = x_scale;
   a->B = B;
@@ -68,17 +70,19 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   a->y = static_cast<_Float16*>(y);
   a->h_final = h_final;
   a->acs = static_cast<float*>(workspace);
-  a->states = reinterpret_cast<float*>(static_cast<char*>(workspace) + s->acs_bytes);
+  char* ws = static_cast<char*>(workspace);
+  a->states = reinterpret_cast<float*>(ws + s->acs_bytes);
+  a->hprev = reinterpret_cast<_Float16*>(ws + s->acs_bytes + s->state_bytes);
+  a->hscale = reinterpret_cast<float*>(ws + s->acs_bytes + s->state_bytes + s->hprev_bytes);
   return SSDQ_SUCCESS;
 }
 
 ssdq_status run_stage(int32_t stage, const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   switch (stage) {
-    case 0: e = launch_chunk_cumsum(s, a, stream); break;
-    case 1: e = launch_chunk_state(s, a, stream); break;
-    case 2: e = launch_state_passing(s, a, stream); break;
-    case 3: e = launch_chunk_output(s, a, stream); break;
+    case 0: e = launch_chunk_state(s, a, stream); break;
+    case 1: e = launch_state_passing(s, a, stream); break;
+    case 2: e = launch_chunk_output(s, a, stream); break;
     default: return SSDQ_ERROR_INVALID_VALUE;
   }
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
@@ -114,7 +118,7 @@ size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nhe
   ScanShape s;
   // ngroups does not change the workspace; 1 always divides nheads
   if (check_scan_shape(batch, seqlen, nheads, headdim, dstate, 1, chunk, &s) != SSDQ_SUCCESS) return 0;
-  return s.acs_bytes + s.state_bytes;
+  return s.total_bytes();
 }
 
 ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,

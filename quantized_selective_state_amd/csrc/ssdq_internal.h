@@ -25,8 +25,11 @@ struct ScanShape {
   int64_t seqlen;
   int32_t nheads, headdim, dstate, ngroups, chunk;
   int32_t nchunks;
-  size_t acs_bytes;    // Acs region, rounded up to 256 bytes
-  size_t state_bytes;  // chunk-state region
+  size_t acs_bytes;     // Acs region, rounded up to 256 bytes
+  size_t state_bytes;   // chunk-state region (fp32)
+  size_t hprev_bytes;   // fp16 state entering each chunk, rounded up to 256 bytes
+  size_t hscale_bytes;  // its per-row scales, rounded up to 256 bytes
+  size_t total_bytes() const { return acs_bytes + state_bytes + hprev_bytes + hscale_bytes; }
 };
 
 struct ScanArgs {
@@ -42,14 +45,15 @@ struct ScanArgs {
   const float* h0;
   _Float16* y;
   float* h_final;
-  float* acs;     // workspace: (batch, nheads, nchunks, chunk)
-  float* states;  // workspace: (batch, nchunks, nheads, headdim, dstate)
+  float* acs;         // workspace: (batch, nheads, nchunks, chunk)
+  float* states;      // workspace: (batch, nchunks, nheads, headdim, dstate) fp32
+  _Float16* hprev;    // workspace: (batch, nchunks, nheads, headdim, dstate) fp16
+  float* hscale;      // workspace: (batch, nchunks, nheads, headdim)
 };
 
 // Kernel launchers (one per translation unit).  They return hipGetLastError().
 hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
                            int32_t inner, hipStream_t stream);
-hipError_t launch_chunk_cumsum(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream);

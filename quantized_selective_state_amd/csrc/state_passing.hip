@@ -1,64 +1,86 @@
-// Stage 2 of the chunked SSD scan: carry the state across chunks,
+// Stage 1 of the chunked SSD scan: carry the state across chunks,
 //
-//   H_0 = h0 (or 0);   Hprev_c = H_c;   H_{c+1} = exp(Acs[c, last]) H_c + S_c;   h_final = H_nc
+//   H_0 = h0 (or 0);   H_{c+1} = exp(Acs[c, last]) H_c + S_c;   h_final = H_nc
 //
 // i.e. the recurrence h_t = exp(dt_t A) h_{t-1} + ... of the pages applied once per chunk
 // with the chunk's total decay.  Sequential over chunks, parallel over (batch, head, state
-// element); each chunk state S_c is overwritten in place by Hprev_c, the state entering
-// chunk c, which the output stage reads.  HBM-bound: 4 bytes read + 4 written per element
-// per chunk, with the next chunk's load issued before the current one is stored.
+// row).  The state entering chunk c, Hprev_c = H_c, is what the output stage reads; it is
+// written as fp16 with one power-of-two scale per state row p (the row max maps into
+// [2^13, 2^14]), which halves its traffic; the running state and h_final stay fp32.
+//
+// Thread layout: a state row of N floats is handled by G2 = next_pow2(N/4) lanes with
+// 4 consecutive columns each, so the row max is an xor-shuffle reduction inside the wave.
 #include "ssdq_internal.h"
 
 namespace ssdq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerBlock = kThreads * 4;
 
-__global__ void __launch_bounds__(kThreads) state_passing_kernel(float* __restrict__ states,
-                                                                 const float* __restrict__ acs,
-                                                                 const float* h0,  // may alias h_final
-                                                                 float* h_final, int64_t seqlen,
-                                                                 int32_t nheads, int32_t pn, int32_t chunk,
-                                                                 int32_t nchunks, int32_t blocks_per_bh) {
+__global__ void __launch_bounds__(kThreads) state_passing_kernel(
+    const float* __restrict__ states, const float* __restrict__ acs, const float* h0,  // h0 may alias h_final
+    float* h_final, _Float16* __restrict__ hprev, float* __restrict__ hscale, int64_t seqlen, int32_t nheads,
+    int32_t headdim, int32_t dstate, int32_t chunk, int32_t nchunks, int32_t lanes_per_row,
+    int32_t blocks_per_bh) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = bid / blocks_per_bh;
   const int part = bid % blocks_per_bh;
   const int h = bh % nheads;
   const int b = bh / nheads;
-  const int e = part * kPerBlock + threadIdx.x * 4;
-  if (e >= pn) return;
+  const int P = headdim, N = dstate;
+  const int rows_per_block = kThreads / lanes_per_row;
+  const int p = part * rows_per_block + threadIdx.x / lanes_per_row;
+  const int nq = threadIdx.x % lanes_per_row;
+  const bool active = p < P && 4 * nq < N;
+  const int64_t pn = int64_t(P) * N;
+  const int64_t e = int64_t(p) * N + 4 * nq;
 
-  float4 H = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (h0) H = *reinterpret_cast<const float4*>(h0 + int64_t(bh) * pn + e);
+  v4f H = {0.f, 0.f, 0.f, 0.f};
+  if (active && h0) H = *reinterpret_cast<const v4f*>(h0 + int64_t(bh) * pn + e);
   const float* acs_bh = acs + int64_t(bh) * nchunks * chunk;
   const int64_t cstride = int64_t(nheads) * pn;  // between consecutive chunks of one (b, h)
-  float* S = states + (int64_t(b) * nchunks * nheads + h) * pn + e;
+  const int64_t base = (int64_t(b) * nchunks * nheads + h) * pn;
 
-  float4 s_next = *reinterpret_cast<const float4*>(S);
+  v4f s_next = {0.f, 0.f, 0.f, 0.f};
+  if (active) s_next = *reinterpret_cast<const v4f*>(states + base + e);
   for (int c = 0; c < nchunks; ++c) {
-    const float4 s = s_next;
-    if (c + 1 < nchunks) s_next = *reinterpret_cast<const float4*>(S + (c + 1) * cstride);
+    const v4f s = s_next;
+    if (active && c + 1 < nchunks) s_next = *reinterpret_cast<const v4f*>(states + base + (c + 1) * cstride + e);
+    // fp16 copy of H_c with a per-row power-of-two scale
+    float m = fmaxf(fmaxf(fabsf(H[0]), fabsf(H[1])), fmaxf(fabsf(H[2]), fabsf(H[3])));
+    for (int o = lanes_per_row / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    const int ex = min(max(ceil_log2_pos(m) - 14, -120), 120);
+    const float inv = exp2i(-ex);
+    if (active) {
+      const int64_t off = base + c * cstride + e;
+      v4h q;
+      q[0] = _Float16(H[0] * inv);
+      q[1] = _Float16(H[1] * inv);
+      q[2] = _Float16(H[2] * inv);
+      q[3] = _Float16(H[3] * inv);
+      *reinterpret_cast<v4h*>(hprev + off) = q;
+      if (nq == 0) hscale[(off - e) / N + p] = exp2i(ex);
+    }
     const int64_t rem = seqlen - int64_t(c) * chunk;
     const int last = int(rem < chunk ? rem : chunk) - 1;
-    const float decay = __expf(acs_bh[int64_t(c) * chunk + last]);
-    *reinterpret_cast<float4*>(S + c * cstride) = H;
-    H.x = decay * H.x + s.x;
-    H.y = decay * H.y + s.y;
-    H.z = decay * H.z + s.z;
-    H.w = decay * H.w + s.w;
+    const float decay = exp2f(acs_bh[int64_t(c) * chunk + last] * 1.4426950408889634f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) H[i] = decay * H[i] + s[i];
   }
-  if (h_final) *reinterpret_cast<float4*>(h_final + int64_t(bh) * pn + e) = H;
+  if (active && h_final) *reinterpret_cast<v4f*>(h_final + int64_t(bh) * pn + e) = H;
 }
 
 }  // namespace
 
 hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
-  const int pn = s.headdim * s.dstate;
-  const int per_bh = (pn + kPerBlock - 1) / kPerBlock;
+  int lanes = 1;
+  while (lanes < s.dstate / 4) lanes <<= 1;   // next power of two of N/4 (<= 32 for N <= 128)
+  const int rows_per_block = kThreads / lanes;
+  const int per_bh = (s.headdim + rows_per_block - 1) / rows_per_block;
   const int nblocks = s.batch * s.nheads * per_bh;
   hipLaunchKernelGGL(state_passing_kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.states, a.acs, a.h0,
-                     a.h_final, s.seqlen, s.nheads, pn, s.chunk, s.nchunks, per_bh);
+                     a.h_final, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim, s.dstate, s.chunk, s.nchunks,
+                     lanes, per_bh);
   return hipGetLastError();
 }
 

@@ -5,11 +5,12 @@
 //   h[p, n] <- exp(dt A) h[p, n] + (dt xhat[p]) Bhat[n];    y[p] = sum_n Chat[n] h[p, n] + D xhat[p]
 //
 // HBM-bound: every state element is read once and written once (8 bytes) for ~6 flops.
-// One block per (batch, head); thread t owns the 4 consecutive state columns 4 (t % (N/4))
-// of rows t / (N/4) + R k (R = 1024 / N rows per pass), so each pass of the block reads a
-// contiguous 4 KiB stretch with 16-byte loads.  All passes are loaded before any is
-// computed (8 x 16 bytes in flight per thread at N = 128).  y[p] is reduced across the N/4
-// lanes that share row p with xor-shuffles.
+// One block per (batch, head).  Thread t owns the 4 consecutive state columns 4 (t % (N/4))
+// of rows t / (N/4) + R k (R = 1024 / N rows per pass), so each pass of the block covers a
+// contiguous 4 KiB stretch with 16-byte loads.  Every load of the step is issued before any
+// arithmetic (addresses of rows past headdim are clamped, so no load sits behind a branch),
+// and y[p] is reduced across the N/4 lanes of row p with DPP row shifts (an in-row prefix
+// sum; lane 15 of each 16-lane DPP row holds its row total, row_bcast15 joins two rows).
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -21,7 +22,24 @@ __device__ __forceinline__ float sbyte(uint32_t w, int i) {
   return float(int32_t(w << (24 - 8 * i)) >> 24);
 }
 
-template <int N, int MAXP>
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xF, false);
+  return v + __int_as_float(moved);
+}
+
+// Sum over groups of LPR consecutive lanes (16 or 32); the total lands in the group's last lane.
+template <int LPR>
+__device__ __forceinline__ float group_sum_to_last_lane(float v) {
+  v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);   // row_shr:8   -> lane 15 of each row: row total
+  if constexpr (LPR == 32) v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  return v;
+}
+
+template <int N>
 __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
@@ -29,7 +47,7 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads, int32_t headdim, int32_t ngroups) {
   constexpr int kLanesPerRow = N / 4;
   constexpr int kRows = kThreads / kLanesPerRow;   // rows per pass
-  constexpr int kPasses = (MAXP + kRows - 1) / kRows;
+  constexpr int kPasses = 64 / kRows;              // headdim <= 64
   const int bh = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bh % nheads;
   const int b = bh / nheads;
@@ -40,20 +58,23 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
   const int P = headdim;
 
   float* st = state + int64_t(bh) * P * N;
+  const int8_t* xr = x + int64_t(bh) * P;
   v4f hv[kPasses];
+  int xq[kPasses];
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
-    const int p = r0 + kRows * k;
-    if (p < P) hv[k] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(st + int64_t(p) * N + 4 * nq));
+    const int p = min(r0 + kRows * k, P - 1);
+    hv[k] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(st + int64_t(p) * N + 4 * nq));
   }
-
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) xq[k] = xr[min(r0 + kRows * k, P - 1)];
+  const uint32_t bw = *reinterpret_cast<const uint32_t*>(Bm + (int64_t(b) * ngroups + g) * N + 4 * nq);
+  const uint32_t cw = *reinterpret_cast<const uint32_t*>(Cm + (int64_t(b) * ngroups + g) * N + 4 * nq);
   const float d = dt[bh];
   const float a = __expf(d * A[h]);
   const float sx = x_scale[h];
   const float dx = d * sx;
-  const float Dh = D ? D[h] : 0.f;
-  const uint32_t bw = *reinterpret_cast<const uint32_t*>(Bm + (int64_t(b) * ngroups + g) * N + 4 * nq);
-  const uint32_t cw = *reinterpret_cast<const uint32_t*>(Cm + (int64_t(b) * ngroups + g) * N + 4 * nq);
+  const float Dsx = (D ? D[h] : 0.f) * sx;
   const float sB = B_scale[g], sC = C_scale[g];
   float bh4[4], ch4[4];
 #pragma unroll
@@ -61,23 +82,19 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     bh4[i] = sB * sbyte(bw, i);
     ch4[i] = sC * sbyte(cw, i);
   }
-  const int8_t* xr = x + int64_t(bh) * P;
 
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
     const int p = r0 + kRows * k;
-    if (p < P) {   // uniform across the lanes of one row
-      const float xp = float(xr[p]);
-      const float u = dx * xp;
-      v4f v = hv[k];
+    const float xp = float(xq[k]);
+    const float u = dx * xp;
+    v4f v = hv[k];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = a * v[i] + u * bh4[i];
-      __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(st + int64_t(p) * N + 4 * nq));
-      float part = ch4[0] * v[0] + ch4[1] * v[1] + ch4[2] * v[2] + ch4[3] * v[3];
-#pragma unroll
-      for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, kWave);
-      if (nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dh * sx * xp);
-    }
+    for (int i = 0; i < 4; ++i) v[i] = a * v[i] + u * bh4[i];
+    if (p < P) __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(st + int64_t(p) * N + 4 * nq));
+    float part = ch4[0] * v[0] + ch4[1] * v[1] + ch4[2] * v[2] + ch4[3] * v[3];
+    part = group_sum_to_last_lane<kLanesPerRow>(part);
+    if (p < P && nq == kLanesPerRow - 1) y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp);
   }
 }
 
@@ -87,7 +104,7 @@ hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const i
                     _Float16* y, int32_t batch, int32_t nheads, int32_t headdim, int32_t ngroups,
                     hipStream_t stream) {
   const int nblocks = batch * nheads;
-  hipLaunchKernelGGL((state_update_kernel<N, 64>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
+  hipLaunchKernelGGL((state_update_kernel<N>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
                      B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }

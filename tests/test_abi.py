@@ -60,14 +60,17 @@ def test_status_strings(lib):
     assert lib.ssdq_status_string(99) == b"SSDQ_UNKNOWN_STATUS"
 
 
+def _ws(b, L, H, P, N, Q):
+    r = lambda v: (v + 255) // 256 * 256
+    nc = -(-L // Q)
+    return (r(4 * b * H * nc * Q) + 4 * b * nc * H * P * N + r(2 * b * nc * H * P * N) + r(4 * b * nc * H * P))
+
+
 def test_workspace_size(lib):
-    # Acs: 4 * b*H*nc*Q rounded to 256; states: 4 * b*nc*H*P*N
-    b, L, H, P, N, Q = 4, 2048, 64, 64, 128, 256
-    nc = L // Q
-    acs = 4 * b * H * nc * Q
-    assert lib.ssdq_chunk_scan_workspace_size(b, L, H, P, N, Q) == acs + 4 * b * nc * H * P * N
-    # ragged: L = 250, Q = 64 -> 4 chunks
-    assert lib.ssdq_chunk_scan_workspace_size(1, 250, 2, 16, 16, 64) == 2048 + 4 * 4 * 2 * 16 * 16
+    # Acs fp32 + chunk states fp32 + carried state fp16 + row scales fp32, 256-byte aligned regions
+    assert lib.ssdq_chunk_scan_workspace_size(4, 2048, 64, 64, 128, 256) == _ws(4, 2048, 64, 64, 128, 256)
+    assert lib.ssdq_chunk_scan_workspace_size(1, 250, 2, 16, 16, 64) == _ws(1, 250, 2, 16, 16, 64)
+    assert _ws(1, 250, 2, 16, 16, 64) == 2048 + 4 * 4 * 2 * 16 * 16 + 2 * 4 * 2 * 16 * 16 + 512
     assert lib.ssdq_chunk_scan_workspace_size(1, 256, 4, 16, 16, 48) == 0     # unsupported chunk
     assert lib.ssdq_chunk_scan_workspace_size(0, 256, 4, 16, 16, 64) == 0
 
@@ -100,7 +103,7 @@ def _scan(lib, **kw):
     (dict(Q=32), UNSUPPORTED),
     (dict(Q=100), UNSUPPORTED),
     (dict(wsb=100), WS_SMALL),
-    (dict(stage=4, wsb=100), INVALID),
+    (dict(stage=3, wsb=100), INVALID),
     (dict(stage=-1), INVALID),
     (dict(stage=2, wsb=100), WS_SMALL),
 ])

@@ -105,13 +105,14 @@ def test_stage_intermediates():
                            to_dev(inp["h0"]), chunk=256)
     c = oracle_codes(inp)
     views = buf.workspace_views()
-    buf.run_stage(0)
+    buf.run_stage(0)                       # chunk cumsum + chunk states
+    torch.cuda.synchronize()
     acs = views["acs"].cpu().numpy()
-    buf.run_stage(1)
     S = views["states"].cpu().numpy().copy()
-    buf.run_stage(2)
-    Hprev = views["states"].cpu().numpy().copy()
-    buf.run_stage(3)
+    buf.run_stage(1)                       # state passing -> fp16 carried state + row scales
+    torch.cuda.synchronize()
+    Hprev = views["hprev"].float().cpu().numpy() * views["hscale"].cpu().numpy()[..., None]
+    buf.run_stage(2)                       # chunk output
     torch.cuda.synchronize()
     nc = acs.shape[2]
     _, h_ref, bounds = oracle.ssd(c, chunk=256)
@@ -122,9 +123,10 @@ def test_stage_intermediates():
             # fp32 accumulation of up to 256 terms
             assert np.max(np.abs(acs[b, h][valid] - a_ref[valid])) <= 2e-5 * max(1.0, np.max(np.abs(a_ref[valid])))
             S_ref = oracle.chunk_state(c, b, h, 256)
-            # three INT8 limbs (~2^-21) plus fp32 cumsum/exp of the decay
+            # three INT8 limbs (~2^-23 of the chunk max) plus fp32 cumsum/exp of the decay
             assert rel_err(S[b, :, h], S_ref) <= 5e-5
-            assert rel_err(Hprev[b, :, h], bounds[b, :, h]) <= H_TOL
+            # the carried state is stored as fp16 with a power-of-two scale per row
+            assert rel_err(Hprev[b, :, h], bounds[b, :, h]) <= 1e-3
     assert nc == 3
     y_ref, _, _ = oracle.ssd(c)
     assert rel_err(buf.y.float().cpu().numpy(), y_ref) <= Y_TOL
