@@ -55,38 +55,41 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
   out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-// Transposition task -> (channel quad, token quad).  When there are 16k channel quads,
-// a wave's 64 lanes take 16 consecutive channel quads x 4 consecutive token quads, which
-// makes the swizzled LDS writes conflict-free; other shapes use a plain mapping.
-__device__ __forceinline__ void task_coords(int task, int xq_n, int& xq, int& jq) {
-  if ((xq_n & 15) == 0) {
-    const int hi_n = xq_n >> 4;
-    const int rest = task >> 6;
-    xq = (task & 15) + 16 * (rest % hi_n);
-    jq = ((task >> 4) & 3) + 4 * (rest / hi_n);
-  } else {
-    xq = task % xq_n;
-    jq = task / xq_n;
-  }
-}
-
-// Load `rows`-channel codes of the chunk (row stride `stride` bytes in global memory)
-// and store them token-contiguous into the swizzled LDS matrix.
+// Load the int8 codes of the chunk for `channels` (<= kChan) channels (row stride `stride`
+// bytes in global memory) and store them token-contiguous into the swizzled LDS matrix of
+// kChan rows; channels >= `channels` and tokens >= len are zero.  A task is 4 channels x 4
+// tokens; a wave's 64 lanes take 16 consecutive channel quads x 4 consecutive token quads,
+// which makes the swizzled LDS writes conflict-free.  Loads use clamped addresses and a
+// select, so none of them sits behind a branch.
+template <int kChan>
 __device__ __forceinline__ void transpose_into(uint8_t* lds, const int8_t* src, int64_t stride, int channels,
                                                int Q, int len, int tid) {
-  const int xq_n = channels / 4, jq_n = Q / 4;
-  for (int task = tid; task < xq_n * jq_n; task += kThreads) {
-    int xq, jq;
-    task_coords(task, xq_n, xq, jq);
+  constexpr int kXq = kChan / 4;             // channel quads (multiple of 16)
+  constexpr int kHi = kXq / 16;
+  constexpr int kIters = kXq * (kMaxQ / 4) / kThreads;
+  const int ntasks = kXq * (Q / 4);
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int task = tid + it * kThreads;
+    const int rest = task >> 6;
+    const int xq = (task & 15) + 16 * (rest % kHi);
+    const int jq = ((task >> 4) & 3) + 4 * (rest / kHi);
+    const bool chan_ok = 4 * xq < channels;
     uint32_t in[4], out[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = 4 * jq + r;
-      in[r] = (j < len) ? *reinterpret_cast<const uint32_t*>(src + int64_t(j) * stride + 4 * xq) : 0u;
+      const bool ok = chan_ok && j < len && task < ntasks;
+      const int jj = min(j, len - 1);
+      const int xx = chan_ok ? 4 * xq : 0;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(src + int64_t(jj) * stride + xx);
+      in[r] = ok ? v : 0u;
     }
     transpose4x4(in, out);
+    if (task < ntasks) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(lds + tpos(4 * xq + i, 4 * jq)) = out[i];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(lds + tpos(4 * xq + i, 4 * jq)) = out[i];
+    }
   }
 }
 
@@ -152,67 +155,63 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
   }
 
   // ---- x and B codes of the chunk, token-contiguous in LDS
-  transpose_into(xT, x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, int64_t(nheads) * P, P, Q, len, tid);
-  transpose_into(BT, Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, int64_t(ngroups) * N, N, Q, len, tid);
+  transpose_into<kMaxP>(xT, x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, int64_t(nheads) * P, P, Q, len,
+                        tid);
+  transpose_into<kMaxN>(BT, Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, int64_t(ngroups) * N, N, Q,
+                        len, tid);
   __syncthreads();
 
-  // ---- S tiles: a work unit is one 16-channel tile x up to four 16-state tiles
+  // ---- S tiles on the zero-padded 64 x 128 space: wave w owns channel tile w % 4 and the
+  // four 16-state tiles of half w / 4 (one work unit per wave, fully unrolled)
   const float post = x_scale[h] * B_scale[g] * exp2i(e);
   float* Sc = states + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N;
-  const int ptn = P / 16, ntn = N / 16, ngn = (ntn + 3) / 4;
   const int lcol = lane % 16, kg = lane / 16;
-  for (int unit = wave; unit < ptn * ngn; unit += kWaves) {
-    const int pt = unit % ptn, ng = unit / ptn;
-    const int nt0 = 4 * ng;
-    const int nts = min(4, ntn - nt0);
-    v4i acc[4][3];
+  const int pt = wave % 4, nt0 = 4 * (wave / 4);
+  v4i acc[4][3];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
-    const int p = 16 * pt + lcol;
-    for (int kb = 0; kb < Q; kb += 64) {
-      const int j0 = kb + 16 * kg;
-      const v4u xw = *reinterpret_cast<const v4u*>(xT + tpos(p, j0));
-      v4i l1, l2, l3;
+    for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
+  const int p = 16 * pt + lcol;
+  for (int kb = 0; kb < Q; kb += 64) {
+    const int j0 = kb + 16 * kg;
+    const v4u xw = *reinterpret_cast<const v4u*>(xT + tpos(p, j0));
+    v4i bop[4];
 #pragma unroll
-      for (int dw = 0; dw < 4; ++dw) {
-        const float4 o4 = *reinterpret_cast<const float4*>(&om[j0 + 4 * dw]);
-        const float4 c4 = *reinterpret_cast<const float4*>(&cb[j0 + 4 * dw]);
-        const uint32_t u = xw[dw] ^ 0x80808080u;   // biased codes q + 128
-        uint32_t V[4], pl[4];
-        V[0] = uint32_t(int32_t(fmaf(float(u & 0xffu), o4.x, c4.x)));
-        V[1] = uint32_t(int32_t(fmaf(float((u >> 8) & 0xffu), o4.y, c4.y)));
-        V[2] = uint32_t(int32_t(fmaf(float((u >> 16) & 0xffu), o4.z, c4.z)));
-        V[3] = uint32_t(int32_t(fmaf(float(u >> 24), o4.w, c4.w)));
-        transpose4x4(V, pl);
-        l1[dw] = int(pl[2]);
-        l2[dw] = int(pl[1] ^ 0x80808080u);
-        l3[dw] = int(pl[0] ^ 0x80808080u);
-      }
+    for (int t = 0; t < 4; ++t) bop[t] = *reinterpret_cast<const v4i*>(BT + tpos(16 * (nt0 + t) + lcol, j0));
+    v4i l1, l2, l3;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        if (t < nts) {
-          const v4i bop = *reinterpret_cast<const v4i*>(BT + tpos(16 * (nt0 + t) + lcol, j0));
-          acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, bop, acc[t][0], 0, 0, 0);
-          acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l2, bop, acc[t][1], 0, 0, 0);
-          acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l3, bop, acc[t][2], 0, 0, 0);
-        }
-      }
+    for (int dw = 0; dw < 4; ++dw) {
+      const float4 o4 = *reinterpret_cast<const float4*>(&om[j0 + 4 * dw]);
+      const float4 c4 = *reinterpret_cast<const float4*>(&cb[j0 + 4 * dw]);
+      const uint32_t u = xw[dw] ^ 0x80808080u;   // biased codes q + 128
+      uint32_t V[4], pl[4];
+      V[0] = uint32_t(int32_t(fmaf(float(u & 0xffu), o4.x, c4.x)));
+      V[1] = uint32_t(int32_t(fmaf(float((u >> 8) & 0xffu), o4.y, c4.y)));
+      V[2] = uint32_t(int32_t(fmaf(float((u >> 16) & 0xffu), o4.z, c4.z)));
+      V[3] = uint32_t(int32_t(fmaf(float(u >> 24), o4.w, c4.w)));
+      transpose4x4(V, pl);
+      l1[dw] = int(pl[2]);
+      l2[dw] = int(pl[1] ^ 0x80808080u);
+      l3[dw] = int(pl[0] ^ 0x80808080u);
     }
-    // D layout of a 16x16 MFMA: lane holds rows 4 (lane/16) + i, column lane % 16
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (t < nts) {
-        const int n = 16 * (nt0 + t) + lcol;
+      acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, bop[t], acc[t][0], 0, 0, 0);
+      acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l2, bop[t], acc[t][1], 0, 0, 0);
+      acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l3, bop[t], acc[t][2], 0, 0, 0);
+    }
+  }
+  // D layout of a 16x16 MFMA: lane holds rows 4 (lane/16) + i, column lane % 16
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pr = 16 * pt + 4 * kg + i;
-          const float s = float(acc[t][0][i]) + float(acc[t][1][i]) * (1.f / 256.f) +
-                          float(acc[t][2][i]) * (1.f / 65536.f);
-          Sc[int64_t(pr) * N + n] = s * post;
-        }
-      }
+  for (int t = 0; t < 4; ++t) {
+    const int n = 16 * (nt0 + t) + lcol;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pr = 16 * pt + 4 * kg + i;
+      const float sv = float(acc[t][0][i]) + float(acc[t][1][i]) * (1.f / 256.f) +
+                       float(acc[t][2][i]) * (1.f / 65536.f);
+      if (pr < P && n < N) Sc[int64_t(pr) * N + n] = sv * post;
     }
   }
 }
