@@ -53,7 +53,7 @@ def kernel_bytes(b, L, H, P, N, G, Q):
     dt = tok * H * 4
     acs = b * H * nc * Q * 4
     st32 = b * nc * H * P * N * 4          # chunk states, fp32
-    st16 = b * nc * H * P * N * 2 + b * nc * H * P * 4   # fp16 carried state + row scales
+    st16 = b * nc * H * P * N * 2 + b * nc * H * P * 4   # carried state: two int8 limbs + row scales
     hfin = b * H * P * N * 4
     return {
         "quantize_x": 3 * x,

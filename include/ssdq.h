@@ -75,9 +75,10 @@ ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int6
  *   Acs     fp32 (batch, nheads, nchunks, chunk): within-chunk inclusive cumsum of dt * A
  *           (padded past the sequence end with the last value)           -- written by stage 0
  *   S       fp32 (batch, nchunks, nheads, headdim, dstate): chunk states  -- written by stage 0
- *   Hprev   fp16 (batch, nchunks, nheads, headdim, dstate) and
+ *   Hprev   int8 (batch, nchunks, nheads, 2, headdim, dstate) and
  *   Hscale  fp32 (batch, nchunks, nheads, headdim): the state entering each chunk is
- *           Hprev[..., p, n] * Hscale[..., p] (a power of two per state row) -- stage 1 */
+ *           (Hprev[..., 0, p, n] + Hprev[..., 1, p, n] / 256) * Hscale[..., p], two INT8
+ *           limbs with a power-of-two scale per state row           -- written by stage 1 */
 size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                       int32_t dstate, int32_t chunk);
 

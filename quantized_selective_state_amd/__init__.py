@@ -137,7 +137,7 @@ def workspace_layout(batch: int, seqlen: int, nheads: int, headdim: int, dstate:
     return dict(nchunks=nc,
                 acs=(0, "float32", (batch, nheads, nc, chunk)),
                 states=(acs, "float32", (batch, nc, nheads, headdim, dstate)),
-                hprev=(acs + st, "float16", (batch, nc, nheads, headdim, dstate)),
+                hprev=(acs + st, "int8", (batch, nc, nheads, 2, headdim, dstate)),
                 hscale=(acs + st + hp, "float32", (batch, nc, nheads, headdim)))
 
 

@@ -6,7 +6,9 @@
 // (the state-space-duality form: the masked "attention" C B^T inside a chunk plus the
 // carried state read out by C; SSDi8 Figure 1b / Table 5: ChunkBMM C.B^T on INT8).
 //
-// One block (16 waves) per (batch, chunk, head); each wave owns one 16-row output block.
+// A persistent block (8 waves) walks (batch, chunk, head) items; each wave owns two 16-row
+// output blocks of an item (l and 15 - l, for balance), and the next item's global loads are in flight while an item is
+// computed (register prefetch, committed to LDS after the item).
 //  - G^T[j, l] = sum_n q_B[j, n] q_C[l, n] on v_mfma_i32_16x16x64_i8 (exact int32).
 //  - Decay mask, SSDi8-style decoupled from the matrix products: for a 32-token block that
 //    lies entirely before the 16 output rows l0..l0+15, exp(Acs_l - Acs_j) =
@@ -17,31 +19,34 @@
 //  - The masked fragment, rounded to fp16 under a power-of-two guard, feeds the next product
 //    as its B operand straight from registers: the fp16 MFMA's K slots are matched to the
 //    rows the int32 fragment holds, and x^T is read from LDS in the same slot order.
-//  - y^T += x^T M^T and y_off^T = Hprev C^T on v_mfma_f32_16x16x32_f16 (fp32 accumulation):
-//    x codes are exact in fp16; Hprev arrives as fp16 with one power-of-two scale per row.
-//  - LDS matrices use 16-byte-chunk XOR swizzles so that the transposing writes and the
-//    MFMA operand reads are free of bank conflicts.
+//  - y^T += x^T M^T on v_mfma_f32_16x16x32_f16 (fp32 accumulation, x codes exact in fp16).
+//  - y_off^T = Hprev C^T on v_mfma_i32_16x16x64_i8: Hprev arrives as two INT8 limbs with one
+//    power-of-two scale per row and meets the C codes directly (persistent INT8 operands).
+//  - LDS matrices are padded or 16-byte-chunk XOR swizzled so that the MFMA operand reads
+//    are free of bank conflicts with addresses that advance linearly in the hot loop.
 #include "ssdq_internal.h"
 
 namespace ssdq {
 namespace {
 
-constexpr int kThreads = 1024;   // 16 waves: one 16-row output block each at chunk 256
+constexpr int kThreads = 512;    // 8 waves: two 16-row output blocks (l and 15 - l) each at chunk 256
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxQ = 256;
 constexpr int kMaxP = 64;
 constexpr int kMaxN = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// x^T: [p][j] fp16, 512-byte rows, 16-byte chunk c stored at c ^ xswz(p)
-__device__ __forceinline__ int xswz(int p) { return (p & 15) ^ ((p >> 4) & 3); }
-__device__ __forceinline__ int xpos(int p, int j) { return p * kMaxQ + ((((j >> 3) ^ xswz(p)) << 3) | (j & 7)); }
+// x^T: [p][j] fp16, rows padded to 264 halves (528 bytes = 132 banks, i.e. 4 banks apart),
+// so the hot-loop reads of 16 consecutive rows are conflict-free with linear addresses
+constexpr int kXS = kMaxQ + 8;
+__device__ __forceinline__ int xpos(int p, int j) { return p * kXS + j; }
 // B codes: [j][n] int8, 128-byte rows, chunk c stored at c ^ ((j >> 1) & 7)
 __device__ __forceinline__ int bpos(int j, int byte) {
   return j * kMaxN + ((((byte >> 4) ^ ((j >> 1) & 7)) << 4) | (byte & 15));
 }
-// Hprev: [p][n] fp16, 256-byte rows, chunk c stored at c ^ (p & 15)
-__device__ __forceinline__ int hpos(int p, int n) { return p * kMaxN + ((((n >> 3) ^ (p & 15)) << 3) | (n & 7)); }
+// Hprev limbs: two [p][n] int8 planes, 128-byte rows, same swizzle as the B codes
+constexpr int kHPlane = kMaxP * kMaxN;
+__device__ __forceinline__ int hpos(int p, int byte) { return bpos(p, byte); }
 
 __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
   const uint32_t t01lo = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
@@ -65,269 +70,349 @@ __device__ __forceinline__ v4h codes_to_f16(uint32_t biased) {
   return v4h{a[0], a[1], b[0], b[1]};
 }
 
-__global__ void __launch_bounds__(kThreads) chunk_output_kernel(
-    const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
-    const float* __restrict__ B_scale, const int8_t* __restrict__ Cm, const float* __restrict__ C_scale,
-    const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ acs,
-    const _Float16* __restrict__ hprev, const float* __restrict__ hscale, _Float16* __restrict__ y,
-    int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk,
-    int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) _Float16 xT[kMaxP * kMaxQ];
+struct Item {
+  int b, c, h, g, len;
+  int64_t t0;
+};
+
+__device__ __forceinline__ Item item_of(int it, int nheads, int nchunks, int ngroups, int64_t seqlen, int chunk) {
+  Item r;
+  r.h = it % nheads;
+  r.c = (it / nheads) % nchunks;
+  r.b = it / (nheads * nchunks);
+  r.g = r.h / (nheads / ngroups);
+  r.t0 = int64_t(r.c) * chunk;
+  r.len = int(seqlen - r.t0 < chunk ? seqlen - r.t0 : chunk);
+  return r;
+}
+
+// Global data of one work item held in registers between its load and its LDS commit.
+constexpr int kBTasks = kMaxQ * 8 / kThreads;     // 16-byte B pieces per thread
+constexpr int kHTasks = 2 * kMaxP * 8 / kThreads;   // 16-byte Hprev-limb pieces per thread
+constexpr int kXTasks = 16 * (kMaxQ / 4) / kThreads;   // 4x4 x transposition tasks per thread
+struct Prefetch {
+  float acs, dt, hs;
+  v4u bq[kBTasks];
+  v4u hq[kHTasks];
+  uint32_t xw[kXTasks][4];
+};
+
+struct Params {
+  const int8_t* x;
+  const float* x_scale;
+  const int8_t* B;
+  const float* B_scale;
+  const int8_t* C;
+  const float* C_scale;
+  const float* dt;
+  const float* D;
+  const float* acs;
+  const int8_t* hprev;
+  const float* hscale;
+  _Float16* y;
+  int64_t seqlen;
+  int nheads, P, N, ngroups, Q, nchunks, nitems;
+};
+
+// Issue every global load of one item (clamped addresses; nothing waits here).
+__device__ __forceinline__ void prefetch(Prefetch& f, const Item& it, const Params& a, int tid) {
+  const int P = a.P, N = a.N, G = a.ngroups, H = a.nheads;
+  {
+    const int t = min(tid & (kMaxQ - 1), a.Q - 1);
+    f.acs = a.acs[((int64_t(it.b) * H + it.h) * a.nchunks + it.c) * a.Q + t];
+    f.dt = a.dt[(int64_t(it.b) * a.seqlen + it.t0 + min(t, it.len - 1)) * H + it.h];
+    f.hs = a.hscale[((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * P + min(tid & (kMaxP - 1), P - 1)];
+  }
+  const int8_t* Bb = a.B + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N;
+#pragma unroll
+  for (int k = 0; k < kBTasks; ++k) {
+    const int task = tid + k * kThreads;
+    const int j = task >> 3, sg = task & 7;
+    f.bq[k] = *reinterpret_cast<const v4u*>(Bb + int64_t(min(j, it.len - 1)) * G * N + (16 * sg < N ? 16 * sg : 0));
+  }
+  const int8_t* Hb = a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N;
+#pragma unroll
+  for (int k = 0; k < kHTasks; ++k) {
+    const int task = tid + k * kThreads;
+    const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
+    f.hq[k] = *reinterpret_cast<const v4u*>(Hb + int64_t(limb) * P * N + int64_t(min(p, P - 1)) * N +
+                                            (16 * sg < N ? 16 * sg : 0));
+  }
+  const int8_t* xb = a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P;
+#pragma unroll
+  for (int k = 0; k < kXTasks; ++k) {
+    const int task = tid + k * kThreads;
+    const int pq = task & 15, jq = task >> 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      f.xw[k][r] = *reinterpret_cast<const uint32_t*>(xb + int64_t(min(4 * jq + r, it.len - 1)) * H * P +
+                                                      (4 * pq < P ? 4 * pq : 0));
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xT[kMaxP * kXS];
   __shared__ __attribute__((aligned(16))) int8_t Bs[kMaxQ * kMaxN];
-  __shared__ __attribute__((aligned(16))) _Float16 Hh[kMaxP * kMaxN];
+  __shared__ __attribute__((aligned(16))) int8_t Hq[2 * kHPlane];
   __shared__ __attribute__((aligned(16))) float hsc[kMaxP];
   __shared__ __attribute__((aligned(16))) float acs2[kMaxQ];   // Acs * log2(e)
-  __shared__ __attribute__((aligned(16))) float dts[kMaxQ];    // dt * 2^-kM
+  __shared__ __attribute__((aligned(16))) float dts[kMaxQ];    // dt (0 past the sequence end)
   __shared__ __attribute__((aligned(16))) float wl[kWaves][kMaxQ];
   __shared__ float red[kWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = bid % nheads;
-  const int c = (bid / nheads) % nchunks;
-  const int b = bid / (nheads * nchunks);
-  const int g = h / (nheads / ngroups);
-  const int64_t t0 = int64_t(c) * chunk;
-  const int len = int(seqlen - t0 < chunk ? seqlen - t0 : chunk);
-  const int Q = chunk, P = headdim, N = dstate;
+  const int Q = a.Q, P = a.P, N = a.N;
+  const int lcol = lane % 16, kg = lane / 16;
 
-  // All products run on the zero-padded 64-channel x 128-state tile space; the loads below
-  // use clamped addresses and selects (no load sits behind a branch), the stores of padded
-  // rows and columns are skipped.
+  // Persistent block: items blockIdx.x, blockIdx.x + gridDim.x, ...  The global loads of the
+  // next item are issued right after the current item is committed to LDS and complete
+  // while the current item is computed.
+  int it = blockIdx.x;
+  if (it >= a.nitems) return;
+  Prefetch f;
+  prefetch(f, item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a, tid);
 
-  // ---- per-token decay log and dt
-  const float* acs_c = acs + ((int64_t(b) * nheads + h) * nchunks + c) * chunk;
-  float dtv = 0.f;
-  if (tid < kMaxQ) {
-    const int t = min(tid, Q - 1);
-    const float av = acs_c[t];
-    const float dv = dt[(int64_t(b) * seqlen + t0 + min(t, len - 1)) * nheads + h];
-    if (tid < Q) acs2[tid] = av * kLog2e;
-    dtv = (tid < len) ? dv : 0.f;
-  }
-  {
-    const float dm = wave_max(dtv);
-    if (lane == 0) red[wave] = dm;
-  }
-  // ---- B codes: row-major [token][state], 8 chunks of 16 bytes per row
-  {
-    const int8_t* Bb = Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N;
+  for (; it < a.nitems; it += gridDim.x) {
+    const Item cur = item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q);
+    const int len = cur.len;
+
+    // ---- commit the prefetched item to LDS (zero padding past the sequence end, P and N)
+    if (tid < kMaxQ) {
+      if (tid < Q) acs2[tid] = f.acs * kLog2e;
+      dts[tid] = tid < len ? f.dt : 0.f;
+    }
+    {
+      const float dm = wave_max(tid < kMaxQ && tid < len ? f.dt : 0.f);
+      if (lane == 0) red[wave] = dm;
+    }
+    if (tid < kMaxP) hsc[tid] = tid < P ? f.hs : 0.f;
 #pragma unroll
-    for (int it = 0; it < kMaxQ * 8 / kThreads; ++it) {
-      const int task = tid + it * kThreads;
+    for (int k = 0; k < kBTasks; ++k) {
+      const int task = tid + k * kThreads;
       const int j = task >> 3, sg = task & 7;
-      const bool ok = j < len && 16 * sg < N;
-      const v4u v = *reinterpret_cast<const v4u*>(Bb + int64_t(min(j, len - 1)) * ngroups * N +
-                                                  (16 * sg < N ? 16 * sg : 0));
       const v4u z = {0u, 0u, 0u, 0u};
-      if (j < Q) *reinterpret_cast<v4u*>(Bs + bpos(j, 16 * sg)) = ok ? v : z;
+      if (j < Q) *reinterpret_cast<v4u*>(Bs + bpos(j, 16 * sg)) = (j < len && 16 * sg < N) ? f.bq[k] : z;
     }
-  }
-  // ---- Hprev (fp16) and its per-row scales
-  {
-    const _Float16* Hb = hprev + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N;
 #pragma unroll
-    for (int it = 0; it < kMaxP * 16 / kThreads; ++it) {
-      const int task = tid + it * kThreads;
-      const int p = task >> 4, sg = task & 15;
-      const bool ok = p < P && 8 * sg < N;
-      const v4u v = *reinterpret_cast<const v4u*>(Hb + int64_t(min(p, P - 1)) * N + (8 * sg < N ? 8 * sg : 0));
+    for (int k = 0; k < kHTasks; ++k) {
+      const int task = tid + k * kThreads;
+      const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
       const v4u z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<v4u*>(Hh + hpos(p, 8 * sg)) = ok ? v : z;
+      *reinterpret_cast<v4u*>(Hq + limb * kHPlane + hpos(p, 16 * sg)) = (p < P && 16 * sg < N) ? f.hq[k] : z;
     }
-    if (tid < kMaxP) {
-      const float sv = hscale[((int64_t(b) * nchunks + c) * nheads + h) * P + min(tid, P - 1)];
-      hsc[tid] = tid < P ? sv : 0.f;
-    }
-  }
-  // ---- x codes as exact fp16, token-contiguous: xT[p][j]
-  {
-    const int8_t* xb = x + ((int64_t(b) * seqlen + t0) * nheads + h) * P;
-    const int ntasks = 16 * (Q / 4);
 #pragma unroll
-    for (int it = 0; it < 16 * (kMaxQ / 4) / kThreads; ++it) {
-      const int task = tid + it * kThreads;
+    for (int k = 0; k < kXTasks; ++k) {
+      const int task = tid + k * kThreads;
       const int pq = task & 15, jq = task >> 4;
       const bool chan_ok = 4 * pq < P;
       uint32_t in[4], out[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 4 * jq + r;
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(xb + int64_t(min(j, len - 1)) * nheads * P +
-                                                              (chan_ok ? 4 * pq : 0));
-        in[r] = ((chan_ok && j < len) ? v : 0u) ^ 0x80808080u;
-      }
+      for (int r = 0; r < 4; ++r) in[r] = ((chan_ok && 4 * jq + r < len) ? f.xw[k][r] : 0u) ^ 0x80808080u;
       transpose4x4(in, out);
-      if (task < ntasks) {
+      if (4 * jq < Q) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + xpos(4 * pq + i, 4 * jq)) = codes_to_f16(out[i]);
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  float dtmax = red[0];
+    // ---- loads the current item still needs, for both of this wave's row blocks.  They are
+    // issued and consumed before the next item's prefetch: vmcnt retires in order, so any
+    // wait on a load issued after the prefetch would also wait for the prefetch.
+    const int nlb = Q / 16;
+    v4i cqs[2][2];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) dtmax = fmaxf(dtmax, red[i]);
-  // |M'| <= N 127^2 dtmax 2^-kM <= 2^15; clamped so that 2^kM and 2^-kM are exact
-  const int kM = min(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, -120), 120);
-  if (tid < kMaxQ) dts[tid] = dtv * exp2i(-kM);
-  __syncthreads();
-
-  // ---- one 16-row output block per wave
-  const int l0 = 16 * wave;
-  if (l0 >= Q) return;
-  const int lcol = lane % 16, kg = lane / 16;
-  const float sx = x_scale[h], sB = B_scale[g], sC = C_scale[g];
-  const float Dh = D ? D[h] : 0.f;
-  const float s_in = sx * sC * sB * exp2i(kM);
-  const int l = l0 + lcol;
-  const bool lvalid = l < len;
-  const int8_t* Crow = Cm + ((int64_t(b) * seqlen + t0 + min(l, len - 1)) * ngroups + g) * N;
-  const int jdiag = l0 & ~31;          // the 32-token block that holds the diagonal
-  const float a_l = acs2[l];
-  const float a_0 = acs2[l0];
-  float* wlw = wl[wave];
-
-  // weights of the blocks before the diagonal, relative to row l0
-  for (int j = lane; j < jdiag; j += kWave) wlw[j] = exp2f(a_0 - acs2[j]) * dts[j];
-  __builtin_amdgcn_wave_barrier();
-  const float u_l = exp2f(a_l - a_0);
-
-  // C row of this lane's output token: int8 K-slices for C.B^T, fp16 K-slices for Hprev.C^T
-  v4i cq[2];
-  v8h cop[4];
+    for (int pass = 0; pass < 2; ++pass) {
+      const int lbp = pass == 0 ? wave : 2 * kWaves - 1 - wave;
+      const int l = 16 * lbp + lcol;
+      const bool lvalid = lbp < nlb && l < len;
+      const int8_t* Crow =
+          a.C + ((int64_t(cur.b) * a.seqlen + cur.t0 + min(l, len - 1)) * a.ngroups + cur.g) * N;
+      v4i cv[2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int off = 64 * s + 16 * kg;
-    const v4i v = *reinterpret_cast<const v4i*>(Crow + (off < N ? off : 0));
-    cq[s] = (lvalid && off < N) ? v : v4i{0, 0, 0, 0};
-  }
+      for (int s2 = 0; s2 < 2; ++s2) cv[s2] = *reinterpret_cast<const v4i*>(Crow + min(64 * s2 + 16 * kg, N - 16));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int off = 32 * k + 8 * kg;
-    const v2u v = *reinterpret_cast<const v2u*>(Crow + (off < N ? off : 0));
-    const v2u raw = (lvalid && off < N) ? v : v2u{0u, 0u};
-    const v4h c0 = codes_to_f16(raw[0] ^ 0x80808080u);
-    const v4h c1 = codes_to_f16(raw[1] ^ 0x80808080u);
-    cop[k] = v8h{c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-  }
-
-  v4f yf[4], yd[4], yo[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    yf[pt] = v4f{0.f, 0.f, 0.f, 0.f};
-    yd[pt] = v4f{0.f, 0.f, 0.f, 0.f};
-    yo[pt] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // carried state read out by C: y_off^T[p][l] = sum_n Hprev[p][n] q_C[l][n]
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const v8h hop = *reinterpret_cast<const v8h*>(Hh + hpos(16 * pt + lcol, 32 * k + 8 * kg));
-      yo[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hop, cop[k], yo[pt], 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2)
+        cqs[pass][s2] = (lvalid && 64 * s2 + 16 * kg < N) ? cv[s2] : v4i{0, 0, 0, 0};
     }
-  }
+    const int hu = __builtin_amdgcn_readfirstlane(cur.h);
+    const int gu = __builtin_amdgcn_readfirstlane(cur.g);
+    const float sx = a.x_scale[hu], sB = a.B_scale[gu], sC = a.C_scale[gu];
+    const float Dh = a.D ? a.D[hu] : 0.f;
+    __builtin_amdgcn_sched_barrier(0);
 
-  // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized decay
-  for (int jb = 0; jb < jdiag; jb += 32) {
-    v4i gm[2];
-    float4 w4[2];
+    // unconditional (the last item re-reads a valid item): a prefetch behind a branch would
+    // make the wait counts after it conservative
+    const int nx = min(it + int(gridDim.x), a.nitems - 1);
+    prefetch(f, item_of(nx, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a, tid);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float dtmax = red[0];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int js = jb + 16 * sb;
-      const v4i b0 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 16 * kg));
-      const v4i b1 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 64 + 16 * kg));
-      w4[sb] = *reinterpret_cast<const float4*>(&wlw[js + 4 * kg]);
-      gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
-      gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
-    }
-    v8h xop[4];
+    for (int i = 1; i < kWaves; ++i) dtmax = fmaxf(dtmax, red[i]);
+    // |M'| <= N 127^2 dtmax 2^-kM <= 2^15; clamped so that 2^kM and 2^-kM are exact
+    const int kM = min(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, -120), 120);
+    const float s_in = sx * sC * sB * exp2i(kM);
+    const float fkM = float(kM);
+
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+    const int lb = pass == 0 ? wave : 2 * kWaves - 1 - wave;
+    if (lb >= nlb || (pass == 1 && nlb <= kWaves)) continue;
+    const int l0 = 16 * lb;
+    const int l = l0 + lcol;
+    const bool lvalid = l < len;
+    const v4i cq[2] = {pass == 0 ? cqs[0][0] : cqs[1][0], pass == 0 ? cqs[0][1] : cqs[1][1]};
+    {
+      const int jdiag = l0 & ~31;          // the 32-token block that holds the diagonal
+      const float a_l = acs2[l];
+      const float a_0 = acs2[l0];
+      float* wlw = wl[wave];
+
+      // weights of the blocks before the diagonal, relative to row l0, times 2^-kM
+      for (int j = lane; j < jdiag; j += kWave) wlw[j] = exp2f(a_0 - acs2[j] - fkM) * dts[j];
+      __builtin_amdgcn_wave_barrier();
+      const float u_l = exp2f(a_l - a_0);
+
+      v4f yf[4], yd[4];
+      v4i yo1[4], yo2[4];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const int p = 16 * pt + lcol;
-      const v4h lo = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 4 * kg));
-      const v4h hi = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 16 + 4 * kg));
-      xop[pt] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    v8h mop;
+      for (int pt = 0; pt < 4; ++pt) {
+        yf[pt] = v4f{0.f, 0.f, 0.f, 0.f};
+        yd[pt] = v4f{0.f, 0.f, 0.f, 0.f};
+        yo1[pt] = v4i{0, 0, 0, 0};
+        yo2[pt] = v4i{0, 0, 0, 0};
+      }
+
+      // carried state read out by C: y_off^T[p][l] = sum_n Hprev[p][n] q_C[l][n], both limbs
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      mop[4 * sb + 0] = _Float16(float(gm[sb][0]) * w4[sb].x);
-      mop[4 * sb + 1] = _Float16(float(gm[sb][1]) * w4[sb].y);
-      mop[4 * sb + 2] = _Float16(float(gm[sb][2]) * w4[sb].z);
-      mop[4 * sb + 3] = _Float16(float(gm[sb][3]) * w4[sb].w);
-    }
+      for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) yf[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[pt], mop, yf[pt], 0, 0, 0);
-  }
-  // the block holding the diagonal: exact per-element decay and the causal mask
-  {
-    const int jb = jdiag;
-    v4i gm[2];
+        for (int pt = 0; pt < 4; ++pt) {
+          const int hp = hpos(16 * pt + lcol, 64 * s2 + 16 * kg);
+          const v4i h1 = *reinterpret_cast<const v4i*>(Hq + hp);
+          const v4i h2 = *reinterpret_cast<const v4i*>(Hq + kHPlane + hp);
+          yo1[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h1, cq[s2], yo1[pt], 0, 0, 0);
+          yo2[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h2, cq[s2], yo2[pt], 0, 0, 0);
+        }
+      }
+
+      // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized
+      // decay.  For rows js + lcol with js a multiple of 16 the B swizzle term depends on lcol
+      // only, so every hot-loop address is a per-lane base plus a multiple of the step.
+      const int8_t* bs_lane = Bs + bpos(lcol, 16 * kg);                    // + js * 128
+      const int bs_half = bpos(lcol, 64 + 16 * kg) - bpos(lcol, 16 * kg);   // second K half
+      const _Float16* xt_lane = xT + xpos(lcol, 4 * kg);                    // + 16 pt rows, + jb
+      const float* wl_lane = wlw + 4 * kg;
+      for (int jb = 0; jb < jdiag; jb += 32) {
+        v4i gm[2];
+        float4 w4[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int js = min(jb + 16 * sb, Q - 16);
-      const v4i b0 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 16 * kg));
-      const v4i b1 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 64 + 16 * kg));
-      gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
-      gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
-    }
-    v8h mop;
+        for (int sb = 0; sb < 2; ++sb) {
+          const int js = jb + 16 * sb;
+          const int8_t* bp = bs_lane + js * kMaxN;
+          const v4i b0 = *reinterpret_cast<const v4i*>(bp);
+          const v4i b1 = *reinterpret_cast<const v4i*>(bp + bs_half);
+          w4[sb] = *reinterpret_cast<const float4*>(wl_lane + js);
+          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
+        }
+        v8h xop[4];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      const int jq = min(jb + 16 * sb, Q - 16) + 4 * kg;
-      const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int pt = 0; pt < 4; ++pt) {
+          const _Float16* xp = xt_lane + 16 * pt * kXS + jb;
+          const v4h lo = *reinterpret_cast<const v4h*>(xp);
+          const v4h hi = *reinterpret_cast<const v4h*>(xp + 16);
+          xop[pt] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        v8h mop;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = jb + 16 * sb + 4 * kg + i;     // > l (masked) whenever the clamp applied
-        const float m = float(gm[sb][i]) * exp2f(fminf(a_l - av[i], 0.f)) * dv[i];
-        mop[4 * sb + i] = _Float16(j <= l ? m : 0.f);
+        for (int sb = 0; sb < 2; ++sb) {
+          mop[4 * sb + 0] = _Float16(float(gm[sb][0]) * w4[sb].x);
+          mop[4 * sb + 1] = _Float16(float(gm[sb][1]) * w4[sb].y);
+          mop[4 * sb + 2] = _Float16(float(gm[sb][2]) * w4[sb].z);
+          mop[4 * sb + 3] = _Float16(float(gm[sb][3]) * w4[sb].w);
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          yf[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[pt], mop, yf[pt], 0, 0, 0);
+      }
+      // the block holding the diagonal: exact per-element decay and the causal mask
+      {
+        const int jb = jdiag;
+        v4i gm[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int js = min(jb + 16 * sb, Q - 16);
+          const v4i b0 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 16 * kg));
+          const v4i b1 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 64 + 16 * kg));
+          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
+        }
+        v8h mop;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int jq = min(jb + 16 * sb, Q - 16) + 4 * kg;
+          const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = jb + 16 * sb + 4 * kg + i;     // > l (masked) whenever the clamp applied
+            const float m = float(gm[sb][i]) * exp2f(fminf(a_l - av[i], 0.f) - fkM) * dv[i];
+            mop[4 * sb + i] = _Float16(j <= l ? m : 0.f);
+          }
+        }
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const int p = 16 * pt + lcol;
+          const int j1 = min(jb + 16, Q - 16);
+          const v4h lo = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 4 * kg));
+          const v4h hi = *reinterpret_cast<const v4h*>(xT + xpos(p, j1 + 4 * kg));
+          const v8h xop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          yd[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yd[pt], 0, 0, 0);
+        }
+      }
+
+      // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
+      const float s_off = exp2f(a_l) * sC;
+      _Float16* yrow = a.y + ((int64_t(cur.b) * a.seqlen + cur.t0 + min(l, len - 1)) * a.nheads + cur.h) * P;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
+        const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
+        v4h out;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = 16 * pt + 4 * kg + i;
+          const float xd = float(xT[xpos(p, l)]) * sx * Dh;
+          const float yo = float(yo1[pt][i]) + float(yo2[pt][i]) * (1.f / 256.f);
+          out[i] = _Float16((u_l * yf[pt][i] + yd[pt][i]) * s_in + yo * (s_off * hv[i]) + xd);
+        }
+        if (lvalid && 16 * pt + 4 * kg < P) *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg) = out;
       }
     }
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const int p = 16 * pt + lcol;
-      const int j1 = min(jb + 16, Q - 16);
-      const v4h lo = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 4 * kg));
-      const v4h hi = *reinterpret_cast<const v4h*>(xT + xpos(p, j1 + 4 * kg));
-      const v8h xop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      yd[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yd[pt], 0, 0, 0);
     }
-  }
-
-  // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
-  const float s_off = exp2f(a_l) * sC;
-  _Float16* yrow = y + ((int64_t(b) * seqlen + t0 + l) * nheads + h) * P;
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
-    const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
-    v4h out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = 16 * pt + 4 * kg + i;
-      const float xd = float(xT[xpos(p, l)]) * sx * Dh;
-      out[i] = _Float16((u_l * yf[pt][i] + yd[pt][i]) * s_in + yo[pt][i] * (s_off * hv[i]) + xd);
-    }
-    if (lvalid && 16 * pt + 4 * kg < P) *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg) = out;
+    __syncthreads();   // LDS is rewritten by the next item's commit
   }
 }
 
 }  // namespace
 
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
-  const int nblocks = s.batch * s.nchunks * s.nheads;
-  hipLaunchKernelGGL(chunk_output_kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
-                     a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.y, s.seqlen, s.nheads, s.headdim,
-                     s.dstate, s.ngroups, s.chunk, s.nchunks);
+  Params p{a.x, a.x_scale, a.B, a.B_scale, a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.y,
+           s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.nchunks,
+           s.batch * s.nchunks * s.nheads};
+  // one persistent block per CU (the LDS footprint allows one resident block)
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess)
+    cus = 256;
+  const int nblocks = p.nitems < cus ? p.nitems : cus;
+  hipLaunchKernelGGL(chunk_output_kernel, dim3(nblocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   a->acs = static_cast<float*>(workspace);
   char* ws = static_cast<char*>(workspace);
   a->states = reinterpret_cast<float*>(ws + s->acs_bytes);
-  a->hprev = reinterpret_cast<_Float16*>(ws + s->acs_bytes + s->state_bytes);
+  a->hprev = reinterpret_cast<int8_t*>(ws + s->acs_bytes + s->state_bytes);
   a->hscale = reinterpret_cast<float*>(ws + s->acs_bytes + s->state_bytes + s->hprev_bytes);
   return SSDQ_SUCCESS;
 }

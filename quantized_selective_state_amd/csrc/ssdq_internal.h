@@ -27,7 +27,7 @@ struct ScanShape {
   int32_t nchunks;
   size_t acs_bytes;     // Acs region, rounded up to 256 bytes
   size_t state_bytes;   // chunk-state region (fp32)
-  size_t hprev_bytes;   // fp16 state entering each chunk, rounded up to 256 bytes
+  size_t hprev_bytes;   // state entering each chunk as two int8 limbs, rounded up to 256 bytes
   size_t hscale_bytes;  // its per-row scales, rounded up to 256 bytes
   size_t total_bytes() const { return acs_bytes + state_bytes + hprev_bytes + hscale_bytes; }
 };
@@ -47,7 +47,7 @@ struct ScanArgs {
   float* h_final;
   float* acs;         // workspace: (batch, nheads, nchunks, chunk)
   float* states;      // workspace: (batch, nchunks, nheads, headdim, dstate) fp32
-  _Float16* hprev;    // workspace: (batch, nchunks, nheads, headdim, dstate) fp16
+  int8_t* hprev;      // workspace: (batch, nchunks, nheads, 2, headdim, dstate) int8 limbs
   float* hscale;      // workspace: (batch, nchunks, nheads, headdim)
 };
 

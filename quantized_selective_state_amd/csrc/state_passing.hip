@@ -5,8 +5,11 @@
 // i.e. the recurrence h_t = exp(dt_t A) h_{t-1} + ... of the pages applied once per chunk
 // with the chunk's total decay.  Sequential over chunks, parallel over (batch, head, state
 // row).  The state entering chunk c, Hprev_c = H_c, is what the output stage reads; it is
-// written as fp16 with one power-of-two scale per state row p (the row max maps into
-// [2^13, 2^14]), which halves its traffic; the running state and h_final stay fp32.
+// written as two INT8 limbs per element with one power-of-two scale 2^e per state row p
+// (2 bytes per element, half of fp32), so that the output stage can read it out with C on
+// the INT8 matrix cores: with t = H 2^-e (|t| <= 127) and V = trunc(256 t + 128),
+// V = 256 l1 + (l2 + 128), so H = 2^e (l1 + l2 / 256) to within 2^e / 256.  The running
+// state and h_final stay fp32.
 //
 // Thread layout: a state row of N floats is handled by G2 = next_pow2(N/4) lanes with
 // 4 consecutive columns each, so the row max is an xor-shuffle reduction inside the wave.
@@ -19,7 +22,7 @@ constexpr int kThreads = 256;
 
 __global__ void __launch_bounds__(kThreads) state_passing_kernel(
     const float* __restrict__ states, const float* __restrict__ acs, const float* h0,  // h0 may alias h_final
-    float* h_final, _Float16* __restrict__ hprev, float* __restrict__ hscale, int64_t seqlen, int32_t nheads,
+    float* h_final, int8_t* __restrict__ hprev, float* __restrict__ hscale, int64_t seqlen, int32_t nheads,
     int32_t headdim, int32_t dstate, int32_t chunk, int32_t nchunks, int32_t lanes_per_row,
     int32_t blocks_per_bh) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
@@ -46,20 +49,24 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
   for (int c = 0; c < nchunks; ++c) {
     const v4f s = s_next;
     if (active && c + 1 < nchunks) s_next = *reinterpret_cast<const v4f*>(states + base + (c + 1) * cstride + e);
-    // fp16 copy of H_c with a per-row power-of-two scale
+    // two INT8 limbs of H_c with a per-row power-of-two scale 2^ex >= row max / 127
     float m = fmaxf(fmaxf(fabsf(H[0]), fabsf(H[1])), fmaxf(fabsf(H[2]), fabsf(H[3])));
     for (int o = lanes_per_row / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    const int ex = min(max(ceil_log2_pos(m) - 14, -120), 120);
-    const float inv = exp2i(-ex);
+    const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
+    const float inv = exp2i(8 - ex);   // 256 / 2^ex
     if (active) {
-      const int64_t off = base + c * cstride + e;
-      v4h q;
-      q[0] = _Float16(H[0] * inv);
-      q[1] = _Float16(H[1] * inv);
-      q[2] = _Float16(H[2] * inv);
-      q[3] = _Float16(H[3] * inv);
-      *reinterpret_cast<v4h*>(hprev + off) = q;
-      if (nq == 0) hscale[(off - e) / N + p] = exp2i(ex);
+      uint32_t q1 = 0, q2 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t V = int32_t(fmaf(H[i], inv, 128.f));   // 256 t + 128, |t| <= 127
+        q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
+        q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
+      }
+      // per (b, c, h): limb-1 plane [P][N] then limb-2 plane [P][N]
+      int8_t* dst = hprev + 2 * (base + c * cstride) + e;
+      *reinterpret_cast<uint32_t*>(dst) = q1;
+      *reinterpret_cast<uint32_t*>(dst + pn) = q2;
+      if (nq == 0) hscale[(base + c * cstride) / N + p] = exp2i(ex);
     }
     const int64_t rem = seqlen - int64_t(c) * chunk;
     const int last = int(rem < chunk ? rem : chunk) - 1;

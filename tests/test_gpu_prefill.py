@@ -109,9 +109,10 @@ def test_stage_intermediates():
     torch.cuda.synchronize()
     acs = views["acs"].cpu().numpy()
     S = views["states"].cpu().numpy().copy()
-    buf.run_stage(1)                       # state passing -> fp16 carried state + row scales
+    buf.run_stage(1)                       # state passing -> carried state as two int8 limbs + row scales
     torch.cuda.synchronize()
-    Hprev = views["hprev"].float().cpu().numpy() * views["hscale"].cpu().numpy()[..., None]
+    limbs = views["hprev"].cpu().numpy().astype(np.float64)
+    Hprev = (limbs[:, :, :, 0] + limbs[:, :, :, 1] / 256.0) * views["hscale"].cpu().numpy()[..., None]
     buf.run_stage(2)                       # chunk output
     torch.cuda.synchronize()
     nc = acs.shape[2]
@@ -125,8 +126,8 @@ def test_stage_intermediates():
             S_ref = oracle.chunk_state(c, b, h, 256)
             # three INT8 limbs (~2^-23 of the chunk max) plus fp32 cumsum/exp of the decay
             assert rel_err(S[b, :, h], S_ref) <= 5e-5
-            # the carried state is stored as fp16 with a power-of-two scale per row
-            assert rel_err(Hprev[b, :, h], bounds[b, :, h]) <= 1e-3
+            # the carried state is stored as two int8 limbs (~2^-15 of each row max)
+            assert rel_err(Hprev[b, :, h], bounds[b, :, h]) <= 1e-4
     assert nc == 3
     y_ref, _, _ = oracle.ssd(c)
     assert rel_err(buf.y.float().cpu().numpy(), y_ref) <= Y_TOL
