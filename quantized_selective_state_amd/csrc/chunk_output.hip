@@ -87,8 +87,8 @@ __device__ __forceinline__ Item item_of(int it, int nheads, int nchunks, int ngr
 }
 
 // Global data of one work item held in registers between its load and its LDS commit.
-constexpr int kBTasks = kMaxQ * 8 / kThreads;     // 16-byte B pieces per thread
-constexpr int kHTasks = 2 * kMaxP * 8 / kThreads;   // 16-byte Hprev-limb pieces per thread
+constexpr int kBTasks = kMaxQ * 8 / kThreads;          // 16-byte B pieces per thread
+constexpr int kHTasks = 2 * kMaxP * 8 / kThreads;      // 16-byte Hprev-limb pieces per thread
 constexpr int kXTasks = 16 * (kMaxQ / 4) / kThreads;   // 4x4 x transposition tasks per thread
 struct Prefetch {
   float acs, dt, hs;
@@ -114,39 +114,70 @@ struct Params {
   int nheads, P, N, ngroups, Q, nchunks, nitems;
 };
 
-// Issue every global load of one item (clamped addresses; nothing waits here).
-__device__ __forceinline__ void prefetch(Prefetch& f, const Item& it, const Params& a, int tid) {
+// Per-lane offsets that do not depend on the work item (computed once per block).
+struct LaneConst {
+  uint32_t b_off[kBTasks];      // byte offset of the B piece in a token-major chunk (row j * G*N)
+  int b_row[kBTasks];           // its token row j
+  int b_lds[kBTasks];
+  bool b_colok[kBTasks];
+  uint32_t h_off[kHTasks];      // byte offset of the Hprev-limb piece in its (b, c, h) block
+  int h_lds[kHTasks];
+  bool h_ok[kHTasks];
+  uint32_t x_off[kXTasks];      // byte offset of the first row of the x task (row 4 jq)
+  int x_jq[kXTasks];
+  int x_lds[kXTasks];
+  bool x_chan_ok;
+};
+
+// Uniform per-item base pointers.
+struct ItemBase {
+  const float* acs;
+  const float* dt;
+  const float* hs;
+  const int8_t* B;
+  const int8_t* H;
+  const int8_t* x;
+  int len;
+};
+
+__device__ __forceinline__ ItemBase item_base(const Item& it, const Params& a) {
   const int P = a.P, N = a.N, G = a.ngroups, H = a.nheads;
-  {
-    const int t = min(tid & (kMaxQ - 1), a.Q - 1);
-    f.acs = a.acs[((int64_t(it.b) * H + it.h) * a.nchunks + it.c) * a.Q + t];
-    f.dt = a.dt[(int64_t(it.b) * a.seqlen + it.t0 + min(t, it.len - 1)) * H + it.h];
-    f.hs = a.hscale[((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * P + min(tid & (kMaxP - 1), P - 1)];
-  }
-  const int8_t* Bb = a.B + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N;
+  ItemBase r;
+  r.acs = a.acs + ((int64_t(it.b) * H + it.h) * a.nchunks + it.c) * a.Q;
+  r.dt = a.dt + (int64_t(it.b) * a.seqlen + it.t0) * H + it.h;
+  r.hs = a.hscale + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * P;
+  r.B = a.B + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N;
+  r.H = a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N;
+  r.x = a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P;
+  r.len = it.len;
+  return r;
+}
+
+// Issue every global load of one item (clamped addresses; nothing waits here).
+__device__ __forceinline__ void prefetch(Prefetch& f, const ItemBase& ib, const LaneConst& lc, const Params& a,
+                                         int tid) {
+  const int t = min(tid & (kMaxQ - 1), a.Q - 1);
+  f.acs = ib.acs[t];
+  f.dt = ib.dt[int64_t(min(t, ib.len - 1)) * a.nheads];
+  f.hs = ib.hs[min(tid & (kMaxP - 1), a.P - 1)];
+  const uint32_t brow = uint32_t(a.ngroups) * a.N;
+  const uint32_t bmax = uint32_t(ib.len - 1) * brow;
 #pragma unroll
   for (int k = 0; k < kBTasks; ++k) {
-    const int task = tid + k * kThreads;
-    const int j = task >> 3, sg = task & 7;
-    f.bq[k] = *reinterpret_cast<const v4u*>(Bb + int64_t(min(j, it.len - 1)) * G * N + (16 * sg < N ? 16 * sg : 0));
+    const uint32_t row = min(uint32_t(lc.b_row[k]) * brow, bmax);
+    f.bq[k] = *reinterpret_cast<const v4u*>(ib.B + row + lc.b_off[k]);
   }
-  const int8_t* Hb = a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N;
 #pragma unroll
-  for (int k = 0; k < kHTasks; ++k) {
-    const int task = tid + k * kThreads;
-    const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
-    f.hq[k] = *reinterpret_cast<const v4u*>(Hb + int64_t(limb) * P * N + int64_t(min(p, P - 1)) * N +
-                                            (16 * sg < N ? 16 * sg : 0));
-  }
-  const int8_t* xb = a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P;
+  for (int k = 0; k < kHTasks; ++k) f.hq[k] = *reinterpret_cast<const v4u*>(ib.H + lc.h_off[k]);
+  const uint32_t xrow = uint32_t(a.nheads) * a.P;
+  const uint32_t xmax = uint32_t(ib.len - 1) * xrow;
 #pragma unroll
   for (int k = 0; k < kXTasks; ++k) {
-    const int task = tid + k * kThreads;
-    const int pq = task & 15, jq = task >> 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      f.xw[k][r] = *reinterpret_cast<const uint32_t*>(xb + int64_t(min(4 * jq + r, it.len - 1)) * H * P +
-                                                      (4 * pq < P ? 4 * pq : 0));
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t row = min(uint32_t(4 * lc.x_jq[k] + r) * xrow, xmax);
+      f.xw[k][r] = *reinterpret_cast<const uint32_t*>(ib.x + row + lc.x_off[k]);
+    }
   }
 }
 
@@ -165,6 +196,50 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   const int lane = tid % kWave;
   const int Q = a.Q, P = a.P, N = a.N;
   const int lcol = lane % 16, kg = lane / 16;
+  const int nlb = Q / 16;
+
+  // ---- lane constants (item independent)
+  LaneConst lc;
+#pragma unroll
+  for (int k = 0; k < kBTasks; ++k) {
+    const int task = tid + k * kThreads;
+    const int j = task >> 3, sg = task & 7;
+    lc.b_row[k] = j;
+    lc.b_colok[k] = 16 * sg < N;
+    lc.b_off[k] = 16 * sg < N ? 16 * sg : 0;
+    lc.b_lds[k] = bpos(j, 16 * sg);
+  }
+#pragma unroll
+  for (int k = 0; k < kHTasks; ++k) {
+    const int task = tid + k * kThreads;
+    const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
+    lc.h_ok[k] = p < P && 16 * sg < N;
+    lc.h_off[k] = uint32_t(limb * P * N + min(p, P - 1) * N + (16 * sg < N ? 16 * sg : 0));
+    lc.h_lds[k] = limb * kHPlane + hpos(p, 16 * sg);
+  }
+  {
+    const int pq = tid & 15;
+    lc.x_chan_ok = 4 * pq < P;
+#pragma unroll
+    for (int k = 0; k < kXTasks; ++k) {
+      const int jq = (tid + k * kThreads) >> 4;
+      lc.x_jq[k] = jq;
+      lc.x_off[k] = lc.x_chan_ok ? 4 * pq : 0;
+      lc.x_lds[k] = xpos(4 * pq, 4 * jq);
+    }
+  }
+  // hot-loop LDS bases: for rows js + lcol with js a multiple of 16 the B swizzle term depends
+  // on lcol only, so every hot-loop address is a per-lane base plus a multiple of the step
+  const int8_t* bs_lane = Bs + bpos(lcol, 16 * kg);                    // + js * 128
+  const int bs_half = bpos(lcol, 64 + 16 * kg) - bpos(lcol, 16 * kg);   // second K half
+  const _Float16* xt_lane = xT + xpos(lcol, 4 * kg);                    // + 16 pt rows, + jb
+  float* wlw = wl[wave];
+  const float* wl_lane = wlw + 4 * kg;
+  int hq_lane[2][4];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) hq_lane[s2][pt] = hpos(16 * pt + lcol, 64 * s2 + 16 * kg);
 
   // Persistent block: items blockIdx.x, blockIdx.x + gridDim.x, ...  The global loads of the
   // next item are issued right after the current item is committed to LDS and complete
@@ -172,7 +247,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   int it = blockIdx.x;
   if (it >= a.nitems) return;
   Prefetch f;
-  prefetch(f, item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a, tid);
+  prefetch(f, item_base(item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, a, tid);
 
   for (; it < a.nitems; it += gridDim.x) {
     const Item cur = item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q);
@@ -190,30 +265,25 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     if (tid < kMaxP) hsc[tid] = tid < P ? f.hs : 0.f;
 #pragma unroll
     for (int k = 0; k < kBTasks; ++k) {
-      const int task = tid + k * kThreads;
-      const int j = task >> 3, sg = task & 7;
       const v4u z = {0u, 0u, 0u, 0u};
-      if (j < Q) *reinterpret_cast<v4u*>(Bs + bpos(j, 16 * sg)) = (j < len && 16 * sg < N) ? f.bq[k] : z;
+      if (lc.b_row[k] < Q)
+        *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = (lc.b_row[k] < len && lc.b_colok[k]) ? f.bq[k] : z;
     }
 #pragma unroll
     for (int k = 0; k < kHTasks; ++k) {
-      const int task = tid + k * kThreads;
-      const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
       const v4u z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<v4u*>(Hq + limb * kHPlane + hpos(p, 16 * sg)) = (p < P && 16 * sg < N) ? f.hq[k] : z;
+      *reinterpret_cast<v4u*>(Hq + lc.h_lds[k]) = lc.h_ok[k] ? f.hq[k] : z;
     }
 #pragma unroll
     for (int k = 0; k < kXTasks; ++k) {
-      const int task = tid + k * kThreads;
-      const int pq = task & 15, jq = task >> 4;
-      const bool chan_ok = 4 * pq < P;
       uint32_t in[4], out[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) in[r] = ((chan_ok && 4 * jq + r < len) ? f.xw[k][r] : 0u) ^ 0x80808080u;
+      for (int r = 0; r < 4; ++r)
+        in[r] = ((lc.x_chan_ok && 4 * lc.x_jq[k] + r < len) ? f.xw[k][r] : 0u) ^ 0x80808080u;
       transpose4x4(in, out);
-      if (4 * jq < Q) {
+      if (4 * lc.x_jq[k] < Q) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + xpos(4 * pq + i, 4 * jq)) = codes_to_f16(out[i]);
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + lc.x_lds[k] + i * kXS) = codes_to_f16(out[i]);
       }
     }
     __syncthreads();
@@ -221,15 +291,15 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // ---- loads the current item still needs, for both of this wave's row blocks.  They are
     // issued and consumed before the next item's prefetch: vmcnt retires in order, so any
     // wait on a load issued after the prefetch would also wait for the prefetch.
-    const int nlb = Q / 16;
+    const int8_t* Cbase = a.C + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.ngroups + cur.g) * N;
+    const uint32_t crow = uint32_t(a.ngroups) * N;
     v4i cqs[2][2];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
       const int lbp = pass == 0 ? wave : 2 * kWaves - 1 - wave;
       const int l = 16 * lbp + lcol;
       const bool lvalid = lbp < nlb && l < len;
-      const int8_t* Crow =
-          a.C + ((int64_t(cur.b) * a.seqlen + cur.t0 + min(l, len - 1)) * a.ngroups + cur.g) * N;
+      const int8_t* Crow = Cbase + uint32_t(min(l, len - 1)) * crow;
       v4i cv[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) cv[s2] = *reinterpret_cast<const v4i*>(Crow + min(64 * s2 + 16 * kg, N - 16));
@@ -241,12 +311,13 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
     const float sx = a.x_scale[hu], sB = a.B_scale[gu], sC = a.C_scale[gu];
     const float Dh = a.D ? a.D[hu] : 0.f;
+    _Float16* ybase = a.y + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.nheads + cur.h) * P;
     __builtin_amdgcn_sched_barrier(0);
 
     // unconditional (the last item re-reads a valid item): a prefetch behind a branch would
     // make the wait counts after it conservative
     const int nx = min(it + int(gridDim.x), a.nitems - 1);
-    prefetch(f, item_of(nx, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a, tid);
+    prefetch(f, item_base(item_of(nx, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, a, tid);
     __builtin_amdgcn_sched_barrier(0);
 
     float dtmax = red[0];
@@ -256,25 +327,24 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const int kM = min(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, -120), 120);
     const float s_in = sx * sC * sB * exp2i(kM);
     const float fkM = float(kM);
+    const float sxD = sx * Dh;
 
 #pragma unroll 1
     for (int pass = 0; pass < 2; ++pass) {
-    const int lb = pass == 0 ? wave : 2 * kWaves - 1 - wave;
-    if (lb >= nlb || (pass == 1 && nlb <= kWaves)) continue;
-    const int l0 = 16 * lb;
-    const int l = l0 + lcol;
-    const bool lvalid = l < len;
-    const v4i cq[2] = {pass == 0 ? cqs[0][0] : cqs[1][0], pass == 0 ? cqs[0][1] : cqs[1][1]};
-    {
+      const int lb = pass == 0 ? wave : 2 * kWaves - 1 - wave;
+      if (lb >= nlb || (pass == 1 && nlb <= kWaves)) continue;
+      const int l0 = 16 * lb;
+      const int l = l0 + lcol;
+      const bool lvalid = l < len;
+      const v4i cq[2] = {pass == 0 ? cqs[0][0] : cqs[1][0], pass == 0 ? cqs[0][1] : cqs[1][1]};
       const int jdiag = l0 & ~31;          // the 32-token block that holds the diagonal
       const float a_l = acs2[l];
       const float a_0 = acs2[l0];
-      float* wlw = wl[wave];
 
-      // weights of the blocks before the diagonal, relative to row l0, times 2^-kM
-      for (int j = lane; j < jdiag; j += kWave) wlw[j] = exp2f(a_0 - acs2[j] - fkM) * dts[j];
+      // weights of the blocks before the diagonal, relative to row l0, times 2^-kM (<= 1 each)
+      for (int j = lane; j < jdiag; j += kWave) wlw[j] = __builtin_amdgcn_exp2f(a_0 - acs2[j] - fkM) * dts[j];
       __builtin_amdgcn_wave_barrier();
-      const float u_l = exp2f(a_l - a_0);
+      const float u_l = __builtin_amdgcn_exp2f(a_l - a_0);
 
       v4f yf[4], yd[4];
       v4i yo1[4], yo2[4];
@@ -291,21 +361,15 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const int hp = hpos(16 * pt + lcol, 64 * s2 + 16 * kg);
-          const v4i h1 = *reinterpret_cast<const v4i*>(Hq + hp);
-          const v4i h2 = *reinterpret_cast<const v4i*>(Hq + kHPlane + hp);
+          const v4i h1 = *reinterpret_cast<const v4i*>(Hq + hq_lane[s2][pt]);
+          const v4i h2 = *reinterpret_cast<const v4i*>(Hq + kHPlane + hq_lane[s2][pt]);
           yo1[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h1, cq[s2], yo1[pt], 0, 0, 0);
           yo2[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h2, cq[s2], yo2[pt], 0, 0, 0);
         }
       }
 
-      // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized
-      // decay.  For rows js + lcol with js a multiple of 16 the B swizzle term depends on lcol
-      // only, so every hot-loop address is a per-lane base plus a multiple of the step.
-      const int8_t* bs_lane = Bs + bpos(lcol, 16 * kg);                    // + js * 128
-      const int bs_half = bpos(lcol, 64 + 16 * kg) - bpos(lcol, 16 * kg);   // second K half
-      const _Float16* xt_lane = xT + xpos(lcol, 4 * kg);                    // + 16 pt rows, + jb
-      const float* wl_lane = wlw + 4 * kg;
+      // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized decay
+#pragma unroll 2
       for (int jb = 0; jb < jdiag; jb += 32) {
         v4i gm[2];
         float4 w4[2];
@@ -342,19 +406,21 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       // the block holding the diagonal: exact per-element decay and the causal mask
       {
         const int jb = jdiag;
+        const int j1 = min(jb + 16, Q - 16);   // second sub-block (fully masked when clamped)
         v4i gm[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const int js = min(jb + 16 * sb, Q - 16);
-          const v4i b0 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 16 * kg));
-          const v4i b1 = *reinterpret_cast<const v4i*>(Bs + bpos(js + lcol, 64 + 16 * kg));
+          const int8_t* bp = bs_lane + (sb == 0 ? jb : j1) * kMaxN;
+          const v4i b0 = *reinterpret_cast<const v4i*>(bp);
+          const v4i b1 = *reinterpret_cast<const v4i*>(bp + bs_half);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
         }
+        const float a_lk = a_l - fkM;
         v8h mop;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const int jq = min(jb + 16 * sb, Q - 16) + 4 * kg;
+          const int jq = (sb == 0 ? jb : j1) + 4 * kg;
           const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
           const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
           const float av[4] = {a4.x, a4.y, a4.z, a4.w};
@@ -362,24 +428,24 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = jb + 16 * sb + 4 * kg + i;     // > l (masked) whenever the clamp applied
-            const float m = float(gm[sb][i]) * exp2f(fminf(a_l - av[i], 0.f) - fkM) * dv[i];
+            const float m = float(gm[sb][i]) * __builtin_amdgcn_exp2f(fminf(a_lk - av[i], -fkM)) * dv[i];
             mop[4 * sb + i] = _Float16(j <= l ? m : 0.f);
           }
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const int p = 16 * pt + lcol;
-          const int j1 = min(jb + 16, Q - 16);
-          const v4h lo = *reinterpret_cast<const v4h*>(xT + xpos(p, jb + 4 * kg));
-          const v4h hi = *reinterpret_cast<const v4h*>(xT + xpos(p, j1 + 4 * kg));
+          const _Float16* xp = xt_lane + 16 * pt * kXS;
+          const v4h lo = *reinterpret_cast<const v4h*>(xp + jb);
+          const v4h hi = *reinterpret_cast<const v4h*>(xp + j1);
           const v8h xop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           yd[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yd[pt], 0, 0, 0);
         }
       }
 
       // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
-      const float s_off = exp2f(a_l) * sC;
-      _Float16* yrow = a.y + ((int64_t(cur.b) * a.seqlen + cur.t0 + min(l, len - 1)) * a.nheads + cur.h) * P;
+      const float s_off = __builtin_amdgcn_exp2f(fminf(a_l, 0.f)) * sC;
+      const float c_f = u_l * s_in;
+      _Float16* yrow = ybase + uint32_t(min(l, len - 1)) * uint32_t(a.nheads * P);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
@@ -388,13 +454,16 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int p = 16 * pt + 4 * kg + i;
-          const float xd = float(xT[xpos(p, l)]) * sx * Dh;
-          const float yo = float(yo1[pt][i]) + float(yo2[pt][i]) * (1.f / 256.f);
-          out[i] = _Float16((u_l * yf[pt][i] + yd[pt][i]) * s_in + yo * (s_off * hv[i]) + xd);
+          const float c1 = s_off * hv[i];
+          float v = float(xT[xpos(p, l)]) * sxD;
+          v = fmaf(float(yo2[pt][i]), c1 * (1.f / 256.f), v);
+          v = fmaf(float(yo1[pt][i]), c1, v);
+          v = fmaf(yd[pt][i], s_in, v);
+          v = fmaf(yf[pt][i], c_f, v);
+          out[i] = _Float16(v);
         }
         if (lvalid && 16 * pt + 4 * kg < P) *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg) = out;
       }
-    }
     }
     __syncthreads();   // LDS is rewritten by the next item's commit
   }
