@@ -14,6 +14,7 @@ the same prefill workload.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -28,6 +29,42 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_PEAK_OPS = 5.0e15         # MI355X dense INT8 MFMA
 METRIC = "SSD scan tokens/s + % INT8 MFMA peak (prefill); decode HBM GB/s"
+
+
+# HBM bytes per launch measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE, each scaled by what
+# the same counter reads for a plain 1 GiB device copy), one row per kernel, keyed by a digest of
+# the kernel's source so that a reading taken on an older version of a kernel is not reported.
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_mamba2-1.3b-prefill_mamba2-8b-decode.md")
+KERNEL_SOURCE = {"quantize_x": "quantize.hip", "quantize_B": "quantize.hip", "quantize_C": "quantize.hip",
+                 "chunk_state": "chunk_state.hip", "state_passing": "state_passing.hip",
+                 "chunk_output": "chunk_output.hip", "state_update": "state_update.hip"}
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kernel], "ssdq_internal.h"):
+        with open(os.path.join(ROOT, "quantized_selective_state_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """Counter-measured HBM bytes per launch of `kernel`, or None if the table has no row for
+    the kernel's current source."""
+    try:
+        with open(TRAFFIC_TABLE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    digest = source_digest(kernel)
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) >= 4 and cells[0] == kernel and cells[1] == digest:
+            try:
+                return int(cells[-1])
+            except ValueError:
+                return None
+    return None
 
 
 def parse():
@@ -168,7 +205,8 @@ def main():
         "config": {"workload": name, "batch": b, "seqlen": L, "nheads": H, "headdim": P, "dstate": N,
                    "ngroups": G, "chunk": Q},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dominant)},
         "scan_tokens_per_s": round(tokens / (scan_ms / 1e3), 1),
         "event_ms_per_step_median": round(float(np.median(step_ms)), 5),
         "mfma_pct_of_int8_peak": round(100 * total_ops / (scan_ms / 1e3) / INT8_PEAK_OPS, 3),
@@ -225,7 +263,7 @@ def bench_decode(args, torch, ssdq, workloads, dev):
     return {"workload": name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "ngroups": G, "steps": steps,
             "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms / 1e3), 1),
             "alg_bytes_per_step": per_step, "achieved_GBs": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("state_update")}
 
 
 def cpu_baseline(inp):

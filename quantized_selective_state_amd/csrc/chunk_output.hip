@@ -241,10 +241,12 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) hq_lane[s2][pt] = hpos(16 * pt + lcol, 64 * s2 + 16 * kg);
 
-  // Persistent block: items blockIdx.x, blockIdx.x + gridDim.x, ...  The global loads of the
-  // next item are issued right after the current item is committed to LDS and complete
-  // while the current item is computed.
-  int it = blockIdx.x;
+  // Persistent block: items slot, slot + gridDim.x, ...  The global loads of the next item are
+  // issued right after the current item is committed to LDS and complete while the current
+  // item is computed.  slot is XCD-aware: the blocks of one XCD take consecutive items, i.e.
+  // neighbouring heads of one (batch, chunk), so that chunk's B and C and the dt lines it
+  // shares across heads are fetched into one L2 rather than into all of them.
+  int it = xcd_remap(blockIdx.x, gridDim.x);
   if (it >= a.nitems) return;
   Prefetch f;
   prefetch(f, item_base(item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, a, tid);
