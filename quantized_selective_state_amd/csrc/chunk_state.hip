@@ -1,4 +1,4 @@
-// Stage 0 of the chunked SSD scan, one block (8 waves) per (batch, chunk, head):
+// Stage 0 of the chunked SSD scan, one block (4 waves) per (batch, chunk, head):
 //
 //  (a) chunk cumsum: Acs[j] = sum_{i <= j} dt_i A_h inside the chunk (tokens past the end
 //      of the sequence add 0), written to the workspace for the later stages;
@@ -22,14 +22,15 @@
 // Both operands contract over tokens, the slow axis in memory, so x and B are transposed
 // into LDS (token-contiguous 256-byte rows).  Rows use a 16-byte-chunk XOR swizzle that
 // keeps both the transposing writes (rows 4q+i of 16 consecutive q) and the MFMA operand
-// reads (16 consecutive rows) free of bank conflicts.  The limbs are built in registers
-// from the x^T rows right before the MFMAs.
+// reads (16 consecutive rows) free of bank conflicts.  Each wave owns one 16-channel tile of
+// S across all states and tokens, so every limb is built exactly once, in registers, from the
+// x^T rows right before its MFMAs.
 #include "ssdq_internal.h"
 
 namespace ssdq {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxQ = 256;
 constexpr int kMaxP = 64;
@@ -55,45 +56,67 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
   out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-// Load the int8 codes of the chunk for `channels` (<= kChan) channels (row stride `stride`
-// bytes in global memory) and store them token-contiguous into the swizzled LDS matrix of
-// kChan rows; channels >= `channels` and tokens >= len are zero.  A task is 4 channels x 4
-// tokens; a wave's 64 lanes take 16 consecutive channel quads x 4 consecutive token quads,
-// which makes the swizzled LDS writes conflict-free.  Loads use clamped addresses and a
-// select, so none of them sits behind a branch.
+// Transposing the int8 codes of the chunk for `channels` (<= kChan) channels into the swizzled
+// token-contiguous LDS matrix of kChan rows.  A task is 4 channels x 4 tokens; a wave's 64
+// lanes take 16 consecutive channel quads x 4 consecutive token quads, which makes the
+// swizzled LDS writes conflict-free.  Tasks cover all kMaxQ token positions of a row.
+//
+// The global loads are issued first (stage_load, at kernel entry) and committed to LDS later
+// (stage_commit), so their latency overlaps the chunk cumsum.  Every load is unconditional:
+// rows past the sequence end and channel quads past `channels` read a clamped in-chunk
+// address, and stage_commit replaces them with zeros.  Addresses are 32-bit offsets from the
+// chunk's base (the host bounds a chunk of x and of B below 2^31 bytes).
 template <int kChan>
-__device__ __forceinline__ void transpose_into(uint8_t* lds, const int8_t* src, int64_t stride, int channels,
-                                               int Q, int len, int tid) {
-  constexpr int kXq = kChan / 4;             // channel quads (multiple of 16)
-  constexpr int kHi = kXq / 16;
-  constexpr int kIters = kXq * (kMaxQ / 4) / kThreads;
-  const int ntasks = kXq * (Q / 4);
+struct Staged {
+  static constexpr int kXq = kChan / 4;             // channel quads (multiple of 16)
+  static constexpr int kHi = kXq / 16;
+  static constexpr int kIters = kXq * (kMaxQ / 4) / kThreads;
+  uint32_t v[kIters][4];
+};
+
+template <int kChan>
+__device__ __forceinline__ void task_of(int task, int& xq, int& jq) {
+  constexpr int kHi = Staged<kChan>::kHi;
+  const int rest = task >> 6;
+  xq = (task & 15) + 16 * (rest % kHi);
+  jq = ((task >> 4) & 3) + 4 * (rest / kHi);
+}
+
+template <int kChan>
+__device__ __forceinline__ void stage_load(Staged<kChan>& st, const int8_t* base, uint32_t stride, int channels,
+                                           int len, int tid) {
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const int task = tid + it * kThreads;
-    const int rest = task >> 6;
-    const int xq = (task & 15) + 16 * (rest % kHi);
-    const int jq = ((task >> 4) & 3) + 4 * (rest / kHi);
-    const bool chan_ok = 4 * xq < channels;
-    uint32_t in[4], out[4];
+  for (int it = 0; it < Staged<kChan>::kIters; ++it) {
+    int xq, jq;
+    task_of<kChan>(tid + it * kThreads, xq, jq);
+    const uint32_t xx = uint32_t(min(4 * xq, channels - 4));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = 4 * jq + r;
-      const bool ok = chan_ok && j < len && task < ntasks;
-      const int jj = min(j, len - 1);
-      const int xx = chan_ok ? 4 * xq : 0;
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(src + int64_t(jj) * stride + xx);
-      in[r] = ok ? v : 0u;
-    }
-    transpose4x4(in, out);
-    if (task < ntasks) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(lds + tpos(4 * xq + i, 4 * jq)) = out[i];
+      const uint32_t j = uint32_t(min(4 * jq + r, len - 1));
+      st.v[it][r] = *reinterpret_cast<const uint32_t*>(base + (j * stride + xx));
     }
   }
 }
 
-__global__ void __launch_bounds__(kThreads) chunk_state_kernel(
+template <int kChan>
+__device__ __forceinline__ void stage_commit(uint8_t* lds, const Staged<kChan>& st, int channels, int len,
+                                             int tid) {
+#pragma unroll
+  for (int it = 0; it < Staged<kChan>::kIters; ++it) {
+    int xq, jq;
+    task_of<kChan>(tid + it * kThreads, xq, jq);
+    const bool chan_ok = 4 * xq < channels;
+    uint32_t in[4], out[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) in[r] = (chan_ok && 4 * jq + r < len) ? st.v[it][r] : 0u;
+    transpose4x4(in, out);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(lds + tpos(4 * xq + i, 4 * jq)) = out[i];
+  }
+}
+
+// 3 waves per SIMD (<= 168 VGPRs): three blocks per CU, bounded by LDS as well.
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) chunk_state_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
     const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ acs, float* __restrict__ states, int64_t seqlen, int32_t nheads, int32_t headdim,
@@ -117,12 +140,16 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
   const int len = int(seqlen - t0 < chunk ? seqlen - t0 : chunk);
   const int Q = chunk, P = headdim, N = dstate;
 
+  // ---- global loads: dt of this thread's token, then the x and B codes of the chunk
+  const float dt_raw = dt[(int64_t(b) * seqlen + t0 + min(tid, len - 1)) * nheads + h];
+  Staged<kMaxP> xs;
+  Staged<kMaxN> bs;
+  stage_load(xs, x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, uint32_t(nheads * P), P, len, tid);
+  stage_load(bs, Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, uint32_t(ngroups * N), N, len, tid);
+
   // ---- (a) chunk cumsum of dt A, one token per thread of waves 0..Q/64-1
-  float d = 0.f, v = 0.f;
-  if (tid < len) {
-    d = dt[(int64_t(b) * seqlen + t0 + tid) * nheads + h];
-    v = d * A[h];
-  }
+  const float d = tid < len ? dt_raw : 0.f;
+  float v = d * A[h];
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
     const float up = __shfl_up(v, o, kWave);
@@ -131,7 +158,8 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
   if (lane == kWave - 1) red[wave] = v;
   __syncthreads();
   float pre = 0.f;
-  for (int w2 = 0; w2 < wave; ++w2) pre += red[w2];
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves - 1; ++w2) pre += w2 < wave ? red[w2] : 0.f;
   const float acs_t = v + pre;
   if (tid < Q) acs[((int64_t(b) * nheads + h) * nchunks + c) * chunk + tid] = acs_t;
   if (tid == len - 1) acs_last_s = acs_t;
@@ -155,30 +183,26 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
   }
 
   // ---- x and B codes of the chunk, token-contiguous in LDS
-  transpose_into<kMaxP>(xT, x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, int64_t(nheads) * P, P, Q, len,
-                        tid);
-  transpose_into<kMaxN>(BT, Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, int64_t(ngroups) * N, N, Q,
-                        len, tid);
+  stage_commit(xT, xs, P, len, tid);
+  stage_commit(BT, bs, N, len, tid);
   __syncthreads();
 
-  // ---- S tiles on the zero-padded 64 x 128 space: wave w owns channel tile w % 4 and the
-  // four 16-state tiles of half w / 4 (one work unit per wave, fully unrolled)
+  // ---- S tiles on the zero-padded 64 x 128 space: wave w owns channel tile w and all eight
+  // 16-state tiles
   const float post = x_scale[h] * B_scale[g] * exp2i(e);
   float* Sc = states + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N;
   const int lcol = lane % 16, kg = lane / 16;
-  const int pt = wave % 4, nt0 = 4 * (wave / 4);
-  v4i acc[4][3];
+  const int pt = wave;
+  constexpr int kNt = kMaxN / 16;
+  v4i acc[kNt][3];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < kNt; ++t)
 #pragma unroll
     for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
   const int p = 16 * pt + lcol;
   for (int kb = 0; kb < Q; kb += 64) {
     const int j0 = kb + 16 * kg;
     const v4u xw = *reinterpret_cast<const v4u*>(xT + tpos(p, j0));
-    v4i bop[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) bop[t] = *reinterpret_cast<const v4i*>(BT + tpos(16 * (nt0 + t) + lcol, j0));
     v4i l1, l2, l3;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
@@ -196,16 +220,17 @@ __global__ void __launch_bounds__(kThreads) chunk_state_kernel(
       l3[dw] = int(pl[0] ^ 0x80808080u);
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, bop[t], acc[t][0], 0, 0, 0);
-      acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l2, bop[t], acc[t][1], 0, 0, 0);
-      acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l3, bop[t], acc[t][2], 0, 0, 0);
+    for (int t = 0; t < kNt; ++t) {
+      const v4i bop = *reinterpret_cast<const v4i*>(BT + tpos(16 * t + lcol, j0));
+      acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, bop, acc[t][0], 0, 0, 0);
+      acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l2, bop, acc[t][1], 0, 0, 0);
+      acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l3, bop, acc[t][2], 0, 0, 0);
     }
   }
   // D layout of a 16x16 MFMA: lane holds rows 4 (lane/16) + i, column lane % 16
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int n = 16 * (nt0 + t) + lcol;
+  for (int t = 0; t < kNt; ++t) {
+    const int n = 16 * t + lcol;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pr = 16 * pt + 4 * kg + i;
