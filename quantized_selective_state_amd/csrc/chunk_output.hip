@@ -114,71 +114,53 @@ struct Params {
   int nheads, P, N, ngroups, Q, nchunks, nitems;
 };
 
-// Per-lane offsets that do not depend on the work item (computed once per block).
+// Per-lane byte offsets that do not depend on the work item (computed once per block).  Pieces
+// that fall outside the operand (channels past P, states past N) get kOutOfRange and load as
+// zeros; rows past the sequence end load as zeros through the item's buffer sizes.
 struct LaneConst {
-  uint32_t b_off[kBTasks];      // byte offset of the B piece in a token-major chunk (row j * G*N)
-  int b_row[kBTasks];           // its token row j
+  uint32_t b_off[kBTasks];      // B piece: token row j * G*N + 16-byte column group
   int b_lds[kBTasks];
-  bool b_colok[kBTasks];
-  uint32_t h_off[kHTasks];      // byte offset of the Hprev-limb piece in its (b, c, h) block
+  uint32_t h_off[kHTasks];      // Hprev-limb piece in its (b, c, h) block
   int h_lds[kHTasks];
-  bool h_ok[kHTasks];
-  uint32_t x_off[kXTasks];      // byte offset of the first row of the x task (row 4 jq)
-  int x_jq[kXTasks];
+  uint32_t x_off[kXTasks];      // first row (4 jq) of an x transposition task, channel quad
   int x_lds[kXTasks];
-  bool x_chan_ok;
+  uint32_t c_off[2][2];         // C codes of this lane's output row, per pass and K half
+  uint32_t acs_off, dt_off, hs_off;
 };
 
-// Uniform per-item base pointers.
-struct ItemBase {
-  const float* acs;
-  const float* dt;
-  const float* hs;
-  const int8_t* B;
-  const int8_t* H;
-  const int8_t* x;
-  int len;
+// Buffer resources of one item: base at the item's first element, size up to the end of its
+// last valid row.
+struct ItemRsrc {
+  Rsrc acs, dt, hs, B, H, x;
 };
 
-__device__ __forceinline__ ItemBase item_base(const Item& it, const Params& a) {
+__device__ __forceinline__ ItemRsrc item_rsrc(const Item& it, const Params& a) {
   const int P = a.P, N = a.N, G = a.ngroups, H = a.nheads;
-  ItemBase r;
-  r.acs = a.acs + ((int64_t(it.b) * H + it.h) * a.nchunks + it.c) * a.Q;
-  r.dt = a.dt + (int64_t(it.b) * a.seqlen + it.t0) * H + it.h;
-  r.hs = a.hscale + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * P;
-  r.B = a.B + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N;
-  r.H = a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N;
-  r.x = a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P;
-  r.len = it.len;
+  const uint32_t last = uint32_t(it.len - 1);
+  ItemRsrc r;
+  r.acs = make_rsrc(a.acs + ((int64_t(it.b) * H + it.h) * a.nchunks + it.c) * a.Q, uint32_t(a.Q) * 4u);
+  r.dt = make_rsrc(a.dt + (int64_t(it.b) * a.seqlen + it.t0) * H + it.h, (last * uint32_t(H) + 1u) * 4u);
+  r.hs = make_rsrc(a.hscale + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * P, uint32_t(P) * 4u);
+  r.B = make_rsrc(a.B + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N, last * uint32_t(G * N) + N);
+  r.H = make_rsrc(a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N,
+                  uint32_t(2 * P * N));
+  r.x = make_rsrc(a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P, last * uint32_t(H * P) + P);
   return r;
 }
 
-// Issue every global load of one item (clamped addresses; nothing waits here).
-__device__ __forceinline__ void prefetch(Prefetch& f, const ItemBase& ib, const LaneConst& lc, const Params& a,
-                                         int tid) {
-  const int t = min(tid & (kMaxQ - 1), a.Q - 1);
-  f.acs = ib.acs[t];
-  f.dt = ib.dt[int64_t(min(t, ib.len - 1)) * a.nheads];
-  f.hs = ib.hs[min(tid & (kMaxP - 1), a.P - 1)];
-  const uint32_t brow = uint32_t(a.ngroups) * a.N;
-  const uint32_t bmax = uint32_t(ib.len - 1) * brow;
+// Issue every global load of one item (nothing waits here).
+__device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow) {
+  f.acs = buf_loadf(r.acs, lc.acs_off);
+  f.dt = buf_loadf(r.dt, lc.dt_off);
+  f.hs = buf_loadf(r.hs, lc.hs_off);
 #pragma unroll
-  for (int k = 0; k < kBTasks; ++k) {
-    const uint32_t row = min(uint32_t(lc.b_row[k]) * brow, bmax);
-    f.bq[k] = *reinterpret_cast<const v4u*>(ib.B + row + lc.b_off[k]);
-  }
+  for (int k = 0; k < kBTasks; ++k) f.bq[k] = buf_load16(r.B, lc.b_off[k]);
 #pragma unroll
-  for (int k = 0; k < kHTasks; ++k) f.hq[k] = *reinterpret_cast<const v4u*>(ib.H + lc.h_off[k]);
-  const uint32_t xrow = uint32_t(a.nheads) * a.P;
-  const uint32_t xmax = uint32_t(ib.len - 1) * xrow;
+  for (int k = 0; k < kHTasks; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
 #pragma unroll
-  for (int k = 0; k < kXTasks; ++k) {
+  for (int k = 0; k < kXTasks; ++k)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t row = min(uint32_t(4 * lc.x_jq[k] + r) * xrow, xmax);
-      f.xw[k][r] = *reinterpret_cast<const uint32_t*>(ib.x + row + lc.x_off[k]);
-    }
-  }
+    for (int rr = 0; rr < 4; ++rr) f.xw[k][rr] = buf_load4(r.x, lc.x_off[k] + uint32_t(rr) * xrow);
 }
 
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
@@ -199,35 +181,42 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   const int nlb = Q / 16;
 
   // ---- lane constants (item independent)
+  const uint32_t gn = uint32_t(a.ngroups * N), xrow = uint32_t(a.nheads * P);
   LaneConst lc;
 #pragma unroll
   for (int k = 0; k < kBTasks; ++k) {
     const int task = tid + k * kThreads;
     const int j = task >> 3, sg = task & 7;
-    lc.b_row[k] = j;
-    lc.b_colok[k] = 16 * sg < N;
-    lc.b_off[k] = 16 * sg < N ? 16 * sg : 0;
+    lc.b_off[k] = 16 * sg < N ? uint32_t(j) * gn + 16 * sg : kOutOfRange;
     lc.b_lds[k] = bpos(j, 16 * sg);
   }
 #pragma unroll
   for (int k = 0; k < kHTasks; ++k) {
     const int task = tid + k * kThreads;
     const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
-    lc.h_ok[k] = p < P && 16 * sg < N;
-    lc.h_off[k] = uint32_t(limb * P * N + min(p, P - 1) * N + (16 * sg < N ? 16 * sg : 0));
+    lc.h_off[k] = (p < P && 16 * sg < N) ? uint32_t(limb * P * N + p * N + 16 * sg) : kOutOfRange;
     lc.h_lds[k] = limb * kHPlane + hpos(p, 16 * sg);
   }
   {
     const int pq = tid & 15;
-    lc.x_chan_ok = 4 * pq < P;
 #pragma unroll
     for (int k = 0; k < kXTasks; ++k) {
       const int jq = (tid + k * kThreads) >> 4;
-      lc.x_jq[k] = jq;
-      lc.x_off[k] = lc.x_chan_ok ? 4 * pq : 0;
+      lc.x_off[k] = 4 * pq < P ? uint32_t(4 * jq) * xrow + 4 * pq : kOutOfRange;
       lc.x_lds[k] = xpos(4 * pq, 4 * jq);
     }
   }
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int lbp = pass == 0 ? wave : 2 * kWaves - 1 - wave;
+    const uint32_t l = uint32_t(16 * lbp + lcol);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+      lc.c_off[pass][s2] = (lbp < nlb && 64 * s2 + 16 * kg < N) ? l * gn + 64 * s2 + 16 * kg : kOutOfRange;
+  }
+  lc.acs_off = uint32_t(tid & (kMaxQ - 1)) * 4u;
+  lc.dt_off = uint32_t(tid & (kMaxQ - 1)) * uint32_t(a.nheads) * 4u;
+  lc.hs_off = uint32_t(tid & (kMaxP - 1)) * 4u;
   // hot-loop LDS bases: for rows js + lcol with js a multiple of 16 the B swizzle term depends
   // on lcol only, so every hot-loop address is a per-lane base plus a multiple of the step
   const int8_t* bs_lane = Bs + bpos(lcol, 16 * kg);                    // + js * 128
@@ -249,66 +238,49 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   int it = xcd_remap(blockIdx.x, gridDim.x);
   if (it >= a.nitems) return;
   Prefetch f;
-  prefetch(f, item_base(item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, a, tid);
+  prefetch(f, item_rsrc(item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, xrow);
 
   for (; it < a.nitems; it += gridDim.x) {
     const Item cur = item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q);
     const int len = cur.len;
 
-    // ---- commit the prefetched item to LDS (zero padding past the sequence end, P and N)
+    // ---- commit the prefetched item to LDS.  Rows past the sequence end arrived as zeros;
+    // channels past P and states past N hold zeros or values that only meet zeros (the C codes
+    // past N are zero, and rows past P are never stored).
     if (tid < kMaxQ) {
-      if (tid < Q) acs2[tid] = f.acs * kLog2e;
-      dts[tid] = tid < len ? f.dt : 0.f;
+      acs2[tid] = f.acs * kLog2e;
+      dts[tid] = f.dt;
     }
     {
-      const float dm = wave_max(tid < kMaxQ && tid < len ? f.dt : 0.f);
+      const float dm = wave_max(f.dt);   // waves 4..7 hold the same tokens as waves 0..3
       if (lane == 0) red[wave] = dm;
     }
-    if (tid < kMaxP) hsc[tid] = tid < P ? f.hs : 0.f;
+    if (tid < kMaxP) hsc[tid] = f.hs;
 #pragma unroll
-    for (int k = 0; k < kBTasks; ++k) {
-      const v4u z = {0u, 0u, 0u, 0u};
-      if (lc.b_row[k] < Q)
-        *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = (lc.b_row[k] < len && lc.b_colok[k]) ? f.bq[k] : z;
-    }
+    for (int k = 0; k < kBTasks; ++k) *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
 #pragma unroll
-    for (int k = 0; k < kHTasks; ++k) {
-      const v4u z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<v4u*>(Hq + lc.h_lds[k]) = lc.h_ok[k] ? f.hq[k] : z;
-    }
+    for (int k = 0; k < kHTasks; ++k) *reinterpret_cast<v4u*>(Hq + lc.h_lds[k]) = f.hq[k];
 #pragma unroll
     for (int k = 0; k < kXTasks; ++k) {
       uint32_t in[4], out[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        in[r] = ((lc.x_chan_ok && 4 * lc.x_jq[k] + r < len) ? f.xw[k][r] : 0u) ^ 0x80808080u;
+      for (int r = 0; r < 4; ++r) in[r] = f.xw[k][r] ^ 0x80808080u;
       transpose4x4(in, out);
-      if (4 * lc.x_jq[k] < Q) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + lc.x_lds[k] + i * kXS) = codes_to_f16(out[i]);
-      }
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + lc.x_lds[k] + i * kXS) = codes_to_f16(out[i]);
     }
     __syncthreads();
 
     // ---- loads the current item still needs, for both of this wave's row blocks.  They are
     // issued and consumed before the next item's prefetch: vmcnt retires in order, so any
     // wait on a load issued after the prefetch would also wait for the prefetch.
-    const int8_t* Cbase = a.C + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.ngroups + cur.g) * N;
-    const uint32_t crow = uint32_t(a.ngroups) * N;
+    const Rsrc crs = make_rsrc(a.C + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.ngroups + cur.g) * N,
+                               uint32_t(len - 1) * gn + N);
     v4i cqs[2][2];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int lbp = pass == 0 ? wave : 2 * kWaves - 1 - wave;
-      const int l = 16 * lbp + lcol;
-      const bool lvalid = lbp < nlb && l < len;
-      const int8_t* Crow = Cbase + uint32_t(min(l, len - 1)) * crow;
-      v4i cv[2];
+    for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) cv[s2] = *reinterpret_cast<const v4i*>(Crow + min(64 * s2 + 16 * kg, N - 16));
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        cqs[pass][s2] = (lvalid && 64 * s2 + 16 * kg < N) ? cv[s2] : v4i{0, 0, 0, 0};
-    }
+      for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = __builtin_bit_cast(v4i, buf_load16(crs, lc.c_off[pass][s2]));
     const int hu = __builtin_amdgcn_readfirstlane(cur.h);
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
     const float sx = a.x_scale[hu], sB = a.B_scale[gu], sC = a.C_scale[gu];
@@ -319,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // unconditional (the last item re-reads a valid item): a prefetch behind a branch would
     // make the wait counts after it conservative
     const int nx = min(it + int(gridDim.x), a.nitems - 1);
-    prefetch(f, item_base(item_of(nx, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, a, tid);
+    prefetch(f, item_rsrc(item_of(nx, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, xrow);
     __builtin_amdgcn_sched_barrier(0);
 
     float dtmax = red[0];

@@ -65,6 +65,24 @@ hipError_t launch_state_update(float* state, const int8_t* x, const float* x_sca
 // ---------------------------------------------------------------------------------------------
 // device helpers
 
+// Raw buffer loads (gfx9 buffer resource: base address, size in bytes, dword 3 = 0x00020000).
+// A load whose byte offset is at or past the size returns zeros without touching memory: the
+// kernels use this to zero-pad ragged chunk tails and padded tiles with no clamps or selects.
+// Sizes and offsets stay below 2^31 (the host bounds one chunk of any operand below that).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a byte offset that is never in range
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ v4u buf_load16(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ float buf_loadf(Rsrc r, uint32_t off) { return __uint_as_float(buf_load4(r, off)); }
+
 // Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8).  Remap the
 // linear block index so that consecutive *logical* tiles land on the same XCD and share
 // its L2 (neighbouring heads read the same 128-byte lines of x and the same B/C rows).
