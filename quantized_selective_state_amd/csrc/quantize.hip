@@ -3,16 +3,17 @@
 // for B and C).  code = clamp(rint(float(v) / s), -127, 127), the quotient
 // correctly rounded, NaN -> 0.
 //
-// HBM-bound elementwise pass: 2 bytes in, 1 byte out per element; each thread handles
-// 8 consecutive elements with one 16-byte load and one 8-byte store.
+// HBM-bound elementwise pass: 2 bytes in, 1 byte out per element.  The main kernel gives each
+// thread 16 consecutive elements of one row (two 16-byte loads issued together, one 16-byte
+// store), so that enough bytes are in flight to cover the memory latency.  Plain (cached)
+// loads and stores: on MI355X they stream faster here than nontemporal ones.
 //
-// Exactness without a division per element: with r = fl(1/s) (one correctly rounded
-// division per thread) and y = fl(v r), |y - v/s| <= 2^-23 |v/s| and
-// |fl(v/s) - v/s| <= 2^-24 |v/s|, so for |y| < 256 the two are within 1.5 * 2^-15.
-// rint(y) and rint(fl(v/s)) can only differ when a half-integer lies in between, i.e.
-// when y is within 2^-13 of one; those (rare) elements take the exact division.  Beyond
-// |y| >= 256 both saturate.  The int conversion maps NaN to 0 and the integer clamp
-// gives +-127 for infinities.
+// Exactness without a division per element: with r = rcp(s) (the hardware reciprocal, within
+// 1 ulp) and y = fl(v r), |y - v/s| <= 1.5 * 2^-23 |v/s| and |fl(v/s) - v/s| <= 2^-24 |v/s|,
+// so for |y| < 256 the two are within 2^-14.  rint(y) and rint(fl(v/s)) can only differ when
+// a half-integer lies in between, i.e. when y is within 2^-13 of one; those (rare) elements
+// take the exact division.  Beyond |y| >= 256 both saturate.  The float -> int conversion
+// maps NaN to 0 and saturates infinities, and the clamp is done on the integer.
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -26,13 +27,27 @@ __device__ __forceinline__ uint32_t code_exact(float v, float s) {
   return uint32_t(int32_t(r)) & 0xffu;
 }
 
-// fast code and a flag that is set when the exact division must decide
+// fast code, and whether the exact division must decide this element (also for NaN and
+// |y| >= 256, which are rare and which the exact path maps to 0 and +-127)
 __device__ __forceinline__ uint32_t code_fast(float v, float rcp, bool& slow) {
   const float y = v * rcp;
   const float k = rintf(y);
-  slow |= (fabsf(y - k) > 0.5f - 1.0f / 8192.f) && (fabsf(y) < 256.f);
-  const float kc = fminf(fmaxf(k, -127.f), 127.f);   // a NaN y is replaced below
-  return (y == y ? uint32_t(int32_t(kc)) : 0u) & 0xffu;
+  slow = !(fabsf(y - k) <= 0.5f - 1.0f / 8192.f) || !(fabsf(y) < 256.f);
+  const float kc = __builtin_amdgcn_fmed3f(k, -127.f, 127.f);   // finite whenever slow is false
+  return uint32_t(int32_t(kc)) & 0xffu;
+}
+
+// n codes of one scale: the fast path for all, the exact division only for the elements that
+// need it (a per-element branch: a wave pays for an element only when one of its lanes needs it)
+template <int n>
+__device__ __forceinline__ void codes(const float (&v)[n], float s, uint32_t (&c)[n]) {
+  const float rcp = __builtin_amdgcn_rcpf(s);
+  bool slow[n];
+#pragma unroll
+  for (int e = 0; e < n; ++e) c[e] = code_fast(v[e], rcp, slow[e]);
+#pragma unroll
+  for (int e = 0; e < n; ++e)
+    if (slow[e]) c[e] = code_exact(v[e], s);
 }
 
 // Division by an invariant divisor d for n < 2^31 (round-up multiplier):
@@ -50,6 +65,36 @@ FastDiv make_fastdiv(uint32_t d) {
 
 __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
 
+__device__ __forceinline__ void unpack8(v4u raw, float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] & 0xffffu)));
+    v[2 * e + 1] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] >> 16)));
+  }
+}
+
+__device__ __forceinline__ uint32_t pack4(const uint32_t* c) { return c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24); }
+
+// inner % 16 == 0: a thread quantizes 16 consecutive elements of one row (one scale index).
+// Pair indices i < 2^31 (host-checked), so the scale index uses 32-bit invariant division.
+__global__ void __launch_bounds__(256) quantize_vec16(const v4u* __restrict__ x, v4u* __restrict__ q,
+                                                      const float* __restrict__ scale, uint32_t npair,
+                                                      FastDiv by_inner, FastDiv by_nscale) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < npair; i += stride) {
+    const v4u raw0 = x[2 * i];
+    const v4u raw1 = x[2 * i + 1];
+    const uint32_t row = fdiv(i, by_inner);
+    const int k = int(row - fdiv(row, by_nscale) * by_nscale.d);
+    float v[16];
+    unpack8(raw0, *reinterpret_cast<float(*)[8]>(&v[0]));
+    unpack8(raw1, *reinterpret_cast<float(*)[8]>(&v[8]));
+    uint32_t c[16];
+    codes(v, scale[k], c);
+    q[i] = v4u{pack4(c), pack4(c + 4), pack4(c + 8), pack4(c + 12)};
+  }
+}
+
 // inner % 8 == 0: the 8 elements of a thread share one scale index.
 // Vector indices i < 2^31 (host-checked), so the scale index uses 32-bit invariant division.
 __global__ void __launch_bounds__(256) quantize_vec8(const v4u* __restrict__ x, v2u* __restrict__ q,
@@ -57,28 +102,14 @@ __global__ void __launch_bounds__(256) quantize_vec8(const v4u* __restrict__ x, 
                                                      FastDiv by_inner, FastDiv by_nscale) {
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
+    const v4u raw = x[i];
     const uint32_t row = fdiv(i, by_inner);
     const int k = int(row - fdiv(row, by_nscale) * by_nscale.d);
-    const float s = scale[k];
-    const float rcp = __fdiv_rn(1.f, s);
-    const v4u raw = __builtin_nontemporal_load(x + i);
     float v[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] & 0xffffu)));
-      v[2 * e + 1] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] >> 16)));
-    }
-    bool slow = false;
+    unpack8(raw, v);
     uint32_t c[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) c[e] = code_fast(v[e], rcp, slow);
-    if (slow) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = code_exact(v[e], s);
-    }
-    const uint32_t lo = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-    const uint32_t hi = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    __builtin_nontemporal_store(v2u{lo, hi}, q + i);
+    codes(v, scale[k], c);
+    q[i] = v2u{pack4(c), pack4(c + 4)};
   }
 }
 
@@ -109,7 +140,13 @@ hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int
   const int64_t n = rows * int64_t(nscale) * inner;
   if (n == 0) return hipSuccess;
   int64_t done = 0;
-  if (inner % 8 == 0 && n / 8 < (int64_t(1) << 31)) {
+  if (inner % 16 == 0 && n / 16 < (int64_t(1) << 31)) {
+    const int64_t npair = n / 16;
+    hipLaunchKernelGGL(quantize_vec16, dim3(grid_for(npair, 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const v4u*>(x), reinterpret_cast<v4u*>(q), scale, uint32_t(npair),
+                       make_fastdiv(uint32_t(inner / 16)), make_fastdiv(uint32_t(nscale)));
+    done = npair * 16;
+  } else if (inner % 8 == 0 && n / 8 < (int64_t(1) << 31)) {
     const int64_t nvec = n / 8;
     hipLaunchKernelGGL(quantize_vec8, dim3(grid_for(nvec, 256)), dim3(256), 0, stream,
                        reinterpret_cast<const v4u*>(x), reinterpret_cast<v2u*>(q), scale, uint32_t(nvec),
