@@ -22,12 +22,15 @@
 // MFMA operand words directly.  Each limb goes through v_mfma_i32_16x16x64_i8 with exact
 // int32 sums (|sum| <= Q 128 127 < 2^23) and an fp32 epilogue recombines them.
 //
-// Both operands contract over tokens, the slow axis in memory, so x and B are transposed
-// into LDS (token-contiguous 256-byte rows).  Rows use a 16-byte-chunk XOR swizzle that
-// keeps both the transposing writes (rows 4q+i of 16 consecutive q) and the MFMA operand
-// reads (16 consecutive rows) free of bank conflicts.  Each wave owns one 16-channel tile of
-// S across all states and tokens, so every limb is built exactly once, in registers, from the
-// x^T rows right before its MFMAs.
+// Both operands contract over tokens, the slow axis in memory.  x and B are copied into LDS
+// in their natural token-major layout (16-byte pieces, XOR-swizzled per row), and the MFMA
+// operands are read with gfx950's transposing LDS read ds_read_b64_tr_b8: within a group of
+// 16 lanes, lane i receives byte (i % 8) of the 8-byte chunks addressed by lanes 2k + i / 8,
+// k = 0..7.  With lane 2k + h of a group addressing token row j0 + k at columns c0 + 8 h,
+// lane i gets the 8 tokens j0..j0+7 of column c0 + i, so two reads give a lane its 16
+// K-consecutive bytes with no byte transposes in registers.  Each wave owns one 16-channel
+// tile of S across all states and tokens, so every limb is built exactly once, in registers,
+// right before its MFMAs.
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -39,14 +42,15 @@ constexpr int kMaxP = 64;
 constexpr int kMaxN = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// byte offset of (row, token byte) in a swizzled [rows][Q] int8 matrix: 16-byte chunk c of
-// row r is stored at chunk c ^ swz(r), swz(r) < Q / 16.  For rows 4q + i (i < 4),
-// swz(4q + i) = swz(4q) ^ i (Q / 16 >= 4), so tpos(4q + i, b) = (tpos(4q, b) ^ 16 i) + Q i.
-template <int Q>
-__device__ __forceinline__ int swz(int row) { return ((row & 15) ^ ((row >> 4) & 3)) & (Q / 16 - 1); }
-template <int Q>
-__device__ __forceinline__ int tpos(int row, int byte) {
-  return row * Q + ((((byte >> 4) ^ swz<Q>(row)) << 4) | (byte & 15));
+// LDS layouts (byte offsets), token-major with the 16-byte chunks of each row XOR-swizzled so
+// that both the 16-byte copies and the transposing reads are free of bank conflicts:
+//   x codes [Q][64]:  chunk c of row j at c ^ ((j >> 2) & 3)
+//   B codes [Q][128]: chunk c of row j at c ^ ((j >> 1) & 7)
+__device__ __forceinline__ int xpos(int j, int byte) {
+  return j * kMaxP + ((((byte >> 4) ^ ((j >> 2) & 3)) << 4) | (byte & 15));
+}
+__device__ __forceinline__ int bpos(int j, int byte) {
+  return j * kMaxN + ((((byte >> 4) ^ ((j >> 1) & 7)) << 4) | (byte & 15));
 }
 
 // a * b + c for a, b < 2^24 (one v_mad_u32_u24), modulo 2^32
@@ -64,55 +68,22 @@ __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[
   out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
 }
 
-// Transposing the int8 codes of the chunk (kChan channel rows) into the swizzled
-// token-contiguous LDS matrix.  A task is 4 channels x 4 tokens; a wave's 64 lanes take 16
-// consecutive channel quads x 4 consecutive token quads, which makes the swizzled LDS writes
-// conflict-free.  The global loads are issued first (stage_load, at kernel entry) and
-// committed to LDS later (stage_commit), so their latency overlaps the chunk cumsum.  Loads
-// go through a buffer whose size ends at the chunk's last valid row, so rows past the
-// sequence end read as zeros; channel quads past `channels` use an out-of-range offset.
-template <int Q, int kChan>
+__device__ __forceinline__ v2u tr8(const uint8_t* lds_byte) {
+  return __builtin_bit_cast(v2u, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                     (__attribute__((address_space(3))) v2i*)(lds_byte)));
+}
+
+// The x and B codes of the chunk as 16-byte pieces (x: 4 per token row, B: 8), loaded at kernel
+// entry and copied to LDS after the cumsum.  Loads go through a buffer whose size ends at the
+// chunk's last valid row, so rows past the sequence end read as zeros; pieces past P or N use
+// an out-of-range offset and read as zeros too.
+template <int Q>
 struct Staged {
-  static constexpr int kXq = kChan / 4;             // channel quads (multiple of 16)
-  static constexpr int kHi = kXq / 16;
-  static constexpr int kIters = kXq * (Q / 4) / kThreads;
-  static_assert(kXq * (Q / 4) % kThreads == 0, "tasks must tile the block");
-  uint32_t v[kIters][4];
+  static constexpr int kX = Q * (kMaxP / 16) / kThreads;
+  static constexpr int kB = Q * (kMaxN / 16) / kThreads;
+  v4u x[kX];
+  v4u b[kB];
 };
-
-template <int kChan>
-__device__ __forceinline__ void task_of(int task, int& xq, int& jq) {
-  constexpr int kHi = kChan / 64;
-  const int rest = task >> 6;
-  xq = (task & 15) + 16 * (rest % kHi);
-  jq = ((task >> 4) & 3) + 4 * (rest / kHi);
-}
-
-template <int Q, int kChan>
-__device__ __forceinline__ void stage_load(Staged<Q, kChan>& st, Rsrc r, uint32_t stride, int channels, int tid) {
-#pragma unroll
-  for (int it = 0; it < Staged<Q, kChan>::kIters; ++it) {
-    int xq, jq;
-    task_of<kChan>(tid + it * kThreads, xq, jq);
-    const uint32_t o = 4 * xq < channels ? uint32_t(4 * jq) * stride + 4 * xq : kOutOfRange;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) st.v[it][rr] = buf_load4(r, o + uint32_t(rr) * stride);
-  }
-}
-
-template <int Q, int kChan>
-__device__ __forceinline__ void stage_commit(uint8_t* lds, const Staged<Q, kChan>& st, int tid) {
-#pragma unroll
-  for (int it = 0; it < Staged<Q, kChan>::kIters; ++it) {
-    int xq, jq;
-    task_of<kChan>(tid + it * kThreads, xq, jq);
-    uint32_t out[4];
-    transpose4x4(st.v[it], out);
-    const int t0 = tpos<Q>(4 * xq, 4 * jq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(lds + (t0 ^ (16 * i)) + Q * i) = out[i];
-  }
-}
 
 // 3 waves per SIMD (<= 168 VGPRs): three blocks per CU, bounded by LDS as well.
 template <int Q>
@@ -121,8 +92,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ acs, float* __restrict__ states, int64_t seqlen, int32_t nheads, int32_t headdim,
     int32_t dstate, int32_t ngroups, int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) uint8_t xT[kMaxP * Q];
-  __shared__ __attribute__((aligned(16))) uint8_t BT[kMaxN * Q];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
+  __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
   __shared__ __attribute__((aligned(16))) uint32_t om[Q];   // OM_j
   __shared__ __attribute__((aligned(16))) uint32_t cb[Q];   // CB_j
   __shared__ float red[kWaves];
@@ -144,12 +115,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   const uint32_t xrow = uint32_t(nheads * P), brow = uint32_t(ngroups * N);
   const Rsrc rdt = make_rsrc(dt + (int64_t(b) * seqlen + t0) * nheads + h, (uint32_t(len - 1) * nheads + 1u) * 4u);
   const float d = tid < Q ? buf_loadf(rdt, uint32_t(tid) * uint32_t(nheads) * 4u) : 0.f;   // 0 past the end
-  Staged<Q, kMaxP> xs;
-  Staged<Q, kMaxN> bs;
-  stage_load(xs, make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, uint32_t(len - 1) * xrow + P),
-             xrow, P, tid);
-  stage_load(bs, make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, uint32_t(len - 1) * brow + N),
-             brow, N, tid);
+  Staged<Q> st;
+  {
+    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, uint32_t(len - 1) * xrow + P);
+    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, uint32_t(len - 1) * brow + N);
+#pragma unroll
+    for (int k = 0; k < Staged<Q>::kX; ++k) {
+      const int piece = tid + k * kThreads, j = piece >> 2, cc = piece & 3;
+      st.x[k] = buf_load16(rx, 16 * cc < P ? uint32_t(j) * xrow + 16 * cc : kOutOfRange);
+    }
+#pragma unroll
+    for (int k = 0; k < Staged<Q>::kB; ++k) {
+      const int piece = tid + k * kThreads, j = piece >> 3, cc = piece & 7;
+      st.b[k] = buf_load16(rb, 16 * cc < N ? uint32_t(j) * brow + 16 * cc : kOutOfRange);
+    }
+  }
 
   // ---- (a) chunk cumsum of dt A, one token per thread of waves 0..Q/64-1
   float v = d * A[h];
@@ -184,22 +164,39 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     cb[tid] = 8421376u - (o << 7);   // 256 * 32896 - 128 OM (mod 2^32)
   }
 
-  // ---- x and B codes of the chunk, token-contiguous in LDS
-  stage_commit(xT, xs, tid);
-  stage_commit(BT, bs, tid);
+  // ---- the x and B codes of the chunk into LDS (16-byte copies)
+#pragma unroll
+  for (int k = 0; k < Staged<Q>::kX; ++k) {
+    const int piece = tid + k * kThreads;
+    *reinterpret_cast<v4u*>(xs + xpos(piece >> 2, 16 * (piece & 3))) = st.x[k];
+  }
+#pragma unroll
+  for (int k = 0; k < Staged<Q>::kB; ++k) {
+    const int piece = tid + k * kThreads;
+    *reinterpret_cast<v4u*>(bs + bpos(piece >> 3, 16 * (piece & 7))) = st.b[k];
+  }
   __syncthreads();
 
   // ---- S tiles on the zero-padded 64 x 128 space: wave w owns channel tile w and all eight
-  // 16-state tiles; the K loop is unrolled, its first step starts the accumulators
+  // 16-state tiles; the K loop is unrolled, its first step starts the accumulators.
   const int lcol = lane % 16, kg = lane / 16;
   const int pt = wave;
   constexpr int kNt = kMaxN / 16;
+  // transposing-read addresses: lane 2k + h of its group addresses token row 16 kg + k (+ 8 for
+  // the second read) at column 16 tile + 8 h; the K step adds 64 rows (a constant offset)
+  const int rowb = 16 * kg + (lcol >> 1), half8 = 8 * (lcol & 1);
+  const int xa0 = xpos(rowb, 16 * pt + half8), xa1 = xpos(rowb + 8, 16 * pt + half8);
+  // B: bpos(rowb + 8 hh, 16 t + half8) = ba[t ^ 4 hh] + 8 hh * 128, since the row swizzle of
+  // rowb + 8 is that of rowb with bit 2 flipped
+  int ba[kNt];
+#pragma unroll
+  for (int t = 0; t < kNt; ++t) ba[t] = bpos(rowb, 16 * t + half8);
   v4i acc[kNt][3];
-  const int p = 16 * pt + lcol;
 #pragma unroll
   for (int kb = 0; kb < Q; kb += 64) {
     const int j0 = kb + 16 * kg;
-    const v4u xw = *reinterpret_cast<const v4u*>(xT + tpos<Q>(p, j0));
+    const v2u xlo = tr8(xs + xa0 + kb * kMaxP), xhi = tr8(xs + xa1 + kb * kMaxP);
+    const uint32_t xw[4] = {xlo[0], xlo[1], xhi[0], xhi[1]};   // tokens j0..j0+15 of channel p
     v4i l1, l2, l3;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
@@ -218,7 +215,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     }
 #pragma unroll
     for (int t = 0; t < kNt; ++t) {
-      const v4i bop = *reinterpret_cast<const v4i*>(BT + tpos<Q>(16 * t + lcol, j0));
+      const v2u blo = tr8(bs + ba[t] + kb * kMaxN), bhi = tr8(bs + ba[t ^ 4] + (kb + 8) * kMaxN);
+      const v4i bop = {int(blo[0]), int(blo[1]), int(bhi[0]), int(bhi[1])};
       const v4i z = {0, 0, 0, 0};
       acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, bop, kb == 0 ? z : acc[t][0], 0, 0, 0);
       acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l2, bop, kb == 0 ? z : acc[t][1], 0, 0, 0);
@@ -230,16 +228,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   if (16 * pt >= P) return;
   const float post = x_scale[h] * B_scale[g] * exp2i(e);
   const float post_lo = post * (1.f / 65536.f);
-  float* Sc = states + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N + int64_t(16 * pt) * N;
-  const uint32_t lane_off = uint32_t(4 * kg) * uint32_t(N) + lcol;
+  // buffer stores: lane offset + row offset (scalar) + state-tile offset (immediate)
+  const Rsrc rs = make_rsrc(states + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N, uint32_t(P * N) * 4u);
+  const uint32_t lane_off = (uint32_t(16 * pt + 4 * kg) * uint32_t(N) + lcol) * 4u;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float* Srow = Sc + int64_t(i) * N;   // uniform
+    const int row_off = i * N * 4;   // uniform
 #pragma unroll
     for (int t = 0; t < kNt; ++t) {
       if (16 * t >= N) break;
       const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];   // exact: |lo| < 2^31
-      Srow[lane_off + 16 * t] = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+      const float sv = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), rs, lane_off + 64u * t, row_off, 0);
     }
   }
 }
