@@ -36,10 +36,19 @@ constexpr int kMaxP = 64;
 constexpr int kMaxN = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// x^T: [p][j] fp16, rows padded to 264 halves (528 bytes = 132 banks, i.e. 4 banks apart),
-// so the hot-loop reads of 16 consecutive rows are conflict-free with linear addresses
-constexpr int kXS = kMaxQ + 8;
-__device__ __forceinline__ int xpos(int p, int j) { return p * kXS + j; }
+// x: [j][p] fp16 (token-major, 128-byte rows), 16-byte chunk c of row j stored at c ^ xswz(j),
+// xswz(j) = 4 bit2(j) + 3 bit1(j): with this swizzle the 16-byte commit stores and the
+// transposing operand reads (ds_read_b64_tr_b16) are both free of bank conflicts.
+__device__ __forceinline__ int xswz(int j) { return (((j >> 2) & 1) << 2) | (((j >> 1) & 1) * 3); }
+__device__ __forceinline__ int xpos(int j, int p) { return j * kMaxP + ((((p >> 3) ^ xswz(j)) << 3) | (p & 7)); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i % 4 of the
+// 8-byte chunks addressed by lanes 4 k + i / 4, k = 0..3.  With lane 4 k + q of a group
+// addressing x[j0 + k][16 pt + 4 q], lane i gets x[j0 + k][16 pt + i] for k = 0..3.
+__device__ __forceinline__ v4h tr16(const _Float16* lds) {
+  return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                     (__attribute__((address_space(3))) v4s*)(lds)));
+}
 // B codes: [j][n] int8, 128-byte rows, chunk c stored at c ^ ((j >> 1) & 7)
 __device__ __forceinline__ int bpos(int j, int byte) {
   return j * kMaxN + ((((byte >> 4) ^ ((j >> 1) & 7)) << 4) | (byte & 15));
@@ -89,12 +98,13 @@ __device__ __forceinline__ Item item_of(int it, int nheads, int nchunks, int ngr
 // Global data of one work item held in registers between its load and its LDS commit.
 constexpr int kBTasks = kMaxQ * 8 / kThreads;          // 16-byte B pieces per thread
 constexpr int kHTasks = 2 * kMaxP * 8 / kThreads;      // 16-byte Hprev-limb pieces per thread
-constexpr int kXTasks = 16 * (kMaxQ / 4) / kThreads;   // 4x4 x transposition tasks per thread
+constexpr int kXTasks = kMaxQ * (kMaxP / 16) / kThreads;   // 16-byte x pieces per thread
 struct Prefetch {
   float acs, dt, hs;
+  v4i cq[2][2];                 // C codes of this lane's two output rows (per pass, K half)
   v4u bq[kBTasks];
   v4u hq[kHTasks];
-  uint32_t xw[kXTasks][4];
+  v4u xq[kXTasks];
 };
 
 struct Params {
@@ -122,8 +132,8 @@ struct LaneConst {
   int b_lds[kBTasks];
   uint32_t h_off[kHTasks];      // Hprev-limb piece in its (b, c, h) block
   int h_lds[kHTasks];
-  uint32_t x_off[kXTasks];      // first row (4 jq) of an x transposition task, channel quad
-  int x_lds[kXTasks];
+  uint32_t x_off[kXTasks];      // x piece: token row j * H*P + 16-byte column group
+  int x_lds[kXTasks];           // LDS position (halves) of its first 8 channels
   uint32_t c_off[2][2];         // C codes of this lane's output row, per pass and K half
   uint32_t acs_off, dt_off, hs_off;
 };
@@ -131,7 +141,7 @@ struct LaneConst {
 // Buffer resources of one item: base at the item's first element, size up to the end of its
 // last valid row.
 struct ItemRsrc {
-  Rsrc acs, dt, hs, B, H, x;
+  Rsrc acs, dt, hs, B, H, x, C;
 };
 
 __device__ __forceinline__ ItemRsrc item_rsrc(const Item& it, const Params& a) {
@@ -145,6 +155,7 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const Item& it, const Params& a) {
   r.H = make_rsrc(a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N,
                   uint32_t(2 * P * N));
   r.x = make_rsrc(a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P, last * uint32_t(H * P) + P);
+  r.C = make_rsrc(a.C + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N, last * uint32_t(G * N) + N);
   return r;
 }
 
@@ -154,17 +165,19 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
   f.dt = buf_loadf(r.dt, lc.dt_off);
   f.hs = buf_loadf(r.hs, lc.hs_off);
 #pragma unroll
+  for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) f.cq[pass][s2] = __builtin_bit_cast(v4i, buf_load16(r.C, lc.c_off[pass][s2]));
+#pragma unroll
   for (int k = 0; k < kBTasks; ++k) f.bq[k] = buf_load16(r.B, lc.b_off[k]);
 #pragma unroll
   for (int k = 0; k < kHTasks; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
 #pragma unroll
-  for (int k = 0; k < kXTasks; ++k)
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) f.xw[k][rr] = buf_load4(r.x, lc.x_off[k] + uint32_t(rr) * xrow);
+  for (int k = 0; k < kXTasks; ++k) f.xq[k] = buf_load16(r.x, lc.x_off[k]);
 }
 
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
-  __shared__ __attribute__((aligned(16))) _Float16 xT[kMaxP * kXS];
+  __shared__ __attribute__((aligned(16))) _Float16 xs[kMaxQ * kMaxP];
   __shared__ __attribute__((aligned(16))) int8_t Bs[kMaxQ * kMaxN];
   __shared__ __attribute__((aligned(16))) int8_t Hq[2 * kHPlane];
   __shared__ __attribute__((aligned(16))) float hsc[kMaxP];
@@ -197,14 +210,12 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     lc.h_off[k] = (p < P && 16 * sg < N) ? uint32_t(limb * P * N + p * N + 16 * sg) : kOutOfRange;
     lc.h_lds[k] = limb * kHPlane + hpos(p, 16 * sg);
   }
-  {
-    const int pq = tid & 15;
 #pragma unroll
-    for (int k = 0; k < kXTasks; ++k) {
-      const int jq = (tid + k * kThreads) >> 4;
-      lc.x_off[k] = 4 * pq < P ? uint32_t(4 * jq) * xrow + 4 * pq : kOutOfRange;
-      lc.x_lds[k] = xpos(4 * pq, 4 * jq);
-    }
+  for (int k = 0; k < kXTasks; ++k) {
+    const int piece = tid + k * kThreads;
+    const int j = piece >> 2, cc = piece & 3;
+    lc.x_off[k] = 16 * cc < P ? uint32_t(j) * xrow + 16 * cc : kOutOfRange;
+    lc.x_lds[k] = xpos(j, 16 * cc);
   }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -221,7 +232,11 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // on lcol only, so every hot-loop address is a per-lane base plus a multiple of the step
   const int8_t* bs_lane = Bs + bpos(lcol, 16 * kg);                    // + js * 128
   const int bs_half = bpos(lcol, 64 + 16 * kg) - bpos(lcol, 16 * kg);   // second K half
-  const _Float16* xt_lane = xT + xpos(lcol, 4 * kg);                    // + 16 pt rows, + jb
+  // transposing x reads: lane 4 k + q of its group addresses token row 4 kg + k at channels
+  // 16 pt + 4 q; a step adds whole 32-token blocks (the swizzle repeats every 8 rows)
+  int xa[4];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) xa[pt] = xpos(4 * kg + (lcol >> 2), 16 * pt + 4 * (lcol & 3));
   float* wlw = wl[wave];
   const float* wl_lane = wlw + 4 * kg;
   int hq_lane[2][4];
@@ -262,25 +277,21 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     for (int k = 0; k < kHTasks; ++k) *reinterpret_cast<v4u*>(Hq + lc.h_lds[k]) = f.hq[k];
 #pragma unroll
     for (int k = 0; k < kXTasks; ++k) {
-      uint32_t in[4], out[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) in[r] = f.xw[k][r] ^ 0x80808080u;
-      transpose4x4(in, out);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<v4h*>(xT + lc.x_lds[k] + i * kXS) = codes_to_f16(out[i]);
+      const v4u u = f.xq[k] ^ 0x80808080u;
+      const v4h h0 = codes_to_f16(u[0]), h1 = codes_to_f16(u[1]), h2 = codes_to_f16(u[2]), h3 = codes_to_f16(u[3]);
+      *reinterpret_cast<v8h*>(xs + lc.x_lds[k]) = v8h{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      // the second 8 channels: chunk + 1 before the swizzle
+      *reinterpret_cast<v8h*>(xs + (lc.x_lds[k] ^ 8)) = v8h{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
     }
     __syncthreads();
 
-    // ---- loads the current item still needs, for both of this wave's row blocks.  They are
-    // issued and consumed before the next item's prefetch: vmcnt retires in order, so any
-    // wait on a load issued after the prefetch would also wait for the prefetch.
-    const Rsrc crs = make_rsrc(a.C + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.ngroups + cur.g) * N,
-                               uint32_t(len - 1) * gn + N);
+    // ---- the C codes of this lane's output rows arrived with the prefetch; keep them before the
+    // next item's prefetch reuses the registers
     v4i cqs[2][2];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = __builtin_bit_cast(v4i, buf_load16(crs, lc.c_off[pass][s2]));
+      for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = f.cq[pass][s2];
     const int hu = __builtin_amdgcn_readfirstlane(cur.h);
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
     const float sx = a.x_scale[hu], sB = a.B_scale[gu], sC = a.C_scale[gu];
@@ -297,21 +308,30 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     float dtmax = red[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) dtmax = fmaxf(dtmax, red[i]);
-    // |M'| <= N 127^2 dtmax 2^-kM <= 2^15; clamped so that 2^kM and 2^-kM are exact
-    const int kM = min(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, -120), 120);
-    const float s_in = sx * sC * sB * exp2i(kM);
+    // Power-of-two guard 2^-kM on the fp16 operand M': the masked C.B^T entries stay within
+    // |M'| <= N 127^2 dtmax 2^-kM <= 2^15 and the D term folded into its diagonal within
+    // |D'| = |D| / (sC sB) 2^-kM <= 2^14, so their sum is a finite fp16.  Clamped so that 2^kM
+    // and 2^-kM are exact.
+    const float sCB = sC * sB;
+    const int kM = min(max(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, ceil_log2_pos(fabsf(Dh) / sCB) - 14),
+                           -120), 120);
+    const float s_in = sx * sCB * exp2i(kM);
     const float fkM = float(kM);
-    const float sxD = sx * Dh;
+    const float Dp = Dh / sCB * exp2i(-kM);   // D' (0 without D)
 
-#pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int lb = pass == 0 ? wave : 2 * kWaves - 1 - wave;
-      if (lb >= nlb || (pass == 1 && nlb <= kWaves)) continue;
+    // The lane index is re-materialized per item (an empty asm makes it opaque), so that the
+    // per-lane masks below (causal mask, store guards) are recomputed with a few compares
+    // instead of being hoisted out of the item loop into scalar registers that would spill.
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
+    const int lcol_v = lane_v & 15, kg_v = lane_v >> 4;
+
+    auto do_pass = [&](const int lb, const v4i (&cq)[2]) {
       const int l0 = 16 * lb;
-      const int l = l0 + lcol;
+      const int l = l0 + lcol_v;
       const bool lvalid = l < len;
-      const v4i cq[2] = {pass == 0 ? cqs[0][0] : cqs[1][0], pass == 0 ? cqs[0][1] : cqs[1][1]};
       const int jdiag = l0 & ~31;          // the 32-token block that holds the diagonal
+      const bool half = l0 != jdiag;       // its first 16 tokens lie before row l0
       const float a_l = acs2[l];
       const float a_0 = acs2[l0];
 
@@ -320,26 +340,30 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       __builtin_amdgcn_wave_barrier();
       const float u_l = __builtin_amdgcn_exp2f(a_l - a_0);
 
-      v4f yf[4], yd[4];
+      // carried state read out by C on the INT8 matrix cores: y_off^T[p][l] =
+      // exp(Acs_l) sC hs_p / 256 * (256 yo1 + yo2).  It starts the accumulator of the blocks
+      // before the diagonal, which the epilogue scales by u_l s_in = exp(Acs_l - Acs_l0) s_in,
+      // hence the factor kap_p = exp(Acs_l0) sC hs_p / (256 s_in).
       v4i yo1[4], yo2[4];
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        yf[pt] = v4f{0.f, 0.f, 0.f, 0.f};
-        yd[pt] = v4f{0.f, 0.f, 0.f, 0.f};
-        yo1[pt] = v4i{0, 0, 0, 0};
-        yo2[pt] = v4i{0, 0, 0, 0};
-      }
-
-      // carried state read out by C: y_off^T[p][l] = sum_n Hprev[p][n] q_C[l][n], both limbs
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
           const v4i h1 = *reinterpret_cast<const v4i*>(Hq + hq_lane[s2][pt]);
           const v4i h2 = *reinterpret_cast<const v4i*>(Hq + kHPlane + hq_lane[s2][pt]);
-          yo1[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h1, cq[s2], yo1[pt], 0, 0, 0);
-          yo2[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h2, cq[s2], yo2[pt], 0, 0, 0);
+          const v4i z = {0, 0, 0, 0};
+          yo1[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h1, cq[s2], s2 == 0 ? z : yo1[pt], 0, 0, 0);
+          yo2[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h2, cq[s2], s2 == 0 ? z : yo2[pt], 0, 0, 0);
         }
+      }
+      const float E = __builtin_amdgcn_exp2f(fminf(a_0, 0.f)) * sC / (256.f * s_in);
+      v4f yf[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
+        const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) yf[pt][i] = float((yo1[pt][i] << 8) + yo2[pt][i]) * (E * hv[i]);
       }
 
       // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized decay
@@ -360,9 +384,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         v8h xop[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const _Float16* xp = xt_lane + 16 * pt * kXS + jb;
-          const v4h lo = *reinterpret_cast<const v4h*>(xp);
-          const v4h hi = *reinterpret_cast<const v4h*>(xp + 16);
+          const v4h lo = tr16(xs + xa[pt] + jb * kMaxP);
+          const v4h hi = tr16(xs + xa[pt] + (jb + 16) * kMaxP);
           xop[pt] = v8h{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
         v8h mop;
@@ -377,10 +400,14 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         for (int pt = 0; pt < 4; ++pt)
           yf[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[pt], mop, yf[pt], 0, 0, 0);
       }
-      // the block holding the diagonal: exact per-element decay and the causal mask
+
+      // the block holding the diagonal, exact per-element decay: sub-block 0 (tokens jdiag..+15)
+      // lies before row l0 when `half`, else it holds the diagonal and sub-block 1 is masked
+      // entirely; the diagonal sub-block gets the causal mask and D' on j == l.
+      v4f yd[4];
       {
         const int jb = jdiag;
-        const int j1 = min(jb + 16, Q - 16);   // second sub-block (fully masked when clamped)
+        const int j1 = min(jb + 16, Q - 16);   // sub-block 1 (fully masked when clamped)
         v4i gm[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -394,6 +421,12 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         v8h mop;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
+          const bool diag_sb = half ? sb == 1 : sb == 0;
+          if (!half && sb == 1) {   // entirely after the block's rows
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mop[4 + i] = _Float16(0.f);
+            continue;
+          }
           const int jq = (sb == 0 ? jb : j1) + 4 * kg;
           const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
           const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
@@ -401,44 +434,38 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
           const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int j = jb + 16 * sb + 4 * kg + i;     // > l (masked) whenever the clamp applied
-            const float m = float(gm[sb][i]) * __builtin_amdgcn_exp2f(fminf(a_lk - av[i], -fkM)) * dv[i];
-            mop[4 * sb + i] = _Float16(j <= l ? m : 0.f);
+            float m = float(gm[sb][i]) * __builtin_amdgcn_exp2f(fminf(a_lk - av[i], -fkM)) * dv[i];
+            if (diag_sb) {
+              const int j = jb + 16 * sb + 4 * kg_v + i;
+              m = j < l ? m : (j == l ? m + Dp : 0.f);
+            }
+            mop[4 * sb + i] = _Float16(m);
           }
         }
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const _Float16* xp = xt_lane + 16 * pt * kXS;
-          const v4h lo = *reinterpret_cast<const v4h*>(xp + jb);
-          const v4h hi = *reinterpret_cast<const v4h*>(xp + j1);
+          const v4h lo = tr16(xs + xa[pt] + jb * kMaxP);
+          const v4h hi = tr16(xs + xa[pt] + j1 * kMaxP);
           const v8h xop = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          yd[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, yd[pt], 0, 0, 0);
+          yd[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, mop, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
       }
 
       // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
-      const float s_off = __builtin_amdgcn_exp2f(fminf(a_l, 0.f)) * sC;
       const float c_f = u_l * s_in;
       _Float16* yrow = ybase + uint32_t(min(l, len - 1)) * uint32_t(a.nheads * P);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
-        const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
         v4h out;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = 16 * pt + 4 * kg + i;
-          const float c1 = s_off * hv[i];
-          float v = float(xT[xpos(p, l)]) * sxD;
-          v = fmaf(float(yo2[pt][i]), c1 * (1.f / 256.f), v);
-          v = fmaf(float(yo1[pt][i]), c1, v);
-          v = fmaf(yd[pt][i], s_in, v);
-          v = fmaf(yf[pt][i], c_f, v);
-          out[i] = _Float16(v);
-        }
-        if (lvalid && 16 * pt + 4 * kg < P) *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg) = out;
+        for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(yf[pt][i], c_f, yd[pt][i] * s_in));
+        if (lvalid && 16 * pt + 4 * kg_v < P) *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg_v) = out;
       }
-    }
+    };
+
+    // two 16-row blocks per wave, l and 15 - l (balanced work)
+    if (wave < nlb) do_pass(wave, cqs[0]);
+    if (nlb > kWaves) do_pass(2 * kWaves - 1 - wave, cqs[1]);
     __syncthreads();   // LDS is rewritten by the next item's commit
   }
 }
