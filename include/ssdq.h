@@ -78,7 +78,9 @@ ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int6
  *   Hprev   int8 (batch, nchunks, nheads, 2, headdim, dstate) and
  *   Hscale  fp32 (batch, nchunks, nheads, headdim): the state entering each chunk is
  *           (Hprev[..., 0, p, n] + Hprev[..., 1, p, n] / 256) * Hscale[..., p], two INT8
- *           limbs with a power-of-two scale per state row           -- written by stage 1 */
+ *           limbs with a power-of-two scale per state row           -- written by stage 1
+ * When ssdq_chunk_scan_state_fused(batch, nheads) is 1, stage 0 writes Acs, Hprev, Hscale
+ * (and h_final) itself, stage 1 does nothing, and S is not written. */
 size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                       int32_t dstate, int32_t chunk);
 
@@ -117,6 +119,15 @@ ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t*
 /* Number of stages ssdq_chunk_scan runs, in order: 0 chunk cumsum + chunk state,
  * 1 state passing, 2 chunk output. */
 #define SSDQ_CHUNK_SCAN_STAGES 3
+
+/*
+ * 1 if, on the current device, ssdq_chunk_scan folds state passing into stage 0 for this
+ * batch and head count, else 0 (also for non-positive arguments or without a device).
+ * Folding applies when batch * nheads is at least the device's CU count: one block per
+ * (batch, head) sequence then walks its chunks in order (Mamba-2 SSD state passing,
+ * Ternary Mamba sec. 1 recurrence per chunk) and the fp32 chunk states never reach memory.
+ */
+int32_t ssdq_chunk_scan_state_fused(int32_t batch, int32_t nheads);
 
 /*
  * One stage of ssdq_chunk_scan, with the same arguments and validation.

@@ -44,12 +44,20 @@ lib.ssdq_chunk_scan_stage.argtypes = [_i32] + _SCAN_ARGS
 lib.ssdq_chunk_scan_stage.restype = ctypes.c_int
 lib.ssdq_state_update.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update.restype = ctypes.c_int
+lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
+lib.ssdq_chunk_scan_state_fused.restype = _i32
 
 
 class SSDQError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {status_string(status)}")
+
+
+def chunk_scan_state_fused(batch: int, nheads: int) -> bool:
+    """True when, on the current device, stage 0 of the chunk scan also carries the state across
+    chunks (stage 1 then does nothing and the chunk states are not written)."""
+    return bool(lib.ssdq_chunk_scan_state_fused(batch, nheads))
 
 
 def status_string(status: int) -> str:

@@ -244,6 +244,292 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Stages 0 and 1 fused, for shapes with at least one (batch, head) sequence per CU: one block
+// per (batch, head) walks the chunks in order and carries the running state H in registers,
+//
+//   Hprev_c = H (written as two INT8 limbs + a power-of-two row scale, as stage 1 writes it),
+//   H <- exp(Acs_c[last]) H + S_c,
+//
+// with S_c from the same INT8-limb MFMAs as above, so the fp32 chunk states never leave the
+// CU.  S_c is computed transposed (the B codes as the A operand), so that a lane holds four
+// consecutive states n = 16 t + 4 kg + i of one channel row p = 16 pt + lcol: the limb bytes of
+// four states are one 4-byte store and the row max is a short shuffle.  Eight waves: waves w and
+// w + 4 own channel tile w % 4 and split the chunk's 64-token steps between them (no limb is
+// built twice); each converts its partial S to fp32, hands the other the half of the state
+// tiles it does not own through LDS, and updates its own half of H.  The next chunk's dt, x and
+// B loads are issued before the current chunk's MFMAs.
+constexpr int kSThreads = 512;
+constexpr int kSWaves = kSThreads / kWave;
+
+template <int Q>
+struct StagedS {
+  static constexpr int kX = (Q * (kMaxP / 16) + kSThreads - 1) / kSThreads;
+  static constexpr int kB = (Q * (kMaxN / 16) + kSThreads - 1) / kSThreads;
+  v4u x[kX];
+  v4u b[kB];
+};
+
+template <int Q>
+__global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(2))) state_scan_kernel(
+    const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
+    const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ A,
+    const float* h0, float* h_final, float* __restrict__ acs, int8_t* __restrict__ hprev,
+    float* __restrict__ hscale, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+    int32_t ngroups, int32_t nchunks) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
+  __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
+  __shared__ __attribute__((aligned(16))) uint32_t om[Q];
+  __shared__ __attribute__((aligned(16))) uint32_t cb[Q];
+  __shared__ __attribute__((aligned(16))) v4f xch[kSWaves][4][kWave];   // partial S handed over
+  __shared__ float rmax[2][kMaxP];                                      // half-row maxima
+  __shared__ float red[kSWaves];
+  __shared__ float acs_last_s;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = bh % nheads;
+  const int b = bh / nheads;
+  const int g = h / (nheads / ngroups);
+  const int P = headdim, N = dstate;
+  const int lcol = lane % 16, kg = lane / 16;
+  const int pt = wave & 3, kh = wave >> 2;   // channel tile; half of the K steps and of the state tiles
+  constexpr int kNt = kMaxN / 16;
+  constexpr int kOwn = kNt / 2;               // state tiles 4 kh .. 4 kh + 3 belong to this wave
+  const bool prow = 16 * pt < P;               // this wave's channel tile exists (uniform)
+  const uint32_t xrow = uint32_t(nheads * P), brow = uint32_t(ngroups * N);
+  const float sxB = x_scale[h] * B_scale[g];
+  const float Ah = A[h];
+
+  // ---- running state H[p = 16 pt + lcol][n = 16 (4 kh + t) + 4 kg + i], own tiles t = 0..3
+  const int64_t pn = int64_t(P) * N;
+  const uint32_t hoff = (uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh + 4 * kg) * 4u;   // bytes
+  v4f H[kOwn];
+  {
+    const Rsrc r0 = make_rsrc(h0 ? h0 + int64_t(bh) * pn : h0, h0 && prow ? uint32_t(pn) * 4u : 0u);
+#pragma unroll
+    for (int t = 0; t < kOwn; ++t)
+      H[t] = __builtin_bit_cast(v4f, buf_load16(r0, 16 * (kOwn * kh + t) < N ? hoff + 64u * t : kOutOfRange));
+  }
+
+  // ---- chunk loads (dt of this thread's token, x and B codes), for chunk c; a chunk past the
+  // end gets empty buffers (its loads return zeros and touch no memory)
+  float dnext;
+  StagedS<Q> st;
+  auto load_chunk = [&](int c) {
+    const bool ok = c < nchunks;
+    const int64_t t0 = ok ? int64_t(c) * Q : 0;
+    const int len = ok ? int(seqlen - t0 < Q ? seqlen - t0 : Q) : 1;
+    const Rsrc rdt = make_rsrc(dt + (int64_t(b) * seqlen + t0) * nheads + h, ok ? (uint32_t(len - 1) * nheads + 1u) * 4u : 0u);
+    dnext = buf_loadf(rdt, tid < Q ? uint32_t(tid) * uint32_t(nheads) * 4u : kOutOfRange);
+    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, ok ? uint32_t(len - 1) * xrow + P : 0u);
+    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, ok ? uint32_t(len - 1) * brow + N : 0u);
+#pragma unroll
+    for (int k = 0; k < StagedS<Q>::kX; ++k) {
+      const int piece = tid + k * kSThreads, j = piece >> 2, cc = piece & 3;
+      st.x[k] = buf_load16(rx, (16 * cc < P && j < Q) ? uint32_t(j) * xrow + 16 * cc : kOutOfRange);
+    }
+#pragma unroll
+    for (int k = 0; k < StagedS<Q>::kB; ++k) {
+      const int piece = tid + k * kSThreads, j = piece >> 3, cc = piece & 7;
+      st.b[k] = buf_load16(rb, (16 * cc < N && j < Q) ? uint32_t(j) * brow + 16 * cc : kOutOfRange);
+    }
+  };
+  load_chunk(0);
+
+  // transposing-read addresses (as in the kernel above)
+  const int rowb = 16 * kg + (lcol >> 1), half8 = 8 * (lcol & 1);
+  const int xa0 = xpos(rowb, 16 * pt + half8), xa1 = xpos(rowb + 8, 16 * pt + half8);
+  int ba[kNt];
+#pragma unroll
+  for (int t = 0; t < kNt; ++t) ba[t] = bpos(rowb, 16 * t + half8);
+
+  // one 64-token step of S^T into acc (first step starts the accumulators)
+  v4i acc[kNt][3];
+  auto kstep = [&](int kb, bool first) {
+    const int j0 = kb + 16 * kg;
+    const v2u xlo = tr8(xs + xa0 + kb * kMaxP), xhi = tr8(xs + xa1 + kb * kMaxP);
+    const uint32_t xw[4] = {xlo[0], xlo[1], xhi[0], xhi[1]};
+    v4i l1, l2, l3;
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      const v4u o4 = *reinterpret_cast<const v4u*>(&om[j0 + 4 * dw]);
+      const v4u c4 = *reinterpret_cast<const v4u*>(&cb[j0 + 4 * dw]);
+      const uint32_t u = xw[dw] ^ 0x80808080u;
+      uint32_t W[4], pl[4];
+      W[0] = mad24(u & 0xffu, o4[0], c4[0]);
+      W[1] = mad24((u >> 8) & 0xffu, o4[1], c4[1]);
+      W[2] = mad24((u >> 16) & 0xffu, o4[2], c4[2]);
+      W[3] = mad24(u >> 24, o4[3], c4[3]);
+      transpose4x4(W, pl);
+      l1[dw] = int(pl[3]);
+      l2[dw] = int(pl[2] ^ 0x80808080u);
+      l3[dw] = int(pl[1] ^ 0x80808080u);
+    }
+#pragma unroll
+    for (int t = 0; t < kNt; ++t) {
+      const v2u blo = tr8(bs + ba[t] + kb * kMaxN), bhi = tr8(bs + ba[t ^ 4] + (kb + 8) * kMaxN);
+      const v4i bop = {int(blo[0]), int(blo[1]), int(bhi[0]), int(bhi[1])};
+      const v4i z = {0, 0, 0, 0};
+      acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l1, first ? z : acc[t][0], 0, 0, 0);
+      acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l2, first ? z : acc[t][1], 0, 0, 0);
+      acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l3, first ? z : acc[t][2], 0, 0, 0);
+    }
+  };
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t t0 = int64_t(c) * Q;
+    const int len = int(seqlen - t0 < Q ? seqlen - t0 : Q);
+    const float d = tid < len ? dnext : 0.f;
+
+    // ---- (a) chunk cumsum of dt A, one token per thread of waves 0..Q/64-1
+    float v = d * Ah;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float up = __shfl_up(v, o, kWave);
+      if (lane >= o) v += up;
+    }
+    if (lane == kWave - 1) red[wave] = v;
+    __syncthreads();   // also: every wave is done with the previous chunk's LDS tiles
+    float pre = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kSWaves - 1; ++w2) pre += w2 < wave ? red[w2] : 0.f;
+    const float acs_t = v + pre;
+    if (tid < Q) acs[((int64_t(b) * nheads + h) * nchunks + c) * Q + tid] = acs_t;
+    if (tid == len - 1) acs_last_s = acs_t;
+    // the x and B codes of the chunk into LDS (16-byte copies)
+#pragma unroll
+    for (int k = 0; k < StagedS<Q>::kX; ++k) {
+      const int piece = tid + k * kSThreads;
+      if (piece < Q * 4) *reinterpret_cast<v4u*>(xs + xpos(piece >> 2, 16 * (piece & 3))) = st.x[k];
+    }
+#pragma unroll
+    for (int k = 0; k < StagedS<Q>::kB; ++k) {
+      const int piece = tid + k * kSThreads;
+      if (piece < Q * 8) *reinterpret_cast<v4u*>(bs + bpos(piece >> 3, 16 * (piece & 7))) = st.b[k];
+    }
+    __syncthreads();
+
+    // ---- LUT_state weights and their power-of-two range
+    const float a_last = acs_last_s;
+    const float w = d > 0.f ? __builtin_amdgcn_exp2f((a_last - acs_t) * kLog2e) * d : 0.f;
+    const float wm = wave_max(w);
+    __syncthreads();   // red[] reuse
+    if (lane == 0) red[wave] = wm;
+    // half-row maxima of the state entering the chunk (own 16 states x the 4 lanes of the row)
+    float m = 0.f;
+#pragma unroll
+    for (int t = 0; t < kOwn; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    if (kg == 0) rmax[kh][16 * pt + lcol] = m;
+    __syncthreads();
+    float wmax = red[0];
+#pragma unroll
+    for (int i = 1; i < kSWaves; ++i) wmax = fmaxf(wmax, red[i]);
+    const int e = min(max(ceil_log2_pos(wmax), -100), 100);
+    if (tid < Q) {
+      const uint32_t o = uint32_t(fminf(w * exp2i(24 - e), 16777215.f) + 0.5f);
+      om[tid] = o;
+      cb[tid] = 8421376u - (o << 7);
+    }
+
+    // ---- the state entering the chunk, Hprev_c = H, as two INT8 limbs and a power-of-two row scale
+    if (prow) {
+      m = fmaxf(rmax[0][16 * pt + lcol], rmax[1][16 * pt + lcol]);
+      const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
+      const float inv = exp2i(8 - ex);
+      const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
+      const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
+      const uint32_t loff = uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh + 4 * kg;
+#pragma unroll
+      for (int t = 0; t < kOwn; ++t) {
+        if (16 * (kOwn * kh + t) >= N) break;
+        uint32_t q1 = 0, q2 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t V = int32_t(fmaf(H[t][i], inv, 128.f));   // 256 t + 128, |t| <= 127
+          q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
+          q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(q1, rh, loff + 16u * t, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(q2, rh, loff + 16u * t, int(pn), 0);
+      }
+      if (kh == 0 && kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
+    }
+    __syncthreads();   // om / cb visible; rmax read
+
+    // ---- next chunk's loads, in flight during this chunk's MFMAs
+    load_chunk(c + 1);
+
+    // ---- S_c^T partial over this wave's 64-token steps (interleaved between the two waves)
+    if constexpr (Q == 64) {
+      if (kh == 0) {
+        kstep(0, true);
+      } else {
+#pragma unroll
+        for (int t = 0; t < kNt; ++t)
+#pragma unroll
+          for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
+      }
+    } else {
+      kstep(64 * kh, true);
+      if constexpr (Q == 256) kstep(64 * kh + 128, false);
+    }
+
+    // ---- fp32 partials; hand over the other wave's tiles, then H <- exp(Acs_last) H + S_c
+    const float post = sxB * exp2i(e);
+    const float post_lo = post * (1.f / 65536.f);
+    auto partial = [&](int t) {
+      v4f r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
+        r[i] = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+      }
+      return r;
+    };
+    // (wave-uniform branches with constant tile indices keep acc in registers)
+    if (kh == 0) {
+#pragma unroll
+      for (int t = 0; t < kOwn; ++t) xch[wave][t][lane] = partial(kOwn + t);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kOwn; ++t) xch[wave][t][lane] = partial(t);
+    }
+    v4f mine[kOwn];
+    if (kh == 0) {
+#pragma unroll
+      for (int t = 0; t < kOwn; ++t) mine[t] = partial(t);
+    } else {
+#pragma unroll
+      for (int t = 0; t < kOwn; ++t) mine[t] = partial(kOwn + t);
+    }
+    __syncthreads();
+    const float decay = __builtin_amdgcn_exp2f(a_last * kLog2e);
+#pragma unroll
+    for (int t = 0; t < kOwn; ++t) {
+      const v4f other = xch[wave ^ 4][t][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) H[t][i] = fmaf(decay, H[t][i], mine[t][i] + other[i]);
+    }
+  }
+
+  // ---- final state
+  if (h_final && prow) {
+    const Rsrc rf = make_rsrc(h_final + int64_t(bh) * pn, uint32_t(pn) * 4u);
+#pragma unroll
+    for (int t = 0; t < kOwn; ++t) {
+      if (16 * (kOwn * kh + t) >= N) break;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, H[t]), rf, hoff + 64u * t, 0, 0);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
@@ -256,6 +542,33 @@ hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t
     case 64: go(chunk_state_kernel<64>); break;
     case 128: go(chunk_state_kernel<128>); break;
     default: go(chunk_state_kernel<256>); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssdq
+
+namespace ssdq {
+
+bool state_scan_fused(int32_t batch, int32_t nheads) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess)
+    return false;
+  return cus > 0 && int64_t(batch) * nheads >= cus;
+}
+
+hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
+  const int nblocks = s.batch * s.nheads;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kSThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale, a.dt, a.A,
+                       a.h0, a.h_final, a.acs, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim, s.dstate,
+                       s.ngroups, s.nchunks);
+  };
+  switch (s.chunk) {
+    case 64: go(state_scan_kernel<64>); break;
+    case 128: go(state_scan_kernel<128>); break;
+    default: go(state_scan_kernel<256>); break;
   }
   return hipGetLastError();
 }

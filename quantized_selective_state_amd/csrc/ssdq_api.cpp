@@ -81,11 +81,14 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   return SSDQ_SUCCESS;
 }
 
+// With at least one (batch, head) sequence per CU, stage 0 carries the state across chunks
+// itself (chunk states never reach memory) and stage 1 has nothing left to do.
 ssdq_status run_stage(int32_t stage, const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
+  const bool fused = state_scan_fused(s.batch, s.nheads);
   hipError_t e = hipSuccess;
   switch (stage) {
-    case 0: e = launch_chunk_state(s, a, stream); break;
-    case 1: e = launch_state_passing(s, a, stream); break;
+    case 0: e = fused ? launch_state_scan(s, a, stream) : launch_chunk_state(s, a, stream); break;
+    case 1: e = fused ? hipSuccess : launch_state_passing(s, a, stream); break;
     case 2: e = launch_chunk_output(s, a, stream); break;
     default: return SSDQ_ERROR_INVALID_VALUE;
   }
@@ -123,6 +126,11 @@ size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nhe
   // ngroups does not change the workspace; 1 always divides nheads
   if (check_scan_shape(batch, seqlen, nheads, headdim, dstate, 1, chunk, &s) != SSDQ_SUCCESS) return 0;
   return s.total_bytes();
+}
+
+int32_t ssdq_chunk_scan_state_fused(int32_t batch, int32_t nheads) {
+  if (batch <= 0 || nheads <= 0) return 0;
+  return state_scan_fused(batch, nheads) ? 1 : 0;
 }
 
 ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,

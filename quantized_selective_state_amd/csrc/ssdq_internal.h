@@ -58,6 +58,10 @@ hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int
                            int32_t inner, hipStream_t stream);
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+// Stages 0 and 1 in one kernel (one block per (batch, head), chunks in order); used when
+// state_scan_fused(batch, nheads), i.e. when there are at least as many sequences as CUs.
+bool state_scan_fused(int32_t batch, int32_t nheads);
+hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
