@@ -79,6 +79,10 @@ ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int6
  *   Hscale  fp32 (batch, nchunks, nheads, headdim): the state entering each chunk is
  *           (Hprev[..., 0, p, n] + Hprev[..., 1, p, n] / 256) * Hscale[..., p], two INT8
  *           limbs with a power-of-two scale per state row           -- written by stage 1
+ *           Within each full 64-state block of a row, the 4 bytes of states
+ *           64 blk + 16 t + 4 k + (0..3) are stored at 64 blk + 16 k + 4 t + (0..3) (a 4x4
+ *           transpose of 4-byte groups: the writing lanes store 16 contiguous bytes); a
+ *           partial last block (dstate % 64 != 0) is stored in natural order.
  * When ssdq_chunk_scan_state_fused(batch, nheads) is 1, stage 0 writes Acs, Hprev, Hscale
  * (and h_final) itself, stage 1 does nothing, and S is not written. */
 size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,

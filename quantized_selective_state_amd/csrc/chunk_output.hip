@@ -97,13 +97,13 @@ __device__ __forceinline__ Item item_of(int it, int nheads, int nchunks, int ngr
 
 // Global data of one work item held in registers between its load and its LDS commit.
 constexpr int kBTasks = kMaxQ * 8 / kThreads;          // 16-byte B pieces per thread
-constexpr int kHTasks = 2 * kMaxP * 8 / kThreads;      // 16-byte Hprev-limb pieces per thread
+constexpr int kHThreads = 2 * kMaxP * 2;                // threads that load a 64-byte carried-state block
 constexpr int kXTasks = kMaxQ * (kMaxP / 16) / kThreads;   // 16-byte x pieces per thread
 struct Prefetch {
   float acs, dt, hs;
   v4i cq[2][2];                 // C codes of this lane's two output rows (per pass, K half)
   v4u bq[kBTasks];
-  v4u hq[kHTasks];
+  v4u hq[4];                    // one 64-state block of one limb row (4 pieces)
   v4u xq[kXTasks];
 };
 
@@ -130,8 +130,9 @@ struct Params {
 struct LaneConst {
   uint32_t b_off[kBTasks];      // B piece: token row j * G*N + 16-byte column group
   int b_lds[kBTasks];
-  uint32_t h_off[kHTasks];      // Hprev-limb piece in its (b, c, h) block
-  int h_lds[kHTasks];
+  uint32_t h_off[4];            // carried-state pieces of this thread's 64-state block
+  int h_lds;                    // LDS position of its first natural-order piece
+  bool h_full;                  // the block is full (stored dword-transposed)
   uint32_t x_off[kXTasks];      // x piece: token row j * H*P + 16-byte column group
   int x_lds[kXTasks];           // LDS position (halves) of its first 8 channels
   uint32_t c_off[2][2];         // C codes of this lane's output row, per pass and K half
@@ -171,7 +172,7 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
 #pragma unroll
   for (int k = 0; k < kBTasks; ++k) f.bq[k] = buf_load16(r.B, lc.b_off[k]);
 #pragma unroll
-  for (int k = 0; k < kHTasks; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
+  for (int k = 0; k < 4; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
 #pragma unroll
   for (int k = 0; k < kXTasks; ++k) f.xq[k] = buf_load16(r.x, lc.x_off[k]);
 }
@@ -203,12 +204,15 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     lc.b_off[k] = 16 * sg < N ? uint32_t(j) * gn + 16 * sg : kOutOfRange;
     lc.b_lds[k] = bpos(j, 16 * sg);
   }
+  {
+    // threads 0..255: limb tid / 128, row (tid / 2) % 64, 64-state block tid % 2
+    const int limb = tid >> 7, p = (tid >> 1) & (kMaxP - 1), bk = tid & 1;
 #pragma unroll
-  for (int k = 0; k < kHTasks; ++k) {
-    const int task = tid + k * kThreads;
-    const int limb = task / (kMaxP * 8), p = (task / 8) % kMaxP, sg = task & 7;
-    lc.h_off[k] = (p < P && 16 * sg < N) ? uint32_t(limb * P * N + p * N + 16 * sg) : kOutOfRange;
-    lc.h_lds[k] = limb * kHPlane + hpos(p, 16 * sg);
+    for (int q = 0; q < 4; ++q)
+      lc.h_off[q] = (tid < kHThreads && p < P && 64 * bk + 16 * q < N) ? uint32_t(limb * P * N + p * N + 64 * bk + 16 * q)
+                                                                       : kOutOfRange;
+    lc.h_lds = limb * kHPlane + hpos(p, 64 * bk);
+    lc.h_full = 64 * bk + 64 <= N;
   }
 #pragma unroll
   for (int k = 0; k < kXTasks; ++k) {
@@ -273,8 +277,14 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     if (tid < kMaxP) hsc[tid] = f.hs;
 #pragma unroll
     for (int k = 0; k < kBTasks; ++k) *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
+    if (tid < kHThreads) {   // wave-uniform
+      // a full block arrives dword-transposed (piece q holds dword t of natural piece t, q)
 #pragma unroll
-    for (int k = 0; k < kHTasks; ++k) *reinterpret_cast<v4u*>(Hq + lc.h_lds[k]) = f.hq[k];
+      for (int t = 0; t < 4; ++t) {
+        const v4u tr = {f.hq[0][t], f.hq[1][t], f.hq[2][t], f.hq[3][t]};
+        *reinterpret_cast<v4u*>(Hq + (lc.h_lds ^ (t << 4))) = lc.h_full ? tr : f.hq[t];
+      }
+    }
 #pragma unroll
     for (int k = 0; k < kXTasks; ++k) {
       const v4u u = f.xq[k] ^ 0x80808080u;

@@ -445,10 +445,12 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
       const float inv = exp2i(8 - ex);
       const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
       const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
-      const uint32_t loff = uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh + 4 * kg;
+      // this lane's 16 states of the row (4 tiles x 4): one 16-byte piece per limb when the
+      // 64-state block is full (the workspace stores full blocks dword-transposed), else
+      // 4-byte pieces in natural order
+      v4u Q1, Q2;
 #pragma unroll
       for (int t = 0; t < kOwn; ++t) {
-        if (16 * (kOwn * kh + t) >= N) break;
         uint32_t q1 = 0, q2 = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -456,8 +458,20 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
           q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
           q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
         }
-        __builtin_amdgcn_raw_buffer_store_b32(q1, rh, loff + 16u * t, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(q2, rh, loff + 16u * t, int(pn), 0);
+        Q1[t] = q1;
+        Q2[t] = q2;
+      }
+      const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh;
+      if (64 * kh + 64 <= N) {
+        __builtin_amdgcn_raw_buffer_store_b128(Q1, rh, row + 16 * kg, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(Q2, rh, row + 16 * kg, int(pn), 0);
+      } else {
+#pragma unroll
+        for (int t = 0; t < kOwn; ++t) {
+          if (64 * kh + 16 * t >= N) break;
+          __builtin_amdgcn_raw_buffer_store_b32(Q1[t], rh, row + 16 * t + 4 * kg, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(Q2[t], rh, row + 16 * t + 4 * kg, int(pn), 0);
+        }
       }
       if (kh == 0 && kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
     }

@@ -6,7 +6,8 @@
 // with the chunk's total decay.  Sequential over chunks, parallel over (batch, head, state
 // row).  The state entering chunk c, Hprev_c = H_c, is what the output stage reads; it is
 // written as two INT8 limbs per element with one power-of-two scale 2^e per state row p
-// (2 bytes per element, half of fp32), so that the output stage can read it out with C on
+// (2 bytes per element, half of fp32; full 64-state blocks of a row dword-transposed), so that
+// the output stage can read it out with C on
 // the INT8 matrix cores: with t = H 2^-e (|t| <= 127) and V = trunc(256 t + 128),
 // V = 256 l1 + (l2 + 128), so H = 2^e (l1 + l2 / 256) to within 2^e / 256.  The running
 // state and h_final stay fp32.
@@ -37,6 +38,10 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
   const bool active = p < P && 4 * nq < N;
   const int64_t pn = int64_t(P) * N;
   const int64_t e = int64_t(p) * N + 4 * nq;
+  // position of this lane's 4 states in a carried-state row: full 64-state blocks are stored
+  // dword-transposed (states 64 blk + 16 t + 4 k + i at 64 blk + 16 k + 4 t + i)
+  const int n0 = 4 * nq, blk = n0 >> 6, m = n0 & 63;
+  const int64_t eh = int64_t(p) * N + (64 * blk + 64 <= N ? 64 * blk + 16 * ((m >> 2) & 3) + 4 * (m >> 4) : n0);
 
   v4f H = {0.f, 0.f, 0.f, 0.f};
   if (active && h0) H = *reinterpret_cast<const v4f*>(h0 + int64_t(bh) * pn + e);
@@ -63,7 +68,7 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
         q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
       }
       // per (b, c, h): limb-1 plane [P][N] then limb-2 plane [P][N]
-      int8_t* dst = hprev + 2 * (base + c * cstride) + e;
+      int8_t* dst = hprev + 2 * (base + c * cstride) + eh;
       *reinterpret_cast<uint32_t*>(dst) = q1;
       *reinterpret_cast<uint32_t*>(dst + pn) = q2;
       if (nq == 0) hscale[(base + c * cstride) / N + p] = exp2i(ex);

@@ -76,3 +76,17 @@ def sample_pairs(batch: int, nheads: int, n: int, seed: int, must_heads=()):
     while len(pairs) < min(n, batch * nheads):
         pairs.add((int(rng.integers(batch)), int(rng.integers(nheads))))
     return sorted(pairs)
+
+
+def carried_state(hprev: np.ndarray, hscale: np.ndarray) -> np.ndarray:
+    """The state entering each chunk from the workspace's two INT8 limbs and row scales,
+    (..., 2, P, N) int8 + (..., P) fp32 -> (..., P, N) fp64.  Full 64-state blocks of a row are
+    stored with their 4-byte groups transposed (state 64 blk + 16 t + 4 k + i at
+    64 blk + 16 k + 4 t + i); a partial last block is in natural order."""
+    N = hprev.shape[-1]
+    nat = hprev.astype(np.float64).copy()
+    for blk in range(N // 64):
+        sl = hprev[..., 64 * blk:64 * blk + 64].astype(np.float64)
+        g = sl.reshape(sl.shape[:-1] + (4, 4, 4))          # stored (k, t, i)
+        nat[..., 64 * blk:64 * blk + 64] = np.swapaxes(g, -3, -2).reshape(sl.shape)   # natural (t, k, i)
+    return (nat[..., 0, :, :] + nat[..., 1, :, :] / 256.0) * hscale[..., None].astype(np.float64)

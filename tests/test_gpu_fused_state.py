@@ -9,7 +9,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import H_TOL, Y_TOL, gpu_prefill, gpu_quantize_inputs, note, oracle_codes, rel_err, to_dev
+from gpu_util import (H_TOL, Y_TOL, carried_state, gpu_prefill, gpu_quantize_inputs, note, oracle_codes, rel_err,
+                      to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,7 +113,7 @@ def test_intermediates():
     c = oracle_codes(inp)
     pairs = [(0, 0), (0, 5), (1, 17), (inp["batch"] - 1, 63)]
     _, h_ref, bounds = oracle.ssd(c, pairs=pairs, chunk=256)
-    Hprev = (limbs0[:, :, :, 0].astype(np.float64) + limbs0[:, :, :, 1] / 256.0) * hs0[..., None]
+    Hprev = carried_state(limbs0, hs0)
     for b, h in pairs:
         a_ref = oracle.chunk_cumsum(c, b, h, 256)
         valid = np.isfinite(a_ref)

@@ -13,8 +13,8 @@ import torch
 
 import oracle
 import workloads
-from gpu_util import (H_TOL, Y_TOL, dev, gpu_prefill, gpu_quantize_inputs, note, oracle_codes, rel_err,
-                      sample_pairs, to_dev)
+from gpu_util import (H_TOL, Y_TOL, carried_state, dev, gpu_prefill, gpu_quantize_inputs, note, oracle_codes,
+                      rel_err, sample_pairs, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,8 +111,7 @@ def test_stage_intermediates():
     S = views["states"].cpu().numpy().copy()
     buf.run_stage(1)                       # state passing -> carried state as two int8 limbs + row scales
     torch.cuda.synchronize()
-    limbs = views["hprev"].cpu().numpy().astype(np.float64)
-    Hprev = (limbs[:, :, :, 0] + limbs[:, :, :, 1] / 256.0) * views["hscale"].cpu().numpy()[..., None]
+    Hprev = carried_state(views["hprev"].cpu().numpy(), views["hscale"].cpu().numpy())
     buf.run_stage(2)                       # chunk output
     torch.cuda.synchronize()
     nc = acs.shape[2]
