@@ -71,11 +71,58 @@ def measured_traffic(kernel: str):
     return None
 
 
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it does not write back
+    and invalidate the caches (a default event's system-scope release does, which costs a few
+    microseconds per record and leaves the next kernel with cold caches).  Elapsed times are read
+    only after a device synchronisation."""
+
+    _hip = None
+    FLAGS = 0x20000000   # hipEventDisableSystemFence
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            lib = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch already loaded (same soname)
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = lib
+        return cls._hip
+
+    def __init__(self, stream: int):
+        import ctypes
+        self.stream = ctypes.c_void_p(stream)
+        self.h = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(ctypes.byref(self.h), self.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        rc = self.hip().hipEventRecord(self.h, self.stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end: "HipEvent") -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -169,19 +216,22 @@ def main():
             if marks and i in marks:
                 marks[i][1].record()
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream().cuda_stream   # the stream every kernel is launched on
+    ev = lambda: HipEvent(stream)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # per-kernel breakdown: K steps with events around every kernel (recording an event costs a
-    # few microseconds, so these steps are not the ones whose wall time gives the throughput)
-    prof = [{i: (ev(), ev()) for i in range(len(fns))} for _ in range(args.steps)]
-    for k in range(args.steps):
+    # per-kernel breakdown: up to 200 steps with events around every kernel (an event between
+    # two kernels can delay the second, so these steps are not the ones whose wall time gives
+    # the throughput)
+    nprof = min(args.steps, 200)
+    prof = [{i: (ev(), ev()) for i in range(len(fns))} for _ in range(nprof)]
+    for k in range(nprof):
         step(prof[k])
     torch.cuda.synchronize()
-    per_kernel_ms = {n: sum(prof[k][i][0].elapsed_time(prof[k][i][1]) for k in range(args.steps)) / args.steps
+    per_kernel_ms = {n: sum(prof[k][i][0].elapsed_time(prof[k][i][1]) for k in range(nprof)) / nprof
                      for i, n in enumerate(names)}
     dominant = max(names, key=lambda n: per_kernel_ms[n])
     di = names.index(dominant)

@@ -1,6 +1,6 @@
 """Build libssdq.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m quantized_selective_state_amd.build
+    python quantized_selective_state_amd/build.py     (or __graft_entry__.build())
 
 Objects go to quantized_selective_state_amd/_build/, the library next to this file.
 """

@@ -100,7 +100,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   __shared__ float acs_last_s;
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: scalar descriptors, no waterfall
   const int lane = tid % kWave;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bid % nheads;
@@ -260,15 +260,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 // tiles it does not own through LDS, and updates its own half of H.  The next chunk's dt, x and
 // B loads are issued before the current chunk's MFMAs.
 constexpr int kSThreads = 512;
-constexpr int kSWaves = kSThreads / kWave;
-
-template <int Q>
-struct StagedS {
-  static constexpr int kX = (Q * (kMaxP / 16) + kSThreads - 1) / kSThreads;
-  static constexpr int kB = (Q * (kMaxN / 16) + kSThreads - 1) / kSThreads;
-  v4u x[kX];
-  v4u b[kB];
+template <int v>
+struct Parity {
+  static constexpr int value = v;
 };
+constexpr int kSWaves = kSThreads / kWave;
+constexpr int kGroup = kSWaves;   // chunks whose weights one prologue prepares (one per wave)
+static_assert(kGroup % 2 == 0, "groups start at even chunks (tile buffer parity)");
 
 template <int Q>
 __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(2))) state_scan_kernel(
@@ -277,17 +275,21 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     const float* h0, float* h_final, float* __restrict__ acs, int8_t* __restrict__ hprev,
     float* __restrict__ hscale, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
     int32_t ngroups, int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
-  __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
-  __shared__ __attribute__((aligned(16))) uint32_t om[Q];
-  __shared__ __attribute__((aligned(16))) uint32_t cb[Q];
+  // double-buffered chunk tiles, as separate objects so that the compiler can tell the buffer
+  // being filled from the one being read (no wait on the fill before each read)
+  __shared__ __attribute__((aligned(16))) uint8_t xs0[Q * kMaxP];
+  __shared__ __attribute__((aligned(16))) uint8_t xs1[Q * kMaxP];
+  __shared__ __attribute__((aligned(16))) uint8_t bs0[Q * kMaxN];
+  __shared__ __attribute__((aligned(16))) uint8_t bs1[Q * kMaxN];
+  __shared__ __attribute__((aligned(16))) uint32_t om[kGroup][Q];       // OM_j of the group's chunks
+  __shared__ __attribute__((aligned(16))) uint32_t cb[kGroup][Q];       // CB_j
   __shared__ __attribute__((aligned(16))) v4f xch[kSWaves][4][kWave];   // partial S handed over
   __shared__ float rmax[2][kMaxP];                                      // half-row maxima
-  __shared__ float red[kSWaves];
-  __shared__ float acs_last_s;
+  __shared__ float gdec[kGroup];                                        // exp(Acs_last) per chunk
+  __shared__ int gexp[kGroup];                                          // 2^e >= max_j w_j per chunk
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: scalar descriptors, no waterfall
   const int lane = tid % kWave;
   const int bh = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bh % nheads;
@@ -298,6 +300,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
   const int pt = wave & 3, kh = wave >> 2;   // channel tile; half of the K steps and of the state tiles
   constexpr int kNt = kMaxN / 16;
   constexpr int kOwn = kNt / 2;               // state tiles 4 kh .. 4 kh + 3 belong to this wave
+  constexpr int kTok = Q / kWave;              // tokens per lane in a group prologue
   const bool prow = 16 * pt < P;               // this wave's channel tile exists (uniform)
   const uint32_t xrow = uint32_t(nheads * P), brow = uint32_t(ngroups * N);
   const float sxB = x_scale[h] * B_scale[g];
@@ -314,49 +317,128 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
       H[t] = __builtin_bit_cast(v4f, buf_load16(r0, 16 * (kOwn * kh + t) < N ? hoff + 64u * t : kOutOfRange));
   }
 
-  // ---- chunk loads (dt of this thread's token, x and B codes), for chunk c; a chunk past the
-  // end gets empty buffers (its loads return zeros and touch no memory)
-  float dnext;
-  StagedS<Q> st;
-  auto load_chunk = [&](int c) {
+  // ---- the x and B codes of chunk c, straight into LDS tile buffer c % 2 (buffer loads to LDS:
+  // a wave's 64 lanes fill 1 KB of LDS in lane order, so each lane loads the global piece that
+  // belongs at its slot of the swizzled layout).  A chunk past the end gets empty buffers: its
+  // loads write zeros and touch no memory.
+  constexpr int kXd = Q * (kMaxP / 16) / kSThreads;   // 16-byte x slots per thread (0 for Q = 64: below)
+  constexpr int kBd = Q * (kMaxN / 16) / kSThreads;
+  constexpr int kXs = kXd > 0 ? kXd : 1;
+  uint32_t xoff[kXs], boff[kBd];
+#pragma unroll
+  for (int k = 0; k < kXs; ++k) {
+    const int slot = k * kSThreads + tid, j = slot >> 2, pc = slot & 3, cc = pc ^ ((j >> 2) & 3);
+    xoff[k] = (16 * cc < P && j < Q) ? uint32_t(j) * xrow + 16 * cc : kOutOfRange;
+  }
+#pragma unroll
+  for (int k = 0; k < kBd; ++k) {
+    const int slot = k * kSThreads + tid, j = slot >> 3, pc = slot & 7, cc = pc ^ ((j >> 1) & 7);
+    boff[k] = (16 * cc < N && j < Q) ? uint32_t(j) * brow + 16 * cc : kOutOfRange;
+  }
+  auto dma_chunk = [&](int c, auto par) {
+    const bool ok = c < nchunks;
+    const int64_t t0 = ok ? int64_t(c) * Q : 0;
+    const int len = ok ? int(seqlen - t0 < Q ? seqlen - t0 : Q) : 1;
+    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, ok ? uint32_t(len - 1) * xrow + P : 0u);
+    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, ok ? uint32_t(len - 1) * brow + N : 0u);
+    uint8_t* xd = par.value ? xs1 : xs0;
+    uint8_t* bd = par.value ? bs1 : bs0;
+#pragma unroll
+    for (int k = 0; k < kXs; ++k) {
+      if (kXd == 0 && wave >= Q * 4 / kWave) break;   // Q = 64: 256 slots, waves 0..3
+      buf_load16_lds(rx, xd + 16 * (k * kSThreads + kWave * wave), xoff[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kBd; ++k)
+      buf_load16_lds(rb, bd + 16 * (k * kSThreads + kWave * wave), boff[k]);
+  };
+  // ---- dt of a group of kGroup chunks: wave w takes chunk g0 + w, lane l its tokens
+  // l * kTok .. l * kTok + kTok - 1 (zeros past the sequence end)
+  float dtg[kTok];
+  auto load_dt_group = [&](int g0) {
+    const int c = g0 + wave;
     const bool ok = c < nchunks;
     const int64_t t0 = ok ? int64_t(c) * Q : 0;
     const int len = ok ? int(seqlen - t0 < Q ? seqlen - t0 : Q) : 1;
     const Rsrc rdt = make_rsrc(dt + (int64_t(b) * seqlen + t0) * nheads + h, ok ? (uint32_t(len - 1) * nheads + 1u) * 4u : 0u);
-    dnext = buf_loadf(rdt, tid < Q ? uint32_t(tid) * uint32_t(nheads) * 4u : kOutOfRange);
-    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, ok ? uint32_t(len - 1) * xrow + P : 0u);
-    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, ok ? uint32_t(len - 1) * brow + N : 0u);
 #pragma unroll
-    for (int k = 0; k < StagedS<Q>::kX; ++k) {
-      const int piece = tid + k * kSThreads, j = piece >> 2, cc = piece & 3;
-      st.x[k] = buf_load16(rx, (16 * cc < P && j < Q) ? uint32_t(j) * xrow + 16 * cc : kOutOfRange);
+    for (int u = 0; u < kTok; ++u) dtg[u] = buf_loadf(rdt, uint32_t(lane * kTok + u) * uint32_t(nheads) * 4u);
+  };
+  // ---- per-chunk quantities of a group, one chunk per wave and no block barriers: the chunk
+  // cumsum of dt A (written to the workspace), its decay exp(Acs_last), the LUT_state weights
+  // w_j = exp(Acs_last - Acs_j) dt_j, their power-of-two range 2^e and the integer limb
+  // coefficients OM_j, CB_j
+  auto group_prologue = [&](int g0) {
+    const int c = g0 + wave;
+    if (c >= nchunks) return;   // wave-uniform
+    const int64_t t0 = int64_t(c) * Q;
+    const int len = int(seqlen - t0 < Q ? seqlen - t0 : Q);
+    float a[kTok];
+    float run = 0.f;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      run += dtg[u] * Ah;   // tokens past the end have dt = 0
+      a[u] = run;
     }
+    float incl = run;   // inclusive scan of the lane totals
 #pragma unroll
-    for (int k = 0; k < StagedS<Q>::kB; ++k) {
-      const int piece = tid + k * kSThreads, j = piece >> 3, cc = piece & 7;
-      st.b[k] = buf_load16(rb, (16 * cc < N && j < Q) ? uint32_t(j) * brow + 16 * cc : kOutOfRange);
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float up = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += up;
+    }
+    const float excl = incl - run;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) a[u] += excl;
+    float* arow = acs + ((int64_t(b) * nheads + h) * nchunks + c) * Q + lane * kTok;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) arow[u] = a[u];
+    // Acs at the chunk's last token
+    const int lastl = (len - 1) / kTok, lastu = (len - 1) % kTok;
+    float asel = a[0];
+#pragma unroll
+    for (int u = 1; u < kTok; ++u) asel = lastu == u ? a[u] : asel;
+    const float a_last = __shfl(asel, lastl, kWave);
+    float w[kTok], wm = 0.f;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      w[u] = dtg[u] > 0.f ? __builtin_amdgcn_exp2f((a_last - a[u]) * kLog2e) * dtg[u] : 0.f;
+      wm = fmaxf(wm, w[u]);
+    }
+    const int e = min(max(ceil_log2_pos(wave_max(wm)), -100), 100);
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      const uint32_t o = uint32_t(fminf(w[u] * exp2i(24 - e), 16777215.f) + 0.5f);
+      om[wave][lane * kTok + u] = o;
+      cb[wave][lane * kTok + u] = 8421376u - (o << 7);   // 256 * 32896 - 128 OM (mod 2^32)
+    }
+    if (lane == 0) {
+      gdec[wave] = __builtin_amdgcn_exp2f(a_last * kLog2e);
+      gexp[wave] = e;
     }
   };
-  load_chunk(0);
+  load_dt_group(0);
+  dma_chunk(0, Parity<0>{});
 
   // transposing-read addresses (as in the kernel above)
   const int rowb = 16 * kg + (lcol >> 1), half8 = 8 * (lcol & 1);
   const int xa0 = xpos(rowb, 16 * pt + half8), xa1 = xpos(rowb + 8, 16 * pt + half8);
+  // accumulator t holds state tile (t + 4 kh) % 8: the wave's own tiles are always acc[0..3]
+  // and the ones it hands over acc[4..7], with no selects on kh (tile u ^ 4 stays at t ^ 4)
   int ba[kNt];
 #pragma unroll
-  for (int t = 0; t < kNt; ++t) ba[t] = bpos(rowb, 16 * t + half8);
+  for (int t = 0; t < kNt; ++t) ba[t] = bpos(rowb, 16 * ((t + kOwn * kh) % kNt) + half8);
 
   // one 64-token step of S^T into acc (first step starts the accumulators)
-  v4i acc[kNt][3];
-  auto kstep = [&](int kb, bool first) {
+  auto kstep = [&](v4i (&acc)[kNt][3], const uint8_t* xt, const uint8_t* bt, int cl, int kb, bool first)
+      {
     const int j0 = kb + 16 * kg;
-    const v2u xlo = tr8(xs + xa0 + kb * kMaxP), xhi = tr8(xs + xa1 + kb * kMaxP);
+    const v2u xlo = tr8(xt + xa0 + kb * kMaxP), xhi = tr8(xt + xa1 + kb * kMaxP);
     const uint32_t xw[4] = {xlo[0], xlo[1], xhi[0], xhi[1]};
     v4i l1, l2, l3;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
-      const v4u o4 = *reinterpret_cast<const v4u*>(&om[j0 + 4 * dw]);
-      const v4u c4 = *reinterpret_cast<const v4u*>(&cb[j0 + 4 * dw]);
+      const v4u o4 = *reinterpret_cast<const v4u*>(&om[cl][j0 + 4 * dw]);
+      const v4u c4 = *reinterpret_cast<const v4u*>(&cb[cl][j0 + 4 * dw]);
       const uint32_t u = xw[dw] ^ 0x80808080u;
       uint32_t W[4], pl[4];
       W[0] = mad24(u & 0xffu, o4[0], c4[0]);
@@ -370,7 +452,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     }
 #pragma unroll
     for (int t = 0; t < kNt; ++t) {
-      const v2u blo = tr8(bs + ba[t] + kb * kMaxN), bhi = tr8(bs + ba[t ^ 4] + (kb + 8) * kMaxN);
+      const v2u blo = tr8(bt + ba[t] + kb * kMaxN), bhi = tr8(bt + ba[t ^ 4] + (kb + 8) * kMaxN);
       const v4i bop = {int(blo[0]), int(blo[1]), int(bhi[0]), int(bhi[1])};
       const v4i z = {0, 0, 0, 0};
       acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l1, first ? z : acc[t][0], 0, 0, 0);
@@ -379,157 +461,116 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int64_t t0 = int64_t(c) * Q;
-    const int len = int(seqlen - t0 < Q ? seqlen - t0 : Q);
-    const float d = tid < len ? dnext : 0.f;
-
-    // ---- (a) chunk cumsum of dt A, one token per thread of waves 0..Q/64-1
-    float v = d * Ah;
+  for (int g0 = 0; g0 < nchunks; g0 += kGroup) {
+    group_prologue(g0);
+    load_dt_group(g0 + kGroup);   // in flight during the group's chunks
+    const int gend = min(g0 + kGroup, nchunks);
+    auto chunk_body = [&](int c, auto par) {   // par: c % 2, a compile-time constant
+      const int cl = c - g0;
+      const uint8_t* xt = par.value ? xs1 : xs0;
+      const uint8_t* bt = par.value ? bs1 : bs0;
+      v4i acc[kNt][3];
+      // half-row maxima of the state entering the chunk (own 16 states x the 4 lanes of the row)
+      {
+        float m = 0.f;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const float up = __shfl_up(v, o, kWave);
-      if (lane >= o) v += up;
-    }
-    if (lane == kWave - 1) red[wave] = v;
-    __syncthreads();   // also: every wave is done with the previous chunk's LDS tiles
-    float pre = 0.f;
+        for (int t = 0; t < kOwn; ++t)
 #pragma unroll
-    for (int w2 = 0; w2 < kSWaves - 1; ++w2) pre += w2 < wave ? red[w2] : 0.f;
-    const float acs_t = v + pre;
-    if (tid < Q) acs[((int64_t(b) * nheads + h) * nchunks + c) * Q + tid] = acs_t;
-    if (tid == len - 1) acs_last_s = acs_t;
-    // the x and B codes of the chunk into LDS (16-byte copies)
-#pragma unroll
-    for (int k = 0; k < StagedS<Q>::kX; ++k) {
-      const int piece = tid + k * kSThreads;
-      if (piece < Q * 4) *reinterpret_cast<v4u*>(xs + xpos(piece >> 2, 16 * (piece & 3))) = st.x[k];
-    }
-#pragma unroll
-    for (int k = 0; k < StagedS<Q>::kB; ++k) {
-      const int piece = tid + k * kSThreads;
-      if (piece < Q * 8) *reinterpret_cast<v4u*>(bs + bpos(piece >> 3, 16 * (piece & 7))) = st.b[k];
-    }
-    __syncthreads();
-
-    // ---- LUT_state weights and their power-of-two range
-    const float a_last = acs_last_s;
-    const float w = d > 0.f ? __builtin_amdgcn_exp2f((a_last - acs_t) * kLog2e) * d : 0.f;
-    const float wm = wave_max(w);
-    __syncthreads();   // red[] reuse
-    if (lane == 0) red[wave] = wm;
-    // half-row maxima of the state entering the chunk (own 16 states x the 4 lanes of the row)
-    float m = 0.f;
-#pragma unroll
-    for (int t = 0; t < kOwn; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
-    m = fmaxf(m, __shfl_xor(m, 16, kWave));
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    if (kg == 0) rmax[kh][16 * pt + lcol] = m;
-    __syncthreads();
-    float wmax = red[0];
-#pragma unroll
-    for (int i = 1; i < kSWaves; ++i) wmax = fmaxf(wmax, red[i]);
-    const int e = min(max(ceil_log2_pos(wmax), -100), 100);
-    if (tid < Q) {
-      const uint32_t o = uint32_t(fminf(w * exp2i(24 - e), 16777215.f) + 0.5f);
-      om[tid] = o;
-      cb[tid] = 8421376u - (o << 7);
-    }
-
-    // ---- the state entering the chunk, Hprev_c = H, as two INT8 limbs and a power-of-two row scale
-    if (prow) {
-      m = fmaxf(rmax[0][16 * pt + lcol], rmax[1][16 * pt + lcol]);
-      const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
-      const float inv = exp2i(8 - ex);
-      const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
-      const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
-      // this lane's 16 states of the row (4 tiles x 4): one 16-byte piece per limb when the
-      // 64-state block is full (the workspace stores full blocks dword-transposed), else
-      // 4-byte pieces in natural order
-      v4u Q1, Q2;
-#pragma unroll
-      for (int t = 0; t < kOwn; ++t) {
-        uint32_t q1 = 0, q2 = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int32_t V = int32_t(fmaf(H[t][i], inv, 128.f));   // 256 t + 128, |t| <= 127
-          q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
-          q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
-        }
-        Q1[t] = q1;
-        Q2[t] = q2;
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        if (kg == 0) rmax[kh][16 * pt + lcol] = m;
       }
-      const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh;
-      if (64 * kh + 64 <= N) {
-        __builtin_amdgcn_raw_buffer_store_b128(Q1, rh, row + 16 * kg, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(Q2, rh, row + 16 * kg, int(pn), 0);
-      } else {
+      // this chunk's tiles (loaded into LDS one chunk ago) have landed: wait for every
+      // outstanding vector-memory operation of this wave, then for all waves
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      __syncthreads();   // tiles, rmax (and, at a group start, the prologue's weights) visible
+      // ---- the next chunk's tiles, into the other buffer (its last readers passed the barrier)
+      dma_chunk(c + 1, Parity<1 - par.value>{});
+
+      // ---- the state entering the chunk, Hprev_c = H, as two INT8 limbs and a power-of-two row scale
+      if (prow) {
+        const float m = fmaxf(rmax[0][16 * pt + lcol], rmax[1][16 * pt + lcol]);
+        const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
+        const float inv = exp2i(8 - ex);
+        const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
+        const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
+        // this lane's 16 states of the row (4 tiles x 4): one 16-byte piece per limb when the
+        // 64-state block is full (the workspace stores full blocks dword-transposed), else
+        // 4-byte pieces in natural order
+        v4u Q1, Q2;
 #pragma unroll
         for (int t = 0; t < kOwn; ++t) {
-          if (64 * kh + 16 * t >= N) break;
-          __builtin_amdgcn_raw_buffer_store_b32(Q1[t], rh, row + 16 * t + 4 * kg, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(Q2[t], rh, row + 16 * t + 4 * kg, int(pn), 0);
+          uint32_t q1 = 0, q2 = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int32_t V = int32_t(fmaf(H[t][i], inv, 128.f));   // 256 t + 128, |t| <= 127
+            q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
+            q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
+          }
+          Q1[t] = q1;
+          Q2[t] = q2;
         }
+        const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh;
+        if (64 * kh + 64 <= N) {
+          __builtin_amdgcn_raw_buffer_store_b128(Q1, rh, row + 16 * kg, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(Q2, rh, row + 16 * kg, int(pn), 0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < kOwn; ++t) {
+            if (64 * kh + 16 * t >= N) break;
+            __builtin_amdgcn_raw_buffer_store_b32(Q1[t], rh, row + 16 * t + 4 * kg, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(Q2[t], rh, row + 16 * t + 4 * kg, int(pn), 0);
+          }
+        }
+        if (kh == 0 && kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
       }
-      if (kh == 0 && kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
-    }
-    __syncthreads();   // om / cb visible; rmax read
 
-    // ---- next chunk's loads, in flight during this chunk's MFMAs
-    load_chunk(c + 1);
 
-    // ---- S_c^T partial over this wave's 64-token steps (interleaved between the two waves)
-    if constexpr (Q == 64) {
-      if (kh == 0) {
-        kstep(0, true);
+      // ---- S_c^T partial over this wave's 64-token steps (interleaved between the two waves)
+      if constexpr (Q == 64) {
+        if (kh == 0) {
+          kstep(acc, xt, bt, cl, 0, true);
+        } else {
+#pragma unroll
+          for (int t = 0; t < kNt; ++t)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
+        }
       } else {
-#pragma unroll
-        for (int t = 0; t < kNt; ++t)
-#pragma unroll
-          for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
+        kstep(acc, xt, bt, cl, 64 * kh, true);
+        if constexpr (Q == 256) kstep(acc, xt, bt, cl, 64 * kh + 128, false);
       }
-    } else {
-      kstep(64 * kh, true);
-      if constexpr (Q == 256) kstep(64 * kh + 128, false);
-    }
 
-    // ---- fp32 partials; hand over the other wave's tiles, then H <- exp(Acs_last) H + S_c
-    const float post = sxB * exp2i(e);
-    const float post_lo = post * (1.f / 65536.f);
-    auto partial = [&](int t) {
-      v4f r;
+      // ---- fp32 partials; hand over the other wave's tiles, then H <- exp(Acs_last) H + S_c
+      const float post = sxB * exp2i(gexp[cl]);
+      const float post_lo = post * (1.f / 65536.f);
+      auto partial = [&](int t) {
+        v4f r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
-        r[i] = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
-      }
-      return r;
-    };
-    // (wave-uniform branches with constant tile indices keep acc in registers)
-    if (kh == 0) {
+        for (int i = 0; i < 4; ++i) {
+          const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
+          r[i] = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+        }
+        return r;
+      };
 #pragma unroll
       for (int t = 0; t < kOwn; ++t) xch[wave][t][lane] = partial(kOwn + t);
-    } else {
-#pragma unroll
-      for (int t = 0; t < kOwn; ++t) xch[wave][t][lane] = partial(t);
-    }
-    v4f mine[kOwn];
-    if (kh == 0) {
+      v4f mine[kOwn];
 #pragma unroll
       for (int t = 0; t < kOwn; ++t) mine[t] = partial(t);
-    } else {
+      const float decay = gdec[cl];   // read before the barrier: the next group's prologue rewrites it
+      __syncthreads();
 #pragma unroll
-      for (int t = 0; t < kOwn; ++t) mine[t] = partial(kOwn + t);
-    }
-    __syncthreads();
-    const float decay = __builtin_amdgcn_exp2f(a_last * kLog2e);
+      for (int t = 0; t < kOwn; ++t) {
+        const v4f other = xch[wave ^ 4][t][lane];
 #pragma unroll
-    for (int t = 0; t < kOwn; ++t) {
-      const v4f other = xch[wave ^ 4][t][lane];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) H[t][i] = fmaf(decay, H[t][i], mine[t][i] + other[i]);
+        for (int i = 0; i < 4; ++i) H[t][i] = fmaf(decay, H[t][i], mine[t][i] + other[i]);
+      }
+    };
+    for (int c = g0; c < gend; c += 2) {   // g0 is even
+      chunk_body(c, Parity<0>{});
+      if (c + 1 < gend) chunk_body(c + 1, Parity<1>{});
     }
   }
 

@@ -88,6 +88,13 @@ __device__ __forceinline__ uint32_t buf_load4(Rsrc r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 __device__ __forceinline__ float buf_loadf(Rsrc r, uint32_t off) { return __uint_as_float(buf_load4(r, off)); }
+// 16 bytes per lane from a buffer straight into LDS: a wave's lanes fill 16 * 64 consecutive
+// bytes starting at the wave-uniform `lds`, in lane order (no registers involved).  Completion
+// is tracked by vmcnt.  (Called through this plain function: used directly inside a kernel
+// template, the builtin keeps the host pass from emitting the kernel's launch stub.)
+__device__ __forceinline__ void buf_load16_lds(Rsrc r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
 
 // Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8).  Remap the
 // linear block index so that consecutive *logical* tiles land on the same XCD and share
