@@ -69,6 +69,31 @@ const char* ssdq_status_string(ssdq_status status);
 ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
                           int32_t inner, hipStream_t stream);
 
+/* One tensor of a batched quantize: the arguments of ssdq_quantize. */
+typedef struct {
+  const void* x_f16;   /* (rows, nscale, inner) IEEE binary16, device */
+  int8_t* q;           /* (rows, nscale, inner) int8, device, written */
+  const float* scale;  /* [nscale] fp32, device */
+  int64_t rows;
+  int32_t nscale;
+  int32_t inner;
+} ssdq_quantize_job;
+
+#define SSDQ_QUANTIZE_MAX_JOBS 8
+
+/*
+ * The same static INT8 quantizer applied to several tensors (x, B and C of one step) in
+ * one kernel launch where their shapes allow it: each job's codes equal those of
+ * ssdq_quantize with the same arguments.  Jobs whose inner is a multiple of 16 share one
+ * launch; any other job is launched on its own (same stream, same result).
+ *   jobs  : host array of `count` jobs, read during the call only
+ *   count : 1 .. SSDQ_QUANTIZE_MAX_JOBS
+ * Every job is validated as ssdq_quantize validates its arguments before anything is
+ * launched (one invalid job: nothing runs).  Jobs with rows == 0 are skipped.  No output
+ * may overlap another job's output or any job's input.
+ */
+ssdq_status ssdq_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream);
+
 /* Bytes of workspace ssdq_chunk_scan needs for this shape (host; 0 on invalid shapes).
  * Layout (stable, used by the stage-level tests), with nchunks = ceil(seqlen / chunk) and
  * each region starting at a 256-byte boundary:

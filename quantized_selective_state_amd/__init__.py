@@ -26,7 +26,8 @@ CHUNK_SCAN_STAGES = 3
 STAGE_NAMES = ("chunk_state", "state_passing", "chunk_output")   # stage 0 also runs the chunk cumsum
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m quantized_selective_state_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python quantized_selective_state_amd/build.py` "
+                      "(or __graft_entry__.build())")
 
 lib = ctypes.CDLL(LIB_PATH)
 _P, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -35,6 +36,16 @@ lib.ssdq_status_string.argtypes = [ctypes.c_int]
 lib.ssdq_status_string.restype = ctypes.c_char_p
 lib.ssdq_quantize.argtypes = [_P, _P, _P, _i64, _i32, _i32, _P]
 lib.ssdq_quantize.restype = ctypes.c_int
+
+
+class QuantizeJob(ctypes.Structure):
+    """ssdq_quantize_job: the arguments of one ssdq_quantize call."""
+    _fields_ = [("x_f16", _P), ("q", _P), ("scale", _P), ("rows", _i64), ("nscale", _i32), ("inner", _i32)]
+
+
+QUANTIZE_MAX_JOBS = 8
+lib.ssdq_quantize_batch.argtypes = [ctypes.POINTER(QuantizeJob), _i32, _P]
+lib.ssdq_quantize_batch.restype = ctypes.c_int
 lib.ssdq_chunk_scan_workspace_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32]
 lib.ssdq_chunk_scan_workspace_size.restype = _sz
 _SCAN_ARGS = [_P] * 12 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
@@ -119,6 +130,31 @@ class QuantizeCall:
     def run(self) -> torch.Tensor:
         _check(lib.ssdq_quantize(*self._args, _stream(self.device)), "ssdq_quantize")
         return self.out
+
+
+class QuantizeBatch:
+    """Several quantize calls (e.g. x, B and C of one step) as one ssdq_quantize_batch call."""
+
+    def __init__(self, calls: list[QuantizeCall]):
+        if not 1 <= len(calls) <= QUANTIZE_MAX_JOBS:
+            raise ValueError(f"a batch holds 1 to {QUANTIZE_MAX_JOBS} quantize calls")
+        devices = {c.device for c in calls}
+        if len(devices) != 1:
+            raise ValueError("every tensor of a batch must be on one device")
+        self.device = calls[0].device
+        self.calls = calls
+        self._jobs = (QuantizeJob * len(calls))(*[QuantizeJob(*c._args) for c in calls])
+
+    def run(self) -> list[torch.Tensor]:
+        _check(lib.ssdq_quantize_batch(self._jobs, len(self.calls), _stream(self.device)), "ssdq_quantize_batch")
+        return [c.out for c in self.calls]
+
+
+def quantize_batch(pairs, outs=None) -> list[torch.Tensor]:
+    """INT8 codes of several fp16 tensors in one launch; pairs holds (x, scale) per tensor and
+    outs (optional) the output tensors.  Each result equals quantize(x, scale)."""
+    outs = outs if outs is not None else [None] * len(pairs)
+    return QuantizeBatch([QuantizeCall(x, s, o) for (x, s), o in zip(pairs, outs)]).run()
 
 
 def quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:

@@ -77,22 +77,50 @@ __device__ __forceinline__ uint32_t pack4(const uint32_t* c) { return c[0] | (c[
 
 // inner % 16 == 0: a thread quantizes 16 consecutive elements of one row (one scale index).
 // Pair indices i < 2^31 (host-checked), so the scale index uses 32-bit invariant division.
+__device__ __forceinline__ void quantize16(const v4u* __restrict__ x, v4u* __restrict__ q,
+                                           const float* __restrict__ scale, uint32_t i, FastDiv by_inner,
+                                           FastDiv by_nscale) {
+  const v4u raw0 = x[2 * i];
+  const v4u raw1 = x[2 * i + 1];
+  const uint32_t row = fdiv(i, by_inner);
+  const int k = int(row - fdiv(row, by_nscale) * by_nscale.d);
+  float v[16];
+  unpack8(raw0, *reinterpret_cast<float(*)[8]>(&v[0]));
+  unpack8(raw1, *reinterpret_cast<float(*)[8]>(&v[8]));
+  uint32_t c[16];
+  codes(v, scale[k], c);
+  q[i] = v4u{pack4(c), pack4(c + 4), pack4(c + 8), pack4(c + 12)};
+}
+
 __global__ void __launch_bounds__(256) quantize_vec16(const v4u* __restrict__ x, v4u* __restrict__ q,
                                                       const float* __restrict__ scale, uint32_t npair,
                                                       FastDiv by_inner, FastDiv by_nscale) {
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < npair; i += stride) {
-    const v4u raw0 = x[2 * i];
-    const v4u raw1 = x[2 * i + 1];
-    const uint32_t row = fdiv(i, by_inner);
-    const int k = int(row - fdiv(row, by_nscale) * by_nscale.d);
-    float v[16];
-    unpack8(raw0, *reinterpret_cast<float(*)[8]>(&v[0]));
-    unpack8(raw1, *reinterpret_cast<float(*)[8]>(&v[8]));
-    uint32_t c[16];
-    codes(v, scale[k], c);
-    q[i] = v4u{pack4(c), pack4(c + 4), pack4(c + 8), pack4(c + 12)};
-  }
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < npair; i += stride)
+    quantize16(x, q, scale, i, by_inner, by_nscale);
+}
+
+// Several tensors in one launch: job k owns the blocks block0 .. block0 + nblocks - 1 and walks
+// its pairs grid-stride over them.
+struct Job16 {
+  const v4u* x;
+  v4u* q;
+  const float* scale;
+  uint32_t npair, block0, nblocks;
+  FastDiv by_inner, by_nscale;
+};
+struct Jobs16 {
+  Job16 job[SSDQ_QUANTIZE_MAX_JOBS];
+  int32_t count;
+};
+
+__global__ void __launch_bounds__(256) quantize_vec16_batch(const Jobs16 jobs) {
+  int k = 0;   // the job of this block (uniform)
+  for (int t = 1; t < jobs.count; ++t) k = blockIdx.x >= jobs.job[t].block0 ? t : k;
+  const Job16& J = jobs.job[k];
+  const uint32_t stride = J.nblocks * blockDim.x;
+  for (uint32_t i = (blockIdx.x - J.block0) * blockDim.x + threadIdx.x; i < J.npair; i += stride)
+    quantize16(J.x, J.q, J.scale, i, J.by_inner, J.by_nscale);
 }
 
 // inner % 8 == 0: the 8 elements of a thread share one scale index.
@@ -134,6 +162,42 @@ int grid_for(int64_t work, int block) {
 }
 
 }  // namespace
+
+hipError_t launch_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream) {
+  // jobs with 16-element rows share one launch, smallest first (their blocks are dispatched
+  // first and finish under the large job); the others take their own launches
+  int order[SSDQ_QUANTIZE_MAX_JOBS];
+  int64_t size[SSDQ_QUANTIZE_MAX_JOBS];
+  for (int k = 0; k < count; ++k) {
+    order[k] = k;
+    size[k] = jobs[k].rows * int64_t(jobs[k].nscale) * jobs[k].inner;
+  }
+  for (int a = 1; a < count; ++a)
+    for (int k = a; k > 0 && size[order[k]] < size[order[k - 1]]; --k) {
+      const int t = order[k];
+      order[k] = order[k - 1];
+      order[k - 1] = t;
+    }
+  Jobs16 p{};
+  uint32_t blocks = 0;
+  for (int a = 0; a < count; ++a) {
+    const ssdq_quantize_job& j = jobs[order[a]];
+    const int64_t n = size[order[a]];
+    if (n == 0) continue;
+    if (j.inner % 16 == 0 && n / 16 < (int64_t(1) << 31)) {
+      const uint32_t npair = uint32_t(n / 16), nb = uint32_t(grid_for(npair, 256));
+      p.job[p.count++] = Job16{static_cast<const v4u*>(j.x_f16), reinterpret_cast<v4u*>(j.q), j.scale, npair, blocks,
+                               nb, make_fastdiv(uint32_t(j.inner / 16)), make_fastdiv(uint32_t(j.nscale))};
+      blocks += nb;
+    } else {
+      const hipError_t e = launch_quantize(static_cast<const uint16_t*>(j.x_f16), j.q, j.scale, j.rows, j.nscale,
+                                           j.inner, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  if (p.count > 0) hipLaunchKernelGGL(quantize_vec16_batch, dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
                            int32_t inner, hipStream_t stream) {

@@ -120,6 +120,20 @@ ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int6
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
+ssdq_status ssdq_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream) {
+  if (jobs == nullptr || count < 1 || count > SSDQ_QUANTIZE_MAX_JOBS) return SSDQ_ERROR_INVALID_VALUE;
+  bool work = false;
+  for (int32_t k = 0; k < count; ++k) {
+    const ssdq_quantize_job& j = jobs[k];
+    if (j.rows < 0 || j.nscale <= 0 || j.inner <= 0) return SSDQ_ERROR_INVALID_VALUE;
+    if (j.rows > 0 && (!ok_ptr(j.x_f16) || !ok_ptr(j.q) || !ok_ptr(j.scale))) return SSDQ_ERROR_INVALID_VALUE;
+    work = work || j.rows > 0;
+  }
+  if (!work) return SSDQ_SUCCESS;
+  const hipError_t e = launch_quantize_batch(jobs, count, stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
 size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                       int32_t dstate, int32_t chunk) {
   ScanShape s;

@@ -54,6 +54,7 @@ struct ScanArgs {
 };
 
 // Kernel launchers (one per translation unit).  They return hipGetLastError().
+hipError_t launch_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream);
 hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
                            int32_t inner, hipStream_t stream);
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream);

@@ -125,6 +125,38 @@ def test_quantize_validation(lib, args, status):
     assert lib.ssdq_quantize(*args, None) == status
 
 
+class Job(ctypes.Structure):
+    _fields_ = [("x_f16", ctypes.c_void_p), ("q", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("nscale", ctypes.c_int32), ("inner", ctypes.c_int32)]
+
+
+def test_quantize_job_layout():
+    # the C struct: three pointers, an int64 and two int32 (no padding)
+    assert ctypes.sizeof(Job) == 40
+    assert "SSDQ_QUANTIZE_MAX_JOBS 8" in open(HEADER).read()
+
+
+@pytest.mark.parametrize("jobs,count,status", [
+    ([], 0, INVALID),                                             # count below 1
+    ([(A16, A16, A16, 10, 4, 16)] * 9, 9, INVALID),               # count above the maximum
+    ([(A16, A16, A16, 10, 4, 16), (A16, A16, A16, -1, 4, 16)], 2, INVALID),
+    ([(A16, A16, A16, 10, 4, 16), (A16, A16, A16, 10, 0, 16)], 2, INVALID),
+    ([(A16, A16, A16, 10, 4, 0)], 1, INVALID),
+    ([(A16, A16 + 1, A16, 10, 4, 16)], 1, INVALID),               # misaligned output
+    ([(A16, A16, None, 10, 4, 16)], 1, INVALID),                  # missing scales
+    ([(None, None, None, 0, 4, 16), (None, None, None, 0, 2, 8)], 2, OK),   # nothing to do
+])
+def test_quantize_batch_validation(lib, jobs, count, status):
+    lib.ssdq_quantize_batch.argtypes = [ctypes.POINTER(Job), ctypes.c_int32, ctypes.c_void_p]
+    arr = (Job * max(len(jobs), 1))(*[Job(*j) for j in jobs])
+    assert lib.ssdq_quantize_batch(arr, count, None) == status
+
+
+def test_quantize_batch_rejects_null_jobs(lib):
+    lib.ssdq_quantize_batch.argtypes = [ctypes.POINTER(Job), ctypes.c_int32, ctypes.c_void_p]
+    assert lib.ssdq_quantize_batch(None, 1, None) == INVALID
+
+
 def _upd(lib, **kw):
     a = dict(state=A16, x=A16, xs=A16, B=A16, Bs=A16, C=A16, Cs=A16, dt=A16, A=A16, D=None, y=A16,
              b=2, H=8, P=64, N=128, G=2)

@@ -55,3 +55,39 @@ def test_empty_rows_is_a_noop():
     x = torch.empty((0, 4, 16), dtype=torch.float16, device=dev())
     out = ssdq.quantize(x, torch.ones(4, device=dev()))
     assert out.shape == (0, 4, 16)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mamba2-1.3b-prefill"])
+def test_batch_equals_the_oracle(name):
+    """x, B, C of a workload in one batched call, plus a ragged tensor (its own launch) and an
+    empty one: every code equals the oracle's."""
+    import quantized_selective_state_amd as ssdq
+    inp = workloads.make_prefill(name)
+    rng = np.random.default_rng(11)
+    rag = (rng.standard_normal((37, 3, 5)) * 30).astype(np.float16)
+    rag_s = rng.uniform(0.05, 1.0, size=3).astype(np.float32)
+    pairs = [(inp["x16"], inp["x_scale"]), (inp["B16"], inp["B_scale"]), (inp["C16"], inp["C_scale"]),
+             (rag, rag_s), (np.zeros((0, 2, 16), np.float16), np.ones(2, np.float32))]
+    note(f"quantize batch {name}: {[p[0].shape for p in pairs]}")
+    got = ssdq.quantize_batch([(to_dev(x), to_dev(s)) for x, s in pairs])
+    for (x, s), g in zip(pairs, got):
+        ref = oracle.quantize(x, s)
+        g = g.cpu().numpy()
+        assert g.shape == ref.shape
+        assert np.array_equal(g, ref), f"{x.shape}: {np.count_nonzero(g != ref)} mismatches"
+
+
+def test_batch_into_given_outputs_twice():
+    """Outputs passed in are written in place; a second run with new inputs overwrites them."""
+    import quantized_selective_state_amd as ssdq
+    rng = np.random.default_rng(12)
+    shapes = [(64, 4, 32), (64, 1, 128), (64, 1, 128)]
+    outs = [torch.full(s, 99, dtype=torch.int8, device=dev()) for s in shapes]
+    for rep in range(2):
+        xs = [(rng.standard_normal(s) * (20 + 10 * rep)).astype(np.float16) for s in shapes]
+        ss = [rng.uniform(0.05, 1.0, size=s[1]).astype(np.float32) for s in shapes]
+        batch = ssdq.QuantizeBatch([ssdq.QuantizeCall(to_dev(x), to_dev(s), o) for x, s, o in zip(xs, ss, outs)])
+        got = batch.run()
+        for x, s, g, o in zip(xs, ss, got, outs):
+            assert g.data_ptr() == o.data_ptr()
+            assert np.array_equal(g.cpu().numpy(), oracle.quantize(x, s))
