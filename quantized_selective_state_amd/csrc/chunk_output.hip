@@ -84,12 +84,16 @@ struct Item {
   int64_t t0;
 };
 
-__device__ __forceinline__ Item item_of(int it, int nheads, int nchunks, int ngroups, int64_t seqlen, int chunk) {
+// item index -> (batch, chunk, head), head fastest; invariant divisions by multipliers
+__device__ __forceinline__ Item item_of(int it, FastDiv by_heads, FastDiv by_chunks, FastDiv by_hpg, int64_t seqlen,
+                                        int chunk) {
   Item r;
-  r.h = it % nheads;
-  r.c = (it / nheads) % nchunks;
-  r.b = it / (nheads * nchunks);
-  r.g = r.h / (nheads / ngroups);
+  const uint32_t q1 = fdiv(uint32_t(it), by_heads);
+  const uint32_t q2 = fdiv(q1, by_chunks);
+  r.h = int(uint32_t(it) - q1 * by_heads.d);
+  r.c = int(q1 - q2 * by_chunks.d);
+  r.b = int(q2);
+  r.g = int(fdiv(uint32_t(r.h), by_hpg));
   r.t0 = int64_t(r.c) * chunk;
   r.len = int(seqlen - r.t0 < chunk ? seqlen - r.t0 : chunk);
   return r;
@@ -122,6 +126,7 @@ struct Params {
   _Float16* y;
   int64_t seqlen;
   int nheads, P, N, ngroups, Q, nchunks, nitems;
+  FastDiv by_heads, by_chunks, by_hpg;   // nheads, nchunks, nheads / ngroups
 };
 
 // Per-lane byte offsets that do not depend on the work item (computed once per block).  Pieces
@@ -257,10 +262,11 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   int it = xcd_remap(blockIdx.x, gridDim.x);
   if (it >= a.nitems) return;
   Prefetch f;
-  prefetch(f, item_rsrc(item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, xrow);
+  Item nxt = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
+  prefetch(f, item_rsrc(nxt, a), lc, xrow);
 
   for (; it < a.nitems; it += gridDim.x) {
-    const Item cur = item_of(it, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q);
+    const Item cur = nxt;   // the item prefetched last
     const int len = cur.len;
 
     // ---- commit the prefetched item to LDS.  Rows past the sequence end arrived as zeros;
@@ -312,7 +318,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // unconditional (the last item re-reads a valid item): a prefetch behind a branch would
     // make the wait counts after it conservative
     const int nx = min(it + int(gridDim.x), a.nitems - 1);
-    prefetch(f, item_rsrc(item_of(nx, a.nheads, a.nchunks, a.ngroups, a.seqlen, Q), a), lc, xrow);
+    nxt = item_of(nx, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
+    prefetch(f, item_rsrc(nxt, a), lc, xrow);
     __builtin_amdgcn_sched_barrier(0);
 
     float dtmax = red[0];
@@ -340,7 +347,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       const int l0 = 16 * lb;
       const int l = l0 + lcol_v;
       const bool lvalid = l < len;
-      const int jdiag = l0 & ~31;          // the 32-token block that holds the diagonal
+      // the 32-token block that holds the diagonal (uniform: scalar loop bounds below)
+      const int jdiag = __builtin_amdgcn_readfirstlane(l0 & ~31);
       const bool half = l0 != jdiag;       // its first 16 tokens lie before row l0
       const float a_l = acs2[l];
       const float a_0 = acs2[l0];
@@ -376,11 +384,11 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         for (int i = 0; i < 4; ++i) yf[pt][i] = float((yo1[pt][i] << 8) + yo2[pt][i]) * (E * hv[i]);
       }
 
-      // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized decay
-#pragma unroll 2
-      for (int jb = 0; jb < jdiag; jb += 32) {
-        v4i gm[2];
-        float4 w4[2];
+      // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized decay.
+      // G^T for a step on the INT8 matrix cores, then M' = fp16(G w) and y^T += x^T M'^T; two
+      // steps at a time with their own G and M' registers, so that the second step's integer
+      // products overlap the first step's conversions.
+      auto gstep = [&](int jb, v4i (&gm)[2], float4 (&w4)[2]) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
           const int js = jb + 16 * sb;
@@ -391,6 +399,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
         }
+      };
+      auto mstep = [&](int jb, const v4i (&gm)[2], const float4 (&w4)[2]) {
         v8h xop[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
@@ -409,6 +419,21 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt)
           yf[pt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop[pt], mop, yf[pt], 0, 0, 0);
+      };
+      int jb = 0;
+      for (; jb + 32 < jdiag; jb += 64) {
+        v4i ga[2], gb[2];
+        float4 wa[2], wb[2];
+        gstep(jb, ga, wa);
+        gstep(jb + 32, gb, wb);
+        mstep(jb, ga, wa);
+        mstep(jb + 32, gb, wb);
+      }
+      if (jb < jdiag) {
+        v4i ga[2];
+        float4 wa[2];
+        gstep(jb, ga, wa);
+        mstep(jb, ga, wa);
       }
 
       // the block holding the diagonal, exact per-element decay: sub-block 0 (tokens jdiag..+15)
@@ -485,7 +510,9 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   Params p{a.x, a.x_scale, a.B, a.B_scale, a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.y,
            s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.nchunks,
-           s.batch * s.nchunks * s.nheads};
+           s.batch * s.nchunks * s.nheads,
+           make_fastdiv(uint32_t(s.nheads)), make_fastdiv(uint32_t(s.nchunks)),
+           make_fastdiv(uint32_t(s.nheads / s.ngroups))};
   // one persistent block per CU (the LDS footprint allows one resident block)
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=

@@ -50,21 +50,6 @@ __device__ __forceinline__ void codes(const float (&v)[n], float s, uint32_t (&c
     if (slow[e]) c[e] = code_exact(v[e], s);
 }
 
-// Division by an invariant divisor d for n < 2^31 (round-up multiplier):
-// l = ceil(log2 d), m = ceil(2^(32+l) / d) - 2^32, n / d = (mulhi(n, m) + n) >> l.
-struct FastDiv {
-  uint32_t d, m, l;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint64_t m = ((uint64_t(1) << (32 + l)) + d - 1) / d - (uint64_t(1) << 32);
-  return FastDiv{d, uint32_t(m), l};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
-
 __device__ __forceinline__ void unpack8(v4u raw, float (&v)[8]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

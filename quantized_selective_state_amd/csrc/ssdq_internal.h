@@ -21,6 +21,21 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
+// Division by an invariant divisor d for n < 2^31 (round-up multiplier):
+// l = ceil(log2 d), m = ceil(2^(32+l) / d) - 2^32, n / d = (mulhi(n, m) + n) >> l.
+struct FastDiv {
+  uint32_t d, m, l;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << (32 + l)) + d - 1) / d - (uint64_t(1) << 32);
+  return FastDiv{d, uint32_t(m), l};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.l; }
+
 // Shape of one prefill call after validation.
 struct ScanShape {
   int32_t batch;
