@@ -165,17 +165,20 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const Item& it, const Params& a) {
   return r;
 }
 
-// Issue every global load of one item (nothing waits here).
-__device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow) {
+// Issue every global load of one item (nothing waits here); B and C only when the item starts
+// a new (batch, chunk, group) (bc, block-uniform).
+__device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow, bool bc) {
+  if (bc) {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) f.cq[pass][s2] = __builtin_bit_cast(v4i, buf_load16(r.C, lc.c_off[pass][s2]));
+#pragma unroll
+    for (int k = 0; k < kBTasks; ++k) f.bq[k] = buf_load16(r.B, lc.b_off[k]);
+  }
   f.acs = buf_loadf(r.acs, lc.acs_off);
   f.dt = buf_loadf(r.dt, lc.dt_off);
   f.hs = buf_loadf(r.hs, lc.hs_off);
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) f.cq[pass][s2] = __builtin_bit_cast(v4i, buf_load16(r.C, lc.c_off[pass][s2]));
-#pragma unroll
-  for (int k = 0; k < kBTasks; ++k) f.bq[k] = buf_load16(r.B, lc.b_off[k]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
 #pragma unroll
@@ -254,19 +257,26 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) hq_lane[s2][pt] = hpos(16 * pt + lcol, 64 * s2 + 16 * kg);
 
-  // Persistent block: items slot, slot + gridDim.x, ...  The global loads of the next item are
-  // issued right after the current item is committed to LDS and complete while the current
-  // item is computed.  slot is XCD-aware: the blocks of one XCD take consecutive items, i.e.
-  // neighbouring heads of one (batch, chunk), so that chunk's B and C and the dt lines it
-  // shares across heads are fetched into one L2 rather than into all of them.
-  int it = xcd_remap(blockIdx.x, gridDim.x);
-  if (it >= a.nitems) return;
+  // Persistent block: a contiguous range of items, i.e. consecutive heads of one (batch, chunk)
+  // (heads are the fastest item index).  Heads of one group share that chunk's B and C codes:
+  // they are loaded and committed only when the group changes, and C's registers and the B
+  // tile in LDS serve all the group's items of the range.  The global loads of the next item
+  // are issued right after the current item is committed to LDS and complete while the
+  // current item is computed.  The range is XCD-aware: the blocks of one XCD take consecutive
+  // ranges, so a chunk's B, C and the dt lines its heads share are fetched into one L2.
+  const int per = (a.nitems + int(gridDim.x) - 1) / int(gridDim.x);
+  int it = xcd_remap(blockIdx.x, gridDim.x) * per;
+  const int it_end = min(it + per, a.nitems);
+  if (it >= it_end) return;
   Prefetch f;
   Item nxt = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
-  prefetch(f, item_rsrc(nxt, a), lc, xrow);
+  bool nxt_bc = true;
+  prefetch(f, item_rsrc(nxt, a), lc, xrow, true);
+  v4i cqs[2][2];   // C codes of this lane's output rows (per pass, K half) for the current group
 
-  for (; it < a.nitems; it += gridDim.x) {
+  for (; it < it_end; ++it) {
     const Item cur = nxt;   // the item prefetched last
+    const bool new_bc = nxt_bc;
     const int len = cur.len;
 
     // ---- commit the prefetched item to LDS.  Rows past the sequence end arrived as zeros;
@@ -281,8 +291,10 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       if (lane == 0) red[wave] = dm;
     }
     if (tid < kMaxP) hsc[tid] = f.hs;
+    if (new_bc) {
 #pragma unroll
-    for (int k = 0; k < kBTasks; ++k) *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
+      for (int k = 0; k < kBTasks; ++k) *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
+    }
     if (tid < kHThreads) {   // wave-uniform
       // a full block arrives dword-transposed (piece q holds dword t of natural piece t, q)
 #pragma unroll
@@ -301,13 +313,14 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     }
     __syncthreads();
 
-    // ---- the C codes of this lane's output rows arrived with the prefetch; keep them before the
-    // next item's prefetch reuses the registers
-    v4i cqs[2][2];
+    // ---- the C codes of this lane's output rows arrived with the prefetch (new group); keep
+    // them before the next prefetch reuses the registers
+    if (new_bc) {
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass)
+      for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = f.cq[pass][s2];
+        for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = f.cq[pass][s2];
+    }
     const int hu = __builtin_amdgcn_readfirstlane(cur.h);
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
     const float sx = a.x_scale[hu], sB = a.B_scale[gu], sC = a.C_scale[gu];
@@ -315,11 +328,12 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     _Float16* ybase = a.y + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.nheads + cur.h) * P;
     __builtin_amdgcn_sched_barrier(0);
 
-    // unconditional (the last item re-reads a valid item): a prefetch behind a branch would
-    // make the wait counts after it conservative
-    const int nx = min(it + int(gridDim.x), a.nitems - 1);
+    // issued on every trip (the last item re-reads itself); only the B and C loads depend on
+    // whether the next item starts a new group
+    const int nx = min(it + 1, it_end - 1);
     nxt = item_of(nx, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
-    prefetch(f, item_rsrc(nxt, a), lc, xrow);
+    nxt_bc = nxt.b != cur.b || nxt.c != cur.c || nxt.g != cur.g;
+    prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc);
     __builtin_amdgcn_sched_barrier(0);
 
     float dtmax = red[0];
