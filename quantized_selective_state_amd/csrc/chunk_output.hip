@@ -7,8 +7,8 @@
 // carried state read out by C; SSDi8 Figure 1b / Table 5: ChunkBMM C.B^T on INT8).
 //
 // A persistent block (8 waves) walks (batch, chunk, head) items; each wave owns two 16-row
-// output blocks of an item (l and 15 - l, for balance), and the next item's global loads are in flight while an item is
-// computed (register prefetch, committed to LDS after the item).
+// output blocks of an item (see row_block), and the next item's global loads are in flight
+// while an item is computed (register prefetch, committed to LDS after the item).
 //  - G^T[j, l] = sum_n q_B[j, n] q_C[l, n] on v_mfma_i32_16x16x64_i8 (exact int32).
 //  - Decay mask, SSDi8-style decoupled from the matrix products: for a 32-token block that
 //    lies entirely before the 16 output rows l0..l0+15, exp(Acs_l - Acs_j) =
@@ -29,7 +29,7 @@
 namespace ssdq {
 namespace {
 
-constexpr int kThreads = 512;    // 8 waves: two 16-row output blocks (l and 15 - l) each at chunk 256
+constexpr int kThreads = 512;    // 8 waves: two 16-row output blocks each at chunk 256
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxQ = 256;
 constexpr int kMaxP = 64;
@@ -77,6 +77,17 @@ __device__ __forceinline__ v4h codes_to_f16(uint32_t biased) {
   const v2h a = __builtin_bit_cast(v2h, lo) + off;
   const v2h b = __builtin_bit_cast(v2h, hi) + off;
   return v4h{a[0], a[1], b[0], b[1]};
+}
+
+// The 16-row output block of a wave's pass.  Waves s and s + 4 share a SIMD and together own
+// blocks s, 15 - s, 4 + s, 11 - s, whose causal work (blocks before the diagonal: floor(b / 2))
+// is the same on every SIMD.  The SIMD issues the older wave s first, so it takes the larger
+// share (15 - s and 4 + s: 9 steps against 5), and the pair finishes together instead of
+// leaving wave s + 4 to run alone at the end.  Blocks at or past Q / 16 do not exist.
+static_assert(kWaves == 8 && kMaxQ == 256, "row_block covers 16 blocks with 8 waves");
+__device__ __forceinline__ int row_block(int wave, int pass) {
+  const int s = wave & 3;
+  return (wave >> 2) == 0 ? (pass == 0 ? 15 - s : 4 + s) : (pass == 0 ? s : 11 - s);
 }
 
 struct Item {
@@ -231,7 +242,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   }
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    const int lbp = pass == 0 ? wave : 2 * kWaves - 1 - wave;
+    const int lbp = row_block(wave, pass);
     const uint32_t l = uint32_t(16 * lbp + lcol);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -513,8 +524,9 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     };
 
     // two 16-row blocks per wave, l and 15 - l (balanced work)
-    if (wave < nlb) do_pass(wave, cqs[0]);
-    if (nlb > kWaves) do_pass(2 * kWaves - 1 - wave, cqs[1]);
+    const int lb0 = row_block(wave, 0), lb1 = row_block(wave, 1);
+    if (lb0 < nlb) do_pass(lb0, cqs[0]);
+    if (lb1 < nlb) do_pass(lb1, cqs[1]);
     __syncthreads();   // LDS is rewritten by the next item's commit
   }
 }
