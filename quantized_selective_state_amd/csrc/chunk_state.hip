@@ -488,7 +488,23 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
       // ---- the next chunk's tiles, into the other buffer (its last readers passed the barrier)
       dma_chunk(c + 1, Parity<1 - par.value>{});
 
-      // ---- the state entering the chunk, Hprev_c = H, as two INT8 limbs and a power-of-two row scale
+      // ---- S_c^T partial over this wave's 64-token steps (interleaved between the two waves)
+      if constexpr (Q == 64) {
+        if (kh == 0) {
+          kstep(acc, xt, bt, cl, 0, true);
+        } else {
+#pragma unroll
+          for (int t = 0; t < kNt; ++t)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
+        }
+      } else {
+        kstep(acc, xt, bt, cl, 64 * kh, true);
+        if constexpr (Q == 256) kstep(acc, xt, bt, cl, 64 * kh + 128, false);
+      }
+
+      // ---- the state entering the chunk, Hprev_c = H, as two INT8 limbs and a power-of-two row
+      // scale (after the products are issued: this VALU work runs while the matrix cores do)
       if (prow) {
         const float m = fmaxf(rmax[0][16 * pt + lcol], rmax[1][16 * pt + lcol]);
         const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
@@ -526,21 +542,6 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
         if (kh == 0 && kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
       }
 
-
-      // ---- S_c^T partial over this wave's 64-token steps (interleaved between the two waves)
-      if constexpr (Q == 64) {
-        if (kh == 0) {
-          kstep(acc, xt, bt, cl, 0, true);
-        } else {
-#pragma unroll
-          for (int t = 0; t < kNt; ++t)
-#pragma unroll
-            for (int k = 0; k < 3; ++k) acc[t][k] = v4i{0, 0, 0, 0};
-        }
-      } else {
-        kstep(acc, xt, bt, cl, 64 * kh, true);
-        if constexpr (Q == 256) kstep(acc, xt, bt, cl, 64 * kh + 128, false);
-      }
 
       // ---- fp32 partials; hand over the other wave's tiles, then H <- exp(Acs_last) H + S_c
       const float post = sxB * exp2i(gexp[cl]);
