@@ -501,6 +501,8 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
       } else {
         kstep(acc, xt, bt, cl, 64 * kh, true);
         if constexpr (Q == 256) kstep(acc, xt, bt, cl, 64 * kh + 128, false);
+        // let the scheduler interleave the operand reads, the limb arithmetic and the products
+        __builtin_amdgcn_iglp_opt(0);
       }
 
       // ---- the state entering the chunk, Hprev_c = H, as two INT8 limbs and a power-of-two row
