@@ -280,19 +280,12 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   const int it_end = min(it + per, a.nitems);
   if (it >= it_end) return;
   Prefetch f;
-  Item nxt = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
-  bool nxt_bc = true;
-  prefetch(f, item_rsrc(nxt, a), lc, xrow, true);
   v4i cqs[2][2];   // C codes of this lane's output rows (per pass, K half) for the current group
 
-  for (; it < it_end; ++it) {
-    const Item cur = nxt;   // the item prefetched last
-    const bool new_bc = nxt_bc;
-    const int len = cur.len;
-
-    // ---- commit the prefetched item to LDS.  Rows past the sequence end arrived as zeros;
-    // channels past P and states past N hold zeros or values that only meet zeros (the C codes
-    // past N are zero, and rows past P are never stored).
+  // ---- commit a prefetched item to LDS.  Rows past the sequence end arrived as zeros;
+  // channels past P and states past N hold zeros or values that only meet zeros (the C codes
+  // past N are zero, and rows past P are never stored).
+  auto commit = [&](bool new_bc) {
     if (tid < kMaxQ) {
       acs2[tid] = f.acs * kLog2e;
       dts[tid] = f.dt;
@@ -322,28 +315,43 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       // the second 8 channels: chunk + 1 before the swizzle
       *reinterpret_cast<v8h*>(xs + (lc.x_lds[k] ^ 8)) = v8h{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
     }
-    __syncthreads();
+  };
+  // the C codes of this lane's output rows arrive with a new group's prefetch; they are kept
+  // before the next prefetch reuses the registers
+  auto keep_c = [&] {
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = f.cq[pass][s2];
+  };
 
-    // ---- the C codes of this lane's output rows arrived with the prefetch (new group); keep
-    // them before the next prefetch reuses the registers
-    if (new_bc) {
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) cqs[pass][s2] = f.cq[pass][s2];
-    }
+  // The loop is rotated: an item's prefetch, its predecessor's stores and its commit all lie in
+  // one trip, so the commit's wait for the prefetched data counts back over a fixed number of
+  // stores (unconditional buffer stores) and never waits for the stores themselves.
+  Item cur = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
+  prefetch(f, item_rsrc(cur, a), lc, xrow, true);
+  commit(true);
+  __syncthreads();
+  keep_c();
+
+  for (; it < it_end; ++it) {
+    const int len = cur.len;
     const int hu = __builtin_amdgcn_readfirstlane(cur.h);
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
-    const float sx = a.x_scale[hu], sB = a.B_scale[gu], sC = a.C_scale[gu];
-    const float Dh = a.D ? a.D[hu] : 0.f;
-    _Float16* ybase = a.y + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.nheads + cur.h) * P;
+    // per-item scalars through the scalar cache (read-only data)
+    typedef const __attribute__((address_space(4))) float* cfp;
+    const float sx = *cfp(a.x_scale + hu), sB = *cfp(a.B_scale + gu), sC = *cfp(a.C_scale + gu);
+    const float Dh = a.D ? *cfp(a.D + hu) : 0.f;
+    const uint32_t yrow = uint32_t(a.nheads * P);
+    const Rsrc ry = make_rsrc(a.y + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.nheads + cur.h) * P,
+                              (uint32_t(len - 1) * yrow + uint32_t(P)) * 2u);
     __builtin_amdgcn_sched_barrier(0);
 
-    // issued on every trip (the last item re-reads itself); only the B and C loads depend on
-    // whether the next item starts a new group
+    // the next item's loads (the last trip re-reads its own item); only the B and C loads
+    // depend on whether the next item starts a new group
     const int nx = min(it + 1, it_end - 1);
-    nxt = item_of(nx, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
-    nxt_bc = nxt.b != cur.b || nxt.c != cur.c || nxt.g != cur.g;
+    const Item nxt = item_of(nx, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
+    const bool nxt_bc = nxt.b != cur.b || nxt.c != cur.c || nxt.g != cur.g;
     prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -513,21 +521,29 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 
       // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
       const float c_f = u_l * s_in;
-      _Float16* yrow = ybase + uint32_t(min(l, len - 1)) * uint32_t(a.nheads * P);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         v4h out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(yf[pt][i], c_f, yd[pt][i] * s_in));
-        if (lvalid && 16 * pt + 4 * kg_v < P) *reinterpret_cast<v4h*>(yrow + 16 * pt + 4 * kg_v) = out;
+        // unconditional store: rows past len and channels past P go out of range (dropped)
+        const uint32_t voff = (uint32_t(l) * yrow + uint32_t(16 * pt + 4 * kg_v)) * 2u;
+        const bool ok = lvalid & (16 * pt + 4 * kg_v < P);   // a select, not a branch
+        const uint32_t off = ok ? voff : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, out), ry, off, 0, 0);
       }
     };
 
     // two 16-row blocks per wave, l and 15 - l (balanced work)
-    const int lb0 = row_block(wave, 0), lb1 = row_block(wave, 1);
-    if (lb0 < nlb) do_pass(lb0, cqs[0]);
-    if (lb1 < nlb) do_pass(lb1, cqs[1]);
-    __syncthreads();   // LDS is rewritten by the next item's commit
+    // both passes run on every trip (a block past Q / 16 computes on zero rows and stores
+    // nothing), so that the number of stores after the prefetch is the same on every path
+    do_pass(row_block(wave, 0), cqs[0]);
+    do_pass(row_block(wave, 1), cqs[1]);
+    __syncthreads();   // every wave is done with the LDS tiles
+    commit(nxt_bc);
+    __syncthreads();
+    if (nxt_bc) keep_c();
+    cur = nxt;
   }
 }
 
