@@ -49,11 +49,15 @@ __device__ __forceinline__ v4h tr16(const _Float16* lds) {
   return __builtin_bit_cast(v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                      (__attribute__((address_space(3))) v4s*)(lds)));
 }
-// B codes: [j][n] int8, 128-byte rows, chunk c stored at c ^ ((j >> 1) & 7)
+// B codes: [j][n] int8, 128-byte rows, chunk c stored at c ^ ((j >> 1) & 7); within a full
+// 64-state block the states are in the carried state's order (dword-transposed), so that
+// C.B^T and C.Hprev share the C operand
 __device__ __forceinline__ int bpos(int j, int byte) {
   return j * kMaxN + ((((byte >> 4) ^ ((j >> 1) & 7)) << 4) | (byte & 15));
 }
-// Hprev limbs: two [p][n] int8 planes, 128-byte rows, same swizzle as the B codes
+// Hprev limbs: two [p][n] int8 planes, 128-byte rows in the workspace's byte order (a full
+// 64-state block dword-transposed), same 16-byte-chunk swizzle as the B codes.  C.Hprev sums
+// over the states in that order: the C operand of a full block is loaded in the same order.
 constexpr int kHPlane = kMaxP * kMaxN;
 __device__ __forceinline__ int hpos(int p, int byte) { return bpos(p, byte); }
 
@@ -112,13 +116,13 @@ __device__ __forceinline__ Item item_of(int it, FastDiv by_heads, FastDiv by_chu
 
 // Global data of one work item held in registers between its load and its LDS commit.
 constexpr int kBTasks = kMaxQ * 8 / kThreads;          // 16-byte B pieces per thread
-constexpr int kHThreads = 2 * kMaxP * 2;                // threads that load a 64-byte carried-state block
+static_assert(2 * kMaxP * (kMaxN / 32) == kThreads, "two 16-byte carried-state pieces per thread");
 constexpr int kXTasks = kMaxQ * (kMaxP / 16) / kThreads;   // 16-byte x pieces per thread
 struct Prefetch {
   float acs, dt, hs;
   v4i cq[2][2];                 // C codes of this lane's two output rows (per pass, K half)
   v4u bq[kBTasks];
-  v4u hq[4];                    // one 64-state block of one limb row (4 pieces)
+  v4u hq[2];                    // two 16-byte pieces of one limb row
   v4u xq[kXTasks];
 };
 
@@ -146,9 +150,8 @@ struct Params {
 struct LaneConst {
   uint32_t b_off[kBTasks];      // B piece: token row j * G*N + 16-byte column group
   int b_lds[kBTasks];
-  uint32_t h_off[4];            // carried-state pieces of this thread's 64-state block
-  int h_lds;                    // LDS position of its first natural-order piece
-  bool h_full;                  // the block is full (stored dword-transposed)
+  uint32_t h_off[2];            // this thread's two carried-state pieces (limb, row, 32 bytes)
+  int h_lds[2];                 // their LDS positions (the workspace order is kept)
   uint32_t x_off[kXTasks];      // x piece: token row j * H*P + 16-byte column group
   int x_lds[kXTasks];           // LDS position (halves) of its first 8 channels
   uint32_t c_off[2][2];         // C codes of this lane's output row, per pass and K half
@@ -178,20 +181,37 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const Item& it, const Params& a) {
 
 // Issue every global load of one item (nothing waits here); B and C only when the item starts
 // a new (batch, chunk, group) (bc, block-uniform).
-__device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow, bool bc) {
+__device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow, bool bc,
+                                         int N, int kg) {
   if (bc) {
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) f.cq[pass][s2] = __builtin_bit_cast(v4i, buf_load16(r.C, lc.c_off[pass][s2]));
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint32_t o = lc.c_off[pass][s2];
+        if (64 * s2 + 64 <= N) {
+          // a full 64-state block: the carried state sits in LDS in its workspace order
+          // (dword-transposed), so this operand takes the same K order: dword t holds states
+          // 64 s2 + 16 t + 4 kg + (0..3)
+          const uint32_t ob = o == kOutOfRange ? kOutOfRange : o - 12u * uint32_t(kg);
+          v4u c;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) c[t] = buf_load4(r.C, ob == kOutOfRange ? kOutOfRange : ob + 16u * t);
+          f.cq[pass][s2] = __builtin_bit_cast(v4i, c);
+        } else {
+          f.cq[pass][s2] = __builtin_bit_cast(v4i, buf_load16(r.C, o));
+        }
+      }
 #pragma unroll
     for (int k = 0; k < kBTasks; ++k) f.bq[k] = buf_load16(r.B, lc.b_off[k]);
   }
-  f.acs = buf_loadf(r.acs, lc.acs_off);
-  f.dt = buf_loadf(r.dt, lc.dt_off);
-  f.hs = buf_loadf(r.hs, lc.hs_off);
+  if (threadIdx.x < kMaxQ) {   // wave-uniform: one value per token
+    f.acs = buf_loadf(r.acs, lc.acs_off);
+    f.dt = buf_loadf(r.dt, lc.dt_off);
+  }
+  if (threadIdx.x < kMaxP) f.hs = buf_loadf(r.hs, lc.hs_off);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
+  for (int k = 0; k < 2; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
 #pragma unroll
   for (int k = 0; k < kXTasks; ++k) f.xq[k] = buf_load16(r.x, lc.x_off[k]);
 }
@@ -224,14 +244,13 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     lc.b_lds[k] = bpos(j, 16 * sg);
   }
   {
-    // threads 0..255: limb tid / 128, row (tid / 2) % 64, 64-state block tid % 2
-    const int limb = tid >> 7, p = (tid >> 1) & (kMaxP - 1), bk = tid & 1;
+    // limb tid / 256, row (tid / 4) % 64, bytes 32 (tid % 4) .. + 31 of the row
+    const int limb = tid >> 8, p = (tid >> 2) & (kMaxP - 1), b0 = 32 * (tid & 3);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      lc.h_off[q] = (tid < kHThreads && p < P && 64 * bk + 16 * q < N) ? uint32_t(limb * P * N + p * N + 64 * bk + 16 * q)
-                                                                       : kOutOfRange;
-    lc.h_lds = limb * kHPlane + hpos(p, 64 * bk);
-    lc.h_full = 64 * bk + 64 <= N;
+    for (int q = 0; q < 2; ++q) {
+      lc.h_off[q] = (p < P && b0 + 16 * q < N) ? uint32_t(limb * P * N + p * N + b0 + 16 * q) : kOutOfRange;
+      lc.h_lds[q] = limb * kHPlane + hpos(p, b0 + 16 * q);
+    }
   }
 #pragma unroll
   for (int k = 0; k < kXTasks; ++k) {
@@ -279,7 +298,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   int it = xcd_remap(blockIdx.x, gridDim.x) * per;
   const int it_end = min(it + per, a.nitems);
   if (it >= it_end) return;
-  Prefetch f;
+  Prefetch f{};
   v4i cqs[2][2];   // C codes of this lane's output rows (per pass, K half) for the current group
 
   // ---- commit a prefetched item to LDS.  Rows past the sequence end arrived as zeros;
@@ -291,22 +310,29 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       dts[tid] = f.dt;
     }
     {
-      const float dm = wave_max(f.dt);   // waves 4..7 hold the same tokens as waves 0..3
+      const float dm = tid < kMaxQ ? wave_max(f.dt) : 0.f;   // dt >= 0; waves 4..7 load none
       if (lane == 0) red[wave] = dm;
     }
     if (tid < kMaxP) hsc[tid] = f.hs;
     if (new_bc) {
+      // B goes to LDS in the same state order as the carried state and the C operand: in a
+      // full 64-state block, dword q of natural piece t (states 16 t + 4 q ..) lands at dword t
+      // of piece q (the 16-byte-chunk swizzle keeps the dword position)
+      const int t = tid & 3;                             // piece within its 64-state block
+      const bool full = 64 * ((tid >> 2) & 1) + 64 <= N;   // that block is full
 #pragma unroll
-      for (int k = 0; k < kBTasks; ++k) *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
-    }
-    if (tid < kHThreads) {   // wave-uniform
-      // a full block arrives dword-transposed (piece q holds dword t of natural piece t, q)
+      for (int k = 0; k < kBTasks; ++k) {
+        if (full) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4u tr = {f.hq[0][t], f.hq[1][t], f.hq[2][t], f.hq[3][t]};
-        *reinterpret_cast<v4u*>(Hq + (lc.h_lds ^ (t << 4))) = lc.h_full ? tr : f.hq[t];
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint32_t*>(Bs + ((lc.b_lds[k] ^ ((t ^ q) << 4)) + 4 * t)) = f.bq[k][q];
+        } else {
+          *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
+        }
       }
     }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(Hq + lc.h_lds[q]) = f.hq[q];
 #pragma unroll
     for (int k = 0; k < kXTasks; ++k) {
       const v4u u = f.xq[k] ^ 0x80808080u;
@@ -329,7 +355,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // one trip, so the commit's wait for the prefetched data counts back over a fixed number of
   // stores (unconditional buffer stores) and never waits for the stores themselves.
   Item cur = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
-  prefetch(f, item_rsrc(cur, a), lc, xrow, true);
+  prefetch(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
   commit(true);
   __syncthreads();
   keep_c();
@@ -352,7 +378,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const int nx = min(it + 1, it_end - 1);
     const Item nxt = item_of(nx, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
     const bool nxt_bc = nxt.b != cur.b || nxt.c != cur.c || nxt.g != cur.g;
-    prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc);
+    prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc, N, kg);
     __builtin_amdgcn_sched_barrier(0);
 
     float dtmax = red[0];
