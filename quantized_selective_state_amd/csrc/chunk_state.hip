@@ -55,6 +55,10 @@ __device__ __forceinline__ int bpos(int j, int byte) {
 
 // a * b + c for a, b < 2^24 (one v_mad_u32_u24), modulo 2^32
 __device__ __forceinline__ uint32_t mad24(uint32_t a, uint32_t b, uint32_t c) { return __umul24(a, b) + c; }
+// a * b + c for signed 24-bit a, b (one v_mad_i32_i24), |a b + c| < 2^31
+__device__ __forceinline__ int32_t mad24s(int32_t a, int32_t b, int32_t c) { return __mul24(a, b) + c; }
+// byte k of x, sign-extended (one v_bfe_i32)
+__device__ __forceinline__ int32_t sbyte(uint32_t x, int k) { return __builtin_amdgcn_sbfe(int32_t(x), 8 * k, 8); }
 
 // 4x4 byte transpose: out[i] byte r = in[r] byte i.
 __device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
@@ -282,7 +286,6 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(16))) uint8_t bs0[Q * kMaxN];
   __shared__ __attribute__((aligned(16))) uint8_t bs1[Q * kMaxN];
   __shared__ __attribute__((aligned(16))) uint32_t om[kGroup][Q];       // OM_j of the group's chunks
-  __shared__ __attribute__((aligned(16))) uint32_t cb[kGroup][Q];       // CB_j
   __shared__ __attribute__((aligned(16))) v4f xch[kSWaves][4][kWave];   // partial S handed over
   __shared__ float rmax[2][kMaxP];                                      // half-row maxima
   __shared__ float gdec[kGroup];                                        // exp(Acs_last) per chunk
@@ -407,9 +410,8 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     const int e = min(max(ceil_log2_pos(wave_max(wm)), -100), 100);
 #pragma unroll
     for (int u = 0; u < kTok; ++u) {
-      const uint32_t o = uint32_t(fminf(w[u] * exp2i(24 - e), 16777215.f) + 0.5f);
-      om[wave][lane * kTok + u] = o;
-      cb[wave][lane * kTok + u] = 8421376u - (o << 7);   // 256 * 32896 - 128 OM (mod 2^32)
+      // a signed 24-bit weight (23 bits of magnitude): OM_j = round(w_j 2^(23 - e))
+      om[wave][lane * kTok + u] = uint32_t(fminf(w[u] * exp2i(23 - e), 8388607.f) + 0.5f);
     }
     if (lane == 0) {
       gdec[wave] = __builtin_amdgcn_exp2f(a_last * kLog2e);
@@ -438,13 +440,10 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
       const v4u o4 = *reinterpret_cast<const v4u*>(&om[cl][j0 + 4 * dw]);
-      const v4u c4 = *reinterpret_cast<const v4u*>(&cb[cl][j0 + 4 * dw]);
-      const uint32_t u = xw[dw] ^ 0x80808080u;
+      // W = q OM + 256 * 32896: floor(W / 256) = floor(65536 t + 32896), t = q OM / 2^24
       uint32_t W[4], pl[4];
-      W[0] = mad24(u & 0xffu, o4[0], c4[0]);
-      W[1] = mad24((u >> 8) & 0xffu, o4[1], c4[1]);
-      W[2] = mad24((u >> 16) & 0xffu, o4[2], c4[2]);
-      W[3] = mad24(u >> 24, o4[3], c4[3]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) W[k] = uint32_t(mad24s(sbyte(xw[dw], k), int32_t(o4[k]), 8421376));
       transpose4x4(W, pl);
       l1[dw] = int(pl[3]);
       l2[dw] = int(pl[2] ^ 0x80808080u);
@@ -546,7 +545,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
 
 
       // ---- fp32 partials; hand over the other wave's tiles, then H <- exp(Acs_last) H + S_c
-      const float post = sxB * exp2i(gexp[cl]);
+      const float post = sxB * exp2i(gexp[cl] + 1);   // t = x_scaled / 2^(e + 1) (23-bit weights)
       const float post_lo = post * (1.f / 65536.f);
       auto partial = [&](int t) {
         v4f r;
