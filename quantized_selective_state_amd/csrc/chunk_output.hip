@@ -217,14 +217,18 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
 }
 
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[kMaxQ * kMaxP];
+  // Per-item tiles in two buffers (item k of the block in buffer k % 2): a wave commits the next
+  // item into the other buffer as soon as its own passes are done, and one barrier per item
+  // separates it from the waves still reading the current one.  B changes only with the group
+  // and has one buffer.
+  __shared__ __attribute__((aligned(16))) _Float16 xs_buf[2][kMaxQ * kMaxP];
+  __shared__ __attribute__((aligned(16))) int8_t Hq_buf[2][2 * kHPlane];
+  __shared__ __attribute__((aligned(16))) float hsc_buf[2][kMaxP];
+  __shared__ __attribute__((aligned(16))) float acs2_buf[2][kMaxQ];   // Acs * log2(e)
+  __shared__ __attribute__((aligned(16))) float dts_buf[2][kMaxQ];    // dt (0 past the sequence end)
+  __shared__ float red_buf[2][kWaves];
   __shared__ __attribute__((aligned(16))) int8_t Bs[kMaxQ * kMaxN];
-  __shared__ __attribute__((aligned(16))) int8_t Hq[2 * kHPlane];
-  __shared__ __attribute__((aligned(16))) float hsc[kMaxP];
-  __shared__ __attribute__((aligned(16))) float acs2[kMaxQ];   // Acs * log2(e)
-  __shared__ __attribute__((aligned(16))) float dts[kMaxQ];    // dt (0 past the sequence end)
   __shared__ __attribute__((aligned(16))) float wl[kWaves][kMaxQ];
-  __shared__ float red[kWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -304,17 +308,30 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // ---- commit a prefetched item to LDS.  Rows past the sequence end arrived as zeros;
   // channels past P and states past N hold zeros or values that only meet zeros (the C codes
   // past N are zero, and rows past P are never stored).
-  auto commit = [&](bool new_bc) {
+  auto commit = [&](int bf) {
     if (tid < kMaxQ) {
-      acs2[tid] = f.acs * kLog2e;
-      dts[tid] = f.dt;
+      acs2_buf[bf][tid] = f.acs * kLog2e;
+      dts_buf[bf][tid] = f.dt;
     }
     {
       const float dm = tid < kMaxQ ? wave_max(f.dt) : 0.f;   // dt >= 0; waves 4..7 load none
-      if (lane == 0) red[wave] = dm;
+      if (lane == 0) red_buf[bf][wave] = dm;
     }
-    if (tid < kMaxP) hsc[tid] = f.hs;
-    if (new_bc) {
+    if (tid < kMaxP) hsc_buf[bf][tid] = f.hs;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(Hq_buf[bf] + lc.h_lds[q]) = f.hq[q];
+#pragma unroll
+    for (int k = 0; k < kXTasks; ++k) {
+      const v4u u = f.xq[k] ^ 0x80808080u;
+      const v4h h0 = codes_to_f16(u[0]), h1 = codes_to_f16(u[1]), h2 = codes_to_f16(u[2]), h3 = codes_to_f16(u[3]);
+      *reinterpret_cast<v8h*>(xs_buf[bf] + lc.x_lds[k]) = v8h{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      // the second 8 channels: chunk + 1 before the swizzle
+      *reinterpret_cast<v8h*>(xs_buf[bf] + (lc.x_lds[k] ^ 8)) = v8h{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
+    }
+  };
+  // B of a new group (its prefetch arrived with the item's); written while no wave reads B
+  auto commit_b = [&] {
+    {
       // B goes to LDS in the same state order as the carried state and the C operand: in a
       // full 64-state block, dword q of natural piece t (states 16 t + 4 q ..) lands at dword t
       // of piece q (the 16-byte-chunk swizzle keeps the dword position)
@@ -331,16 +348,6 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         }
       }
     }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(Hq + lc.h_lds[q]) = f.hq[q];
-#pragma unroll
-    for (int k = 0; k < kXTasks; ++k) {
-      const v4u u = f.xq[k] ^ 0x80808080u;
-      const v4h h0 = codes_to_f16(u[0]), h1 = codes_to_f16(u[1]), h2 = codes_to_f16(u[2]), h3 = codes_to_f16(u[3]);
-      *reinterpret_cast<v8h*>(xs + lc.x_lds[k]) = v8h{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-      // the second 8 channels: chunk + 1 before the swizzle
-      *reinterpret_cast<v8h*>(xs + (lc.x_lds[k] ^ 8)) = v8h{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
-    }
   };
   // the C codes of this lane's output rows arrive with a new group's prefetch; they are kept
   // before the next prefetch reuses the registers
@@ -356,9 +363,11 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // stores (unconditional buffer stores) and never waits for the stores themselves.
   Item cur = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
   prefetch(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
-  commit(true);
+  commit(0);
+  commit_b();
   __syncthreads();
   keep_c();
+  int buf = 0;   // the current item's buffer
 
   for (; it < it_end; ++it) {
     const int len = cur.len;
@@ -381,6 +390,13 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc, N, kg);
     __builtin_amdgcn_sched_barrier(0);
 
+    // this trip's view of the per-item tiles
+    const _Float16* const xs = xs_buf[buf];
+    const int8_t* const Hq = Hq_buf[buf];
+    const float* const hsc = hsc_buf[buf];
+    const float* const acs2 = acs2_buf[buf];
+    const float* const dts = dts_buf[buf];
+    const float* const red = red_buf[buf];
     float dtmax = red[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) dtmax = fmaxf(dtmax, red[i]);
@@ -565,11 +581,15 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // nothing), so that the number of stores after the prefetch is the same on every path
     do_pass(row_block(wave, 0), cqs[0]);
     do_pass(row_block(wave, 1), cqs[1]);
-    __syncthreads();   // every wave is done with the LDS tiles
-    commit(nxt_bc);
-    __syncthreads();
-    if (nxt_bc) keep_c();
+    commit(buf ^ 1);   // the other buffer: its last readers passed the previous barrier
+    __syncthreads();   // the next item is in LDS, and every wave is done with this one
+    if (nxt_bc) {
+      commit_b();
+      __syncthreads();
+      keep_c();
+    }
     cur = nxt;
+    buf ^= 1;
   }
 }
 
