@@ -164,18 +164,62 @@ struct ItemRsrc {
   Rsrc acs, dt, hs, B, H, x, C;
 };
 
-__device__ __forceinline__ ItemRsrc item_rsrc(const Item& it, const Params& a) {
-  const int P = a.P, N = a.N, G = a.ngroups, H = a.nheads;
-  const uint32_t last = uint32_t(it.len - 1);
+// One work item's position, as 32-bit row indices into its operands (every index is below
+// batch * seqlen * nheads < 2^31).  Consecutive items of a block's range are mostly consecutive
+// heads of one (batch, chunk): the next one is then reached by adding fixed steps, and only a
+// change of (batch, chunk) decodes the item index again.
+struct ItemPos {
+  int h, g, hg, len;   // hg: the head's index within its group
+  uint32_t row;        // (b seqlen + t0) nheads + h: first (token, head) row of x, y and dt
+  uint32_t grow;       // (b seqlen + t0) ngroups + g: first (token, group) row of B and C
+  uint32_t seg;        // (b nchunks + c) nheads + h: carried-state slot (limbs, row scales)
+  uint32_t aseg;       // (b nheads + h) nchunks + c: the Acs row
+};
+
+__device__ __forceinline__ ItemPos item_at(int it, const Params& a) {
+  const Item r = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, a.Q);
+  const uint32_t tok = uint32_t(int64_t(r.b) * a.seqlen + r.t0);
+  ItemPos p;
+  p.h = r.h;
+  p.g = r.g;
+  p.hg = r.h - r.g * int(a.by_hpg.d);
+  p.len = r.len;
+  p.row = tok * uint32_t(a.nheads) + uint32_t(r.h);
+  p.grow = tok * uint32_t(a.ngroups) + uint32_t(r.g);
+  p.seg = (uint32_t(r.b) * uint32_t(a.nchunks) + uint32_t(r.c)) * uint32_t(a.nheads) + uint32_t(r.h);
+  p.aseg = (uint32_t(r.b) * uint32_t(a.nheads) + uint32_t(r.h)) * uint32_t(a.nchunks) + uint32_t(r.c);
+  return p;
+}
+
+// p (item it) becomes item it + 1; returns whether the (batch, chunk, group) changed
+__device__ __forceinline__ bool item_next(ItemPos& p, int it, const Params& a) {
+  if (p.h + 1 < a.nheads) {
+    p.h += 1;
+    p.row += 1;
+    p.seg += 1;
+    p.aseg += uint32_t(a.nchunks);
+    if (++p.hg < int(a.by_hpg.d)) return false;
+    p.hg = 0;
+    p.g += 1;
+    p.grow += 1;
+    return true;
+  }
+  p = item_at(it + 1, a);
+  return true;
+}
+
+__device__ __forceinline__ uint64_t wide(uint32_t i, uint32_t stride) { return uint64_t(i) * stride; }
+
+__device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a) {
+  const uint32_t last = uint32_t(p.len - 1), gn = uint32_t(a.ngroups * a.N), P = uint32_t(a.P), N = uint32_t(a.N);
   ItemRsrc r;
-  r.acs = make_rsrc(a.acs + ((int64_t(it.b) * H + it.h) * a.nchunks + it.c) * a.Q, uint32_t(a.Q) * 4u);
-  r.dt = make_rsrc(a.dt + (int64_t(it.b) * a.seqlen + it.t0) * H + it.h, (last * uint32_t(H) + 1u) * 4u);
-  r.hs = make_rsrc(a.hscale + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * P, uint32_t(P) * 4u);
-  r.B = make_rsrc(a.B + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N, last * uint32_t(G * N) + N);
-  r.H = make_rsrc(a.hprev + ((int64_t(it.b) * a.nchunks + it.c) * H + it.h) * int64_t(2 * P) * N,
-                  uint32_t(2 * P * N));
-  r.x = make_rsrc(a.x + ((int64_t(it.b) * a.seqlen + it.t0) * H + it.h) * P, last * uint32_t(H * P) + P);
-  r.C = make_rsrc(a.C + ((int64_t(it.b) * a.seqlen + it.t0) * G + it.g) * N, last * uint32_t(G * N) + N);
+  r.acs = make_rsrc(a.acs + wide(p.aseg, uint32_t(a.Q)), uint32_t(a.Q) * 4u);
+  r.dt = make_rsrc(a.dt + p.row, (last * uint32_t(a.nheads) + 1u) * 4u);
+  r.hs = make_rsrc(a.hscale + wide(p.seg, P), P * 4u);
+  r.B = make_rsrc(a.B + wide(p.grow, N), last * gn + N);
+  r.H = make_rsrc(a.hprev + wide(p.seg, 2u * P * N), 2u * P * N);
+  r.x = make_rsrc(a.x + wide(p.row, P), last * uint32_t(a.nheads) * P + P);
+  r.C = make_rsrc(a.C + wide(p.grow, N), last * gn + N);
   return r;
 }
 
@@ -361,7 +405,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // The loop is rotated: an item's prefetch, its predecessor's stores and its commit all lie in
   // one trip, so the commit's wait for the prefetched data counts back over a fixed number of
   // stores (unconditional buffer stores) and never waits for the stores themselves.
-  Item cur = item_of(it, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
+  ItemPos cur = item_at(it, a);
   prefetch(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
   commit(0);
   commit_b();
@@ -378,15 +422,14 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const float sx = *cfp(a.x_scale + hu), sB = *cfp(a.B_scale + gu), sC = *cfp(a.C_scale + gu);
     const float Dh = a.D ? *cfp(a.D + hu) : 0.f;
     const uint32_t yrow = uint32_t(a.nheads * P);
-    const Rsrc ry = make_rsrc(a.y + ((int64_t(cur.b) * a.seqlen + cur.t0) * a.nheads + cur.h) * P,
-                              (uint32_t(len - 1) * yrow + uint32_t(P)) * 2u);
+    const Rsrc ry = make_rsrc(a.y + wide(cur.row, uint32_t(P)), (uint32_t(len - 1) * yrow + uint32_t(P)) * 2u);
     __builtin_amdgcn_sched_barrier(0);
 
     // the next item's loads (the last trip re-reads its own item); only the B and C loads
     // depend on whether the next item starts a new group
-    const int nx = min(it + 1, it_end - 1);
-    const Item nxt = item_of(nx, a.by_heads, a.by_chunks, a.by_hpg, a.seqlen, Q);
-    const bool nxt_bc = nxt.b != cur.b || nxt.c != cur.c || nxt.g != cur.g;
+    ItemPos nxt = cur;
+    bool nxt_bc = false;
+    if (it + 1 < it_end) nxt_bc = item_next(nxt, it, a);
     prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc, N, kg);
     __builtin_amdgcn_sched_barrier(0);
 
