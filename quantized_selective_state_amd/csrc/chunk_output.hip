@@ -223,8 +223,8 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a)
   return r;
 }
 
-// Issue every global load of one item (nothing waits here); B and C only when the item starts
-// a new (batch, chunk, group) (bc, block-uniform).
+// Issue the global loads of one item except its x codes (nothing waits here); B and C only when
+// the item starts a new (batch, chunk, group) (bc, block-uniform).
 __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow, bool bc,
                                          int N, int kg) {
   if (bc) {
@@ -256,6 +256,10 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
   if (threadIdx.x < kMaxP) f.hs = buf_loadf(r.hs, lc.hs_off);
 #pragma unroll
   for (int k = 0; k < 2; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
+}
+// The x codes of one item: issued apart from the rest, so that fewer loads queue at once for the
+// CU's address units and the wave stalls less at their issue.
+__device__ __forceinline__ void prefetch_x(Prefetch& f, const ItemRsrc& r, const LaneConst& lc) {
 #pragma unroll
   for (int k = 0; k < kXTasks; ++k) f.xq[k] = buf_load16(r.x, lc.x_off[k]);
 }
@@ -407,6 +411,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // stores (unconditional buffer stores) and never waits for the stores themselves.
   ItemPos cur = item_at(it, a);
   prefetch(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
+  prefetch_x(f, item_rsrc(cur, a), lc);
   commit(0);
   commit_b();
   __syncthreads();
@@ -430,7 +435,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     ItemPos nxt = cur;
     bool nxt_bc = false;
     if (it + 1 < it_end) nxt_bc = item_next(nxt, it, a);
-    prefetch(f, item_rsrc(nxt, a), lc, xrow, nxt_bc, N, kg);
+    const ItemRsrc nrs = item_rsrc(nxt, a);
+    prefetch(f, nrs, lc, xrow, nxt_bc, N, kg);
     __builtin_amdgcn_sched_barrier(0);
 
     // this trip's view of the per-item tiles
@@ -453,6 +459,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const float s_in = sx * sCB * exp2i(kM);
     const float fkM = float(kM);
     const float Dp = Dh / sCB * exp2i(-kM);   // D' (0 without D)
+    const float Ek = sC / (256.f * s_in);      // carried-state readout factor, times exp(Acs_l0) per pass
 
     // The lane index is re-materialized per item (an empty asm makes it opaque), so that the
     // per-lane masks below (causal mask, store guards) are recomputed with a few compares
@@ -471,8 +478,32 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       const float a_l = acs2[l];
       const float a_0 = acs2[l0];
 
-      // weights of the blocks before the diagonal, relative to row l0, times 2^-kM (<= 1 each)
-      for (int j = lane; j < jdiag; j += kWave) wlw[j] = __builtin_amdgcn_exp2f(a_0 - acs2[j] - fkM) * dts[j];
+      // Token weights times 2^-kM.  Blocks before the diagonal: relative to row l0,
+      // exp(Acs_l0 - Acs_j) dt_j <= dt_j.  The 32 tokens of the diagonal block: relative to its
+      // first token m = jdiag, exp(Acs_m - Acs_j) dt_j >= dt_j, which with the row factor
+      // exp(Acs_l - Acs_m) <= 1 gives the decay of each entry.  That factorized form is used
+      // while the block's weights stay below 2^100 (their products with the int32 C.B^T
+      // entries are then finite fp32); otherwise every entry's decay is taken on its own.
+      const float a_m = acs2[jdiag];
+      bool big = false;
+      {
+        const int j = 4 * lane;   // four tokens per lane, all on one side of jdiag (a multiple of 32)
+        if (j < jdiag + 32) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&acs2[j]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&dts[j]);
+          const float r = (j < jdiag ? a_0 : a_m) - fkM;
+          float4 w;
+          w.x = __builtin_amdgcn_exp2f(r - a4.x) * d4.x;
+          w.y = __builtin_amdgcn_exp2f(r - a4.y) * d4.y;
+          w.z = __builtin_amdgcn_exp2f(r - a4.z) * d4.z;
+          w.w = __builtin_amdgcn_exp2f(r - a4.w) * d4.w;
+          *reinterpret_cast<float4*>(&wlw[j]) = w;
+          // compared one by one: an inf weight times dt = 0 (rows past the sequence end) is NaN
+          const bool fin = (w.x < 0x1p100f) & (w.y < 0x1p100f) & (w.z < 0x1p100f) & (w.w < 0x1p100f);
+          big = (j >= jdiag) & !fin;
+        }
+      }
+      const bool factored = __builtin_amdgcn_ballot_w64(big) == 0;
       __builtin_amdgcn_wave_barrier();
       const float u_l = __builtin_amdgcn_exp2f(a_l - a_0);
 
@@ -492,7 +523,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
           yo2[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h2, cq[s2], s2 == 0 ? z : yo2[pt], 0, 0, 0);
         }
       }
-      const float E = __builtin_amdgcn_exp2f(fminf(a_0, 0.f)) * sC / (256.f * s_in);
+      const float E = __builtin_amdgcn_exp2f(fminf(a_0, 0.f)) * Ek;
       v4f yf[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
@@ -570,29 +601,53 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
         }
-        const float a_lk = a_l - fkM;
         v8h mop;
+        if (factored) {
+          const float e_l = __builtin_amdgcn_exp2f(a_l - a_m);   // rows l >= m: <= 1
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const bool diag_sb = half ? sb == 1 : sb == 0;
-          if (!half && sb == 1) {   // entirely after the block's rows
+          for (int sb = 0; sb < 2; ++sb) {
+            const bool diag_sb = half ? sb == 1 : sb == 0;
+            if (!half && sb == 1) {   // entirely after the block's rows
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mop[4 + i] = _Float16(0.f);
-            continue;
-          }
-          const int jq = (sb == 0 ? jb : j1) + 4 * kg;
-          const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
-          const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float m = float(gm[sb][i]) * __builtin_amdgcn_exp2f(fminf(a_lk - av[i], -fkM)) * dv[i];
-            if (diag_sb) {
-              const int j = jb + 16 * sb + 4 * kg_v + i;
-              m = j < l ? m : (j == l ? m + Dp : 0.f);
+              for (int i = 0; i < 4; ++i) mop[4 + i] = _Float16(0.f);
+              continue;
             }
-            mop[4 * sb + i] = _Float16(m);
+            const float4 f4 = *reinterpret_cast<const float4*>(wl_lane + (sb == 0 ? jb : j1));
+            const float fv[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float m = float(gm[sb][i]) * fv[i] * e_l;
+              if (diag_sb) {
+                const int j = jb + 16 * sb + 4 * kg_v + i;
+                m = j < l ? m : (j == l ? m + Dp : 0.f);
+              }
+              mop[4 * sb + i] = _Float16(m);
+            }
+          }
+        } else {
+          const float a_lk = a_l - fkM;
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const bool diag_sb = half ? sb == 1 : sb == 0;
+            if (!half && sb == 1) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) mop[4 + i] = _Float16(0.f);
+              continue;
+            }
+            const int jq = (sb == 0 ? jb : j1) + 4 * kg;
+            const float4 a4 = *reinterpret_cast<const float4*>(&acs2[jq]);
+            const float4 d4 = *reinterpret_cast<const float4*>(&dts[jq]);
+            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float m = float(gm[sb][i]) * __builtin_amdgcn_exp2f(fminf(a_lk - av[i], -fkM)) * dv[i];
+              if (diag_sb) {
+                const int j = jb + 16 * sb + 4 * kg_v + i;
+                m = j < l ? m : (j == l ? m + Dp : 0.f);
+              }
+              mop[4 * sb + i] = _Float16(m);
+            }
           }
         }
 #pragma unroll
@@ -619,10 +674,13 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       }
     };
 
-    // two 16-row blocks per wave, l and 15 - l (balanced work)
-    // both passes run on every trip (a block past Q / 16 computes on zero rows and stores
-    // nothing), so that the number of stores after the prefetch is the same on every path
+    // two 16-row blocks per wave, l and 15 - l (balanced work), the next item's x codes loaded
+    // between them.  Both passes run on every trip (a block past Q / 16 computes on zero rows and
+    // stores nothing), so that the number of stores after each load is the same on every path.
     do_pass(row_block(wave, 0), cqs[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_x(f, nrs, lc);
+    __builtin_amdgcn_sched_barrier(0);
     do_pass(row_block(wave, 1), cqs[1]);
     commit(buf ^ 1);   // the other buffer: its last readers passed the previous barrier
     __syncthreads();   // the next item is in LDS, and every wave is done with this one

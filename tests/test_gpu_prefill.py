@@ -65,7 +65,9 @@ def test_without_D_and_h0():
 
 
 def test_large_dt_and_strong_decay():
-    # dt up to ~8 and A down to -16: the decay mask spans many orders of magnitude
+    # dt up to ~8 and A down to -16: the decay mask spans many orders of magnitude, and within
+    # a 32-token block the decay can pass 2^100, where the output kernel stops factorizing the
+    # block's decay and takes each entry's own (both forms occur across the heads here)
     inp = workloads.make_custom_prefill(15, batch=1, seqlen=512, nheads=4, headdim=64, dstate=128, ngroups=1,
                                         chunk=256)
     inp["dt"] = (inp["dt"] * 30).astype(np.float32)
@@ -77,8 +79,18 @@ def test_no_decay_and_decay_to_zero():
                                         chunk=128, h0_std=0.1)
     inp["A"] = np.zeros_like(inp["A"])
     _check_full(inp, tag="A=0")
-    inp["A"] = np.full_like(inp["A"], -1e5)
+    inp["A"] = np.full_like(inp["A"], -1e5)   # every diagonal block past the factorized range
     _check_full(inp, tag="A=-1e5")
+
+
+def test_strong_decay_with_ragged_tail():
+    # the last chunk ends mid-block: past the sequence end dt is 0 while the decay weights of a
+    # strongly decaying block overflow, and no inf * 0 may reach the outputs
+    inp = workloads.make_custom_prefill(17, batch=2, seqlen=300, nheads=4, headdim=64, dstate=128, ngroups=1,
+                                        chunk=128, h0_std=0.1)
+    inp["dt"] = (inp["dt"] * 30).astype(np.float32)
+    inp["A"][::2] = -1e3
+    _check_full(inp, tag="ragged strong decay")
 
 
 def test_h_final_may_alias_h0():
