@@ -83,6 +83,25 @@ __device__ __forceinline__ v4h codes_to_f16(uint32_t biased) {
   return v4h{a[0], a[1], b[0], b[1]};
 }
 
+// LDS pointers whose per-lane base is opaque to the compiler: the hot loops then address every
+// read as that base plus an immediate offset (the arrays lie past the 16-bit offset range of
+// the LDS instructions, so a known array base would cost an add per read).
+#define LDSP __attribute__((address_space(3)))
+template <typename T>
+__device__ __forceinline__ const LDSP T* lds_base(const T* p) {
+  uint32_t a = uint32_t(uintptr_t((const LDSP T*)p));
+  asm volatile("" : "+v"(a));
+  return (const LDSP T*)uintptr_t(a);
+}
+template <typename V, typename T>
+__device__ __forceinline__ V lds_ld(const LDSP T* p, int off) {
+  return *reinterpret_cast<const LDSP V*>(p + off);
+}
+__device__ __forceinline__ float4 lds_f4(const LDSP float* p, int off) {
+  const v4f v = lds_ld<v4f>(p, off);
+  return float4{v[0], v[1], v[2], v[3]};
+}
+
 // The 16-row output block of a wave's pass.  Waves s and s + 4 share a SIMD and together own
 // blocks s, 15 - s, 4 + s, 11 - s, whose causal work (blocks before the diagonal: floor(b / 2))
 // is the same on every SIMD.  The SIMD issues the older wave s first, so it takes the larger
@@ -324,20 +343,18 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   lc.hs_off = uint32_t(tid & (kMaxP - 1)) * 4u;
   // hot-loop LDS bases: for rows js + lcol with js a multiple of 16 the B swizzle term depends
   // on lcol only, so every hot-loop address is a per-lane base plus a multiple of the step
-  const int8_t* bs_lane = Bs + bpos(lcol, 16 * kg);                    // + js * 128
-  const int bs_half = bpos(lcol, 64 + 16 * kg) - bpos(lcol, 16 * kg);   // second K half
+  const LDSP int8_t* const bs_lane = lds_base(Bs + bpos(lcol, 16 * kg));   // + js * 128
+  const LDSP int8_t* const bs_lane2 = lds_base(Bs + bpos(lcol, 64 + 16 * kg));   // second K half
   // transposing x reads: lane 4 k + q of its group addresses token row 4 kg + k at channels
   // 16 pt + 4 q; a step adds whole 32-token blocks (the swizzle repeats every 8 rows)
   int xa[4];
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) xa[pt] = xpos(4 * kg + (lcol >> 2), 16 * pt + 4 * (lcol & 3));
   float* wlw = wl[wave];
-  const float* wl_lane = wlw + 4 * kg;
-  int hq_lane[2][4];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) hq_lane[s2][pt] = hpos(16 * pt + lcol, 64 * s2 + 16 * kg);
+  const LDSP float* const wl_lane = lds_base(wlw + 4 * kg);
+  // carried-state rows 16 pt + lcol: the swizzle repeats every 16 rows, so row block pt lies
+  // 16 pt rows (2048 bytes) past row lcol for both K halves
+  const int hq_lane[2] = {hpos(lcol, 16 * kg), hpos(lcol, 64 + 16 * kg)};
 
   // Persistent block: a contiguous range of items, i.e. consecutive heads of one (batch, chunk)
   // (heads are the fastest item index).  Heads of one group share that chunk's B and C codes:
@@ -442,7 +459,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // this trip's view of the per-item tiles
     const _Float16* const xs = xs_buf[buf];
     const int8_t* const Hq = Hq_buf[buf];
-    const float* const hsc = hsc_buf[buf];
+    const LDSP int8_t* const hqb[2] = {lds_base(Hq + hq_lane[0]), lds_base(Hq + hq_lane[1])};
+    const LDSP float* const hsb = lds_base(hsc_buf[buf] + 4 * kg);   // + 16 pt: this lane's row scales
     const float* const acs2 = acs2_buf[buf];
     const float* const dts = dts_buf[buf];
     const float* const red = red_buf[buf];
@@ -516,8 +534,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const v4i h1 = *reinterpret_cast<const v4i*>(Hq + hq_lane[s2][pt]);
-          const v4i h2 = *reinterpret_cast<const v4i*>(Hq + kHPlane + hq_lane[s2][pt]);
+          const v4i h1 = lds_ld<v4i>(hqb[s2], 16 * kMaxN * pt);
+          const v4i h2 = lds_ld<v4i>(hqb[s2], kHPlane + 16 * kMaxN * pt);
           const v4i z = {0, 0, 0, 0};
           yo1[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h1, cq[s2], s2 == 0 ? z : yo1[pt], 0, 0, 0);
           yo2[pt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h2, cq[s2], s2 == 0 ? z : yo2[pt], 0, 0, 0);
@@ -527,7 +545,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       v4f yf[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const float4 hs = *reinterpret_cast<const float4*>(&hsc[16 * pt + 4 * kg]);
+        const float4 hs = lds_f4(hsb, 16 * pt);
         const float hv[4] = {hs.x, hs.y, hs.z, hs.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) yf[pt][i] = float((yo1[pt][i] << 8) + yo2[pt][i]) * (E * hv[i]);
@@ -541,10 +559,9 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
           const int js = jb + 16 * sb;
-          const int8_t* bp = bs_lane + js * kMaxN;
-          const v4i b0 = *reinterpret_cast<const v4i*>(bp);
-          const v4i b1 = *reinterpret_cast<const v4i*>(bp + bs_half);
-          w4[sb] = *reinterpret_cast<const float4*>(wl_lane + js);
+          const v4i b0 = lds_ld<v4i>(bs_lane, js * kMaxN);
+          const v4i b1 = lds_ld<v4i>(bs_lane2, js * kMaxN);
+          w4[sb] = lds_f4(wl_lane, js);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
         }
@@ -595,9 +612,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         v4i gm[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const int8_t* bp = bs_lane + (sb == 0 ? jb : j1) * kMaxN;
-          const v4i b0 = *reinterpret_cast<const v4i*>(bp);
-          const v4i b1 = *reinterpret_cast<const v4i*>(bp + bs_half);
+          const v4i b0 = lds_ld<v4i>(bs_lane, (sb == 0 ? jb : j1) * kMaxN);
+          const v4i b1 = lds_ld<v4i>(bs_lane2, (sb == 0 ? jb : j1) * kMaxN);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
           gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
         }
@@ -612,7 +628,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
               for (int i = 0; i < 4; ++i) mop[4 + i] = _Float16(0.f);
               continue;
             }
-            const float4 f4 = *reinterpret_cast<const float4*>(wl_lane + (sb == 0 ? jb : j1));
+            const float4 f4 = lds_f4(wl_lane, sb == 0 ? jb : j1);
             const float fv[4] = {f4.x, f4.y, f4.z, f4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
