@@ -134,7 +134,7 @@ size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nhe
  *               owned by the caller, not shared with a concurrent call
  * Supported shapes: headdim % 16 == 0 and headdim <= 64; dstate % 16 == 0 and
  * dstate <= 128; chunk in {64, 128, 256}; any seqlen >= 1 (a ragged last chunk
- * is masked); nheads % ngroups == 0; nheads * headdim * chunk < 2^31,
+ * is masked); nheads % ngroups == 0; nheads * headdim * chunk < 2^30,
  * ngroups * dstate * chunk < 2^31 and batch * seqlen * nheads < 2^31.  Others
  * return SSDQ_ERROR_UNSUPPORTED.
  * Accuracy: y within 2e-3 * max|y| and h_final within 1e-4 * max|h| of the exact

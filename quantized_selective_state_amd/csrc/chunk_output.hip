@@ -608,7 +608,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       v4f yd[4];
       {
         const int jb = jdiag;
-        const int j1 = min(jb + 16, Q - 16);   // sub-block 1 (fully masked when clamped)
+        const int j1 = jb + 16;   // sub-block 1 (jdiag <= 224: inside the 256-row tiles)
         v4i gm[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {

@@ -30,9 +30,10 @@ ssdq_status check_scan_shape(int32_t batch, int64_t seqlen, int32_t nheads, int3
   if (nchunks > 65535) return SSDQ_ERROR_UNSUPPORTED;
   // (token, head) rows of x, y and dt are indexed in 32 bits
   if (int64_t(batch) * seqlen * nheads >= (int64_t(1) << 31)) return SSDQ_ERROR_UNSUPPORTED;
-  // the kernels address one chunk of x, B, C (chunk rows of nheads*headdim or ngroups*dstate
-  // bytes) with 32-bit offsets from a per-chunk base
-  if (int64_t(nheads) * headdim * chunk >= (int64_t(1) << 31)) return SSDQ_ERROR_UNSUPPORTED;
+  // the kernels address one chunk of x, y, B, C (chunk rows of nheads*headdim or
+  // ngroups*dstate elements) with 32-bit offsets from a per-chunk base, and 2^31 is the offset
+  // that is never in range: a chunk of fp16 y must stay below it
+  if (int64_t(nheads) * headdim * chunk >= (int64_t(1) << 30)) return SSDQ_ERROR_UNSUPPORTED;
   if (int64_t(ngroups) * dstate * chunk >= (int64_t(1) << 31)) return SSDQ_ERROR_UNSUPPORTED;
   s->batch = batch;
   s->seqlen = seqlen;

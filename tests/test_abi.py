@@ -103,6 +103,7 @@ def _scan(lib, **kw):
     (dict(Q=32), UNSUPPORTED),
     (dict(Q=100), UNSUPPORTED),
     (dict(H=1 << 17, G=1, P=64, N=16, Q=256), UNSUPPORTED),        # a chunk of x: 2^31 bytes
+    (dict(H=1 << 16, G=1, P=64, N=16, Q=256), UNSUPPORTED),        # a chunk of fp16 y: 2^31 bytes
     (dict(H=1 << 16, G=1 << 16, P=16, N=128, Q=256), UNSUPPORTED),  # a chunk of B, C: 2^31 bytes
     (dict(wsb=100), WS_SMALL),
     (dict(stage=3, wsb=100), INVALID),
