@@ -8,14 +8,17 @@
 //
 // A persistent block (8 waves) walks (batch, chunk, head) items; each wave owns two 16-row
 // output blocks of an item (see row_block), and the next item's global loads are in flight
-// while an item is computed (register prefetch, committed to LDS after the item).
+// while an item is computed (register prefetch, committed into the other of two LDS tile
+// buffers as soon as the wave's own passes are done: one barrier per item).
 //  - G^T[j, l] = sum_n q_B[j, n] q_C[l, n] on v_mfma_i32_16x16x64_i8 (exact int32).
 //  - Decay mask, SSDi8-style decoupled from the matrix products: for a 32-token block that
 //    lies entirely before the 16 output rows l0..l0+15, exp(Acs_l - Acs_j) =
 //    exp(Acs_l - Acs_l0) exp(Acs_l0 - Acs_j), both factors <= 1, so the per-element work is
 //    G * w_j (w_j = exp(Acs_l0 - Acs_j) dt_j, once per token) and the row factor
-//    u_l = exp(Acs_l - Acs_l0) is applied in the epilogue.  The block holding the diagonal
-//    uses the exact per-element exp with the causal mask.
+//    u_l = exp(Acs_l - Acs_l0) is applied in the epilogue.  The 32-token block holding the
+//    diagonal is split around its first token m instead (a row factor exp(Acs_l - Acs_m) <= 1
+//    times a token weight exp(Acs_m - Acs_j) dt_j), with the causal mask; when its weights
+//    would leave the safe fp32 range it takes the exact per-element exp.
 //  - The masked fragment, rounded to fp16 under a power-of-two guard, feeds the next product
 //    as its B operand straight from registers: the fp16 MFMA's K slots are matched to the
 //    rows the int32 fragment holds, and x^T is read from LDS in the same slot order.
@@ -602,9 +605,10 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         mstep(jb, ga, wa);
       }
 
-      // the block holding the diagonal, exact per-element decay: sub-block 0 (tokens jdiag..+15)
-      // lies before row l0 when `half`, else it holds the diagonal and sub-block 1 is masked
-      // entirely; the diagonal sub-block gets the causal mask and D' on j == l.
+      // the block holding the diagonal, each entry with its own decay (factorized around the
+      // block's first token, or the exact exp): sub-block 0 (tokens jdiag..+15) lies before row
+      // l0 when `half`, else it holds the diagonal and sub-block 1 is masked entirely; the
+      // diagonal sub-block gets the causal mask and D' on j == l.
       v4f yd[4];
       {
         const int jb = jdiag;
