@@ -681,16 +681,31 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 
       // ---- epilogue: lane holds y[l, 16 pt + 4 kg + i], i = 0..3
       const float c_f = u_l * s_in;
+      v2u o4[4];   // channels 16 pt + 4 kg .. + 3 of row l, as fp16
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         v4h out;
 #pragma unroll
         for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(yf[pt][i], c_f, yd[pt][i] * s_in));
+        o4[pt] = __builtin_bit_cast(v2u, out);
+      }
+      // Channel tiles pt and pt + 1 trade halves between 16-lane rows (the odd rows of the first
+      // operand with the even rows of the second): a lane then holds 8 consecutive channels,
+      // 16 (pt + kg % 2) + 8 (kg / 2) .. + 7, and stores them with one 16-byte store.
+#pragma unroll
+      for (int pp = 0; pp < 4; pp += 2) {
+        v4u v;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto r = __builtin_amdgcn_permlane16_swap(o4[pp][d], o4[pp + 1][d], false, false);
+          v[d] = r[0];
+          v[2 + d] = r[1];
+        }
+        const int ch0 = 16 * (pp + (kg_v & 1)) + 8 * (kg_v >> 1);
         // unconditional store: rows past len and channels past P go out of range (dropped)
-        const uint32_t voff = (uint32_t(l) * yrow + uint32_t(16 * pt + 4 * kg_v)) * 2u;
-        const bool ok = lvalid & (16 * pt + 4 * kg_v < P);   // a select, not a branch
-        const uint32_t off = ok ? voff : kOutOfRange;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, out), ry, off, 0, 0);
+        const uint32_t voff = (uint32_t(l) * yrow + uint32_t(ch0)) * 2u;
+        const bool ok = lvalid & (ch0 < P);   // a select, not a branch
+        __builtin_amdgcn_raw_buffer_store_b128(v, ry, ok ? voff : kOutOfRange, 0, 0);
       }
     };
 
