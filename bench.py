@@ -21,6 +21,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -44,11 +45,19 @@ KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "chunk_output": "chunk_output.hip", "state_update": "state_update.hip"}
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and blank lines: editing a comment does not change the
+    kernel, so it does not void a counter reading."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
     for f in (KERNEL_SOURCE[kernel], "ssdq_internal.h"):
-        with open(os.path.join(ROOT, "quantized_selective_state_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantized_selective_state_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

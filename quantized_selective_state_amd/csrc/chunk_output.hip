@@ -363,8 +363,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // (heads are the fastest item index).  Heads of one group share that chunk's B and C codes:
   // they are loaded and committed only when the group changes, and C's registers and the B
   // tile in LDS serve all the group's items of the range.  The global loads of the next item
-  // are issued right after the current item is committed to LDS and complete while the
-  // current item is computed.  The range is XCD-aware: the blocks of one XCD take consecutive
+  // are issued while the current item is computed (at the start of its trip, the x codes
+  // between its two passes).  The range is XCD-aware: the blocks of one XCD take consecutive
   // ranges, so a chunk's B, C and the dt lines its heads share are fetched into one L2.
   const int per = (a.nitems + int(gridDim.x) - 1) / int(gridDim.x);
   int it = xcd_remap(blockIdx.x, gridDim.x) * per;

@@ -65,6 +65,13 @@ def test_digest_follows_the_kernel_source():
     assert bench.source_digest("quantize") != bench.source_digest("chunk_output")
 
 
+def test_digest_ignores_comments_only():
+    code = "int a; // note\n/* block\n comment */\nint b;\n\n"
+    assert bench._code_only(code) == "int a;\nint b;"
+    assert bench._code_only(code.replace("note", "another note")) == bench._code_only(code)
+    assert bench._code_only(code.replace("int b", "int c")) != bench._code_only(code)
+
+
 @pytest.mark.parametrize("kernel", sorted(bench.KERNEL_SOURCE))
 def test_every_kernel_maps_to_an_existing_source(kernel):
     path = os.path.join(ROOT, "quantized_selective_state_amd", "csrc", bench.KERNEL_SOURCE[kernel])
