@@ -12,20 +12,43 @@
 // V = 256 l1 + (l2 + 128), so H = 2^e (l1 + l2 / 256) to within 2^e / 256.  The running
 // state and h_final stay fp32.
 //
-// Thread layout: a state row of N floats is handled by G2 = next_pow2(N/4) lanes with
-// 4 consecutive columns each, so the row max is an xor-shuffle reduction inside the wave.
+// Thread layout: a state row of N floats is handled by LPR = next_pow2(N/4) lanes with
+// 4 consecutive columns each, so the row max is a reduction inside the wave (DPP lane moves
+// and a cross-row swap: no LDS traffic, hence no wait that would also drain the loads).
 #include "ssdq_internal.h"
 
 namespace ssdq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kDepth = 4;   // chunks of states in flight per thread
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(moved));
+}
+
+// Maximum over each group of LPR consecutive lanes, in every lane of the group.
+template <int LPR>
+__device__ __forceinline__ float group_max(float m) {
+  if constexpr (LPR >= 2) m = dpp_max<0xB1>(m);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+  if constexpr (LPR >= 4) m = dpp_max<0x4E>(m);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+  if constexpr (LPR >= 8) m = dpp_max<0x141>(m);   // row_half_mirror: the other quad of the 8
+  if constexpr (LPR >= 16) m = dpp_max<0x140>(m);  // row_mirror: the other half of the row
+  if constexpr (LPR == 32) {                       // rows 0 and 1, rows 2 and 3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return m;
+}
+
+template <int LPR>
 __global__ void __launch_bounds__(kThreads) state_passing_kernel(
     const float* __restrict__ states, const float* __restrict__ acs, const float* h0,  // h0 may alias h_final
     float* h_final, int8_t* __restrict__ hprev, float* __restrict__ hscale, int64_t seqlen, int32_t nheads,
-    int32_t headdim, int32_t dstate, int32_t chunk, int32_t nchunks, int32_t lanes_per_row,
-    int32_t blocks_per_bh) {
+    int32_t headdim, int32_t dstate, int32_t chunk, int32_t nchunks, int32_t blocks_per_bh) {
+  constexpr int lanes_per_row = LPR;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = bid / blocks_per_bh;
   const int part = bid % blocks_per_bh;
@@ -49,35 +72,62 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
   const int64_t cstride = int64_t(nheads) * pn;  // between consecutive chunks of one (b, h)
   const int64_t base = (int64_t(b) * nchunks * nheads + h) * pn;
 
-  v4f s_next = {0.f, 0.f, 0.f, 0.f};
-  if (active) s_next = *reinterpret_cast<const v4f*>(states + base + e);
-  for (int c = 0; c < nchunks; ++c) {
-    const v4f s = s_next;
-    if (active && c + 1 < nchunks) s_next = *reinterpret_cast<const v4f*>(states + base + (c + 1) * cstride + e);
-    // two INT8 limbs of H_c with a per-row power-of-two scale 2^ex >= row max / 127
-    float m = fmaxf(fmaxf(fabsf(H[0]), fabsf(H[1])), fmaxf(fabsf(H[2]), fabsf(H[3])));
-    for (int o = lanes_per_row / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
-    const float inv = exp2i(8 - ex);   // 256 / 2^ex
-    if (active) {
-      uint32_t q1 = 0, q2 = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t V = int32_t(fmaf(H[i], inv, 128.f));   // 256 t + 128, |t| <= 127
-        q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
-        q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
-      }
-      // per (b, c, h): limb-1 plane [P][N] then limb-2 plane [P][N]
-      int8_t* dst = hprev + 2 * (base + c * cstride) + eh;
-      *reinterpret_cast<uint32_t*>(dst) = q1;
-      *reinterpret_cast<uint32_t*>(dst + pn) = q2;
-      if (nq == 0) hscale[(base + c * cstride) / N + p] = exp2i(ex);
-    }
+  // The chunk states are read kDepth chunks ahead (a ring of registers, the loop unrolled by
+  // its depth so that every index is static): enough bytes in flight to cover the HBM latency
+  // with the few blocks a small batch launches.  The chunks' Acs[c, last] come 64 at a time as
+  // one vector load (lane k: chunk 64 i + k; the next 64 in flight) and are picked out with
+  // readlane, so the loop holds no scalar load that a wait would have to drain.
+  const int lane = int(threadIdx.x) % kWave;
+  auto acs_last_of = [&](int c) -> float {   // per lane; 0 past the last chunk
+    if (c >= nchunks) return 0.f;
     const int64_t rem = seqlen - int64_t(c) * chunk;
     const int last = int(rem < chunk ? rem : chunk) - 1;
-    const float decay = exp2f(acs_bh[int64_t(c) * chunk + last] * 1.4426950408889634f);
+    return acs_bh[int64_t(c) * chunk + last];
+  };
+  float acs_cur = acs_last_of(lane), acs_nxt = acs_last_of(kWave + lane);
+  v4f ring[kDepth];
+  auto load_chunk = [&](int c, v4f& sv) {
+    sv = v4f{0.f, 0.f, 0.f, 0.f};
+    if (c < nchunks && active) sv = *reinterpret_cast<const v4f*>(states + base + c * cstride + e);
+  };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) H[i] = decay * H[i] + s[i];
+  for (int k = 0; k < kDepth; ++k) load_chunk(k, ring[k]);
+  static_assert(kWave % kDepth == 0, "a group of 64 chunks starts at a ring boundary");
+  for (int c0 = 0; c0 < nchunks; c0 += kDepth) {
+    if (c0 > 0 && c0 % kWave == 0) {   // uniform: the next 64 chunks' Acs[c, last]
+      acs_cur = acs_nxt;
+      acs_nxt = acs_last_of(c0 + kWave + lane);
+    }
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int c = c0 + k;
+      if (c >= nchunks) break;   // uniform
+      const v4f sv = ring[k];
+      const float al = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acs_cur), c % kWave));
+      const float decay = exp2f(al * 1.4426950408889634f);
+      load_chunk(c + kDepth, ring[k]);
+      // two INT8 limbs of H_c with a per-row power-of-two scale 2^ex >= row max / 127
+      float m = fmaxf(fmaxf(fabsf(H[0]), fabsf(H[1])), fmaxf(fabsf(H[2]), fabsf(H[3])));
+      m = group_max<LPR>(m);
+      const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
+      const float inv = exp2i(8 - ex);   // 256 / 2^ex
+      if (active) {
+        uint32_t q1 = 0, q2 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t V = int32_t(fmaf(H[i], inv, 128.f));   // 256 t + 128, |t| <= 127
+          q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
+          q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
+        }
+        // per (b, c, h): limb-1 plane [P][N] then limb-2 plane [P][N]
+        int8_t* dst = hprev + 2 * (base + c * cstride) + eh;
+        *reinterpret_cast<uint32_t*>(dst) = q1;
+        *reinterpret_cast<uint32_t*>(dst + pn) = q2;
+        if (nq == 0) hscale[(base + c * cstride) / N + p] = exp2i(ex);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) H[i] = decay * H[i] + sv[i];
+    }
   }
   if (active && h_final) *reinterpret_cast<v4f*>(h_final + int64_t(bh) * pn + e) = H;
 }
@@ -90,9 +140,16 @@ hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream
   const int rows_per_block = kThreads / lanes;
   const int per_bh = (s.headdim + rows_per_block - 1) / rows_per_block;
   const int nblocks = s.batch * s.nheads * per_bh;
-  hipLaunchKernelGGL(state_passing_kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.states, a.acs, a.h0,
-                     a.h_final, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim, s.dstate, s.chunk, s.nchunks,
-                     lanes, per_bh);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.states, a.acs, a.h0, a.h_final, a.hprev,
+                       a.hscale, s.seqlen, s.nheads, s.headdim, s.dstate, s.chunk, s.nchunks, per_bh);
+  };
+  switch (lanes) {   // N / 4 = 4 .. 32 for the supported dstate
+    case 4: go(state_passing_kernel<4>); break;
+    case 8: go(state_passing_kernel<8>); break;
+    case 16: go(state_passing_kernel<16>); break;
+    default: go(state_passing_kernel<32>); break;
+  }
   return hipGetLastError();
 }
 
