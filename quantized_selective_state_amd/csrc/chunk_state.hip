@@ -476,8 +476,16 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
         for (int t = 0; t < kOwn; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
-        m = fmaxf(m, __shfl_xor(m, 16, kWave));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        // lanes l ^ 16 and l ^ 32 (the row's other kg) by swapping 16- and 32-lane halves in
+        // registers: no LDS round trip on the way to the barrier
+        {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
+        {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        }
         if (kg == 0) rmax[kh][16 * pt + lcol] = m;
       }
       // this chunk's tiles (loaded into LDS one chunk ago) have landed: wait for every
