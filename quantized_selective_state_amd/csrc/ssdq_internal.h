@@ -123,11 +123,32 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (bid % kXcd) * per + bid / kXcd;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Maximum over each group of LPR consecutive lanes (LPR a power of two up to the wave),
+// left in every lane of the group, entirely in registers: DPP lane moves within a 16-lane row
+// and gfx950's 16- and 32-lane half swaps across rows (no LDS round trip, so no wait that
+// would also drain outstanding loads).  For values >= 0: a lane masked off reads as 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(moved));
 }
+template <int LPR>
+__device__ __forceinline__ float group_max(float m) {
+  if constexpr (LPR >= 2) m = dpp_max<0xB1>(m);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+  if constexpr (LPR >= 4) m = dpp_max<0x4E>(m);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+  if constexpr (LPR >= 8) m = dpp_max<0x141>(m);   // row_half_mirror: the other quad of the 8
+  if constexpr (LPR >= 16) m = dpp_max<0x140>(m);  // row_mirror: the other half of the row
+  if constexpr (LPR >= 32) {                       // rows 0 and 1, rows 2 and 3
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (LPR >= 64) {                       // the two halves of the wave
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return m;
+}
+__device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -23,26 +23,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kDepth = 4;   // chunks of states in flight per thread
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
-  return fmaxf(v, __int_as_float(moved));
-}
-
-// Maximum over each group of LPR consecutive lanes, in every lane of the group.
-template <int LPR>
-__device__ __forceinline__ float group_max(float m) {
-  if constexpr (LPR >= 2) m = dpp_max<0xB1>(m);    // quad_perm [1, 0, 3, 2]: lane ^ 1
-  if constexpr (LPR >= 4) m = dpp_max<0x4E>(m);    // quad_perm [2, 3, 0, 1]: lane ^ 2
-  if constexpr (LPR >= 8) m = dpp_max<0x141>(m);   // row_half_mirror: the other quad of the 8
-  if constexpr (LPR >= 16) m = dpp_max<0x140>(m);  // row_mirror: the other half of the row
-  if constexpr (LPR == 32) {                       // rows 0 and 1, rows 2 and 3
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  }
-  return m;
-}
-
 template <int LPR>
 __global__ void __launch_bounds__(kThreads) state_passing_kernel(
     const float* __restrict__ states, const float* __restrict__ acs, const float* h0,  // h0 may alias h_final
