@@ -136,12 +136,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   }
 
   // ---- (a) chunk cumsum of dt A, one token per thread of waves 0..Q/64-1
-  float v = d * A[h];
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float up = __shfl_up(v, o, kWave);
-    if (lane >= o) v += up;
-  }
+  const float v = wave_inclusive_sum(d * A[h]);
   if (lane == kWave - 1) red[wave] = v;
   __syncthreads();
   float pre = 0.f;
@@ -383,12 +378,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
       run += dtg[u] * Ah;   // tokens past the end have dt = 0
       a[u] = run;
     }
-    float incl = run;   // inclusive scan of the lane totals
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const float up = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += up;
-    }
+    const float incl = wave_inclusive_sum(run);   // inclusive scan of the lane totals
     const float excl = incl - run;
 #pragma unroll
     for (int u = 0; u < kTok; ++u) a[u] += excl;
@@ -400,7 +390,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     float asel = a[0];
 #pragma unroll
     for (int u = 1; u < kTok; ++u) asel = lastu == u ? a[u] : asel;
-    const float a_last = __shfl(asel, lastl, kWave);
+    const float a_last = lane_broadcast(asel, lastl);
     float w[kTok], wm = 0.f;
 #pragma unroll
     for (int u = 0; u < kTok; ++u) {

@@ -150,6 +150,27 @@ __device__ __forceinline__ float group_max(float m) {
 }
 __device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: a Hillis-Steele scan inside
+// each 16-lane row with DPP right shifts (lanes shifted in from outside the row read 0), then
+// the row totals carried across rows with DPP row broadcasts.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+  return v + __int_as_float(moved);
+}
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  v = dpp_add<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_add<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_add<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_add<0x118, 0xF>(v);   // row_shr:8   -> inclusive sums within each row
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 -> rows 1 and 3 add lane 15 of the row before
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 -> rows 2 and 3 add lane 31
+  return v;
+}
+__device__ __forceinline__ float lane_broadcast(float v, int src_lane) {   // src_lane uniform
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
