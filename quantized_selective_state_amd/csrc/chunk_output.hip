@@ -475,11 +475,12 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // |D'| = |D| / (sC sB) 2^-kM <= 2^14, so their sum is a finite fp16.  Clamped so that 2^kM
     // and 2^-kM are exact.
     const float sCB = sC * sB;
-    const int kM = min(max(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, ceil_log2_pos(fabsf(Dh) / sCB) - 14),
+    const float DsCB = Dh / sCB;   // scales are positive: |D| / (sC sB) = |D / (sC sB)|
+    const int kM = min(max(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, ceil_log2_pos(fabsf(DsCB)) - 14),
                            -120), 120);
     const float s_in = sx * sCB * exp2i(kM);
     const float fkM = float(kM);
-    const float Dp = Dh / sCB * exp2i(-kM);   // D' (0 without D)
+    const float Dp = DsCB * exp2i(-kM);   // D' (0 without D)
     const float Ek = sC / (256.f * s_in);      // carried-state readout factor, times exp(Acs_l0) per pass
 
     // The lane index is re-materialized per item (an empty asm makes it opaque), so that the
