@@ -44,6 +44,10 @@ def _load():
     lib.oracle_quantize_f16.restype = None
     lib.oracle_ssd_sequential.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, i32, P]
     lib.oracle_ssd_sequential.restype = None
+    lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P]
+    lib.oracle_ssd_sequential_state_f16.restype = None
+    lib.oracle_round_binary16.argtypes = [P, P, i64]
+    lib.oracle_round_binary16.restype = None
     lib.oracle_chunk_cumsum.argtypes = [P, P, i64, i32, i32, i32, i32, P]
     lib.oracle_chunk_cumsum.restype = None
     lib.oracle_chunk_state.argtypes = [P] * 6 + [i64, i32, i32, i32, i32, i32, i32, i32, P]
@@ -121,11 +125,17 @@ def codes_from_inputs(inp: dict) -> Codes:
                  inp["dt"], inp["A"], inp.get("D"), inp.get("h0"))
 
 
-def ssd_one(c: Codes, b: int, h: int, chunk: int = 0):
-    """(y (L,P), h_final (P,N), bounds (nc,P,N) or None) for one (b, h) in float64."""
+def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
+    """(y (L,P), h_final (P,N), bounds (nc,P,N) or None) for one (b, h) in float64.  With
+    state_f16 the state is cached in binary16 between tokens (no chunk bounds then)."""
     lib = _load()
     y = np.empty((c.L, c.P), np.float64)
     hf = np.empty((c.P, c.N), np.float64)
+    if state_f16:
+        lib.oracle_ssd_sequential_state_f16(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
+                                            _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
+                                            c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf))
+        return y, hf, None
     bounds = None
     if chunk > 0:
         bounds = np.empty(((c.L + chunk - 1) // chunk, c.P, c.N), np.float64)
@@ -136,10 +146,10 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0):
     return y, hf, bounds
 
 
-def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None):
+def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None, state_f16: bool = False):
     """Run the recurrence for the given (b, h) pairs (default: all) on `threads` host threads.
     Returns (y, h_final, bounds) as full-size float64 arrays (NaN where not computed),
-    bounds only when chunk > 0."""
+    bounds only when chunk > 0.  state_f16: the state cached in binary16 between tokens."""
     if pairs is None:
         pairs = [(b, h) for b in range(c.batch) for h in range(c.H)]
     y = np.full((c.batch, c.L, c.H, c.P), np.nan)
@@ -151,7 +161,7 @@ def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None):
 
     def one(bh):
         b, h = bh
-        yy, hh, bb = ssd_one(c, b, h, chunk)
+        yy, hh, bb = ssd_one(c, b, h, chunk, state_f16)
         y[b, :, h, :] = yy
         hf[b, h] = hh
         if bb is not None:
@@ -164,6 +174,15 @@ def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None):
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(one, pairs))
     return y, hf, bounds
+
+
+def round_binary16(v: np.ndarray) -> np.ndarray:
+    """The binary16 value nearest to each element (ties to even), as float64."""
+    lib = _load()
+    src = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty_like(src)
+    lib.oracle_round_binary16(_ptr(src), _ptr(out), src.size)
+    return out
 
 
 def chunk_cumsum(c: Codes, b: int, h: int, chunk: int) -> np.ndarray:

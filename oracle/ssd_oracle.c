@@ -23,6 +23,12 @@
  *    Head h reads group g = h / (H / G).  Optionally records the state at every
  *    chunk boundary (the state entering chunk c, i.e. after token cQ - 1).
  *
+ *  - oracle_ssd_sequential_state_f16: the same recurrence with the state cached
+ *    in IEEE binary16 between tokens (a lower-precision cached decode state, as
+ *    the Quamba2 rebuttal's Tables R7/R8 discuss for 8-bit states): each token's
+ *    update is formed in double from the cached value, y_t reads that update,
+ *    and the cache keeps it rounded to the nearest binary16 (ties to even).
+ *
  *  - oracle_chunk_cumsum / oracle_chunk_state: the two per-chunk quantities of
  *    the chunked (state-space-duality) evaluation, each from its definition:
  *    Acs[c, j] = sum_{i <= j} dt_{cQ+i} A_h  and
@@ -81,11 +87,34 @@ void oracle_quantize_f16(const uint16_t* x, int8_t* q, const float* scale, int64
  *  y_out: L x P doubles; h_out: P x N doubles (final state).
  *  bound_out (optional, chunk > 0): ceil(L/chunk) x P x N doubles, the state
  *  entering each chunk. */
-void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
+/* The binary16 value nearest to v (ties to even), by the format's definition: binary16 has
+ * 11 significant bits, exponents -14 .. 15 and subnormals spaced 2^-24, so in the binade
+ * [2^E, 2^(E+1)) the representable values are the multiples of 2^(E-10) (2^-24 below 2^-14);
+ * magnitudes that round to 2^16 or beyond overflow to infinity.  NaN stays NaN. */
+static double round_to_binary16(double v) {
+  if (v != v || v == 0.0) return v;
+  const double a = fabs(v);
+  double quantum = 0x1p-24;
+  if (a >= 0x1p-14) {
+    int e2;
+    frexp(a, &e2);                    /* a = f 2^e2, f in [0.5, 1): binade exponent E = e2 - 1 */
+    quantum = ldexp(1.0, e2 - 1 - 10);
+  }
+  const double r = nearbyint(a / quantum) * quantum;   /* a / quantum is exact; ties to even */
+  if (r >= 65536.0) return copysign(INFINITY, v);
+  return copysign(r, v);
+}
+
+/* out[i] = the binary16 value nearest to in[i] (for pinning the rounding on its own). */
+void oracle_round_binary16(const double* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = round_to_binary16(in[i]);
+}
+
+static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
                            const int8_t* qC, const float* sC, const float* dt, const float* A,
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                           double* h_out, int32_t chunk, double* bound_out) {
+                           double* h_out, int32_t chunk, double* bound_out, int round_state) {
   (void)batch;
   const int32_t g = h / (H / G);
   double* S = (double*)calloc((size_t)P * N, sizeof(double));
@@ -116,6 +145,7 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
       for (int32_t n = 0; n < N; ++n) {
         Sp[n] = a * Sp[n] + u * Bv[n];
         acc += Cv[n] * Sp[n];
+        if (round_state) Sp[n] = round_to_binary16(Sp[n]);
       }
       y_out[t * P + p] = acc + Dh * xv[p];
     }
@@ -125,6 +155,24 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
   free(xv);
   free(Bv);
   free(Cv);
+}
+
+/* The recurrence with an fp32-exact (double) state. */
+void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
+                           const int8_t* qC, const float* sC, const float* dt, const float* A,
+                           const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
+                           int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
+                           double* h_out, int32_t chunk, double* bound_out) {
+  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0);
+}
+
+/* The recurrence with the state cached in binary16 between tokens (h0 is taken as given). */
+void oracle_ssd_sequential_state_f16(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
+                                     const int8_t* qC, const float* sC, const float* dt, const float* A,
+                                     const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
+                                     int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
+                                     double* h_out) {
+  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1);
 }
 
 /* Acs for one (b, h): out[c * chunk + j] = sum_{i <= j} dt[cQ + i] * A[h] within chunk c,
