@@ -42,7 +42,8 @@ TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_mamba2-1.3b-prefill_
 KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "chunk_state": "chunk_state.hip", "state_scan": "chunk_state.hip",
                  "state_passing": "state_passing.hip",
-                 "chunk_output": "chunk_output.hip", "state_update": "state_update.hip"}
+                 "chunk_output": "chunk_output.hip", "state_update": "state_update.hip",
+                 "state_update_f16": "state_update.hip"}
 
 
 def _code_only(text: str) -> str:
@@ -341,13 +342,33 @@ def bench_decode(args, torch, ssdq, workloads, dev):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    state_bytes = b * H * P * N * 4
-    per_step = 2 * state_bytes + b * H * P + 2 * b * G * N + b * H * 4 + b * H * P * 2
+    io_bytes = b * H * P + 2 * b * G * N + b * H * 4 + b * H * P * 2   # x codes, B/C codes, dt, y
+    per_step = 2 * b * H * P * N * 4 + io_bytes
     gbs = per_step / (ms / 1e3) / 1e9
-    return {"workload": name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "ngroups": G, "steps": steps,
-            "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms / 1e3), 1),
-            "alg_bytes_per_step": per_step, "achieved_GBs": round(gbs, 1),
-            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("state_update")}
+    out = {"workload": name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "ngroups": G, "steps": steps,
+           "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms / 1e3), 1),
+           "alg_bytes_per_step": per_step, "achieved_GBs": round(gbs, 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("state_update")}
+
+    # the same steps on the state cached in binary16 (half the state bytes per step)
+    del state
+    state16 = T(dec["state"]).half()
+    for t in range(min(8, steps)):
+        ssdq.state_update(state16, qx[t], sx, qB[t], sB, qC[t], sC, dt[t], A, D, y=ys[t])
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(steps):
+        ssdq.state_update(state16, qx[t], sx, qB[t], sB, qC[t], sC, dt[t], A, D, y=ys[t])
+    e1.record()
+    torch.cuda.synchronize()
+    ms16 = e0.elapsed_time(e1) / steps
+    per_step16 = 2 * b * H * P * N * 2 + io_bytes
+    gbs16 = per_step16 / (ms16 / 1e3) / 1e9
+    out["f16_state"] = {"us_per_step": round(ms16 * 1e3, 2), "tokens_per_s": round(b / (ms16 / 1e3), 1),
+                        "alg_bytes_per_step": per_step16, "achieved_GBs": round(gbs16, 1),
+                        "hbm_frac": round(gbs16 / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("state_update_f16")}
+    return out
 
 
 def cpu_baseline(inp):

@@ -190,6 +190,27 @@ ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scal
                               const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
                               int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
 
+/*
+ * The decode step with the state cached in IEEE binary16: half the bytes per step of the fp32
+ * state on the HBM-bound update (a lower-precision cached SSM state, as the Quamba2
+ * rebuttal's Tables R7/R8 discuss for decode-time memory and latency).
+ *
+ *   u[b,h,p,n] = exp(dt[b,h] A[h]) state[b,h,p,n] + dt[b,h] xhat[b,h,p] Bhat[b,g,n]   (fp32)
+ *   y[b,h,p]   = sum_n Chat[b,g,n] u[b,h,p,n] + D[h] xhat[b,h,p]                   (from u)
+ *   state[b,h,p,n] <- u rounded to the nearest binary16 (ties to even; |u| beyond the
+ *                     format's range gives +-inf)
+ *
+ *   state : (batch, nheads, headdim, dstate) IEEE binary16, read and written
+ * Every other argument, the shapes supported and the validation are those of
+ * ssdq_state_update.  Each step rounds the state once (2^-11 relative at most), so after T
+ * steps the cached state is within T * 2^-11 of the largest state magnitude of the fp32
+ * recurrence; the caller chooses it where that is acceptable.
+ */
+ssdq_status ssdq_state_update_f16(void* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                                  const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                                  const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
+                                  int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

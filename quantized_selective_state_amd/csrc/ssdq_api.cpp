@@ -184,10 +184,12 @@ ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t*
   return SSDQ_SUCCESS;
 }
 
-ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
-                              const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
-                              const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
-                              int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+namespace {
+// Arguments of a decode step (fp32 or binary16 state alike).
+ssdq_status check_decode(const void* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                         const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                         const float* A, const float* D, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                         int32_t dstate, int32_t ngroups) {
   if (!ok_ptr(state) || !ok_ptr(x) || !ok_ptr(x_scale) || !ok_ptr(B) || !ok_ptr(B_scale) || !ok_ptr(C) ||
       !ok_ptr(C_scale) || !ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(y) || !ok_opt(D))
     return SSDQ_ERROR_INVALID_VALUE;
@@ -195,9 +197,33 @@ ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scal
   if (nheads % ngroups != 0) return SSDQ_ERROR_INVALID_VALUE;
   if ((dstate != 64 && dstate != 128) || headdim > 64) return SSDQ_ERROR_UNSUPPORTED;
   if (int64_t(batch) * nheads > (int64_t(1) << 30)) return SSDQ_ERROR_UNSUPPORTED;
+  return SSDQ_SUCCESS;
+}
+}  // namespace
+
+ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                              const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                              const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
+                              int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  const ssdq_status st =
+      check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
+  if (st != SSDQ_SUCCESS) return st;
   const hipError_t e = launch_state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
                                            static_cast<_Float16*>(y), batch, nheads, headdim, dstate, ngroups,
                                            stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
+ssdq_status ssdq_state_update_f16(void* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                                  const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                                  const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
+                                  int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  const ssdq_status st =
+      check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
+  if (st != SSDQ_SUCCESS) return st;
+  const hipError_t e = launch_state_update_f16(static_cast<uint16_t*>(state), x, x_scale, B, B_scale, C, C_scale,
+                                               dt, A, D, static_cast<_Float16*>(y), batch, nheads, headdim, dstate,
+                                               ngroups, stream);
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 

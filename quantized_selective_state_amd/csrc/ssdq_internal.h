@@ -79,6 +79,10 @@ hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream
 bool state_scan_fused(int32_t batch, int32_t nheads);
 hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                                   const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                                   const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
+                                   int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
@@ -149,6 +153,23 @@ __device__ __forceinline__ float group_max(float m) {
   return m;
 }
 __device__ __forceinline__ float wave_max(float v) { return group_max<kWave>(v); }
+
+// Sum over each group of LPR consecutive lanes (LPR a power of two up to 16), left in every
+// lane of the group: the same DPP pairings as group_max, each joining two disjoint sub-groups.
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return v + __int_as_float(moved);
+}
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LPR >= 1 && LPR <= 16, "groups within one 16-lane row");
+  if constexpr (LPR >= 2) v = dpp_sum<0xB1>(v);
+  if constexpr (LPR >= 4) v = dpp_sum<0x4E>(v);
+  if constexpr (LPR >= 8) v = dpp_sum<0x141>(v);
+  if constexpr (LPR >= 16) v = dpp_sum<0x140>(v);
+  return v;
+}
 
 // Inclusive prefix sum over the 64 lanes of a wave, in registers: a Hillis-Steele scan inside
 // each 16-lane row with DPP right shifts (lanes shifted in from outside the row read 0), then

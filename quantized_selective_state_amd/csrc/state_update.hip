@@ -98,6 +98,81 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
   }
 }
 
+// The same step with the state cached in IEEE binary16 (half the bytes of the fp32 state):
+// thread t owns the 8 consecutive state columns 8 (t % (N/8)) of its rows (one 16-byte load
+// and store per row), forms the update in fp32 from the cached value, reads y out of that
+// update and stores it rounded to nearest binary16 (ties to even; past the format's range:
+// inf).  y[p] is summed across the N/8 lanes of row p with DPP lane pairings.
+template <int N>
+__global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
+    uint16_t* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
+    const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
+    const float* __restrict__ C_scale, const float* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads, int32_t headdim, int32_t ngroups) {
+  constexpr int kLanesPerRow = N / 8;               // 16 (N = 128) or 8 (N = 64)
+  constexpr int kRows = kThreads / kLanesPerRow;    // rows per pass
+  constexpr int kPasses = 64 / kRows;               // headdim <= 64
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = bh % nheads;
+  const int b = bh / nheads;
+  const int g = h / (nheads / ngroups);
+  const int tid = threadIdx.x;
+  const int nq = tid % kLanesPerRow;
+  const int r0 = tid / kLanesPerRow;
+  const int P = headdim;
+
+  uint16_t* st = state + int64_t(bh) * P * N;
+  const int8_t* xr = x + int64_t(bh) * P;
+  v4u hv[kPasses];
+  int xq[kPasses];
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = min(r0 + kRows * k, P - 1);   // rows past headdim: a clamped, unused load
+    hv[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(st + int64_t(p) * N + 8 * nq));
+  }
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) xq[k] = xr[min(r0 + kRows * k, P - 1)];
+  const v2u bw = *reinterpret_cast<const v2u*>(Bm + (int64_t(b) * ngroups + g) * N + 8 * nq);
+  const v2u cw = *reinterpret_cast<const v2u*>(Cm + (int64_t(b) * ngroups + g) * N + 8 * nq);
+  const float d = dt[bh];
+  const float a = __expf(d * A[h]);
+  const float sx = x_scale[h];
+  const float dx = d * sx;
+  const float Dsx = (D ? D[h] : 0.f) * sx;
+  const float sB = B_scale[g], sC = C_scale[g];
+  float bh8[8], ch8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bh8[i] = sB * sbyte(bw[i >> 2], i & 3);
+    ch8[i] = sC * sbyte(cw[i >> 2], i & 3);
+  }
+
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = r0 + kRows * k;
+    const float xp = float(xq[k]);
+    const float u = dx * xp;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w = hv[k][i >> 1];
+      const float cached = float(__builtin_bit_cast(_Float16, uint16_t((i & 1) ? w >> 16 : w & 0xffffu)));
+      v[i] = a * cached + u * bh8[i];
+    }
+    v4u out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      out[j] = uint32_t(__builtin_bit_cast(uint16_t, _Float16(v[2 * j]))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(v[2 * j + 1]))) << 16);
+    if (p < P) __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(st + int64_t(p) * N + 8 * nq));
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part = fmaf(ch8[i], v[i], part);
+    part = group_sum<kLanesPerRow>(part);
+    if (p < P && nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp);
+  }
+}
+
 template <int N>
 hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
                     const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
@@ -110,6 +185,20 @@ hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const i
 }
 
 }  // namespace
+
+hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float* x_scale, const int8_t* B,
+                                   const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                                   const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
+                                   int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  const int nblocks = batch * nheads;
+  if (dstate == 128)
+    hipLaunchKernelGGL((state_update_f16_kernel<128>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
+                       B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+  else
+    hipLaunchKernelGGL((state_update_f16_kernel<64>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
+                       B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+  return hipGetLastError();
+}
 
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,

@@ -32,6 +32,7 @@ def lib():
     lib.ssdq_chunk_scan_workspace_size.argtypes = [i32, i64, i32, i32, i32, i32]
     lib.ssdq_chunk_scan_workspace_size.restype = sz
     lib.ssdq_state_update.argtypes = [P] * 11 + [i32] * 5 + [P]
+    lib.ssdq_state_update_f16.argtypes = [P] * 11 + [i32] * 5 + [P]
     lib.ssdq_status_string.argtypes = [ctypes.c_int]
     lib.ssdq_status_string.restype = ctypes.c_char_p
     return lib
@@ -158,12 +159,13 @@ def test_quantize_batch_rejects_null_jobs(lib):
     assert lib.ssdq_quantize_batch(None, 1, None) == INVALID
 
 
-def _upd(lib, **kw):
+def _upd(lib, f16=False, **kw):
     a = dict(state=A16, x=A16, xs=A16, B=A16, Bs=A16, C=A16, Cs=A16, dt=A16, A=A16, D=None, y=A16,
              b=2, H=8, P=64, N=128, G=2)
     a.update(kw)
-    return lib.ssdq_state_update(*[a[k] for k in ("state", "x", "xs", "B", "Bs", "C", "Cs", "dt", "A", "D", "y",
-                                                 "b", "H", "P", "N", "G")], None)
+    call = lib.ssdq_state_update_f16 if f16 else lib.ssdq_state_update
+    return call(*[a[k] for k in ("state", "x", "xs", "B", "Bs", "C", "Cs", "dt", "A", "D", "y",
+                                 "b", "H", "P", "N", "G")], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -174,5 +176,6 @@ def _upd(lib, **kw):
     (dict(N=96), UNSUPPORTED),
     (dict(P=128), UNSUPPORTED),
 ])
-def test_state_update_validation(lib, kw, status):
-    assert _upd(lib, **kw) == status
+@pytest.mark.parametrize("f16", [False, True])   # fp32 state and binary16-cached state
+def test_state_update_validation(lib, kw, status, f16):
+    assert _upd(lib, f16=f16, **kw) == status
