@@ -47,6 +47,10 @@ def _load():
     lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P]
     lib.oracle_ssd_sequential_state_f16.restype = None
     lib.oracle_round_binary16.argtypes = [P, P, i64]
+    lib.oracle_requantize_rows_i8.argtypes = [P, i64, i32, P, P, P]
+    lib.oracle_requantize_rows_i8.restype = None
+    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_ssd_sequential_state_i8.restype = None
     lib.oracle_round_binary16.restype = None
     lib.oracle_chunk_cumsum.argtypes = [P, P, i64, i32, i32, i32, i32, P]
     lib.oracle_chunk_cumsum.restype = None
@@ -174,6 +178,42 @@ def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None, state_
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(one, pairs))
     return y, hf, bounds
+
+
+def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None):
+    """The recurrence for one (b, h) with the state cached as 8-bit codes and one binary32
+    scale per state row between tokens, starting from codes q0 (batch,H,P,N) int8 with row
+    scales s0 (batch,H,P) float32 (None: a zero state).  Returns (y (L,P), decoded final state
+    (P,N), final codes (P,N) int8, final scales (P,) float32, last token's update before
+    re-quantization (P,N)), all from the oracle."""
+    lib = _load()
+    y = np.empty((c.L, c.P), np.float64)
+    hf = np.empty((c.P, c.N), np.float64)
+    q = np.empty((c.P, c.N), np.int8)
+    s = np.empty(c.P, np.float32)
+    u = np.empty((c.P, c.N), np.float64)
+    q0 = None if q0 is None else _c(q0, np.int8)
+    s0 = None if s0 is None else _c(s0, np.float32)
+    if (q0 is None) != (s0 is None):
+        raise ValueError("q0 and s0 go together")
+    if q0 is not None and (q0.shape != (c.batch, c.H, c.P, c.N) or s0.shape != (c.batch, c.H, c.P)):
+        raise ValueError("q0 must be (batch,H,P,N) and s0 (batch,H,P)")
+    lib.oracle_ssd_sequential_state_i8(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
+                                       _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(q0), _ptr(s0),
+                                       c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf), _ptr(q),
+                                       _ptr(s), _ptr(u))
+    return y, hf, q, s, u
+
+
+def requantize_rows_i8(rows: np.ndarray):
+    """Each row of a (rows, N) array as 8-bit codes with one binary32 scale: (codes, scales,
+    decoded rows)."""
+    r = _c(np.atleast_2d(rows), np.float64)
+    q = np.empty(r.shape, np.int8)
+    s = np.empty(r.shape[0], np.float32)
+    out = np.empty(r.shape, np.float64)
+    _load().oracle_requantize_rows_i8(_ptr(r), r.shape[0], r.shape[1], _ptr(q), _ptr(s), _ptr(out))
+    return q, s, out
 
 
 def round_binary16(v: np.ndarray) -> np.ndarray:

@@ -29,6 +29,13 @@
  *    update is formed in double from the cached value, y_t reads that update,
  *    and the cache keeps it rounded to the nearest binary16 (ties to even).
  *
+ *  - oracle_ssd_sequential_state_i8: the same recurrence with the state cached
+ *    as 8-bit codes (the 8-bit cached states of those tables) with one binary32
+ *    scale per state row: each token's update in double from the decoded cache,
+ *    y_t from that update, then every row re-quantized symmetrically to
+ *    [-127, 127] with s = max|row| / 127 (the reading stated at
+ *    requantize_row_i8).
+ *
  *  - oracle_chunk_cumsum / oracle_chunk_state: the two per-chunk quantities of
  *    the chunked (state-space-duality) evaluation, each from its definition:
  *    Acs[c, j] = sum_{i <= j} dt_{cQ+i} A_h  and
@@ -110,20 +117,64 @@ void oracle_round_binary16(const double* in, double* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = round_to_binary16(in[i]);
 }
 
+/* One state row cached as 8-bit codes with one binary32 scale (an 8-bit cached SSM state,
+ * Quamba2 rebuttal Tables R7/R8; the scale granularity, one per state row (b, h, p), and
+ * its choice from the row's largest magnitude are this oracle's reading, the same symmetric
+ * max/127 rule the pages use for activations).  s = binary32(max_n |row[n]| / 127); each
+ * code is row[n] / s rounded to nearest with ties to even and saturated to [-127, 127]; the
+ * row becomes s * code.  A zero row (or a scale that rounds to 0) gives zero codes and s = 0. */
+static void requantize_row_i8(double* row, int32_t N, int8_t* q, float* s_out) {
+  double m = 0.0;
+  for (int32_t n = 0; n < N; ++n) m = fmax(m, fabs(row[n]));
+  const float s = (float)(m / 127.0);
+  for (int32_t n = 0; n < N; ++n) {
+    double c = 0.0;
+    if (s > 0.0f) {
+      c = nearbyint(row[n] / (double)s);
+      c = c > 127.0 ? 127.0 : (c < -127.0 ? -127.0 : c);
+    }
+    q[n] = (int8_t)c;
+    row[n] = (double)s * c;
+  }
+  *s_out = s;
+}
+
+/* Re-quantize rows on their own (for pinning): rows x N doubles in; codes, scales and the
+ * decoded rows out. */
+void oracle_requantize_rows_i8(const double* in, int64_t rows, int32_t N, int8_t* q, float* s, double* out) {
+  for (int64_t r = 0; r < rows; ++r) {
+    memcpy(out + r * N, in + r * N, sizeof(double) * N);
+    requantize_row_i8(out + r * N, N, q + r * N, s + r);
+  }
+}
+
+/* round_state: 0 none, 1 binary16 per element, 2 8-bit codes per row (requantize_row_i8).
+ * q0/s0 (mode 2, optional): the starting state as codes (batch, H, P, N) and row scales
+ * (batch, H, P); q_out/s_out: the final codes and scales; u_last: the last token's update
+ * before it is re-quantized (P x N). */
 static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
                            const int8_t* qC, const float* sC, const float* dt, const float* A,
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                           double* h_out, int32_t chunk, double* bound_out, int round_state) {
+                           double* h_out, int32_t chunk, double* bound_out, int round_state,
+                           const int8_t* q0, const float* s0, int8_t* q_out, float* s_out, double* u_last) {
   (void)batch;
   const int32_t g = h / (H / G);
   double* S = (double*)calloc((size_t)P * N, sizeof(double));
   double* xv = (double*)malloc(sizeof(double) * P);
   double* Bv = (double*)malloc(sizeof(double) * N);
   double* Cv = (double*)malloc(sizeof(double) * N);
+  int8_t* codes = (int8_t*)calloc((size_t)P * N, 1);
+  float* scales = (float*)calloc((size_t)P, sizeof(float));
   if (h0) {
     const float* src = h0 + ((int64_t)b * H + h) * P * N;
     for (int64_t i = 0; i < (int64_t)P * N; ++i) S[i] = (double)src[i];
+  }
+  if (q0 && s0) {
+    const int64_t bh = (int64_t)b * H + h;
+    for (int32_t p = 0; p < P; ++p)
+      for (int32_t n = 0; n < N; ++n)
+        S[(int64_t)p * N + n] = (double)s0[bh * P + p] * (double)q0[(bh * P + p) * N + n];
   }
   const double Ah = (double)A[h];
   const double Dh = D ? (double)D[h] : 0.0;
@@ -145,12 +196,20 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
       for (int32_t n = 0; n < N; ++n) {
         Sp[n] = a * Sp[n] + u * Bv[n];
         acc += Cv[n] * Sp[n];
-        if (round_state) Sp[n] = round_to_binary16(Sp[n]);
+        if (round_state == 1) Sp[n] = round_to_binary16(Sp[n]);
       }
       y_out[t * P + p] = acc + Dh * xv[p];
+      if (round_state == 2) {
+        if (u_last && t == L - 1) memcpy(u_last + (int64_t)p * N, Sp, sizeof(double) * N);
+        requantize_row_i8(Sp, N, codes + (int64_t)p * N, scales + p);
+      }
     }
   }
   memcpy(h_out, S, sizeof(double) * P * N);
+  if (q_out) memcpy(q_out, codes, (size_t)P * N);
+  if (s_out) memcpy(s_out, scales, sizeof(float) * P);
+  free(codes);
+  free(scales);
   free(S);
   free(xv);
   free(Bv);
@@ -163,7 +222,8 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out) {
-  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0);
+  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0,
+                 NULL, NULL, NULL, NULL, NULL);
 }
 
 /* The recurrence with the state cached in binary16 between tokens (h0 is taken as given). */
@@ -172,7 +232,21 @@ void oracle_ssd_sequential_state_f16(const int8_t* qx, const float* sx, const in
                                      const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                                      int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                                      double* h_out) {
-  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1);
+  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1,
+                 NULL, NULL, NULL, NULL, NULL);
+}
+
+/* The recurrence with the state cached as 8-bit codes and one scale per state row between
+ * tokens, starting from codes q0 (batch, H, P, N) with row scales s0 (batch, H, P) (both NULL:
+ * a zero state).  h_out: the final state decoded (P x N); q_out/s_out: its codes and scales;
+ * u_last (optional): the last token's update before re-quantization. */
+void oracle_ssd_sequential_state_i8(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
+                                    const int8_t* qC, const float* sC, const float* dt, const float* A,
+                                    const float* D, const int8_t* q0, const float* s0, int32_t batch, int64_t L,
+                                    int32_t H, int32_t P, int32_t N, int32_t G, int32_t b, int32_t h,
+                                    double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last) {
+  ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, NULL, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 2,
+                 q0, s0, q_out, s_out, u_last);
 }
 
 /* Acs for one (b, h): out[c * chunk + j] = sum_{i <= j} dt[cQ + i] * A[h] within chunk c,
