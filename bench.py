@@ -43,7 +43,7 @@ KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "chunk_state": "chunk_state.hip", "state_scan": "chunk_state.hip",
                  "state_passing": "state_passing.hip",
                  "chunk_output": "chunk_output.hip", "state_update": "state_update.hip",
-                 "state_update_f16": "state_update.hip"}
+                 "state_update_f16": "state_update.hip", "state_update_i8": "state_update.hip"}
 
 
 def _code_only(text: str) -> str:
@@ -368,6 +368,28 @@ def bench_decode(args, torch, ssdq, workloads, dev):
                         "alg_bytes_per_step": per_step16, "achieved_GBs": round(gbs16, 1),
                         "hbm_frac": round(gbs16 / HBM_PEAK_GBS, 4),
                         "traffic": measured_traffic("state_update_f16")}
+
+    # and on the state cached as 8-bit codes with one fp32 scale per state row (a quarter of the bytes)
+    del state16
+    st32 = T(dec["state"])
+    scale8 = (st32.abs().amax(dim=-1) / 127.0).contiguous()
+    state8 = torch.round(st32 / scale8[..., None]).clamp_(-127, 127).to(torch.int8).contiguous()
+    del st32
+    for t in range(min(8, steps)):
+        ssdq.state_update(state8, qx[t], sx, qB[t], sB, qC[t], sC, dt[t], A, D, y=ys[t], state_scale=scale8)
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(steps):
+        ssdq.state_update(state8, qx[t], sx, qB[t], sB, qC[t], sC, dt[t], A, D, y=ys[t], state_scale=scale8)
+    e1.record()
+    torch.cuda.synchronize()
+    ms8 = e0.elapsed_time(e1) / steps
+    per_step8 = 2 * (b * H * P * N + b * H * P * 4) + io_bytes
+    gbs8 = per_step8 / (ms8 / 1e3) / 1e9
+    out["i8_state"] = {"us_per_step": round(ms8 * 1e3, 2), "tokens_per_s": round(b / (ms8 / 1e3), 1),
+                       "alg_bytes_per_step": per_step8, "achieved_GBs": round(gbs8, 1),
+                       "hbm_frac": round(gbs8 / HBM_PEAK_GBS, 4),
+                       "traffic": measured_traffic("state_update_i8")}
     return out
 
 

@@ -211,6 +211,32 @@ ssdq_status ssdq_state_update_f16(void* state, const int8_t* x, const float* x_s
                                   const float* A, const float* D, void* y, int32_t batch, int32_t nheads,
                                   int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
 
+/*
+ * The decode step with the state cached as 8-bit codes and one binary32 scale per state row
+ * (b, h, p): a quarter of the fp32 state's bytes per step (the 8-bit cached SSM states of the
+ * Quamba2 rebuttal, Tables R7/R8; the pages do not fix the scale granularity, one scale per
+ * row and the symmetric max/127 rule are the choice made here).
+ *
+ *   u[b,h,p,n] = exp(dt[b,h] A[h]) scale[b,h,p] state[b,h,p,n] + dt[b,h] xhat[b,h,p] Bhat[b,g,n]  (fp32)
+ *   y[b,h,p]   = sum_n Chat[b,g,n] u[b,h,p,n] + D[h] xhat[b,h,p]                               (from u)
+ *   scale[b,h,p] <- max_n |u[b,h,p,n]| / 127                      (binary32; 0 for a zero row)
+ *   state[b,h,p,n] <- u / scale rounded to nearest, ties to even, within [-127, 127] (0 if scale is 0)
+ *
+ *   state       : (batch, nheads, headdim, dstate) int8 codes, read and written
+ *   state_scale : (batch, nheads, headdim) float32, read and written; 16-byte aligned
+ * Every other argument, the shapes supported and the validation are those of
+ * ssdq_state_update; a NULL or misaligned state_scale gives SSDQ_ERROR_INVALID_VALUE.  Each step
+ * moves every element by at most half a code step (max|row| / 254), so after T steps the cached
+ * state is within T/254 of the largest row magnitude of the fp32 recurrence; the values must
+ * stay finite (a non-finite update makes its row's scale non-finite).  Codes where the update
+ * falls within fp32 rounding of a midpoint between two codes may take either neighbour.
+ */
+ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
+                                 const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
+                                 const float* dt, const float* A, const float* D, void* y, int32_t batch,
+                                 int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ lib.ssdq_state_update.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update.restype = ctypes.c_int
 lib.ssdq_state_update_f16.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_f16.restype = ctypes.c_int
+lib.ssdq_state_update_i8.argtypes = [_P] * 12 + [_i32, _i32, _i32, _i32, _i32, _P]
+lib.ssdq_state_update_i8.restype = ctypes.c_int
 lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
 lib.ssdq_chunk_scan_state_fused.restype = _i32
 
@@ -262,16 +264,22 @@ def chunk_scan(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk
 # decode
 
 
-def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=None) -> torch.Tensor:
+def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=None, state_scale=None) -> torch.Tensor:
     """One decode step; `state` (b,H,P,N) is updated in place; returns y fp16 (b,H,P).  An fp32
-    state runs ssdq_state_update, a binary16 (torch.float16) state ssdq_state_update_f16."""
+    state runs ssdq_state_update, a binary16 (torch.float16) state ssdq_state_update_f16, and an
+    int8 state (codes, with its row scales `state_scale` (b,H,P) float32, also updated in place)
+    ssdq_state_update_i8."""
     if state.dim() != 4:
         raise ValueError("state must be (batch, nheads, headdim, dstate)")
     b, H, P, N = state.shape
     G = B.shape[1] if B.dim() == 3 else -1
     dev = state.device
-    cached16 = state.dtype == torch.float16
-    _need(state, "state", torch.float16 if cached16 else torch.float32, (b, H, P, N), dev)
+    kind = {torch.float16: "f16", torch.int8: "i8"}.get(state.dtype, "f32")
+    _need(state, "state", {"f16": torch.float16, "i8": torch.int8}.get(kind, torch.float32), (b, H, P, N), dev)
+    if kind == "i8":
+        _need(state_scale, "state_scale", torch.float32, (b, H, P), dev)
+    elif state_scale is not None:
+        raise ValueError("state_scale goes with an int8 state only")
     _need(x, "x", torch.int8, (b, H, P), dev)
     _need(x_scale, "x_scale", torch.float32, (H,), dev)
     _need(B, "B", torch.int8, (b, G, N), dev)
@@ -284,8 +292,12 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     if y is None:
         y = torch.empty((b, H, P), dtype=torch.float16, device=dev)
     _need(y, "y", torch.float16, (b, H, P), dev)
-    call, name = (lib.ssdq_state_update_f16, "ssdq_state_update_f16") if cached16 else \
-        (lib.ssdq_state_update, "ssdq_state_update")
-    _check(call(_ptr(state), _ptr(x), _ptr(x_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(C_scale), _ptr(dt),
-                _ptr(A), _ptr(D), _ptr(y), b, H, P, N, G, _stream(dev)), name)
+    rest = (_ptr(x), _ptr(x_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(C_scale), _ptr(dt), _ptr(A), _ptr(D),
+            _ptr(y), b, H, P, N, G, _stream(dev))
+    if kind == "i8":
+        _check(lib.ssdq_state_update_i8(_ptr(state), _ptr(state_scale), *rest), "ssdq_state_update_i8")
+    elif kind == "f16":
+        _check(lib.ssdq_state_update_f16(_ptr(state), *rest), "ssdq_state_update_f16")
+    else:
+        _check(lib.ssdq_state_update(_ptr(state), *rest), "ssdq_state_update")
     return y

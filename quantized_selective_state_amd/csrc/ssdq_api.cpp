@@ -227,4 +227,19 @@ ssdq_status ssdq_state_update_f16(void* state, const int8_t* x, const float* x_s
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
+ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
+                                 const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
+                                 const float* dt, const float* A, const float* D, void* y, int32_t batch,
+                                 int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                 hipStream_t stream) {
+  if (!ok_ptr(state_scale)) return SSDQ_ERROR_INVALID_VALUE;
+  const ssdq_status st =
+      check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
+  if (st != SSDQ_SUCCESS) return st;
+  const hipError_t e = launch_state_update_i8(state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
+                                              static_cast<_Float16*>(y), batch, nheads, headdim, dstate, ngroups,
+                                              stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
 }  // extern "C"

@@ -173,6 +173,117 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
   }
 }
 
+// The same step on a state cached as 8-bit codes with one binary32 scale per state row (the
+// 8-bit cached SSM states of the Quamba2 rebuttal, Tables R7/R8; one scale per row is the
+// granularity chosen here): the row is decoded (scale times code), updated in fp32, y is read
+// from the update, and the row is re-quantized with s = max|row| / 127 and codes rounded to
+// nearest even.  A row of N codes is N/16 lanes with one 16-byte load each, so the row maximum
+// and y's dot product are reductions over at most 8 neighbouring lanes (DPP, in registers).
+//
+// Arithmetic per element, kept short because at 1 byte per element the step is close to
+// VALU-bound as well: the cached code arrives as an unsigned byte (sign bit flipped, converted
+// with the byte-select conversion) and its offset of 128 is folded into a per-element constant;
+// the new code is one fma into the binade of 1.5 * 2^23, whose unit spacing makes the fma's own
+// rounding the round-to-nearest-even of the quotient and leaves the code in the low byte.
+template <int N>
+__global__ void __launch_bounds__(kThreads) state_update_i8_kernel(
+    int8_t* __restrict__ state, float* __restrict__ state_scale, const int8_t* __restrict__ x,
+    const float* __restrict__ x_scale, const int8_t* __restrict__ Bm, const float* __restrict__ B_scale,
+    const int8_t* __restrict__ Cm, const float* __restrict__ C_scale, const float* __restrict__ dt,
+    const float* __restrict__ A, const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads,
+    int32_t headdim, int32_t ngroups) {
+  constexpr int kLanesPerRow = N / 16;                 // 8 (N = 128) or 4 (N = 64)
+  constexpr int kRows = kThreads / kLanesPerRow;       // rows per pass: 32 or 64
+  constexpr int kPasses = (64 + kRows - 1) / kRows;    // headdim <= 64
+  constexpr float kMagic = 12582912.f;                 // 1.5 * 2^23: unit spacing, code in the low byte
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = bh % nheads;
+  const int b = bh / nheads;
+  const int g = h / (nheads / ngroups);
+  const int tid = threadIdx.x;
+  const int nq = tid % kLanesPerRow;
+  const int r0 = tid / kLanesPerRow;
+  const int P = headdim;
+
+  int8_t* st = state + int64_t(bh) * P * N;
+  float* ss = state_scale + int64_t(bh) * P;
+  const int8_t* xr = x + int64_t(bh) * P;
+  v4u hv[kPasses];
+  float so[kPasses];
+  int xq[kPasses];
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = min(r0 + kRows * k, P - 1);   // rows past headdim: a clamped, unused load
+    hv[k] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(st + int64_t(p) * N + 16 * nq));
+  }
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = min(r0 + kRows * k, P - 1);
+    so[k] = ss[p];
+    xq[k] = xr[p];
+  }
+  const v4u bw = *reinterpret_cast<const v4u*>(Bm + (int64_t(b) * ngroups + g) * N + 16 * nq);
+  const v4u cw = *reinterpret_cast<const v4u*>(Cm + (int64_t(b) * ngroups + g) * N + 16 * nq);
+  const float d = dt[bh];
+  const float a = __expf(d * A[h]);
+  const float sx = x_scale[h];
+  const float dxB = d * sx * B_scale[g];
+  const float Dsx = (D ? D[h] : 0.f) * sx;
+  const float sC = C_scale[g];
+  float bq[16], cq[16];   // the B and C codes as floats (scales applied per row / at the end)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    bq[i] = sbyte(bw[i >> 2], i & 3);
+    cq[i] = sbyte(cw[i >> 2], i & 3);
+  }
+
+#pragma unroll
+  for (int k = 0; k < kPasses; ++k) {
+    const int p = r0 + kRows * k;
+    const float xp = float(xq[k]);
+    const float uB = dxB * xp;          // dt xhat[p] sB
+    const float as = a * so[k];         // exp(dt A) times the cached row's scale
+    const float c0 = -128.f * as;       // the code offset of the unsigned bytes
+    float v[16];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = hv[k][j] ^ 0x80808080u;   // code + 128 in every byte
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ub = float((w >> (8 * i)) & 0xffu);
+        v[4 * j + i] = fmaf(as, ub, fmaf(uB, bq[4 * j + i], c0));
+        m = fmaxf(m, fabsf(v[4 * j + i]));
+      }
+    }
+    m = group_max<kLanesPerRow>(m);
+    const float s = m / 127.f;
+    const float inv = s > 0.f ? 1.f / s : 0.f;
+    v4u out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = __builtin_amdgcn_fmed3f(fmaf(v[4 * j + i], inv, kMagic), kMagic - 127.f, kMagic + 127.f);
+        t[i] = __float_as_uint(c);
+      }
+      const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);   // bytes: t0.b0, t1.b0, 0, 0
+      const uint32_t hi = __builtin_amdgcn_perm(t[3], t[2], 0x0c0c0400u);
+      out[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);                   // lo.b0, lo.b1, hi.b0, hi.b1
+    }
+    if (p < P) __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(st + int64_t(p) * N + 16 * nq));
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part = fmaf(cq[i], v[i], part);
+    part = group_sum<kLanesPerRow>(part);
+    if (p < P && nq == 0) {
+      ss[p] = s;
+      y[int64_t(bh) * P + p] = _Float16(fmaf(sC, part, Dsx * xp));
+    }
+  }
+}
+
 template <int N>
 hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
                     const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
@@ -197,6 +308,21 @@ hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float
   else
     hipLaunchKernelGGL((state_update_f16_kernel<64>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
                        B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
+                                  const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
+                                  const float* dt, const float* A, const float* D, _Float16* y, int32_t batch,
+                                  int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                  hipStream_t stream) {
+  const int nblocks = batch * nheads;
+  if (dstate == 128)
+    hipLaunchKernelGGL((state_update_i8_kernel<128>), dim3(nblocks), dim3(kThreads), 0, stream, state, state_scale,
+                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+  else
+    hipLaunchKernelGGL((state_update_i8_kernel<64>), dim3(nblocks), dim3(kThreads), 0, stream, state, state_scale,
+                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }
 

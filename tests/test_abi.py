@@ -33,6 +33,7 @@ def lib():
     lib.ssdq_chunk_scan_workspace_size.restype = sz
     lib.ssdq_state_update.argtypes = [P] * 11 + [i32] * 5 + [P]
     lib.ssdq_state_update_f16.argtypes = [P] * 11 + [i32] * 5 + [P]
+    lib.ssdq_state_update_i8.argtypes = [P] * 12 + [i32] * 5 + [P]
     lib.ssdq_status_string.argtypes = [ctypes.c_int]
     lib.ssdq_status_string.restype = ctypes.c_char_p
     return lib
@@ -159,13 +160,15 @@ def test_quantize_batch_rejects_null_jobs(lib):
     assert lib.ssdq_quantize_batch(None, 1, None) == INVALID
 
 
-def _upd(lib, f16=False, **kw):
-    a = dict(state=A16, x=A16, xs=A16, B=A16, Bs=A16, C=A16, Cs=A16, dt=A16, A=A16, D=None, y=A16,
+def _upd(lib, kind="f32", **kw):
+    a = dict(state=A16, scale=A16, x=A16, xs=A16, B=A16, Bs=A16, C=A16, Cs=A16, dt=A16, A=A16, D=None, y=A16,
              b=2, H=8, P=64, N=128, G=2)
     a.update(kw)
-    call = lib.ssdq_state_update_f16 if f16 else lib.ssdq_state_update
-    return call(*[a[k] for k in ("state", "x", "xs", "B", "Bs", "C", "Cs", "dt", "A", "D", "y",
-                                 "b", "H", "P", "N", "G")], None)
+    rest = [a[k] for k in ("x", "xs", "B", "Bs", "C", "Cs", "dt", "A", "D", "y", "b", "H", "P", "N", "G")]
+    if kind == "i8":
+        return lib.ssdq_state_update_i8(a["state"], a["scale"], *rest, None)
+    call = lib.ssdq_state_update_f16 if kind == "f16" else lib.ssdq_state_update
+    return call(a["state"], *rest, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -176,6 +179,11 @@ def _upd(lib, f16=False, **kw):
     (dict(N=96), UNSUPPORTED),
     (dict(P=128), UNSUPPORTED),
 ])
-@pytest.mark.parametrize("f16", [False, True])   # fp32 state and binary16-cached state
-def test_state_update_validation(lib, kw, status, f16):
-    assert _upd(lib, f16=f16, **kw) == status
+@pytest.mark.parametrize("kind", ["f32", "f16", "i8"])   # fp32, binary16-cached and 8-bit-cached state
+def test_state_update_validation(lib, kw, status, kind):
+    assert _upd(lib, kind=kind, **kw) == status
+
+
+@pytest.mark.parametrize("scale", [None, A16 + 4])
+def test_state_update_i8_needs_an_aligned_scale(lib, scale):
+    assert _upd(lib, kind="i8", scale=scale) == INVALID
