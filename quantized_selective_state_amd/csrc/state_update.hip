@@ -180,20 +180,24 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
 // nearest even.  A row of N codes is N/16 lanes with one 16-byte load each, so the row maximum
 // and y's dot product are reductions over at most 8 neighbouring lanes (DPP, in registers).
 //
-// Arithmetic per element, kept short because at 1 byte per element the step is close to
-// VALU-bound as well: the cached code arrives as an unsigned byte (sign bit flipped, converted
-// with the byte-select conversion) and its offset of 128 is folded into a per-element constant;
-// the new code is one fma into the binade of 1.5 * 2^23, whose unit spacing makes the fma's own
-// rounding the round-to-nearest-even of the quotient and leaves the code in the low byte.
+// At 1 byte per element the step would be VALU-bound with a plain float loop, so:
+//  - y needs no per-element float work: with u = (e s) q + (dt xhat sB) b (q the cached codes,
+//    b the B codes, e = exp(dt A)), sum_n c_n u_n = (e s) <c, q> + (dt xhat sB) <c, b>, and
+//    both dot products are over int8 codes: four-way int8 dot instructions, exact in int32;
+//  - the new code is one fma into the binade of 1.5 * 2^23, whose unit spacing makes the fma's
+//    own rounding the round-to-nearest-even of u / s and leaves the code in the low byte, then
+//    a clamp and byte permutes pack four codes per dword.
+constexpr int kI8Threads = 128;   // two waves per (batch, head): four row passes per lane amortize the set-up
+
 template <int N>
-__global__ void __launch_bounds__(kThreads) state_update_i8_kernel(
+__global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     int8_t* __restrict__ state, float* __restrict__ state_scale, const int8_t* __restrict__ x,
     const float* __restrict__ x_scale, const int8_t* __restrict__ Bm, const float* __restrict__ B_scale,
     const int8_t* __restrict__ Cm, const float* __restrict__ C_scale, const float* __restrict__ dt,
     const float* __restrict__ A, const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads,
     int32_t headdim, int32_t ngroups) {
   constexpr int kLanesPerRow = N / 16;                 // 8 (N = 128) or 4 (N = 64)
-  constexpr int kRows = kThreads / kLanesPerRow;       // rows per pass: 32 or 64
+  constexpr int kRows = kI8Threads / kLanesPerRow;     // rows per pass: 16 or 32
   constexpr int kPasses = (64 + kRows - 1) / kRows;    // headdim <= 64
   constexpr float kMagic = 12582912.f;                 // 1.5 * 2^23: unit spacing, code in the low byte
   const int bh = xcd_remap(blockIdx.x, gridDim.x);
@@ -230,12 +234,13 @@ __global__ void __launch_bounds__(kThreads) state_update_i8_kernel(
   const float dxB = d * sx * B_scale[g];
   const float Dsx = (D ? D[h] : 0.f) * sx;
   const float sC = C_scale[g];
-  float bq[16], cq[16];   // the B and C codes as floats (scales applied per row / at the end)
+  float bq[16];   // the B codes as floats (the scale is applied per row)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    bq[i] = sbyte(bw[i >> 2], i & 3);
-    cq[i] = sbyte(cw[i >> 2], i & 3);
-  }
+  for (int i = 0; i < 16; ++i) bq[i] = sbyte(bw[i >> 2], i & 3);
+  int cb = 0;     // <c, b> over this lane's 16 states
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cb = __builtin_amdgcn_sdot4(int(cw[j]), int(bw[j]), cb, false);
+  const float cbf = float(cb);
 
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
@@ -243,22 +248,22 @@ __global__ void __launch_bounds__(kThreads) state_update_i8_kernel(
     const float xp = float(xq[k]);
     const float uB = dxB * xp;          // dt xhat[p] sB
     const float as = a * so[k];         // exp(dt A) times the cached row's scale
-    const float c0 = -128.f * as;       // the code offset of the unsigned bytes
     float v[16];
     float m = 0.f;
+    int cq = 0;                         // <c, q> over this lane's 16 cached codes
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w = hv[k][j] ^ 0x80808080u;   // code + 128 in every byte
+      cq = __builtin_amdgcn_sdot4(int(cw[j]), int(hv[k][j]), cq, false);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ub = float((w >> (8 * i)) & 0xffu);
-        v[4 * j + i] = fmaf(as, ub, fmaf(uB, bq[4 * j + i], c0));
+        v[4 * j + i] = fmaf(as, sbyte(hv[k][j], i), uB * bq[4 * j + i]);
         m = fmaxf(m, fabsf(v[4 * j + i]));
       }
     }
     m = group_max<kLanesPerRow>(m);
     const float s = m / 127.f;
-    const float inv = s > 0.f ? 1.f / s : 0.f;
+    // 1 / s to within an ulp: a code can move only where u / s is that close to a midpoint
+    const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
     v4u out;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -273,9 +278,7 @@ __global__ void __launch_bounds__(kThreads) state_update_i8_kernel(
       out[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);                   // lo.b0, lo.b1, hi.b0, hi.b1
     }
     if (p < P) __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(st + int64_t(p) * N + 16 * nq));
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) part = fmaf(cq[i], v[i], part);
+    float part = fmaf(as, float(cq), uB * cbf);
     part = group_sum<kLanesPerRow>(part);
     if (p < P && nq == 0) {
       ss[p] = s;
@@ -318,10 +321,10 @@ hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_
                                   hipStream_t stream) {
   const int nblocks = batch * nheads;
   if (dstate == 128)
-    hipLaunchKernelGGL((state_update_i8_kernel<128>), dim3(nblocks), dim3(kThreads), 0, stream, state, state_scale,
+    hipLaunchKernelGGL((state_update_i8_kernel<128>), dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale,
                        x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
   else
-    hipLaunchKernelGGL((state_update_i8_kernel<64>), dim3(nblocks), dim3(kThreads), 0, stream, state, state_scale,
+    hipLaunchKernelGGL((state_update_i8_kernel<64>), dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale,
                        x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }
