@@ -47,6 +47,10 @@ def _load():
     lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P]
     lib.oracle_ssd_sequential_state_f16.restype = None
     lib.oracle_round_binary16.argtypes = [P, P, i64]
+    lib.oracle_frontend.argtypes = [P, P, P, i32, i32, i64, i32, P, P, P]
+    lib.oracle_frontend.restype = None
+    lib.oracle_softplus_dt.argtypes = [P, P, i64, i32, P]
+    lib.oracle_softplus_dt.restype = None
     lib.oracle_requantize_rows_i8.argtypes = [P, i64, i32, P, P, P]
     lib.oracle_requantize_rows_i8.restype = None
     lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
@@ -214,6 +218,40 @@ def requantize_rows_i8(rows: np.ndarray):
     out = np.empty(r.shape, np.float64)
     _load().oracle_requantize_rows_i8(_ptr(r), r.shape[0], r.shape[1], _ptr(q), _ptr(s), _ptr(out))
     return q, s, out
+
+
+def frontend(xbc16: np.ndarray, w: np.ndarray, bias, x_scale, B_scale, C_scale, H: int, P: int,
+             G: int, N: int) -> dict:
+    """The block's front end on (batch, L, H*P + 2*G*N) binary16 activations: the convolution +
+    bias (`pre`), SiLU of it (`act`, unrounded), the binary16 module output (`act16`), and the
+    static INT8 codes of its x, B and C slices (`qx` (b,L,H,P), `qB`, `qC` (b,L,G,N))."""
+    x = _c(xbc16, np.float16)
+    b, L, C = x.shape
+    if C != H * P + 2 * G * N:
+        raise ValueError("channels must be H*P + 2*G*N")
+    w = _c(w, np.float32)
+    dconv = w.shape[1]
+    bias = _c(bias, np.float32)
+    pre = np.empty((b, L, C), np.float64)
+    act = np.empty((b, L, C), np.float64)
+    a16 = np.empty((b, L, C), np.float64)
+    _load().oracle_frontend(_ptr(x.view(np.uint16)), _ptr(w), _ptr(bias), dconv, b, L, C, _ptr(pre), _ptr(act),
+                            _ptr(a16))
+    act16 = a16.astype(np.float16)          # exact: every value is a binary16 value
+    hp, gn = H * P, G * N
+    return dict(pre=pre, act=act, act16=act16,
+                qx=quantize(act16[..., :hp].reshape(b, L, H, P), x_scale),
+                qB=quantize(act16[..., hp:hp + gn].reshape(b, L, G, N), B_scale),
+                qC=quantize(act16[..., hp + gn:].reshape(b, L, G, N), C_scale))
+
+
+def softplus_dt(dt_raw: np.ndarray, dt_bias) -> np.ndarray:
+    """softplus(dt_raw + dt_bias[h]) in float64; dt_raw (..., H)."""
+    d = _c(dt_raw, np.float32)
+    H = d.shape[-1]
+    out = np.empty(d.shape, np.float64)
+    _load().oracle_softplus_dt(_ptr(d), _ptr(_c(dt_bias, np.float32)), d.size // H, H, _ptr(out))
+    return out
 
 
 def round_binary16(v: np.ndarray) -> np.ndarray:

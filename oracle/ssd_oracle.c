@@ -36,6 +36,10 @@
  *    [-127, 127] with s = max|row| / 127 (the reading stated at
  *    requantize_row_i8).
  *
+ *  - oracle_frontend / oracle_softplus_dt: the block's front end ahead of the
+ *    quantizer (depthwise causal conv1d + bias + SiLU, rounded to binary16) and
+ *    dt = softplus(dt_raw + dt_bias), each as the reading stated at the function.
+ *
  *  - oracle_chunk_cumsum / oracle_chunk_state: the two per-chunk quantities of
  *    the chunked (state-space-duality) evaluation, each from its definition:
  *    Acs[c, j] = sum_{i <= j} dt_{cQ+i} A_h  and
@@ -247,6 +251,47 @@ void oracle_ssd_sequential_state_i8(const int8_t* qx, const float* sx, const int
                                     double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, NULL, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 2,
                  q0, s0, q_out, s_out, u_last);
+}
+
+/* Front end of the SSD block (the causal convolution ahead of the SSD box, Quamba2 rebuttal
+ * Tables R6/R7, kept in FP16 as Ternary Mamba's quantization section lists; SSDi8 Table 16's
+ * Conv column).  The pages give no algebra for it; the reading taken is the one the rest
+ * supports: a depthwise causal convolution of width dconv along the tokens of every channel of
+ * the in-projection output xBC (channels x, then B, then C), zero before the first token, plus a
+ * per-channel bias, then SiLU(v) = v / (1 + exp(-v)); the module's FP16 output is that value
+ * rounded to binary16 (then quantized by the static quantizer above).
+ *   xbc: (batch, L, C) binary16 bits; w: (C, dconv) (tap k multiplies token t - dconv + 1 + k);
+ *   bias: (C) or NULL.  pre_out (optional): the convolution + bias; act_out: SiLU of it (both
+ *   double, unrounded); act16_out: act rounded to the nearest binary16 (as a double). */
+void oracle_frontend(const uint16_t* xbc, const float* w, const float* bias, int32_t dconv, int32_t batch,
+                     int64_t L, int32_t C, double* pre_out, double* act_out, double* act16_out) {
+  for (int32_t b = 0; b < batch; ++b)
+    for (int64_t t = 0; t < L; ++t)
+      for (int32_t ch = 0; ch < C; ++ch) {
+        double v = bias ? (double)bias[ch] : 0.0;
+        for (int32_t k = 0; k < dconv; ++k) {
+          const int64_t src = t - dconv + 1 + k;
+          if (src < 0) continue;
+          v += (double)w[(int64_t)ch * dconv + k] * half_bits_to_double(xbc[((int64_t)b * L + src) * C + ch]);
+        }
+        const int64_t o = ((int64_t)b * L + t) * C + ch;
+        const double a = v / (1.0 + exp(-v));
+        if (pre_out) pre_out[o] = v;
+        if (act_out) act_out[o] = a;
+        act16_out[o] = round_to_binary16(a);
+      }
+}
+
+/* dt = softplus(dt_raw + dt_bias[h]) (Ternary Mamba names dt_bias among the SSM parameters; the
+ * softplus is Mamba's positive map for dt), softplus(v) = log(1 + exp(v)) evaluated as
+ * max(v, 0) + log1p(exp(-|v|)), which is the same function without overflow.
+ * dt_raw: (rows, H); out: (rows, H) double. */
+void oracle_softplus_dt(const float* dt_raw, const float* dt_bias, int64_t rows, int32_t H, double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t h = 0; h < H; ++h) {
+      const double v = (double)dt_raw[r * H + h] + (dt_bias ? (double)dt_bias[h] : 0.0);
+      out[r * H + h] = fmax(v, 0.0) + log1p(exp(-fabs(v)));
+    }
 }
 
 /* Acs for one (b, h): out[c * chunk + j] = sum_{i <= j} dt[cQ + i] * A[h] within chunk c,

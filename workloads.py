@@ -174,6 +174,33 @@ def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch
                 batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=shape.chunk)
 
 
+def make_frontend(shape: PrefillShape | str, seed_index: int | None = None, batch: int | None = None,
+                  seqlen: int | None = None) -> dict:
+    """Seeded inputs of the block's front end for a prefill shape: the in-projection output xBC
+    (b, L, H*P + 2*G*N) fp16 with channels [x | B | C] (the prefill draw's activations), depthwise
+    conv taps (C, 4) close to a pass-through of the newest token (tap 3 ~ 1 + N(0, 0.05), the
+    older taps ~ N(0, 0.1)) and a small bias, all fp16-representable fp32, raw dt ~ N(-4, 1) with
+    a per-head dt_bias ~ U(-0.5, 0.5), and the prefill draw's static x/B/C scales."""
+    inp = make_prefill(shape, seed_index, batch, seqlen)
+    b, L = inp["batch"], inp["seqlen"]
+    H, P, N, G = inp["nheads"], inp["headdim"], inp["dstate"], inp["ngroups"]
+    xbc = np.concatenate([inp["x16"].reshape(b, L, H * P), inp["B16"].reshape(b, L, G * N),
+                          inp["C16"].reshape(b, L, G * N)], axis=2)
+    C = xbc.shape[2]
+    name = shape if isinstance(shape, str) else shape.name
+    k = SEED_INDEX.get(name, 0) if seed_index is None else seed_index
+    rng = _rng(400 + k)
+    w = rng.standard_normal((C, 4)).astype(np.float32) * np.float32(0.1)
+    w[:, 3] = 1.0 + rng.standard_normal(C).astype(np.float32) * np.float32(0.05)
+    w = w.astype(np.float16).astype(np.float32)
+    bias = (rng.standard_normal(C) * 0.02).astype(np.float16).astype(np.float32)
+    dt_raw = (rng.standard_normal((b, L, H)) - 4.0).astype(np.float32)
+    dt_bias = rng.uniform(-0.5, 0.5, H).astype(np.float32)
+    return dict(xbc16=np.ascontiguousarray(xbc), conv_w=w, conv_b=bias, dt_raw=dt_raw, dt_bias=dt_bias,
+                x_scale=inp["x_scale"], B_scale=inp["B_scale"], C_scale=inp["C_scale"],
+                batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G)
+
+
 def make_decode(shape: DecodeShape | str, seed_index: int | None = None, batch: int | None = None,
                 steps: int | None = None) -> dict:
     """Seeded decode inputs: an fp32 state (b,H,P,N) and `steps` tokens per sequence.
