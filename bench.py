@@ -43,7 +43,8 @@ KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "chunk_state": "chunk_state.hip", "state_scan": "chunk_state.hip",
                  "state_passing": "state_passing.hip",
                  "chunk_output": "chunk_output.hip", "state_update": "state_update.hip",
-                 "state_update_f16": "state_update.hip", "state_update_i8": "state_update.hip"}
+                 "state_update_f16": "state_update.hip", "state_update_i8": "state_update.hip",
+                 "frontend": "quantize.hip"}
 
 
 def _code_only(text: str) -> str:
@@ -136,6 +137,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling HBM counter readings)")
     return ap.parse_args()
@@ -300,6 +302,9 @@ def main():
         "kernels": kernels,
     }
 
+    del buf, quant, fns, x16, B16, C16, qx, qB, qC
+    if not args.no_frontend:
+        result["frontend"] = bench_frontend(args, torch, ssdq, workloads, dev)
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, ssdq, workloads, dev)
 
@@ -317,6 +322,63 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_frontend(args, torch, ssdq, workloads, dev):
+    """The same prefill step with the fused front end in place of the quantize launch: the
+    depthwise causal conv1d + SiLU + static quantize of the in-projection output (x, B, C
+    channels) and dt = softplus(dt_raw + dt_bias), then the scan.  Times the front end alone
+    (events around each launch pair) and the whole step."""
+    name = "mamba2-1.3b-prefill"
+    print(f"[bench] generating {name} front end", file=sys.stderr, flush=True)
+    fe = workloads.make_frontend(name)
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    b, L, H, P, N, G, Q = (fe[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"))
+    xbc, w, cb = T(fe["xbc16"]), T(fe["conv_w"]), T(fe["conv_b"])
+    sx, sB, sC = T(fe["x_scale"]), T(fe["B_scale"]), T(fe["C_scale"])
+    raw, dtb, A, D = T(fe["dt_raw"]), T(fe["dt_bias"]), T(fe["A"]), T(fe["D"])
+    out = (torch.empty((b, L, H, P), dtype=torch.int8, device=dev),
+           torch.empty((b, L, G, N), dtype=torch.int8, device=dev),
+           torch.empty((b, L, G, N), dtype=torch.int8, device=dev),
+           torch.empty((b, L, H), dtype=torch.float32, device=dev))
+    qx, qB, qC, dt = out
+    buf = ssdq.ScanBuffers(qx, sx, qB, sB, qC, sC, dt, A, D, None, chunk=Q)
+    stages = [0, 2] if ssdq.chunk_scan_state_fused(b, H) else [0, 1, 2]
+    front = lambda: ssdq.frontend(xbc, w, cb, sx, sB, sC, raw, dtb, H, P, G, N, out=out)
+
+    def step():
+        front()
+        for st in stages:
+            buf.run_stage(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    steps = min(args.steps, 500)
+    pairs = [(HipEvent(stream), HipEvent(stream)) for _ in range(steps)]
+    for e0, e1 in pairs:
+        e0.record()
+        front()
+        e1.record()
+        for st in stages:
+            buf.run_stage(st)
+    torch.cuda.synchronize()
+    fe_ms = sum(e0.elapsed_time(e1) for e0, e1 in pairs) / steps
+    r0, r1 = HipEvent(stream), HipEvent(stream)
+    r0.record()
+    for _ in range(steps):
+        step()
+    r1.record()
+    torch.cuda.synchronize()
+    step_ms = r0.elapsed_time(r1) / steps
+    C = H * P + 2 * G * N
+    alg = 3 * b * L * C + 8 * b * L * H + 4 * 5 * C   # fp16 in + int8 out; dt in/out; taps + bias
+    gbs = alg / (fe_ms / 1e3) / 1e9
+    return {"workload": name, "channels": C, "frontend_us": round(fe_ms * 1e3, 2), "alg_bytes": alg,
+            "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("frontend"),
+            "step_us": round(step_ms * 1e3, 2), "step_tokens_per_s": round(b * L / (step_ms / 1e3), 1)}
 
 
 def bench_decode(args, torch, ssdq, workloads, dev):

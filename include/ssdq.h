@@ -237,6 +237,36 @@ ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t
                                  int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                                  hipStream_t stream);
 
+/*
+ * Front end of the SSD block, fused with the static quantizer: the causal convolution that the
+ * pages keep in FP16 ahead of the SSD box (Quamba2 rebuttal Tables R6/R7; SSDi8 Table 16, Conv
+ * column), read as Mamba-2's depthwise convolution of width 4 over the tokens of every channel
+ * of the in-projection output, with a per-channel bias and SiLU; its binary16 output is
+ * quantized as ssdq_quantize does, straight into the scan's layouts; and dt = softplus(dt_raw
+ * + dt_bias), the positive step size the scan takes.
+ *
+ *   xbc    : (batch, seqlen, nheads*headdim + 2*ngroups*dstate) binary16, channels [x | B | C]
+ *            (x channel h*headdim + p, then B channel g*dstate + n, then C likewise)
+ *   conv_w : (channels, d_conv) float32; tap k multiplies token t - d_conv + 1 + k (zero before 0)
+ *   conv_b : (channels) float32, or NULL for no bias
+ *   a[b,t,c] = binary16( SiLU( conv_b[c] + sum_k conv_w[c,k] xbc[b, t-3+k, c] ) ),  SiLU(v) = v / (1 + e^-v)
+ *   x      : (batch, seqlen, nheads, headdim) int8 = quantize(a[.., x channels], x_scale (nheads))
+ *   B, C   : (batch, seqlen, ngroups, dstate) int8 = quantize(a[.., B / C channels], B_scale / C_scale (ngroups))
+ *   dt_raw : (batch, seqlen, nheads) float32; dt_bias: (nheads) float32 or NULL
+ *   dt     : (batch, seqlen, nheads) float32 = softplus(dt_raw + dt_bias) = max(v,0) + log1p(e^-|v|)
+ * The codes are those of ssdq_quantize applied to a (bit-exact); a is formed in fp32, so an
+ * element whose exact SiLU value lies within fp32 rounding of a binary16 midpoint may take the
+ * other neighbour (and its code).  seqlen 0 is a no-op (after the size checks; pointers are not
+ * looked at then).  Errors: NULL or misaligned (16-byte) pointers, non-positive sizes or nheads % ngroups != 0 -> SSDQ_ERROR_INVALID_VALUE; d_conv other
+ * than 4, headdim or dstate not a multiple of 8, batch > 65536 or seqlen > 2^20 ->
+ * SSDQ_ERROR_UNSUPPORTED.  All pointers are device memory owned by the caller.
+ */
+ssdq_status ssdq_frontend(const void* xbc, const float* conv_w, const float* conv_b, int32_t d_conv,
+                          const float* x_scale, const float* B_scale, const float* C_scale, const float* dt_raw,
+                          const float* dt_bias, int8_t* x, int8_t* B, int8_t* C, float* dt, int32_t batch,
+                          int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -57,6 +57,8 @@ lib.ssdq_state_update.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update.restype = ctypes.c_int
 lib.ssdq_state_update_f16.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_f16.restype = ctypes.c_int
+lib.ssdq_frontend.argtypes = [_P, _P, _P, _i32] + [_P] * 9 + [_i32, ctypes.c_int64, _i32, _i32, _i32, _i32, _P]
+lib.ssdq_frontend.restype = ctypes.c_int
 lib.ssdq_state_update_i8.argtypes = [_P] * 12 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_i8.restype = ctypes.c_int
 lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
@@ -262,6 +264,40 @@ def chunk_scan(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk
 
 # ---------------------------------------------------------------------------------------------
 # decode
+
+
+def frontend(xbc, conv_w, conv_b, x_scale, B_scale, C_scale, dt_raw, dt_bias, nheads: int, headdim: int,
+             ngroups: int, dstate: int, out=None):
+    """The block's front end fused with the quantizer (ssdq_frontend): xbc (b,L,H*P+2*G*N) fp16
+    -> codes x (b,L,H,P), B, C (b,L,G,N) int8 and dt (b,L,H) fp32 = softplus(dt_raw + dt_bias).
+    Returns (x, B, C, dt); `out` may give those four tensors."""
+    if xbc.dim() != 3:
+        raise ValueError("xbc must be (batch, seqlen, channels)")
+    b, L, ch = xbc.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    dev = xbc.device
+    _need(xbc, "xbc", torch.float16, (b, L, H * P + 2 * G * N), dev)
+    _need(conv_w, "conv_w", torch.float32, (ch, 4), dev)
+    _need(conv_b, "conv_b", torch.float32, (ch,), dev, optional=True)
+    _need(x_scale, "x_scale", torch.float32, (H,), dev)
+    _need(B_scale, "B_scale", torch.float32, (G,), dev)
+    _need(C_scale, "C_scale", torch.float32, (G,), dev)
+    _need(dt_raw, "dt_raw", torch.float32, (b, L, H), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (H,), dev, optional=True)
+    if out is None:
+        out = (torch.empty((b, L, H, P), dtype=torch.int8, device=dev),
+               torch.empty((b, L, G, N), dtype=torch.int8, device=dev),
+               torch.empty((b, L, G, N), dtype=torch.int8, device=dev),
+               torch.empty((b, L, H), dtype=torch.float32, device=dev))
+    x, B, C, dt = out
+    _need(x, "x", torch.int8, (b, L, H, P), dev)
+    _need(B, "B", torch.int8, (b, L, G, N), dev)
+    _need(C, "C", torch.int8, (b, L, G, N), dev)
+    _need(dt, "dt", torch.float32, (b, L, H), dev)
+    _check(lib.ssdq_frontend(_ptr(xbc), _ptr(conv_w), _ptr(conv_b), 4, _ptr(x_scale), _ptr(B_scale),
+                             _ptr(C_scale), _ptr(dt_raw), _ptr(dt_bias), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), b, L,
+                             H, P, N, G, _stream(dev)), "ssdq_frontend")
+    return x, B, C, dt
 
 
 def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=None, state_scale=None) -> torch.Tensor:

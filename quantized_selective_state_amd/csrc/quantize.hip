@@ -146,6 +146,119 @@ int grid_for(int64_t work, int block) {
   return int(g < 1 ? 1 : g);
 }
 
+// Front end of the SSD block fused with the quantizer: the depthwise causal convolution of
+// width 4 over the tokens of every in-projection channel (channels x | B | C, zero before the
+// first token) plus a bias, SiLU, the binary16 module output, and its static INT8 code written
+// straight into the scan's x, B or C layout (the causal convolution the pages keep in FP16
+// ahead of the SSD box: Quamba2 rebuttal Tables R6/R7, SSDi8 Table 16's Conv column).  One
+// read of the fp16 activations and one write of the codes, instead of a convolution pass that
+// writes fp16 and a quantize pass that reads it again.
+//
+// A lane owns 8 consecutive channels (one 16-byte load per token) and walks a strip of
+// kFeTokens tokens, keeping the three previous tokens in registers; only the three tokens
+// before the strip are read twice.  The strip is short so that the launch has several waves
+// per SIMD to overlap the SiLU arithmetic (two quarter-rate transcendentals per element) with
+// the loads; all of the strip's loads are issued before any arithmetic.
+constexpr int kFeTokens = 16;
+
+__global__ void __launch_bounds__(64) frontend_kernel(
+    const uint16_t* __restrict__ xbc, const float* __restrict__ w, const float* __restrict__ bias,
+    const float* __restrict__ x_scale, const float* __restrict__ B_scale, const float* __restrict__ C_scale,
+    int8_t* __restrict__ qx, int8_t* __restrict__ qB, int8_t* __restrict__ qC, int64_t seqlen, int32_t HP,
+    int32_t GN, int32_t P, int32_t N, int32_t nvec) {
+  const int vec = int(blockIdx.x) * 64 + int(threadIdx.x);
+  if (vec >= nvec) return;   // no barriers below
+  const int C = HP + 2 * GN;
+  const int ch0 = 8 * vec;
+  const int64_t b = blockIdx.z;
+  const int64_t t0 = int64_t(blockIdx.y) * kFeTokens;
+  const int64_t t1 = min(t0 + kFeTokens, seqlen);
+  int8_t* dst;
+  int64_t stride;
+  float s;
+  if (ch0 < HP) {
+    dst = qx + ch0;
+    stride = HP;
+    s = x_scale[ch0 / P];
+  } else if (ch0 < HP + GN) {
+    dst = qB + (ch0 - HP);
+    stride = GN;
+    s = B_scale[(ch0 - HP) / N];
+  } else {
+    dst = qC + (ch0 - HP - GN);
+    stride = GN;
+    s = C_scale[(ch0 - HP - GN) / N];
+  }
+  float tap[4][8], bi[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {   // taps of channel ch0 + e are w[4 (ch0 + e) + k]: 32 floats
+    const v4f t = *reinterpret_cast<const v4f*>(w + int64_t(ch0) * 4 + 4 * q);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tap[k][q] = t[k];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) bi[e] = bias ? bias[ch0 + e] : 0.f;
+  const uint16_t* src = xbc + b * seqlen * C + ch0;
+  float h1[8], h2[8], h3[8];   // tokens t - 1, t - 2, t - 3
+  {
+    float v[8];
+    v4u raw[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int64_t t = t0 - 1 - j;
+      raw[j] = t >= 0 ? *reinterpret_cast<const v4u*>(src + t * C) : v4u{0u, 0u, 0u, 0u};
+    }
+    unpack8(raw[0], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h1[e] = v[e];
+    unpack8(raw[1], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h2[e] = v[e];
+    unpack8(raw[2], v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h3[e] = v[e];
+  }
+  int8_t* out = dst + b * seqlen * stride;
+  v4u raw[kFeTokens];
+#pragma unroll
+  for (int u = 0; u < kFeTokens; ++u)
+    raw[u] = t0 + u < t1 ? *reinterpret_cast<const v4u*>(src + (t0 + u) * C) : v4u{0u, 0u, 0u, 0u};
+  {
+    const int64_t t = t0;
+#pragma unroll
+    for (int u = 0; u < kFeTokens; ++u) {   // fully unrolled; tokens past the strip are not stored
+      float cur[8], a[8];
+      unpack8(raw[u], cur);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = fmaf(tap[0][e], h3[e], bi[e]);
+        v = fmaf(tap[1][e], h2[e], v);
+        v = fmaf(tap[2][e], h1[e], v);
+        v = fmaf(tap[3][e], cur[e], v);
+        const float silu = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+        a[e] = float(_Float16(silu));   // the module's binary16 output (round to nearest even)
+        h3[e] = h2[e];
+        h2[e] = h1[e];
+        h1[e] = cur[e];
+      }
+      uint32_t c[8];
+      codes<8>(a, s, c);
+      const v2u packed = {pack4(c), pack4(c + 4)};
+      if (t + u < t1) *reinterpret_cast<v2u*>(out + (t + u) * stride) = packed;
+    }
+  }
+}
+
+// dt = softplus(dt_raw + dt_bias[h]) = max(v, 0) + log1p(exp(-|v|)), one element per thread
+__global__ void __launch_bounds__(256) softplus_dt_kernel(const float* __restrict__ raw,
+                                                          const float* __restrict__ dt_bias,
+                                                          float* __restrict__ dt, int64_t n, int32_t H) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = raw[i] + (dt_bias ? dt_bias[i % H] : 0.f);
+  dt[i] = fmaxf(v, 0.f) + log1pf(__expf(-fabsf(v)));
+}
+
 }  // namespace
 
 hipError_t launch_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream) {
@@ -206,6 +319,23 @@ hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int
     hipLaunchKernelGGL(quantize_scalar, dim3(grid_for(n - done, 256)), dim3(256), 0, stream, x, q, scale, done,
                        n, nscale, inner);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_frontend(const uint16_t* xbc, const float* conv_w, const float* conv_b, const float* x_scale,
+                           const float* B_scale, const float* C_scale, const float* dt_raw, const float* dt_bias,
+                           int8_t* x, int8_t* B, int8_t* C, float* dt, int32_t batch, int64_t seqlen,
+                           int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  const int32_t HP = nheads * headdim, GN = ngroups * dstate;
+  const int32_t nvec = (HP + 2 * GN) / 8;
+  const dim3 grid((nvec + 63) / 64, uint32_t((seqlen + kFeTokens - 1) / kFeTokens), batch);   // y <= 65536 (host-checked)
+  hipLaunchKernelGGL(frontend_kernel, grid, dim3(64), 0, stream, xbc, conv_w, conv_b, x_scale, B_scale, C_scale, x,
+                     B, C, seqlen, HP, GN, headdim, dstate, nvec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = int64_t(batch) * seqlen * nheads;
+  hipLaunchKernelGGL(softplus_dt_kernel, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, stream, dt_raw, dt_bias, dt,
+                     n, nheads);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ def lib():
     lib.ssdq_state_update.argtypes = [P] * 11 + [i32] * 5 + [P]
     lib.ssdq_state_update_f16.argtypes = [P] * 11 + [i32] * 5 + [P]
     lib.ssdq_state_update_i8.argtypes = [P] * 12 + [i32] * 5 + [P]
+    lib.ssdq_frontend.argtypes = [P, P, P, i32] + [P] * 9 + [i32, i64, i32, i32, i32, i32, P]
     lib.ssdq_status_string.argtypes = [ctypes.c_int]
     lib.ssdq_status_string.restype = ctypes.c_char_p
     return lib
@@ -187,3 +188,28 @@ def test_state_update_validation(lib, kw, status, kind):
 @pytest.mark.parametrize("scale", [None, A16 + 4])
 def test_state_update_i8_needs_an_aligned_scale(lib, scale):
     assert _upd(lib, kind="i8", scale=scale) == INVALID
+
+
+def _fe(lib, **kw):
+    a = dict(xbc=A16, w=A16, bias=None, dconv=4, xs=A16, Bs=A16, Cs=A16, raw=A16, dtb=None, x=A16, B=A16, C=A16,
+             dt=A16, b=2, L=100, H=8, P=64, N=128, G=2)
+    a.update(kw)
+    return lib.ssdq_frontend(*[a[k] for k in ("xbc", "w", "bias", "dconv", "xs", "Bs", "Cs", "raw", "dtb", "x", "B",
+                                              "C", "dt", "b", "L", "H", "P", "N", "G")], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(xbc=None), INVALID),
+    (dict(dt=A16 + 4), INVALID),
+    (dict(bias=A16 + 8), INVALID),
+    (dict(b=0), INVALID),
+    (dict(L=-1), INVALID),
+    (dict(H=8, G=3), INVALID),
+    (dict(dconv=3), UNSUPPORTED),
+    (dict(P=20), UNSUPPORTED),
+    (dict(N=12), UNSUPPORTED),
+    (dict(L=(1 << 20) + 1), UNSUPPORTED),
+    (dict(L=0, xbc=None, x=None), OK),
+])
+def test_frontend_validation(lib, kw, status):
+    assert _fe(lib, **kw) == status

@@ -1,0 +1,89 @@
+"""GPU parity of ssdq_frontend: depthwise causal conv1d + bias + SiLU, binary16, static INT8
+codes, and dt = softplus(dt_raw + dt_bias), against the oracle.
+
+The kernel forms the SiLU value in fp32 and rounds it to binary16; the oracle in double.  They
+can part only where the exact value lies within fp32 rounding (a few 2^-24 relative) of a
+midpoint between two binary16 neighbours; everywhere else the binary16 value, hence the code
+(the quantizer is bit-exact), must be the oracle's.  Near a midpoint the code of either
+neighbour is accepted.  dt is compared to a relative 1e-6 (a few fp32 roundings)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import dev, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BAND = 2.0 ** -7   # of a binary16 spacing: far above fp32 SiLU error, far below a spacing
+
+
+def _gpu(fe):
+    import quantized_selective_state_amd as ssdq
+    H, P, G, N = fe["nheads"], fe["headdim"], fe["ngroups"], fe["dstate"]
+    x, B, C, dt = ssdq.frontend(to_dev(fe["xbc16"]), to_dev(fe["conv_w"]), to_dev(fe["conv_b"]),
+                                to_dev(fe["x_scale"]), to_dev(fe["B_scale"]), to_dev(fe["C_scale"]),
+                                to_dev(fe["dt_raw"]), to_dev(fe["dt_bias"]), H, P, G, N)
+    torch.cuda.synchronize()
+    return x.cpu().numpy(), B.cpu().numpy(), C.cpu().numpy(), dt.cpu().numpy()
+
+
+def _check(fe, tag):
+    H, P, G, N = fe["nheads"], fe["headdim"], fe["ngroups"], fe["dstate"]
+    b, L = fe["batch"], fe["seqlen"]
+    qx, qB, qC, dt = _gpu(fe)
+    ref = oracle.frontend(fe["xbc16"], fe["conv_w"], fe["conv_b"], fe["x_scale"], fe["B_scale"], fe["C_scale"],
+                          H, P, G, N)
+    act, a16 = ref["act"], ref["act16"]
+    up = act >= a16.astype(np.float64)
+    other = np.where(up, np.nextafter(a16, np.float16(np.inf)), np.nextafter(a16, np.float16(-np.inf)))
+    spacing = np.abs(other.astype(np.float64) - a16.astype(np.float64))
+    mid = (other.astype(np.float64) + a16.astype(np.float64)) / 2
+    near = np.abs(act - mid) <= BAND * spacing
+    hp, gn = H * P, G * N
+    parts = [("x", qx, ref["qx"], slice(0, hp), (H, P), fe["x_scale"]),
+             ("B", qB, ref["qB"], slice(hp, hp + gn), (G, N), fe["B_scale"]),
+             ("C", qC, ref["qC"], slice(hp + gn, hp + 2 * gn), (G, N), fe["C_scale"])]
+    n_near = n_diff = 0
+    for name, got, want, sl, shp, scale in parts:
+        alt = oracle.quantize(other[..., sl].reshape(b, L, *shp), scale)
+        nr = near[..., sl].reshape(b, L, *shp)
+        diff = got != want
+        assert not np.any(diff & ~nr), f"{name}: {int(np.sum(diff & ~nr))} codes differ away from a midpoint"
+        assert np.all(got[diff] == alt[diff]), f"{name}: a code near a midpoint is neither neighbour's"
+        n_near += int(nr.sum())
+        n_diff += int(diff.sum())
+    dref = oracle.softplus_dt(fe["dt_raw"], fe["dt_bias"])
+    e_dt = float(np.max(np.abs(dt - dref) / np.abs(dref)))
+    note(f"{tag}: {qx.size + qB.size + qC.size} codes, {n_near} near a binary16 midpoint, {n_diff} differ; "
+         f"dt rel {e_dt:.2e}")
+    assert e_dt <= 1e-6
+
+
+def test_tiny():
+    _check(workloads.make_frontend("tiny"), "tiny")
+
+
+def test_ragged_tokens_two_groups_no_bias():
+    shape = workloads.PrefillShape("fe_ragged", 2, 77, 6, 32, 64, 2, 64, "normal", "fixed_bias", 0.0)
+    fe = workloads.make_frontend(shape, seed_index=31)
+    fe["conv_b"] = None
+    fe["dt_bias"] = None
+    _check(fe, "ragged L=77, G=2, no bias")
+
+
+def test_prefill_workload_full():
+    fe = workloads.make_frontend("mamba2-1.3b-prefill")
+    _check(fe, "mamba2-1.3b-prefill")
+
+
+def test_empty_sequence_is_a_noop():
+    import quantized_selective_state_amd as ssdq
+    fe = workloads.make_frontend("tiny")
+    H, P, G, N = fe["nheads"], fe["headdim"], fe["ngroups"], fe["dstate"]
+    z = lambda *s, dt=torch.int8: torch.zeros(s, dtype=dt, device=dev())
+    out = (z(1, 0, H, P), z(1, 0, G, N), z(1, 0, G, N), z(1, 0, H, dt=torch.float32))
+    ssdq.frontend(to_dev(fe["xbc16"][:, :0]), to_dev(fe["conv_w"]), None, to_dev(fe["x_scale"]),
+                  to_dev(fe["B_scale"]), to_dev(fe["C_scale"]), to_dev(fe["dt_raw"][:, :0]), None, H, P, G, N, out=out)
+    torch.cuda.synchronize()

@@ -197,8 +197,8 @@ def make_frontend(shape: PrefillShape | str, seed_index: int | None = None, batc
     dt_raw = (rng.standard_normal((b, L, H)) - 4.0).astype(np.float32)
     dt_bias = rng.uniform(-0.5, 0.5, H).astype(np.float32)
     return dict(xbc16=np.ascontiguousarray(xbc), conv_w=w, conv_b=bias, dt_raw=dt_raw, dt_bias=dt_bias,
-                x_scale=inp["x_scale"], B_scale=inp["B_scale"], C_scale=inp["C_scale"],
-                batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G)
+                x_scale=inp["x_scale"], B_scale=inp["B_scale"], C_scale=inp["C_scale"], A=inp["A"], D=inp["D"],
+                batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=inp["chunk"])
 
 
 def make_decode(shape: DecodeShape | str, seed_index: int | None = None, batch: int | None = None,
