@@ -159,7 +159,7 @@ int grid_for(int64_t work, int block) {
 // before the strip are read twice.  The strip is short so that the launch has several waves
 // per SIMD to overlap the SiLU arithmetic (two quarter-rate transcendentals per element) with
 // the loads; all of the strip's loads are issued before any arithmetic.
-constexpr int kFeTokens = 16;
+constexpr int kFeTokens = 8;
 
 __global__ void __launch_bounds__(64) frontend_kernel(
     const uint16_t* __restrict__ xbc, const float* __restrict__ w, const float* __restrict__ bias,

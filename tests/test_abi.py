@@ -208,7 +208,7 @@ def _fe(lib, **kw):
     (dict(dconv=3), UNSUPPORTED),
     (dict(P=20), UNSUPPORTED),
     (dict(N=12), UNSUPPORTED),
-    (dict(L=(1 << 20) + 1), UNSUPPORTED),
+    (dict(L=(1 << 19) + 1), UNSUPPORTED),
     (dict(L=0, xbc=None, x=None), OK),
 ])
 def test_frontend_validation(lib, kw, status):
