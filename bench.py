@@ -44,7 +44,7 @@ KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "state_passing": "state_passing.hip",
                  "chunk_output": "chunk_output.hip", "state_update": "state_update.hip",
                  "state_update_f16": "state_update.hip", "state_update_i8": "state_update.hip",
-                 "frontend": "quantize.hip"}
+                 "frontend": "quantize.hip", "frontend (dt softplus)": "quantize.hip"}
 
 
 def _code_only(text: str) -> str:
@@ -61,6 +61,10 @@ def source_digest(kernel: str) -> str:
         with open(os.path.join(ROOT, "quantized_selective_state_amd", "csrc", f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def _sum_or_none(*vals):
+    return None if any(v is None for v in vals) else sum(vals)
 
 
 def measured_traffic(kernel: str):
@@ -377,7 +381,7 @@ def bench_frontend(args, torch, ssdq, workloads, dev):
     gbs = alg / (fe_ms / 1e3) / 1e9
     return {"workload": name, "channels": C, "frontend_us": round(fe_ms * 1e3, 2), "alg_bytes": alg,
             "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("frontend"),
+            "traffic": _sum_or_none(measured_traffic("frontend"), measured_traffic("frontend (dt softplus)")),
             "step_us": round(step_ms * 1e3, 2), "step_tokens_per_s": round(b * L / (step_ms / 1e3), 1)}
 
 
