@@ -258,7 +258,8 @@ ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t
  * element whose exact SiLU value lies within fp32 rounding of a binary16 midpoint may take the
  * other neighbour (and its code).  seqlen 0 is a no-op (after the size checks; pointers are not
  * looked at then).  Errors: NULL or misaligned (16-byte) pointers, non-positive sizes or nheads % ngroups != 0 -> SSDQ_ERROR_INVALID_VALUE; d_conv other
- * than 4, headdim or dstate not a multiple of 8, batch > 65536 or seqlen > 2^19 ->
+ * than 4, headdim or dstate not a multiple of 8, or batch * ceil(channels / 512) * ceil(seqlen / 8)
+ * >= 2^31 ->
  * SSDQ_ERROR_UNSUPPORTED.  All pointers are device memory owned by the caller.
  */
 ssdq_status ssdq_frontend(const void* xbc, const float* conv_w, const float* conv_b, int32_t d_conv,

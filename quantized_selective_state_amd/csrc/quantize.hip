@@ -165,13 +165,19 @@ __global__ void __launch_bounds__(64) frontend_kernel(
     const uint16_t* __restrict__ xbc, const float* __restrict__ w, const float* __restrict__ bias,
     const float* __restrict__ x_scale, const float* __restrict__ B_scale, const float* __restrict__ C_scale,
     int8_t* __restrict__ qx, int8_t* __restrict__ qB, int8_t* __restrict__ qC, int64_t seqlen, int32_t HP,
-    int32_t GN, int32_t P, int32_t N, int32_t nvec) {
-  const int vec = int(blockIdx.x) * 64 + int(threadIdx.x);
+    int32_t GN, int32_t P, int32_t N, int32_t nvec, int32_t vec_blocks, int32_t strips) {
+  // logical block = ((b * vec_blocks + channel block) * strips + strip), numbered XCD-aware so
+  // that consecutive strips of one channel block run on one XCD: the three history tokens a
+  // strip reads again were just read by its neighbour and come from that XCD's L2
+  const int lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int strip = lb % strips;
+  const int vb = (lb / strips) % vec_blocks;
+  const int64_t b = lb / strips / vec_blocks;
+  const int vec = vb * 64 + int(threadIdx.x);
   if (vec >= nvec) return;   // no barriers below
   const int C = HP + 2 * GN;
   const int ch0 = 8 * vec;
-  const int64_t b = blockIdx.z;
-  const int64_t t0 = int64_t(blockIdx.y) * kFeTokens;
+  const int64_t t0 = int64_t(strip) * kFeTokens;
   const int64_t t1 = min(t0 + kFeTokens, seqlen);
   int8_t* dst;
   int64_t stride;
@@ -328,9 +334,11 @@ hipError_t launch_frontend(const uint16_t* xbc, const float* conv_w, const float
                            int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
   const int32_t HP = nheads * headdim, GN = ngroups * dstate;
   const int32_t nvec = (HP + 2 * GN) / 8;
-  const dim3 grid((nvec + 63) / 64, uint32_t((seqlen + kFeTokens - 1) / kFeTokens), batch);   // y <= 65536 (host-checked)
-  hipLaunchKernelGGL(frontend_kernel, grid, dim3(64), 0, stream, xbc, conv_w, conv_b, x_scale, B_scale, C_scale, x,
-                     B, C, seqlen, HP, GN, headdim, dstate, nvec);
+  const int32_t vec_blocks = (nvec + 63) / 64;
+  const int32_t strips = int32_t((seqlen + kFeTokens - 1) / kFeTokens);
+  const int32_t nblocks = batch * vec_blocks * strips;   // < 2^31 (host-checked)
+  hipLaunchKernelGGL(frontend_kernel, dim3(nblocks), dim3(64), 0, stream, xbc, conv_w, conv_b, x_scale, B_scale,
+                     C_scale, x, B, C, seqlen, HP, GN, headdim, dstate, nvec, vec_blocks, strips);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = int64_t(batch) * seqlen * nheads;
