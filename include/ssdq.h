@@ -268,6 +268,25 @@ ssdq_status ssdq_frontend(const void* xbc, const float* conv_w, const float* con
                           int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                           hipStream_t stream);
 
+/*
+ * ssdq_frontend for one decode token per sequence, with the convolution's history carried in a
+ * conv state: the same output, codes and dt as ssdq_frontend gives for the last token of a
+ * sequence whose three previous tokens are the state's rows (the cached convolution states of
+ * the Quamba2 rebuttal, Table R7).
+ *
+ *   conv_state : (batch, 3, channels) binary16, read and written: rows are the inputs of tokens
+ *                t-3, t-2, t-1 before the call and t-2, t-1, t after it (zeros at the start)
+ *   xbc        : (batch, channels) binary16, token t
+ *   x (batch, nheads, headdim), B and C (batch, ngroups, dstate) int8; dt_raw, dt (batch, nheads)
+ * Every other argument, its layout and the validation are those of ssdq_frontend (d_conv 4;
+ * headdim and dstate multiples of 8); all pointers are device memory owned by the caller.
+ */
+ssdq_status ssdq_frontend_step(void* conv_state, const void* xbc, const float* conv_w, const float* conv_b,
+                               int32_t d_conv, const float* x_scale, const float* B_scale, const float* C_scale,
+                               const float* dt_raw, const float* dt_bias, int8_t* x, int8_t* B, int8_t* C, float* dt,
+                               int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

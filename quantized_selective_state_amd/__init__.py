@@ -59,6 +59,8 @@ lib.ssdq_state_update_f16.argtypes = [_P] * 11 + [_i32, _i32, _i32, _i32, _i32, 
 lib.ssdq_state_update_f16.restype = ctypes.c_int
 lib.ssdq_frontend.argtypes = [_P, _P, _P, _i32] + [_P] * 9 + [_i32, ctypes.c_int64, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_frontend.restype = ctypes.c_int
+lib.ssdq_frontend_step.argtypes = [_P, _P, _P, _P, _i32] + [_P] * 9 + [_i32] * 5 + [_P]
+lib.ssdq_frontend_step.restype = ctypes.c_int
 lib.ssdq_state_update_i8.argtypes = [_P] * 12 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_i8.restype = ctypes.c_int
 lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
@@ -297,6 +299,39 @@ def frontend(xbc, conv_w, conv_b, x_scale, B_scale, C_scale, dt_raw, dt_bias, nh
     _check(lib.ssdq_frontend(_ptr(xbc), _ptr(conv_w), _ptr(conv_b), 4, _ptr(x_scale), _ptr(B_scale),
                              _ptr(C_scale), _ptr(dt_raw), _ptr(dt_bias), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), b, L,
                              H, P, N, G, _stream(dev)), "ssdq_frontend")
+    return x, B, C, dt
+
+
+def frontend_step(conv_state, xbc, conv_w, conv_b, x_scale, B_scale, C_scale, dt_raw, dt_bias, nheads: int,
+                  headdim: int, ngroups: int, dstate: int, out=None):
+    """One decode token of the front end (ssdq_frontend_step): conv_state (b,3,channels) fp16 is
+    shifted in place; xbc (b,channels) fp16 -> codes x (b,H,P), B, C (b,G,N) and dt (b,H).
+    Returns (x, B, C, dt); `out` may give those four tensors."""
+    b, ch = xbc.shape
+    H, P, G, N = nheads, headdim, ngroups, dstate
+    dev = xbc.device
+    _need(xbc, "xbc", torch.float16, (b, H * P + 2 * G * N), dev)
+    _need(conv_state, "conv_state", torch.float16, (b, 3, ch), dev)
+    _need(conv_w, "conv_w", torch.float32, (ch, 4), dev)
+    _need(conv_b, "conv_b", torch.float32, (ch,), dev, optional=True)
+    _need(x_scale, "x_scale", torch.float32, (H,), dev)
+    _need(B_scale, "B_scale", torch.float32, (G,), dev)
+    _need(C_scale, "C_scale", torch.float32, (G,), dev)
+    _need(dt_raw, "dt_raw", torch.float32, (b, H), dev)
+    _need(dt_bias, "dt_bias", torch.float32, (H,), dev, optional=True)
+    if out is None:
+        out = (torch.empty((b, H, P), dtype=torch.int8, device=dev),
+               torch.empty((b, G, N), dtype=torch.int8, device=dev),
+               torch.empty((b, G, N), dtype=torch.int8, device=dev),
+               torch.empty((b, H), dtype=torch.float32, device=dev))
+    x, B, C, dt = out
+    _need(x, "x", torch.int8, (b, H, P), dev)
+    _need(B, "B", torch.int8, (b, G, N), dev)
+    _need(C, "C", torch.int8, (b, G, N), dev)
+    _need(dt, "dt", torch.float32, (b, H), dev)
+    _check(lib.ssdq_frontend_step(_ptr(conv_state), _ptr(xbc), _ptr(conv_w), _ptr(conv_b), 4, _ptr(x_scale),
+                                  _ptr(B_scale), _ptr(C_scale), _ptr(dt_raw), _ptr(dt_bias), _ptr(x), _ptr(B),
+                                  _ptr(C), _ptr(dt), b, H, P, N, G, _stream(dev)), "ssdq_frontend_step")
     return x, B, C, dt
 
 

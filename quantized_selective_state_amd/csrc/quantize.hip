@@ -255,6 +255,62 @@ __global__ void __launch_bounds__(64) frontend_kernel(
   }
 }
 
+// The front end for one decode token: the convolution's history is the caller's conv state,
+// (batch, 3, channels) binary16 holding the inputs of tokens t-3, t-2, t-1; the step forms
+// token t's output exactly as frontend_kernel does (same arithmetic, same order) and shifts
+// the state in place to t-2, t-1, t.  A lane owns 8 channels of one sequence.
+__global__ void __launch_bounds__(256) frontend_step_kernel(
+    uint16_t* __restrict__ conv_state, const uint16_t* __restrict__ xbc, const float* __restrict__ w,
+    const float* __restrict__ bias, const float* __restrict__ x_scale, const float* __restrict__ B_scale,
+    const float* __restrict__ C_scale, int8_t* __restrict__ qx, int8_t* __restrict__ qB, int8_t* __restrict__ qC,
+    int32_t HP, int32_t GN, int32_t P, int32_t N, int32_t nvec, int32_t batch) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= int64_t(nvec) * batch) return;
+  const int vec = int(i % nvec);
+  const int64_t b = i / nvec;
+  const int C = HP + 2 * GN;
+  const int ch0 = 8 * vec;
+  int8_t* dst;
+  float s;
+  if (ch0 < HP) {
+    dst = qx + b * HP + ch0;
+    s = x_scale[ch0 / P];
+  } else if (ch0 < HP + GN) {
+    dst = qB + b * GN + (ch0 - HP);
+    s = B_scale[(ch0 - HP) / N];
+  } else {
+    dst = qC + b * GN + (ch0 - HP - GN);
+    s = C_scale[(ch0 - HP - GN) / N];
+  }
+  uint16_t* st = conv_state + b * 3 * C + ch0;
+  const v4u r3 = *reinterpret_cast<const v4u*>(st);           // t - 3
+  const v4u r2 = *reinterpret_cast<const v4u*>(st + C);       // t - 2
+  const v4u r1 = *reinterpret_cast<const v4u*>(st + 2 * C);   // t - 1
+  const v4u r0 = *reinterpret_cast<const v4u*>(xbc + b * C + ch0);
+  float h3[8], h2[8], h1[8], cur[8], a[8];
+  unpack8(r3, h3);
+  unpack8(r2, h2);
+  unpack8(r1, h1);
+  unpack8(r0, cur);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const v4f t = *reinterpret_cast<const v4f*>(w + int64_t(ch0) * 4 + 4 * q);
+    const float bq = bias ? bias[ch0 + q] : 0.f;
+    float v = fmaf(t[0], h3[q], bq);
+    v = fmaf(t[1], h2[q], v);
+    v = fmaf(t[2], h1[q], v);
+    v = fmaf(t[3], cur[q], v);
+    const float silu = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+    a[q] = float(_Float16(silu));
+  }
+  uint32_t c[8];
+  codes<8>(a, s, c);
+  *reinterpret_cast<v2u*>(dst) = v2u{pack4(c), pack4(c + 4)};
+  *reinterpret_cast<v4u*>(st) = r2;
+  *reinterpret_cast<v4u*>(st + C) = r1;
+  *reinterpret_cast<v4u*>(st + 2 * C) = r0;
+}
+
 // dt = softplus(dt_raw + dt_bias[h]) = max(v, 0) + log1p(exp(-|v|)), one element per thread
 __global__ void __launch_bounds__(256) softplus_dt_kernel(const float* __restrict__ raw,
                                                           const float* __restrict__ dt_bias,
@@ -342,6 +398,24 @@ hipError_t launch_frontend(const uint16_t* xbc, const float* conv_w, const float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n = int64_t(batch) * seqlen * nheads;
+  hipLaunchKernelGGL(softplus_dt_kernel, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, stream, dt_raw, dt_bias, dt,
+                     n, nheads);
+  return hipGetLastError();
+}
+
+hipError_t launch_frontend_step(uint16_t* conv_state, const uint16_t* xbc, const float* conv_w, const float* conv_b,
+                                const float* x_scale, const float* B_scale, const float* C_scale,
+                                const float* dt_raw, const float* dt_bias, int8_t* x, int8_t* B, int8_t* C,
+                                float* dt, int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate,
+                                int32_t ngroups, hipStream_t stream) {
+  const int32_t HP = nheads * headdim, GN = ngroups * dstate;
+  const int32_t nvec = (HP + 2 * GN) / 8;
+  const int64_t lanes = int64_t(nvec) * batch;
+  hipLaunchKernelGGL(frontend_step_kernel, dim3(uint32_t((lanes + 255) / 256)), dim3(256), 0, stream, conv_state, xbc,
+                     conv_w, conv_b, x_scale, B_scale, C_scale, x, B, C, HP, GN, headdim, dstate, nvec, batch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = int64_t(batch) * nheads;
   hipLaunchKernelGGL(softplus_dt_kernel, dim3(uint32_t((n + 255) / 256)), dim3(256), 0, stream, dt_raw, dt_bias, dt,
                      n, nheads);
   return hipGetLastError();

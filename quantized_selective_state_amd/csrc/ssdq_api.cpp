@@ -265,4 +265,25 @@ ssdq_status ssdq_frontend(const void* xbc, const float* conv_w, const float* con
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
+ssdq_status ssdq_frontend_step(void* conv_state, const void* xbc, const float* conv_w, const float* conv_b,
+                               int32_t d_conv, const float* x_scale, const float* B_scale, const float* C_scale,
+                               const float* dt_raw, const float* dt_bias, int8_t* x, int8_t* B, int8_t* C, float* dt,
+                               int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                               hipStream_t stream) {
+  if (!ok_ptr(conv_state) || !ok_ptr(xbc) || !ok_ptr(conv_w) || !ok_opt(conv_b) || !ok_ptr(x_scale) ||
+      !ok_ptr(B_scale) || !ok_ptr(C_scale) || !ok_ptr(dt_raw) || !ok_opt(dt_bias) || !ok_ptr(x) || !ok_ptr(B) ||
+      !ok_ptr(C) || !ok_ptr(dt))
+    return SSDQ_ERROR_INVALID_VALUE;
+  if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 || nheads % ngroups != 0)
+    return SSDQ_ERROR_INVALID_VALUE;
+  if (d_conv != 4 || headdim % 8 != 0 || dstate % 8 != 0) return SSDQ_ERROR_UNSUPPORTED;
+  const int64_t channels = int64_t(nheads) * headdim + 2 * int64_t(ngroups) * dstate;
+  if (channels >= (int64_t(1) << 31) || int64_t(batch) * channels * 3 >= (int64_t(1) << 40))
+    return SSDQ_ERROR_UNSUPPORTED;
+  const hipError_t e = launch_frontend_step(static_cast<uint16_t*>(conv_state), static_cast<const uint16_t*>(xbc),
+                                            conv_w, conv_b, x_scale, B_scale, C_scale, dt_raw, dt_bias, x, B, C, dt,
+                                            batch, nheads, headdim, dstate, ngroups, stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
 }  // extern "C"

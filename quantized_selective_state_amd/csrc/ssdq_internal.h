@@ -83,6 +83,11 @@ hipError_t launch_frontend(const uint16_t* xbc, const float* conv_w, const float
                            const float* B_scale, const float* C_scale, const float* dt_raw, const float* dt_bias,
                            int8_t* x, int8_t* B, int8_t* C, float* dt, int32_t batch, int64_t seqlen,
                            int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+hipError_t launch_frontend_step(uint16_t* conv_state, const uint16_t* xbc, const float* conv_w, const float* conv_b,
+                                const float* x_scale, const float* B_scale, const float* C_scale,
+                                const float* dt_raw, const float* dt_bias, int8_t* x, int8_t* B, int8_t* C,
+                                float* dt, int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate,
+                                int32_t ngroups, hipStream_t stream);
 hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
                                   const float* dt, const float* A, const float* D, _Float16* y, int32_t batch,

@@ -34,6 +34,7 @@ def lib():
     lib.ssdq_state_update.argtypes = [P] * 11 + [i32] * 5 + [P]
     lib.ssdq_state_update_f16.argtypes = [P] * 11 + [i32] * 5 + [P]
     lib.ssdq_state_update_i8.argtypes = [P] * 12 + [i32] * 5 + [P]
+    lib.ssdq_frontend_step.argtypes = [P, P, P, P, i32] + [P] * 9 + [i32] * 5 + [P]
     lib.ssdq_frontend.argtypes = [P, P, P, i32] + [P] * 9 + [i32, i64, i32, i32, i32, i32, P]
     lib.ssdq_status_string.argtypes = [ctypes.c_int]
     lib.ssdq_status_string.restype = ctypes.c_char_p
@@ -213,3 +214,23 @@ def _fe(lib, **kw):
 ])
 def test_frontend_validation(lib, kw, status):
     assert _fe(lib, **kw) == status
+
+
+def _fes(lib, **kw):
+    a = dict(st=A16, xbc=A16, w=A16, bias=None, dconv=4, xs=A16, Bs=A16, Cs=A16, raw=A16, dtb=None, x=A16, B=A16,
+             C=A16, dt=A16, b=2, H=8, P=64, N=128, G=2)
+    a.update(kw)
+    return lib.ssdq_frontend_step(*[a[k] for k in ("st", "xbc", "w", "bias", "dconv", "xs", "Bs", "Cs", "raw", "dtb",
+                                                   "x", "B", "C", "dt", "b", "H", "P", "N", "G")], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(st=None), INVALID),
+    (dict(st=A16 + 2), INVALID),
+    (dict(b=0), INVALID),
+    (dict(H=8, G=3), INVALID),
+    (dict(dconv=2), UNSUPPORTED),
+    (dict(P=12), UNSUPPORTED),
+])
+def test_frontend_step_validation(lib, kw, status):
+    assert _fes(lib, **kw) == status

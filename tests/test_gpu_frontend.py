@@ -29,10 +29,10 @@ def _gpu(fe):
     return x.cpu().numpy(), B.cpu().numpy(), C.cpu().numpy(), dt.cpu().numpy()
 
 
-def _check(fe, tag):
+def _check(fe, tag, got=None):
     H, P, G, N = fe["nheads"], fe["headdim"], fe["ngroups"], fe["dstate"]
     b, L = fe["batch"], fe["seqlen"]
-    qx, qB, qC, dt = _gpu(fe)
+    qx, qB, qC, dt = _gpu(fe) if got is None else got
     ref = oracle.frontend(fe["xbc16"], fe["conv_w"], fe["conv_b"], fe["x_scale"], fe["B_scale"], fe["C_scale"],
                           H, P, G, N)
     act, a16 = ref["act"], ref["act16"]
@@ -87,3 +87,29 @@ def test_empty_sequence_is_a_noop():
     ssdq.frontend(to_dev(fe["xbc16"][:, :0]), to_dev(fe["conv_w"]), None, to_dev(fe["x_scale"]),
                   to_dev(fe["B_scale"]), to_dev(fe["C_scale"]), to_dev(fe["dt_raw"][:, :0]), None, H, P, G, N, out=out)
     torch.cuda.synchronize()
+
+
+def test_decode_steps_equal_the_prefill_front_end():
+    """Token-by-token steps from a zero conv state give every token the codes and dt of the
+    prefill front end over the whole sequence (checked against the oracle, and bit for bit
+    against the GPU's own prefill pass, which does the same arithmetic), and leave the last
+    three tokens' inputs in the state."""
+    import quantized_selective_state_amd as ssdq
+    shape = workloads.PrefillShape("fe_steps", 3, 12, 4, 32, 64, 2, 64, "normal", "fixed_bias", 0.0)
+    fe = workloads.make_frontend(shape, seed_index=33)
+    H, P, G, N = fe["nheads"], fe["headdim"], fe["ngroups"], fe["dstate"]
+    b, L = fe["batch"], fe["seqlen"]
+    xbc = to_dev(fe["xbc16"])
+    w, cb = to_dev(fe["conv_w"]), to_dev(fe["conv_b"])
+    sx, sB, sC = to_dev(fe["x_scale"]), to_dev(fe["B_scale"]), to_dev(fe["C_scale"])
+    raw, dtb = to_dev(fe["dt_raw"]), to_dev(fe["dt_bias"])
+    state = torch.zeros((b, 3, xbc.shape[2]), dtype=torch.float16, device=dev())
+    steps = [ssdq.frontend_step(state, xbc[:, t].contiguous(), w, cb, sx, sB, sC, raw[:, t].contiguous(), dtb,
+                                H, P, G, N) for t in range(L)]
+    torch.cuda.synchronize()
+    got = tuple(torch.stack([st[k] for st in steps], dim=1).cpu().numpy() for k in range(4))
+    _check(fe, "decode steps", got=got)
+    pre = _gpu(fe)
+    for k in range(4):
+        assert np.array_equal(got[k], pre[k])
+    assert np.array_equal(state.cpu().numpy(), fe["xbc16"][:, L - 3:])
