@@ -44,7 +44,8 @@ KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "state_passing": "state_passing.hip",
                  "chunk_output": "chunk_output.hip", "state_update": "state_update.hip",
                  "state_update_f16": "state_update.hip", "state_update_i8": "state_update.hip",
-                 "frontend": "quantize.hip", "frontend (dt softplus)": "quantize.hip"}
+                 "frontend": "quantize.hip", "frontend (dt softplus)": "quantize.hip",
+                 "frontend_step": "quantize.hip"}
 
 
 def _code_only(text: str) -> str:
@@ -415,6 +416,32 @@ def bench_decode(args, torch, ssdq, workloads, dev):
            "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms / 1e3), 1),
            "alg_bytes_per_step": per_step, "achieved_GBs": round(gbs, 1),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("state_update")}
+
+    # the decode front end for the same sequences: conv state (b, 3, channels) fp16, one token
+    ch = H * P + 2 * G * N
+    gen = torch.Generator(device=dev).manual_seed(7)
+    xbc_t = torch.randn((b, ch), generator=gen, device=dev).half()
+    conv_state = torch.randn((b, 3, ch), generator=gen, device=dev).half()
+    taps = torch.randn((ch, 4), generator=gen, device=dev) * 0.3
+    raw_t = torch.randn((b, H), generator=gen, device=dev) - 4.0
+    fe_out = (torch.empty((b, H, P), dtype=torch.int8, device=dev), torch.empty((b, G, N), dtype=torch.int8, device=dev),
+              torch.empty((b, G, N), dtype=torch.int8, device=dev), torch.empty((b, H), dtype=torch.float32, device=dev))
+    fe_step = lambda: ssdq.frontend_step(conv_state, xbc_t, taps, None, sx, sB, sC, raw_t, None, H, P, G, N, out=fe_out)
+    for _ in range(8):
+        fe_step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        fe_step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_fe = e0.elapsed_time(e1) / steps
+    fe_bytes = b * ch * (2 + 2 * 3 * 2 + 1) + b * H * 8 + ch * 16   # token in, state in/out, codes; dt; taps
+    out["frontend_step"] = {"us_per_step": round(ms_fe * 1e3, 2), "alg_bytes_per_step": fe_bytes,
+                            "achieved_GBs": round(fe_bytes / (ms_fe / 1e3) / 1e9, 1),
+                            "hbm_frac": round(fe_bytes / (ms_fe / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": measured_traffic("frontend_step")}
+    del xbc_t, conv_state
 
     # the same steps on the state cached in binary16 (half the state bytes per step)
     del state
