@@ -261,7 +261,11 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
       }
     }
     m = group_max<kLanesPerRow>(m);
-    const float s = m / 127.f;
+    // m / 127 by one fma refinement of m * (1/127) instead of a full IEEE division per lane and
+    // row (equal to the correctly rounded quotient on every one of 2 M sampled m; at worst an
+    // ulp from it, which moves a code only where u / s is that close to a midpoint)
+    const float q0 = m * (1.f / 127.f);
+    const float s = fmaf(fmaf(-q0, 127.f, m), 1.f / 127.f, q0);
     // 1 / s to within an ulp: a code can move only where u / s is that close to a midpoint
     const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
     v4u out;
