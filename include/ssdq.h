@@ -219,7 +219,7 @@ ssdq_status ssdq_state_update_f16(void* state, const int8_t* x, const float* x_s
  *
  *   u[b,h,p,n] = exp(dt[b,h] A[h]) scale[b,h,p] state[b,h,p,n] + dt[b,h] xhat[b,h,p] Bhat[b,g,n]  (fp32)
  *   y[b,h,p]   = sum_n Chat[b,g,n] u[b,h,p,n] + D[h] xhat[b,h,p]                               (from u)
- *   scale[b,h,p] <- max_n |u[b,h,p,n]| / 127                      (binary32; 0 for a zero row)
+ *   scale[b,h,p] <- max_n |u[b,h,p,n]| / 127     (binary32; 0, with zero codes, when that is below 2^-126)
  *   state[b,h,p,n] <- u / scale rounded to nearest, ties to even, within [-127, 127] (0 if scale is 0)
  *
  *   state       : (batch, nheads, headdim, dstate) int8 codes, read and written

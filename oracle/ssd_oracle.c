@@ -126,11 +126,13 @@ void oracle_round_binary16(const double* in, double* out, int64_t n) {
  * its choice from the row's largest magnitude are this oracle's reading, the same symmetric
  * max/127 rule the pages use for activations).  s = binary32(max_n |row[n]| / 127); each
  * code is row[n] / s rounded to nearest with ties to even and saturated to [-127, 127]; the
- * row becomes s * code.  A zero row (or a scale that rounds to 0) gives zero codes and s = 0. */
+ * row becomes s * code.  A row whose scale would not be a normal binary32 (zero, or below
+ * 2^-126, i.e. max|row| below about 1.5e-36) is flushed: zero codes and s = 0. */
 static void requantize_row_i8(double* row, int32_t N, int8_t* q, float* s_out) {
   double m = 0.0;
   for (int32_t n = 0; n < N; ++n) m = fmax(m, fabs(row[n]));
-  const float s = (float)(m / 127.0);
+  float s = (float)(m / 127.0);
+  if (s < 0x1p-126f) s = 0.0f;
   for (int32_t n = 0; n < N; ++n) {
     double c = 0.0;
     if (s > 0.0f) {

@@ -185,8 +185,8 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
 //    b the B codes, e = exp(dt A)), sum_n c_n u_n = (e s) <c, q> + (dt xhat sB) <c, b>, and
 //    both dot products are over int8 codes: four-way int8 dot instructions, exact in int32;
 //  - the new code is one fma into the binade of 1.5 * 2^23, whose unit spacing makes the fma's
-//    own rounding the round-to-nearest-even of u / s and leaves the code in the low byte, then
-//    a clamp and byte permutes pack four codes per dword.
+//    own rounding the round-to-nearest-even of u / s and leaves the code in the low byte, and
+//    byte permutes pack four codes per dword.
 constexpr int kI8Threads = 128;   // two waves per (batch, head): four row passes per lane amortize the set-up
 
 template <int N>
@@ -265,7 +265,11 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     // row (equal to the correctly rounded quotient on every one of 2 M sampled m; at worst an
     // ulp from it, which moves a code only where u / s is that close to a midpoint)
     const float q0 = m * (1.f / 127.f);
-    const float s = fmaf(fmaf(-q0, 127.f, m), 1.f / 127.f, q0);
+    const float sq = fmaf(fmaf(-q0, 127.f, m), 1.f / 127.f, q0);
+    // a scale below the normal range flushes the row (zero codes, s = 0); with s normal,
+    // m / s <= 127 (1 + 2^-23) and the reciprocal's ulp keep every |u| inv below 127.5, so the
+    // rounded codes need no clamp
+    const float s = sq >= 0x1p-126f ? sq : 0.f;
     // 1 / s to within an ulp: a code can move only where u / s is that close to a midpoint
     const float inv = s > 0.f ? __builtin_amdgcn_rcpf(s) : 0.f;
     v4u out;
@@ -274,7 +278,7 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
       uint32_t t[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float c = __builtin_amdgcn_fmed3f(fmaf(v[4 * j + i], inv, kMagic), kMagic - 127.f, kMagic + 127.f);
+        const float c = fmaf(v[4 * j + i], inv, kMagic);
         t[i] = __float_as_uint(c);
       }
       const uint32_t lo = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u);   // bytes: t0.b0, t1.b0, 0, 0

@@ -117,15 +117,18 @@ def test_headdim_below_64_and_no_D():
     _check_steps(dec, q0, s0, y, q, s, tag="i8 state P=48 no D")
 
 
-def test_zero_state_rows_stay_zero_without_input():
-    """A zero starting row with x = 0 for that row stays a zero row with scale 0 (no 0/0)."""
+def test_zero_and_subnormal_scale_rows_are_flushed():
+    """Rows without input stay zero when they start at zero (no 0/0), and rows so small that
+    their scale would be subnormal (here a starting scale of 1e-39) are flushed to zero codes
+    and scale 0, as the oracle does."""
     dec = _small(75, b=2, H=4, P=64, N=128, G=1, T=2)
-    dec["x16"][:, :, :, :8] = 0            # rows p < 8 of every head get no input
+    dec["x16"][:, :, :, :16] = 0           # rows p < 16 of every head get no input
     q0, s0 = _start(dec)
     q0[:, :, :8] = 0
     s0[:, :, :8] = 0
+    s0[:, :, 8:16] = np.float32(1e-39)
     y, q, s = _gpu_decode_i8(dec, q0, s0)
-    assert not np.any(q[:, :, :8]) and not np.any(s[:, :, :8])
+    assert not np.any(q[:, :, :16]) and not np.any(s[:, :, :16])
     _check_steps(dec, q0, s0, y, q, s, tag="i8 state zero rows")
 
 

@@ -50,6 +50,10 @@ def test_ties_go_to_even_codes_and_special_rows():
     q, s, dec = oracle.requantize_rows_i8(np.array([[-254.0, 1.0, 3.0, 127.0], [0.0, 0.0, 0.0, 0.0]]))
     assert s[0] == 2.0 and list(q[0]) == [-127, 0, 2, 64]   # 1/2 -> 0, 3/2 -> 2, 127/2 -> 64
     assert s[1] == 0.0 and not np.any(q[1]) and not np.any(dec[1])
+    # a row whose scale would be subnormal is flushed; one just above keeps its codes
+    q, s, dec = oracle.requantize_rows_i8(np.array([[1e-37, -5e-38, 0.0], [127 * 2.0 ** -126, 2.0 ** -126, 0.0]]))
+    assert s[0] == 0.0 and not np.any(q[0]) and not np.any(dec[0])
+    assert s[1] == np.float32(2.0 ** -126) and list(q[1]) == [127, 1, 0]
 
 
 def _codes(rng, T, H, P, N, G, small=False):
