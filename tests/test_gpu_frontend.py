@@ -113,3 +113,33 @@ def test_decode_steps_equal_the_prefill_front_end():
     for k in range(4):
         assert np.array_equal(got[k], pre[k])
     assert np.array_equal(state.cpu().numpy(), fe["xbc16"][:, L - 3:])
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_front_end_then_scan_matches_the_oracle(name):
+    """The prefill step with the front end in place of the quantizer: the front end's codes and
+    dt go straight into the chunked scan; y and the final state against the oracle's front end
+    followed by the fp64 sequential recurrence."""
+    import quantized_selective_state_amd as ssdq
+    from gpu_util import Y_TOL
+    if name == "tiny":
+        fe = workloads.make_frontend("tiny")
+    else:
+        shape = workloads.PrefillShape("fe_scan", 2, 77, 6, 32, 64, 2, 64, "normal", "fixed_bias", 0.0)
+        fe = workloads.make_frontend(shape, seed_index=34)
+    H, P, G, N = fe["nheads"], fe["headdim"], fe["ngroups"], fe["dstate"]
+    sx, sB, sC = to_dev(fe["x_scale"]), to_dev(fe["B_scale"]), to_dev(fe["C_scale"])
+    qx, qB, qC, dt = ssdq.frontend(to_dev(fe["xbc16"]), to_dev(fe["conv_w"]), to_dev(fe["conv_b"]), sx, sB, sC,
+                                   to_dev(fe["dt_raw"]), to_dev(fe["dt_bias"]), H, P, G, N)
+    y, hf = ssdq.chunk_scan(qx, sx, qB, sB, qC, sC, dt, to_dev(fe["A"]), to_dev(fe["D"]), None, chunk=fe["chunk"])
+    torch.cuda.synchronize()
+    ref = oracle.frontend(fe["xbc16"], fe["conv_w"], fe["conv_b"], fe["x_scale"], fe["B_scale"], fe["C_scale"],
+                          H, P, G, N)
+    dt_ref = oracle.softplus_dt(fe["dt_raw"], fe["dt_bias"]).astype(np.float32)
+    codes = oracle.Codes(ref["qx"], fe["x_scale"], ref["qB"], fe["B_scale"], ref["qC"], fe["C_scale"], dt_ref,
+                         fe["A"], fe["D"])
+    y_ref, h_ref, _ = oracle.ssd(codes)
+    ey = np.max(np.abs(y.float().cpu().numpy() - y_ref)) / np.max(np.abs(y_ref))
+    eh = np.max(np.abs(hf.cpu().numpy() - h_ref)) / np.max(np.abs(h_ref))
+    note(f"front end + scan ({name}): y {ey:.2e}, h {eh:.2e}")
+    assert ey <= Y_TOL and eh <= 1e-4
