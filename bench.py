@@ -1,18 +1,21 @@
 """Benchmark of the INT8-input Mamba-2 SSD scan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME ...]
 
-A step is one pass of the prefill hot path over the Mamba-2 1.3B-shaped layer
-(batch 4, L 2048, 64 heads x 64, d_state 128, 1 group, chunk 256): static INT8
-quantize of x, B and C (one batched launch), then the chunked scan (chunk cumsum, chunk state, state
-passing, chunk output; with a (batch, head) sequence per CU the first kernel also
-carries the state across chunks).  Inputs are seeded synthetic fp16 activations
-resident in HBM before timing starts.  Per-kernel times come from a pass with
-events around every kernel; the timed steps carry events only around the
-dominant kernel and the region.  The decode update is measured in the same run on
-the 8B-shaped decode workload (batch 256, 128 heads, 8 groups, 128 steps, 1 GiB
-fp32 state), one launch per step.  The CPU oracle is timed on the host cores on
-the same prefill workload.  Prints one JSON line.
+A step is one pass of the prefill hot path: static INT8 quantize of x, B and C (one batched
+launch), then the chunked scan (chunk cumsum, chunk state, state passing, chunk output; with a
+(batch, head) sequence per CU the first kernel also carries the state across chunks).  The
+headline line is the Mamba-2 8B-shaped layer (batch 8, L 4096, 128 heads x 64, d_state 128,
+8 groups, chunk 256: 32,768 tokens per step), the largest prefill configuration; the 1.3B-shaped
+layer (batch 4, L 2048, 64 heads, 1 group) and the 2.7B-shaped long sequence (batch 1,
+L 16384, 80 heads, nonzero initial state) are measured in the same run under `workloads`.
+Inputs are seeded synthetic fp16 activations resident in HBM before timing starts.
+Per-kernel times come from a pass with events around every kernel; the timed steps carry
+events only around the dominant kernel and the region.  The front end (conv1d + SiLU +
+quantize) is measured on the headline shape; the decode update on the 8B-shaped decode
+workload (batch 256, 128 heads, 8 groups, 128 steps, 1 GiB fp32 state), one launch per step,
+and on the binary16 and 8-bit cached states.  The CPU oracle is timed on the host cores on the
+headline workload (and on one thread on a sample of the 1.3B-shaped one).  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -36,9 +39,16 @@ METRIC = "SSD scan tokens/s + % INT8 MFMA peak (prefill); decode HBM GB/s"
 
 
 # HBM bytes per launch measured with rocprofv3 (FETCH_SIZE and WRITE_SIZE, each scaled by what
-# the same counter reads for a plain 1 GiB device copy), one row per kernel, keyed by a digest of
-# the kernel's source so that a reading taken on an older version of a kernel is not reported.
-TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_mamba2-1.3b-prefill_mamba2-8b-decode.md")
+# the same counter reads for a plain 1 GiB device copy), one table per workload and one row per
+# kernel, keyed by a digest of the kernel's source so that a reading taken on an older version of
+# a kernel is not reported.
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+
+
+def traffic_table(workload: str) -> str:
+    return os.path.join(TRAFFIC_DIR, f"hbm_traffic_{workload}.md")
+
+
 KERNEL_SOURCE = {"quantize": "quantize.hip",
                  "chunk_state": "chunk_state.hip", "state_scan": "chunk_state.hip",
                  "state_passing": "state_passing.hip",
@@ -68,11 +78,11 @@ def _sum_or_none(*vals):
     return None if any(v is None for v in vals) else sum(vals)
 
 
-def measured_traffic(kernel: str):
-    """Counter-measured HBM bytes per launch of `kernel`, or None if the table has no row for
-    the kernel's current source."""
+def measured_traffic(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch of `kernel` on `workload`, or None if the workload's
+    table has no row for the kernel's current source."""
     try:
-        with open(TRAFFIC_TABLE) as f:
+        with open(traffic_table(workload)) as f:
             lines = f.read().splitlines()
     except OSError:
         return None
@@ -134,23 +144,29 @@ class HipEvent:
             self._hip.hipEventDestroy(self.h)
 
 
-def parse():
+PREFILL_WORKLOADS = ["mamba2-1.3b-prefill", "mamba2-2.7b-long-prefill", "mamba2-8b-prefill"]
+HEADLINE = "mamba2-8b-prefill"     # the largest prefill configuration that fits one GPU
+
+
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--workload", choices=PREFILL_WORKLOADS, action="append",
+                    help="prefill workload(s) to run (default: all three, the 8B-shaped one as the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling HBM counter readings)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kernel_bytes(b, L, H, P, N, G, Q):
-    """Algorithmic HBM bytes per launch of each prefill kernel: every input read once,
-    every output written once."""
+    """Compulsory HBM bytes per launch of each prefill kernel as built: every input read once,
+    every output written once (the carried state as two int8 limbs plus a row scale)."""
     nc = -(-L // Q)
     tok = b * L
     x = tok * H * P
@@ -170,6 +186,18 @@ def kernel_bytes(b, L, H, P, N, G, Q):
     }
 
 
+def survey_bytes_per_token(H, P, N, G, Q):
+    """Per-token compulsory traffic of the four steps of the chunked scan as the scan is specified
+    (int8 x, B, C in; fp32 dt, Acs and chunk states; fp16 y out): the unit figures the roofline
+    of each step is quoted against.  chunk_scan (the output step) reads x, B, C, dt, Acs and the
+    fp32 state entering the chunk (H P N values per chunk of Q tokens) and writes y."""
+    return {
+        "quantize": 3 * H * P + 6 * G * N,
+        "chunk_state": H * P + G * N + 4 * H + 4 * H + 4 * H * P * N / Q,
+        "chunk_scan": H * P + 2 * G * N + 4 * H + 4 * H + 4 * H * P * N / Q + 2 * H * P,
+    }
+
+
 def scan_ops(b, L, H, P, N, G, Q):
     """Algorithmic contraction ops (2 per multiply-add) of the chunked scan: chunk
     states, causal C.B^T once per group, causal M.x and C.Hprev per head."""
@@ -185,31 +213,24 @@ def scan_ops(b, L, H, P, N, G, Q):
     return {"chunk_state": state, "chunk_output": cb + mx + ch, "cb_int8": cb}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
-              file=sys.stderr)
-        return 2
-
-    import torch
-    import quantized_selective_state_amd as ssdq
-    import workloads
-
-    dev = torch.device("cuda:0")
+def bench_prefill(name, steps, warmup, torch, ssdq, workloads, dev, keep_inputs=False):
+    """One workload's prefill step (batched quantize of x, B, C + the chunked scan), timed over
+    `steps` back-to-back steps after `warmup` untimed ones.  Returns the workload's record (and
+    the seeded inputs when keep_inputs)."""
     T = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-    name = "mamba2-1.3b-prefill"
-    shape = workloads.WORKLOADS[name]
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     inp = workloads.make_prefill(name)
     b, L, H, P, N, G, Q = (inp[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"))
     x16, B16, C16 = T(inp["x16"]), T(inp["B16"]), T(inp["C16"])
     sx, sB, sC = T(inp["x_scale"]), T(inp["B_scale"]), T(inp["C_scale"])
-    dt, A, D = T(inp["dt"]), T(inp["A"]), T(inp["D"])
+    dt, A, D, h0 = T(inp["dt"]), T(inp["A"]), T(inp["D"]), T(inp["h0"])
+    if not keep_inputs:
+        del inp
+        inp = None
     qx = torch.empty(x16.shape, dtype=torch.int8, device=dev)
     qB = torch.empty(B16.shape, dtype=torch.int8, device=dev)
     qC = torch.empty(C16.shape, dtype=torch.int8, device=dev)
-    buf = ssdq.ScanBuffers(qx, sx, qB, sB, qC, sC, dt, A, D, None, chunk=Q)
+    buf = ssdq.ScanBuffers(qx, sx, qB, sB, qC, sC, dt, A, D, h0, chunk=Q)
 
     # With at least one (batch, head) sequence per CU, stage 0 also carries the state across
     # chunks and stage 1 has nothing to launch; the step then runs stages 0 and 2 only.
@@ -235,15 +256,15 @@ def main():
 
     stream = torch.cuda.current_stream().cuda_stream   # the stream every kernel is launched on
     ev = lambda: HipEvent(stream)
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    print(f"[bench] {name}: warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # per-kernel breakdown: up to 200 steps with events around every kernel (an event between
     # two kernels can delay the second, so these steps are not the ones whose wall time gives
     # the throughput)
-    nprof = min(args.steps, 200)
+    nprof = max(1, min(steps, 200))
     prof = [{i: (ev(), ev()) for i in range(len(fns))} for _ in range(nprof)]
     for k in range(nprof):
         step(prof[k])
@@ -253,63 +274,115 @@ def main():
     dominant = max(names, key=lambda n: per_kernel_ms[n])
     di = names.index(dominant)
 
-    # timed region: exactly K steps; events only around the dominant kernel (its live launch
-    # duration for the roofline) and around the whole region, all on the launch stream
+    # timed region: exactly `steps` steps; events only around the dominant kernel (its live
+    # launch duration for the roofline) and around the whole region, all on the launch stream
     # (torch's current stream)
-    marks = [{di: (ev(), ev())} for _ in range(args.steps)]
+    print(f"[bench] {name}: {steps} timed steps", file=sys.stderr, flush=True)
+    marks = [{di: (ev(), ev())} for _ in range(steps)]
     e_start, e_end = ev(), ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start.record()
-    for k in range(args.steps):
+    for k in range(steps):
         step(marks[k])
     e_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dom_ms = sum(m[di][0].elapsed_time(m[di][1]) for m in marks) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    dom_ms = sum(m[di][0].elapsed_time(m[di][1]) for m in marks) / steps
+    ms_per_step = wall * 1e3 / steps
     tokens = b * L
-    value = tokens / (ms_per_step / 1e3)
     scan_ms = sum(per_kernel_ms[n] for n in scan_names)
 
     kb = kernel_bytes(b, L, H, P, N, G, Q)
+    unit = survey_bytes_per_token(H, P, N, G, Q)
+    # the roofline of the dominant kernel, priced by the specified per-token traffic of its step
+    # (the output kernel is the chunk_scan step; the others are priced by their own bytes)
+    spec_name = {"chunk_output": "chunk_scan", "quantize": "quantize", "chunk_state": "chunk_state"}.get(dominant)
+    alg = unit[spec_name] * tokens if spec_name else kb[dominant]
+    ach = alg / (dom_ms / 1e3) / 1e9
+    own = kb[dominant] / (dom_ms / 1e3) / 1e9
     ops = scan_ops(b, L, H, P, N, G, Q)
-    ach = kb[dominant] / (dom_ms / 1e3) / 1e9
     kernels = {n: {"us": round(per_kernel_ms[n] * 1e3, 2),
                    "alg_bytes": kb[n],
                    "alg_GBs": round(kb[n] / (per_kernel_ms[n] / 1e3) / 1e9, 1),
-                   "hbm_frac": round(kb[n] / (per_kernel_ms[n] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)} for n in names}
+                   "hbm_frac": round(kb[n] / (per_kernel_ms[n] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic(n, name)} for n in names}
     total_ops = ops["chunk_state"] + ops["chunk_output"]   # the state contraction is the same in both plans
+    rec = {
+        "workload": name, "batch": b, "seqlen": L, "nheads": H, "headdim": P, "dstate": N, "ngroups": G,
+        "chunk": Q, "tokens": tokens, "h0": h0 is not None,
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "tokens_per_s": round(tokens / (ms_per_step / 1e3), 1),
+        "event_ms_per_step": round(e_start.elapsed_time(e_end) / steps, 5),
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dominant, name), "kernel_us": round(dom_ms * 1e3, 2),
+                     "bytes_per_token": unit[spec_name] if spec_name else kb[dominant] / tokens,
+                     "units_per_launch": tokens,
+                     "kernel_alg_bytes": kb[dominant], "kernel_alg_frac": round(own / HBM_PEAK_GBS, 4)},
+        "plan": "stage 0 carries the state (state passing folded in)" if fused else "three stages",
+        "scan_tokens_per_s": round(tokens / (scan_ms / 1e3), 1),
+        "mfma_pct_of_int8_peak": round(100 * total_ops / (scan_ms / 1e3) / INT8_PEAK_OPS, 3),
+        "chunk_output_mfma_pct_of_int8_peak": round(
+            100 * ops["chunk_output"] / (per_kernel_ms["chunk_output"] / 1e3) / INT8_PEAK_OPS, 3),
+        "chunk_output_int8_ceiling_pct": round(
+            100 * ops["chunk_output"] / (unit["chunk_scan"] * tokens / (HBM_PEAK_GBS * 1e9)) / INT8_PEAK_OPS, 2),
+        "kernels": kernels,
+    }
+    return rec, inp
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import quantized_selective_state_amd as ssdq
+    import workloads
+
+    dev = torch.device("cuda:0")
+    names = args.workload or PREFILL_WORKLOADS
+    head = HEADLINE if HEADLINE in names else names[-1]
+    records = {}
+    head_inp = None
+    for name in [head] + [n for n in names if n != head]:
+        steps = args.steps if name == head else max(1, min(args.steps, 200))
+        warm = args.warmup if name == head else max(1, min(args.warmup, 50))
+        rec, inp = bench_prefill(name, steps, warm, torch, ssdq, workloads, dev,
+                                 keep_inputs=(name == head and not args.no_cpu_baseline))
+        records[name] = rec
+        if inp is not None:
+            head_inp = inp
+        torch.cuda.empty_cache()
+    h = records[head]
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": h["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded; fp16 activations quantized in the timed step)",
-        "config": {"workload": name, "batch": b, "seqlen": L, "nheads": H, "headdim": P, "dstate": N,
-                   "ngroups": G, "chunk": Q},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(dominant), "kernel_us": round(dom_ms * 1e3, 2)},
-        "plan": "stage 0 carries the state (state passing folded in)" if fused else "three stages",
-        "scan_tokens_per_s": round(tokens / (scan_ms / 1e3), 1),
-        "event_ms_per_step": round(e_start.elapsed_time(e_end) / args.steps, 5),
-        "mfma_pct_of_int8_peak": round(100 * total_ops / (scan_ms / 1e3) / INT8_PEAK_OPS, 3),
-        "chunk_output_mfma_pct_of_int8_peak": round(
-            100 * ops["chunk_output"] / (per_kernel_ms["chunk_output"] / 1e3) / INT8_PEAK_OPS, 3),
-        "kernels": kernels,
+        "config": {"workload": head, "batch": h["batch"], "seqlen": h["seqlen"], "nheads": h["nheads"],
+                   "headdim": h["headdim"], "dstate": h["dstate"], "ngroups": h["ngroups"], "chunk": h["chunk"]},
+        "roofline": h["roofline"],
     }
+    for k in ("plan", "scan_tokens_per_s", "event_ms_per_step", "mfma_pct_of_int8_peak",
+              "chunk_output_mfma_pct_of_int8_peak", "chunk_output_int8_ceiling_pct", "kernels"):
+        result[k] = h[k]
+    result["workloads"] = {n: r for n, r in records.items() if n != head}
 
-    del buf, quant, fns, x16, B16, C16, qx, qB, qC
     if not args.no_frontend:
-        result["frontend"] = bench_frontend(args, torch, ssdq, workloads, dev)
+        result["frontend"] = bench_frontend(args, torch, ssdq, workloads, dev, head)
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, ssdq, workloads, dev)
 
@@ -322,19 +395,18 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = n
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp)
+    if not args.no_cpu_baseline and head_inp is not None:
+        result["cpu_baseline"] = cpu_baseline(head_inp, workloads)
 
     print(json.dumps(result), flush=True)
     return 0
 
 
-def bench_frontend(args, torch, ssdq, workloads, dev):
+def bench_frontend(args, torch, ssdq, workloads, dev, name):
     """The same prefill step with the fused front end in place of the quantize launch: the
     depthwise causal conv1d + SiLU + static quantize of the in-projection output (x, B, C
     channels) and dt = softplus(dt_raw + dt_bias), then the scan.  Times the front end alone
     (events around each launch pair) and the whole step."""
-    name = "mamba2-1.3b-prefill"
     print(f"[bench] generating {name} front end", file=sys.stderr, flush=True)
     fe = workloads.make_frontend(name)
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -382,7 +454,8 @@ def bench_frontend(args, torch, ssdq, workloads, dev):
     gbs = alg / (fe_ms / 1e3) / 1e9
     return {"workload": name, "channels": C, "frontend_us": round(fe_ms * 1e3, 2), "alg_bytes": alg,
             "achieved_GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": _sum_or_none(measured_traffic("frontend"), measured_traffic("frontend (dt softplus)")),
+            "traffic": _sum_or_none(measured_traffic("frontend", name),
+                                     measured_traffic("frontend (dt softplus)", name)),
             "step_us": round(step_ms * 1e3, 2), "step_tokens_per_s": round(b * L / (step_ms / 1e3), 1)}
 
 
@@ -415,7 +488,7 @@ def bench_decode(args, torch, ssdq, workloads, dev):
     out = {"workload": name, "batch": b, "nheads": H, "headdim": P, "dstate": N, "ngroups": G, "steps": steps,
            "us_per_step": round(ms * 1e3, 2), "tokens_per_s": round(b / (ms / 1e3), 1),
            "alg_bytes_per_step": per_step, "achieved_GBs": round(gbs, 1),
-           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("state_update")}
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("state_update", name)}
 
     # the decode front end for the same sequences: conv state (b, 3, channels) fp16, one token
     ch = H * P + 2 * G * N
@@ -440,7 +513,7 @@ def bench_decode(args, torch, ssdq, workloads, dev):
     out["frontend_step"] = {"us_per_step": round(ms_fe * 1e3, 2), "alg_bytes_per_step": fe_bytes,
                             "achieved_GBs": round(fe_bytes / (ms_fe / 1e3) / 1e9, 1),
                             "hbm_frac": round(fe_bytes / (ms_fe / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic("frontend_step")}
+                            "traffic": measured_traffic("frontend_step", name)}
     del xbc_t, conv_state
 
     # the same steps on the state cached in binary16 (half the state bytes per step)
@@ -460,7 +533,7 @@ def bench_decode(args, torch, ssdq, workloads, dev):
     out["f16_state"] = {"us_per_step": round(ms16 * 1e3, 2), "tokens_per_s": round(b / (ms16 / 1e3), 1),
                         "alg_bytes_per_step": per_step16, "achieved_GBs": round(gbs16, 1),
                         "hbm_frac": round(gbs16 / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic("state_update_f16")}
+                        "traffic": measured_traffic("state_update_f16", name)}
 
     # and on the state cached as 8-bit codes with one fp32 scale per state row (a quarter of the bytes)
     del state16
@@ -482,37 +555,58 @@ def bench_decode(args, torch, ssdq, workloads, dev):
     out["i8_state"] = {"us_per_step": round(ms8 * 1e3, 2), "tokens_per_s": round(b / (ms8 / 1e3), 1),
                        "alg_bytes_per_step": per_step8, "achieved_GBs": round(gbs8, 1),
                        "hbm_frac": round(gbs8 / HBM_PEAK_GBS, 4),
-                       "traffic": measured_traffic("state_update_i8")}
+                       "traffic": measured_traffic("state_update_i8", name)}
     return out
 
 
-def cpu_baseline(inp):
-    """The oracle as it stands (quantizer + fp64 sequential recurrence) on the host cores,
-    on the whole prefill workload (every (batch, head) sequence)."""
-    import oracle
-    threads = oracle.default_threads()
-    print(f"[bench] cpu oracle on {threads} threads", file=sys.stderr, flush=True)
-    # whole-workload runs repeated until about 10 s of host time have passed (bounded: at most 50)
-    runs, t0 = 0, time.perf_counter()
-    while runs < 50 and (runs == 0 or time.perf_counter() - t0 < 10.0):
-        codes = oracle.codes_from_inputs(inp)
-        oracle.ssd(codes, threads=threads)
-        runs += 1
-    sec = (time.perf_counter() - t0) / runs
-    tokens = inp["batch"] * inp["seqlen"]
+def _cpu_model() -> str:
     cpu = platform.processor() or platform.machine()
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
+    return cpu
+
+
+def cpu_baseline(inp, workloads):
+    """The oracle as it stands (quantizer + fp64 sequential recurrence) on the host cores: the
+    whole headline workload (every (batch, head) sequence) once on all available threads, and a
+    sample of the 1.3B-shaped workload on one thread."""
+    import oracle
+    threads = oracle.default_threads()
+    print(f"[bench] cpu oracle on {threads} threads", file=sys.stderr, flush=True)
+    # whole-workload runs repeated until about 10 s of host time have passed (at most 3)
+    runs, t0 = 0, time.perf_counter()
+    while runs < 3 and (runs == 0 or time.perf_counter() - t0 < 10.0):
+        codes = oracle.codes_from_inputs(inp)
+        oracle.ssd(codes, threads=threads)
+        del codes
+        runs += 1
+    sec = (time.perf_counter() - t0) / runs
+    tokens = inp["batch"] * inp["seqlen"]
+    seqs = inp["batch"] * inp["nheads"]
+    # one thread: the first 64 heads of batch 0 of the 1.3B-shaped workload, scaled to the whole
+    # workload's tokens
+    name1 = "mamba2-1.3b-prefill"
+    print(f"[bench] cpu oracle on 1 thread, {name1} sample", file=sys.stderr, flush=True)
+    small = workloads.make_prefill(name1)
+    c1 = oracle.codes_from_inputs(small)
+    k = 64
+    t1 = time.perf_counter()
+    oracle.ssd(c1, pairs=[(0, h) for h in range(k)], threads=1)
+    sec1 = time.perf_counter() - t1
+    seqs1 = small["batch"] * small["nheads"]
+    tok1 = small["batch"] * small["seqlen"]
     return {"value": round(tokens / sec, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole workload: quantize x,B,C + all {inp['batch'] * inp['nheads']} (batch, head) "
-                      f"sequences of {inp['seqlen']} tokens, fp64; {runs} runs, {sec:.2f} s each",
-            "cpu": cpu}
+            "sample": f"whole workload: quantize x,B,C + all {seqs} (batch, head) sequences of {inp['seqlen']} "
+                      f"tokens, fp64; {runs} runs, {sec:.2f} s each",
+            "cpu": _cpu_model(), "nproc": os.cpu_count(), "threads_available": threads,
+            "one_thread": {"workload": name1, "value": round(tok1 / (sec1 * seqs1 / k), 1), "unit": "tokens/s",
+                           "sample": f"{k} of {seqs1} (batch, head) sequences of {small['seqlen']} tokens, "
+                                     f"{sec1:.2f} s, scaled to the whole workload"}}
 
 
 if __name__ == "__main__":

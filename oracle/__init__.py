@@ -17,27 +17,39 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A different build of the same source (the planted-mistake test points the pins at mutated
+# copies of the oracle through this variable); unset, the library next to the source is used.
+_LIB_OVERRIDE = os.environ.get("SSD_ORACLE_LIB")
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile liboracle.so with gcc (strict IEEE: no fast-math, no contraction)."""
+def compile_library(src: str, out: str, verbose: bool = False) -> str:
+    """Compile an oracle source file to a shared library with gcc (strict IEEE: no fast-math,
+    no contraction)."""
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
-           "-Wall", "-Wextra", _SRC, "-o", _LIB + ".tmp", "-lm"]
+           "-Wall", "-Wextra", src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile liboracle.so from ssd_oracle.c."""
+    return compile_library(_SRC, _LIB, verbose)
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.oracle_quantize_f16.argtypes = [P, P, P, i64, i32, i32]
@@ -53,7 +65,7 @@ def _load():
     lib.oracle_softplus_dt.restype = None
     lib.oracle_requantize_rows_i8.argtypes = [P, i64, i32, P, P, P]
     lib.oracle_requantize_rows_i8.restype = None
-    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P]
+    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
     lib.oracle_ssd_sequential_state_i8.restype = None
     lib.oracle_round_binary16.restype = None
     lib.oracle_chunk_cumsum.argtypes = [P, P, i64, i32, i32, i32, i32, P]
@@ -184,12 +196,31 @@ def ssd(c: Codes, pairs=None, chunk: int = 0, threads: int | None = None, state_
     return y, hf, bounds
 
 
-def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None):
+def ssd_batch(c: Codes, b: int, threads: int | None = None, state_f16: bool = False):
+    """Every head of batch index b: (y (L, H, P), h_final (H, P, N)) in float64, the heads run
+    on `threads` host threads.  Lets a caller compare a whole workload one batch index at a
+    time, holding only that much of the reference in memory."""
+    y = np.empty((c.L, c.H, c.P), np.float64)
+    hf = np.empty((c.H, c.P, c.N), np.float64)
+    threads = threads or default_threads()
+
+    def one(h):
+        yy, hh, _ = ssd_one(c, b, h, 0, state_f16)
+        y[:, h, :] = yy
+        hf[h] = hh
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, range(c.H)))
+    return y, hf
+
+
+def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None, scales_per_step: bool = False):
     """The recurrence for one (b, h) with the state cached as 8-bit codes and one binary32
     scale per state row between tokens, starting from codes q0 (batch,H,P,N) int8 with row
     scales s0 (batch,H,P) float32 (None: a zero state).  Returns (y (L,P), decoded final state
     (P,N), final codes (P,N) int8, final scales (P,) float32, last token's update before
-    re-quantization (P,N)), all from the oracle."""
+    re-quantization (P,N)), all from the oracle; with scales_per_step also the row scales after
+    every token (L,P) float32 as a sixth item."""
     lib = _load()
     y = np.empty((c.L, c.P), np.float64)
     hf = np.empty((c.P, c.N), np.float64)
@@ -202,10 +233,13 @@ def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None):
         raise ValueError("q0 and s0 go together")
     if q0 is not None and (q0.shape != (c.batch, c.H, c.P, c.N) or s0.shape != (c.batch, c.H, c.P)):
         raise ValueError("q0 must be (batch,H,P,N) and s0 (batch,H,P)")
+    steps = np.empty((c.L, c.P), np.float32) if scales_per_step else None
     lib.oracle_ssd_sequential_state_i8(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                        _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(q0), _ptr(s0),
                                        c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf), _ptr(q),
-                                       _ptr(s), _ptr(u))
+                                       _ptr(s), _ptr(u), _ptr(steps))
+    if scales_per_step:
+        return y, hf, q, s, u, steps
     return y, hf, q, s, u
 
 

@@ -157,13 +157,14 @@ void oracle_requantize_rows_i8(const double* in, int64_t rows, int32_t N, int8_t
 /* round_state: 0 none, 1 binary16 per element, 2 8-bit codes per row (requantize_row_i8).
  * q0/s0 (mode 2, optional): the starting state as codes (batch, H, P, N) and row scales
  * (batch, H, P); q_out/s_out: the final codes and scales; u_last: the last token's update
- * before it is re-quantized (P x N). */
+ * before it is re-quantized (P x N); s_steps (optional): every token's row scales (L x P). */
 static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
                            const int8_t* qC, const float* sC, const float* dt, const float* A,
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out, int round_state,
-                           const int8_t* q0, const float* s0, int8_t* q_out, float* s_out, double* u_last) {
+                           const int8_t* q0, const float* s0, int8_t* q_out, float* s_out, double* u_last,
+                           float* s_steps) {
   (void)batch;
   const int32_t g = h / (H / G);
   double* S = (double*)calloc((size_t)P * N, sizeof(double));
@@ -208,6 +209,7 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
       if (round_state == 2) {
         if (u_last && t == L - 1) memcpy(u_last + (int64_t)p * N, Sp, sizeof(double) * N);
         requantize_row_i8(Sp, N, codes + (int64_t)p * N, scales + p);
+        if (s_steps) s_steps[t * P + p] = scales[p];
       }
     }
   }
@@ -229,7 +231,7 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0,
-                 NULL, NULL, NULL, NULL, NULL);
+                 NULL, NULL, NULL, NULL, NULL, NULL);
 }
 
 /* The recurrence with the state cached in binary16 between tokens (h0 is taken as given). */
@@ -239,20 +241,22 @@ void oracle_ssd_sequential_state_f16(const int8_t* qx, const float* sx, const in
                                      int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                                      double* h_out) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1,
-                 NULL, NULL, NULL, NULL, NULL);
+                 NULL, NULL, NULL, NULL, NULL, NULL);
 }
 
 /* The recurrence with the state cached as 8-bit codes and one scale per state row between
  * tokens, starting from codes q0 (batch, H, P, N) with row scales s0 (batch, H, P) (both NULL:
  * a zero state).  h_out: the final state decoded (P x N); q_out/s_out: its codes and scales;
- * u_last (optional): the last token's update before re-quantization. */
+ * u_last (optional): the last token's update before re-quantization; s_steps (optional): the
+ * row scales after every token (L x P). */
 void oracle_ssd_sequential_state_i8(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
                                     const int8_t* qC, const float* sC, const float* dt, const float* A,
                                     const float* D, const int8_t* q0, const float* s0, int32_t batch, int64_t L,
                                     int32_t H, int32_t P, int32_t N, int32_t G, int32_t b, int32_t h,
-                                    double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last) {
+                                    double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last,
+                                    float* s_steps) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, NULL, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 2,
-                 q0, s0, q_out, s_out, u_last);
+                 q0, s0, q_out, s_out, u_last, s_steps);
 }
 
 /* Front end of the SSD block (the causal convolution ahead of the SSD box, Quamba2 rebuttal

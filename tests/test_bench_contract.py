@@ -47,16 +47,34 @@ def test_scan_ops_count_causal_pairs_once():
 
 def test_traffic_is_reported_only_for_the_current_source(tmp_path, monkeypatch):
     digest = bench.source_digest("chunk_output")
-    table = tmp_path / "traffic.md"
+    table = tmp_path / "hbm_traffic_mamba2-8b-prefill.md"
     table.write_text(
         "| kernel | source digest | dispatches | a | b | c | d | e | traffic bytes |\n"
         "|---|---|---|---|---|---|---|---|---|\n"
         f"| chunk_output | {digest} | 5 | 1 | 2 | 3 | 4 | 5 | 123456 |\n"
         "| state_scan | 0000000000000000 | 5 | 1 | 2 | 3 | 4 | 5 | 999 |\n")
-    monkeypatch.setattr(bench, "TRAFFIC_TABLE", str(table))
-    assert bench.measured_traffic("chunk_output") == 123456
-    assert bench.measured_traffic("state_scan") is None      # stale digest
-    assert bench.measured_traffic("quantize") is None        # no row
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    assert bench.measured_traffic("chunk_output", "mamba2-8b-prefill") == 123456
+    assert bench.measured_traffic("state_scan", "mamba2-8b-prefill") is None      # stale digest
+    assert bench.measured_traffic("quantize", "mamba2-8b-prefill") is None        # no row
+    assert bench.measured_traffic("chunk_output", "mamba2-1.3b-prefill") is None  # no table
+
+
+@pytest.mark.parametrize("shape,quant,scan", [((64, 64, 128, 1, 256), 13056, 21248),
+                                              ((80, 64, 128, 1, 256), 16128, 26496),
+                                              ((128, 64, 128, 8, 256), 30720, 44032)])
+def test_specified_bytes_per_token(shape, quant, scan):
+    """The per-token traffic the roofline is priced by, for the three prefill shapes (H, P, N,
+    G, Q): x, B, C int8 in, dt and Acs fp32, the fp32 state entering each chunk, y fp16 out."""
+    u = bench.survey_bytes_per_token(*shape)
+    assert u["quantize"] == quant and u["chunk_scan"] == scan
+
+
+def test_headline_is_the_largest_prefill_workload():
+    import workloads
+    sizes = {n: workloads.WORKLOADS[n].tokens * workloads.WORKLOADS[n].nheads for n in bench.PREFILL_WORKLOADS}
+    assert bench.HEADLINE == max(sizes, key=sizes.get) == "mamba2-8b-prefill"
+    assert bench.parse([]).workload is None          # default: every prefill workload
 
 
 def test_digest_follows_the_kernel_source():

@@ -1,26 +1,60 @@
 """GPU parity of ssdq_state_update_i8: the decode step with the state cached as 8-bit codes and
 one binary32 scale per state row.
 
-One step from the same cached state: every code the oracle fixes is reproduced exactly.  The
-oracle forms the update in double, the kernel in fp32; they can only part where the exact
-quotient update / scale lies within fp32 rounding of a midpoint between two codes, and there
-either neighbour is a correct rounding (checked), so the test compares the codes away from
-midpoints and accepts either neighbour near one.  Over many steps such a flip moves one element
-by one code step and decays afterwards, so the decoded states agree to a few code steps of their
-row and y to the usual tolerance.  Starting codes and scales come from the oracle's own
-re-quantization of the seeded fp32 state."""
+One step from the same cached state.  The oracle forms the update u in double, the kernel in
+fp32, so their row maxima m and scales s = binary32(m / 127) may differ by the fp32 rounding of
+the update, and a code may differ only where u / s lies within the kernel's rounding of a
+midpoint between two codes (there either neighbour is a correct rounding).  The band is derived
+per element from the kernel's arithmetic (unit roundoff e = 2^-24):
+  - e^(dt A) by exp2 of a rounded product: relative error <= (1.5 |dt A| + 1) 2e;
+  - u = fma(e^(dt A) s_old, q_old, ((dt s_x) s_B) x) b): with T1 = e^(dt A) s_old q_old and
+    T2 = dt xhat Bhat, |u_gpu - u| <= |T1| (eps_exp + 2e) + |T2| 4e + |u| e  =: du;
+  - |m_gpu - m| <= max_n du =: dm, and the kernel's scale is within one ulp of binary32(m_gpu / 127)
+    (its division sequence is checked over every binary32 significand on the host), so
+    |s_gpu - s| <= dm / 127 + 2 ulp(s);
+  - the kernel's quotient u_gpu rcp(s_gpu) (reciprocal within an ulp) is rounded to the nearest
+    integer exactly, so |t_gpu - u / s| <= du / s + |u / s| (|s_gpu - s| / s + 2e), with |u / s| <= 127.5.
+Twice that bound is the band: about 2^-14 code units for a slowly decaying row, up to about
+2^-11 for rows whose decay |dt A| is near 5 (the exp's error grows with its argument).  Over many
+steps each such flip moves one element by a code step and then decays, and once a row's largest
+elements differ its scale differs too, so the two caches drift apart by a few code steps of a
+slowly decaying row; the multi-step tests bound that drift per row from the oracle's own scales
+(see _caching_bound) and hold y to the usual tolerance.  Starting codes and scales come from the
+oracle's own re-quantization of the seeded fp32 state."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import workloads
-from gpu_util import Y_TOL, dev, note, sample_pairs, to_dev
+from gpu_util import Y_TOL, dev, note, threaded, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MIDPOINT_BAND = 2e-3   # |frac(u / s) - 1/2| below this: either neighbouring code is correct
-FLIPS = 4              # code steps allowed over many steps for such flips
+EPS = 2.0 ** -24       # binary32 unit roundoff
+ULP = 2.0 ** -23       # binary32 ulp relative to a normal value (upper bound)
+SAFETY = 2.0
+
+
+def _one_step_bounds(c, b, h, q0, s0, u, s_ref):
+    """Per-row bound on |s_gpu - s_ref| and per-element band on the quotient u / s (code units)
+    of one step from the cached codes q0, scales s0 (see the module docstring)."""
+    g = h // (c.H // c.G)
+    dt = float(c.dt[b, 0, h])
+    dA = abs(dt * float(c.A[h]))
+    eps_exp = (1.5 * dA + 1.0) * 2 * EPS
+    T1 = np.exp(dt * float(c.A[h])) * s0[b, h].astype(np.float64)[:, None] * q0[b, h]
+    xhat = float(c.sx[h]) * c.qx[b, 0, h].astype(np.float64)
+    bhat = float(c.sB[g]) * c.qB[b, 0, g].astype(np.float64)
+    T2 = dt * xhat[:, None] * bhat[None, :]
+    du = np.abs(T1) * (eps_exp + 2 * EPS) + np.abs(T2) * 4 * EPS + np.abs(u) * EPS
+    dm = du.max(axis=1)
+    s = s_ref.astype(np.float64)
+    ds = dm / 127 + 2 * ULP * s
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s[:, None] > 0, u / s[:, None], 0.0)
+        band = np.where(s[:, None] > 0, du / s[:, None] + np.abs(t) * (ds / s + 2 * EPS)[:, None], 0.0)
+    return SAFETY * ds, SAFETY * band, t
 
 
 def _start(dec):
@@ -55,24 +89,58 @@ def _small(seed, b, H, P, N, G, T):
     return workloads.make_decode(shape, seed_index=seed)
 
 
-def _check_steps(dec, q0, s0, y, q, s, pairs=None, tag=""):
+def _caching_bound(c, b, h, s0, steps):
+    """Per-row bound on |g_T - o_T| after T steps, g the GPU's cached state and o the oracle's,
+    both starting from the same codes.  With e_t = max_n |g_t - o_t| of a row and a_t = e^(dt_t A):
+    each step the two updates differ by at most a_t e_t plus the kernel's fp32 error err_t, each
+    side re-quantizes within half its own scale, and the GPU's scale exceeds the oracle's s_{t+1}
+    by at most max|u_g - u_o| / 127, so e_{t+1} <= (a_t e_t + err_t)(1 + 1/254) + s_{t+1}, with
+    err_t <= 127 (a_t s_t + s_{t+1})(eps_exp + 6e) (the one-step analysis of the module docstring).
+    A rounding flip near a midpoint moves an element by one code step and then decays with a_t, so
+    over many steps of a slowly decaying head the two caches drift apart by several code steps
+    (each bounded, none accumulating without decay)."""
+    dts = c.dt[b, :, h].astype(np.float64)
+    A = float(c.A[h])
+    s_prev = s0[b, h].astype(np.float64)
+    e = np.zeros_like(s_prev)
+    for t in range(c.L):
+        a = np.exp(dts[t] * A)
+        eps_exp = (1.5 * abs(dts[t] * A) + 1.0) * 2 * EPS
+        s_new = steps[t].astype(np.float64)
+        err = 127 * (a * s_prev + s_new) * (eps_exp + 6 * EPS)
+        e = (a * e + err) * (1 + 1 / 254) + s_new
+        s_prev = s_new
+    return e * (1 + 1e-6)
+
+
+def _check_steps(dec, q0, s0, y, q, s, tag=""):
+    """Every (b, h) sequence against the oracle with the same caching (run on host threads, each
+    sequence reduced to its maxima at once): the decoded cached states within the derived drift
+    bound of every row, and y within the bar."""
     c = oracle.decode_as_prefill(dec)
-    if pairs is None:
-        pairs = [(b, h) for b in range(c.batch) for h in range(c.H)]
-    e_h = e_y = 0.0
-    ymax = 0.0
-    worst_steps = 0.0
-    for b, h in pairs:
-        y8, h8, _, s8, _ = oracle.ssd_one_state_i8(c, b, h, q0, s0)
+
+    def one(bh):
+        b, h = bh
+        y8, h8, _, s8, _, steps = oracle.ssd_one_state_i8(c, b, h, q0, s0, scales_per_step=True)
         got = s[b, h].astype(np.float64)[:, None] * q[b, h]
-        row_step = np.maximum(s8.astype(np.float64), s[b, h])[:, None]     # one code step of each row
-        err = np.abs(got - h8)
-        worst_steps = max(worst_steps, float(np.max(err / np.where(row_step > 0, row_step, 1.0))))
-        assert np.all(err <= FLIPS * row_step * (1 + 1e-5) + 1e-30)
-        ymax = max(ymax, np.max(np.abs(y8)))
-        e_y = max(e_y, np.max(np.abs(y[:, b, h] - y8)))
-        e_h = max(e_h, np.max(err))
-    note(f"{tag}: state within {worst_steps:.2f} code steps of the cached oracle, y {e_y / ymax:.2e}")
+        err = np.abs(got - h8).max(axis=1)                                  # per row
+        bound = _caching_bound(c, b, h, s0, steps)
+        row_step = np.maximum(s8.astype(np.float64), s[b, h])             # one code step of each row
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+            in_steps = np.where(row_step > 0, err / row_step, 0.0)
+        return (bool(np.all(err <= bound)), float(ratio.max()), float(in_steps.max()), float(np.max(np.abs(y8))),
+                float(np.max(np.abs(y[:, b, h] - y8))))
+
+    r = threaded(one, [(b, h) for b in range(c.batch) for h in range(c.H)])
+    worst_ratio = max(v[1] for v in r)
+    steps = np.array([v[2] for v in r])
+    ymax = max(v[3] for v in r)
+    e_y = max(v[4] for v in r)
+    note(f"{tag} ({len(r)} sequences): cached states within {worst_ratio:.2f} of the derived drift bound; "
+         f"worst row {steps.max():.2f} code steps from the cached oracle (99th percentile of sequences "
+         f"{np.percentile(steps, 99):.2f}); y {e_y / ymax:.2e}")
+    assert all(v[0] for v in r), "a cached state drifted beyond its derived bound"
     assert e_y <= Y_TOL * ymax
 
 
@@ -81,24 +149,32 @@ def test_one_step_codes_match_the_oracle():
     q0, s0 = _start(dec)
     y, q, s = _gpu_decode_i8(dec, q0, s0)
     c = oracle.decode_as_prefill(dec)
-    near = mism = total = 0
+    near = mism = total = s_exact = s_rows = 0
+    worst_band = 0.0
     for b in range(c.batch):
         for h in range(c.H):
             y8, _, q8, s8, u = oracle.ssd_one_state_i8(c, b, h, q0, s0)
-            assert np.allclose(s[b, h], s8, rtol=1e-5, atol=0)
-            t = u / np.where(s8 > 0, s8.astype(np.float64), 1.0)[:, None]
-            band = np.abs(np.abs(t - np.floor(t)) - 0.5) < MIDPOINT_BAND
+            ds, band, t = _one_step_bounds(c, b, h, q0, s0, u, s8)
+            assert np.all(np.abs(s[b, h].astype(np.float64) - s8) <= ds), "row scale beyond its derived bound"
+            s_exact += int(np.sum(s[b, h] == s8))
+            s_rows += s8.size
+            near_mid = np.abs(np.abs(t - np.floor(t)) - 0.5) <= band
             diff = q[b, h].astype(np.int32) - q8
-            assert np.all(diff[~band] == 0)
-            qb = q[b, h][band].astype(np.float64)
-            tb = np.clip(t[band], -127, 127)
+            assert np.all(diff[~near_mid] == 0), "a code differs away from a rounding midpoint"
+            qb = q[b, h][near_mid].astype(np.float64)
+            tb = np.clip(t[near_mid], -127, 127)
             assert np.all((qb == np.floor(tb)) | (qb == np.ceil(tb)))   # either neighbour of the quotient
-            near += int(band.sum())
+            near += int(near_mid.sum())
             mism += int(np.count_nonzero(diff))
             total += diff.size
+            worst_band = max(worst_band, float(band.max()))
             assert np.max(np.abs(y[0, b, h] - y8[0])) <= Y_TOL * max(np.max(np.abs(y8)), 1e-30)
-    note(f"one step: {total} codes, {near} within the midpoint band, {mism} differ")
-    assert near < total // 100
+    note(f"one step: {total} codes, {near} within the derived midpoint band (widest {worst_band:.2e} code "
+         f"units), {mism} differ; {s_exact} of {s_rows} row scales equal the oracle's")
+    # the widest bands belong to strongly decaying rows (|dt A| near 5), where the fp32 exp of the
+    # decay contributes most: still below 2^-10 of a code step
+    assert worst_band < 2.0 ** -10
+    assert near < total // 1000
 
 
 @pytest.mark.parametrize("N,G", [(128, 4), (64, 2)])
@@ -132,16 +208,14 @@ def test_zero_and_subnormal_scale_rows_are_flushed():
     _check_steps(dec, q0, s0, y, q, s, tag="i8 state zero rows")
 
 
-def test_full_decode_workload_sampled():
-    """batch 256, 128 heads, 8 groups, 128 steps on the 256 MiB 8-bit state; oracle on sampled
-    sequences (always with the largest and smallest x scales)."""
+def test_full_decode_workload():
+    """batch 256, 128 heads, 8 groups, 128 steps on the 256 MiB 8-bit state: every (batch, head)
+    sequence against the oracle with the same caching."""
     note("generating decode workload")
     dec = workloads.make_decode("mamba2-8b-decode")
     q0, s0 = _start(dec)
     note("gpu decode 128 steps, 8-bit state")
     y, q, s = _gpu_decode_i8(dec, q0, s0)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(s))
-    order = np.argsort(dec["x_scale"])
-    pairs = sample_pairs(256, 128, 12, 23, list(order[-3:]) + list(order[:2]))
-    note(f"oracle decode on {len(pairs)} sequences")
-    _check_steps(dec, q0, s0, y, q, s, pairs=pairs, tag="i8 state full")
+    note("oracle decode, 8-bit state: all sequences")
+    _check_steps(dec, q0, s0, y, q, s, tag="i8 state full")
