@@ -45,7 +45,8 @@ typedef enum {
   SSDQ_ERROR_INVALID_VALUE = 1,       /* null / misaligned pointer, non-positive size, H % G != 0 */
   SSDQ_ERROR_UNSUPPORTED = 2,         /* a shape the kernels do not handle (see each call) */
   SSDQ_ERROR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes below ssdq_chunk_scan_workspace_size() */
-  SSDQ_ERROR_LAUNCH = 4               /* the HIP runtime rejected a kernel launch */
+  SSDQ_ERROR_LAUNCH = 4,              /* the HIP runtime rejected a kernel launch */
+  SSDQ_ERROR_SCRATCH_LIMIT = 5        /* ssdq_chunk_scan_noalloc: the shape needs more than the static scratch */
 } ssdq_status;
 
 /* Human-readable name of a status (host; static storage; never NULL). */
@@ -172,6 +173,38 @@ ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x
                                   float* h_final, int32_t batch, int64_t seqlen, int32_t nheads,
                                   int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of the library's static device scratch that ssdq_chunk_scan_noalloc uses (per device). */
+#define SSDQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * ssdq_chunk_scan without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * intermediates (Acs, the chunk states of the three-kernel plan, the carried-state limbs and
+ * their row scales) live in one static device array of SSDQ_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends; the call allocates and
+ * frees nothing.  Arguments, shapes, accuracy and validation are those of ssdq_chunk_scan, and
+ * the results are those of ssdq_chunk_scan with the same arguments (the same kernels run).
+ *   - A shape whose intermediates exceed the scratch (ssdq_chunk_scan_noalloc_scratch_size()
+ *     above SSDQ_NOALLOC_SCRATCH_BYTES) returns SSDQ_ERROR_SCRATCH_LIMIT and launches nothing.
+ *   - Every call on a device shares that device's scratch, and it keeps the last call's contents:
+ *     calls that overlap on one device (concurrent streams, or several host threads without
+ *     ordering) race on it and must be serialized by the caller.  Calls on one stream are
+ *     ordered and safe.  Nothing in the scratch needs to start at zero.
+ *   - The first call on a device looks up the scratch's device address (hipGetSymbolAddress);
+ *     if that fails the call returns SSDQ_ERROR_LAUNCH.
+ */
+ssdq_status ssdq_chunk_scan_noalloc(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                    const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                    const float* D, const float* h0, void* y, float* h_final, int32_t batch,
+                                    int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                    int32_t ngroups, int32_t chunk, hipStream_t stream);
+
+/* Scratch bytes ssdq_chunk_scan_noalloc needs for this shape on the current device (host; 0 on
+ * invalid shapes): the Acs, carried-state and row-scale regions, plus the fp32 chunk states when
+ * the three-kernel plan runs, each rounded up to 256 bytes. */
+size_t ssdq_chunk_scan_noalloc_scratch_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
+                                            int32_t dstate, int32_t chunk);
 
 /*
  * Decode: one recurrence step per sequence, state updated IN PLACE (the

@@ -22,6 +22,8 @@ SSDQ_ERROR_INVALID_VALUE = 1
 SSDQ_ERROR_UNSUPPORTED = 2
 SSDQ_ERROR_WORKSPACE_TOO_SMALL = 3
 SSDQ_ERROR_LAUNCH = 4
+SSDQ_ERROR_SCRATCH_LIMIT = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 CHUNK_SCAN_STAGES = 3
 STAGE_NAMES = ("chunk_state", "state_passing", "chunk_output")   # stage 0 also runs the chunk cumsum
 
@@ -63,6 +65,10 @@ lib.ssdq_frontend_step.argtypes = [_P, _P, _P, _P, _i32] + [_P] * 9 + [_i32] * 5
 lib.ssdq_frontend_step.restype = ctypes.c_int
 lib.ssdq_state_update_i8.argtypes = [_P] * 12 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_i8.restype = ctypes.c_int
+lib.ssdq_chunk_scan_noalloc.argtypes = [_P] * 12 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P]
+lib.ssdq_chunk_scan_noalloc.restype = ctypes.c_int
+lib.ssdq_chunk_scan_noalloc_scratch_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32]
+lib.ssdq_chunk_scan_noalloc_scratch_size.restype = _sz
 lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
 lib.ssdq_chunk_scan_state_fused.restype = _i32
 
@@ -262,6 +268,41 @@ def chunk_scan(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk
                       want_final_state)
     buf.run()
     return buf.y, buf.h_final
+
+
+def chunk_scan_noalloc_scratch_size(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
+                                    chunk: int) -> int:
+    return int(lib.ssdq_chunk_scan_noalloc_scratch_size(batch, seqlen, nheads, headdim, dstate, chunk))
+
+
+def chunk_scan_noalloc(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk=256, y=None,
+                       h_final=None):
+    """Prefill through ssdq_chunk_scan_noalloc: the library's static device scratch instead of a
+    workspace (the call itself allocates nothing; y and h_final are allocated here unless given).
+    Returns (y, h_final)."""
+    b, L, H, P = x.shape
+    N = B.shape[3]
+    dev = x.device
+    if y is None:
+        y = torch.empty((b, L, H, P), dtype=torch.float16, device=dev)
+    if h_final is None:
+        h_final = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    # the same argument checks as ScanBuffers, with no workspace
+    G = B.shape[2]
+    for t, name, dtype, shape, opt in ((x, "x", torch.int8, (b, L, H, P), False),
+                                      (x_scale, "x_scale", torch.float32, (H,), False),
+                                      (B, "B", torch.int8, (b, L, G, N), False),
+                                      (B_scale, "B_scale", torch.float32, (G,), False),
+                                      (C, "C", torch.int8, (b, L, G, N), False),
+                                      (C_scale, "C_scale", torch.float32, (G,), False),
+                                      (dt, "dt", torch.float32, (b, L, H), False), (A, "A", torch.float32, (H,), False),
+                                      (D, "D", torch.float32, (H,), True), (h0, "h0", torch.float32, (b, H, P, N), True),
+                                      (y, "y", torch.float16, (b, L, H, P), False),
+                                      (h_final, "h_final", torch.float32, (b, H, P, N), False)):
+        _need(t, name, dtype, shape, dev, optional=opt)
+    args = [_ptr(t) for t in (x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final)]
+    _check(lib.ssdq_chunk_scan_noalloc(*args, b, L, H, P, N, G, chunk, _stream(dev)), "ssdq_chunk_scan_noalloc")
+    return y, h_final
 
 
 # ---------------------------------------------------------------------------------------------

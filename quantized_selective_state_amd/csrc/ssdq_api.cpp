@@ -3,6 +3,8 @@
 // paths can be exercised on a machine without a GPU.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ssdq_internal.h"
 
 using namespace ssdq;
@@ -98,6 +100,37 @@ ssdq_status run_stage(int32_t stage, const ScanShape& s, const ScanArgs& a, hipS
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
+// Scratch of the allocation-free prefill entry point: one file-scope device array, which every
+// GPU the library runs on holds for the life of the process.  Host code never uses the array's
+// name as an address (on the host it only names the symbol): the device address is looked up once
+// per device with hipGetSymbolAddress, with that device current, and kept here.
+__device__ __attribute__((aligned(256))) uint8_t scratch[SSDQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that device), or nullptr
+// if the runtime cannot provide it.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// The compact scratch layout of one prefill call: Acs, the fp32 chunk states only when the
+// three-kernel plan runs (fused = false), the carried-state limbs and their row scales, each
+// region starting at a 256-byte boundary.
+size_t noalloc_bytes(const ScanShape& s, bool fused) {
+  return s.acs_bytes + (fused ? 0 : round256(s.state_bytes)) + s.hprev_bytes + s.hscale_bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +142,7 @@ const char* ssdq_status_string(ssdq_status status) {
     case SSDQ_ERROR_UNSUPPORTED: return "SSDQ_ERROR_UNSUPPORTED";
     case SSDQ_ERROR_WORKSPACE_TOO_SMALL: return "SSDQ_ERROR_WORKSPACE_TOO_SMALL";
     case SSDQ_ERROR_LAUNCH: return "SSDQ_ERROR_LAUNCH";
+    case SSDQ_ERROR_SCRATCH_LIMIT: return "SSDQ_ERROR_SCRATCH_LIMIT";
   }
   return "SSDQ_UNKNOWN_STATUS";
 }
@@ -177,6 +211,45 @@ ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t*
                                          seqlen, nheads, headdim, dstate, ngroups, chunk, workspace,
                                          workspace_bytes, &s, &a);
   if (st != SSDQ_SUCCESS) return st;
+  for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
+    const ssdq_status r = run_stage(stage, s, a, stream);
+    if (r != SSDQ_SUCCESS) return r;
+  }
+  return SSDQ_SUCCESS;
+}
+
+size_t ssdq_chunk_scan_noalloc_scratch_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
+                                            int32_t dstate, int32_t chunk) {
+  ScanShape s;
+  if (check_scan_shape(batch, seqlen, nheads, headdim, dstate, 1, chunk, &s) != SSDQ_SUCCESS) return 0;
+  return noalloc_bytes(s, state_scan_fused(batch, nheads));
+}
+
+ssdq_status ssdq_chunk_scan_noalloc(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                    const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                    const float* D, const float* h0, void* y, float* h_final, int32_t batch,
+                                    int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                    int32_t ngroups, int32_t chunk, hipStream_t stream) {
+  // every check the workspace entry point makes, with a stand-in workspace pointer that is only
+  // tested for alignment (the scratch regions are carved below)
+  ScanShape s;
+  ScanArgs a;
+  static const uint8_t kAlignedStandIn alignas(256) = 0;
+  ssdq_status st = check_scan_args(0, x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final, batch, seqlen,
+                                   nheads, headdim, dstate, ngroups, chunk,
+                                   const_cast<uint8_t*>(&kAlignedStandIn), SIZE_MAX, &s, &a);
+  if (st != SSDQ_SUCCESS) return st;
+  const bool fused = state_scan_fused(batch, nheads);
+  if (noalloc_bytes(s, fused) > size_t(SSDQ_NOALLOC_SCRATCH_BYTES)) return SSDQ_ERROR_SCRATCH_LIMIT;
+  char* base = static_cast<char*>(device_scratch());
+  if (base == nullptr) return SSDQ_ERROR_LAUNCH;
+  a.acs = reinterpret_cast<float*>(base);
+  size_t off = s.acs_bytes;
+  a.states = reinterpret_cast<float*>(base + off);   // not read or written by the fused plan
+  if (!fused) off += round256(s.state_bytes);
+  a.hprev = reinterpret_cast<int8_t*>(base + off);
+  off += s.hprev_bytes;
+  a.hscale = reinterpret_cast<float*>(base + off);
   for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
     const ssdq_status r = run_stage(stage, s, a, stream);
     if (r != SSDQ_SUCCESS) return r;

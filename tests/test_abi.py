@@ -234,3 +234,30 @@ def _fes(lib, **kw):
 ])
 def test_frontend_step_validation(lib, kw, status):
     assert _fes(lib, **kw) == status
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.ssdq_chunk_scan_noalloc.argtypes = [P] * 12 + [i32, i64, i32, i32, i32, i32, i32, P]
+    lib.ssdq_chunk_scan_noalloc_scratch_size.argtypes = [i32, i64, i32, i32, i32, i32]
+    lib.ssdq_chunk_scan_noalloc_scratch_size.restype = sz
+    ptrs = [A16] * 12
+    # a misaligned pointer, a bad shape, an unsupported shape: rejected like ssdq_chunk_scan
+    bad = list(ptrs)
+    bad[0] = A16 + 1
+    assert lib.ssdq_chunk_scan_noalloc(*bad, 1, 256, 4, 16, 16, 1, 64, None) == INVALID
+    assert lib.ssdq_chunk_scan_noalloc(*ptrs, 1, 256, 3, 16, 16, 2, 64, None) == INVALID      # H % G
+    assert lib.ssdq_chunk_scan_noalloc(*ptrs, 1, 256, 4, 24, 16, 1, 64, None) == UNSUPPORTED  # headdim
+    # the 8B-shaped layer's intermediates (256 MiB of carried state) exceed the 64 MiB scratch: the
+    # call says so and launches nothing, whichever plan the device would take
+    need = lib.ssdq_chunk_scan_noalloc_scratch_size(8, 4096, 128, 64, 128, 256)
+    assert need > 64 << 20
+    assert lib.ssdq_chunk_scan_noalloc(*ptrs, 8, 4096, 128, 64, 128, 8, 256, None) == 5
+    assert lib.ssdq_status_string(5) == b"SSDQ_ERROR_SCRATCH_LIMIT"
+    # the compact layout without a device (three-kernel plan: the fp32 chunk states included)
+    r = lambda v: (v + 255) // 256 * 256
+    b, L, H, Pd, N, Q = 1, 300, 8, 32, 64, 64
+    nc = -(-L // Q)
+    assert lib.ssdq_chunk_scan_noalloc_scratch_size(b, L, H, Pd, N, Q) == (
+        r(4 * b * H * nc * Q) + r(4 * b * nc * H * Pd * N) + r(2 * b * nc * H * Pd * N) + r(4 * b * nc * H * Pd))
+    assert lib.ssdq_chunk_scan_noalloc_scratch_size(0, L, H, Pd, N, Q) == 0
