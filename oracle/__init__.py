@@ -54,9 +54,9 @@ def _load():
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.oracle_quantize_f16.argtypes = [P, P, P, i64, i32, i32]
     lib.oracle_quantize_f16.restype = None
-    lib.oracle_ssd_sequential.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, i32, P]
+    lib.oracle_ssd_sequential.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, i32, P, P]
     lib.oracle_ssd_sequential.restype = None
-    lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P]
+    lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P]
     lib.oracle_ssd_sequential_state_f16.restype = None
     lib.oracle_round_binary16.argtypes = [P, P, i64]
     lib.oracle_frontend.argtypes = [P, P, P, i32, i32, i64, i32, P, P, P]
@@ -65,7 +65,9 @@ def _load():
     lib.oracle_softplus_dt.restype = None
     lib.oracle_requantize_rows_i8.argtypes = [P, i64, i32, P, P, P]
     lib.oracle_requantize_rows_i8.restype = None
-    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P]
+    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.oracle_ssd_sequential_values.argtypes = [P] * 7 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P]
+    lib.oracle_ssd_sequential_values.restype = None
     lib.oracle_ssd_sequential_state_i8.restype = None
     lib.oracle_round_binary16.restype = None
     lib.oracle_chunk_cumsum.argtypes = [P, P, i64, i32, i32, i32, i32, P]
@@ -121,16 +123,19 @@ def quantize_values(v16: np.ndarray, scale: float) -> np.ndarray:
 
 
 class Codes:
-    """Quantized prefill inputs in the scan's layout."""
+    """Quantized prefill inputs in the scan's layout; y_corr (H, P) float32 is the optional output
+    correction added to every y."""
 
-    def __init__(self, qx, sx, qB, sB, qC, sC, dt, A, D=None, h0=None):
+    def __init__(self, qx, sx, qB, sB, qC, sC, dt, A, D=None, h0=None, y_corr=None):
         self.qx = _c(qx, np.int8)
         self.qB = _c(qB, np.int8)
         self.qC = _c(qC, np.int8)
         self.sx, self.sB, self.sC = _c(sx, np.float32), _c(sB, np.float32), _c(sC, np.float32)
         self.dt, self.A = _c(dt, np.float32), _c(A, np.float32)
         self.D, self.h0 = _c(D, np.float32), _c(h0, np.float32)
+        self.y_corr = _c(y_corr, np.float32)
         self.batch, self.L, self.H, self.P = self.qx.shape
+        assert self.y_corr is None or self.y_corr.shape == (self.H, self.P)
         self.G, self.N = self.qB.shape[2], self.qB.shape[3]
         assert self.qB.shape == (self.batch, self.L, self.G, self.N) == self.qC.shape
         assert self.dt.shape == (self.batch, self.L, self.H)
@@ -138,11 +143,12 @@ class Codes:
 
 
 def codes_from_inputs(inp: dict) -> Codes:
-    """Quantize a workload draw with the oracle's quantizer."""
+    """Quantize a workload draw with the oracle's quantizer (with its output correction y_corr,
+    if the draw carries one)."""
     return Codes(quantize(inp["x16"], inp["x_scale"]), inp["x_scale"],
                  quantize(inp["B16"], inp["B_scale"]), inp["B_scale"],
                  quantize(inp["C16"], inp["C_scale"]), inp["C_scale"],
-                 inp["dt"], inp["A"], inp.get("D"), inp.get("h0"))
+                 inp["dt"], inp["A"], inp.get("D"), inp.get("h0"), inp.get("y_corr"))
 
 
 def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
@@ -154,7 +160,8 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
     if state_f16:
         lib.oracle_ssd_sequential_state_f16(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                             _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
-                                            c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf))
+                                            c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
+                                            _ptr(c.y_corr))
         return y, hf, None
     bounds = None
     if chunk > 0:
@@ -162,7 +169,7 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
     lib.oracle_ssd_sequential(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                               _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
                               c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
-                              chunk, _ptr(bounds))
+                              chunk, _ptr(bounds), _ptr(c.y_corr))
     return y, hf, bounds
 
 
@@ -237,10 +244,51 @@ def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None, scales_per_step
     lib.oracle_ssd_sequential_state_i8(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                        _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(q0), _ptr(s0),
                                        c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf), _ptr(q),
-                                       _ptr(s), _ptr(u), _ptr(steps))
+                                       _ptr(s), _ptr(u), _ptr(steps), _ptr(c.y_corr))
     if scales_per_step:
         return y, hf, q, s, u, steps
     return y, hf, q, s, u
+
+
+def ssd_values_one(v: dict, b: int, h: int):
+    """The recurrence for one (b, h) over real-valued inputs: v holds x (batch, L, H, P), B and C
+    (batch, L, G, N) as float64 (for instance the binary16 activations before quantization), dt,
+    A, and optionally D and h0.  Returns (y (L, P), h_final (P, N)) in float64."""
+    lib = _load()
+    x, B, C = _c(v["x"], np.float64), _c(v["B"], np.float64), _c(v["C"], np.float64)
+    dt, A = _c(v["dt"], np.float32), _c(v["A"], np.float32)
+    D, h0 = _c(v.get("D"), np.float32), _c(v.get("h0"), np.float32)
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    y = np.empty((L, P), np.float64)
+    hf = np.empty((P, N), np.float64)
+    lib.oracle_ssd_sequential_values(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(D), _ptr(h0), batch, L, H,
+                                     P, N, G, b, h, _ptr(y), _ptr(hf))
+    return y, hf
+
+
+def mean_correction(inp: dict, threads: int | None = None) -> np.ndarray:
+    """SSDi8's per-channel mean correction (an error correction term from per-channel error
+    statistics, SSDi8 abstract; "mean correction", Figure 1b), calibrated on a draw `inp` (binary16
+    x, B, C with their static scales, dt, A, D, h0) the plainest way the pages support: the error
+    of the quantized scan's output channel (h, p) is y_ref - y_q, with y_ref the recurrence over the
+    unquantized binary16 inputs and y_q the recurrence over their INT8 codes; the correction is
+    its mean over every (batch, token) position of the draw.  Returns y_corr (H, P) float32, the
+    term added to every y of the corrected scan."""
+    c = codes_from_inputs(inp)
+    vals = dict(x=inp["x16"].astype(np.float64), B=inp["B16"].astype(np.float64), C=inp["C16"].astype(np.float64),
+                dt=inp["dt"], A=inp["A"], D=inp.get("D"), h0=inp.get("h0"))
+    sums = np.zeros((c.batch, c.H, c.P))
+
+    def one(bh):
+        b, h = bh
+        y_q, _, _ = ssd_one(c, b, h)
+        y_ref, _ = ssd_values_one(vals, b, h)
+        sums[b, h] = (y_ref - y_q).sum(axis=0)
+
+    with ThreadPoolExecutor(threads or default_threads()) as ex:
+        list(ex.map(one, [(b, h) for b in range(c.batch) for h in range(c.H)]))
+    return (sums.sum(axis=0) / (c.batch * c.L)).astype(np.float32)
 
 
 def requantize_rows_i8(rows: np.ndarray):

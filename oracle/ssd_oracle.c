@@ -36,6 +36,14 @@
  *    [-127, 127] with s = max|row| / 127 (the reading stated at
  *    requantize_row_i8).
  *
+ *  - the output correction (SSDi8's mean correction: its abstract names an error correction term
+ *    from per-channel error statistics, Figure 1b a mean correction, Table 6 ablates it and
+ *    Table 16 times it; no algebra is given): every y the recurrences above produce may carry a
+ *    per-(head, channel) additive term y_corr[h, p].  oracle_ssd_sequential_values runs the same
+ *    recurrence over real-valued (unquantized) inputs; the calibration of y_corr as the mean,
+ *    over a calibration draw's (batch, token) positions, of that reference's y minus the
+ *    quantized recurrence's y is written out in oracle/__init__.py (mean_correction).
+ *
  *  - oracle_frontend / oracle_softplus_dt: the block's front end ahead of the
  *    quantizer (depthwise causal conv1d + bias + SiLU, rounded to binary16) and
  *    dt = softplus(dt_raw + dt_bias), each as the reading stated at the function.
@@ -164,7 +172,7 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out, int round_state,
                            const int8_t* q0, const float* s0, int8_t* q_out, float* s_out, double* u_last,
-                           float* s_steps) {
+                           float* s_steps, const float* ycorr) {
   (void)batch;
   const int32_t g = h / (H / G);
   double* S = (double*)calloc((size_t)P * N, sizeof(double));
@@ -205,7 +213,8 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
         acc += Cv[n] * Sp[n];
         if (round_state == 1) Sp[n] = round_to_binary16(Sp[n]);
       }
-      y_out[t * P + p] = acc + Dh * xv[p];
+      const double mu = ycorr ? (double)ycorr[(int64_t)h * P + p] : 0.0;
+      y_out[t * P + p] = acc + Dh * xv[p] + mu;
       if (round_state == 2) {
         if (u_last && t == L - 1) memcpy(u_last + (int64_t)p * N, Sp, sizeof(double) * N);
         requantize_row_i8(Sp, N, codes + (int64_t)p * N, scales + p);
@@ -229,9 +238,9 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            const int8_t* qC, const float* sC, const float* dt, const float* A,
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                           double* h_out, int32_t chunk, double* bound_out) {
+                           double* h_out, int32_t chunk, double* bound_out, const float* ycorr) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0,
-                 NULL, NULL, NULL, NULL, NULL, NULL);
+                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr);
 }
 
 /* The recurrence with the state cached in binary16 between tokens (h0 is taken as given). */
@@ -239,9 +248,9 @@ void oracle_ssd_sequential_state_f16(const int8_t* qx, const float* sx, const in
                                      const int8_t* qC, const float* sC, const float* dt, const float* A,
                                      const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                                      int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                                     double* h_out) {
+                                     double* h_out, const float* ycorr) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1,
-                 NULL, NULL, NULL, NULL, NULL, NULL);
+                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr);
 }
 
 /* The recurrence with the state cached as 8-bit codes and one scale per state row between
@@ -254,9 +263,48 @@ void oracle_ssd_sequential_state_i8(const int8_t* qx, const float* sx, const int
                                     const float* D, const int8_t* q0, const float* s0, int32_t batch, int64_t L,
                                     int32_t H, int32_t P, int32_t N, int32_t G, int32_t b, int32_t h,
                                     double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last,
-                                    float* s_steps) {
+                                    float* s_steps, const float* ycorr) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, NULL, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 2,
-                 q0, s0, q_out, s_out, u_last, s_steps);
+                 q0, s0, q_out, s_out, u_last, s_steps, ycorr);
+}
+
+/* The same recurrence over real-valued inputs, for one (b, h): x (batch, L, H, P), B and C
+ * (batch, L, G, N) given as doubles (e.g. the binary16 activations before quantization), dt, A,
+ * D, h0 as in oracle_ssd_sequential.  This is the unquantized reference the output correction is
+ * calibrated against.  y_out: L x P; h_out: P x N. */
+void oracle_ssd_sequential_values(const double* x, const double* Bm, const double* Cm, const float* dt,
+                                  const float* A, const float* D, const float* h0, int32_t batch, int64_t L,
+                                  int32_t H, int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
+                                  double* h_out) {
+  (void)batch;
+  const int32_t g = h / (H / G);
+  double* S = (double*)calloc((size_t)P * N, sizeof(double));
+  if (h0) {
+    const float* src = h0 + ((int64_t)b * H + h) * P * N;
+    for (int64_t i = 0; i < (int64_t)P * N; ++i) S[i] = (double)src[i];
+  }
+  const double Ah = (double)A[h];
+  const double Dh = D ? (double)D[h] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t row = (int64_t)b * L + t;
+    const double d = (double)dt[row * H + h];
+    const double a = exp(d * Ah);
+    const double* xr = x + (row * H + h) * P;
+    const double* Br = Bm + (row * G + g) * N;
+    const double* Cr = Cm + (row * G + g) * N;
+    for (int32_t p = 0; p < P; ++p) {
+      double* Sp = S + (int64_t)p * N;
+      const double u = d * xr[p];
+      double acc = 0.0;
+      for (int32_t n = 0; n < N; ++n) {
+        Sp[n] = a * Sp[n] + u * Br[n];
+        acc += Cr[n] * Sp[n];
+      }
+      y_out[t * P + p] = acc + Dh * xr[p];
+    }
+  }
+  memcpy(h_out, S, sizeof(double) * P * N);
+  free(S);
 }
 
 /* Front end of the SSD block (the causal convolution ahead of the SSD box, Quamba2 rebuttal

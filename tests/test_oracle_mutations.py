@@ -22,14 +22,25 @@ PINS = {
     "f16": ["tests/test_oracle_state_f16.py"],
     "i8": ["tests/test_oracle_state_i8.py"],
     "fe": ["tests/test_oracle_frontend.py"],
+    "corr": ["tests/test_oracle_correction.py"],
 }
 
 # (name, pin files, text in ssd_oracle.c, replacement)
 MUTANTS = [
     ("readout by B instead of C", "rec", "acc += Cv[n] * Sp[n];", "acc += Bv[n] * Sp[n];"),
-    ("D x dropped", "rec", "y_out[t * P + p] = acc + Dh * xv[p];", "y_out[t * P + p] = acc;"),
-    ("decay exponent sign", "rec", "const double a = exp(d * Ah);", "const double a = exp(-d * Ah);"),
-    ("group map h % G", "rec", "const int32_t g = h / (H / G);\n  double* S", "const int32_t g = h % G;\n  double* S"),
+    ("D x dropped", "rec", "y_out[t * P + p] = acc + Dh * xv[p] + mu;", "y_out[t * P + p] = acc + mu;"),
+    ("correction indexed (p, h)", "corr", "ycorr[(int64_t)h * P + p]", "ycorr[(int64_t)p * H + h]"),
+    ("correction subtracted", "corr", "acc + Dh * xv[p] + mu;", "acc + Dh * xv[p] - mu;"),
+    ("unquantized readout by B", "corr", "acc += Cr[n] * Sp[n];", "acc += Br[n] * Sp[n];"),
+    ("unquantized x dropped", "corr", "const double u = d * xr[p];", "const double u = d;"),
+    ("unquantized decay sign", "corr", "const double a = exp(d * Ah);\n    const double* xr",
+     "const double a = exp(-d * Ah);\n    const double* xr"),
+    ("decay exponent sign", "rec", "const double a = exp(d * Ah);\n    for (int32_t p = 0; p < P; ++p) xv[p]",
+     "const double a = exp(-d * Ah);\n    for (int32_t p = 0; p < P; ++p) xv[p]"),
+    ("group map h % G", "rec", "const int32_t g = h / (H / G);\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  double* xv",
+     "const int32_t g = h % G;\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  double* xv"),
+    ("unquantized group map h % G", "corr", "const int32_t g = h / (H / G);\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  if (h0)",
+     "const int32_t g = h % G;\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  if (h0)"),
     ("x dropped from the input term", "rec", "const double u = d * xv[p];", "const double u = d;"),
     ("dt dropped from the input term", "rec", "const double u = d * xv[p];", "const double u = xv[p];"),
     ("y read before the update", "rec", "Sp[n] = a * Sp[n] + u * Bv[n];\n        acc += Cv[n] * Sp[n];",
