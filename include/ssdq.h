@@ -174,6 +174,27 @@ ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x
                                   int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk,
                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * ssdq_chunk_scan with SSDi8's output correction: every output also receives a per-(head,
+ * channel) term (SSDi8 abstract: an error correction term based on per-channel error statistics;
+ * Figure 1b: mean correction; Tables 6 and 16).  The pages give no algebra for it; the reading
+ * taken is the plainest they support: an additive term, calibrated offline (like the static
+ * scales) as the mean over a calibration set of the unquantized scan's y minus the quantized
+ * scan's y, channel by channel.  Calibration is the caller's; the library only applies it:
+ *
+ *   y[b,t,h,p] = (the output of ssdq_chunk_scan) + y_corr[h, p]     (added in fp32 before the fp16 rounding)
+ *
+ *   y_corr : (nheads, headdim) fp32, device, 16-byte aligned (NULL: SSDQ_ERROR_INVALID_VALUE)
+ * Every other argument, the shapes, the accuracy and the validation are those of ssdq_chunk_scan,
+ * and h_final does not depend on y_corr.
+ */
+ssdq_status ssdq_chunk_scan_corrected(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                      const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                      const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
+                                      int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                      int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* Bytes of the library's static device scratch that ssdq_chunk_scan_noalloc uses (per device). */
 #define SSDQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 
@@ -269,6 +290,33 @@ ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t
                                  const float* dt, const float* A, const float* D, void* y, int32_t batch,
                                  int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                                  hipStream_t stream);
+
+/* Formats of the decode state for ssdq_state_update_corrected. */
+typedef enum {
+  SSDQ_STATE_F32 = 0,   /* fp32 state, as ssdq_state_update */
+  SSDQ_STATE_F16 = 1,   /* IEEE binary16 cache, as ssdq_state_update_f16 */
+  SSDQ_STATE_I8 = 2     /* 8-bit codes + row scales, as ssdq_state_update_i8 */
+} ssdq_state_format;
+
+/*
+ * The decode step with the output correction of ssdq_chunk_scan_corrected: the step of the given
+ * state format (its arguments, layout, validation and in-place update unchanged) whose y also
+ * receives y_corr[h, p]:
+ *
+ *   y[b,h,p] = (the y of the plain step) + y_corr[h, p]
+ *
+ *   state_format : SSDQ_STATE_F32, SSDQ_STATE_F16 or SSDQ_STATE_I8 (else SSDQ_ERROR_INVALID_VALUE)
+ *   state        : (batch, nheads, headdim, dstate) fp32, binary16 or int8 codes, read and written
+ *   state_scale  : (batch, nheads, headdim) fp32 row scales for SSDQ_STATE_I8, read and written;
+ *                  ignored (may be NULL) for the other formats
+ *   y_corr       : (nheads, headdim) fp32, device, 16-byte aligned (NULL: SSDQ_ERROR_INVALID_VALUE)
+ * The state does not depend on y_corr.
+ */
+ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float* state_scale, const int8_t* x,
+                                        const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
+                                        const float* C_scale, const float* dt, const float* A, const float* D,
+                                        const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                                        int32_t dstate, int32_t ngroups, hipStream_t stream);
 
 /*
  * Front end of the SSD block, fused with the static quantizer: the causal convolution that the

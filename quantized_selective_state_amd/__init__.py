@@ -65,6 +65,11 @@ lib.ssdq_frontend_step.argtypes = [_P, _P, _P, _P, _i32] + [_P] * 9 + [_i32] * 5
 lib.ssdq_frontend_step.restype = ctypes.c_int
 lib.ssdq_state_update_i8.argtypes = [_P] * 12 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_i8.restype = ctypes.c_int
+lib.ssdq_chunk_scan_corrected.argtypes = [_P] * 13 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
+lib.ssdq_chunk_scan_corrected.restype = ctypes.c_int
+lib.ssdq_state_update_corrected.argtypes = [_i32] + [_P] * 13 + [_i32, _i32, _i32, _i32, _i32, _P]
+lib.ssdq_state_update_corrected.restype = ctypes.c_int
+STATE_F32, STATE_F16, STATE_I8 = 0, 1, 2
 lib.ssdq_chunk_scan_noalloc.argtypes = [_P] * 12 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_chunk_scan_noalloc.restype = ctypes.c_int
 lib.ssdq_chunk_scan_noalloc_scratch_size.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32]
@@ -203,7 +208,7 @@ class ScanBuffers:
     """Validated arguments of one prefill call, reusable across calls (no allocation per call)."""
 
     def __init__(self, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk=256, y=None,
-                 h_final=None, workspace=None, want_final_state=True):
+                 h_final=None, workspace=None, want_final_state=True, y_corr=None):
         if x.dim() != 4 or B.dim() != 4:
             raise ValueError("x must be (batch, seqlen, nheads, headdim) and B, C (batch, seqlen, ngroups, dstate)")
         b, L, H, P = x.shape
@@ -219,6 +224,7 @@ class ScanBuffers:
         _need(A, "A", torch.float32, (H,), dev)
         _need(D, "D", torch.float32, (H,), dev, optional=True)
         _need(h0, "h0", torch.float32, (b, H, P, N), dev, optional=True)
+        _need(y_corr, "y_corr", torch.float32, (H, P), dev, optional=True)
         if y is None:
             y = torch.empty((b, L, H, P), dtype=torch.float16, device=dev)
         _need(y, "y", torch.float16, (b, L, H, P), dev)
@@ -232,6 +238,7 @@ class ScanBuffers:
             workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
         _need(workspace, "workspace", torch.uint8, None, dev)
         self.tensors = (x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final)
+        self.y_corr = y_corr
         self.dims = (b, L, H, P, N, G, chunk)
         self.workspace = workspace
         self.device = dev
@@ -240,9 +247,17 @@ class ScanBuffers:
             _ptr(workspace), workspace.numel()]
 
     def run(self) -> None:
-        _check(lib.ssdq_chunk_scan(*self._args, _stream(self.device)), "ssdq_chunk_scan")
+        """The whole scan (ssdq_chunk_scan, or ssdq_chunk_scan_corrected with an output correction)."""
+        if self.y_corr is not None:
+            a = self._args
+            _check(lib.ssdq_chunk_scan_corrected(*a[:9], _ptr(self.y_corr), *a[9:], _stream(self.device)),
+                   "ssdq_chunk_scan_corrected")
+        else:
+            _check(lib.ssdq_chunk_scan(*self._args, _stream(self.device)), "ssdq_chunk_scan")
 
     def run_stage(self, stage: int) -> None:
+        if self.y_corr is not None:
+            raise ValueError("the stage-level calls have no output correction; use run()")
         _check(lib.ssdq_chunk_scan_stage(stage, *self._args, _stream(self.device)), "ssdq_chunk_scan_stage")
 
     def workspace_views(self) -> dict:
@@ -262,10 +277,11 @@ class ScanBuffers:
 
 
 def chunk_scan(x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, h0=None, chunk=256, y=None, h_final=None,
-               workspace=None, want_final_state=True):
-    """Prefill over INT8 inputs; returns (y fp16 (b,L,H,P), h_final fp32 (b,H,P,N) or None)."""
+               workspace=None, want_final_state=True, y_corr=None):
+    """Prefill over INT8 inputs; returns (y fp16 (b,L,H,P), h_final fp32 (b,H,P,N) or None).  y_corr
+    (H, P) fp32, if given, is the output correction added to every y (ssdq_chunk_scan_corrected)."""
     buf = ScanBuffers(x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, chunk, y, h_final, workspace,
-                      want_final_state)
+                      want_final_state, y_corr)
     buf.run()
     return buf.y, buf.h_final
 
@@ -376,11 +392,13 @@ def frontend_step(conv_state, xbc, conv_w, conv_b, x_scale, B_scale, C_scale, dt
     return x, B, C, dt
 
 
-def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=None, state_scale=None) -> torch.Tensor:
+def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=None, state_scale=None,
+                 y_corr=None) -> torch.Tensor:
     """One decode step; `state` (b,H,P,N) is updated in place; returns y fp16 (b,H,P).  An fp32
     state runs ssdq_state_update, a binary16 (torch.float16) state ssdq_state_update_f16, and an
     int8 state (codes, with its row scales `state_scale` (b,H,P) float32, also updated in place)
-    ssdq_state_update_i8."""
+    ssdq_state_update_i8; with y_corr (H, P) fp32 the step runs ssdq_state_update_corrected and
+    y also receives that output correction."""
     if state.dim() != 4:
         raise ValueError("state must be (batch, nheads, headdim, dstate)")
     b, H, P, N = state.shape
@@ -401,9 +419,17 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     _need(dt, "dt", torch.float32, (b, H), dev)
     _need(A, "A", torch.float32, (H,), dev)
     _need(D, "D", torch.float32, (H,), dev, optional=True)
+    _need(y_corr, "y_corr", torch.float32, (H, P), dev, optional=True)
     if y is None:
         y = torch.empty((b, H, P), dtype=torch.float16, device=dev)
     _need(y, "y", torch.float16, (b, H, P), dev)
+    if y_corr is not None:
+        fmt = {"f32": STATE_F32, "f16": STATE_F16, "i8": STATE_I8}[kind]
+        _check(lib.ssdq_state_update_corrected(fmt, _ptr(state), _ptr(state_scale), _ptr(x), _ptr(x_scale), _ptr(B),
+                                               _ptr(B_scale), _ptr(C), _ptr(C_scale), _ptr(dt), _ptr(A), _ptr(D),
+                                               _ptr(y_corr), _ptr(y), b, H, P, N, G, _stream(dev)),
+               "ssdq_state_update_corrected")
+        return y
     rest = (_ptr(x), _ptr(x_scale), _ptr(B), _ptr(B_scale), _ptr(C), _ptr(C_scale), _ptr(dt), _ptr(A), _ptr(D),
             _ptr(y), b, H, P, N, G, _stream(dev))
     if kind == "i8":

@@ -141,7 +141,7 @@ constexpr int kBTasks = kMaxQ * 8 / kThreads;          // 16-byte B pieces per t
 static_assert(2 * kMaxP * (kMaxN / 32) == kThreads, "two 16-byte carried-state pieces per thread");
 constexpr int kXTasks = kMaxQ * (kMaxP / 16) / kThreads;   // 16-byte x pieces per thread
 struct Prefetch {
-  float acs, dt, hs;
+  float acs, dt, hs, mu;
   v4i cq[2][2];                 // C codes of this lane's two output rows (per pass, K half)
   v4u bq[kBTasks];
   v4u hq[2];                    // two 16-byte pieces of one limb row
@@ -160,6 +160,7 @@ struct Params {
   const float* acs;
   const int8_t* hprev;
   const float* hscale;
+  const float* ycorr;   // (nheads, headdim) output correction, read only by the corrected instance
   _Float16* y;
   int64_t seqlen;
   int nheads, P, N, ngroups, Q, nchunks, nitems;
@@ -183,7 +184,7 @@ struct LaneConst {
 // Buffer resources of one item: base at the item's first element, size up to the end of its
 // last valid row.
 struct ItemRsrc {
-  Rsrc acs, dt, hs, B, H, x, C;
+  Rsrc acs, dt, hs, mu, B, H, x, C;
 };
 
 // One work item's position, as 32-bit row indices into its operands (every index is below
@@ -238,6 +239,7 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a)
   r.acs = make_rsrc(a.acs + wide(p.aseg, uint32_t(a.Q)), uint32_t(a.Q) * 4u);
   r.dt = make_rsrc(a.dt + p.row, (last * uint32_t(a.nheads) + 1u) * 4u);
   r.hs = make_rsrc(a.hscale + wide(p.seg, P), P * 4u);
+  r.mu = make_rsrc(a.ycorr + uint32_t(p.h) * P, a.ycorr ? P * 4u : 0u);
   r.B = make_rsrc(a.B + wide(p.grow, N), last * gn + N);
   r.H = make_rsrc(a.hprev + wide(p.seg, 2u * P * N), 2u * P * N);
   r.x = make_rsrc(a.x + wide(p.row, P), last * uint32_t(a.nheads) * P + P);
@@ -246,7 +248,9 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a)
 }
 
 // Issue the global loads of one item except its x codes (nothing waits here); B and C only when
-// the item starts a new (batch, chunk, group) (bc, block-uniform).
+// the item starts a new (batch, chunk, group) (bc, block-uniform); the head's output correction
+// only in the corrected instance.
+template <bool kCorr>
 __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow, bool bc,
                                          int N, int kg) {
   if (bc) {
@@ -275,7 +279,10 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
     f.acs = buf_loadf(r.acs, lc.acs_off);
     f.dt = buf_loadf(r.dt, lc.dt_off);
   }
-  if (threadIdx.x < kMaxP) f.hs = buf_loadf(r.hs, lc.hs_off);
+  if (threadIdx.x < kMaxP) {
+    f.hs = buf_loadf(r.hs, lc.hs_off);
+    if constexpr (kCorr) f.mu = buf_loadf(r.mu, lc.hs_off);
+  }
 #pragma unroll
   for (int k = 0; k < 2; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
 }
@@ -286,6 +293,9 @@ __device__ __forceinline__ void prefetch_x(Prefetch& f, const ItemRsrc& r, const
   for (int k = 0; k < kXTasks; ++k) f.xq[k] = buf_load16(r.x, lc.x_off[k]);
 }
 
+// kCorr: y also receives the per-(head, channel) output correction ycorr[h, p] (SSDi8's mean
+// correction), added in the epilogue.
+template <bool kCorr>
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // Per-item tiles in two buffers (item k of the block in buffer k % 2): a wave commits the next
   // item into the other buffer as soon as its own passes are done, and one barrier per item
@@ -294,6 +304,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   __shared__ __attribute__((aligned(16))) _Float16 xs_buf[2][kMaxQ * kMaxP];
   __shared__ __attribute__((aligned(16))) int8_t Hq_buf[2][2 * kHPlane];
   __shared__ __attribute__((aligned(16))) float hsc_buf[2][kMaxP];
+  __shared__ __attribute__((aligned(16))) float mu_buf[2][kCorr ? kMaxP : 4];
   __shared__ __attribute__((aligned(16))) float acs2_buf[2][kMaxQ];   // Acs * log2(e)
   __shared__ __attribute__((aligned(16))) float dts_buf[2][kMaxQ];    // dt (0 past the sequence end)
   __shared__ float red_buf[2][kWaves];
@@ -385,7 +396,10 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       const float dm = tid < kMaxQ ? wave_max(f.dt) : 0.f;   // dt >= 0; waves 4..7 load none
       if (lane == 0) red_buf[bf][wave] = dm;
     }
-    if (tid < kMaxP) hsc_buf[bf][tid] = f.hs;
+    if (tid < kMaxP) {
+      hsc_buf[bf][tid] = f.hs;
+      if constexpr (kCorr) mu_buf[bf][tid] = f.mu;
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(Hq_buf[bf] + lc.h_lds[q]) = f.hq[q];
 #pragma unroll
@@ -430,7 +444,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // one trip, so the commit's wait for the prefetched data counts back over a fixed number of
   // stores (unconditional buffer stores) and never waits for the stores themselves.
   ItemPos cur = item_at(it, a);
-  prefetch(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
+  prefetch<kCorr>(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
   prefetch_x(f, item_rsrc(cur, a), lc);
   commit(0);
   commit_b();
@@ -456,7 +470,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     bool nxt_bc = false;
     if (it + 1 < it_end) nxt_bc = item_next(nxt, it, a);
     const ItemRsrc nrs = item_rsrc(nxt, a);
-    prefetch(f, nrs, lc, xrow, nxt_bc, N, kg);
+    prefetch<kCorr>(f, nrs, lc, xrow, nxt_bc, N, kg);
     __builtin_amdgcn_sched_barrier(0);
 
     // this trip's view of the per-item tiles
@@ -464,6 +478,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const int8_t* const Hq = Hq_buf[buf];
     const LDSP int8_t* const hqb[2] = {lds_base(Hq + hq_lane[0]), lds_base(Hq + hq_lane[1])};
     const LDSP float* const hsb = lds_base(hsc_buf[buf] + 4 * kg);   // + 16 pt: this lane's row scales
+    const LDSP float* const mub = lds_base(mu_buf[buf] + (kCorr ? 4 * kg : 0));   // + 16 pt: its corrections
     const float* const acs2 = acs2_buf[buf];
     const float* const dts = dts_buf[buf];
     const float* const red = red_buf[buf];
@@ -686,8 +701,15 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         v4h out;
+        if constexpr (kCorr) {
+          const float4 m4 = lds_f4(mub, 16 * pt);
+          const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(yf[pt][i], c_f, yd[pt][i] * s_in));
+          for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(yf[pt][i], c_f, fmaf(yd[pt][i], s_in, mv[i])));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(yf[pt][i], c_f, yd[pt][i] * s_in));
+        }
         o4[pt] = __builtin_bit_cast(v2u, out);
       }
       // Channel tiles pt and pt + 1 trade halves between 16-lane rows (the odd rows of the first
@@ -733,7 +755,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 }  // namespace
 
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
-  Params p{a.x, a.x_scale, a.B, a.B_scale, a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.y,
+  Params p{a.x, a.x_scale, a.B, a.B_scale, a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.ycorr, a.y,
            s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.nchunks,
            s.batch * s.nchunks * s.nheads,
            make_fastdiv(uint32_t(s.nheads)), make_fastdiv(uint32_t(s.nchunks)),
@@ -744,7 +766,10 @@ hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_
                                               hipSuccess)
     cus = 256;
   const int nblocks = p.nitems < cus ? p.nitems : cus;
-  hipLaunchKernelGGL(chunk_output_kernel, dim3(nblocks), dim3(kThreads), 0, stream, p);
+  if (p.ycorr)
+    hipLaunchKernelGGL(chunk_output_kernel<true>, dim3(nblocks), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(chunk_output_kernel<false>, dim3(nblocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

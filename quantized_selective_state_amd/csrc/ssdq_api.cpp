@@ -75,6 +75,7 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   a->dt = dt;
   a->A = A;
   a->D = D;
+  a->ycorr = nullptr;
   a->h0 = h0;
   a->y = static_cast<_Float16*>(y);
   a->h_final = h_final;
@@ -218,6 +219,27 @@ ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t*
   return SSDQ_SUCCESS;
 }
 
+ssdq_status ssdq_chunk_scan_corrected(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                      const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                      const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
+                                      int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                      int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (!ok_ptr(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  ScanShape s;
+  ScanArgs a;
+  const ssdq_status st = check_scan_args(0, x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final, batch,
+                                         seqlen, nheads, headdim, dstate, ngroups, chunk, workspace,
+                                         workspace_bytes, &s, &a);
+  if (st != SSDQ_SUCCESS) return st;
+  a.ycorr = y_corr;
+  for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
+    const ssdq_status r = run_stage(stage, s, a, stream);
+    if (r != SSDQ_SUCCESS) return r;
+  }
+  return SSDQ_SUCCESS;
+}
+
 size_t ssdq_chunk_scan_noalloc_scratch_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                             int32_t dstate, int32_t chunk) {
   ScanShape s;
@@ -281,7 +303,7 @@ ssdq_status ssdq_state_update(float* state, const int8_t* x, const float* x_scal
   const ssdq_status st =
       check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
   if (st != SSDQ_SUCCESS) return st;
-  const hipError_t e = launch_state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
+  const hipError_t e = launch_state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, nullptr,
                                            static_cast<_Float16*>(y), batch, nheads, headdim, dstate, ngroups,
                                            stream);
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
@@ -295,8 +317,8 @@ ssdq_status ssdq_state_update_f16(void* state, const int8_t* x, const float* x_s
       check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
   if (st != SSDQ_SUCCESS) return st;
   const hipError_t e = launch_state_update_f16(static_cast<uint16_t*>(state), x, x_scale, B, B_scale, C, C_scale,
-                                               dt, A, D, static_cast<_Float16*>(y), batch, nheads, headdim, dstate,
-                                               ngroups, stream);
+                                               dt, A, D, nullptr, static_cast<_Float16*>(y), batch, nheads, headdim,
+                                               dstate, ngroups, stream);
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
@@ -310,8 +332,34 @@ ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t
       check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
   if (st != SSDQ_SUCCESS) return st;
   const hipError_t e = launch_state_update_i8(state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
-                                              static_cast<_Float16*>(y), batch, nheads, headdim, dstate, ngroups,
-                                              stream);
+                                              nullptr, static_cast<_Float16*>(y), batch, nheads, headdim, dstate,
+                                              ngroups, stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
+ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float* state_scale, const int8_t* x,
+                                        const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
+                                        const float* C_scale, const float* dt, const float* A, const float* D,
+                                        const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                                        int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  if (!ok_ptr(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  if (state_format != SSDQ_STATE_F32 && state_format != SSDQ_STATE_F16 && state_format != SSDQ_STATE_I8)
+    return SSDQ_ERROR_INVALID_VALUE;
+  if (state_format == SSDQ_STATE_I8 && !ok_ptr(state_scale)) return SSDQ_ERROR_INVALID_VALUE;
+  const ssdq_status st =
+      check_decode(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, dstate, ngroups);
+  if (st != SSDQ_SUCCESS) return st;
+  _Float16* yo = static_cast<_Float16*>(y);
+  hipError_t e;
+  if (state_format == SSDQ_STATE_F32)
+    e = launch_state_update(static_cast<float*>(state), x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, yo,
+                            batch, nheads, headdim, dstate, ngroups, stream);
+  else if (state_format == SSDQ_STATE_F16)
+    e = launch_state_update_f16(static_cast<uint16_t*>(state), x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr,
+                                yo, batch, nheads, headdim, dstate, ngroups, stream);
+  else
+    e = launch_state_update_i8(static_cast<int8_t*>(state), state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
+                               y_corr, yo, batch, nheads, headdim, dstate, ngroups, stream);
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 

@@ -59,6 +59,7 @@ struct ScanArgs {
   const float* dt;
   const float* A;
   const float* D;
+  const float* ycorr;   // (nheads, headdim) fp32 output correction or nullptr
   const float* h0;
   _Float16* y;
   float* h_final;
@@ -90,17 +91,18 @@ hipError_t launch_frontend_step(uint16_t* conv_state, const uint16_t* xbc, const
                                 int32_t ngroups, hipStream_t stream);
 hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
-                                  const float* dt, const float* A, const float* D, _Float16* y, int32_t batch,
-                                  int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                  const float* dt, const float* A, const float* D, const float* ycorr, _Float16* y,
+                                  int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                                   hipStream_t stream);
 hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                    const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
-                                   const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
-                                   int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+                                   const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
+                                   int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                   hipStream_t stream);
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
-                               const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
-                               int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+                               const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
+                               int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------
 // device helpers

@@ -44,7 +44,8 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
     const float* __restrict__ C_scale, const float* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads, int32_t headdim, int32_t ngroups) {
+    const float* __restrict__ D, const float* __restrict__ ycorr, _Float16* __restrict__ y, int32_t nheads,
+    int32_t headdim, int32_t ngroups) {
   constexpr int kLanesPerRow = N / 4;
   constexpr int kRows = kThreads / kLanesPerRow;   // rows per pass
   constexpr int kPasses = 64 / kRows;              // headdim <= 64
@@ -94,7 +95,8 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     if (p < P) __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(st + int64_t(p) * N + 4 * nq));
     float part = ch4[0] * v[0] + ch4[1] * v[1] + ch4[2] * v[2] + ch4[3] * v[3];
     part = group_sum_to_last_lane<kLanesPerRow>(part);
-    if (p < P && nq == kLanesPerRow - 1) y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp);
+    if (p < P && nq == kLanesPerRow - 1)
+      y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp + (ycorr ? ycorr[h * P + p] : 0.f));
   }
 }
 
@@ -108,7 +110,8 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
     uint16_t* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
     const float* __restrict__ C_scale, const float* __restrict__ dt, const float* __restrict__ A,
-    const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads, int32_t headdim, int32_t ngroups) {
+    const float* __restrict__ D, const float* __restrict__ ycorr, _Float16* __restrict__ y, int32_t nheads,
+    int32_t headdim, int32_t ngroups) {
   constexpr int kLanesPerRow = N / 8;               // 16 (N = 128) or 8 (N = 64)
   constexpr int kRows = kThreads / kLanesPerRow;    // rows per pass
   constexpr int kPasses = 64 / kRows;               // headdim <= 64
@@ -169,7 +172,7 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) part = fmaf(ch8[i], v[i], part);
     part = group_sum<kLanesPerRow>(part);
-    if (p < P && nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp);
+    if (p < P && nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp + (ycorr ? ycorr[h * P + p] : 0.f));
   }
 }
 
@@ -194,8 +197,8 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     int8_t* __restrict__ state, float* __restrict__ state_scale, const int8_t* __restrict__ x,
     const float* __restrict__ x_scale, const int8_t* __restrict__ Bm, const float* __restrict__ B_scale,
     const int8_t* __restrict__ Cm, const float* __restrict__ C_scale, const float* __restrict__ dt,
-    const float* __restrict__ A, const float* __restrict__ D, _Float16* __restrict__ y, int32_t nheads,
-    int32_t headdim, int32_t ngroups) {
+    const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ ycorr,
+    _Float16* __restrict__ y, int32_t nheads, int32_t headdim, int32_t ngroups) {
   constexpr int kLanesPerRow = N / 16;                 // 8 (N = 128) or 4 (N = 64)
   constexpr int kRows = kI8Threads / kLanesPerRow;     // rows per pass: 16 or 32
   constexpr int kPasses = (64 + kRows - 1) / kRows;    // headdim <= 64
@@ -290,7 +293,7 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     part = group_sum<kLanesPerRow>(part);
     if (p < P && nq == 0) {
       ss[p] = s;
-      y[int64_t(bh) * P + p] = _Float16(fmaf(sC, part, Dsx * xp));
+      y[int64_t(bh) * P + p] = _Float16(fmaf(sC, part, Dsx * xp) + (ycorr ? ycorr[h * P + p] : 0.f));
     }
   }
 }
@@ -298,11 +301,11 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
 template <int N>
 hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
                     const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
-                    _Float16* y, int32_t batch, int32_t nheads, int32_t headdim, int32_t ngroups,
+                    const float* ycorr, _Float16* y, int32_t batch, int32_t nheads, int32_t headdim, int32_t ngroups,
                     hipStream_t stream) {
   const int nblocks = batch * nheads;
   hipLaunchKernelGGL((state_update_kernel<N>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
-                     B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+                     B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }
 
@@ -310,41 +313,42 @@ hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const i
 
 hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                    const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
-                                   const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
-                                   int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+                                   const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
+                                   int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                   hipStream_t stream) {
   const int nblocks = batch * nheads;
   if (dstate == 128)
     hipLaunchKernelGGL((state_update_f16_kernel<128>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
-                       B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+                       B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
   else
     hipLaunchKernelGGL((state_update_f16_kernel<64>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
-                       B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+                       B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }
 
 hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
-                                  const float* dt, const float* A, const float* D, _Float16* y, int32_t batch,
-                                  int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
+                                  const float* dt, const float* A, const float* D, const float* ycorr, _Float16* y,
+                                  int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
                                   hipStream_t stream) {
   const int nblocks = batch * nheads;
   if (dstate == 128)
     hipLaunchKernelGGL((state_update_i8_kernel<128>), dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale,
-                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
   else
     hipLaunchKernelGGL((state_update_i8_kernel<64>), dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale,
-                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, nheads, headdim, ngroups);
+                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }
 
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
-                               const float* A, const float* D, _Float16* y, int32_t batch, int32_t nheads,
-                               int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+                               const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
+                               int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
   if (dstate == 128)
-    return launch_n<128>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, ngroups,
-                         stream);
-  return launch_n<64>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y, batch, nheads, headdim, ngroups,
+    return launch_n<128>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads, headdim,
+                         ngroups, stream);
+  return launch_n<64>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads, headdim, ngroups,
                       stream);
 }
 

@@ -261,3 +261,24 @@ def test_noalloc_validates_before_touching_the_device(lib):
     assert lib.ssdq_chunk_scan_noalloc_scratch_size(b, L, H, Pd, N, Q) == (
         r(4 * b * H * nc * Q) + r(4 * b * nc * H * Pd * N) + r(2 * b * nc * H * Pd * N) + r(4 * b * nc * H * Pd))
     assert lib.ssdq_chunk_scan_noalloc_scratch_size(0, L, H, Pd, N, Q) == 0
+
+
+def test_corrected_calls_validate_on_the_host(lib):
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.ssdq_chunk_scan_corrected.argtypes = [P] * 13 + [i32, i64, i32, i32, i32, i32, i32, P, sz, P]
+    lib.ssdq_state_update_corrected.argtypes = [i32] + [P] * 13 + [i32] * 5 + [P]
+    ptrs = [A16] * 13
+    no_corr = list(ptrs)
+    no_corr[9] = None                                   # y_corr
+    assert lib.ssdq_chunk_scan_corrected(*no_corr, 1, 256, 4, 16, 16, 1, 64, A16, 1 << 30, None) == INVALID
+    assert lib.ssdq_chunk_scan_corrected(*ptrs, 1, 256, 4, 16, 16, 1, 64, A16, 16, None) == WS_SMALL
+    assert lib.ssdq_chunk_scan_corrected(*ptrs, 1, 256, 3, 16, 16, 2, 64, A16, 1 << 30, None) == INVALID
+    dec = [A16] * 13
+    assert lib.ssdq_state_update_corrected(3, *dec, 2, 4, 64, 128, 2, None) == INVALID        # no such format
+    bad = list(dec)
+    bad[11] = None                                      # y_corr
+    assert lib.ssdq_state_update_corrected(0, *bad, 2, 4, 64, 128, 2, None) == INVALID
+    no_scale = list(dec)
+    no_scale[1] = None                                  # state_scale, needed by the 8-bit format only
+    assert lib.ssdq_state_update_corrected(2, *no_scale, 2, 4, 64, 128, 2, None) == INVALID
+    assert lib.ssdq_state_update_corrected(0, *no_scale, 2, 4, 64, 96, 2, None) == UNSUPPORTED

@@ -46,3 +46,26 @@ def test_decode_shapes():
     assert d["x16"].shape == (3, 2, 128, 64)
     assert d["B16"].shape == (3, 2, 8, 128)
     assert d["dt"].shape == (3, 2, 128)
+
+
+def test_percentile_scale_clips_at_the_quantile():
+    rng = np.random.default_rng(3)
+    t = rng.normal(size=(5000, 2, 8)).astype(np.float16)
+    s = workloads.percentile_scale(t, -2, 99.0)
+    a = np.abs(t.astype(np.float32))
+    for h in range(2):
+        q = np.float32(np.percentile(a[:, h, :], 99.0))
+        assert s[h] == q / np.float32(127)
+        assert np.mean(a[:, h, :] > q) <= 0.011              # about 1% saturates
+    assert np.all(workloads.percentile_scale(np.zeros((4, 2, 8), np.float16), -2, 99.0) == 1)
+
+
+def test_calibrated_pair_shares_model_and_scales():
+    shape = workloads.PrefillShape("pair", 2, 64, 4, 16, 32, 2, 64, "outlier_heads", "fixed_bias", 0.1)
+    cal, test = workloads.make_calibrated_pair(shape, 60, x_mean=0.5, x_clip_pct=99.0)
+    for k in ("A", "D", "x_scale", "B_scale", "C_scale"):
+        assert np.array_equal(cal[k], test[k])
+    assert not np.array_equal(cal["x16"], test["x16"]) and cal["h0"] is not None
+    assert np.array_equal(cal["x_scale"], workloads.percentile_scale(cal["x16"], -2, 99.0))
+    # x = m_h (N(0, 1) + 0.5): one-sided on average
+    assert np.mean(test["x16"].astype(np.float32)) > 0.2

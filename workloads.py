@@ -145,6 +145,19 @@ def absmax_scale(t16: np.ndarray, axis_keep: int) -> np.ndarray:
     return s.astype(np.float32)
 
 
+def percentile_scale(t16: np.ndarray, axis_keep: int, q: float) -> np.ndarray:
+    """Static scale per index of `axis_keep` with percentile clipping (the calibration of x the
+    Quamba2 rebuttal compares in Table R9): fp32(the q-th percentile of |t| over the calibration
+    tensor for that index) / 127, or 1 where it is 0.  Values beyond it saturate to +-127."""
+    t = np.abs(t16.astype(np.float32))
+    keep = axis_keep % t.ndim
+    moved = np.moveaxis(t, keep, 0).reshape(t.shape[keep], -1)
+    amax = np.percentile(moved, q, axis=1).astype(np.float32)
+    s = amax / np.float32(127.0)
+    s[amax == 0] = np.float32(1.0)
+    return s.astype(np.float32)
+
+
 def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch: int | None = None,
                  seqlen: int | None = None) -> dict:
     """Seeded prefill inputs.  `batch`/`seqlen` may shrink the test draw (the
@@ -172,6 +185,38 @@ def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch
     return dict(x16=x, B16=B, C16=C, dt=dt, A=params.A, D=params.D, h0=h0,
                 x_scale=sx, B_scale=sB, C_scale=sC,
                 batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=shape.chunk)
+
+
+def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0.0,
+                         x_clip_pct: float | None = None) -> tuple[dict, dict]:
+    """A calibration draw and a test draw of one prefill shape that share the model's per-head
+    properties and the static scales calibrated on the first: (cal, test), each in make_prefill's
+    format.  x = m_h (N(0, 1) + x_mean), so a nonzero x_mean makes the activations one-sided; with
+    x_clip_pct the x scales clip at that percentile of |x| (percentile_scale), else absmax / 127,
+    so the test draw's x codes saturate where it exceeds the calibrated range.  The calibration
+    draw also carries dt (and h0, when the shape has one), so that a scan can be run over it."""
+    k = seed_index
+    b, L, H, P, N, G = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    params = model_params(H, shape.x_dist, shape.dt_dist, 100 + k)
+
+    def draw(seed):
+        rng = _rng(seed)
+        x, B, C = _draw_activations(rng, (b, L), H, P, G, N, params)
+        if x_mean:
+            x = (x.astype(np.float32) + np.float32(x_mean) * params.x_mag.astype(np.float32)[:, None]).astype(np.float16)
+        dt = _draw_dt(rng, (b, L), H, params, shape.dt_dist)
+        h0 = None
+        if shape.h0_std > 0:
+            h0 = rng.standard_normal(size=(b, H, P, N), dtype=np.float32) * np.float32(shape.h0_std)
+        return dict(x16=x, B16=B, C16=C, dt=dt, A=params.A, D=params.D, h0=h0,
+                    batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=shape.chunk)
+
+    cal, test = draw(300 + k), draw(200 + k)
+    sx = absmax_scale(cal["x16"], -2) if x_clip_pct is None else percentile_scale(cal["x16"], -2, x_clip_pct)
+    scales = dict(x_scale=sx, B_scale=absmax_scale(cal["B16"], -2), C_scale=absmax_scale(cal["C16"], -2))
+    cal.update(scales)
+    test.update(scales)
+    return cal, test
 
 
 def make_frontend(shape: PrefillShape | str, seed_index: int | None = None, batch: int | None = None,
