@@ -126,6 +126,8 @@ size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nhe
  *   x  : (batch, seqlen, nheads, headdim) int8      x_scale : [nheads] fp32
  *   B  : (batch, seqlen, ngroups, dstate) int8      B_scale : [ngroups] fp32
  *   C  : (batch, seqlen, ngroups, dstate) int8      C_scale : [ngroups] fp32
+ *   (every scale finite and > 0: the output kernel divides by them, and a zero or non-finite
+ *   scale gives non-finite y; calibration gives a zero-absmax group the scale 1)
  *   dt : (batch, seqlen, nheads) fp32, > 0, already passed through softplus
  *   A  : [nheads] fp32, finite, <= 0          D : [nheads] fp32 or NULL (= 0)
  *   h0 : (batch, nheads, headdim, dstate) fp32 or NULL (= 0)

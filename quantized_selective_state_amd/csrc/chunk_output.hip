@@ -490,13 +490,14 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // |D'| = |D| / (sC sB) 2^-kM <= 2^14, so their sum is a finite fp16.  Clamped so that 2^kM
     // and 2^-kM are exact.
     const float sCB = sC * sB;
-    const float DsCB = Dh / sCB;   // scales are positive: |D| / (sC sB) = |D / (sC sB)|
+    const float DsCB = Dh * __builtin_amdgcn_rcpf(sCB);   // scales are positive: |D| / (sC sB) = |D / (sC sB)|
     const int kM = min(max(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, ceil_log2_pos(fabsf(DsCB)) - 14),
                            -120), 120);
     const float s_in = sx * sCB * exp2i(kM);
     const float fkM = float(kM);
     const float Dp = DsCB * exp2i(-kM);   // D' (0 without D)
-    const float Ek = sC / (256.f * s_in);      // carried-state readout factor, times exp(Acs_l0) per pass
+    // carried-state readout factor sC / (256 s_in) = 2^-(kM + 8) / (sx sB), times exp(Acs_l0) per pass
+    const float Ek = __builtin_amdgcn_rcpf(sx * sB) * exp2i(-kM - 8);
 
     // The lane index is re-materialized per item (an empty asm makes it opaque), so that the
     // per-lane masks below (causal mask, store guards) are recomputed with a few compares
@@ -535,8 +536,9 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
           w.z = __builtin_amdgcn_exp2f(r - a4.z) * d4.z;
           w.w = __builtin_amdgcn_exp2f(r - a4.w) * d4.w;
           *reinterpret_cast<float4*>(&wlw[j]) = w;
-          // compared one by one: an inf weight times dt = 0 (rows past the sequence end) is NaN
-          const bool fin = (w.x < 0x1p100f) & (w.y < 0x1p100f) & (w.z < 0x1p100f) & (w.w < 0x1p100f);
+          // the weights are >= 0, so their sum bounds each; an inf weight times dt = 0 (rows past
+          // the sequence end) is NaN, which fails the comparison as well
+          const bool fin = (w.x + w.y) + (w.z + w.w) < 0x1p100f;
           big = (j >= jdiag) & !fin;
         }
       }
