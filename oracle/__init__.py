@@ -54,9 +54,9 @@ def _load():
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.oracle_quantize_f16.argtypes = [P, P, P, i64, i32, i32]
     lib.oracle_quantize_f16.restype = None
-    lib.oracle_ssd_sequential.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, i32, P, P]
+    lib.oracle_ssd_sequential.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, i32, P, P, i32]
     lib.oracle_ssd_sequential.restype = None
-    lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.oracle_ssd_sequential_state_f16.argtypes = [P] * 10 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, i32]
     lib.oracle_ssd_sequential_state_f16.restype = None
     lib.oracle_round_binary16.argtypes = [P, P, i64]
     lib.oracle_frontend.argtypes = [P, P, P, i32, i32, i64, i32, P, P, P]
@@ -65,14 +65,16 @@ def _load():
     lib.oracle_softplus_dt.restype = None
     lib.oracle_requantize_rows_i8.argtypes = [P, i64, i32, P, P, P]
     lib.oracle_requantize_rows_i8.restype = None
-    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.oracle_ssd_sequential_state_i8.argtypes = [P] * 11 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
     lib.oracle_ssd_sequential_values.argtypes = [P] * 7 + [i32, i64, i32, i32, i32, i32, i32, i32, P, P]
     lib.oracle_ssd_sequential_values.restype = None
     lib.oracle_ssd_sequential_state_i8.restype = None
     lib.oracle_round_binary16.restype = None
     lib.oracle_chunk_cumsum.argtypes = [P, P, i64, i32, i32, i32, i32, P]
     lib.oracle_chunk_cumsum.restype = None
-    lib.oracle_chunk_state.argtypes = [P] * 6 + [i64, i32, i32, i32, i32, i32, i32, i32, P]
+    lib.oracle_chunk_state.argtypes = [P] * 6 + [i64, i32, i32, i32, i32, i32, i32, i32, P, i32]
+    lib.oracle_quantize_f16_per_channel.argtypes = [P, P, P, i64, i32, i32]
+    lib.oracle_quantize_f16_per_channel.restype = None
     lib.oracle_chunk_state.restype = None
     _lib = lib
     return lib
@@ -112,6 +114,21 @@ def quantize(x16: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return q
 
 
+def quantize_per_channel(x16: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Codes of an fp16 tensor (..., K, I) with one scale per (k, i): scale (K, I) (B or C with a
+    scale per (group, state))."""
+    lib = _load()
+    x16 = np.ascontiguousarray(x16, dtype=np.float16)
+    scale = _c(scale, np.float32)
+    nscale, inner = x16.shape[-2], x16.shape[-1]
+    assert scale.shape == (nscale, inner)
+    rows = x16.size // (nscale * inner) if x16.size else 0
+    q = np.empty(x16.shape, dtype=np.int8)
+    if x16.size:
+        lib.oracle_quantize_f16_per_channel(_ptr(x16.view(np.uint16)), _ptr(q), _ptr(scale), rows, nscale, inner)
+    return q
+
+
 def quantize_values(v16: np.ndarray, scale: float) -> np.ndarray:
     """Codes of a flat fp16 array under one scale."""
     v16 = np.ascontiguousarray(v16, dtype=np.float16).reshape(-1, 1, 1)
@@ -124,7 +141,8 @@ def quantize_values(v16: np.ndarray, scale: float) -> np.ndarray:
 
 class Codes:
     """Quantized prefill inputs in the scan's layout; y_corr (H, P) float32 is the optional output
-    correction added to every y."""
+    correction added to every y.  sB and sC are one scale per group (G,) or one per (group,
+    state) (G, N)."""
 
     def __init__(self, qx, sx, qB, sB, qC, sC, dt, A, D=None, h0=None, y_corr=None):
         self.qx = _c(qx, np.int8)
@@ -140,14 +158,20 @@ class Codes:
         assert self.qB.shape == (self.batch, self.L, self.G, self.N) == self.qC.shape
         assert self.dt.shape == (self.batch, self.L, self.H)
         assert self.H % self.G == 0
+        assert self.sB.shape == self.sC.shape and self.sB.shape in ((self.G,), (self.G, self.N))
+        self.per_state = int(self.sB.shape == (self.G, self.N))
+
+
+def _quantize_bc(t16: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    return quantize_per_channel(t16, scale) if np.ndim(scale) == 2 else quantize(t16, scale)
 
 
 def codes_from_inputs(inp: dict) -> Codes:
     """Quantize a workload draw with the oracle's quantizer (with its output correction y_corr,
-    if the draw carries one)."""
+    if the draw carries one; B and C scales per group (G,) or per (group, state) (G, N))."""
     return Codes(quantize(inp["x16"], inp["x_scale"]), inp["x_scale"],
-                 quantize(inp["B16"], inp["B_scale"]), inp["B_scale"],
-                 quantize(inp["C16"], inp["C_scale"]), inp["C_scale"],
+                 _quantize_bc(inp["B16"], inp["B_scale"]), inp["B_scale"],
+                 _quantize_bc(inp["C16"], inp["C_scale"]), inp["C_scale"],
                  inp["dt"], inp["A"], inp.get("D"), inp.get("h0"), inp.get("y_corr"))
 
 
@@ -161,7 +185,7 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
         lib.oracle_ssd_sequential_state_f16(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                             _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
                                             c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
-                                            _ptr(c.y_corr))
+                                            _ptr(c.y_corr), c.per_state)
         return y, hf, None
     bounds = None
     if chunk > 0:
@@ -169,7 +193,7 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
     lib.oracle_ssd_sequential(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                               _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
                               c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
-                              chunk, _ptr(bounds), _ptr(c.y_corr))
+                              chunk, _ptr(bounds), _ptr(c.y_corr), c.per_state)
     return y, hf, bounds
 
 
@@ -244,7 +268,7 @@ def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None, scales_per_step
     lib.oracle_ssd_sequential_state_i8(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                        _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(q0), _ptr(s0),
                                        c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf), _ptr(q),
-                                       _ptr(s), _ptr(u), _ptr(steps), _ptr(c.y_corr))
+                                       _ptr(s), _ptr(u), _ptr(steps), _ptr(c.y_corr), c.per_state)
     if scales_per_step:
         return y, hf, q, s, u, steps
     return y, hf, q, s, u
@@ -358,7 +382,7 @@ def chunk_state(c: Codes, b: int, h: int, chunk: int) -> np.ndarray:
     nc = (c.L + chunk - 1) // chunk
     out = np.empty((nc, c.P, c.N))
     lib.oracle_chunk_state(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.dt), _ptr(c.A),
-                           c.L, c.H, c.P, c.N, c.G, b, h, chunk, _ptr(out))
+                           c.L, c.H, c.P, c.N, c.G, b, h, chunk, _ptr(out), c.per_state)
     return out
 
 
@@ -366,8 +390,8 @@ def decode_as_prefill(dec: dict) -> Codes:
     """The decode workload as one prefill over its steps: the recurrence is the
     same, with the decode state as h0.  Codes come from the oracle quantizer."""
     qx = quantize(dec["x16"], dec["x_scale"])      # (T, b, H, P)
-    qB = quantize(dec["B16"], dec["B_scale"])      # (T, b, G, N)
-    qC = quantize(dec["C16"], dec["C_scale"])
+    qB = _quantize_bc(dec["B16"], dec["B_scale"])      # (T, b, G, N)
+    qC = _quantize_bc(dec["C16"], dec["C_scale"])
     tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))
     return Codes(tr(qx), dec["x_scale"], tr(qB), dec["B_scale"], tr(qC), dec["C_scale"],
                  tr(dec["dt"]), dec["A"], dec["D"], dec["state"])

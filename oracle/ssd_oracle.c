@@ -19,8 +19,9 @@
  *    token (Ternary Mamba, Section 1: h_t = Abar_t h_{t-1} + Bbar_t x_t), with
  *    the zero-order-hold decay Abar_t = exp(dt_t * A_h) and Bbar_t = dt_t * B_t,
  *    and the readout y_t = C_t . h_t + D_h x_t, over the DEQUANTIZED codes
- *    x = s_x[h] q_x, B = s_B[g] q_B, C = s_C[g] q_C (exact in double).
- *    Head h reads group g = h / (H / G).  Optionally records the state at every
+ *    x = s_x[h] q_x, B = s_B[g] q_B, C = s_C[g] q_C (exact in double), or, with scales
+ *    per (group, state) (SSDi8 Table 10: per-P(N) and per-H(G) together), B = s_B[g, n] q_B
+ *    and C = s_C[g, n] q_C.  Head h reads group g = h / (H / G).  Optionally records the state at every
  *    chunk boundary (the state entering chunk c, i.e. after token cQ - 1).
  *
  *  - oracle_ssd_sequential_state_f16: the same recurrence with the state cached
@@ -100,6 +101,18 @@ void oracle_quantize_f16(const uint16_t* x, int8_t* q, const float* scale, int64
       }
 }
 
+/* The same quantizer with one scale per (k, i): q[r, k, i] = quantize(x[r, k, i], scale[k * inner + i])
+ * (B and C with a scale per (group, state), SSDi8 Table 10's per-P(N) axis together with per-H(G)). */
+void oracle_quantize_f16_per_channel(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
+                                     int32_t inner) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int32_t k = 0; k < nscale; ++k)
+      for (int32_t i = 0; i < inner; ++i) {
+        int64_t e = (r * nscale + k) * (int64_t)inner + i;
+        q[e] = quantize_one(x[e], scale[(int64_t)k * inner + i]);
+      }
+}
+
 /* One (b, h) sequence of the recurrence.
  *  qx (batch, L, H, P) int8, qB/qC (batch, L, G, N) int8, dt (batch, L, H),
  *  A[H], D[H] (NULL = 0), h0 (batch, H, P, N) float (NULL = 0).
@@ -172,7 +185,7 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out, int round_state,
                            const int8_t* q0, const float* s0, int8_t* q_out, float* s_out, double* u_last,
-                           float* s_steps, const float* ycorr) {
+                           float* s_steps, const float* ycorr, int32_t bc_per_state) {
   (void)batch;
   const int32_t g = h / (H / G);
   double* S = (double*)calloc((size_t)P * N, sizeof(double));
@@ -201,8 +214,9 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
     const double a = exp(d * Ah);
     for (int32_t p = 0; p < P; ++p) xv[p] = (double)sx[h] * (double)qx[(row * H + h) * P + p];
     for (int32_t n = 0; n < N; ++n) {
-      Bv[n] = (double)sB[g] * (double)qB[(row * G + g) * N + n];
-      Cv[n] = (double)sC[g] * (double)qC[(row * G + g) * N + n];
+      const int32_t k = bc_per_state ? g * N + n : g;   /* scale of state n of group g */
+      Bv[n] = (double)sB[k] * (double)qB[(row * G + g) * N + n];
+      Cv[n] = (double)sC[k] * (double)qC[(row * G + g) * N + n];
     }
     for (int32_t p = 0; p < P; ++p) {
       double* Sp = S + (int64_t)p * N;
@@ -238,9 +252,10 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            const int8_t* qC, const float* sC, const float* dt, const float* A,
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                           double* h_out, int32_t chunk, double* bound_out, const float* ycorr) {
+                           double* h_out, int32_t chunk, double* bound_out, const float* ycorr,
+                           int32_t bc_per_state) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0,
-                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr);
+                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr, bc_per_state);
 }
 
 /* The recurrence with the state cached in binary16 between tokens (h0 is taken as given). */
@@ -248,9 +263,9 @@ void oracle_ssd_sequential_state_f16(const int8_t* qx, const float* sx, const in
                                      const int8_t* qC, const float* sC, const float* dt, const float* A,
                                      const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                                      int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                                     double* h_out, const float* ycorr) {
+                                     double* h_out, const float* ycorr, int32_t bc_per_state) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1,
-                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr);
+                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr, bc_per_state);
 }
 
 /* The recurrence with the state cached as 8-bit codes and one scale per state row between
@@ -263,9 +278,9 @@ void oracle_ssd_sequential_state_i8(const int8_t* qx, const float* sx, const int
                                     const float* D, const int8_t* q0, const float* s0, int32_t batch, int64_t L,
                                     int32_t H, int32_t P, int32_t N, int32_t G, int32_t b, int32_t h,
                                     double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last,
-                                    float* s_steps, const float* ycorr) {
+                                    float* s_steps, const float* ycorr, int32_t bc_per_state) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, NULL, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 2,
-                 q0, s0, q_out, s_out, u_last, s_steps, ycorr);
+                 q0, s0, q_out, s_out, u_last, s_steps, ycorr, bc_per_state);
 }
 
 /* The same recurrence over real-valued inputs, for one (b, h): x (batch, L, H, P), B and C
@@ -366,7 +381,7 @@ void oracle_chunk_cumsum(const float* dt, const float* A, int64_t L, int32_t H, 
  * where `last` is the chunk's last valid token. */
 void oracle_chunk_state(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
                         const float* dt, const float* A, int64_t L, int32_t H, int32_t P, int32_t N,
-                        int32_t G, int32_t b, int32_t h, int32_t chunk, double* out) {
+                        int32_t G, int32_t b, int32_t h, int32_t chunk, double* out, int32_t bc_per_state) {
   const int32_t g = h / (H / G);
   const int64_t nc = (L + chunk - 1) / chunk;
   double* acs = (double*)malloc(sizeof(double) * nc * chunk);
@@ -383,7 +398,7 @@ void oracle_chunk_state(const int8_t* qx, const float* sx, const int8_t* qB, con
       for (int32_t p = 0; p < P; ++p) {
         const double xw = w * (double)sx[h] * (double)qx[(row * H + h) * P + p];
         for (int32_t n = 0; n < N; ++n)
-          Sc[(int64_t)p * N + n] += xw * (double)sB[g] * (double)qB[(row * G + g) * N + n];
+          Sc[(int64_t)p * N + n] += xw * (double)sB[bc_per_state ? g * N + n : g] * (double)qB[(row * G + g) * N + n];
       }
     }
   }

@@ -23,6 +23,7 @@ PINS = {
     "i8": ["tests/test_oracle_state_i8.py"],
     "fe": ["tests/test_oracle_frontend.py"],
     "corr": ["tests/test_oracle_correction.py"],
+    "pn": ["tests/test_oracle_per_state.py"],
 }
 
 # (name, pin files, text in ssd_oracle.c, replacement)
@@ -50,6 +51,11 @@ MUTANTS = [
      "const double w = exp(last - acs[c * chunk + j]);"),
     ("chunk cumsum restarts wrong", "rec", "for (int32_t j = 0; j < chunk && c * chunk + j < L; ++j) {\n      acc +=",
      "for (int32_t j = 0; j < chunk && c * chunk + j < L; ++j) {\n      acc = 0.0;\n      acc +="),
+    ("per-state scale indexed (n, g)", "pn", "const int32_t k = bc_per_state ? g * N + n : g;",
+     "const int32_t k = bc_per_state ? n * G + g : g;"),
+    ("per-state B scale dropped from the chunk state", "pn", "(double)sB[bc_per_state ? g * N + n : g]", "(double)sB[g]"),
+    ("per-channel quantizer indexed by k only", "pn", "quantize_one(x[e], scale[(int64_t)k * inner + i])",
+     "quantize_one(x[e], scale[k])"),
     ("quantizer ties away from zero", "quant", "float r = rintf(t);", "float r = roundf(t);"),
     ("quantizer by reciprocal multiply", "quant", "volatile float t = v / scale;",
      "volatile float t = v * (1.0f / scale);"),

@@ -69,3 +69,13 @@ def test_calibrated_pair_shares_model_and_scales():
     assert np.array_equal(cal["x_scale"], workloads.percentile_scale(cal["x16"], -2, 99.0))
     # x = m_h (N(0, 1) + 0.5): one-sided on average
     assert np.mean(test["x16"].astype(np.float32)) > 0.2
+
+
+def test_per_state_scales():
+    shape = workloads.PrefillShape("pn", 2, 64, 4, 16, 32, 2, 64, "normal", "fixed_bias", 0.0)
+    cal, test = workloads.make_calibrated_pair(shape, 61, bc_per_state=True, state_spread=1.0)
+    assert cal["B_scale"].shape == (2, 32) and test["C_scale"].shape == (2, 32)
+    amax = np.abs(cal["B16"].astype(np.float32)).max(axis=(0, 1))
+    assert np.array_equal(cal["B_scale"], (amax / np.float32(127)).astype(np.float32))
+    # the state columns carry their own magnitudes: the scales spread well beyond one group's
+    assert cal["B_scale"].max() / cal["B_scale"].min() > 4

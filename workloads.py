@@ -145,6 +145,16 @@ def absmax_scale(t16: np.ndarray, axis_keep: int) -> np.ndarray:
     return s.astype(np.float32)
 
 
+def absmax_scale_per_state(t16: np.ndarray) -> np.ndarray:
+    """Static scale per (group, state) of a B or C calibration tensor (..., G, N): fp32(absmax over
+    the leading axes) / 127, or 1 where it is 0 (SSDi8 Table 10: per-P(N) together with per-H(G))."""
+    t = np.abs(t16.astype(np.float32))
+    amax = t.reshape(-1, t.shape[-2], t.shape[-1]).max(axis=0).astype(np.float32)
+    s = amax / np.float32(127.0)
+    s[amax == 0] = np.float32(1.0)
+    return s.astype(np.float32)
+
+
 def percentile_scale(t16: np.ndarray, axis_keep: int, q: float) -> np.ndarray:
     """Static scale per index of `axis_keep` with percentile clipping (the calibration of x the
     Quamba2 rebuttal compares in Table R9): fp32(the q-th percentile of |t| over the calibration
@@ -188,20 +198,30 @@ def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch
 
 
 def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0.0,
-                         x_clip_pct: float | None = None) -> tuple[dict, dict]:
+                         x_clip_pct: float | None = None, bc_per_state: bool = False,
+                         state_spread: float = 0.0) -> tuple[dict, dict]:
     """A calibration draw and a test draw of one prefill shape that share the model's per-head
     properties and the static scales calibrated on the first: (cal, test), each in make_prefill's
     format.  x = m_h (N(0, 1) + x_mean), so a nonzero x_mean makes the activations one-sided; with
     x_clip_pct the x scales clip at that percentile of |x| (percentile_scale), else absmax / 127,
-    so the test draw's x codes saturate where it exceeds the calibrated range.  The calibration
-    draw also carries dt (and h0, when the shape has one), so that a scan can be run over it."""
+    so the test draw's x codes saturate where it exceeds the calibrated range.  With bc_per_state
+    the B and C scales are one per (group, state) (absmax_scale_per_state); state_spread > 0 gives
+    every state column of B and C its own magnitude exp(N(0, state_spread)) (drawn by the model
+    seed), the case those scales are for.  The calibration draw also carries dt (and h0, when the
+    shape has one), so that a scan can be run over it."""
     k = seed_index
     b, L, H, P, N, G = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
     params = model_params(H, shape.x_dist, shape.dt_dist, 100 + k)
+    col = np.ones((2, G, N), np.float32)
+    if state_spread > 0:
+        col = np.exp(_rng(500 + k).normal(0.0, state_spread, size=(2, G, N))).astype(np.float32)
 
     def draw(seed):
         rng = _rng(seed)
         x, B, C = _draw_activations(rng, (b, L), H, P, G, N, params)
+        if state_spread > 0:
+            B = (B.astype(np.float32) * col[0]).astype(np.float16)
+            C = (C.astype(np.float32) * col[1]).astype(np.float16)
         if x_mean:
             x = (x.astype(np.float32) + np.float32(x_mean) * params.x_mag.astype(np.float32)[:, None]).astype(np.float16)
         dt = _draw_dt(rng, (b, L), H, params, shape.dt_dist)
@@ -213,7 +233,8 @@ def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0
 
     cal, test = draw(300 + k), draw(200 + k)
     sx = absmax_scale(cal["x16"], -2) if x_clip_pct is None else percentile_scale(cal["x16"], -2, x_clip_pct)
-    scales = dict(x_scale=sx, B_scale=absmax_scale(cal["B16"], -2), C_scale=absmax_scale(cal["C16"], -2))
+    bc = absmax_scale_per_state if bc_per_state else (lambda t: absmax_scale(t, -2))
+    scales = dict(x_scale=sx, B_scale=bc(cal["B16"]), C_scale=bc(cal["C16"]))
     cal.update(scales)
     test.update(scales)
     return cal, test
