@@ -95,6 +95,20 @@ typedef struct {
  */
 ssdq_status ssdq_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream);
 
+/*
+ * The static INT8 quantizer with one scale per (k, i) instead of one per k: B or C with a scale per
+ * (group, state), the finer granularity of SSDi8 Table 10 (per-P(N) together with per-H(G)).
+ *
+ *   q[r, k, i] = clamp(round_half_even(float(x[r, k, i]) / scale[k, i]), -127, 127)
+ *
+ *   scale : (nscale, inner) fp32, device (each positive finite)
+ * Arguments, layout, rounding, special values and validation otherwise as ssdq_quantize (B or C
+ * (b, L, G, N): rows = b*L, nscale = G, inner = N, scale (G, N)); codes bit-exact to the
+ * correctly rounded quotient.
+ */
+ssdq_status ssdq_quantize_per_channel(const void* x_f16, int8_t* q, const float* scale, int64_t rows,
+                                      int32_t nscale, int32_t inner, hipStream_t stream);
+
 /* Bytes of workspace ssdq_chunk_scan needs for this shape (host; 0 on invalid shapes).
  * Layout (stable, used by the stage-level tests), with nchunks = ceil(seqlen / chunk) and
  * each region starting at a 256-byte boundary:
@@ -191,6 +205,30 @@ ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x
  * and h_final does not depend on y_corr.
  */
 ssdq_status ssdq_chunk_scan_corrected(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                      const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                      const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
+                                      int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                      int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/*
+ * ssdq_chunk_scan with B and C scales per (group, state) (SSDi8 Table 10: per-P(N) together with
+ * per-H(G)) and an optional output correction:
+ *
+ *   Bhat[b,t,g,n] = B_scale[g, n] B[b,t,g,n],   Chat[b,t,g,n] = C_scale[g, n] C[b,t,g,n]
+ *   (the recurrence and readout of ssdq_chunk_scan over these), plus y_corr[h, p] on every y
+ *
+ *   B_scale, C_scale : (ngroups, dstate) fp32, device, each finite and > 0
+ *   y_corr           : (nheads, headdim) fp32 or NULL (no correction)
+ * Everything else as ssdq_chunk_scan, except:
+ *  - C.B^T over the per-state scales runs on the INT8 matrix cores with the product
+ *    B_scale C_scale of each state folded into the B codes as a 16-bit fixed-point number (two
+ *    INT8 limbs) relative to the group's largest product: each term of the sum carries at most
+ *    2^-9 of that largest product times |C code|, well inside the stated y accuracy;
+ *  - the workspace regions of the chunk states and the carried state hold those states times
+ *    C_scale[g, n] of each state column (h_final is unscaled).
+ */
+ssdq_status ssdq_chunk_scan_per_state(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
                                       const int8_t* C, const float* C_scale, const float* dt, const float* A,
                                       const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
                                       int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
@@ -315,6 +353,19 @@ typedef enum {
  * The state does not depend on y_corr.
  */
 ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float* state_scale, const int8_t* x,
+                                        const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
+                                        const float* C_scale, const float* dt, const float* A, const float* D,
+                                        const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                                        int32_t dstate, int32_t ngroups, hipStream_t stream);
+
+/*
+ * The decode step of ssdq_state_update_corrected with B and C scales per (group, state):
+ * B_scale, C_scale (ngroups, dstate) fp32; y_corr (nheads, headdim) fp32 or NULL (no correction).
+ * Formats, arguments, layouts and validation otherwise as ssdq_state_update_corrected.  (On the
+ * 8-bit cached state, y is then summed in fp32 over the per-state C values instead of by integer
+ * dot products.)
+ */
+ssdq_status ssdq_state_update_per_state(int32_t state_format, void* state, float* state_scale, const int8_t* x,
                                         const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
                                         const float* C_scale, const float* dt, const float* A, const float* D,
                                         const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,

@@ -66,6 +66,12 @@ lib.ssdq_frontend_step.restype = ctypes.c_int
 lib.ssdq_state_update_i8.argtypes = [_P] * 12 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_i8.restype = ctypes.c_int
 lib.ssdq_chunk_scan_corrected.argtypes = [_P] * 13 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
+lib.ssdq_chunk_scan_per_state.argtypes = [_P] * 13 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
+lib.ssdq_chunk_scan_per_state.restype = ctypes.c_int
+lib.ssdq_state_update_per_state.argtypes = [_i32] + [_P] * 13 + [_i32, _i32, _i32, _i32, _i32, _P]
+lib.ssdq_state_update_per_state.restype = ctypes.c_int
+lib.ssdq_quantize_per_channel.argtypes = [_P, _P, _P, _i64, _i32, _i32, _P]
+lib.ssdq_quantize_per_channel.restype = ctypes.c_int
 lib.ssdq_chunk_scan_corrected.restype = ctypes.c_int
 lib.ssdq_state_update_corrected.argtypes = [_i32] + [_P] * 13 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_corrected.restype = ctypes.c_int
@@ -178,7 +184,21 @@ def quantize_batch(pairs, outs=None) -> list[torch.Tensor]:
 
 def quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """INT8 codes of an fp16 tensor (..., S, I) with one fp32 scale per index of the
-    second-to-last axis (heads for x, groups for B and C)."""
+    second-to-last axis (heads for x, groups for B and C), or, with a 2-D scale (S, I), one per
+    (s, i) (B and C with a scale per (group, state): ssdq_quantize_per_channel)."""
+    if scale.dim() == 2:
+        if x.dim() < 2:
+            raise ValueError("x must have at least 2 dimensions (..., nscale, inner)")
+        nscale, inner = x.shape[-2], x.shape[-1]
+        _need(x, "x", torch.float16, None, None)
+        _need(scale, "scale", torch.float32, (nscale, inner), x.device)
+        if out is None:
+            out = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+        _need(out, "out", torch.int8, tuple(x.shape), x.device)
+        rows = x.numel() // (nscale * inner) if x.numel() else 0
+        _check(lib.ssdq_quantize_per_channel(_ptr(x), _ptr(out), _ptr(scale), rows, nscale, inner, _stream(x.device)),
+               "ssdq_quantize_per_channel")
+        return out
     return QuantizeCall(x, scale, out).run()
 
 
@@ -217,9 +237,11 @@ class ScanBuffers:
         _need(x, "x", torch.int8, (b, L, H, P), dev)
         _need(x_scale, "x_scale", torch.float32, (H,), dev)
         _need(B, "B", torch.int8, (b, L, G, N), dev)
-        _need(B_scale, "B_scale", torch.float32, (G,), dev)
+        self.per_state = B_scale.dim() == 2
+        sshape = (G, N) if self.per_state else (G,)
+        _need(B_scale, "B_scale", torch.float32, sshape, dev)
         _need(C, "C", torch.int8, (b, L, G, N), dev)
-        _need(C_scale, "C_scale", torch.float32, (G,), dev)
+        _need(C_scale, "C_scale", torch.float32, sshape, dev)
         _need(dt, "dt", torch.float32, (b, L, H), dev)
         _need(A, "A", torch.float32, (H,), dev)
         _need(D, "D", torch.float32, (H,), dev, optional=True)
@@ -248,16 +270,19 @@ class ScanBuffers:
 
     def run(self) -> None:
         """The whole scan (ssdq_chunk_scan, or ssdq_chunk_scan_corrected with an output correction)."""
-        if self.y_corr is not None:
-            a = self._args
+        a = self._args
+        if self.per_state:
+            _check(lib.ssdq_chunk_scan_per_state(*a[:9], _ptr(self.y_corr), *a[9:], _stream(self.device)),
+                   "ssdq_chunk_scan_per_state")
+        elif self.y_corr is not None:
             _check(lib.ssdq_chunk_scan_corrected(*a[:9], _ptr(self.y_corr), *a[9:], _stream(self.device)),
                    "ssdq_chunk_scan_corrected")
         else:
             _check(lib.ssdq_chunk_scan(*self._args, _stream(self.device)), "ssdq_chunk_scan")
 
     def run_stage(self, stage: int) -> None:
-        if self.y_corr is not None:
-            raise ValueError("the stage-level calls have no output correction; use run()")
+        if self.y_corr is not None or self.per_state:
+            raise ValueError("the stage-level calls have neither output correction nor per-state scales; use run()")
         _check(lib.ssdq_chunk_scan_stage(stage, *self._args, _stream(self.device)), "ssdq_chunk_scan_stage")
 
     def workspace_views(self) -> dict:
@@ -398,7 +423,8 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     state runs ssdq_state_update, a binary16 (torch.float16) state ssdq_state_update_f16, and an
     int8 state (codes, with its row scales `state_scale` (b,H,P) float32, also updated in place)
     ssdq_state_update_i8; with y_corr (H, P) fp32 the step runs ssdq_state_update_corrected and
-    y also receives that output correction."""
+    y also receives that output correction; with B and C scales per (group, state) (G, N) it runs
+    ssdq_state_update_per_state (y_corr optional)."""
     if state.dim() != 4:
         raise ValueError("state must be (batch, nheads, headdim, dstate)")
     b, H, P, N = state.shape
@@ -410,12 +436,14 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
         _need(state_scale, "state_scale", torch.float32, (b, H, P), dev)
     elif state_scale is not None:
         raise ValueError("state_scale goes with an int8 state only")
+    per_state = B_scale.dim() == 2
+    sshape = (G, N) if per_state else (G,)
     _need(x, "x", torch.int8, (b, H, P), dev)
     _need(x_scale, "x_scale", torch.float32, (H,), dev)
     _need(B, "B", torch.int8, (b, G, N), dev)
-    _need(B_scale, "B_scale", torch.float32, (G,), dev)
+    _need(B_scale, "B_scale", torch.float32, sshape, dev)
     _need(C, "C", torch.int8, (b, G, N), dev)
-    _need(C_scale, "C_scale", torch.float32, (G,), dev)
+    _need(C_scale, "C_scale", torch.float32, sshape, dev)
     _need(dt, "dt", torch.float32, (b, H), dev)
     _need(A, "A", torch.float32, (H,), dev)
     _need(D, "D", torch.float32, (H,), dev, optional=True)
@@ -423,6 +451,13 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     if y is None:
         y = torch.empty((b, H, P), dtype=torch.float16, device=dev)
     _need(y, "y", torch.float16, (b, H, P), dev)
+    if per_state:
+        fmt = {"f32": STATE_F32, "f16": STATE_F16, "i8": STATE_I8}[kind]
+        _check(lib.ssdq_state_update_per_state(fmt, _ptr(state), _ptr(state_scale), _ptr(x), _ptr(x_scale), _ptr(B),
+                                               _ptr(B_scale), _ptr(C), _ptr(C_scale), _ptr(dt), _ptr(A), _ptr(D),
+                                               _ptr(y_corr), _ptr(y), b, H, P, N, G, _stream(dev)),
+               "ssdq_state_update_per_state")
+        return y
     if y_corr is not None:
         fmt = {"f32": STATE_F32, "f16": STATE_F16, "i8": STATE_I8}[kind]
         _check(lib.ssdq_state_update_corrected(fmt, _ptr(state), _ptr(state_scale), _ptr(x), _ptr(x_scale), _ptr(B),

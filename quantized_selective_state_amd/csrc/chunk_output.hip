@@ -295,20 +295,30 @@ __device__ __forceinline__ void prefetch_x(Prefetch& f, const ItemRsrc& r, const
 
 // kCorr: y also receives the per-(head, channel) output correction ycorr[h, p] (SSDi8's mean
 // correction), added in the epilogue.
-template <bool kCorr>
+// kPS: B and C scales per (group, state) (SSDi8 Table 10: per-P(N) together with per-H(G)).  The
+// carried state then arrives scaled by each state's C scale (the state stages do that), so C.Hprev
+// needs no C scale; C.B^T needs sigma[n] = B_scale[n] C_scale[n] inside the sum over states.  It is
+// carried by the B operand: with 2^s >= max sigma, V[j, n] = rint(256 q_B[j, n] sigma[n] / 2^s)
+// (|V| <= 32512) is split into two INT8 limbs V = 256 hi + lo (hi = floor((V + 128) / 256), so
+// lo is in [-128, 127]), both planes go through the INT8 matrix cores against the C codes, and
+// 256 G_hi + G_lo (exact int32) stands for sum_n sigma[n] q_C q_B to within 2^(s - 9) per term.
+// The second B plane takes the LDS of the second x tile buffer, so this instance commits the next
+// item's x after a barrier instead of into a free buffer.
+template <bool kCorr, bool kPS>
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // Per-item tiles in two buffers (item k of the block in buffer k % 2): a wave commits the next
   // item into the other buffer as soon as its own passes are done, and one barrier per item
   // separates it from the waves still reading the current one.  B changes only with the group
   // and has one buffer.
-  __shared__ __attribute__((aligned(16))) _Float16 xs_buf[2][kMaxQ * kMaxP];
+  __shared__ __attribute__((aligned(16))) _Float16 xs_buf[kPS ? 1 : 2][kMaxQ * kMaxP];
   __shared__ __attribute__((aligned(16))) int8_t Hq_buf[2][2 * kHPlane];
   __shared__ __attribute__((aligned(16))) float hsc_buf[2][kMaxP];
   __shared__ __attribute__((aligned(16))) float mu_buf[2][kCorr ? kMaxP : 4];
   __shared__ __attribute__((aligned(16))) float acs2_buf[2][kMaxQ];   // Acs * log2(e)
   __shared__ __attribute__((aligned(16))) float dts_buf[2][kMaxQ];    // dt (0 past the sequence end)
   __shared__ float red_buf[2][kWaves];
-  __shared__ __attribute__((aligned(16))) int8_t Bs[kMaxQ * kMaxN];
+  __shared__ __attribute__((aligned(16))) int8_t Bs[(kPS ? 2 : 1) * kMaxQ * kMaxN];   // kPS: hi plane, lo plane
+  __shared__ float sig2_s;   // kPS: 2^s >= max_n sigma[n] of the current group
   __shared__ __attribute__((aligned(16))) float wl[kWaves][kMaxQ];
 
   const int tid = threadIdx.x;
@@ -384,6 +394,17 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   Prefetch f{};
   v4i cqs[2][2];   // C codes of this lane's output rows (per pass, K half) for the current group
 
+  // x codes of the prefetched item into x tile buffer xb, as fp16
+  auto commit_x = [&](int xb) {
+#pragma unroll
+    for (int k = 0; k < kXTasks; ++k) {
+      const v4u u = f.xq[k] ^ 0x80808080u;
+      const v4h h0 = codes_to_f16(u[0]), h1 = codes_to_f16(u[1]), h2 = codes_to_f16(u[2]), h3 = codes_to_f16(u[3]);
+      *reinterpret_cast<v8h*>(xs_buf[xb] + lc.x_lds[k]) = v8h{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+      // the second 8 channels: chunk + 1 before the swizzle
+      *reinterpret_cast<v8h*>(xs_buf[xb] + (lc.x_lds[k] ^ 8)) = v8h{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
+    }
+  };
   // ---- commit a prefetched item to LDS.  Rows past the sequence end arrived as zeros;
   // channels past P and states past N hold zeros or values that only meet zeros (the C codes
   // past N are zero, and rows past P are never stored).
@@ -402,33 +423,71 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(Hq_buf[bf] + lc.h_lds[q]) = f.hq[q];
-#pragma unroll
-    for (int k = 0; k < kXTasks; ++k) {
-      const v4u u = f.xq[k] ^ 0x80808080u;
-      const v4h h0 = codes_to_f16(u[0]), h1 = codes_to_f16(u[1]), h2 = codes_to_f16(u[2]), h3 = codes_to_f16(u[3]);
-      *reinterpret_cast<v8h*>(xs_buf[bf] + lc.x_lds[k]) = v8h{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-      // the second 8 channels: chunk + 1 before the swizzle
-      *reinterpret_cast<v8h*>(xs_buf[bf] + (lc.x_lds[k] ^ 8)) = v8h{h2[0], h2[1], h2[2], h2[3], h3[0], h3[1], h3[2], h3[3]};
-    }
+    if constexpr (!kPS) commit_x(bf);
   };
-  // B of a new group (its prefetch arrived with the item's); written while no wave reads B
-  auto commit_b = [&] {
-    {
-      // B goes to LDS in the same state order as the carried state and the C operand: in a
-      // full 64-state block, dword q of natural piece t (states 16 t + 4 q ..) lands at dword t
-      // of piece q (the 16-byte-chunk swizzle keeps the dword position)
-      const int t = tid & 3;                             // piece within its 64-state block
-      const bool full = 64 * ((tid >> 2) & 1) + 64 <= N;   // that block is full
+  // B of a new group (its prefetch arrived with the item's); written while no wave reads B.
+  // kPS: the two limb planes of V = rint(256 q_B sigma[n] / 2^s); this thread's pieces all hold
+  // states 16 (tid % 8) .. + 15, and the 8 threads tid % 8 = 0..7 together cover the 128 states,
+  // so 2^s is an 8-lane maximum
+  auto commit_b = [&](int grp) {
+    // B goes to LDS in the same state order as the carried state and the C operand: in a full
+    // 64-state block, dword q of natural piece t (states 16 t + 4 q ..) lands at dword t of
+    // piece q (the 16-byte-chunk swizzle keeps the dword position)
+    const int t = tid & 3;                             // piece within its 64-state block
+    const bool full = 64 * ((tid >> 2) & 1) + 64 <= N;   // that block is full
+    auto store_piece = [&](int plane, int k, const v4u& w) {
+      int8_t* const bp = Bs + plane * kMaxQ * kMaxN;
+      if (full) {
 #pragma unroll
-      for (int k = 0; k < kBTasks; ++k) {
-        if (full) {
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(bp + ((lc.b_lds[k] ^ ((t ^ q) << 4)) + 4 * t)) = w[q];
+      } else {
+        *reinterpret_cast<v4u*>(bp + lc.b_lds[k]) = w;
+      }
+    };
+    if constexpr (kPS) {
+      const int sg = tid & 7;
+      const Rsrc rsb = make_rsrc(a.B_scale + grp * N, uint32_t(N) * 4u), rsc = make_rsrc(a.C_scale + grp * N, uint32_t(N) * 4u);
+      float sig[16];
+      float m = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<uint32_t*>(Bs + ((lc.b_lds[k] ^ ((t ^ q) << 4)) + 4 * t)) = f.bq[k][q];
-        } else {
-          *reinterpret_cast<v4u*>(Bs + lc.b_lds[k]) = f.bq[k];
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t o = 16 * sg < N ? uint32_t(16 * sg + 4 * u) * 4u : kOutOfRange;
+        const v4f sb = __builtin_bit_cast(v4f, buf_load16(rsb, o)), sc = __builtin_bit_cast(v4f, buf_load16(rsc, o));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sig[4 * u + i] = sb[i] * sc[i];
+          m = fmaxf(m, sig[4 * u + i]);
         }
       }
+      m = group_max<8>(m);
+      const int s2 = ceil_log2_pos(m);
+      const float r256 = exp2i(8 - s2);   // 256 / 2^s
+      if (tid == 0) sig2_s = exp2i(s2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sig[i] *= r256;   // exact: a power of two
+#pragma unroll
+      for (int k = 0; k < kBTasks; ++k) {
+        v4u hi, lo;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t wh = 0, wl = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int code = int(int8_t((f.bq[k][q] >> (8 * i)) & 0xffu));
+            const int V = __float2int_rn(float(code) * sig[4 * q + i]);
+            const int vh = (V + 128) >> 8;   // floor((V + 128) / 256): V - 256 vh in [-128, 127]
+            wh |= (uint32_t(vh) & 0xffu) << (8 * i);
+            wl |= (uint32_t(V - 256 * vh) & 0xffu) << (8 * i);
+          }
+          hi[q] = wh;
+          lo[q] = wl;
+        }
+        store_piece(0, k, hi);
+        store_piece(1, k, lo);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kBTasks; ++k) store_piece(0, k, f.bq[k]);
     }
   };
   // the C codes of this lane's output rows arrive with a new group's prefetch; they are kept
@@ -447,7 +506,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   prefetch<kCorr>(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
   prefetch_x(f, item_rsrc(cur, a), lc);
   commit(0);
-  commit_b();
+  if constexpr (kPS) commit_x(0);
+  commit_b(cur.g);
   __syncthreads();
   keep_c();
   int buf = 0;   // the current item's buffer
@@ -458,7 +518,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
     // per-item scalars through the scalar cache (read-only data)
     typedef const __attribute__((address_space(4))) float* cfp;
-    const float sx = *cfp(a.x_scale + hu), sB = *cfp(a.B_scale + gu), sC = *cfp(a.C_scale + gu);
+    const float sx = *cfp(a.x_scale + hu);
+    const float sB = kPS ? 1.f : *cfp(a.B_scale + gu), sC = kPS ? 1.f : *cfp(a.C_scale + gu);
     const float Dh = a.D ? *cfp(a.D + hu) : 0.f;
     const uint32_t yrow = uint32_t(a.nheads * P);
     const Rsrc ry = make_rsrc(a.y + wide(cur.row, uint32_t(P)), (uint32_t(len - 1) * yrow + uint32_t(P)) * 2u);
@@ -474,7 +535,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // this trip's view of the per-item tiles
-    const _Float16* const xs = xs_buf[buf];
+    const _Float16* const xs = xs_buf[kPS ? 0 : buf];
     const int8_t* const Hq = Hq_buf[buf];
     const LDSP int8_t* const hqb[2] = {lds_base(Hq + hq_lane[0]), lds_base(Hq + hq_lane[1])};
     const LDSP float* const hsb = lds_base(hsc_buf[buf] + 4 * kg);   // + 16 pt: this lane's row scales
@@ -489,15 +550,18 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     // |M'| <= N 127^2 dtmax 2^-kM <= 2^15 and the D term folded into its diagonal within
     // |D'| = |D| / (sC sB) 2^-kM <= 2^14, so their sum is a finite fp16.  Clamped so that 2^kM
     // and 2^-kM are exact.
-    const float sCB = sC * sB;
+    // (kPS: the C.B^T entries are 256 G_hi + G_lo in units of 2^s / 256, |.| <= N 127 32512)
+    const float sCB = kPS ? sig2_s * (1.f / 256.f) : sC * sB;
     const float DsCB = Dh * __builtin_amdgcn_rcpf(sCB);   // scales are positive: |D| / (sC sB) = |D / (sC sB)|
-    const int kM = min(max(max(ceil_log2_pos(float(N) * 16129.f * dtmax) - 15, ceil_log2_pos(fabsf(DsCB)) - 14),
+    const int kM = min(max(max(ceil_log2_pos(float(N) * (kPS ? 127.f * 32512.f : 16129.f) * dtmax) - 15,
+                               ceil_log2_pos(fabsf(DsCB)) - 14),
                            -120), 120);
     const float s_in = sx * sCB * exp2i(kM);
     const float fkM = float(kM);
     const float Dp = DsCB * exp2i(-kM);   // D' (0 without D)
-    // carried-state readout factor sC / (256 s_in) = 2^-(kM + 8) / (sx sB), times exp(Acs_l0) per pass
-    const float Ek = __builtin_amdgcn_rcpf(sx * sB) * exp2i(-kM - 8);
+    // carried-state readout factor sC / (256 s_in) = 2^-(kM + 8) / (sx sB), times exp(Acs_l0) per
+    // pass (kPS: the carried state already holds the C scales, so 1 / (256 s_in))
+    const float Ek = __builtin_amdgcn_rcpf(kPS ? sx * sCB : sx * sB) * exp2i(-kM - 8);
 
     // The lane index is re-materialized per item (an empty asm makes it opaque), so that the
     // per-lane masks below (causal mask, store guards) are recomputed with a few compares
@@ -572,6 +636,24 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         for (int i = 0; i < 4; ++i) yf[pt][i] = float((yo1[pt][i] << 8) + yo2[pt][i]) * (E * hv[i]);
       }
 
+      // G^T of the 16 tokens from jj against this pass's rows (kPS: 256 G_hi + G_lo of the two
+      // B limb planes; the lo plane lies one plane past the hi plane)
+      auto cbt = [&](int jj) {
+        const v4i b0 = lds_ld<v4i>(bs_lane, jj * kMaxN);
+        const v4i b1 = lds_ld<v4i>(bs_lane2, jj * kMaxN);
+        v4i g = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+        g = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], g, 0, 0, 0);
+        if constexpr (kPS) {
+          const v4i l0 = lds_ld<v4i>(bs_lane, jj * kMaxN + kMaxQ * kMaxN);
+          const v4i l1 = lds_ld<v4i>(bs_lane2, jj * kMaxN + kMaxQ * kMaxN);
+          v4i gl = __builtin_amdgcn_mfma_i32_16x16x64_i8(l0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
+          gl = __builtin_amdgcn_mfma_i32_16x16x64_i8(l1, cq[1], gl, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) g[i] = (g[i] << 8) + gl[i];   // exact: |.| <= 128 127 32512 < 2^31
+        }
+        return g;
+      };
+
       // intra-chunk part, 32 tokens per step: blocks before the diagonal use the factorized decay.
       // G^T for a step on the INT8 matrix cores, then M' = fp16(G w) and y^T += x^T M'^T; two
       // steps at a time with their own G and M' registers, so that the second step's integer
@@ -580,11 +662,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
           const int js = jb + 16 * sb;
-          const v4i b0 = lds_ld<v4i>(bs_lane, js * kMaxN);
-          const v4i b1 = lds_ld<v4i>(bs_lane2, js * kMaxN);
           w4[sb] = lds_f4(wl_lane, js);
-          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
-          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
+          gm[sb] = cbt(js);
         }
       };
       auto mstep = [&](int jb, const v4i (&gm)[2], const float4 (&w4)[2]) {
@@ -633,12 +712,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
         const int j1 = jb + 16;   // sub-block 1 (jdiag <= 224: inside the 256-row tiles)
         v4i gm[2];
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const v4i b0 = lds_ld<v4i>(bs_lane, (sb == 0 ? jb : j1) * kMaxN);
-          const v4i b1 = lds_ld<v4i>(bs_lane2, (sb == 0 ? jb : j1) * kMaxN);
-          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b0, cq[0], v4i{0, 0, 0, 0}, 0, 0, 0);
-          gm[sb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(b1, cq[1], gm[sb], 0, 0, 0);
-        }
+        for (int sb = 0; sb < 2; ++sb) gm[sb] = cbt(sb == 0 ? jb : j1);
         v8h mop;
         if (factored) {
           const float e_l = __builtin_amdgcn_exp2f(a_l - a_m);   // rows l >= m: <= 1
@@ -744,10 +818,13 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     do_pass(row_block(wave, 1), cqs[1]);
     commit(buf ^ 1);   // the other buffer: its last readers passed the previous barrier
     __syncthreads();   // the next item is in LDS, and every wave is done with this one
+    if constexpr (kPS) commit_x(0);   // the single x tile: every wave is done with it now
     if (nxt_bc) {
-      commit_b();
+      commit_b(nxt.g);
       __syncthreads();
       keep_c();
+    } else {
+      if constexpr (kPS) __syncthreads();
     }
     cur = nxt;
     buf ^= 1;
@@ -768,10 +845,17 @@ hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_
                                               hipSuccess)
     cus = 256;
   const int nblocks = p.nitems < cus ? p.nitems : cus;
-  if (p.ycorr)
-    hipLaunchKernelGGL(chunk_output_kernel<true>, dim3(nblocks), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(chunk_output_kernel<false>, dim3(nblocks), dim3(kThreads), 0, stream, p);
+  if (a.bc_per_state) {
+    if (p.ycorr)
+      hipLaunchKernelGGL((chunk_output_kernel<true, true>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((chunk_output_kernel<false, true>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+  } else {
+    if (p.ycorr)
+      hipLaunchKernelGGL((chunk_output_kernel<true, false>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((chunk_output_kernel<false, false>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

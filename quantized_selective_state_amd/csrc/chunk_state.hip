@@ -93,9 +93,9 @@ struct Staged {
 template <int Q>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) chunk_state_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
-    const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ A,
-    float* __restrict__ acs, float* __restrict__ states, int64_t seqlen, int32_t nheads, int32_t headdim,
-    int32_t dstate, int32_t ngroups, int32_t nchunks) {
+    const float* __restrict__ B_scale, const float* __restrict__ C_scale_ps, const float* __restrict__ dt,
+    const float* __restrict__ A, float* __restrict__ acs, float* __restrict__ states, int64_t seqlen, int32_t nheads,
+    int32_t headdim, int32_t dstate, int32_t ngroups, int32_t nchunks) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
   __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
   __shared__ __attribute__((aligned(16))) uint32_t om[Q];   // OM_j
@@ -225,7 +225,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   // ---- epilogue.  D layout of a 16x16 MFMA: lane holds rows 4 (lane/16) + i, column lane % 16.
   // Rows past P and states past N are skipped with wave-uniform tests (P, N multiples of 16).
   if (16 * pt >= P) return;
-  const float post = x_scale[h] * B_scale[g] * exp2i(e);
+  // per group: the B scale of the group; with scales per (group, state) (C_scale_ps non-null) the
+  // state column's B scale times its C scale: the chunk states are then written scaled by the C
+  // scale of each state (the form the carried state takes for the output stage)
+  const float post = x_scale[h] * (C_scale_ps ? 1.f : B_scale[g]) * exp2i(e);
   const float post_lo = post * (1.f / 65536.f);
   // buffer stores: lane offset + row offset (scalar) + state-tile offset (immediate)
   const Rsrc rs = make_rsrc(states + ((int64_t(b) * nchunks + c) * nheads + h) * int64_t(P) * N, uint32_t(P * N) * 4u);
@@ -237,7 +240,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     for (int t = 0; t < kNt; ++t) {
       if (16 * t >= N) break;
       const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];   // exact: |lo| < 2^31
-      const float sv = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+      float sv = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+      if (C_scale_ps) {   // uniform
+        const int n = 16 * t + lcol;
+        sv *= B_scale[g * N + n] * C_scale_ps[g * N + n];
+      }
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sv), rs, lane_off + 64u * t, row_off, 0);
     }
   }
@@ -267,10 +274,16 @@ constexpr int kSWaves = kSThreads / kWave;
 constexpr int kGroup = kSWaves;   // chunks whose weights one prologue prepares (one per wave)
 static_assert(kGroup % 2 == 0, "groups start at even chunks (tile buffer parity)");
 
-template <int Q>
+// kPS: B and C scales per (group, state).  The running state is then kept scaled by the C scale
+// of each state, H_C[p, n] = C_scale[g, n] H[p, n] (h0 scaled on the way in, h_final unscaled on
+// the way out), so that each chunk adds sigma[n] S'[p, n] with sigma = B_scale C_scale and S' the
+// products without the B scale, and the carried state the output stage reads out with the C codes
+// already holds the C scale of its state.
+template <int Q, bool kPS>
 __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(2))) state_scan_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
-    const float* __restrict__ B_scale, const float* __restrict__ dt, const float* __restrict__ A,
+    const float* __restrict__ B_scale, const float* __restrict__ C_scale, const float* __restrict__ dt,
+    const float* __restrict__ A,
     const float* h0, float* h_final, float* __restrict__ acs, int8_t* __restrict__ hprev,
     float* __restrict__ hscale, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
     int32_t ngroups, int32_t nchunks) {
@@ -301,18 +314,29 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int kTok = Q / kWave;              // tokens per lane in a group prologue
   const bool prow = 16 * pt < P;               // this wave's channel tile exists (uniform)
   const uint32_t xrow = uint32_t(nheads * P), brow = uint32_t(ngroups * N);
-  const float sxB = x_scale[h] * B_scale[g];
+  const float sxB = x_scale[h] * (kPS ? 1.f : B_scale[g]);
   const float Ah = A[h];
 
   // ---- running state H[p = 16 pt + lcol][n = 16 (4 kh + t) + 4 kg + i], own tiles t = 0..3
   const int64_t pn = int64_t(P) * N;
   const uint32_t hoff = (uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh + 4 * kg) * 4u;   // bytes
   v4f H[kOwn];
+  v4f sig[kPS ? kOwn : 1];   // per state: B_scale C_scale of this lane's own states
   {
     const Rsrc r0 = make_rsrc(h0 ? h0 + int64_t(bh) * pn : h0, h0 && prow ? uint32_t(pn) * 4u : 0u);
 #pragma unroll
     for (int t = 0; t < kOwn; ++t)
       H[t] = __builtin_bit_cast(v4f, buf_load16(r0, 16 * (kOwn * kh + t) < N ? hoff + 64u * t : kOutOfRange));
+    if constexpr (kPS) {
+      const Rsrc rsb = make_rsrc(B_scale + g * N, uint32_t(N) * 4u), rsc = make_rsrc(C_scale + g * N, uint32_t(N) * 4u);
+#pragma unroll
+      for (int t = 0; t < kOwn; ++t) {
+        const uint32_t o = 16 * (kOwn * kh + t) < N ? uint32_t(64 * kh + 16 * t + 4 * kg) * 4u : kOutOfRange;
+        const v4f sb = __builtin_bit_cast(v4f, buf_load16(rsb, o)), sc = __builtin_bit_cast(v4f, buf_load16(rsc, o));
+        sig[t] = sb * sc;
+        H[t] = H[t] * sc;   // H_C
+      }
+    }
   }
 
   // ---- the x and B codes of chunk c, straight into LDS tile buffer c % 2 (buffer loads to LDS:
@@ -565,7 +589,12 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
       for (int t = 0; t < kOwn; ++t) {
         const v4f other = xch[wave ^ 4][t][lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) H[t][i] = fmaf(decay, H[t][i], mine[t][i] + other[i]);
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (kPS)
+            H[t][i] = fmaf(decay, H[t][i], (mine[t][i] + other[i]) * sig[t][i]);
+          else
+            H[t][i] = fmaf(decay, H[t][i], mine[t][i] + other[i]);
+        }
       }
     };
     for (int c = g0; c < gend; c += 2) {   // g0 is even
@@ -574,13 +603,19 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  // ---- final state
+  // ---- final state (per state: H_C / C_scale)
   if (h_final && prow) {
     const Rsrc rf = make_rsrc(h_final + int64_t(bh) * pn, uint32_t(pn) * 4u);
 #pragma unroll
     for (int t = 0; t < kOwn; ++t) {
       if (16 * (kOwn * kh + t) >= N) break;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, H[t]), rf, hoff + 64u * t, 0, 0);
+      v4f hf = H[t];
+      if constexpr (kPS) {
+        const v4f sc = *reinterpret_cast<const v4f*>(C_scale + g * N + 64 * kh + 16 * t + 4 * kg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hf[i] = hf[i] / sc[i];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, hf), rf, hoff + 64u * t, 0, 0);
     }
   }
 }
@@ -590,8 +625,9 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   const int nblocks = s.batch * s.nchunks * s.nheads;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale, a.dt, a.A,
-                       a.acs, a.states, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.nchunks);
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
+                       a.bc_per_state ? a.C_scale : nullptr, a.dt, a.A, a.acs, a.states, s.seqlen, s.nheads,
+                       s.headdim, s.dstate, s.ngroups, s.nchunks);
   };
   switch (s.chunk) {
     case 64: go(chunk_state_kernel<64>); break;
@@ -616,14 +652,22 @@ bool state_scan_fused(int32_t batch, int32_t nheads) {
 hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   const int nblocks = s.batch * s.nheads;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kSThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale, a.dt, a.A,
-                       a.h0, a.h_final, a.acs, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim, s.dstate,
-                       s.ngroups, s.nchunks);
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kSThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale, a.C_scale,
+                       a.dt, a.A, a.h0, a.h_final, a.acs, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim,
+                       s.dstate, s.ngroups, s.nchunks);
   };
-  switch (s.chunk) {
-    case 64: go(state_scan_kernel<64>); break;
-    case 128: go(state_scan_kernel<128>); break;
-    default: go(state_scan_kernel<256>); break;
+  if (a.bc_per_state) {
+    switch (s.chunk) {
+      case 64: go(state_scan_kernel<64, true>); break;
+      case 128: go(state_scan_kernel<128, true>); break;
+      default: go(state_scan_kernel<256, true>); break;
+    }
+  } else {
+    switch (s.chunk) {
+      case 64: go(state_scan_kernel<64, false>); break;
+      case 128: go(state_scan_kernel<128, false>); break;
+      default: go(state_scan_kernel<256, false>); break;
+    }
   }
   return hipGetLastError();
 }

@@ -85,6 +85,52 @@ __global__ void __launch_bounds__(256) quantize_vec16(const v4u* __restrict__ x,
     quantize16(x, q, scale, i, by_inner, by_nscale);
 }
 
+// One scale per (k, i) (B or C with a scale per (group, state)): inner % 16 == 0, a thread's 16
+// consecutive elements of one row take the 16 consecutive scales scale[k, i0 .. i0 + 15] (four
+// 16-byte loads, cached: the scale table is small), each element its own reciprocal.
+__global__ void __launch_bounds__(256) quantize_vec16_pc(const v4u* __restrict__ x, v4u* __restrict__ q,
+                                                         const float* __restrict__ scale, uint32_t npair,
+                                                         FastDiv by_inner, FastDiv by_nscale, int32_t inner) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < npair; i += stride) {
+    const v4u raw0 = x[2 * i];
+    const v4u raw1 = x[2 * i + 1];
+    const uint32_t row = fdiv(i, by_inner);                        // (r, k) row of `inner` elements
+    const uint32_t i0 = 16u * (i - row * by_inner.d);              // first inner index
+    const uint32_t k = row - fdiv(row, by_nscale) * by_nscale.d;
+    const v4f* sp = reinterpret_cast<const v4f*>(scale + int64_t(k) * inner + i0);
+    float v[16], sv[16];
+    unpack8(raw0, *reinterpret_cast<float(*)[8]>(&v[0]));
+    unpack8(raw1, *reinterpret_cast<float(*)[8]>(&v[8]));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const v4f s4 = sp[t];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[4 * t + e] = s4[e];
+    }
+    uint32_t c[16];
+    bool slow[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) c[e] = code_fast(v[e], __builtin_amdgcn_rcpf(sv[e]), slow[e]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      if (slow[e]) c[e] = code_exact(v[e], sv[e]);
+    q[i] = v4u{pack4(c), pack4(c + 4), pack4(c + 8), pack4(c + 12)};
+  }
+}
+
+// Any inner: one element per iteration, one scale per (k, i).
+__global__ void __launch_bounds__(256) quantize_scalar_pc(const uint16_t* __restrict__ x, int8_t* __restrict__ q,
+                                                          const float* __restrict__ scale, int64_t n, int32_t nscale,
+                                                          int32_t inner) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const int64_t ki = e % (int64_t(nscale) * inner);   // k * inner + i
+    const _Float16 h = __builtin_bit_cast(_Float16, x[e]);
+    q[e] = int8_t(code_exact(float(h), scale[ki]));
+  }
+}
+
 // Several tensors in one launch: job k owns the blocks block0 .. block0 + nblocks - 1 and walks
 // its pairs grid-stride over them.
 struct Job16 {
@@ -380,6 +426,22 @@ hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int
   if (done < n) {
     hipLaunchKernelGGL(quantize_scalar, dim3(grid_for(n - done, 256)), dim3(256), 0, stream, x, q, scale, done,
                        n, nscale, inner);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_per_channel(const uint16_t* x, int8_t* q, const float* scale, int64_t rows,
+                                      int32_t nscale, int32_t inner, hipStream_t stream) {
+  const int64_t n = rows * int64_t(nscale) * inner;
+  if (n == 0) return hipSuccess;
+  if (inner % 16 == 0 && n / 16 < (int64_t(1) << 31)) {
+    const int64_t npair = n / 16;
+    hipLaunchKernelGGL(quantize_vec16_pc, dim3(grid_for(npair, 256)), dim3(256), 0, stream,
+                       reinterpret_cast<const v4u*>(x), reinterpret_cast<v4u*>(q), scale, uint32_t(npair),
+                       make_fastdiv(uint32_t(inner / 16)), make_fastdiv(uint32_t(nscale)), inner);
+  } else {
+    hipLaunchKernelGGL(quantize_scalar_pc, dim3(grid_for(n, 256)), dim3(256), 0, stream, x, q, scale, n, nscale,
+                       inner);
   }
   return hipGetLastError();
 }

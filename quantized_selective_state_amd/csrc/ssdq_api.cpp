@@ -76,6 +76,7 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   a->A = A;
   a->D = D;
   a->ycorr = nullptr;
+  a->bc_per_state = false;
   a->h0 = h0;
   a->y = static_cast<_Float16*>(y);
   a->h_final = h_final;
@@ -158,6 +159,16 @@ ssdq_status ssdq_quantize(const void* x_f16, int8_t* q, const float* scale, int6
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
+ssdq_status ssdq_quantize_per_channel(const void* x_f16, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
+                                      int32_t inner, hipStream_t stream) {
+  if (rows < 0 || nscale <= 0 || inner <= 0) return SSDQ_ERROR_INVALID_VALUE;
+  if (rows == 0) return SSDQ_SUCCESS;
+  if (!ok_ptr(x_f16) || !ok_ptr(q) || !ok_ptr(scale)) return SSDQ_ERROR_INVALID_VALUE;
+  const hipError_t e =
+      launch_quantize_per_channel(static_cast<const uint16_t*>(x_f16), q, scale, rows, nscale, inner, stream);
+  return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
+}
+
 ssdq_status ssdq_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream) {
   if (jobs == nullptr || count < 1 || count > SSDQ_QUANTIZE_MAX_JOBS) return SSDQ_ERROR_INVALID_VALUE;
   bool work = false;
@@ -233,6 +244,28 @@ ssdq_status ssdq_chunk_scan_corrected(const int8_t* x, const float* x_scale, con
                                          workspace_bytes, &s, &a);
   if (st != SSDQ_SUCCESS) return st;
   a.ycorr = y_corr;
+  for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
+    const ssdq_status r = run_stage(stage, s, a, stream);
+    if (r != SSDQ_SUCCESS) return r;
+  }
+  return SSDQ_SUCCESS;
+}
+
+ssdq_status ssdq_chunk_scan_per_state(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                      const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                      const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
+                                      int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                      int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (!ok_opt(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  ScanShape s;
+  ScanArgs a;
+  const ssdq_status st = check_scan_args(0, x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final, batch,
+                                         seqlen, nheads, headdim, dstate, ngroups, chunk, workspace,
+                                         workspace_bytes, &s, &a);
+  if (st != SSDQ_SUCCESS) return st;
+  a.ycorr = y_corr;
+  a.bc_per_state = true;
   for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
     const ssdq_status r = run_stage(stage, s, a, stream);
     if (r != SSDQ_SUCCESS) return r;
@@ -337,12 +370,40 @@ ssdq_status ssdq_state_update_i8(int8_t* state, float* state_scale, const int8_t
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 
+namespace {
+ssdq_status decode_any(int32_t state_format, void* state, float* state_scale, const int8_t* x, const float* x_scale,
+                       const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                       const float* A, const float* D, const float* y_corr, void* y, int32_t batch, int32_t nheads,
+                       int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream, bool per_state);
+}  // namespace
+
+ssdq_status ssdq_state_update_per_state(int32_t state_format, void* state, float* state_scale, const int8_t* x,
+                                        const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
+                                        const float* C_scale, const float* dt, const float* A, const float* D,
+                                        const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                                        int32_t dstate, int32_t ngroups, hipStream_t stream) {
+  if (!ok_opt(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  return decode_any(state_format, state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, y, batch,
+                    nheads, headdim, dstate, ngroups, stream, true);
+}
+
 ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float* state_scale, const int8_t* x,
                                         const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
                                         const float* C_scale, const float* dt, const float* A, const float* D,
                                         const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
                                         int32_t dstate, int32_t ngroups, hipStream_t stream) {
   if (!ok_ptr(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  return decode_any(state_format, state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, y, batch,
+                    nheads, headdim, dstate, ngroups, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+ssdq_status decode_any(int32_t state_format, void* state, float* state_scale, const int8_t* x, const float* x_scale,
+                       const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
+                       const float* A, const float* D, const float* y_corr, void* y, int32_t batch, int32_t nheads,
+                       int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream, bool per_state) {
   if (state_format != SSDQ_STATE_F32 && state_format != SSDQ_STATE_F16 && state_format != SSDQ_STATE_I8)
     return SSDQ_ERROR_INVALID_VALUE;
   if (state_format == SSDQ_STATE_I8 && !ok_ptr(state_scale)) return SSDQ_ERROR_INVALID_VALUE;
@@ -353,15 +414,18 @@ ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float
   hipError_t e;
   if (state_format == SSDQ_STATE_F32)
     e = launch_state_update(static_cast<float*>(state), x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, yo,
-                            batch, nheads, headdim, dstate, ngroups, stream);
+                            batch, nheads, headdim, dstate, ngroups, stream, per_state);
   else if (state_format == SSDQ_STATE_F16)
     e = launch_state_update_f16(static_cast<uint16_t*>(state), x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr,
-                                yo, batch, nheads, headdim, dstate, ngroups, stream);
+                                yo, batch, nheads, headdim, dstate, ngroups, stream, per_state);
   else
     e = launch_state_update_i8(static_cast<int8_t*>(state), state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
-                               y_corr, yo, batch, nheads, headdim, dstate, ngroups, stream);
+                               y_corr, yo, batch, nheads, headdim, dstate, ngroups, stream, per_state);
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
+}  // namespace
+
+extern "C" {
 
 ssdq_status ssdq_frontend(const void* xbc, const float* conv_w, const float* conv_b, int32_t d_conv,
                           const float* x_scale, const float* B_scale, const float* C_scale, const float* dt_raw,

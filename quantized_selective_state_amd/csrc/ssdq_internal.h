@@ -67,12 +67,15 @@ struct ScanArgs {
   float* states;      // workspace: (batch, nchunks, nheads, headdim, dstate) fp32
   int8_t* hprev;      // workspace: (batch, nchunks, nheads, 2, headdim, dstate) int8 limbs
   float* hscale;      // workspace: (batch, nchunks, nheads, headdim)
+  bool bc_per_state;  // B_scale and C_scale hold one scale per (group, state), not one per group
 };
 
 // Kernel launchers (one per translation unit).  They return hipGetLastError().
 hipError_t launch_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hipStream_t stream);
 hipError_t launch_quantize(const uint16_t* x, int8_t* q, const float* scale, int64_t rows, int32_t nscale,
                            int32_t inner, hipStream_t stream);
+hipError_t launch_quantize_per_channel(const uint16_t* x, int8_t* q, const float* scale, int64_t rows,
+                                      int32_t nscale, int32_t inner, hipStream_t stream);
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 // Stages 0 and 1 in one kernel (one block per (batch, head), chunks in order); used when
@@ -93,16 +96,17 @@ hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
                                   const float* dt, const float* A, const float* D, const float* ycorr, _Float16* y,
                                   int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                  hipStream_t stream);
+                                  hipStream_t stream, bool per_state = false);
 hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                    const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                    const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
                                    int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                   hipStream_t stream);
+                                   hipStream_t stream, bool per_state = false);
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
-                               int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream);
+                               int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream,
+                               bool per_state = false);
 
 // ---------------------------------------------------------------------------------------------
 // device helpers

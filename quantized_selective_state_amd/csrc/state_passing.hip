@@ -26,8 +26,9 @@ constexpr int kDepth = 4;   // chunks of states in flight per thread
 template <int LPR>
 __global__ void __launch_bounds__(kThreads) state_passing_kernel(
     const float* __restrict__ states, const float* __restrict__ acs, const float* h0,  // h0 may alias h_final
-    float* h_final, int8_t* __restrict__ hprev, float* __restrict__ hscale, int64_t seqlen, int32_t nheads,
-    int32_t headdim, int32_t dstate, int32_t chunk, int32_t nchunks, int32_t blocks_per_bh) {
+    float* h_final, int8_t* __restrict__ hprev, float* __restrict__ hscale, const float* __restrict__ C_scale_ps,
+    int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, int32_t chunk, int32_t nchunks,
+    int32_t blocks_per_bh) {
   constexpr int lanes_per_row = LPR;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = bid / blocks_per_bh;
@@ -46,8 +47,12 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
   const int n0 = 4 * nq, blk = n0 >> 6, m = n0 & 63;
   const int64_t eh = int64_t(p) * N + (64 * blk + 64 <= N ? 64 * blk + 16 * ((m >> 2) & 3) + 4 * (m >> 4) : n0);
 
+  // with B and C scales per (group, state) (C_scale_ps non-null) the chunk states arrive scaled by
+  // the C scale of each state, and the running state is kept so (h0 scaled in, h_final scaled out)
+  v4f sc = {1.f, 1.f, 1.f, 1.f};
+  if (C_scale_ps && active) sc = *reinterpret_cast<const v4f*>(C_scale_ps + (h / (nheads / ngroups)) * N + 4 * nq);
   v4f H = {0.f, 0.f, 0.f, 0.f};
-  if (active && h0) H = *reinterpret_cast<const v4f*>(h0 + int64_t(bh) * pn + e);
+  if (active && h0) H = *reinterpret_cast<const v4f*>(h0 + int64_t(bh) * pn + e) * sc;
   const float* acs_bh = acs + int64_t(bh) * nchunks * chunk;
   const int64_t cstride = int64_t(nheads) * pn;  // between consecutive chunks of one (b, h)
   const int64_t base = (int64_t(b) * nchunks * nheads + h) * pn;
@@ -109,7 +114,13 @@ __global__ void __launch_bounds__(kThreads) state_passing_kernel(
       for (int i = 0; i < 4; ++i) H[i] = decay * H[i] + sv[i];
     }
   }
-  if (active && h_final) *reinterpret_cast<v4f*>(h_final + int64_t(bh) * pn + e) = H;
+  if (active && h_final) {
+    if (C_scale_ps) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) H[i] = H[i] / sc[i];
+    }
+    *reinterpret_cast<v4f*>(h_final + int64_t(bh) * pn + e) = H;
+  }
 }
 
 }  // namespace
@@ -122,7 +133,8 @@ hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream
   const int nblocks = s.batch * s.nheads * per_bh;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.states, a.acs, a.h0, a.h_final, a.hprev,
-                       a.hscale, s.seqlen, s.nheads, s.headdim, s.dstate, s.chunk, s.nchunks, per_bh);
+                       a.hscale, a.bc_per_state ? a.C_scale : nullptr, s.seqlen, s.nheads, s.headdim, s.dstate,
+                       s.ngroups, s.chunk, s.nchunks, per_bh);
   };
   switch (lanes) {   // N / 4 = 4 .. 32 for the supported dstate
     case 4: go(state_passing_kernel<4>); break;

@@ -39,7 +39,8 @@ __device__ __forceinline__ float group_sum_to_last_lane(float v) {
   return v;
 }
 
-template <int N>
+// kPS: B_scale and C_scale hold one scale per (group, state) (ngroups x N) instead of one per group.
+template <int N, bool kPS>
 __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
@@ -76,12 +77,22 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
   const float sx = x_scale[h];
   const float dx = d * sx;
   const float Dsx = (D ? D[h] : 0.f) * sx;
-  const float sB = B_scale[g], sC = C_scale[g];
   float bh4[4], ch4[4];
+  if constexpr (kPS) {
+    const v4f sb4 = *reinterpret_cast<const v4f*>(B_scale + g * N + 4 * nq);
+    const v4f sc4 = *reinterpret_cast<const v4f*>(C_scale + g * N + 4 * nq);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bh4[i] = sB * sbyte(bw, i);
-    ch4[i] = sC * sbyte(cw, i);
+    for (int i = 0; i < 4; ++i) {
+      bh4[i] = sb4[i] * sbyte(bw, i);
+      ch4[i] = sc4[i] * sbyte(cw, i);
+    }
+  } else {
+    const float sB = B_scale[g], sC = C_scale[g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bh4[i] = sB * sbyte(bw, i);
+      ch4[i] = sC * sbyte(cw, i);
+    }
   }
 
 #pragma unroll
@@ -105,7 +116,7 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
 // and store per row), forms the update in fp32 from the cached value, reads y out of that
 // update and stores it rounded to nearest binary16 (ties to even; past the format's range:
 // inf).  y[p] is summed across the N/8 lanes of row p with DPP lane pairings.
-template <int N>
+template <int N, bool kPS>
 __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
     uint16_t* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
@@ -142,12 +153,22 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
   const float sx = x_scale[h];
   const float dx = d * sx;
   const float Dsx = (D ? D[h] : 0.f) * sx;
-  const float sB = B_scale[g], sC = C_scale[g];
   float bh8[8], ch8[8];
+  if constexpr (kPS) {
+    const v4f* sbp = reinterpret_cast<const v4f*>(B_scale + g * N + 8 * nq);
+    const v4f* scp = reinterpret_cast<const v4f*>(C_scale + g * N + 8 * nq);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bh8[i] = sB * sbyte(bw[i >> 2], i & 3);
-    ch8[i] = sC * sbyte(cw[i >> 2], i & 3);
+    for (int i = 0; i < 8; ++i) {
+      bh8[i] = sbp[i >> 2][i & 3] * sbyte(bw[i >> 2], i & 3);
+      ch8[i] = scp[i >> 2][i & 3] * sbyte(cw[i >> 2], i & 3);
+    }
+  } else {
+    const float sB = B_scale[g], sC = C_scale[g];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bh8[i] = sB * sbyte(bw[i >> 2], i & 3);
+      ch8[i] = sC * sbyte(cw[i >> 2], i & 3);
+    }
   }
 
 #pragma unroll
@@ -192,7 +213,10 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
 //    byte permutes pack four codes per dword.
 constexpr int kI8Threads = 128;   // two waves per (batch, head): four row passes per lane amortize the set-up
 
-template <int N>
+// kPS: per-(group, state) B and C scales.  The B scale then goes into each state's B value and
+// y is summed in fp32 over the C values scaled per state (the int8 dot products factor only
+// with one C scale per row).
+template <int N, bool kPS>
 __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     int8_t* __restrict__ state, float* __restrict__ state_scale, const int8_t* __restrict__ x,
     const float* __restrict__ x_scale, const int8_t* __restrict__ Bm, const float* __restrict__ B_scale,
@@ -234,15 +258,28 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
   const float d = dt[bh];
   const float a = __expf(d * A[h]);
   const float sx = x_scale[h];
-  const float dxB = d * sx * B_scale[g];
+  const float dxB = d * sx * (kPS ? 1.f : B_scale[g]);
   const float Dsx = (D ? D[h] : 0.f) * sx;
-  const float sC = C_scale[g];
-  float bq[16];   // the B codes as floats (the scale is applied per row)
+  const float sC = kPS ? 1.f : C_scale[g];
+  float bq[16];   // the B codes as floats (per group: the scale is applied per row; per state: included)
+  float cf[kPS ? 16 : 1];   // per state: the C values sC[n] c_n
+  if constexpr (kPS) {
+    const v4f* sbp = reinterpret_cast<const v4f*>(B_scale + g * N + 16 * nq);
+    const v4f* scp = reinterpret_cast<const v4f*>(C_scale + g * N + 16 * nq);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bq[i] = sbyte(bw[i >> 2], i & 3);
-  int cb = 0;     // <c, b> over this lane's 16 states
+    for (int i = 0; i < 16; ++i) {
+      bq[i] = sbp[i >> 2][i & 3] * sbyte(bw[i >> 2], i & 3);
+      cf[i] = scp[i >> 2][i & 3] * sbyte(cw[i >> 2], i & 3);
+    }
+  } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cb = __builtin_amdgcn_sdot4(int(cw[j]), int(bw[j]), cb, false);
+    for (int i = 0; i < 16; ++i) bq[i] = sbyte(bw[i >> 2], i & 3);
+  }
+  int cb = 0;     // <c, b> over this lane's 16 states (per group only)
+  if constexpr (!kPS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cb = __builtin_amdgcn_sdot4(int(cw[j]), int(bw[j]), cb, false);
+  }
   const float cbf = float(cb);
 
 #pragma unroll
@@ -253,10 +290,10 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     const float as = a * so[k];         // exp(dt A) times the cached row's scale
     float v[16];
     float m = 0.f;
-    int cq = 0;                         // <c, q> over this lane's 16 cached codes
+    int cq = 0;                         // <c, q> over this lane's 16 cached codes (per group only)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      cq = __builtin_amdgcn_sdot4(int(cw[j]), int(hv[k][j]), cq, false);
+      if constexpr (!kPS) cq = __builtin_amdgcn_sdot4(int(cw[j]), int(hv[k][j]), cq, false);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v[4 * j + i] = fmaf(as, sbyte(hv[k][j], i), uB * bq[4 * j + i]);
@@ -289,7 +326,14 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
       out[j] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);                   // lo.b0, lo.b1, hi.b0, hi.b1
     }
     if (p < P) __builtin_nontemporal_store(out, reinterpret_cast<v4u*>(st + int64_t(p) * N + 16 * nq));
-    float part = fmaf(as, float(cq), uB * cbf);
+    float part;
+    if constexpr (kPS) {
+      part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = fmaf(cf[i], v[i], part);
+    } else {
+      part = fmaf(as, float(cq), uB * cbf);
+    }
     part = group_sum<kLanesPerRow>(part);
     if (p < P && nq == 0) {
       ss[p] = s;
@@ -298,13 +342,13 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
   }
 }
 
-template <int N>
+template <int N, bool kPS>
 hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
                     const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
                     const float* ycorr, _Float16* y, int32_t batch, int32_t nheads, int32_t headdim, int32_t ngroups,
                     hipStream_t stream) {
   const int nblocks = batch * nheads;
-  hipLaunchKernelGGL((state_update_kernel<N>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
+  hipLaunchKernelGGL((state_update_kernel<N, kPS>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
                      B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
   return hipGetLastError();
 }
@@ -315,14 +359,16 @@ hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float
                                    const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                    const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
                                    int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, bool per_state) {
   const int nblocks = batch * nheads;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B, B_scale, C, C_scale,
+                       dt, A, D, ycorr, y, nheads, headdim, ngroups);
+  };
   if (dstate == 128)
-    hipLaunchKernelGGL((state_update_f16_kernel<128>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
-                       B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
+    per_state ? go(state_update_f16_kernel<128, true>) : go(state_update_f16_kernel<128, false>);
   else
-    hipLaunchKernelGGL((state_update_f16_kernel<64>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale,
-                       B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
+    per_state ? go(state_update_f16_kernel<64, true>) : go(state_update_f16_kernel<64, false>);
   return hipGetLastError();
 }
 
@@ -330,26 +376,33 @@ hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
                                   const float* dt, const float* A, const float* D, const float* ycorr, _Float16* y,
                                   int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, bool per_state) {
   const int nblocks = batch * nheads;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale, x, x_scale, B, B_scale,
+                       C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
+  };
   if (dstate == 128)
-    hipLaunchKernelGGL((state_update_i8_kernel<128>), dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale,
-                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
+    per_state ? go(state_update_i8_kernel<128, true>) : go(state_update_i8_kernel<128, false>);
   else
-    hipLaunchKernelGGL((state_update_i8_kernel<64>), dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale,
-                       x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
+    per_state ? go(state_update_i8_kernel<64, true>) : go(state_update_i8_kernel<64, false>);
   return hipGetLastError();
 }
 
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
-                               int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
+                               int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream,
+                               bool per_state) {
   if (dstate == 128)
-    return launch_n<128>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads, headdim,
-                         ngroups, stream);
-  return launch_n<64>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads, headdim, ngroups,
-                      stream);
+    return per_state ? launch_n<128, true>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads,
+                                           headdim, ngroups, stream)
+                     : launch_n<128, false>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch,
+                                            nheads, headdim, ngroups, stream);
+  return per_state ? launch_n<64, true>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads,
+                                        headdim, ngroups, stream)
+                   : launch_n<64, false>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads,
+                                         headdim, ngroups, stream);
 }
 
 }  // namespace ssdq

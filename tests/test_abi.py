@@ -282,3 +282,32 @@ def test_corrected_calls_validate_on_the_host(lib):
     no_scale[1] = None                                  # state_scale, needed by the 8-bit format only
     assert lib.ssdq_state_update_corrected(2, *no_scale, 2, 4, 64, 128, 2, None) == INVALID
     assert lib.ssdq_state_update_corrected(0, *no_scale, 2, 4, 64, 96, 2, None) == UNSUPPORTED
+
+
+def test_per_state_calls_validate_on_the_host(lib):
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.ssdq_chunk_scan_per_state.argtypes = [P] * 13 + [i32, i64, i32, i32, i32, i32, i32, P, sz, P]
+    lib.ssdq_state_update_per_state.argtypes = [i32] + [P] * 13 + [i32] * 5 + [P]
+    lib.ssdq_quantize_per_channel.argtypes = [P, P, P, i64, i32, i32, P]
+    ptrs = [A16] * 13
+    odd = list(ptrs)
+    odd[9] = A16 + 4                                     # y_corr (optional) misaligned
+    assert lib.ssdq_chunk_scan_per_state(*odd, 1, 256, 4, 16, 16, 1, 64, A16, 1 << 30, None) == INVALID
+    assert lib.ssdq_chunk_scan_per_state(*ptrs, 1, 256, 4, 16, 16, 1, 64, A16, 16, None) == WS_SMALL
+    assert lib.ssdq_chunk_scan_per_state(*ptrs, 1, 256, 3, 16, 16, 2, 64, A16, 1 << 30, None) == INVALID
+    no_B_scale = list(ptrs)
+    no_B_scale[3] = None
+    assert lib.ssdq_chunk_scan_per_state(*no_B_scale, 1, 256, 4, 16, 16, 1, 64, A16, 1 << 30, None) == INVALID
+    dec = [A16] * 13
+    assert lib.ssdq_state_update_per_state(3, *dec, 2, 4, 64, 128, 2, None) == INVALID        # no such format
+    bad = list(dec)
+    bad[11] = A16 + 4                                    # y_corr misaligned
+    assert lib.ssdq_state_update_per_state(0, *bad, 2, 4, 64, 128, 2, None) == INVALID
+    no_scale = list(dec)
+    no_scale[1] = None                                   # state_scale, needed by the 8-bit format only
+    assert lib.ssdq_state_update_per_state(2, *no_scale, 2, 4, 64, 128, 2, None) == INVALID
+    assert lib.ssdq_state_update_per_state(0, *no_scale, 2, 4, 64, 96, 2, None) == UNSUPPORTED
+    assert lib.ssdq_quantize_per_channel(A16, A16, A16, -1, 2, 16, None) == INVALID
+    assert lib.ssdq_quantize_per_channel(A16, A16, None, 4, 2, 16, None) == INVALID
+    assert lib.ssdq_quantize_per_channel(A16, A16, A16, 4, 0, 16, None) == INVALID
+    assert lib.ssdq_quantize_per_channel(None, None, None, 0, 2, 16, None) == 0                # nothing to do
