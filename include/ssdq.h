@@ -392,7 +392,7 @@ ssdq_status ssdq_state_update_per_state(int32_t state_format, void* state, float
  * element whose exact SiLU value lies within fp32 rounding of a binary16 midpoint may take the
  * other neighbour (and its code).  seqlen 0 is a no-op (after the size checks; pointers are not
  * looked at then).  Errors: NULL or misaligned (16-byte) pointers, non-positive sizes or nheads % ngroups != 0 -> SSDQ_ERROR_INVALID_VALUE; d_conv other
- * than 4, headdim or dstate not a multiple of 8, or batch * ceil(channels / 512) * ceil(seqlen / 8)
+ * than 4, headdim or dstate not a multiple of 8, or batch * ceil(channels / 256) * ceil(seqlen / 16)
  * >= 2^31 ->
  * SSDQ_ERROR_UNSUPPORTED.  All pointers are device memory owned by the caller.
  */

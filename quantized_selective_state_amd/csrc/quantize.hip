@@ -9,11 +9,15 @@
 // loads and stores: on MI355X they stream faster here than nontemporal ones.
 //
 // Exactness without a division per element: with r = rcp(s) (the hardware reciprocal, within
-// 1 ulp) and y = fl(v r), |y - v/s| <= 1.5 * 2^-23 |v/s| and |fl(v/s) - v/s| <= 2^-24 |v/s|,
-// so for |y| < 256 the two are within 2^-14.  rint(y) and rint(fl(v/s)) can only differ when
-// a half-integer lies in between, i.e. when y is within 2^-13 of one; those (rare) elements
-// take the exact division.  Beyond |y| >= 256 both saturate.  The float -> int conversion
-// maps NaN to 0 and saturates infinities, and the clamp is done on the integer.
+// 1 ulp) and the exact product y = v r (inside an fma), |y - v/s| <= 2^-23 |v/s|, and
+// |fl(v/s) - v/s| <= 2^-24 |v/s|, so for |v/s| < 256 the two are within 2^-14.  rint(y) and
+// rint(fl(v/s)) can only differ when a half-integer lies in between, i.e. when y is within
+// 2^-13 of one; those (rare) elements, NaN and infinities take the exact division.  The fast
+// code rounds through the binade of 1.5 * 2^23, where the float spacing is 1: fl(y + 1.5 * 2^23)
+// = 1.5 * 2^23 + rint(y) (ties to even) for |y| < 2^22, and the integer image of that float is
+// 0x4B400000 + rint(y), so the clamp to +-127 is one integer median and the code is the low
+// byte.  Past 2^22 the sum is still monotonic in y and lands beyond either clamp bound, and from
+// |v/s| >= 127 on both sides give +-127, so large values need no exact division either.
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -27,18 +31,24 @@ __device__ __forceinline__ uint32_t code_exact(float v, float s) {
   return uint32_t(int32_t(r)) & 0xffu;
 }
 
-// fast code, and whether the exact division must decide this element (also for NaN and
-// |y| >= 256, which are rare and which the exact path maps to 0 and +-127)
+constexpr float kRound = 12582912.f;        // 1.5 * 2^23
+constexpr int32_t kRoundBits = 0x4B400000;  // its binary32 image
+
+// fast code in the low byte of the result (the upper bytes are not cleared), and whether the
+// exact division must decide this element: y within 2^-13 of a half-integer, NaN or infinity
+// (their residual d is NaN or large)
 __device__ __forceinline__ uint32_t code_fast(float v, float rcp, bool& slow) {
-  const float y = v * rcp;
-  const float k = rintf(y);
-  slow = !(fabsf(y - k) <= 0.5f - 1.0f / 8192.f) || !(fabsf(y) < 256.f);
-  const float kc = __builtin_amdgcn_fmed3f(k, -127.f, 127.f);   // finite whenever slow is false
-  return uint32_t(int32_t(kc)) & 0xffu;
+  const float t = fmaf(v, rcp, kRound);   // 1.5 * 2^23 + rint(v rcp)
+  const float k = t - kRound;             // rint(v rcp), exact
+  const float d = fmaf(v, rcp, -k);       // v rcp - k
+  slow = !(fabsf(d) <= 0.5f - 1.0f / 8192.f);
+  const int32_t b = __builtin_bit_cast(int32_t, t);
+  return uint32_t(min(max(b, kRoundBits - 127), kRoundBits + 127));
 }
 
 // n codes of one scale: the fast path for all, the exact division only for the elements that
-// need it (a per-element branch: a wave pays for an element only when one of its lanes needs it)
+// need it, behind one branch for the n elements (a wave enters it only when one of its lanes
+// has such an element)
 template <int n>
 __device__ __forceinline__ void codes(const float (&v)[n], float s, uint32_t (&c)[n]) {
   const float rcp = __builtin_amdgcn_rcpf(s);
@@ -58,7 +68,13 @@ __device__ __forceinline__ void unpack8(v4u raw, float (&v)[8]) {
   }
 }
 
-__device__ __forceinline__ uint32_t pack4(const uint32_t* c) { return c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24); }
+// the low bytes of c[0..3] in one word (v_perm_b32: selector bytes 0-3 take bytes of the second
+// operand, 4-7 of the first, 0x0c gives zero)
+__device__ __forceinline__ uint32_t pack4(const uint32_t* c) {
+  const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
 
 // inner % 16 == 0: a thread quantizes 16 consecutive elements of one row (one scale index).
 // Pair indices i < 2^31 (host-checked), so the scale index uses 32-bit invariant division.
@@ -110,11 +126,17 @@ __global__ void __launch_bounds__(256) quantize_vec16_pc(const v4u* __restrict__
     }
     uint32_t c[16];
     bool slow[16];
+    bool any = false;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) c[e] = code_fast(v[e], __builtin_amdgcn_rcpf(sv[e]), slow[e]);
+    for (int e = 0; e < 16; ++e) {
+      c[e] = code_fast(v[e], __builtin_amdgcn_rcpf(sv[e]), slow[e]);
+      any = any || slow[e];
+    }
+    if (any) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (slow[e]) c[e] = code_exact(v[e], sv[e]);
+      for (int e = 0; e < 16; ++e)
+        if (slow[e]) c[e] = code_exact(v[e], sv[e]);
+    }
     q[i] = v4u{pack4(c), pack4(c + 4), pack4(c + 8), pack4(c + 12)};
   }
 }
@@ -200,21 +222,34 @@ int grid_for(int64_t work, int block) {
 // read of the fp16 activations and one write of the codes, instead of a convolution pass that
 // writes fp16 and a quantize pass that reads it again.
 //
-// A lane owns 8 consecutive channels (one 16-byte load per token) and walks a strip of
-// kFeTokens tokens, keeping the three previous tokens in registers; only the three tokens
-// before the strip are read twice.  The strip is short so that the launch has several waves
-// per SIMD to overlap the SiLU arithmetic (two quarter-rate transcendentals per element) with
-// the loads; all of the strip's loads are issued before any arithmetic.
-constexpr int kFeTokens = 8;
+// A lane owns kFeChannels = 4 consecutive channels (one 8-byte load per token) and walks a strip
+// of kFeTokens = 16 tokens, keeping the three previous tokens in registers; only the three
+// tokens before the strip are read twice (from L2: the neighbouring strip just read them).  All
+// of the strip's loads are issued before any arithmetic.  The kernel is bound by its VALU work
+// (two transcendentals per element for SiLU, then the code), so the lane is kept narrow: at 4
+// channels it needs 80 VGPRs, six waves per SIMD to overlap that arithmetic with the loads (at
+// 8 channels per lane, 125 VGPRs and four waves, it took 16% longer at the 8B-shaped layer).
+// kCh fp16 values of one token: 8 -> one 16-byte word, 4 -> one 8-byte word
+template <int kCh> struct ChVec;
+template <> struct ChVec<8> { using T = v4u; };
+template <> struct ChVec<4> { using T = v2u; };
 
+template <int kCh>
+__device__ __forceinline__ void unpack_ch(typename ChVec<kCh>::T raw, float (&v)[kCh]) {
+#pragma unroll
+  for (int e = 0; e < kCh / 2; ++e) {
+    v[2 * e] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] & 0xffffu)));
+    v[2 * e + 1] = float(__builtin_bit_cast(_Float16, uint16_t(raw[e] >> 16)));
+  }
+}
+
+template <int kCh>
 __global__ void __launch_bounds__(64) frontend_kernel(
     const uint16_t* __restrict__ xbc, const float* __restrict__ w, const float* __restrict__ bias,
     const float* __restrict__ x_scale, const float* __restrict__ B_scale, const float* __restrict__ C_scale,
     int8_t* __restrict__ qx, int8_t* __restrict__ qB, int8_t* __restrict__ qC, int64_t seqlen, int32_t HP,
     int32_t GN, int32_t P, int32_t N, int32_t nvec, int32_t vec_blocks, int32_t strips) {
-  // logical block = ((b * vec_blocks + channel block) * strips + strip), numbered XCD-aware so
-  // that consecutive strips of one channel block run on one XCD: the three history tokens a
-  // strip reads again were just read by its neighbour and come from that XCD's L2
+  using VT = typename ChVec<kCh>::T;
   const int lb = xcd_remap(blockIdx.x, gridDim.x);
   const int strip = lb % strips;
   const int vb = (lb / strips) % vec_blocks;
@@ -222,7 +257,7 @@ __global__ void __launch_bounds__(64) frontend_kernel(
   const int vec = vb * 64 + int(threadIdx.x);
   if (vec >= nvec) return;   // no barriers below
   const int C = HP + 2 * GN;
-  const int ch0 = 8 * vec;
+  const int ch0 = kCh * vec;
   const int64_t t0 = int64_t(strip) * kFeTokens;
   const int64_t t1 = min(t0 + kFeTokens, seqlen);
   int8_t* dst;
@@ -241,62 +276,56 @@ __global__ void __launch_bounds__(64) frontend_kernel(
     stride = GN;
     s = C_scale[(ch0 - HP - GN) / N];
   }
-  float tap[4][8], bi[8];
+  float tap[4][kCh], bi[kCh];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {   // taps of channel ch0 + e are w[4 (ch0 + e) + k]: 32 floats
+  for (int q = 0; q < kCh; ++q) {
     const v4f t = *reinterpret_cast<const v4f*>(w + int64_t(ch0) * 4 + 4 * q);
 #pragma unroll
     for (int k = 0; k < 4; ++k) tap[k][q] = t[k];
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) bi[e] = bias ? bias[ch0 + e] : 0.f;
+  for (int e = 0; e < kCh; ++e) bi[e] = bias ? bias[ch0 + e] : 0.f;
   const uint16_t* src = xbc + b * seqlen * C + ch0;
-  float h1[8], h2[8], h3[8];   // tokens t - 1, t - 2, t - 3
+  float h1[kCh], h2[kCh], h3[kCh];   // tokens t - 1, t - 2, t - 3
   {
-    float v[8];
-    v4u raw[3];
+    VT raw[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const int64_t t = t0 - 1 - j;
-      raw[j] = t >= 0 ? *reinterpret_cast<const v4u*>(src + t * C) : v4u{0u, 0u, 0u, 0u};
+      raw[j] = t >= 0 ? *reinterpret_cast<const VT*>(src + t * C) : VT{};
     }
-    unpack8(raw[0], v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h1[e] = v[e];
-    unpack8(raw[1], v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h2[e] = v[e];
-    unpack8(raw[2], v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h3[e] = v[e];
+    unpack_ch<kCh>(raw[0], h1);
+    unpack_ch<kCh>(raw[1], h2);
+    unpack_ch<kCh>(raw[2], h3);
   }
   int8_t* out = dst + b * seqlen * stride;
-  v4u raw[kFeTokens];
+  VT raw[kFeTokens];
 #pragma unroll
   for (int u = 0; u < kFeTokens; ++u)
-    raw[u] = t0 + u < t1 ? *reinterpret_cast<const v4u*>(src + (t0 + u) * C) : v4u{0u, 0u, 0u, 0u};
-  {
-    const int64_t t = t0;
+    raw[u] = t0 + u < t1 ? *reinterpret_cast<const VT*>(src + (t0 + u) * C) : VT{};
 #pragma unroll
-    for (int u = 0; u < kFeTokens; ++u) {   // fully unrolled; tokens past the strip are not stored
-      float cur[8], a[8];
-      unpack8(raw[u], cur);
+  for (int u = 0; u < kFeTokens; ++u) {   // fully unrolled; tokens past the strip are not stored
+    float cur[kCh], a[kCh];
+    unpack_ch<kCh>(raw[u], cur);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = fmaf(tap[0][e], h3[e], bi[e]);
-        v = fmaf(tap[1][e], h2[e], v);
-        v = fmaf(tap[2][e], h1[e], v);
-        v = fmaf(tap[3][e], cur[e], v);
-        const float silu = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
-        a[e] = float(_Float16(silu));   // the module's binary16 output (round to nearest even)
-        h3[e] = h2[e];
-        h2[e] = h1[e];
-        h1[e] = cur[e];
-      }
-      uint32_t c[8];
-      codes<8>(a, s, c);
-      const v2u packed = {pack4(c), pack4(c + 4)};
-      if (t + u < t1) *reinterpret_cast<v2u*>(out + (t + u) * stride) = packed;
+    for (int e = 0; e < kCh; ++e) {
+      float v = fmaf(tap[0][e], h3[e], bi[e]);
+      v = fmaf(tap[1][e], h2[e], v);
+      v = fmaf(tap[2][e], h1[e], v);
+      v = fmaf(tap[3][e], cur[e], v);
+      const float silu = v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+      a[e] = float(_Float16(silu));   // the module's binary16 output (round to nearest even)
+      h3[e] = h2[e];
+      h2[e] = h1[e];
+      h1[e] = cur[e];
+    }
+    uint32_t c[kCh];
+    codes<kCh>(a, s, c);
+    if (t0 + u < t1) {
+      if constexpr (kCh == 8)
+        *reinterpret_cast<v2u*>(out + (t0 + u) * stride) = v2u{pack4(c), pack4(c + 4)};
+      else
+        *reinterpret_cast<uint32_t*>(out + (t0 + u) * stride) = pack4(c);
     }
   }
 }
@@ -451,11 +480,11 @@ hipError_t launch_frontend(const uint16_t* xbc, const float* conv_w, const float
                            int8_t* x, int8_t* B, int8_t* C, float* dt, int32_t batch, int64_t seqlen,
                            int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream) {
   const int32_t HP = nheads * headdim, GN = ngroups * dstate;
-  const int32_t nvec = (HP + 2 * GN) / 8;
+  const int32_t nvec = (HP + 2 * GN) / kFeChannels;
   const int32_t vec_blocks = (nvec + 63) / 64;
   const int32_t strips = int32_t((seqlen + kFeTokens - 1) / kFeTokens);
   const int32_t nblocks = batch * vec_blocks * strips;   // < 2^31 (host-checked)
-  hipLaunchKernelGGL(frontend_kernel, dim3(nblocks), dim3(64), 0, stream, xbc, conv_w, conv_b, x_scale, B_scale,
+  hipLaunchKernelGGL(frontend_kernel<kFeChannels>, dim3(nblocks), dim3(64), 0, stream, xbc, conv_w, conv_b, x_scale, B_scale,
                      C_scale, x, B, C, seqlen, HP, GN, headdim, dstate, nvec, vec_blocks, strips);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

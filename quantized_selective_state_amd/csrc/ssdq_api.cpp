@@ -437,7 +437,8 @@ ssdq_status ssdq_frontend(const void* xbc, const float* conv_w, const float* con
     return SSDQ_ERROR_INVALID_VALUE;
   if (d_conv != 4 || headdim % 8 != 0 || dstate % 8 != 0) return SSDQ_ERROR_UNSUPPORTED;
   const int64_t channels = int64_t(nheads) * headdim + 2 * int64_t(ngroups) * dstate;
-  const int64_t blocks = int64_t(batch) * ((channels / 8 + 63) / 64) * ((seqlen + 7) / 8);   // front-end launch
+  const int64_t blocks =   // front-end launch
+      int64_t(batch) * ((channels / kFeChannels + 63) / 64) * ((seqlen + kFeTokens - 1) / kFeTokens);
   if (channels >= (int64_t(1) << 31) || blocks >= (int64_t(1) << 31)) return SSDQ_ERROR_UNSUPPORTED;
   if (seqlen == 0) return SSDQ_SUCCESS;   // nothing to read or write (empty tensors may have no address)
   if (!ok_ptr(xbc) || !ok_ptr(conv_w) || !ok_opt(conv_b) || !ok_ptr(x_scale) || !ok_ptr(B_scale) ||

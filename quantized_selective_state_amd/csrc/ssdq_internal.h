@@ -83,6 +83,10 @@ hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream
 bool state_scan_fused(int32_t batch, int32_t nheads);
 hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
+// front-end launch geometry: a lane owns kFeChannels channels and a strip of kFeTokens tokens;
+// blocks of 64 lanes (the host checks the block count against the grid limit with these)
+constexpr int kFeChannels = 4;
+constexpr int kFeTokens = 16;
 hipError_t launch_frontend(const uint16_t* xbc, const float* conv_w, const float* conv_b, const float* x_scale,
                            const float* B_scale, const float* C_scale, const float* dt_raw, const float* dt_bias,
                            int8_t* x, int8_t* B, int8_t* C, float* dt, int32_t batch, int64_t seqlen,

@@ -209,7 +209,7 @@ def _fe(lib, **kw):
     (dict(dconv=3), UNSUPPORTED),
     (dict(P=20), UNSUPPORTED),
     (dict(N=12), UNSUPPORTED),
-    (dict(b=65536, L=(1 << 19)), UNSUPPORTED),   # 2^16 batches * 2 channel blocks * 2^16 strips
+    (dict(b=65536, L=(1 << 19)), UNSUPPORTED),   # 2^16 batches * 4 channel blocks * 2^15 strips
     (dict(L=0, xbc=None, x=None), OK),
 ])
 def test_frontend_validation(lib, kw, status):
