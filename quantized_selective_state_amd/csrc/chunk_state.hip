@@ -537,18 +537,18 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
         // this lane's 16 states of the row (4 tiles x 4): one 16-byte piece per limb when the
         // 64-state block is full (the workspace stores full blocks dword-transposed), else
         // 4-byte pieces in natural order
+        // V = trunc(256 t + 128), |t| <= 127: limb 1 is byte 1 of V, limb 2 byte 0 with the bias
+        // bit flipped; byte permutes gather them four at a time
         v4u Q1, Q2;
 #pragma unroll
         for (int t = 0; t < kOwn; ++t) {
-          uint32_t q1 = 0, q2 = 0;
+          uint32_t V[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int32_t V = int32_t(fmaf(H[t][i], inv, 128.f));   // 256 t + 128, |t| <= 127
-            q1 |= (uint32_t(V >> 8) & 0xffu) << (8 * i);
-            q2 |= ((uint32_t(V) & 0xffu) ^ 0x80u) << (8 * i);
-          }
-          Q1[t] = q1;
-          Q2[t] = q2;
+          for (int i = 0; i < 4; ++i) V[i] = uint32_t(int32_t(fmaf(H[t][i], inv, 128.f)));
+          const uint32_t b1lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0501u), b1hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0501u);
+          const uint32_t b0lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0400u), b0hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0400u);
+          Q1[t] = __builtin_amdgcn_perm(b1hi, b1lo, 0x05040100u);
+          Q2[t] = __builtin_amdgcn_perm(b0hi, b0lo, 0x05040100u) ^ 0x80808080u;
         }
         const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N) + 64 * kh;
         if (64 * kh + 64 <= N) {
@@ -568,13 +568,13 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
 
       // ---- fp32 partials; hand over the other wave's tiles, then H <- exp(Acs_last) H + S_c
       const float post = sxB * exp2i(gexp[cl] + 1);   // t = x_scaled / 2^(e + 1) (23-bit weights)
-      const float post_lo = post * (1.f / 65536.f);
+      // partial S / post = acc0 + (256 acc1 + acc2) / 65536; post is applied once, in the update
       auto partial = [&](int t) {
         v4f r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
-          r[i] = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+          r[i] = fmaf(float(lo), 1.f / 65536.f, float(acc[t][0][i]));
         }
         return r;
       };
@@ -591,9 +591,9 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if constexpr (kPS)
-            H[t][i] = fmaf(decay, H[t][i], (mine[t][i] + other[i]) * sig[t][i]);
+            H[t][i] = fmaf(decay, H[t][i], (mine[t][i] + other[i]) * (post * sig[t][i]));
           else
-            H[t][i] = fmaf(decay, H[t][i], mine[t][i] + other[i]);
+            H[t][i] = fmaf(decay, H[t][i], (mine[t][i] + other[i]) * post);
         }
       }
     };
