@@ -192,8 +192,8 @@ ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x
 
 /*
  * ssdq_chunk_scan with SSDi8's output correction: every output also receives a per-(head,
- * channel) term (SSDi8 abstract: an error correction term based on per-channel error statistics;
- * Figure 1b: mean correction; Tables 6 and 16).  The pages give no algebra for it; the reading
+ * channel) term (the SSDi8 abstract describes a correction derived from error statistics gathered
+ * per channel, Figure 1b labels it a mean correction; Tables 6 and 16).  The pages give no algebra for it; the reading
  * taken is the plainest they support: an additive term, calibrated offline (like the static
  * scales) as the mean over a calibration set of the unquantized scan's y minus the quantized
  * scan's y, channel by channel.  Calibration is the caller's; the library only applies it:

@@ -292,8 +292,8 @@ def ssd_values_one(v: dict, b: int, h: int):
 
 
 def mean_correction(inp: dict, threads: int | None = None) -> np.ndarray:
-    """SSDi8's per-channel mean correction (an error correction term from per-channel error
-    statistics, SSDi8 abstract; "mean correction", Figure 1b), calibrated on a draw `inp` (binary16
+    """SSDi8's per-channel mean correction (its abstract describes a correction derived from error
+    statistics gathered per channel; Figure 1b labels it a mean correction), calibrated on a draw `inp` (binary16
     x, B, C with their static scales, dt, A, D, h0) the plainest way the pages support: the error
     of the quantized scan's output channel (h, p) is y_ref - y_q, with y_ref the recurrence over the
     unquantized binary16 inputs and y_q the recurrence over their INT8 codes; the correction is

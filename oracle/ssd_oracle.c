@@ -37,9 +37,9 @@
  *    [-127, 127] with s = max|row| / 127 (the reading stated at
  *    requantize_row_i8).
  *
- *  - the output correction (SSDi8's mean correction: its abstract names an error correction term
- *    from per-channel error statistics, Figure 1b a mean correction, Table 6 ablates it and
- *    Table 16 times it; no algebra is given): every y the recurrences above produce may carry a
+ *  - the output correction (SSDi8's mean correction: its abstract describes a correction derived
+ *    from error statistics gathered per channel, Figure 1b labels it a mean correction, Table 6
+ *    ablates it and Table 16 times it; no algebra is given): every y the recurrences above produce may carry a
  *    per-(head, channel) additive term y_corr[h, p].  oracle_ssd_sequential_values runs the same
  *    recurrence over real-valued (unquantized) inputs; the calibration of y_corr as the mean,
  *    over a calibration draw's (batch, token) positions, of that reference's y minus the

@@ -1,8 +1,9 @@
 """Pins for the oracle's output correction (SSDi8's per-channel mean correction) and for the
 recurrence over real-valued inputs that the correction is calibrated against (CPU only).
 
-The pages name the correction (an error correction term from per-channel error statistics,
-SSDi8 abstract; "mean correction", Figure 1b; ablated in Table 6, timed in Table 16) but give
+The pages name the correction (the SSDi8 abstract describes a correction derived from error
+statistics gathered per channel; Figure 1b labels it a mean correction; ablated in Table 6, timed
+in Table 16) but give
 neither its algebra nor any value, so nothing here is pinned by a printed number; the reading
 (an additive per-(head, channel) term, calibrated as the mean over a calibration draw of the
 unquantized scan's y minus the quantized scan's y) is pinned by exact identities instead:
