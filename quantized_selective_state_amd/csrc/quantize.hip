@@ -209,7 +209,10 @@ __global__ void __launch_bounds__(256) quantize_scalar(const uint16_t* __restric
 
 int grid_for(int64_t work, int block) {
   int64_t g = (work + block - 1) / block;
-  const int64_t cap = 256 * 64;  // enough blocks to fill 256 CUs; grid-stride beyond that
+  // one work unit per thread (a 16-element piece, say): at the benchmark's sizes a grid of
+  // 2^14 grid-striding blocks was 5% slower than a block per 256 pieces; grid-stride only past
+  // 2^22 blocks (so that a 32-bit grid stride stays below 2^30)
+  const int64_t cap = int64_t(1) << 22;
   if (g > cap) g = cap;
   return int(g < 1 ? 1 : g);
 }
