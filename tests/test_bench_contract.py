@@ -73,6 +73,7 @@ def test_specified_bytes_per_token(shape, quant, scan):
 def test_headline_is_the_largest_prefill_workload():
     import workloads
     sizes = {n: workloads.WORKLOADS[n].tokens * workloads.WORKLOADS[n].nheads for n in bench.PREFILL_WORKLOADS}
+    assert "tiny" in bench.PREFILL_WORKLOADS and "tiny" in bench.LATENCY_ONLY
     assert bench.HEADLINE == max(sizes, key=sizes.get) == "mamba2-8b-prefill"
     assert bench.parse([]).workload is None          # default: every prefill workload
 
