@@ -173,3 +173,21 @@ def test_full_workload(name):
     del qx, qB, qC
     note(f"oracle {name}: all {c.batch * c.H} sequences")
     compare_full(c, lambda b: y[b].float().cpu().numpy(), lambda b: hf[b].cpu().numpy(), name)
+
+
+def test_maximum_chunk_count():
+    # the longest sequence the scan accepts at chunk 64: 65535 chunks (4,194,240 tokens), one
+    # narrow head (three-kernel plan: state passing walks all 65535 chunks in one sequence);
+    # one chunk more is refused on the host
+    import quantized_selective_state_amd as ssdq
+    L = 65535 * 64
+    inp = workloads.make_custom_prefill(18, batch=1, seqlen=L, nheads=1, headdim=16, dstate=16, ngroups=1,
+                                        chunk=64, h0_std=0.1)
+    note(f"maximum chunk count: L={L}")
+    _check_full(inp, tag="65535 chunks")
+    qx = torch.zeros((1, L + 64, 1, 16), dtype=torch.int8, device=dev())
+    qb = torch.zeros((1, L + 64, 1, 16), dtype=torch.int8, device=dev())
+    one = torch.ones(1, device=dev())
+    with pytest.raises(ssdq.SSDQError) as e:
+        ssdq.chunk_scan(qx, one, qb, one, qb, one, torch.zeros((1, L + 64, 1), device=dev()), -one, chunk=64)
+    assert e.value.status == ssdq.SSDQ_ERROR_UNSUPPORTED
