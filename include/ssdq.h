@@ -114,6 +114,8 @@ ssdq_status ssdq_quantize_per_channel(const void* x_f16, int8_t* q, const float*
  * each region starting at a 256-byte boundary:
  *   Acs     fp32 (batch, nheads, nchunks, chunk): within-chunk inclusive cumsum of dt * A
  *           (padded past the sequence end with the last value)           -- written by stage 0
+ *   Dtc     fp32 (batch, nheads, nchunks, chunk): dt in the same chunk order, 0 past the
+ *           sequence end (one contiguous row per chunk for stage 2)      -- written by stage 0
  *   S       fp32 (batch, nchunks, nheads, headdim, dstate): chunk states  -- written by stage 0
  *   Hprev   int8 (batch, nchunks, nheads, 2, headdim, dstate) and
  *   Hscale  fp32 (batch, nchunks, nheads, headdim): the state entering each chunk is
@@ -123,7 +125,7 @@ ssdq_status ssdq_quantize_per_channel(const void* x_f16, int8_t* q, const float*
  *           64 blk + 16 t + 4 k + (0..3) are stored at 64 blk + 16 k + 4 t + (0..3) (a 4x4
  *           transpose of 4-byte groups: the writing lanes store 16 contiguous bytes); a
  *           partial last block (dstate % 64 != 0) is stored in natural order.
- * When ssdq_chunk_scan_state_fused(batch, nheads) is 1, stage 0 writes Acs, Hprev, Hscale
+ * When ssdq_chunk_scan_state_fused(batch, nheads) is 1, stage 0 writes Acs, Dtc, Hprev, Hscale
  * (and h_final) itself, stage 1 does nothing, and S is not written. */
 size_t ssdq_chunk_scan_workspace_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                       int32_t dstate, int32_t chunk);
@@ -241,8 +243,8 @@ ssdq_status ssdq_chunk_scan_per_state(const int8_t* x, const float* x_scale, con
 /*
  * ssdq_chunk_scan without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The
- * intermediates (Acs, the chunk states of the three-kernel plan, the carried-state limbs and
- * their row scales) live in one static device array of SSDQ_NOALLOC_SCRATCH_BYTES that the
+ * intermediates (Acs, the chunk-ordered dt, the chunk states of the three-kernel plan, the
+ * carried-state limbs and their row scales) live in one static device array of SSDQ_NOALLOC_SCRATCH_BYTES that the
  * library holds on every device it runs on until the process ends; the call allocates and
  * frees nothing.  Arguments, shapes, accuracy and validation are those of ssdq_chunk_scan, and
  * the results are those of ssdq_chunk_scan with the same arguments (the same kernels run).
@@ -262,7 +264,7 @@ ssdq_status ssdq_chunk_scan_noalloc(const int8_t* x, const float* x_scale, const
                                     int32_t ngroups, int32_t chunk, hipStream_t stream);
 
 /* Scratch bytes ssdq_chunk_scan_noalloc needs for this shape on the current device (host; 0 on
- * invalid shapes): the Acs, carried-state and row-scale regions, plus the fp32 chunk states when
+ * invalid shapes): the Acs, Dtc, carried-state and row-scale regions, plus the fp32 chunk states when
  * the three-kernel plan runs, each rounded up to 256 bytes. */
 size_t ssdq_chunk_scan_noalloc_scratch_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                             int32_t dstate, int32_t chunk);

@@ -219,9 +219,10 @@ def workspace_layout(batch: int, seqlen: int, nheads: int, headdim: int, dstate:
     hp = r256(2 * batch * nc * nheads * headdim * dstate)
     return dict(nchunks=nc,
                 acs=(0, "float32", (batch, nheads, nc, chunk)),
-                states=(acs, "float32", (batch, nc, nheads, headdim, dstate)),
-                hprev=(acs + st, "int8", (batch, nc, nheads, 2, headdim, dstate)),
-                hscale=(acs + st + hp, "float32", (batch, nc, nheads, headdim)))
+                dtc=(acs, "float32", (batch, nheads, nc, chunk)),
+                states=(2 * acs, "float32", (batch, nc, nheads, headdim, dstate)),
+                hprev=(2 * acs + st, "int8", (batch, nc, nheads, 2, headdim, dstate)),
+                hscale=(2 * acs + st + hp, "float32", (batch, nc, nheads, headdim)))
 
 
 class ScanBuffers:
@@ -290,7 +291,7 @@ class ScanBuffers:
         b, L, H, P, N, G, Q = self.dims
         lay = workspace_layout(b, L, H, P, N, Q)
         out = {}
-        for key in ("acs", "states", "hprev", "hscale"):
+        for key in ("acs", "dtc", "states", "hprev", "hscale"):
             off, dtype, shape = lay[key]
             dt = getattr(torch, dtype)
             n = 1

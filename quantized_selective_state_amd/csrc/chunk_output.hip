@@ -155,7 +155,7 @@ struct Params {
   const float* B_scale;
   const int8_t* C;
   const float* C_scale;
-  const float* dt;
+  const float* dtc;   // dt in chunk order: (batch, nheads, nchunks, chunk), 0 past the end
   const float* D;
   const float* acs;
   const int8_t* hprev;
@@ -178,7 +178,7 @@ struct LaneConst {
   uint32_t x_off[kXTasks];      // x piece: token row j * H*P + 16-byte column group
   int x_lds[kXTasks];           // LDS position (halves) of its first 8 channels
   uint32_t c_off[2][2];         // C codes of this lane's output row, per pass and K half
-  uint32_t acs_off, dt_off, hs_off;
+  uint32_t acs_off, hs_off;   // acs_off also addresses the chunk-ordered dt row
 };
 
 // Buffer resources of one item: base at the item's first element, size up to the end of its
@@ -193,7 +193,7 @@ struct ItemRsrc {
 // change of (batch, chunk) decodes the item index again.
 struct ItemPos {
   int h, g, hg, len;   // hg: the head's index within its group
-  uint32_t row;        // (b seqlen + t0) nheads + h: first (token, head) row of x, y and dt
+  uint32_t row;        // (b seqlen + t0) nheads + h: first (token, head) row of x and y
   uint32_t grow;       // (b seqlen + t0) ngroups + g: first (token, group) row of B and C
   uint32_t seg;        // (b nchunks + c) nheads + h: carried-state slot (limbs, row scales)
   uint32_t aseg;       // (b nheads + h) nchunks + c: the Acs row
@@ -237,7 +237,7 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a)
   const uint32_t last = uint32_t(p.len - 1), gn = uint32_t(a.ngroups * a.N), P = uint32_t(a.P), N = uint32_t(a.N);
   ItemRsrc r;
   r.acs = make_rsrc(a.acs + wide(p.aseg, uint32_t(a.Q)), uint32_t(a.Q) * 4u);
-  r.dt = make_rsrc(a.dt + p.row, (last * uint32_t(a.nheads) + 1u) * 4u);
+  r.dt = make_rsrc(a.dtc + wide(p.aseg, uint32_t(a.Q)), uint32_t(a.Q) * 4u);
   r.hs = make_rsrc(a.hscale + wide(p.seg, P), P * 4u);
   r.mu = make_rsrc(a.ycorr + uint32_t(p.h) * P, a.ycorr ? P * 4u : 0u);
   r.B = make_rsrc(a.B + wide(p.grow, N), last * gn + N);
@@ -277,7 +277,7 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
   }
   if (threadIdx.x < kMaxQ) {   // wave-uniform: one value per token
     f.acs = buf_loadf(r.acs, lc.acs_off);
-    f.dt = buf_loadf(r.dt, lc.dt_off);
+    f.dt = buf_loadf(r.dt, lc.acs_off);
   }
   if (threadIdx.x < kMaxP) {
     f.hs = buf_loadf(r.hs, lc.hs_off);
@@ -363,7 +363,6 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       lc.c_off[pass][s2] = (lbp < nlb && 64 * s2 + 16 * kg < N) ? l * gn + 64 * s2 + 16 * kg : kOutOfRange;
   }
   lc.acs_off = uint32_t(tid & (kMaxQ - 1)) * 4u;
-  lc.dt_off = uint32_t(tid & (kMaxQ - 1)) * uint32_t(a.nheads) * 4u;
   lc.hs_off = uint32_t(tid & (kMaxP - 1)) * 4u;
   // hot-loop LDS bases: for rows js + lcol with js a multiple of 16 the B swizzle term depends
   // on lcol only, so every hot-loop address is a per-lane base plus a multiple of the step
@@ -386,7 +385,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // tile in LDS serve all the group's items of the range.  The global loads of the next item
   // are issued while the current item is computed (at the start of its trip, the x codes
   // between its two passes).  The range is XCD-aware: the blocks of one XCD take consecutive
-  // ranges, so a chunk's B, C and the dt lines its heads share are fetched into one L2.
+  // ranges, so a chunk's B, C and the x lines its heads share are fetched into one L2.
   const int per = (a.nitems + int(gridDim.x) - 1) / int(gridDim.x);
   int it = xcd_remap(blockIdx.x, gridDim.x) * per;
   const int it_end = min(it + per, a.nitems);
@@ -834,7 +833,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 }  // namespace
 
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
-  Params p{a.x, a.x_scale, a.B, a.B_scale, a.C, a.C_scale, a.dt, a.D, a.acs, a.hprev, a.hscale, a.ycorr, a.y,
+  Params p{a.x, a.x_scale, a.B, a.B_scale, a.C, a.C_scale, a.dtc, a.D, a.acs, a.hprev, a.hscale, a.ycorr, a.y,
            s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.nchunks,
            s.batch * s.nchunks * s.nheads,
            make_fastdiv(uint32_t(s.nheads)), make_fastdiv(uint32_t(s.nchunks)),

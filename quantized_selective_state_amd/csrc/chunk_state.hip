@@ -2,7 +2,9 @@
 // chunk size:
 //
 //  (a) chunk cumsum: Acs[j] = sum_{i <= j} dt_i A_h inside the chunk (tokens past the end
-//      of the sequence add 0), written to the workspace for the later stages;
+//      of the sequence add 0), written to the workspace for the later stages, and dt itself in
+//      the same chunk order (one contiguous row per chunk and head for the output stage, where
+//      the token-major dt would cost a separate cache line per token);
 //  (b) chunk state: the state the chunk contributes on its own,
 //
 //        S_c[p, n] = sum_j w_j xhat[j, p] Bhat[j, n],   w_j = exp(Acs_last - Acs_j) dt_j
@@ -94,7 +96,8 @@ template <int Q>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) chunk_state_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
     const float* __restrict__ B_scale, const float* __restrict__ C_scale_ps, const float* __restrict__ dt,
-    const float* __restrict__ A, float* __restrict__ acs, float* __restrict__ states, int64_t seqlen, int32_t nheads,
+    const float* __restrict__ A, float* __restrict__ acs, float* __restrict__ dtc, float* __restrict__ states,
+    int64_t seqlen, int32_t nheads,
     int32_t headdim, int32_t dstate, int32_t ngroups, int32_t nchunks) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
   __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
@@ -143,7 +146,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
   for (int w2 = 0; w2 < kWaves - 1; ++w2) pre += w2 < wave ? red[w2] : 0.f;
   const float acs_t = v + pre;
-  if (tid < Q) acs[((int64_t(b) * nheads + h) * nchunks + c) * Q + tid] = acs_t;
+  if (tid < Q) {
+    const int64_t o = ((int64_t(b) * nheads + h) * nchunks + c) * Q + tid;
+    acs[o] = acs_t;
+    dtc[o] = d;   // dt in chunk order for the output stage (0 past the end)
+  }
   if (tid == len - 1) acs_last_s = acs_t;
   __syncthreads();
 
@@ -284,7 +291,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
     const float* __restrict__ B_scale, const float* __restrict__ C_scale, const float* __restrict__ dt,
     const float* __restrict__ A,
-    const float* h0, float* h_final, float* __restrict__ acs, int8_t* __restrict__ hprev,
+    const float* h0, float* h_final, float* __restrict__ acs, float* __restrict__ dtc, int8_t* __restrict__ hprev,
     float* __restrict__ hscale, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
     int32_t ngroups, int32_t nchunks) {
   // double-buffered chunk tiles, as separate objects so that the compiler can tell the buffer
@@ -387,7 +394,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     for (int u = 0; u < kTok; ++u) dtg[u] = buf_loadf(rdt, uint32_t(lane * kTok + u) * uint32_t(nheads) * 4u);
   };
   // ---- per-chunk quantities of a group, one chunk per wave and no block barriers: the chunk
-  // cumsum of dt A (written to the workspace), its decay exp(Acs_last), the LUT_state weights
+  // cumsum of dt A (written to the workspace with dt in chunk order), its decay exp(Acs_last), the LUT_state weights
   // w_j = exp(Acs_last - Acs_j) dt_j, their power-of-two range 2^e and the integer limb
   // coefficients OM_j, CB_j
   auto group_prologue = [&](int g0) {
@@ -406,9 +413,12 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
     const float excl = incl - run;
 #pragma unroll
     for (int u = 0; u < kTok; ++u) a[u] += excl;
-    float* arow = acs + ((int64_t(b) * nheads + h) * nchunks + c) * Q + lane * kTok;
+    const int64_t ro = ((int64_t(b) * nheads + h) * nchunks + c) * Q + lane * kTok;
 #pragma unroll
-    for (int u = 0; u < kTok; ++u) arow[u] = a[u];
+    for (int u = 0; u < kTok; ++u) {
+      acs[ro + u] = a[u];
+      dtc[ro + u] = dtg[u];   // dt in chunk order for the output stage (0 past the end)
+    }
     // Acs at the chunk's last token
     const int lastl = (len - 1) / kTok, lastu = (len - 1) % kTok;
     float asel = a[0];
@@ -626,7 +636,7 @@ hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t
   const int nblocks = s.batch * s.nchunks * s.nheads;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
-                       a.bc_per_state ? a.C_scale : nullptr, a.dt, a.A, a.acs, a.states, s.seqlen, s.nheads,
+                       a.bc_per_state ? a.C_scale : nullptr, a.dt, a.A, a.acs, a.dtc, a.states, s.seqlen, s.nheads,
                        s.headdim, s.dstate, s.ngroups, s.nchunks);
   };
   switch (s.chunk) {
@@ -653,7 +663,7 @@ hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t 
   const int nblocks = s.batch * s.nheads;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kSThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale, a.C_scale,
-                       a.dt, a.A, a.h0, a.h_final, a.acs, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim,
+                       a.dt, a.A, a.h0, a.h_final, a.acs, a.dtc, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim,
                        s.dstate, s.ngroups, s.nchunks);
   };
   if (a.bc_per_state) {

@@ -52,6 +52,22 @@ ssdq_status check_scan_shape(int32_t batch, int64_t seqlen, int32_t nheads, int3
   return SSDQ_SUCCESS;
 }
 
+// Workspace regions in order, each at a 256-byte boundary: Acs, the chunk-ordered dt, the fp32
+// chunk states (left out of the compact layout when the folded state kernel runs), the
+// carried-state limbs and their row scales.
+void carve(const ScanShape& s, char* base, bool with_states, ScanArgs* a) {
+  size_t off = 0;
+  a->acs = reinterpret_cast<float*>(base + off);
+  off += s.acs_bytes;
+  a->dtc = reinterpret_cast<float*>(base + off);
+  off += s.acs_bytes;
+  a->states = reinterpret_cast<float*>(base + off);   // not read or written by the folded plan
+  if (with_states) off += round256(s.state_bytes);
+  a->hprev = reinterpret_cast<int8_t*>(base + off);
+  off += s.hprev_bytes;
+  a->hscale = reinterpret_cast<float*>(base + off);
+}
+
 ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,
                             const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                             const float* A, const float* D, const float* h0, void* y, float* h_final,
@@ -80,11 +96,7 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   a->h0 = h0;
   a->y = static_cast<_Float16*>(y);
   a->h_final = h_final;
-  a->acs = static_cast<float*>(workspace);
-  char* ws = static_cast<char*>(workspace);
-  a->states = reinterpret_cast<float*>(ws + s->acs_bytes);
-  a->hprev = reinterpret_cast<int8_t*>(ws + s->acs_bytes + s->state_bytes);
-  a->hscale = reinterpret_cast<float*>(ws + s->acs_bytes + s->state_bytes + s->hprev_bytes);
+  carve(*s, static_cast<char*>(workspace), true, a);
   return SSDQ_SUCCESS;
 }
 
@@ -126,11 +138,11 @@ void* device_scratch() {
   return g_scratch_ptr[dev];
 }
 
-// The compact scratch layout of one prefill call: Acs, the fp32 chunk states only when the
-// three-kernel plan runs (fused = false), the carried-state limbs and their row scales, each
-// region starting at a 256-byte boundary.
+// The compact scratch layout of one prefill call: Acs, the chunk-ordered dt, the fp32 chunk
+// states only when the three-kernel plan runs (fused = false), the carried-state limbs and their
+// row scales, each region starting at a 256-byte boundary.
 size_t noalloc_bytes(const ScanShape& s, bool fused) {
-  return s.acs_bytes + (fused ? 0 : round256(s.state_bytes)) + s.hprev_bytes + s.hscale_bytes;
+  return 2 * s.acs_bytes + (fused ? 0 : round256(s.state_bytes)) + s.hprev_bytes + s.hscale_bytes;
 }
 
 }  // namespace
@@ -298,13 +310,7 @@ ssdq_status ssdq_chunk_scan_noalloc(const int8_t* x, const float* x_scale, const
   if (noalloc_bytes(s, fused) > size_t(SSDQ_NOALLOC_SCRATCH_BYTES)) return SSDQ_ERROR_SCRATCH_LIMIT;
   char* base = static_cast<char*>(device_scratch());
   if (base == nullptr) return SSDQ_ERROR_LAUNCH;
-  a.acs = reinterpret_cast<float*>(base);
-  size_t off = s.acs_bytes;
-  a.states = reinterpret_cast<float*>(base + off);   // not read or written by the fused plan
-  if (!fused) off += round256(s.state_bytes);
-  a.hprev = reinterpret_cast<int8_t*>(base + off);
-  off += s.hprev_bytes;
-  a.hscale = reinterpret_cast<float*>(base + off);
+  carve(s, base, !fused, &a);
   for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
     const ssdq_status r = run_stage(stage, s, a, stream);
     if (r != SSDQ_SUCCESS) return r;

@@ -42,11 +42,11 @@ struct ScanShape {
   int64_t seqlen;
   int32_t nheads, headdim, dstate, ngroups, chunk;
   int32_t nchunks;
-  size_t acs_bytes;     // Acs region, rounded up to 256 bytes
+  size_t acs_bytes;     // Acs region, rounded up to 256 bytes (the chunk-ordered dt region has the same size)
   size_t state_bytes;   // chunk-state region (fp32)
   size_t hprev_bytes;   // state entering each chunk as two int8 limbs, rounded up to 256 bytes
   size_t hscale_bytes;  // its per-row scales, rounded up to 256 bytes
-  size_t total_bytes() const { return acs_bytes + state_bytes + hprev_bytes + hscale_bytes; }
+  size_t total_bytes() const { return 2 * acs_bytes + state_bytes + hprev_bytes + hscale_bytes; }
 };
 
 struct ScanArgs {
@@ -64,6 +64,7 @@ struct ScanArgs {
   _Float16* y;
   float* h_final;
   float* acs;         // workspace: (batch, nheads, nchunks, chunk)
+  float* dtc;         // workspace: dt in the same (batch, nheads, nchunks, chunk) order, 0 past the end
   float* states;      // workspace: (batch, nchunks, nheads, headdim, dstate) fp32
   int8_t* hprev;      // workspace: (batch, nchunks, nheads, 2, headdim, dstate) int8 limbs
   float* hscale;      // workspace: (batch, nchunks, nheads, headdim)

@@ -67,14 +67,15 @@ def test_status_strings(lib):
 def _ws(b, L, H, P, N, Q):
     r = lambda v: (v + 255) // 256 * 256
     nc = -(-L // Q)
-    return (r(4 * b * H * nc * Q) + 4 * b * nc * H * P * N + r(2 * b * nc * H * P * N) + r(4 * b * nc * H * P))
+    return (2 * r(4 * b * H * nc * Q) + 4 * b * nc * H * P * N + r(2 * b * nc * H * P * N) + r(4 * b * nc * H * P))
 
 
 def test_workspace_size(lib):
-    # Acs fp32 + chunk states fp32 + carried state fp16 + row scales fp32, 256-byte aligned regions
+    # Acs fp32 + chunk-ordered dt fp32 + chunk states fp32 + carried-state limbs (2 x int8) + row
+    # scales fp32, 256-byte aligned regions
     assert lib.ssdq_chunk_scan_workspace_size(4, 2048, 64, 64, 128, 256) == _ws(4, 2048, 64, 64, 128, 256)
     assert lib.ssdq_chunk_scan_workspace_size(1, 250, 2, 16, 16, 64) == _ws(1, 250, 2, 16, 16, 64)
-    assert _ws(1, 250, 2, 16, 16, 64) == 2048 + 4 * 4 * 2 * 16 * 16 + 2 * 4 * 2 * 16 * 16 + 512
+    assert _ws(1, 250, 2, 16, 16, 64) == 2 * 2048 + 4 * 4 * 2 * 16 * 16 + 2 * 4 * 2 * 16 * 16 + 512
     assert lib.ssdq_chunk_scan_workspace_size(1, 256, 4, 16, 16, 48) == 0     # unsupported chunk
     assert lib.ssdq_chunk_scan_workspace_size(0, 256, 4, 16, 16, 64) == 0
 
@@ -259,7 +260,7 @@ def test_noalloc_validates_before_touching_the_device(lib):
     b, L, H, Pd, N, Q = 1, 300, 8, 32, 64, 64
     nc = -(-L // Q)
     assert lib.ssdq_chunk_scan_noalloc_scratch_size(b, L, H, Pd, N, Q) == (
-        r(4 * b * H * nc * Q) + r(4 * b * nc * H * Pd * N) + r(2 * b * nc * H * Pd * N) + r(4 * b * nc * H * Pd))
+        2 * r(4 * b * H * nc * Q) + r(4 * b * nc * H * Pd * N) + r(2 * b * nc * H * Pd * N) + r(4 * b * nc * H * Pd))
     assert lib.ssdq_chunk_scan_noalloc_scratch_size(0, L, H, Pd, N, Q) == 0
 
 

@@ -118,6 +118,7 @@ def test_stage_intermediates():
     buf.run_stage(0)                       # chunk cumsum + chunk states
     torch.cuda.synchronize()
     acs = views["acs"].cpu().numpy()
+    dtc = views["dtc"].cpu().numpy()
     S = views["states"].cpu().numpy().copy()
     buf.run_stage(1)                       # state passing -> carried state as two int8 limbs + row scales
     torch.cuda.synchronize()
@@ -132,6 +133,10 @@ def test_stage_intermediates():
             valid = np.isfinite(a_ref)
             # fp32 accumulation of up to 256 terms
             assert np.max(np.abs(acs[b, h][valid] - a_ref[valid])) <= 2e-5 * max(1.0, np.max(np.abs(a_ref[valid])))
+            # dt in chunk order: the input's values bit for bit, zeros past the sequence end
+            d_pad = np.zeros(nc * 256, dtype=np.float32)
+            d_pad[:c.L] = inp["dt"][b, :, h]
+            assert np.array_equal(dtc[b, h].reshape(-1), d_pad)
             S_ref = oracle.chunk_state(c, b, h, 256)
             # three INT8 limbs (~2^-23 of the chunk max) plus fp32 cumsum/exp of the decay
             assert rel_err(S[b, :, h], S_ref) <= 5e-5
