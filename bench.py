@@ -177,13 +177,15 @@ def kernel_bytes(b, L, H, P, N, G, Q):
     st32 = b * nc * H * P * N * 4          # chunk states, fp32
     st16 = b * nc * H * P * N * 2 + b * nc * H * P * 4   # carried state: two int8 limbs + row scales
     hfin = b * H * P * N * 4
+    # the state stages write Acs and dt in chunk order (each b H nc Q fp32); the output stage reads
+    # both from there
     return {
         "quantize": 3 * x + 6 * bc,            # x, B and C in one launch: fp16 in, int8 out
-        "chunk_state": x + bc + dt + acs + st32,            # also writes Acs
+        "chunk_state": x + bc + dt + 2 * acs + st32,
         "state_passing": st32 + acs // Q * 1 + st16 + hfin,
-        "chunk_output": x + 2 * bc + dt + acs + st16 + 2 * tok * H * P,
+        "chunk_output": x + 2 * bc + 2 * acs + st16 + 2 * tok * H * P,
         # stages 0 + 1 in one kernel: chunk states stay on chip
-        "state_scan": x + bc + dt + acs + st16 + hfin,
+        "state_scan": x + bc + dt + 2 * acs + st16 + hfin,
     }
 
 
