@@ -141,8 +141,8 @@ def quantize_values(v16: np.ndarray, scale: float) -> np.ndarray:
 
 class Codes:
     """Quantized prefill inputs in the scan's layout; y_corr (H, P) float32 is the optional output
-    correction added to every y.  sB and sC are one scale per group (G,) or one per (group,
-    state) (G, N)."""
+    correction added to every y.  sx is one scale per head (H,) or one per (head, channel)
+    (H, P); sB and sC are one scale per group (G,) or one per (group, state) (G, N)."""
 
     def __init__(self, qx, sx, qB, sB, qC, sC, dt, A, D=None, h0=None, y_corr=None):
         self.qx = _c(qx, np.int8)
@@ -159,17 +159,26 @@ class Codes:
         assert self.dt.shape == (self.batch, self.L, self.H)
         assert self.H % self.G == 0
         assert self.sB.shape == self.sC.shape and self.sB.shape in ((self.G,), (self.G, self.N))
+        assert self.sx.shape in ((self.H,), (self.H, self.P))
         self.per_state = int(self.sB.shape == (self.G, self.N))
+        self.x_per_channel = int(self.sx.shape == (self.H, self.P))
+
+    @property
+    def scale_flags(self) -> int:
+        """The oracle's scale-layout word: bit 0 B, C per (group, state); bit 1 x per (head, channel)."""
+        return int(self.per_state) | (int(self.x_per_channel) << 1)
 
 
 def _quantize_bc(t16: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Codes under one scale per row group (1-D scale) or one per (group, element) (2-D)."""
     return quantize_per_channel(t16, scale) if np.ndim(scale) == 2 else quantize(t16, scale)
 
 
 def codes_from_inputs(inp: dict) -> Codes:
     """Quantize a workload draw with the oracle's quantizer (with its output correction y_corr,
-    if the draw carries one; B and C scales per group (G,) or per (group, state) (G, N))."""
-    return Codes(quantize(inp["x16"], inp["x_scale"]), inp["x_scale"],
+    if the draw carries one; x scales per head (H,) or per (head, channel) (H, P); B and C scales
+    per group (G,) or per (group, state) (G, N))."""
+    return Codes(_quantize_bc(inp["x16"], inp["x_scale"]), inp["x_scale"],
                  _quantize_bc(inp["B16"], inp["B_scale"]), inp["B_scale"],
                  _quantize_bc(inp["C16"], inp["C_scale"]), inp["C_scale"],
                  inp["dt"], inp["A"], inp.get("D"), inp.get("h0"), inp.get("y_corr"))
@@ -185,7 +194,7 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
         lib.oracle_ssd_sequential_state_f16(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                             _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
                                             c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
-                                            _ptr(c.y_corr), c.per_state)
+                                            _ptr(c.y_corr), c.scale_flags)
         return y, hf, None
     bounds = None
     if chunk > 0:
@@ -193,7 +202,7 @@ def ssd_one(c: Codes, b: int, h: int, chunk: int = 0, state_f16: bool = False):
     lib.oracle_ssd_sequential(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                               _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(c.h0),
                               c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf),
-                              chunk, _ptr(bounds), _ptr(c.y_corr), c.per_state)
+                              chunk, _ptr(bounds), _ptr(c.y_corr), c.scale_flags)
     return y, hf, bounds
 
 
@@ -268,7 +277,7 @@ def ssd_one_state_i8(c: Codes, b: int, h: int, q0=None, s0=None, scales_per_step
     lib.oracle_ssd_sequential_state_i8(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.qC), _ptr(c.sC),
                                        _ptr(c.dt), _ptr(c.A), _ptr(c.D), _ptr(q0), _ptr(s0),
                                        c.batch, c.L, c.H, c.P, c.N, c.G, b, h, _ptr(y), _ptr(hf), _ptr(q),
-                                       _ptr(s), _ptr(u), _ptr(steps), _ptr(c.y_corr), c.per_state)
+                                       _ptr(s), _ptr(u), _ptr(steps), _ptr(c.y_corr), c.scale_flags)
     if scales_per_step:
         return y, hf, q, s, u, steps
     return y, hf, q, s, u
@@ -382,14 +391,14 @@ def chunk_state(c: Codes, b: int, h: int, chunk: int) -> np.ndarray:
     nc = (c.L + chunk - 1) // chunk
     out = np.empty((nc, c.P, c.N))
     lib.oracle_chunk_state(_ptr(c.qx), _ptr(c.sx), _ptr(c.qB), _ptr(c.sB), _ptr(c.dt), _ptr(c.A),
-                           c.L, c.H, c.P, c.N, c.G, b, h, chunk, _ptr(out), c.per_state)
+                           c.L, c.H, c.P, c.N, c.G, b, h, chunk, _ptr(out), c.scale_flags)
     return out
 
 
 def decode_as_prefill(dec: dict) -> Codes:
     """The decode workload as one prefill over its steps: the recurrence is the
     same, with the decode state as h0.  Codes come from the oracle quantizer."""
-    qx = quantize(dec["x16"], dec["x_scale"])      # (T, b, H, P)
+    qx = _quantize_bc(dec["x16"], dec["x_scale"])      # (T, b, H, P)
     qB = _quantize_bc(dec["B16"], dec["B_scale"])      # (T, b, G, N)
     qC = _quantize_bc(dec["C16"], dec["C_scale"])
     tr = lambda a: np.ascontiguousarray(np.swapaxes(a, 0, 1))

@@ -21,8 +21,12 @@
  *    and the readout y_t = C_t . h_t + D_h x_t, over the DEQUANTIZED codes
  *    x = s_x[h] q_x, B = s_B[g] q_B, C = s_C[g] q_C (exact in double), or, with scales
  *    per (group, state) (SSDi8 Table 10: per-P(N) and per-H(G) together), B = s_B[g, n] q_B
- *    and C = s_C[g, n] q_C.  Head h reads group g = h / (H / G).  Optionally records the state at every
- *    chunk boundary (the state entering chunk c, i.e. after token cQ - 1).
+ *    and C = s_C[g, n] q_C; with x scales per (head, channel), x = s_x[h, p] q_x (the static
+ *    scales that Quamba2's sort-and-cluster of channels leaves behind, one per channel
+ *    cluster, expanded to every channel).  The last argument holds the scale layout: bit 0 set
+ *    for B, C per (group, state), bit 1 for x per (head, channel).  Head h reads group
+ *    g = h / (H / G).  Optionally records the state at every chunk boundary (the state
+ *    entering chunk c, i.e. after token cQ - 1).
  *
  *  - oracle_ssd_sequential_state_f16: the same recurrence with the state cached
  *    in IEEE binary16 between tokens (a lower-precision cached decode state, as
@@ -185,9 +189,10 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out, int round_state,
                            const int8_t* q0, const float* s0, int8_t* q_out, float* s_out, double* u_last,
-                           float* s_steps, const float* ycorr, int32_t bc_per_state) {
+                           float* s_steps, const float* ycorr, int32_t scale_flags) {
   (void)batch;
   const int32_t g = h / (H / G);
+  const int bc_per_state = scale_flags & 1, x_per_channel = (scale_flags >> 1) & 1;
   double* S = (double*)calloc((size_t)P * N, sizeof(double));
   double* xv = (double*)malloc(sizeof(double) * P);
   double* Bv = (double*)malloc(sizeof(double) * N);
@@ -212,7 +217,8 @@ static void ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
     const int64_t row = (int64_t)b * L + t;
     const double d = (double)dt[row * H + h];
     const double a = exp(d * Ah);
-    for (int32_t p = 0; p < P; ++p) xv[p] = (double)sx[h] * (double)qx[(row * H + h) * P + p];
+    for (int32_t p = 0; p < P; ++p)   /* x's scale of head h, or of (head h, channel p) */
+      xv[p] = (double)sx[x_per_channel ? (int64_t)h * P + p : h] * (double)qx[(row * H + h) * P + p];
     for (int32_t n = 0; n < N; ++n) {
       const int32_t k = bc_per_state ? g * N + n : g;   /* scale of state n of group g */
       Bv[n] = (double)sB[k] * (double)qB[(row * G + g) * N + n];
@@ -253,9 +259,9 @@ void oracle_ssd_sequential(const int8_t* qx, const float* sx, const int8_t* qB, 
                            const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                            int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
                            double* h_out, int32_t chunk, double* bound_out, const float* ycorr,
-                           int32_t bc_per_state) {
+                           int32_t scale_flags) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, chunk, bound_out, 0,
-                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr, bc_per_state);
+                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr, scale_flags);
 }
 
 /* The recurrence with the state cached in binary16 between tokens (h0 is taken as given). */
@@ -263,9 +269,9 @@ void oracle_ssd_sequential_state_f16(const int8_t* qx, const float* sx, const in
                                      const int8_t* qC, const float* sC, const float* dt, const float* A,
                                      const float* D, const float* h0, int32_t batch, int64_t L, int32_t H,
                                      int32_t P, int32_t N, int32_t G, int32_t b, int32_t h, double* y_out,
-                                     double* h_out, const float* ycorr, int32_t bc_per_state) {
+                                     double* h_out, const float* ycorr, int32_t scale_flags) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, h0, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 1,
-                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr, bc_per_state);
+                 NULL, NULL, NULL, NULL, NULL, NULL, ycorr, scale_flags);
 }
 
 /* The recurrence with the state cached as 8-bit codes and one scale per state row between
@@ -278,9 +284,9 @@ void oracle_ssd_sequential_state_i8(const int8_t* qx, const float* sx, const int
                                     const float* D, const int8_t* q0, const float* s0, int32_t batch, int64_t L,
                                     int32_t H, int32_t P, int32_t N, int32_t G, int32_t b, int32_t h,
                                     double* y_out, double* h_out, int8_t* q_out, float* s_out, double* u_last,
-                                    float* s_steps, const float* ycorr, int32_t bc_per_state) {
+                                    float* s_steps, const float* ycorr, int32_t scale_flags) {
   ssd_sequential(qx, sx, qB, sB, qC, sC, dt, A, D, NULL, batch, L, H, P, N, G, b, h, y_out, h_out, 0, NULL, 2,
-                 q0, s0, q_out, s_out, u_last, s_steps, ycorr, bc_per_state);
+                 q0, s0, q_out, s_out, u_last, s_steps, ycorr, scale_flags);
 }
 
 /* The same recurrence over real-valued inputs, for one (b, h): x (batch, L, H, P), B and C
@@ -381,8 +387,9 @@ void oracle_chunk_cumsum(const float* dt, const float* A, int64_t L, int32_t H, 
  * where `last` is the chunk's last valid token. */
 void oracle_chunk_state(const int8_t* qx, const float* sx, const int8_t* qB, const float* sB,
                         const float* dt, const float* A, int64_t L, int32_t H, int32_t P, int32_t N,
-                        int32_t G, int32_t b, int32_t h, int32_t chunk, double* out, int32_t bc_per_state) {
+                        int32_t G, int32_t b, int32_t h, int32_t chunk, double* out, int32_t scale_flags) {
   const int32_t g = h / (H / G);
+  const int bc_per_state = scale_flags & 1, x_per_channel = (scale_flags >> 1) & 1;
   const int64_t nc = (L + chunk - 1) / chunk;
   double* acs = (double*)malloc(sizeof(double) * nc * chunk);
   oracle_chunk_cumsum(dt, A, L, H, b, h, chunk, acs);
@@ -396,7 +403,7 @@ void oracle_chunk_state(const int8_t* qx, const float* sx, const int8_t* qB, con
       const int64_t row = (int64_t)b * L + c * chunk + j;
       const double w = exp(last - acs[c * chunk + j]) * (double)dt[row * H + h];
       for (int32_t p = 0; p < P; ++p) {
-        const double xw = w * (double)sx[h] * (double)qx[(row * H + h) * P + p];
+        const double xw = w * (double)sx[x_per_channel ? (int64_t)h * P + p : h] * (double)qx[(row * H + h) * P + p];
         for (int32_t n = 0; n < N; ++n)
           Sc[(int64_t)p * N + n] += xw * (double)sB[bc_per_state ? g * N + n : g] * (double)qB[(row * G + g) * N + n];
       }

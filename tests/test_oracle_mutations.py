@@ -24,6 +24,7 @@ PINS = {
     "fe": ["tests/test_oracle_frontend.py"],
     "corr": ["tests/test_oracle_correction.py"],
     "pn": ["tests/test_oracle_per_state.py"],
+    "pc": ["tests/test_oracle_per_channel.py"],
 }
 
 # (name, pin files, text in ssd_oracle.c, replacement)
@@ -36,17 +37,25 @@ MUTANTS = [
     ("unquantized x dropped", "corr", "const double u = d * xr[p];", "const double u = d;"),
     ("unquantized decay sign", "corr", "const double a = exp(d * Ah);\n    const double* xr",
      "const double a = exp(-d * Ah);\n    const double* xr"),
-    ("decay exponent sign", "rec", "const double a = exp(d * Ah);\n    for (int32_t p = 0; p < P; ++p) xv[p]",
-     "const double a = exp(-d * Ah);\n    for (int32_t p = 0; p < P; ++p) xv[p]"),
-    ("group map h % G", "rec", "const int32_t g = h / (H / G);\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  double* xv",
-     "const int32_t g = h % G;\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  double* xv"),
+    ("decay exponent sign", "rec", "const double a = exp(d * Ah);\n    for (int32_t p = 0; p < P; ++p)   /*",
+     "const double a = exp(-d * Ah);\n    for (int32_t p = 0; p < P; ++p)   /*"),
+    ("group map h % G", "rec", "const int32_t g = h / (H / G);\n  const int bc_per_state = scale_flags & 1, x_per_channel = (scale_flags >> 1) & 1;\n  double* S",
+     "const int32_t g = h % G;\n  const int bc_per_state = scale_flags & 1, x_per_channel = (scale_flags >> 1) & 1;\n  double* S"),
     ("unquantized group map h % G", "corr", "const int32_t g = h / (H / G);\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  if (h0)",
      "const int32_t g = h % G;\n  double* S = (double*)calloc((size_t)P * N, sizeof(double));\n  if (h0)"),
     ("x dropped from the input term", "rec", "const double u = d * xv[p];", "const double u = d;"),
     ("dt dropped from the input term", "rec", "const double u = d * xv[p];", "const double u = xv[p];"),
     ("y read before the update", "rec", "Sp[n] = a * Sp[n] + u * Bv[n];\n        acc += Cv[n] * Sp[n];",
      "acc += Cv[n] * Sp[n];\n        Sp[n] = a * Sp[n] + u * Bv[n];"),
-    ("per-head x scale ignored", "rec", "xv[p] = (double)sx[h] *", "xv[p] = (double)sx[0] *"),
+    ("per-head x scale ignored", "rec", "xv[p] = (double)sx[x_per_channel ? (int64_t)h * P + p : h] *",
+     "xv[p] = (double)sx[x_per_channel ? (int64_t)h * P + p : 0] *"),
+    ("per-channel x scale indexed (p, h)", "pc", "xv[p] = (double)sx[x_per_channel ? (int64_t)h * P + p : h] *",
+     "xv[p] = (double)sx[x_per_channel ? (int64_t)p * H + h : h] *"),
+    ("per-channel x scale taken per head", "pc", "xv[p] = (double)sx[x_per_channel ? (int64_t)h * P + p : h] *",
+     "xv[p] = (double)sx[x_per_channel ? (int64_t)h * P : h] *"),
+    ("per-channel x scale dropped from the chunk state", "pc",
+     "const double xw = w * (double)sx[x_per_channel ? (int64_t)h * P + p : h] *",
+     "const double xw = w * (double)sx[h] *"),
     ("dt dropped from the chunk state", "rec", "const double w = exp(last - acs[c * chunk + j]) * (double)dt[row * H + h];",
      "const double w = exp(last - acs[c * chunk + j]);"),
     ("chunk cumsum restarts wrong", "rec", "for (int32_t j = 0; j < chunk && c * chunk + j < L; ++j) {\n      acc +=",
