@@ -97,7 +97,8 @@ ssdq_status ssdq_quantize_batch(const ssdq_quantize_job* jobs, int32_t count, hi
 
 /*
  * The static INT8 quantizer with one scale per (k, i) instead of one per k: B or C with a scale per
- * (group, state), the finer granularity of SSDi8 Table 10 (per-P(N) together with per-H(G)).
+ * (group, state), the finer granularity of SSDi8 Table 10 (per-P(N) together with per-H(G)), or x
+ * with a scale per (head, channel) (rows = b*L, nscale = H, inner = P, scale (H, P)).
  *
  *   q[r, k, i] = clamp(round_half_even(float(x[r, k, i]) / scale[k, i]), -127, 127)
  *
@@ -237,6 +238,40 @@ ssdq_status ssdq_chunk_scan_per_state(const int8_t* x, const float* x_scale, con
                                       int32_t ngroups, int32_t chunk, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* Scale layouts for ssdq_chunk_scan_scaled and ssdq_state_update_scaled (bit flags; 0 is the
+ * layout of ssdq_chunk_scan: one x scale per head, one B and one C scale per group). */
+#define SSDQ_SCALES_BC_PER_STATE 1u  /* B_scale, C_scale: (ngroups, dstate) */
+#define SSDQ_SCALES_X_PER_CHANNEL 2u /* x_scale: (nheads, headdim) */
+
+/*
+ * ssdq_chunk_scan under any of the static scale layouts, with an optional output correction.
+ * With SSDQ_SCALES_X_PER_CHANNEL, x has one static scale per (head, channel):
+ *
+ *   xhat[b,t,h,p] = x_scale[h, p] x[b,t,h,p]
+ *
+ * the granularity that Quamba2's sort-and-cluster of the x channels produces (its rebuttal names
+ * the sort-and-cluster and the per-state-group quantization as the two steps; each channel cluster
+ * of a head shares one scale, given here expanded to every channel of the cluster, so any
+ * clustering, sorted or not, is one (nheads, headdim) table).  Such a scale factors out of every
+ * contraction of the scan (they sum over tokens and states, never over channels), and is applied
+ * in fp32 per output channel and per state row.  With SSDQ_SCALES_BC_PER_STATE, B and C have
+ * one scale per (group, state) as in ssdq_chunk_scan_per_state.  Both bits may be set.
+ *
+ *   x_scale      : (nheads) fp32, or (nheads, headdim) with SSDQ_SCALES_X_PER_CHANNEL; each
+ *                  finite and > 0
+ *   B_scale, C_scale : (ngroups) fp32, or (ngroups, dstate) with SSDQ_SCALES_BC_PER_STATE
+ *   y_corr       : (nheads, headdim) fp32 or NULL (no correction)
+ *   scale_layout : SSDQ_SCALES_* bits (other bits: SSDQ_ERROR_INVALID_VALUE)
+ * Everything else (shapes, workspace, accuracy, validation) as ssdq_chunk_scan; the codes of x are
+ * those of ssdq_quantize_per_channel under the (nheads, headdim) table.
+ */
+ssdq_status ssdq_chunk_scan_scaled(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                   const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                   const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
+                                   int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                   int32_t ngroups, int32_t chunk, uint32_t scale_layout, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of the library's static device scratch that ssdq_chunk_scan_noalloc uses (per device). */
 #define SSDQ_NOALLOC_SCRATCH_BYTES (64u << 20)
 
@@ -372,6 +407,19 @@ ssdq_status ssdq_state_update_per_state(int32_t state_format, void* state, float
                                         const float* C_scale, const float* dt, const float* A, const float* D,
                                         const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
                                         int32_t dstate, int32_t ngroups, hipStream_t stream);
+
+/*
+ * The decode step of ssdq_state_update_corrected under any of the static scale layouts of
+ * ssdq_chunk_scan_scaled (scale_layout: SSDQ_SCALES_* bits; x_scale (nheads, headdim) with
+ * SSDQ_SCALES_X_PER_CHANNEL, B_scale and C_scale (ngroups, dstate) with
+ * SSDQ_SCALES_BC_PER_STATE); y_corr (nheads, headdim) fp32 or NULL.  Formats, arguments, layouts
+ * and validation otherwise as ssdq_state_update_corrected; other bits: SSDQ_ERROR_INVALID_VALUE.
+ */
+ssdq_status ssdq_state_update_scaled(int32_t state_format, void* state, float* state_scale, const int8_t* x,
+                                     const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
+                                     const float* C_scale, const float* dt, const float* A, const float* D,
+                                     const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                                     int32_t dstate, int32_t ngroups, uint32_t scale_layout, hipStream_t stream);
 
 /*
  * Front end of the SSD block, fused with the static quantizer: the causal convolution that the

@@ -68,6 +68,11 @@ lib.ssdq_state_update_i8.restype = ctypes.c_int
 lib.ssdq_chunk_scan_corrected.argtypes = [_P] * 13 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
 lib.ssdq_chunk_scan_per_state.argtypes = [_P] * 13 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _P, _sz, _P]
 lib.ssdq_chunk_scan_per_state.restype = ctypes.c_int
+lib.ssdq_chunk_scan_scaled.argtypes = [_P] * 13 + [_i32, _i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_uint32, _P, _sz,
+                                                  _P]
+lib.ssdq_chunk_scan_scaled.restype = ctypes.c_int
+lib.ssdq_state_update_scaled.argtypes = [_i32] + [_P] * 13 + [_i32, _i32, _i32, _i32, _i32, ctypes.c_uint32, _P]
+lib.ssdq_state_update_scaled.restype = ctypes.c_int
 lib.ssdq_state_update_per_state.argtypes = [_i32] + [_P] * 13 + [_i32, _i32, _i32, _i32, _i32, _P]
 lib.ssdq_state_update_per_state.restype = ctypes.c_int
 lib.ssdq_quantize_per_channel.argtypes = [_P, _P, _P, _i64, _i32, _i32, _P]
@@ -82,6 +87,11 @@ lib.ssdq_chunk_scan_noalloc_scratch_size.argtypes = [_i32, _i64, _i32, _i32, _i3
 lib.ssdq_chunk_scan_noalloc_scratch_size.restype = _sz
 lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
 lib.ssdq_chunk_scan_state_fused.restype = _i32
+
+
+# scale layouts of ssdq_chunk_scan_scaled / ssdq_state_update_scaled (bit flags)
+SCALES_BC_PER_STATE = 1   # B_scale, C_scale (ngroups, dstate)
+SCALES_X_PER_CHANNEL = 2  # x_scale (nheads, headdim)
 
 
 class SSDQError(RuntimeError):
@@ -185,7 +195,8 @@ def quantize_batch(pairs, outs=None) -> list[torch.Tensor]:
 def quantize(x: torch.Tensor, scale: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """INT8 codes of an fp16 tensor (..., S, I) with one fp32 scale per index of the
     second-to-last axis (heads for x, groups for B and C), or, with a 2-D scale (S, I), one per
-    (s, i) (B and C with a scale per (group, state): ssdq_quantize_per_channel)."""
+    (s, i) (B and C with a scale per (group, state), x with one per (head, channel):
+    ssdq_quantize_per_channel)."""
     if scale.dim() == 2:
         if x.dim() < 2:
             raise ValueError("x must have at least 2 dimensions (..., nscale, inner)")
@@ -236,9 +247,12 @@ class ScanBuffers:
         G, N = B.shape[2], B.shape[3]
         dev = x.device
         _need(x, "x", torch.int8, (b, L, H, P), dev)
-        _need(x_scale, "x_scale", torch.float32, (H,), dev)
+        self.x_per_channel = x_scale.dim() == 2
+        _need(x_scale, "x_scale", torch.float32, (H, P) if self.x_per_channel else (H,), dev)
         _need(B, "B", torch.int8, (b, L, G, N), dev)
         self.per_state = B_scale.dim() == 2
+        self.scale_layout = (SCALES_BC_PER_STATE if self.per_state else 0) | (
+            SCALES_X_PER_CHANNEL if self.x_per_channel else 0)
         sshape = (G, N) if self.per_state else (G,)
         _need(B_scale, "B_scale", torch.float32, sshape, dev)
         _need(C, "C", torch.int8, (b, L, G, N), dev)
@@ -270,9 +284,14 @@ class ScanBuffers:
             _ptr(workspace), workspace.numel()]
 
     def run(self) -> None:
-        """The whole scan (ssdq_chunk_scan, or ssdq_chunk_scan_corrected with an output correction)."""
+        """The whole scan: ssdq_chunk_scan; ssdq_chunk_scan_corrected with an output correction;
+        ssdq_chunk_scan_per_state with B, C scales per (group, state) only; ssdq_chunk_scan_scaled
+        with x scales per (head, channel)."""
         a = self._args
-        if self.per_state:
+        if self.x_per_channel:
+            _check(lib.ssdq_chunk_scan_scaled(*a[:9], _ptr(self.y_corr), *a[9:-2], self.scale_layout, *a[-2:],
+                                              _stream(self.device)), "ssdq_chunk_scan_scaled")
+        elif self.per_state:
             _check(lib.ssdq_chunk_scan_per_state(*a[:9], _ptr(self.y_corr), *a[9:], _stream(self.device)),
                    "ssdq_chunk_scan_per_state")
         elif self.y_corr is not None:
@@ -282,8 +301,8 @@ class ScanBuffers:
             _check(lib.ssdq_chunk_scan(*self._args, _stream(self.device)), "ssdq_chunk_scan")
 
     def run_stage(self, stage: int) -> None:
-        if self.y_corr is not None or self.per_state:
-            raise ValueError("the stage-level calls have neither output correction nor per-state scales; use run()")
+        if self.y_corr is not None or self.scale_layout:
+            raise ValueError("the stage-level calls take neither an output correction nor finer scales; use run()")
         _check(lib.ssdq_chunk_scan_stage(stage, *self._args, _stream(self.device)), "ssdq_chunk_scan_stage")
 
     def workspace_views(self) -> dict:
@@ -425,7 +444,8 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     int8 state (codes, with its row scales `state_scale` (b,H,P) float32, also updated in place)
     ssdq_state_update_i8; with y_corr (H, P) fp32 the step runs ssdq_state_update_corrected and
     y also receives that output correction; with B and C scales per (group, state) (G, N) it runs
-    ssdq_state_update_per_state (y_corr optional)."""
+    ssdq_state_update_per_state (y_corr optional); with x scales per (head, channel) (H, P) it
+    runs ssdq_state_update_scaled (with either B, C layout; y_corr optional)."""
     if state.dim() != 4:
         raise ValueError("state must be (batch, nheads, headdim, dstate)")
     b, H, P, N = state.shape
@@ -438,9 +458,10 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     elif state_scale is not None:
         raise ValueError("state_scale goes with an int8 state only")
     per_state = B_scale.dim() == 2
+    x_per_channel = x_scale.dim() == 2
     sshape = (G, N) if per_state else (G,)
     _need(x, "x", torch.int8, (b, H, P), dev)
-    _need(x_scale, "x_scale", torch.float32, (H,), dev)
+    _need(x_scale, "x_scale", torch.float32, (H, P) if x_per_channel else (H,), dev)
     _need(B, "B", torch.int8, (b, G, N), dev)
     _need(B_scale, "B_scale", torch.float32, sshape, dev)
     _need(C, "C", torch.int8, (b, G, N), dev)
@@ -452,6 +473,14 @@ def state_update(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D=None, y=Non
     if y is None:
         y = torch.empty((b, H, P), dtype=torch.float16, device=dev)
     _need(y, "y", torch.float16, (b, H, P), dev)
+    if x_per_channel:
+        fmt = {"f32": STATE_F32, "f16": STATE_F16, "i8": STATE_I8}[kind]
+        layout = SCALES_X_PER_CHANNEL | (SCALES_BC_PER_STATE if per_state else 0)
+        _check(lib.ssdq_state_update_scaled(fmt, _ptr(state), _ptr(state_scale), _ptr(x), _ptr(x_scale), _ptr(B),
+                                            _ptr(B_scale), _ptr(C), _ptr(C_scale), _ptr(dt), _ptr(A), _ptr(D),
+                                            _ptr(y_corr), _ptr(y), b, H, P, N, G, layout, _stream(dev)),
+               "ssdq_state_update_scaled")
+        return y
     if per_state:
         fmt = {"f32": STATE_F32, "f16": STATE_F16, "i8": STATE_I8}[kind]
         _check(lib.ssdq_state_update_per_state(fmt, _ptr(state), _ptr(state_scale), _ptr(x), _ptr(x_scale), _ptr(B),

@@ -27,6 +27,8 @@
 //    power-of-two scale per row and meets the C codes directly (persistent INT8 operands).
 //  - LDS matrices are padded or 16-byte-chunk XOR swizzled so that the MFMA operand reads
 //    are free of bank conflicts with addresses that advance linearly in the hot loop.
+#include <type_traits>
+
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -96,6 +98,14 @@ __device__ __forceinline__ const LDSP T* lds_base(const T* p) {
   asm volatile("" : "+v"(a));
   return (const LDSP T*)uintptr_t(a);
 }
+// lds_base where the instance uses the array, nothing (and no instruction) where it does not
+template <bool kOn, typename T>
+__device__ __forceinline__ const LDSP T* lds_base_if(const T* p) {
+  if constexpr (kOn)
+    return lds_base(p);
+  else
+    return nullptr;
+}
 template <typename V, typename T>
 __device__ __forceinline__ V lds_ld(const LDSP T* p, int off) {
   return *reinterpret_cast<const LDSP V*>(p + off);
@@ -141,7 +151,7 @@ constexpr int kBTasks = kMaxQ * 8 / kThreads;          // 16-byte B pieces per t
 static_assert(2 * kMaxP * (kMaxN / 32) == kThreads, "two 16-byte carried-state pieces per thread");
 constexpr int kXTasks = kMaxQ * (kMaxP / 16) / kThreads;   // 16-byte x pieces per thread
 struct Prefetch {
-  float acs, dt, hs, mu;
+  float acs, dt, hs, mu, sxp;   // sxp: the x scale of channel tid (x scales per (head, channel))
   v4i cq[2][2];                 // C codes of this lane's two output rows (per pass, K half)
   v4u bq[kBTasks];
   v4u hq[2];                    // two 16-byte pieces of one limb row
@@ -184,7 +194,7 @@ struct LaneConst {
 // Buffer resources of one item: base at the item's first element, size up to the end of its
 // last valid row.
 struct ItemRsrc {
-  Rsrc acs, dt, hs, mu, B, H, x, C;
+  Rsrc acs, dt, hs, mu, B, H, x, C, sx;
 };
 
 // One work item's position, as 32-bit row indices into its operands (every index is below
@@ -233,6 +243,7 @@ __device__ __forceinline__ bool item_next(ItemPos& p, int it, const Params& a) {
 
 __device__ __forceinline__ uint64_t wide(uint32_t i, uint32_t stride) { return uint64_t(i) * stride; }
 
+template <bool kPC = false>
 __device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a) {
   const uint32_t last = uint32_t(p.len - 1), gn = uint32_t(a.ngroups * a.N), P = uint32_t(a.P), N = uint32_t(a.N);
   ItemRsrc r;
@@ -244,13 +255,14 @@ __device__ __forceinline__ ItemRsrc item_rsrc(const ItemPos& p, const Params& a)
   r.H = make_rsrc(a.hprev + wide(p.seg, 2u * P * N), 2u * P * N);
   r.x = make_rsrc(a.x + wide(p.row, P), last * uint32_t(a.nheads) * P + P);
   r.C = make_rsrc(a.C + wide(p.grow, N), last * gn + N);
+  if constexpr (kPC) r.sx = make_rsrc(a.x_scale + uint32_t(p.h) * P, P * 4u);
   return r;
 }
 
 // Issue the global loads of one item except its x codes (nothing waits here); B and C only when
 // the item starts a new (batch, chunk, group) (bc, block-uniform); the head's output correction
 // only in the corrected instance.
-template <bool kCorr>
+template <bool kCorr, bool kPC>
 __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const LaneConst& lc, uint32_t xrow, bool bc,
                                          int N, int kg) {
   if (bc) {
@@ -282,6 +294,7 @@ __device__ __forceinline__ void prefetch(Prefetch& f, const ItemRsrc& r, const L
   if (threadIdx.x < kMaxP) {
     f.hs = buf_loadf(r.hs, lc.hs_off);
     if constexpr (kCorr) f.mu = buf_loadf(r.mu, lc.hs_off);
+    if constexpr (kPC) f.sxp = buf_loadf(r.sx, lc.hs_off);
   }
 #pragma unroll
   for (int k = 0; k < 2; ++k) f.hq[k] = buf_load16(r.H, lc.h_off[k]);
@@ -304,7 +317,11 @@ __device__ __forceinline__ void prefetch_x(Prefetch& f, const ItemRsrc& r, const
 // 256 G_hi + G_lo (exact int32) stands for sum_n sigma[n] q_C q_B to within 2^(s - 9) per term.
 // The second B plane takes the LDS of the second x tile buffer, so this instance commits the next
 // item's x after a barrier instead of into a free buffer.
-template <bool kCorr, bool kPS>
+// kPC: x scales per (head, channel).  Every term of y is linear in x of its own channel p except
+// the carried-state readout (its state already holds the x scales), so the item runs with unit
+// x scale and the epilogue multiplies channel p by x_scale[h, p]; the carried-state row scale of
+// row p is stored divided by that scale so that the readout comes out unscaled.
+template <bool kCorr, bool kPS, bool kPC>
 __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // Per-item tiles in two buffers (item k of the block in buffer k % 2): a wave commits the next
   // item into the other buffer as soon as its own passes are done, and one barrier per item
@@ -314,6 +331,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   __shared__ __attribute__((aligned(16))) int8_t Hq_buf[2][2 * kHPlane];
   __shared__ __attribute__((aligned(16))) float hsc_buf[2][kMaxP];
   __shared__ __attribute__((aligned(16))) float mu_buf[2][kCorr ? kMaxP : 4];
+  __shared__ __attribute__((aligned(16))) float sxc_buf[2][kPC ? kMaxP : 4];   // kPC: x scale per channel
   __shared__ __attribute__((aligned(16))) float acs2_buf[2][kMaxQ];   // Acs * log2(e)
   __shared__ __attribute__((aligned(16))) float dts_buf[2][kMaxQ];    // dt (0 past the sequence end)
   __shared__ float red_buf[2][kWaves];
@@ -417,8 +435,9 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
       if (lane == 0) red_buf[bf][wave] = dm;
     }
     if (tid < kMaxP) {
-      hsc_buf[bf][tid] = f.hs;
+      hsc_buf[bf][tid] = kPC ? f.hs / f.sxp : f.hs;
       if constexpr (kCorr) mu_buf[bf][tid] = f.mu;
+      if constexpr (kPC) sxc_buf[bf][tid] = f.sxp;
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(Hq_buf[bf] + lc.h_lds[q]) = f.hq[q];
@@ -502,7 +521,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
   // one trip, so the commit's wait for the prefetched data counts back over a fixed number of
   // stores (unconditional buffer stores) and never waits for the stores themselves.
   ItemPos cur = item_at(it, a);
-  prefetch<kCorr>(f, item_rsrc(cur, a), lc, xrow, true, N, kg);
+  prefetch<kCorr, kPC>(f, item_rsrc<kPC>(cur, a), lc, xrow, true, N, kg);
   prefetch_x(f, item_rsrc(cur, a), lc);
   commit(0);
   if constexpr (kPS) commit_x(0);
@@ -517,7 +536,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const int gu = __builtin_amdgcn_readfirstlane(cur.g);
     // per-item scalars through the scalar cache (read-only data)
     typedef const __attribute__((address_space(4))) float* cfp;
-    const float sx = *cfp(a.x_scale + hu);
+    const float sx = kPC ? 1.f : *cfp(a.x_scale + hu);
     const float sB = kPS ? 1.f : *cfp(a.B_scale + gu), sC = kPS ? 1.f : *cfp(a.C_scale + gu);
     const float Dh = a.D ? *cfp(a.D + hu) : 0.f;
     const uint32_t yrow = uint32_t(a.nheads * P);
@@ -529,8 +548,8 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     ItemPos nxt = cur;
     bool nxt_bc = false;
     if (it + 1 < it_end) nxt_bc = item_next(nxt, it, a);
-    const ItemRsrc nrs = item_rsrc(nxt, a);
-    prefetch<kCorr>(f, nrs, lc, xrow, nxt_bc, N, kg);
+    const ItemRsrc nrs = item_rsrc<kPC>(nxt, a);
+    prefetch<kCorr, kPC>(f, nrs, lc, xrow, nxt_bc, N, kg);
     __builtin_amdgcn_sched_barrier(0);
 
     // this trip's view of the per-item tiles
@@ -539,6 +558,7 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
     const LDSP int8_t* const hqb[2] = {lds_base(Hq + hq_lane[0]), lds_base(Hq + hq_lane[1])};
     const LDSP float* const hsb = lds_base(hsc_buf[buf] + 4 * kg);   // + 16 pt: this lane's row scales
     const LDSP float* const mub = lds_base(mu_buf[buf] + (kCorr ? 4 * kg : 0));   // + 16 pt: its corrections
+    const LDSP float* const sxb = lds_base_if<kPC>(sxc_buf[buf] + 4 * kg);   // + 16 pt: its x scales
     const float* const acs2 = acs2_buf[buf];
     const float* const dts = dts_buf[buf];
     const float* const red = red_buf[buf];
@@ -776,7 +796,17 @@ __global__ void __launch_bounds__(kThreads) chunk_output_kernel(Params a) {
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         v4h out;
-        if constexpr (kCorr) {
+        if constexpr (kPC) {
+          const float4 x4 = lds_f4(sxb, 16 * pt);
+          const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+          float mv[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (kCorr) {
+            const float4 m4 = lds_f4(mub, 16 * pt);
+            mv[0] = m4.x, mv[1] = m4.y, mv[2] = m4.z, mv[3] = m4.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) out[i] = _Float16(fmaf(xv[i], fmaf(yf[pt][i], c_f, yd[pt][i] * s_in), mv[i]));
+        } else if constexpr (kCorr) {
           const float4 m4 = lds_f4(mub, 16 * pt);
           const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
@@ -844,16 +874,22 @@ hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_
                                               hipSuccess)
     cus = 256;
   const int nblocks = p.nitems < cus ? p.nitems : cus;
-  if (a.bc_per_state) {
-    if (p.ycorr)
-      hipLaunchKernelGGL((chunk_output_kernel<true, true>), dim3(nblocks), dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((chunk_output_kernel<false, true>), dim3(nblocks), dim3(kThreads), 0, stream, p);
-  } else {
-    if (p.ycorr)
-      hipLaunchKernelGGL((chunk_output_kernel<true, false>), dim3(nblocks), dim3(kThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL((chunk_output_kernel<false, false>), dim3(nblocks), dim3(kThreads), 0, stream, p);
+  auto go = [&](auto corr, auto ps, auto pc) {
+    hipLaunchKernelGGL((chunk_output_kernel<decltype(corr)::value, decltype(ps)::value, decltype(pc)::value>),
+                       dim3(nblocks), dim3(kThreads), 0, stream, p);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  const int sel = (p.ycorr ? 4 : 0) | (a.bc_per_state ? 2 : 0) | (a.x_per_channel ? 1 : 0);
+  switch (sel) {
+    case 0: go(F{}, F{}, F{}); break;
+    case 1: go(F{}, F{}, T{}); break;
+    case 2: go(F{}, T{}, F{}); break;
+    case 3: go(F{}, T{}, T{}); break;
+    case 4: go(T{}, F{}, F{}); break;
+    case 5: go(T{}, F{}, T{}); break;
+    case 6: go(T{}, T{}, F{}); break;
+    default: go(T{}, T{}, T{}); break;
   }
   return hipGetLastError();
 }

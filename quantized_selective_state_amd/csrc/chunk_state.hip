@@ -33,6 +33,8 @@
 // K-consecutive bytes with no byte transposes in registers.  Each wave owns one 16-channel
 // tile of S across all states and tokens, so every limb is built exactly once, in registers,
 // right before its MFMAs.
+#include <type_traits>
+
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -98,7 +100,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
     const float* __restrict__ B_scale, const float* __restrict__ C_scale_ps, const float* __restrict__ dt,
     const float* __restrict__ A, float* __restrict__ acs, float* __restrict__ dtc, float* __restrict__ states,
     int64_t seqlen, int32_t nheads,
-    int32_t headdim, int32_t dstate, int32_t ngroups, int32_t nchunks) {
+    int32_t headdim, int32_t dstate, int32_t ngroups, int32_t nchunks, int32_t x_pc) {
   __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
   __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
   __shared__ __attribute__((aligned(16))) uint32_t om[Q];   // OM_j
@@ -235,6 +237,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
   // per group: the B scale of the group; with scales per (group, state) (C_scale_ps non-null) the
   // state column's B scale times its C scale: the chunk states are then written scaled by the C
   // scale of each state (the form the carried state takes for the output stage)
+  // (x_pc: x scales per (head, channel), one per row of S)
   const float post = x_scale[h] * (C_scale_ps ? 1.f : B_scale[g]) * exp2i(e);
   const float post_lo = post * (1.f / 65536.f);
   // buffer stores: lane offset + row offset (scalar) + state-tile offset (immediate)
@@ -243,11 +246,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row_off = i * N * 4;   // uniform
+    float pst = post, pst_lo = post_lo;
+    if (x_pc) {   // uniform
+      pst = x_scale[h * P + 16 * pt + 4 * kg + i] * (C_scale_ps ? 1.f : B_scale[g]) * exp2i(e);
+      pst_lo = pst * (1.f / 65536.f);
+    }
 #pragma unroll
     for (int t = 0; t < kNt; ++t) {
       if (16 * t >= N) break;
       const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];   // exact: |lo| < 2^31
-      float sv = fmaf(float(lo), post_lo, float(acc[t][0][i]) * post);
+      float sv = fmaf(float(lo), pst_lo, float(acc[t][0][i]) * pst);
       if (C_scale_ps) {   // uniform
         const int n = 16 * t + lcol;
         sv *= B_scale[g * N + n] * C_scale_ps[g * N + n];
@@ -286,7 +294,8 @@ static_assert(kGroup % 2 == 0, "groups start at even chunks (tile buffer parity)
 // the way out), so that each chunk adds sigma[n] S'[p, n] with sigma = B_scale C_scale and S' the
 // products without the B scale, and the carried state the output stage reads out with the C codes
 // already holds the C scale of its state.
-template <int Q, bool kPS>
+// kPC: x scales per (head, channel); each lane's channel row takes its own (fixed per block).
+template <int Q, bool kPS, bool kPC>
 __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(2))) state_scan_kernel(
     const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
     const float* __restrict__ B_scale, const float* __restrict__ C_scale, const float* __restrict__ dt,
@@ -321,7 +330,7 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int kTok = Q / kWave;              // tokens per lane in a group prologue
   const bool prow = 16 * pt < P;               // this wave's channel tile exists (uniform)
   const uint32_t xrow = uint32_t(nheads * P), brow = uint32_t(ngroups * N);
-  const float sxB = x_scale[h] * (kPS ? 1.f : B_scale[g]);
+  const float sxB = x_scale[kPC ? h * P + min(16 * pt + lcol, P - 1) : h] * (kPS ? 1.f : B_scale[g]);
   const float Ah = A[h];
 
   // ---- running state H[p = 16 pt + lcol][n = 16 (4 kh + t) + 4 kg + i], own tiles t = 0..3
@@ -637,7 +646,7 @@ hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
                        a.bc_per_state ? a.C_scale : nullptr, a.dt, a.A, a.acs, a.dtc, a.states, s.seqlen, s.nheads,
-                       s.headdim, s.dstate, s.ngroups, s.nchunks);
+                       s.headdim, s.dstate, s.ngroups, s.nchunks, a.x_per_channel ? 1 : 0);
   };
   switch (s.chunk) {
     case 64: go(chunk_state_kernel<64>); break;
@@ -666,19 +675,20 @@ hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t 
                        a.dt, a.A, a.h0, a.h_final, a.acs, a.dtc, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim,
                        s.dstate, s.ngroups, s.nchunks);
   };
-  if (a.bc_per_state) {
+  auto by_chunk = [&](auto ps, auto pc) {
+    constexpr bool kPS = decltype(ps)::value, kPC = decltype(pc)::value;
     switch (s.chunk) {
-      case 64: go(state_scan_kernel<64, true>); break;
-      case 128: go(state_scan_kernel<128, true>); break;
-      default: go(state_scan_kernel<256, true>); break;
+      case 64: go(state_scan_kernel<64, kPS, kPC>); break;
+      case 128: go(state_scan_kernel<128, kPS, kPC>); break;
+      default: go(state_scan_kernel<256, kPS, kPC>); break;
     }
-  } else {
-    switch (s.chunk) {
-      case 64: go(state_scan_kernel<64, false>); break;
-      case 128: go(state_scan_kernel<128, false>); break;
-      default: go(state_scan_kernel<256, false>); break;
-    }
-  }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (a.bc_per_state)
+    a.x_per_channel ? by_chunk(T{}, T{}) : by_chunk(T{}, F{});
+  else
+    a.x_per_channel ? by_chunk(F{}, T{}) : by_chunk(F{}, F{});
   return hipGetLastError();
 }
 

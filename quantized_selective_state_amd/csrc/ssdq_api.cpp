@@ -93,6 +93,7 @@ ssdq_status check_scan_args(int32_t stage, const int8_t* x, const float* x_scale
   a->D = D;
   a->ycorr = nullptr;
   a->bc_per_state = false;
+  a->x_per_channel = false;
   a->h0 = h0;
   a->y = static_cast<_Float16*>(y);
   a->h_final = h_final;
@@ -285,6 +286,30 @@ ssdq_status ssdq_chunk_scan_per_state(const int8_t* x, const float* x_scale, con
   return SSDQ_SUCCESS;
 }
 
+ssdq_status ssdq_chunk_scan_scaled(const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
+                                   const int8_t* C, const float* C_scale, const float* dt, const float* A,
+                                   const float* D, const float* y_corr, const float* h0, void* y, float* h_final,
+                                   int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+                                   int32_t ngroups, int32_t chunk, uint32_t scale_layout, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (!ok_opt(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  if (scale_layout & ~uint32_t(SSDQ_SCALES_BC_PER_STATE | SSDQ_SCALES_X_PER_CHANNEL)) return SSDQ_ERROR_INVALID_VALUE;
+  ScanShape s;
+  ScanArgs a;
+  const ssdq_status st = check_scan_args(0, x, x_scale, B, B_scale, C, C_scale, dt, A, D, h0, y, h_final, batch,
+                                         seqlen, nheads, headdim, dstate, ngroups, chunk, workspace,
+                                         workspace_bytes, &s, &a);
+  if (st != SSDQ_SUCCESS) return st;
+  a.ycorr = y_corr;
+  a.bc_per_state = (scale_layout & SSDQ_SCALES_BC_PER_STATE) != 0;
+  a.x_per_channel = (scale_layout & SSDQ_SCALES_X_PER_CHANNEL) != 0;
+  for (int32_t stage = 0; stage < SSDQ_CHUNK_SCAN_STAGES; ++stage) {
+    const ssdq_status r = run_stage(stage, s, a, stream);
+    if (r != SSDQ_SUCCESS) return r;
+  }
+  return SSDQ_SUCCESS;
+}
+
 size_t ssdq_chunk_scan_noalloc_scratch_size(int32_t batch, int64_t seqlen, int32_t nheads, int32_t headdim,
                                             int32_t dstate, int32_t chunk) {
   ScanShape s;
@@ -380,7 +405,7 @@ namespace {
 ssdq_status decode_any(int32_t state_format, void* state, float* state_scale, const int8_t* x, const float* x_scale,
                        const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                        const float* A, const float* D, const float* y_corr, void* y, int32_t batch, int32_t nheads,
-                       int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream, bool per_state);
+                       int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream, int32_t scales);
 }  // namespace
 
 ssdq_status ssdq_state_update_per_state(int32_t state_format, void* state, float* state_scale, const int8_t* x,
@@ -390,7 +415,18 @@ ssdq_status ssdq_state_update_per_state(int32_t state_format, void* state, float
                                         int32_t dstate, int32_t ngroups, hipStream_t stream) {
   if (!ok_opt(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
   return decode_any(state_format, state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, y, batch,
-                    nheads, headdim, dstate, ngroups, stream, true);
+                    nheads, headdim, dstate, ngroups, stream, SSDQ_SCALES_BC_PER_STATE);
+}
+
+ssdq_status ssdq_state_update_scaled(int32_t state_format, void* state, float* state_scale, const int8_t* x,
+                                     const float* x_scale, const int8_t* B, const float* B_scale, const int8_t* C,
+                                     const float* C_scale, const float* dt, const float* A, const float* D,
+                                     const float* y_corr, void* y, int32_t batch, int32_t nheads, int32_t headdim,
+                                     int32_t dstate, int32_t ngroups, uint32_t scale_layout, hipStream_t stream) {
+  if (!ok_opt(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
+  if (scale_layout & ~uint32_t(SSDQ_SCALES_BC_PER_STATE | SSDQ_SCALES_X_PER_CHANNEL)) return SSDQ_ERROR_INVALID_VALUE;
+  return decode_any(state_format, state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, y, batch,
+                    nheads, headdim, dstate, ngroups, stream, int32_t(scale_layout));
 }
 
 ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float* state_scale, const int8_t* x,
@@ -400,7 +436,7 @@ ssdq_status ssdq_state_update_corrected(int32_t state_format, void* state, float
                                         int32_t dstate, int32_t ngroups, hipStream_t stream) {
   if (!ok_ptr(y_corr)) return SSDQ_ERROR_INVALID_VALUE;
   return decode_any(state_format, state, state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, y, batch,
-                    nheads, headdim, dstate, ngroups, stream, false);
+                    nheads, headdim, dstate, ngroups, stream, 0);
 }
 
 }  // extern "C"
@@ -409,7 +445,7 @@ namespace {
 ssdq_status decode_any(int32_t state_format, void* state, float* state_scale, const int8_t* x, const float* x_scale,
                        const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                        const float* A, const float* D, const float* y_corr, void* y, int32_t batch, int32_t nheads,
-                       int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream, bool per_state) {
+                       int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream, int32_t scales) {
   if (state_format != SSDQ_STATE_F32 && state_format != SSDQ_STATE_F16 && state_format != SSDQ_STATE_I8)
     return SSDQ_ERROR_INVALID_VALUE;
   if (state_format == SSDQ_STATE_I8 && !ok_ptr(state_scale)) return SSDQ_ERROR_INVALID_VALUE;
@@ -420,13 +456,13 @@ ssdq_status decode_any(int32_t state_format, void* state, float* state_scale, co
   hipError_t e;
   if (state_format == SSDQ_STATE_F32)
     e = launch_state_update(static_cast<float*>(state), x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr, yo,
-                            batch, nheads, headdim, dstate, ngroups, stream, per_state);
+                            batch, nheads, headdim, dstate, ngroups, stream, scales);
   else if (state_format == SSDQ_STATE_F16)
     e = launch_state_update_f16(static_cast<uint16_t*>(state), x, x_scale, B, B_scale, C, C_scale, dt, A, D, y_corr,
-                                yo, batch, nheads, headdim, dstate, ngroups, stream, per_state);
+                                yo, batch, nheads, headdim, dstate, ngroups, stream, scales);
   else
     e = launch_state_update_i8(static_cast<int8_t*>(state), state_scale, x, x_scale, B, B_scale, C, C_scale, dt, A, D,
-                               y_corr, yo, batch, nheads, headdim, dstate, ngroups, stream, per_state);
+                               y_corr, yo, batch, nheads, headdim, dstate, ngroups, stream, scales);
   return e == hipSuccess ? SSDQ_SUCCESS : SSDQ_ERROR_LAUNCH;
 }
 }  // namespace

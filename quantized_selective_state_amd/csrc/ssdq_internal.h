@@ -69,6 +69,7 @@ struct ScanArgs {
   int8_t* hprev;      // workspace: (batch, nchunks, nheads, 2, headdim, dstate) int8 limbs
   float* hscale;      // workspace: (batch, nchunks, nheads, headdim)
   bool bc_per_state;  // B_scale and C_scale hold one scale per (group, state), not one per group
+  bool x_per_channel; // x_scale holds one scale per (head, channel), not one per head
 };
 
 // Kernel launchers (one per translation unit).  They return hipGetLastError().
@@ -97,21 +98,23 @@ hipError_t launch_frontend_step(uint16_t* conv_state, const uint16_t* xbc, const
                                 const float* dt_raw, const float* dt_bias, int8_t* x, int8_t* B, int8_t* C,
                                 float* dt, int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate,
                                 int32_t ngroups, hipStream_t stream);
+// Decode launchers: `scales` is the scale layout (bit 0: B, C per (group, state); bit 1: x per
+// (head, channel)).
 hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_t* x, const float* x_scale,
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
                                   const float* dt, const float* A, const float* D, const float* ycorr, _Float16* y,
                                   int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                  hipStream_t stream, bool per_state = false);
+                                  hipStream_t stream, int32_t scales = 0);
 hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                    const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                    const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
                                    int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                   hipStream_t stream, bool per_state = false);
+                                   hipStream_t stream, int32_t scales = 0);
 hipError_t launch_state_update(float* state, const int8_t* x, const float* x_scale, const int8_t* B,
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
                                int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream,
-                               bool per_state = false);
+                               int32_t scales = 0);
 
 // ---------------------------------------------------------------------------------------------
 // device helpers

@@ -11,6 +11,8 @@
 // arithmetic (addresses of rows past headdim are clamped, so no load sits behind a branch),
 // and y[p] is reduced across the N/4 lanes of row p with DPP row shifts (an in-row prefix
 // sum; lane 15 of each 16-lane DPP row holds its row total, row_bcast15 joins two rows).
+#include <type_traits>
+
 #include "ssdq_internal.h"
 
 namespace ssdq {
@@ -39,8 +41,10 @@ __device__ __forceinline__ float group_sum_to_last_lane(float v) {
   return v;
 }
 
-// kPS: B_scale and C_scale hold one scale per (group, state) (ngroups x N) instead of one per group.
-template <int N, bool kPS>
+// kSc, the scale layout: bit 0 (kPS) B_scale and C_scale hold one scale per (group, state)
+// (ngroups x N) instead of one per group; bit 1 (kPC) x_scale holds one scale per (head, channel)
+// (nheads x headdim) instead of one per head.
+template <int N, int kSc>
 __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
@@ -50,6 +54,7 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
   constexpr int kLanesPerRow = N / 4;
   constexpr int kRows = kThreads / kLanesPerRow;   // rows per pass
   constexpr int kPasses = 64 / kRows;              // headdim <= 64
+  constexpr bool kPS = kSc & 1, kPC = (kSc & 2) != 0;
   const int bh = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bh % nheads;
   const int b = bh / nheads;
@@ -70,13 +75,19 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
   }
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) xq[k] = xr[min(r0 + kRows * k, P - 1)];
+  float sxq[kPC ? kPasses : 1];   // kPC: the x scale of each of the lane's rows
+  if constexpr (kPC) {
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) sxq[k] = x_scale[h * P + min(r0 + kRows * k, P - 1)];
+  }
   const uint32_t bw = *reinterpret_cast<const uint32_t*>(Bm + (int64_t(b) * ngroups + g) * N + 4 * nq);
   const uint32_t cw = *reinterpret_cast<const uint32_t*>(Cm + (int64_t(b) * ngroups + g) * N + 4 * nq);
   const float d = dt[bh];
   const float a = __expf(d * A[h]);
-  const float sx = x_scale[h];
+  const float sx = kPC ? 1.f : x_scale[h];
   const float dx = d * sx;
-  const float Dsx = (D ? D[h] : 0.f) * sx;
+  const float Dh = D ? D[h] : 0.f;
+  const float Dsx = Dh * sx;
   float bh4[4], ch4[4];
   if constexpr (kPS) {
     const v4f sb4 = *reinterpret_cast<const v4f*>(B_scale + g * N + 4 * nq);
@@ -99,7 +110,8 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
   for (int k = 0; k < kPasses; ++k) {
     const int p = r0 + kRows * k;
     const float xp = float(xq[k]);
-    const float u = dx * xp;
+    const float u = (kPC ? d * sxq[k] : dx) * xp;
+    const float Dx = kPC ? Dh * sxq[k] : Dsx;
     v4f v = hv[k];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = a * v[i] + u * bh4[i];
@@ -107,7 +119,7 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
     float part = ch4[0] * v[0] + ch4[1] * v[1] + ch4[2] * v[2] + ch4[3] * v[3];
     part = group_sum_to_last_lane<kLanesPerRow>(part);
     if (p < P && nq == kLanesPerRow - 1)
-      y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp + (ycorr ? ycorr[h * P + p] : 0.f));
+      y[int64_t(bh) * P + p] = _Float16(part + Dx * xp + (ycorr ? ycorr[h * P + p] : 0.f));
   }
 }
 
@@ -116,7 +128,7 @@ __global__ void __launch_bounds__(kThreads) state_update_kernel(
 // and store per row), forms the update in fp32 from the cached value, reads y out of that
 // update and stores it rounded to nearest binary16 (ties to even; past the format's range:
 // inf).  y[p] is summed across the N/8 lanes of row p with DPP lane pairings.
-template <int N, bool kPS>
+template <int N, int kSc>
 __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
     uint16_t* __restrict__ state, const int8_t* __restrict__ x, const float* __restrict__ x_scale,
     const int8_t* __restrict__ Bm, const float* __restrict__ B_scale, const int8_t* __restrict__ Cm,
@@ -126,6 +138,7 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
   constexpr int kLanesPerRow = N / 8;               // 16 (N = 128) or 8 (N = 64)
   constexpr int kRows = kThreads / kLanesPerRow;    // rows per pass
   constexpr int kPasses = 64 / kRows;               // headdim <= 64
+  constexpr bool kPS = kSc & 1, kPC = (kSc & 2) != 0;
   const int bh = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bh % nheads;
   const int b = bh / nheads;
@@ -146,13 +159,19 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
   }
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) xq[k] = xr[min(r0 + kRows * k, P - 1)];
+  float sxq[kPC ? kPasses : 1];   // kPC: the x scale of each of the lane's rows
+  if constexpr (kPC) {
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) sxq[k] = x_scale[h * P + min(r0 + kRows * k, P - 1)];
+  }
   const v2u bw = *reinterpret_cast<const v2u*>(Bm + (int64_t(b) * ngroups + g) * N + 8 * nq);
   const v2u cw = *reinterpret_cast<const v2u*>(Cm + (int64_t(b) * ngroups + g) * N + 8 * nq);
   const float d = dt[bh];
   const float a = __expf(d * A[h]);
-  const float sx = x_scale[h];
+  const float sx = kPC ? 1.f : x_scale[h];
   const float dx = d * sx;
-  const float Dsx = (D ? D[h] : 0.f) * sx;
+  const float Dh = D ? D[h] : 0.f;
+  const float Dsx = Dh * sx;
   float bh8[8], ch8[8];
   if constexpr (kPS) {
     const v4f* sbp = reinterpret_cast<const v4f*>(B_scale + g * N + 8 * nq);
@@ -175,7 +194,8 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
   for (int k = 0; k < kPasses; ++k) {
     const int p = r0 + kRows * k;
     const float xp = float(xq[k]);
-    const float u = dx * xp;
+    const float u = (kPC ? d * sxq[k] : dx) * xp;
+    const float Dx = kPC ? Dh * sxq[k] : Dsx;
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -193,7 +213,7 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) part = fmaf(ch8[i], v[i], part);
     part = group_sum<kLanesPerRow>(part);
-    if (p < P && nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dsx * xp + (ycorr ? ycorr[h * P + p] : 0.f));
+    if (p < P && nq == 0) y[int64_t(bh) * P + p] = _Float16(part + Dx * xp + (ycorr ? ycorr[h * P + p] : 0.f));
   }
 }
 
@@ -213,10 +233,10 @@ __global__ void __launch_bounds__(kThreads) state_update_f16_kernel(
 //    byte permutes pack four codes per dword.
 constexpr int kI8Threads = 128;   // two waves per (batch, head): four row passes per lane amortize the set-up
 
-// kPS: per-(group, state) B and C scales.  The B scale then goes into each state's B value and
-// y is summed in fp32 over the C values scaled per state (the int8 dot products factor only
-// with one C scale per row).
-template <int N, bool kPS>
+// kSc bit 0 (kPS): per-(group, state) B and C scales.  The B scale then goes into each state's B
+// value and y is summed in fp32 over the C values scaled per state (the int8 dot products factor
+// only with one C scale per row).  Bit 1 (kPC): x scales per (head, channel), one per state row.
+template <int N, int kSc>
 __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     int8_t* __restrict__ state, float* __restrict__ state_scale, const int8_t* __restrict__ x,
     const float* __restrict__ x_scale, const int8_t* __restrict__ Bm, const float* __restrict__ B_scale,
@@ -227,6 +247,7 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
   constexpr int kRows = kI8Threads / kLanesPerRow;     // rows per pass: 16 or 32
   constexpr int kPasses = (64 + kRows - 1) / kRows;    // headdim <= 64
   constexpr float kMagic = 12582912.f;                 // 1.5 * 2^23: unit spacing, code in the low byte
+  constexpr bool kPS = kSc & 1, kPC = (kSc & 2) != 0;
   const int bh = xcd_remap(blockIdx.x, gridDim.x);
   const int h = bh % nheads;
   const int b = bh / nheads;
@@ -242,6 +263,7 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
   v4u hv[kPasses];
   float so[kPasses];
   int xq[kPasses];
+  float sxq[kPC ? kPasses : 1];   // kPC: the x scale of each of the lane's rows
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
     const int p = min(r0 + kRows * k, P - 1);   // rows past headdim: a clamped, unused load
@@ -252,14 +274,17 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     const int p = min(r0 + kRows * k, P - 1);
     so[k] = ss[p];
     xq[k] = xr[p];
+    if constexpr (kPC) sxq[k] = x_scale[h * P + p];
   }
   const v4u bw = *reinterpret_cast<const v4u*>(Bm + (int64_t(b) * ngroups + g) * N + 16 * nq);
   const v4u cw = *reinterpret_cast<const v4u*>(Cm + (int64_t(b) * ngroups + g) * N + 16 * nq);
   const float d = dt[bh];
   const float a = __expf(d * A[h]);
-  const float sx = x_scale[h];
+  const float sx = kPC ? 1.f : x_scale[h];
+  const float dB = d * (kPS ? 1.f : B_scale[g]);
   const float dxB = d * sx * (kPS ? 1.f : B_scale[g]);
-  const float Dsx = (D ? D[h] : 0.f) * sx;
+  const float Dh = D ? D[h] : 0.f;
+  const float Dsx = Dh * sx;
   const float sC = kPS ? 1.f : C_scale[g];
   float bq[16];   // the B codes as floats (per group: the scale is applied per row; per state: included)
   float cf[kPS ? 16 : 1];   // per state: the C values sC[n] c_n
@@ -286,7 +311,8 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
   for (int k = 0; k < kPasses; ++k) {
     const int p = r0 + kRows * k;
     const float xp = float(xq[k]);
-    const float uB = dxB * xp;          // dt xhat[p] sB
+    const float uB = (kPC ? dB * sxq[k] : dxB) * xp;   // dt xhat[p] sB
+    const float Dx = kPC ? Dh * sxq[k] : Dsx;
     const float as = a * so[k];         // exp(dt A) times the cached row's scale
     float v[16];
     float m = 0.f;
@@ -337,21 +363,41 @@ __global__ void __launch_bounds__(kI8Threads) state_update_i8_kernel(
     part = group_sum<kLanesPerRow>(part);
     if (p < P && nq == 0) {
       ss[p] = s;
-      y[int64_t(bh) * P + p] = _Float16(fmaf(sC, part, Dsx * xp) + (ycorr ? ycorr[h * P + p] : 0.f));
+      y[int64_t(bh) * P + p] = _Float16(fmaf(sC, part, Dx * xp) + (ycorr ? ycorr[h * P + p] : 0.f));
     }
   }
 }
 
-template <int N, bool kPS>
-hipError_t launch_n(float* state, const int8_t* x, const float* x_scale, const int8_t* B, const float* B_scale,
-                    const int8_t* C, const float* C_scale, const float* dt, const float* A, const float* D,
-                    const float* ycorr, _Float16* y, int32_t batch, int32_t nheads, int32_t headdim, int32_t ngroups,
-                    hipStream_t stream) {
-  const int nblocks = batch * nheads;
-  hipLaunchKernelGGL((state_update_kernel<N, kPS>), dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B,
-                     B_scale, C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
-  return hipGetLastError();
+// Calls go(kernel template instance) for the (dstate, scale layout) at hand; kernels are
+// instantiated for dstate 64 and 128 and the four scale layouts.
+template <template <int, int> class K, typename Go>
+void dispatch(int32_t dstate, int32_t scales, Go&& go) {
+  auto by_scales = [&](auto n) {
+    constexpr int N = decltype(n)::value;
+    switch (scales & 3) {
+      case 0: go(K<N, 0>::fn); break;
+      case 1: go(K<N, 1>::fn); break;
+      case 2: go(K<N, 2>::fn); break;
+      default: go(K<N, 3>::fn); break;
+    }
+  };
+  if (dstate == 128)
+    by_scales(std::integral_constant<int, 128>{});
+  else
+    by_scales(std::integral_constant<int, 64>{});
 }
+template <int N, int S>
+struct F32 {
+  static constexpr auto fn = state_update_kernel<N, S>;
+};
+template <int N, int S>
+struct F16 {
+  static constexpr auto fn = state_update_f16_kernel<N, S>;
+};
+template <int N, int S>
+struct I8 {
+  static constexpr auto fn = state_update_i8_kernel<N, S>;
+};
 
 }  // namespace
 
@@ -359,16 +405,12 @@ hipError_t launch_state_update_f16(uint16_t* state, const int8_t* x, const float
                                    const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                    const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
                                    int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                   hipStream_t stream, bool per_state) {
+                                   hipStream_t stream, int32_t scales) {
   const int nblocks = batch * nheads;
-  auto go = [&](auto kernel) {
+  dispatch<F16>(dstate, scales, [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B, B_scale, C, C_scale,
                        dt, A, D, ycorr, y, nheads, headdim, ngroups);
-  };
-  if (dstate == 128)
-    per_state ? go(state_update_f16_kernel<128, true>) : go(state_update_f16_kernel<128, false>);
-  else
-    per_state ? go(state_update_f16_kernel<64, true>) : go(state_update_f16_kernel<64, false>);
+  });
   return hipGetLastError();
 }
 
@@ -376,16 +418,12 @@ hipError_t launch_state_update_i8(int8_t* state, float* state_scale, const int8_
                                   const int8_t* B, const float* B_scale, const int8_t* C, const float* C_scale,
                                   const float* dt, const float* A, const float* D, const float* ycorr, _Float16* y,
                                   int32_t batch, int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups,
-                                  hipStream_t stream, bool per_state) {
+                                  hipStream_t stream, int32_t scales) {
   const int nblocks = batch * nheads;
-  auto go = [&](auto kernel) {
+  dispatch<I8>(dstate, scales, [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kI8Threads), 0, stream, state, state_scale, x, x_scale, B, B_scale,
                        C, C_scale, dt, A, D, ycorr, y, nheads, headdim, ngroups);
-  };
-  if (dstate == 128)
-    per_state ? go(state_update_i8_kernel<128, true>) : go(state_update_i8_kernel<128, false>);
-  else
-    per_state ? go(state_update_i8_kernel<64, true>) : go(state_update_i8_kernel<64, false>);
+  });
   return hipGetLastError();
 }
 
@@ -393,16 +431,13 @@ hipError_t launch_state_update(float* state, const int8_t* x, const float* x_sca
                                const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                const float* A, const float* D, const float* ycorr, _Float16* y, int32_t batch,
                                int32_t nheads, int32_t headdim, int32_t dstate, int32_t ngroups, hipStream_t stream,
-                               bool per_state) {
-  if (dstate == 128)
-    return per_state ? launch_n<128, true>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads,
-                                           headdim, ngroups, stream)
-                     : launch_n<128, false>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch,
-                                            nheads, headdim, ngroups, stream);
-  return per_state ? launch_n<64, true>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads,
-                                        headdim, ngroups, stream)
-                   : launch_n<64, false>(state, x, x_scale, B, B_scale, C, C_scale, dt, A, D, ycorr, y, batch, nheads,
-                                         headdim, ngroups, stream);
+                               int32_t scales) {
+  const int nblocks = batch * nheads;
+  dispatch<F32>(dstate, scales, [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kThreads), 0, stream, state, x, x_scale, B, B_scale, C, C_scale,
+                       dt, A, D, ycorr, y, nheads, headdim, ngroups);
+  });
+  return hipGetLastError();
 }
 
 }  // namespace ssdq

@@ -312,3 +312,31 @@ def test_per_state_calls_validate_on_the_host(lib):
     assert lib.ssdq_quantize_per_channel(A16, A16, None, 4, 2, 16, None) == INVALID
     assert lib.ssdq_quantize_per_channel(A16, A16, A16, 4, 0, 16, None) == INVALID
     assert lib.ssdq_quantize_per_channel(None, None, None, 0, 2, 16, None) == 0                # nothing to do
+
+
+def test_scaled_calls_validate_on_the_host(lib):
+    P, i32, i64, sz, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
+    lib.ssdq_chunk_scan_scaled.argtypes = [P] * 13 + [i32, i64, i32, i32, i32, i32, i32, u32, P, sz, P]
+    lib.ssdq_state_update_scaled.argtypes = [i32] + [P] * 13 + [i32] * 5 + [u32, P]
+    ptrs = [A16] * 13
+    for layout in (4, 8, 0x80000000):                    # bits beyond the two layouts
+        assert lib.ssdq_chunk_scan_scaled(*ptrs, 1, 256, 4, 16, 16, 1, 64, layout, A16, 1 << 30, None) == INVALID
+    odd = list(ptrs)
+    odd[9] = A16 + 4                                     # y_corr (optional) misaligned
+    assert lib.ssdq_chunk_scan_scaled(*odd, 1, 256, 4, 16, 16, 1, 64, 2, A16, 1 << 30, None) == INVALID
+    assert lib.ssdq_chunk_scan_scaled(*ptrs, 1, 256, 4, 16, 16, 1, 64, 3, A16, 16, None) == WS_SMALL
+    assert lib.ssdq_chunk_scan_scaled(*ptrs, 1, 256, 3, 16, 16, 2, 64, 2, A16, 1 << 30, None) == INVALID
+    assert lib.ssdq_chunk_scan_scaled(*ptrs, 1, 256, 4, 24, 16, 1, 64, 2, A16, 1 << 30, None) == UNSUPPORTED
+    no_x_scale = list(ptrs)
+    no_x_scale[1] = None
+    assert lib.ssdq_chunk_scan_scaled(*no_x_scale, 1, 256, 4, 16, 16, 1, 64, 2, A16, 1 << 30, None) == INVALID
+    dec = [A16] * 13
+    assert lib.ssdq_state_update_scaled(3, *dec, 2, 4, 64, 128, 2, 2, None) == INVALID      # no such format
+    assert lib.ssdq_state_update_scaled(0, *dec, 2, 4, 64, 128, 2, 4, None) == INVALID      # unknown layout bit
+    bad = list(dec)
+    bad[11] = A16 + 4                                    # y_corr misaligned
+    assert lib.ssdq_state_update_scaled(0, *bad, 2, 4, 64, 128, 2, 2, None) == INVALID
+    no_scale = list(dec)
+    no_scale[1] = None                                   # state_scale, needed by the 8-bit format only
+    assert lib.ssdq_state_update_scaled(2, *no_scale, 2, 4, 64, 128, 2, 3, None) == INVALID
+    assert lib.ssdq_state_update_scaled(0, *no_scale, 2, 4, 64, 96, 2, 2, None) == UNSUPPORTED

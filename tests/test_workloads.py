@@ -79,3 +79,25 @@ def test_per_state_scales():
     assert np.array_equal(cal["B_scale"], (amax / np.float32(127)).astype(np.float32))
     # the state columns carry their own magnitudes: the scales spread well beyond one group's
     assert cal["B_scale"].max() / cal["B_scale"].min() > 4
+
+
+def test_cluster_channel_scales():
+    rng = np.random.default_rng(5)
+    x = (rng.normal(size=(64, 3, 8)) * np.exp(rng.normal(size=(3, 8)))).astype(np.float16)
+    amax = np.abs(x.astype(np.float32)).max(axis=0)
+    # one cluster: the per-head absmax scale on every channel; P clusters: one per channel
+    one = workloads.cluster_channel_scales(x, 1)
+    assert np.array_equal(one, np.repeat(workloads.absmax_scale(x, -2)[:, None], 8, axis=1))
+    assert np.array_equal(workloads.cluster_channel_scales(x, 8), (amax / np.float32(127)).astype(np.float32))
+    # k clusters: k distinct scales per head, each the largest absmax of its members, and the
+    # clusters are runs of the channels sorted by absmax
+    for k in (2, 3):
+        s = workloads.cluster_channel_scales(x, k)
+        assert s.shape == (3, 8) and s.dtype == np.float32
+        for h in range(3):
+            assert len(np.unique(s[h])) == k
+            assert np.all(s[h] * 127 >= amax[h] * (1 - 1e-6))
+            order = np.argsort(amax[h], kind="stable")
+            assert np.all(np.diff(s[h][order]) >= 0)
+            for v in np.unique(s[h]):
+                assert np.isclose(v * 127, amax[h][s[h] == v].max(), rtol=1e-6)

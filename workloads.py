@@ -168,6 +168,30 @@ def percentile_scale(t16: np.ndarray, axis_keep: int, q: float) -> np.ndarray:
     return s.astype(np.float32)
 
 
+def cluster_channel_scales(x16: np.ndarray, nclusters: int) -> np.ndarray:
+    """Static x scales per (head, channel) from channel clusters of an x calibration tensor
+    (..., H, P) -- the reading taken of Quamba2's sort-and-cluster, whose pages name the step but
+    give no algorithm: per head, the channels sorted by their calibration absmax are cut into
+    `nclusters` runs of consecutive sorted order (sizes as equal as possible, the largest channels
+    last), and every channel of a run takes the run's absmax / 127 (1 where it is 0).  Returns
+    (H, P) fp32; nclusters = 1 gives the per-head absmax scale on every channel, nclusters = P
+    one absmax scale per channel."""
+    t = np.abs(x16.astype(np.float32))
+    H, P = t.shape[-2], t.shape[-1]
+    if not 1 <= nclusters <= P:
+        raise ValueError("nclusters must be in 1..headdim")
+    amax = t.reshape(-1, H, P).max(axis=0)                     # (H, P)
+    out = np.empty((H, P), np.float32)
+    bounds = [(k * P) // nclusters for k in range(nclusters + 1)]
+    for h in range(H):
+        order = np.argsort(amax[h], kind="stable")
+        for k in range(nclusters):
+            members = order[bounds[k]:bounds[k + 1]]
+            m = np.float32(amax[h, members].max())
+            out[h, members] = m / np.float32(127.0) if m > 0 else np.float32(1.0)
+    return out
+
+
 def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch: int | None = None,
                  seqlen: int | None = None) -> dict:
     """Seeded prefill inputs.  `batch`/`seqlen` may shrink the test draw (the
@@ -199,7 +223,8 @@ def make_prefill(shape: PrefillShape | str, seed_index: int | None = None, batch
 
 def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0.0,
                          x_clip_pct: float | None = None, bc_per_state: bool = False,
-                         state_spread: float = 0.0) -> tuple[dict, dict]:
+                         state_spread: float = 0.0, channel_spread: float = 0.0,
+                         x_clusters: int | None = None) -> tuple[dict, dict]:
     """A calibration draw and a test draw of one prefill shape that share the model's per-head
     properties and the static scales calibrated on the first: (cal, test), each in make_prefill's
     format.  x = m_h (N(0, 1) + x_mean), so a nonzero x_mean makes the activations one-sided; with
@@ -207,14 +232,20 @@ def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0
     so the test draw's x codes saturate where it exceeds the calibrated range.  With bc_per_state
     the B and C scales are one per (group, state) (absmax_scale_per_state); state_spread > 0 gives
     every state column of B and C its own magnitude exp(N(0, state_spread)) (drawn by the model
-    seed), the case those scales are for.  The calibration draw also carries dt (and h0, when the
-    shape has one), so that a scan can be run over it."""
+    seed), the case those scales are for.  channel_spread > 0 likewise gives every x channel of
+    every head its own magnitude exp(N(0, channel_spread)), and x_clusters = k calibrates x with
+    one scale per (head, channel cluster) (cluster_channel_scales: an (H, P) table).  The
+    calibration draw also carries dt (and h0, when the shape has one), so that a scan can be run
+    over it."""
     k = seed_index
     b, L, H, P, N, G = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
     params = model_params(H, shape.x_dist, shape.dt_dist, 100 + k)
     col = np.ones((2, G, N), np.float32)
     if state_spread > 0:
         col = np.exp(_rng(500 + k).normal(0.0, state_spread, size=(2, G, N))).astype(np.float32)
+    chan = None
+    if channel_spread > 0:
+        chan = np.exp(_rng(600 + k).normal(0.0, channel_spread, size=(H, P))).astype(np.float32)
 
     def draw(seed):
         rng = _rng(seed)
@@ -222,6 +253,8 @@ def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0
         if state_spread > 0:
             B = (B.astype(np.float32) * col[0]).astype(np.float16)
             C = (C.astype(np.float32) * col[1]).astype(np.float16)
+        if chan is not None:
+            x = (x.astype(np.float32) * chan).astype(np.float16)
         if x_mean:
             x = (x.astype(np.float32) + np.float32(x_mean) * params.x_mag.astype(np.float32)[:, None]).astype(np.float16)
         dt = _draw_dt(rng, (b, L), H, params, shape.dt_dist)
@@ -232,7 +265,10 @@ def make_calibrated_pair(shape: PrefillShape, seed_index: int, x_mean: float = 0
                     batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, chunk=shape.chunk)
 
     cal, test = draw(300 + k), draw(200 + k)
-    sx = absmax_scale(cal["x16"], -2) if x_clip_pct is None else percentile_scale(cal["x16"], -2, x_clip_pct)
+    if x_clusters is not None:
+        sx = cluster_channel_scales(cal["x16"], x_clusters)
+    else:
+        sx = absmax_scale(cal["x16"], -2) if x_clip_pct is None else percentile_scale(cal["x16"], -2, x_clip_pct)
     bc = absmax_scale_per_state if bc_per_state else (lambda t: absmax_scale(t, -2))
     scales = dict(x_scale=sx, B_scale=bc(cal["B16"]), C_scale=bc(cal["C16"]))
     cal.update(scales)
