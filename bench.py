@@ -160,6 +160,7 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
+    ap.add_argument("--no-scale-layouts", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (for scaling HBM counter readings)")
     return ap.parse_args(argv)
@@ -392,6 +393,8 @@ def main(argv=None):
 
     if not args.no_frontend:
         result["frontend"] = bench_frontend(args, torch, ssdq, workloads, dev, head)
+    if not args.no_scale_layouts:
+        result["scale_layouts"] = bench_scale_layouts(args, torch, ssdq, workloads, dev, head)
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, ssdq, workloads, dev)
 
@@ -409,6 +412,69 @@ def main(argv=None):
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_scale_layouts(args, torch, ssdq, workloads, dev, name):
+    """The scan (stages only, codes already in HBM) of one workload under each static scale layout
+    and with the output correction, against the plain per-head / per-group layout in the same run:
+    B, C scales per (group, state), x scales per (head, channel) from 8 channel clusters, both,
+    and all of them with the correction.  The scales are calibrated on the draw itself (timing
+    only; parity is the tests' business).  Returns microseconds per scan and the ratio to plain."""
+    print(f"[bench] generating {name} for the scale layouts", file=sys.stderr, flush=True)
+    inp = workloads.make_prefill(name)
+    T = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    b, L, H, P, N, G, Q = (inp[k] for k in ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk"))
+    x16, B16, C16 = T(inp["x16"]), T(inp["B16"]), T(inp["C16"])
+    dt, A, D, h0 = T(inp["dt"]), T(inp["A"]), T(inp["D"]), T(inp["h0"])
+    scales = {"head": (T(inp["x_scale"]), T(inp["B_scale"]), T(inp["C_scale"])),
+              "fine": (T(workloads.cluster_channel_scales(inp["x16"], 8)),
+                       T(workloads.absmax_scale_per_state(inp["B16"])), T(workloads.absmax_scale_per_state(inp["C16"])))}
+    y_corr = T(np.random.default_rng(7).normal(0, 0.01, size=(H, P)).astype(np.float32))
+    del inp
+    y = torch.empty((b, L, H, P), dtype=torch.float16, device=dev)
+    hf = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(ssdq.chunk_scan_workspace_size(b, L, H, P, N, Q), dtype=torch.uint8, device=dev)
+    codes = {}
+    for key, (sx, sB, sC) in scales.items():
+        codes[key] = (ssdq.quantize(x16, sx), ssdq.quantize(B16, sB), ssdq.quantize(C16, sC))
+    del x16, B16, C16
+    variants = {"plain": ("head", "head", None), "corrected": ("head", "head", y_corr),
+                "bc_per_state": ("head", "fine", None), "x_per_channel": ("fine", "head", None),
+                "x_per_channel+bc_per_state": ("fine", "fine", None),
+                "x_per_channel+bc_per_state+corrected": ("fine", "fine", y_corr)}
+    stream = torch.cuda.current_stream().cuda_stream
+    bufs = {}
+    for vname, (xk, bk, corr) in variants.items():
+        qx, sx = codes[xk][0], scales[xk][0]
+        qB, qC = codes[bk][1], codes[bk][2]
+        sB, sC = scales[bk][1], scales[bk][2]
+        bufs[vname] = ssdq.ScanBuffers(qx, sx, qB, sB, qC, sC, dt, A, D, h0, chunk=Q, y=y, h_final=hf,
+                                       workspace=ws, y_corr=corr)
+    # warm-up of every variant, then rounds that visit the variants in turn (alternating order), so
+    # that clock changes over the run fall on all of them alike
+    for _ in range(max(2, min(args.warmup, 10))):
+        for buf in bufs.values():
+            buf.run()
+    torch.cuda.synchronize()
+    rounds, per = 6, max(1, min(args.steps, 120) // 6)
+    total = {v: 0.0 for v in bufs}
+    for r in range(rounds):
+        order = list(bufs) if r % 2 == 0 else list(reversed(list(bufs)))
+        for vname in order:
+            e0, e1 = HipEvent(stream), HipEvent(stream)
+            e0.record()
+            for _ in range(per):
+                bufs[vname].run()
+            e1.record()
+            torch.cuda.synchronize()
+            total[vname] += e0.elapsed_time(e1)
+    steps = rounds * per
+    out = {v: {"scan_us": round(total[v] * 1e3 / steps, 2)} for v in bufs}
+    base = out["plain"]["scan_us"]
+    for v in out.values():
+        v["vs_plain"] = round(v["scan_us"] / base, 4)
+    return {"workload": name, "steps": steps, "note": "scan stages only (codes resident); scales calibrated on "
+            "the draw itself, x per (head, channel) from 8 channel clusters", "layouts": out}
 
 
 def bench_frontend(args, torch, ssdq, workloads, dev, name):
