@@ -180,6 +180,18 @@ ssdq_status ssdq_chunk_scan(const int8_t* x, const float* x_scale, const int8_t*
 int32_t ssdq_chunk_scan_state_fused(int32_t batch, int32_t nheads);
 
 /*
+ * The form of stage 0 that ssdq_chunk_scan (scale_layout 0) or ssdq_chunk_scan_scaled takes on
+ * the current device for this batch and head count (host; informational, the results do not
+ * depend on it beyond fp32 rounding):
+ *   0 : three kernels (chunk states in parallel, then state passing; ssdq_chunk_scan_state_fused 0)
+ *   8 : the folded state kernel in blocks of eight waves, one block per CU at a time
+ *   4 : the folded state kernel in blocks of four waves, two blocks per CU (many more sequences
+ *       than CUs; never with SSDQ_SCALES_BC_PER_STATE)
+ *  -1 : non-positive sizes or unknown scale_layout bits.
+ */
+int32_t ssdq_chunk_scan_plan(int32_t batch, int32_t nheads, uint32_t scale_layout);
+
+/*
  * One stage of ssdq_chunk_scan, with the same arguments and validation.
  * Running stages 0..2 in order on one stream is exactly ssdq_chunk_scan; the
  * intermediate results are in the workspace layout documented above.  This

@@ -87,6 +87,8 @@ lib.ssdq_chunk_scan_noalloc_scratch_size.argtypes = [_i32, _i64, _i32, _i32, _i3
 lib.ssdq_chunk_scan_noalloc_scratch_size.restype = _sz
 lib.ssdq_chunk_scan_state_fused.argtypes = [_i32, _i32]
 lib.ssdq_chunk_scan_state_fused.restype = _i32
+lib.ssdq_chunk_scan_plan.argtypes = [_i32, _i32, ctypes.c_uint32]
+lib.ssdq_chunk_scan_plan.restype = _i32
 
 
 # scale layouts of ssdq_chunk_scan_scaled / ssdq_state_update_scaled (bit flags)
@@ -104,6 +106,12 @@ def chunk_scan_state_fused(batch: int, nheads: int) -> bool:
     """True when, on the current device, stage 0 of the chunk scan also carries the state across
     chunks (stage 1 then does nothing and the chunk states are not written)."""
     return bool(lib.ssdq_chunk_scan_state_fused(batch, nheads))
+
+
+def chunk_scan_plan(batch: int, nheads: int, scale_layout: int = 0) -> int:
+    """The form of stage 0 on the current device: 0 three kernels, 8 or 4 the folded state kernel
+    in blocks of that many waves (ssdq_chunk_scan_plan)."""
+    return int(lib.ssdq_chunk_scan_plan(batch, nheads, scale_layout))
 
 
 def status_string(status: int) -> str:

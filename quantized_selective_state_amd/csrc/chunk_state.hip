@@ -639,6 +639,288 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Four-wave form of the folded state kernel, for shapes with many (batch, head) sequences per
+// CU: one block of four waves per sequence, wave w owning channel tile w over all of a chunk's
+// tokens and all states.  A chunk's products then need no partial exchange between waves (the
+// three limbs of all four K steps accumulate in one wave's int32 registers), a state row's
+// maximum is a reduction inside the wave, and the carried-state encoding covers a whole row per
+// lane group.  The chunk tiles are single-buffered (~53 KB of LDS at chunk 256), so two blocks
+// share a CU: one block's barriers and tile loads are covered by the other's work.  Per chunk:
+// row maxima (registers), wait for the tiles, barrier, products, barrier (the tiles and this
+// group's weights are free again), the next chunk's tile loads, the carried-state encoding and
+// stores, the update of H.
+constexpr int kS4Threads = 256;
+constexpr int kS4Waves = kS4Threads / kWave;
+constexpr int kGroup4 = kS4Waves;   // chunks whose weights one prologue prepares (one per wave)
+
+template <int Q, bool kPS, bool kPC>
+__global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu(2))) state_scan4_kernel(
+    const int8_t* __restrict__ x, const float* __restrict__ x_scale, const int8_t* __restrict__ Bm,
+    const float* __restrict__ B_scale, const float* __restrict__ C_scale, const float* __restrict__ dt,
+    const float* __restrict__ A,
+    const float* h0, float* h_final, float* __restrict__ acs, float* __restrict__ dtc, int8_t* __restrict__ hprev,
+    float* __restrict__ hscale, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
+    int32_t ngroups, int32_t nchunks) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
+  __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
+  __shared__ __attribute__((aligned(16))) uint32_t om[kGroup4][Q];
+  __shared__ float gdec[kGroup4];
+  __shared__ int gexp[kGroup4];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int bh = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = bh % nheads;
+  const int b = bh / nheads;
+  const int g = h / (nheads / ngroups);
+  const int P = headdim, N = dstate;
+  const int lcol = lane % 16, kg = lane / 16;
+  const int pt = wave;
+  constexpr int kNt = kMaxN / 16;
+  constexpr int kTok = Q / kWave;
+  const bool prow = 16 * pt < P;
+  const uint32_t xrow = uint32_t(nheads * P), brow = uint32_t(ngroups * N);
+  const float sxB = x_scale[kPC ? h * P + min(16 * pt + lcol, P - 1) : h] * (kPS ? 1.f : B_scale[g]);
+  const float Ah = A[h];
+
+  // running state H[p = 16 pt + lcol][n = 16 t + 4 kg + i], all eight state tiles
+  const int64_t pn = int64_t(P) * N;
+  const uint32_t hoff = (uint32_t(16 * pt + lcol) * uint32_t(N) + 4 * kg) * 4u;
+  v4f H[kNt];
+  v4f sig[kPS ? kNt : 1];
+  {
+    const Rsrc r0 = make_rsrc(h0 ? h0 + int64_t(bh) * pn : h0, h0 && prow ? uint32_t(pn) * 4u : 0u);
+#pragma unroll
+    for (int t = 0; t < kNt; ++t)
+      H[t] = __builtin_bit_cast(v4f, buf_load16(r0, 16 * t < N ? hoff + 64u * t : kOutOfRange));
+    if constexpr (kPS) {
+      const Rsrc rsb = make_rsrc(B_scale + g * N, uint32_t(N) * 4u), rsc = make_rsrc(C_scale + g * N, uint32_t(N) * 4u);
+#pragma unroll
+      for (int t = 0; t < kNt; ++t) {
+        const uint32_t o = 16 * t < N ? uint32_t(16 * t + 4 * kg) * 4u : kOutOfRange;
+        const v4f sb = __builtin_bit_cast(v4f, buf_load16(rsb, o)), sc = __builtin_bit_cast(v4f, buf_load16(rsc, o));
+        sig[t] = sb * sc;
+        H[t] = H[t] * sc;
+      }
+    }
+  }
+
+  // chunk tiles by buffer loads straight into LDS (16 bytes per lane, swizzled slots)
+  constexpr int kXd = Q * (kMaxP / 16) / kS4Threads;   // Q / 64
+  constexpr int kBd = Q * (kMaxN / 16) / kS4Threads;   // Q / 32
+  // slot k * 256 + tid of a tile: row j, 16-byte chunk pc in LDS, global chunk cc (offsets are
+  // formed at each use: fewer long-lived registers)
+  auto xoff = [&](int k) {
+    const int slot = k * kS4Threads + tid, j = slot >> 2, pc = slot & 3, cc = pc ^ ((j >> 2) & 3);
+    return 16 * cc < P ? uint32_t(j) * xrow + 16 * cc : kOutOfRange;
+  };
+  auto boff = [&](int k) {
+    const int slot = k * kS4Threads + tid, j = slot >> 3, pc = slot & 7, cc = pc ^ ((j >> 1) & 7);
+    return 16 * cc < N ? uint32_t(j) * brow + 16 * cc : kOutOfRange;
+  };
+  auto dma_chunk = [&](int c) {
+    const bool ok = c < nchunks;
+    const int64_t t0 = ok ? int64_t(c) * Q : 0;
+    const int len = ok ? int(seqlen - t0 < Q ? seqlen - t0 : Q) : 1;
+    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, ok ? uint32_t(len - 1) * xrow + P : 0u);
+    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, ok ? uint32_t(len - 1) * brow + N : 0u);
+#pragma unroll
+    for (int k = 0; k < kXd; ++k) buf_load16_lds(rx, xs + 16 * (k * kS4Threads + kWave * wave), xoff(k));
+#pragma unroll
+    for (int k = 0; k < kBd; ++k) buf_load16_lds(rb, bs + 16 * (k * kS4Threads + kWave * wave), boff(k));
+  };
+  float dtg[kTok];
+  auto load_dt_group = [&](int g0) {
+    const int c = g0 + wave;
+    const bool ok = c < nchunks;
+    const int64_t t0 = ok ? int64_t(c) * Q : 0;
+    const int len = ok ? int(seqlen - t0 < Q ? seqlen - t0 : Q) : 1;
+    const Rsrc rdt = make_rsrc(dt + (int64_t(b) * seqlen + t0) * nheads + h, ok ? (uint32_t(len - 1) * nheads + 1u) * 4u : 0u);
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) dtg[u] = buf_loadf(rdt, uint32_t(lane * kTok + u) * uint32_t(nheads) * 4u);
+  };
+  auto group_prologue = [&](int g0) {
+    const int c = g0 + wave;
+    if (c >= nchunks) return;
+    const int64_t t0 = int64_t(c) * Q;
+    const int len = int(seqlen - t0 < Q ? seqlen - t0 : Q);
+    float a[kTok];
+    float run = 0.f;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      run += dtg[u] * Ah;
+      a[u] = run;
+    }
+    const float incl = wave_inclusive_sum(run);
+    const float excl = incl - run;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) a[u] += excl;
+    const int64_t ro = ((int64_t(b) * nheads + h) * nchunks + c) * Q + lane * kTok;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      acs[ro + u] = a[u];
+      dtc[ro + u] = dtg[u];
+    }
+    const int lastl = (len - 1) / kTok, lastu = (len - 1) % kTok;
+    float asel = a[0];
+#pragma unroll
+    for (int u = 1; u < kTok; ++u) asel = lastu == u ? a[u] : asel;
+    const float a_last = lane_broadcast(asel, lastl);
+    float w[kTok], wm = 0.f;
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      w[u] = dtg[u] > 0.f ? __builtin_amdgcn_exp2f((a_last - a[u]) * kLog2e) * dtg[u] : 0.f;
+      wm = fmaxf(wm, w[u]);
+    }
+    const int e = min(max(ceil_log2_pos(wave_max(wm)), -100), 100);
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) om[wave][lane * kTok + u] = uint32_t(fminf(w[u] * exp2i(23 - e), 8388607.f) + 0.5f);
+    if (lane == 0) {
+      gdec[wave] = __builtin_amdgcn_exp2f(a_last * kLog2e);
+      gexp[wave] = e;
+    }
+  };
+  load_dt_group(0);
+  dma_chunk(0);
+
+  const int rowb = 16 * kg + (lcol >> 1), half8 = 8 * (lcol & 1);
+  const int xa0 = xpos(rowb, 16 * pt + half8), xa1 = xpos(rowb + 8, 16 * pt + half8);
+  int ba[kNt];
+#pragma unroll
+  for (int t = 0; t < kNt; ++t) ba[t] = bpos(rowb, 16 * t + half8);
+
+  auto kstep = [&](v4i (&acc)[kNt][3], int cl, int kb, bool first) {
+    const int j0 = kb + 16 * kg;
+    const v2u xlo = tr8(xs + xa0 + kb * kMaxP), xhi = tr8(xs + xa1 + kb * kMaxP);
+    const uint32_t xw[4] = {xlo[0], xlo[1], xhi[0], xhi[1]};
+    v4i l1, l2, l3;
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      const v4u o4 = *reinterpret_cast<const v4u*>(&om[cl][j0 + 4 * dw]);
+      uint32_t W[4], pl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) W[k] = uint32_t(mad24s(sbyte(xw[dw], k), int32_t(o4[k]), 8421376));
+      transpose4x4(W, pl);
+      l1[dw] = int(pl[3]);
+      l2[dw] = int(pl[2] ^ 0x80808080u);
+      l3[dw] = int(pl[1] ^ 0x80808080u);
+    }
+#pragma unroll
+    for (int t = 0; t < kNt; ++t) {
+      const v2u blo = tr8(bs + ba[t] + kb * kMaxN), bhi = tr8(bs + ba[t ^ 4] + (kb + 8) * kMaxN);
+      const v4i bop = {int(blo[0]), int(blo[1]), int(bhi[0]), int(bhi[1])};
+      const v4i z = {0, 0, 0, 0};
+      acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l1, first ? z : acc[t][0], 0, 0, 0);
+      acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l2, first ? z : acc[t][1], 0, 0, 0);
+      acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l3, first ? z : acc[t][2], 0, 0, 0);
+    }
+  };
+
+  for (int g0 = 0; g0 < nchunks; g0 += kGroup4) {
+    group_prologue(g0);
+    load_dt_group(g0 + kGroup4);
+    const int gend = min(g0 + kGroup4, nchunks);
+    for (int c = g0; c < gend; ++c) {
+      const int cl = c - g0;
+      // the row maximum of the state entering the chunk: this lane's 32 states, then the row's
+      // four lanes (kg = 0..3) by half-wave swaps
+      float m = 0.f;
+#pragma unroll
+      for (int t = 0; t < kNt; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
+      {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's tiles have landed
+      __syncthreads();                      // tiles (and, at a group start, the weights) visible
+
+      v4i acc[kNt][3];
+      kstep(acc, cl, 0, true);
+#pragma unroll 1
+      for (int kb = 64; kb < Q; kb += 64) kstep(acc, cl, kb, false);
+      __builtin_amdgcn_iglp_opt(0);
+      const float decay = gdec[cl];
+      const float post = sxB * exp2i(gexp[cl] + 1);
+      __syncthreads();                      // every wave is done with the tiles and this group's weights
+      dma_chunk(c + 1);                     // the next chunk's tiles, into the same buffers
+
+      // the state entering the chunk as two INT8 limbs + a power-of-two row scale
+      if (prow) {
+        const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
+        const float inv = exp2i(8 - ex);
+        const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
+        const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
+        const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {   // 64-state blocks
+          if (64 * hb >= N) break;
+          v4u Q1, Q2;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int t = 4 * hb + tt;
+            uint32_t V[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) V[i] = uint32_t(int32_t(fmaf(H[t][i], inv, 128.f)));
+            const uint32_t b1lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0501u), b1hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0501u);
+            const uint32_t b0lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0400u), b0hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0400u);
+            Q1[tt] = __builtin_amdgcn_perm(b1hi, b1lo, 0x05040100u);
+            Q2[tt] = __builtin_amdgcn_perm(b0hi, b0lo, 0x05040100u) ^ 0x80808080u;
+          }
+          if (64 * hb + 64 <= N) {
+            __builtin_amdgcn_raw_buffer_store_b128(Q1, rh, row + 64 * hb + 16 * kg, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(Q2, rh, row + 64 * hb + 16 * kg, int(pn), 0);
+          } else {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              if (64 * hb + 16 * tt >= N) break;
+              __builtin_amdgcn_raw_buffer_store_b32(Q1[tt], rh, row + 64 * hb + 16 * tt + 4 * kg, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(Q2[tt], rh, row + 64 * hb + 16 * tt + 4 * kg, int(pn), 0);
+            }
+          }
+        }
+        if (kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
+      }
+
+      // H <- exp(Acs_last) H + S_c (the chunk's products recombined from their three limbs)
+#pragma unroll
+      for (int t = 0; t < kNt; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
+          const float sv = fmaf(float(lo), 1.f / 65536.f, float(acc[t][0][i]));
+          if constexpr (kPS)
+            H[t][i] = fmaf(decay, H[t][i], sv * (post * sig[t][i]));
+          else
+            H[t][i] = fmaf(decay, H[t][i], sv * post);
+        }
+      }
+    }
+  }
+
+  if (h_final && prow) {
+    const Rsrc rf = make_rsrc(h_final + int64_t(bh) * pn, uint32_t(pn) * 4u);
+#pragma unroll
+    for (int t = 0; t < kNt; ++t) {
+      if (16 * t >= N) break;
+      v4f hf = H[t];
+      if constexpr (kPS) {
+        const v4f sc = *reinterpret_cast<const v4f*>(C_scale + g * N + 16 * t + 4 * kg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hf[i] = hf[i] / sc[i];
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, hf), rf, hoff + 64u * t, 0, 0);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
@@ -660,16 +942,54 @@ hipError_t launch_chunk_state(const ScanShape& s, const ScanArgs& a, hipStream_t
 
 namespace ssdq {
 
-bool state_scan_fused(int32_t batch, int32_t nheads) {
+namespace {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                               hipSuccess)
-    return false;
+    return 0;
+  return cus;
+}
+}  // namespace
+
+bool state_scan_fused(int32_t batch, int32_t nheads) {
+  const int cus = device_cus();
   return cus > 0 && int64_t(batch) * nheads >= cus;
+}
+
+// With C CUs, b H sequences take ceil(bH / 2C) rounds of two co-resident 4-wave blocks per CU
+// against ceil(bH / C) rounds of one 8-wave block, and a 4-wave block sharing its CU takes ~1.77
+// times as long as an 8-wave block alone (113 against 64 us per block at mamba2-8b-prefill); the
+// four-wave form runs when that model gives it fewer such units.  Not with B, C scales per
+// (group, state): that instance would need more registers than two waves per SIMD leave.
+int state_scan_waves(int32_t batch, int32_t nheads, bool bc_per_state) {
+  const int cus = device_cus();
+  const int64_t bh = int64_t(batch) * nheads;
+  if (cus <= 0 || bh < cus) return 0;
+  if (bc_per_state) return 8;
+  const int64_t r4 = (bh + 2 * cus - 1) / (2 * cus), r8 = (bh + cus - 1) / cus;
+  return 177 * r4 < 100 * r8 ? 4 : 8;
 }
 
 hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream) {
   const int nblocks = s.batch * s.nheads;
+  if (state_scan_waves(s.batch, s.nheads, a.bc_per_state) == 4) {
+    auto go4 = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kS4Threads), 0, stream, a.x, a.x_scale, a.B, a.B_scale,
+                         a.C_scale, a.dt, a.A, a.h0, a.h_final, a.acs, a.dtc, a.hprev, a.hscale, s.seqlen, s.nheads,
+                         s.headdim, s.dstate, s.ngroups, s.nchunks);
+    };
+    auto by_chunk4 = [&](auto pc) {
+      constexpr bool kPC = decltype(pc)::value;
+      switch (s.chunk) {
+        case 64: go4(state_scan4_kernel<64, false, kPC>); break;
+        case 128: go4(state_scan4_kernel<128, false, kPC>); break;
+        default: go4(state_scan4_kernel<256, false, kPC>); break;
+      }
+    };
+    a.x_per_channel ? by_chunk4(std::true_type{}) : by_chunk4(std::false_type{});
+    return hipGetLastError();
+  }
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(nblocks), dim3(kSThreads), 0, stream, a.x, a.x_scale, a.B, a.B_scale, a.C_scale,
                        a.dt, a.A, a.h0, a.h_final, a.acs, a.dtc, a.hprev, a.hscale, s.seqlen, s.nheads, s.headdim,

@@ -209,6 +209,12 @@ int32_t ssdq_chunk_scan_state_fused(int32_t batch, int32_t nheads) {
   return state_scan_fused(batch, nheads) ? 1 : 0;
 }
 
+int32_t ssdq_chunk_scan_plan(int32_t batch, int32_t nheads, uint32_t scale_layout) {
+  if (batch <= 0 || nheads <= 0) return -1;
+  if (scale_layout & ~uint32_t(SSDQ_SCALES_BC_PER_STATE | SSDQ_SCALES_X_PER_CHANNEL)) return -1;
+  return state_scan_waves(batch, nheads, (scale_layout & SSDQ_SCALES_BC_PER_STATE) != 0);
+}
+
 ssdq_status ssdq_chunk_scan_stage(int32_t stage, const int8_t* x, const float* x_scale, const int8_t* B,
                                   const float* B_scale, const int8_t* C, const float* C_scale, const float* dt,
                                   const float* A, const float* D, const float* h0, void* y, float* h_final,

@@ -83,6 +83,8 @@ hipError_t launch_state_passing(const ScanShape& s, const ScanArgs& a, hipStream
 // Stages 0 and 1 in one kernel (one block per (batch, head), chunks in order); used when
 // state_scan_fused(batch, nheads), i.e. when there are at least as many sequences as CUs.
 bool state_scan_fused(int32_t batch, int32_t nheads);
+// Waves per block of the folded state kernel for this shape (4 or 8), or 0 when it does not run.
+int state_scan_waves(int32_t batch, int32_t nheads, bool bc_per_state);
 hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 hipError_t launch_chunk_output(const ScanShape& s, const ScanArgs& a, hipStream_t stream);
 // front-end launch geometry: a lane owns kFeChannels channels and a strip of kFeTokens tokens;
