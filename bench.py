@@ -325,7 +325,8 @@ def bench_prefill(name, steps, warmup, torch, ssdq, workloads, dev, keep_inputs=
                      "bytes_per_token": unit[spec_name] if spec_name else kb[dominant] / tokens,
                      "units_per_launch": tokens,
                      "kernel_alg_bytes": kb[dominant], "kernel_alg_frac": round(own / HBM_PEAK_GBS, 4)},
-        "plan": "stage 0 carries the state (state passing folded in)" if fused else "three stages",
+        "plan": ("stage 0 carries the state (state passing folded in), blocks of "
+                 f"{ssdq.chunk_scan_plan(b, H)} waves") if fused else "three stages",
         "scan_tokens_per_s": round(tokens / (scan_ms / 1e3), 1),
         "mfma_pct_of_int8_peak": round(100 * total_ops / (scan_ms / 1e3) / INT8_PEAK_OPS, 3),
         "chunk_output_mfma_pct_of_int8_peak": round(
