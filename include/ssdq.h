@@ -186,7 +186,7 @@ int32_t ssdq_chunk_scan_state_fused(int32_t batch, int32_t nheads);
  *   0 : three kernels (chunk states in parallel, then state passing; ssdq_chunk_scan_state_fused 0)
  *   8 : the folded state kernel in blocks of eight waves, one block per CU at a time
  *   4 : the folded state kernel in blocks of four waves, two blocks per CU (many more sequences
- *       than CUs; never with SSDQ_SCALES_BC_PER_STATE)
+ *       than CUs)
  *  -1 : non-positive sizes or unknown scale_layout bits.
  */
 int32_t ssdq_chunk_scan_plan(int32_t batch, int32_t nheads, uint32_t scale_layout);

@@ -667,6 +667,7 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(16))) uint32_t om[kGroup4][Q];
   __shared__ float gdec[kGroup4];
   __shared__ int gexp[kGroup4];
+  __shared__ __attribute__((aligned(16))) float sig_s[kPS ? kMaxN : 4];   // kPS: B_scale C_scale per state
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -689,21 +690,22 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
   const int64_t pn = int64_t(P) * N;
   const uint32_t hoff = (uint32_t(16 * pt + lcol) * uint32_t(N) + 4 * kg) * 4u;
   v4f H[kNt];
-  v4f sig[kPS ? kNt : 1];
   {
     const Rsrc r0 = make_rsrc(h0 ? h0 + int64_t(bh) * pn : h0, h0 && prow ? uint32_t(pn) * 4u : 0u);
 #pragma unroll
     for (int t = 0; t < kNt; ++t)
       H[t] = __builtin_bit_cast(v4f, buf_load16(r0, 16 * t < N ? hoff + 64u * t : kOutOfRange));
     if constexpr (kPS) {
-      const Rsrc rsb = make_rsrc(B_scale + g * N, uint32_t(N) * 4u), rsc = make_rsrc(C_scale + g * N, uint32_t(N) * 4u);
+      // the running state is kept as H_C (scaled by each state's C scale); the products' factor
+      // per state, B_scale C_scale, waits in LDS (read back per chunk: registers are short here)
+      const Rsrc rsc = make_rsrc(C_scale + g * N, uint32_t(N) * 4u);
 #pragma unroll
       for (int t = 0; t < kNt; ++t) {
         const uint32_t o = 16 * t < N ? uint32_t(16 * t + 4 * kg) * 4u : kOutOfRange;
-        const v4f sb = __builtin_bit_cast(v4f, buf_load16(rsb, o)), sc = __builtin_bit_cast(v4f, buf_load16(rsc, o));
-        sig[t] = sb * sc;
-        H[t] = H[t] * sc;
+        H[t] = H[t] * __builtin_bit_cast(v4f, buf_load16(rsc, o));
       }
+      if (tid < kMaxN) sig_s[tid] = tid < N ? B_scale[g * N + tid] * C_scale[g * N + tid] : 0.f;
+      // (made visible by the first chunk's barrier)
     }
   }
 
@@ -892,12 +894,14 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
       // H <- exp(Acs_last) H + S_c (the chunk's products recombined from their three limbs)
 #pragma unroll
       for (int t = 0; t < kNt; ++t) {
+        v4f sg = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (kPS) sg = *reinterpret_cast<const v4f*>(&sig_s[16 * t + 4 * kg]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
           const float sv = fmaf(float(lo), 1.f / 65536.f, float(acc[t][0][i]));
           if constexpr (kPS)
-            H[t][i] = fmaf(decay, H[t][i], sv * (post * sig[t][i]));
+            H[t][i] = fmaf(decay, H[t][i], sv * (post * sg[i]));
           else
             H[t][i] = fmaf(decay, H[t][i], sv * post);
         }
@@ -960,13 +964,13 @@ bool state_scan_fused(int32_t batch, int32_t nheads) {
 // With C CUs, b H sequences take ceil(bH / 2C) rounds of two co-resident 4-wave blocks per CU
 // against ceil(bH / C) rounds of one 8-wave block, and a 4-wave block sharing its CU takes ~1.77
 // times as long as an 8-wave block alone (113 against 64 us per block at mamba2-8b-prefill); the
-// four-wave form runs when that model gives it fewer such units.  Not with B, C scales per
-// (group, state): that instance would need more registers than two waves per SIMD leave.
+// four-wave form runs when that model gives it fewer such units (the scale layout does not
+// change the choice).
 int state_scan_waves(int32_t batch, int32_t nheads, bool bc_per_state) {
+  (void)bc_per_state;
   const int cus = device_cus();
   const int64_t bh = int64_t(batch) * nheads;
   if (cus <= 0 || bh < cus) return 0;
-  if (bc_per_state) return 8;
   const int64_t r4 = (bh + 2 * cus - 1) / (2 * cus), r8 = (bh + cus - 1) / cus;
   return 177 * r4 < 100 * r8 ? 4 : 8;
 }
@@ -979,15 +983,20 @@ hipError_t launch_state_scan(const ScanShape& s, const ScanArgs& a, hipStream_t 
                          a.C_scale, a.dt, a.A, a.h0, a.h_final, a.acs, a.dtc, a.hprev, a.hscale, s.seqlen, s.nheads,
                          s.headdim, s.dstate, s.ngroups, s.nchunks);
     };
-    auto by_chunk4 = [&](auto pc) {
-      constexpr bool kPC = decltype(pc)::value;
+    auto by_chunk4 = [&](auto ps, auto pc) {
+      constexpr bool kPS = decltype(ps)::value, kPC = decltype(pc)::value;
       switch (s.chunk) {
-        case 64: go4(state_scan4_kernel<64, false, kPC>); break;
-        case 128: go4(state_scan4_kernel<128, false, kPC>); break;
-        default: go4(state_scan4_kernel<256, false, kPC>); break;
+        case 64: go4(state_scan4_kernel<64, kPS, kPC>); break;
+        case 128: go4(state_scan4_kernel<128, kPS, kPC>); break;
+        default: go4(state_scan4_kernel<256, kPS, kPC>); break;
       }
     };
-    a.x_per_channel ? by_chunk4(std::true_type{}) : by_chunk4(std::false_type{});
+    using T = std::true_type;
+    using F = std::false_type;
+    if (a.bc_per_state)
+      a.x_per_channel ? by_chunk4(T{}, T{}) : by_chunk4(T{}, F{});
+    else
+      a.x_per_channel ? by_chunk4(F{}, T{}) : by_chunk4(F{}, F{});
     return hipGetLastError();
   }
   auto go = [&](auto kernel) {

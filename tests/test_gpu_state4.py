@@ -3,8 +3,8 @@ more (batch, head) sequences than CUs, two blocks of four waves per CU, each wav
 over all tokens and states).  Every sequence of each shape is compared with the oracle at the
 scan's bars; the carried state in the workspace is checked against the oracle's chunk-boundary
 states; the shapes cover the three chunk sizes, ragged lengths, narrow heads, a partial 64-state
-block, x scales per (head, channel), the output correction, an in-place final state, and the
-fallback to eight-wave blocks for B, C scales per (group, state)."""
+block, x scales per (head, channel), B and C scales per (group, state), all scale layouts with
+the output correction, and an in-place final state."""
 import numpy as np
 import pytest
 import torch
@@ -77,12 +77,23 @@ def test_channel_scales_and_correction():
     _check(inp, "x per channel + correction", y_corr=mu)
 
 
-def test_state_scales_fall_back_to_eight_wave_blocks():
+@pytest.mark.parametrize("chunk", [128, 256])
+def test_state_scales(chunk):
+    # B, C scales per (group, state): the per-state factors of the update come from LDS
     nheads = 64
-    shape = workloads.PrefillShape("p4ps", _shape_for_plan4(nheads), 256, nheads, 64, 128, 2, 128, "outlier_heads",
+    shape = workloads.PrefillShape("p4ps", _shape_for_plan4(nheads), 300, nheads, 64, 128, 2, chunk, "outlier_heads",
                                    "fixed_bias", 0.1)
     _, inp = workloads.make_calibrated_pair(shape, 131, bc_per_state=True, state_spread=1.0)
-    _check(inp, "B, C per state", plan=8)
+    _check(inp, f"B, C per state, Q={chunk}")
+
+
+def test_all_scale_layouts_with_correction():
+    nheads = 64
+    shape = workloads.PrefillShape("p4all", _shape_for_plan4(nheads), 256, nheads, 32, 64, 4, 64, "outlier_heads",
+                                   "fixed_bias", 0.2)
+    cal, inp = workloads.make_calibrated_pair(shape, 134, bc_per_state=True, state_spread=1.0, channel_spread=1.0,
+                                              x_clusters=4)
+    _check(inp, "x per channel + B, C per state + correction", y_corr=oracle.mean_correction(cal))
 
 
 def test_final_state_in_place():
