@@ -340,3 +340,12 @@ def test_scaled_calls_validate_on_the_host(lib):
     no_scale[1] = None                                   # state_scale, needed by the 8-bit format only
     assert lib.ssdq_state_update_scaled(2, *no_scale, 2, 4, 64, 128, 2, 3, None) == INVALID
     assert lib.ssdq_state_update_scaled(0, *no_scale, 2, 4, 64, 96, 2, 2, None) == UNSUPPORTED
+
+
+def test_plan_query_on_the_host(lib):
+    lib.ssdq_chunk_scan_plan.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32]
+    lib.ssdq_chunk_scan_plan.restype = ctypes.c_int32
+    assert lib.ssdq_chunk_scan_plan(0, 4, 0) == -1
+    assert lib.ssdq_chunk_scan_plan(1, -4, 0) == -1
+    assert lib.ssdq_chunk_scan_plan(1, 4, 4) == -1                 # unknown layout bit
+    assert lib.ssdq_chunk_scan_plan(8, 128, 3) in (0, 4, 8)        # 0 where no device is visible
