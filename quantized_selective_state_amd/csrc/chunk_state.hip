@@ -643,13 +643,20 @@ __global__ void __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(
 // Four-wave form of the folded state kernel, for shapes with many (batch, head) sequences per
 // CU: one block of four waves per sequence, wave w owning channel tile w over all of a chunk's
 // tokens and all states.  A chunk's products then need no partial exchange between waves (the
-// three limbs of all four K steps accumulate in one wave's int32 registers), a state row's
-// maximum is a reduction inside the wave, and the carried-state encoding covers a whole row per
-// lane group.  The chunk tiles are single-buffered (~53 KB of LDS at chunk 256), so two blocks
-// share a CU: one block's barriers and tile loads are covered by the other's work.  Per chunk:
-// row maxima (registers), wait for the tiles, barrier, products, barrier (the tiles and this
-// group's weights are free again), the next chunk's tile loads, the carried-state encoding and
-// stores, the update of H.
+// three limbs of all K steps accumulate in one wave's int32 registers), a state row's maximum
+// is a reduction inside the wave, and the carried-state encoding covers a whole row per lane
+// group.
+//
+// The chunk is staged in units of up to 128 tokens through two LDS buffers (~57 KB in all at
+// chunk 256 with the weights' two slots, so two blocks share a CU), one barrier per unit, and
+// the loads of unit u + 1 are issued right after unit u's barrier.  The products of a chunk do
+// not depend on the running state, so they are software-pipelined against it: the first unit of
+// chunk c folds chunk c - 1's products into H tile by tile (H_c = exp(Acs_last) H_{c-1} +
+// S_{c-1}) and, as each tile's accumulators are consumed, issues chunk c's first MFMAs into
+// them; the last unit of chunk c issues its MFMAs and then encodes H_c (the state entering the
+// chunk) while they complete.  The matrix cores thus work under the VALU's update and encoding
+// instead of after them.  The chunk weights are
+// prepared one group of four chunks ahead (one chunk per wave) into a second LDS slot.
 constexpr int kS4Threads = 256;
 constexpr int kS4Waves = kS4Threads / kWave;
 constexpr int kGroup4 = kS4Waves;   // chunks whose weights one prologue prepares (one per wave)
@@ -662,11 +669,14 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
     const float* h0, float* h_final, float* __restrict__ acs, float* __restrict__ dtc, int8_t* __restrict__ hprev,
     float* __restrict__ hscale, int64_t seqlen, int32_t nheads, int32_t headdim, int32_t dstate,
     int32_t ngroups, int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) uint8_t xs[Q * kMaxP];
-  __shared__ __attribute__((aligned(16))) uint8_t bs[Q * kMaxN];
-  __shared__ __attribute__((aligned(16))) uint32_t om[kGroup4][Q];
-  __shared__ float gdec[kGroup4];
-  __shared__ int gexp[kGroup4];
+  constexpr int kU = Q > 128 ? 128 : Q;   // tokens per staged unit
+  constexpr int kUnits = Q / kU;          // units per chunk
+  constexpr int kKs = kU / 64;            // K steps per unit
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2][kU * kMaxP];
+  __shared__ __attribute__((aligned(16))) uint8_t bs[2][kU * kMaxN];
+  __shared__ __attribute__((aligned(16))) uint32_t om[2][kGroup4][Q];
+  __shared__ float gdec[2][kGroup4];
+  __shared__ int gexp[2][kGroup4];
   __shared__ __attribute__((aligned(16))) float sig_s[kPS ? kMaxN : 4];   // kPS: B_scale C_scale per state
 
   const int tid = threadIdx.x;
@@ -705,15 +715,14 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
         H[t] = H[t] * __builtin_bit_cast(v4f, buf_load16(rsc, o));
       }
       if (tid < kMaxN) sig_s[tid] = tid < N ? B_scale[g * N + tid] * C_scale[g * N + tid] : 0.f;
-      // (made visible by the first chunk's barrier)
+      // (made visible by the first unit's barrier)
     }
   }
 
-  // chunk tiles by buffer loads straight into LDS (16 bytes per lane, swizzled slots)
-  constexpr int kXd = Q * (kMaxP / 16) / kS4Threads;   // Q / 64
-  constexpr int kBd = Q * (kMaxN / 16) / kS4Threads;   // Q / 32
-  // slot k * 256 + tid of a tile: row j, 16-byte chunk pc in LDS, global chunk cc (offsets are
-  // formed at each use: fewer long-lived registers)
+  // unit tiles by buffer loads straight into LDS (16 bytes per lane, swizzled slots)
+  constexpr int kXd = kU * (kMaxP / 16) / kS4Threads;   // kU / 64
+  constexpr int kBd = kU * (kMaxN / 16) / kS4Threads;   // kU / 32
+  // slot k * 256 + tid of a unit tile: row j, 16-byte chunk pc in LDS, global chunk cc
   auto xoff = [&](int k) {
     const int slot = k * kS4Threads + tid, j = slot >> 2, pc = slot & 3, cc = pc ^ ((j >> 2) & 3);
     return 16 * cc < P ? uint32_t(j) * xrow + 16 * cc : kOutOfRange;
@@ -722,16 +731,21 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
     const int slot = k * kS4Threads + tid, j = slot >> 3, pc = slot & 7, cc = pc ^ ((j >> 1) & 7);
     return 16 * cc < N ? uint32_t(j) * brow + 16 * cc : kOutOfRange;
   };
-  auto dma_chunk = [&](int c) {
-    const bool ok = c < nchunks;
-    const int64_t t0 = ok ? int64_t(c) * Q : 0;
-    const int len = ok ? int(seqlen - t0 < Q ? seqlen - t0 : Q) : 1;
-    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + t0) * nheads + h) * P, ok ? uint32_t(len - 1) * xrow + P : 0u);
-    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + t0) * ngroups + g) * N, ok ? uint32_t(len - 1) * brow + N : 0u);
+  // unit u: tokens [c Q + (u % kUnits) kU, + kU) of chunk c = u / kUnits; rows past the sequence
+  // end (a whole unit, in a short last chunk) read as zeros
+  auto dma_unit = [&](int u) {
+    const int64_t t0 = int64_t(u / kUnits) * Q + (u % kUnits) * kU;
+    const bool ok = t0 < seqlen;
+    const int len = ok ? int(seqlen - t0 < kU ? seqlen - t0 : kU) : 1;
+    const int64_t tb = ok ? t0 : 0;
+    const Rsrc rx = make_rsrc(x + ((int64_t(b) * seqlen + tb) * nheads + h) * P, ok ? uint32_t(len - 1) * xrow + P : 0u);
+    const Rsrc rb = make_rsrc(Bm + ((int64_t(b) * seqlen + tb) * ngroups + g) * N, ok ? uint32_t(len - 1) * brow + N : 0u);
+    uint8_t* xd = xs[u & 1];
+    uint8_t* bd = bs[u & 1];
 #pragma unroll
-    for (int k = 0; k < kXd; ++k) buf_load16_lds(rx, xs + 16 * (k * kS4Threads + kWave * wave), xoff(k));
+    for (int k = 0; k < kXd; ++k) buf_load16_lds(rx, xd + 16 * (k * kS4Threads + kWave * wave), xoff(k));
 #pragma unroll
-    for (int k = 0; k < kBd; ++k) buf_load16_lds(rb, bs + 16 * (k * kS4Threads + kWave * wave), boff(k));
+    for (int k = 0; k < kBd; ++k) buf_load16_lds(rb, bd + 16 * (k * kS4Threads + kWave * wave), boff(k));
   };
   float dtg[kTok];
   auto load_dt_group = [&](int g0) {
@@ -743,7 +757,9 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int u = 0; u < kTok; ++u) dtg[u] = buf_loadf(rdt, uint32_t(lane * kTok + u) * uint32_t(nheads) * 4u);
   };
-  auto group_prologue = [&](int g0) {
+  // chunk g0 + wave's cumsum (to the workspace, with dt in chunk order) and its weights as
+  // 23-bit integers under a power-of-two exponent, into LDS slot s
+  auto group_prologue = [&](int g0, int s) {
     const int c = g0 + wave;
     if (c >= nchunks) return;
     const int64_t t0 = int64_t(c) * Q;
@@ -778,14 +794,12 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
     }
     const int e = min(max(ceil_log2_pos(wave_max(wm)), -100), 100);
 #pragma unroll
-    for (int u = 0; u < kTok; ++u) om[wave][lane * kTok + u] = uint32_t(fminf(w[u] * exp2i(23 - e), 8388607.f) + 0.5f);
+    for (int u = 0; u < kTok; ++u) om[s][wave][lane * kTok + u] = uint32_t(fminf(w[u] * exp2i(23 - e), 8388607.f) + 0.5f);
     if (lane == 0) {
-      gdec[wave] = __builtin_amdgcn_exp2f(a_last * kLog2e);
-      gexp[wave] = e;
+      gdec[s][wave] = __builtin_amdgcn_exp2f(a_last * kLog2e);
+      gexp[s][wave] = e;
     }
   };
-  load_dt_group(0);
-  dma_chunk(0);
 
   const int rowb = 16 * kg + (lcol >> 1), half8 = 8 * (lcol & 1);
   const int xa0 = xpos(rowb, 16 * pt + half8), xa1 = xpos(rowb + 8, 16 * pt + half8);
@@ -793,121 +807,155 @@ __global__ void __launch_bounds__(kS4Threads) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int t = 0; t < kNt; ++t) ba[t] = bpos(rowb, 16 * t + half8);
 
-  auto kstep = [&](v4i (&acc)[kNt][3], int cl, int kb, bool first) {
+  // the three limbs of X_scaled for the K step at unit row kb (weights omu: the unit's first token)
+  auto limbs = [&](v4i (&l)[3], const uint8_t* xb, const uint32_t* omu, int kb) {
     const int j0 = kb + 16 * kg;
-    const v2u xlo = tr8(xs + xa0 + kb * kMaxP), xhi = tr8(xs + xa1 + kb * kMaxP);
+    const v2u xlo = tr8(xb + xa0 + kb * kMaxP), xhi = tr8(xb + xa1 + kb * kMaxP);
     const uint32_t xw[4] = {xlo[0], xlo[1], xhi[0], xhi[1]};
-    v4i l1, l2, l3;
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
-      const v4u o4 = *reinterpret_cast<const v4u*>(&om[cl][j0 + 4 * dw]);
+      const v4u o4 = *reinterpret_cast<const v4u*>(&omu[j0 + 4 * dw]);
       uint32_t W[4], pl[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) W[k] = uint32_t(mad24s(sbyte(xw[dw], k), int32_t(o4[k]), 8421376));
       transpose4x4(W, pl);
-      l1[dw] = int(pl[3]);
-      l2[dw] = int(pl[2] ^ 0x80808080u);
-      l3[dw] = int(pl[1] ^ 0x80808080u);
-    }
-#pragma unroll
-    for (int t = 0; t < kNt; ++t) {
-      const v2u blo = tr8(bs + ba[t] + kb * kMaxN), bhi = tr8(bs + ba[t ^ 4] + (kb + 8) * kMaxN);
-      const v4i bop = {int(blo[0]), int(blo[1]), int(bhi[0]), int(bhi[1])};
-      const v4i z = {0, 0, 0, 0};
-      acc[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l1, first ? z : acc[t][0], 0, 0, 0);
-      acc[t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l2, first ? z : acc[t][1], 0, 0, 0);
-      acc[t][2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l3, first ? z : acc[t][2], 0, 0, 0);
+      l[0][dw] = int(pl[3]);
+      l[1][dw] = int(pl[2] ^ 0x80808080u);
+      l[2][dw] = int(pl[1] ^ 0x80808080u);
     }
   };
-
-  for (int g0 = 0; g0 < nchunks; g0 += kGroup4) {
-    group_prologue(g0);
-    load_dt_group(g0 + kGroup4);
-    const int gend = min(g0 + kGroup4, nchunks);
-    for (int c = g0; c < gend; ++c) {
-      const int cl = c - g0;
-      // the row maximum of the state entering the chunk: this lane's 32 states, then the row's
-      // four lanes (kg = 0..3) by half-wave swaps
-      float m = 0.f;
+  // state tile t's three products for the K step at unit row kb
+  auto mfma_tile = [&](v4i (&a)[3], const v4i (&l)[3], const uint8_t* bb, int t, int kb, bool first) {
+    const v2u blo = tr8(bb + ba[t] + kb * kMaxN), bhi = tr8(bb + ba[t ^ 4] + (kb + 8) * kMaxN);
+    const v4i bop = {int(blo[0]), int(blo[1]), int(bhi[0]), int(bhi[1])};
+    const v4i z = {0, 0, 0, 0};
+    a[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l[0], first ? z : a[0], 0, 0, 0);
+    a[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l[1], first ? z : a[1], 0, 0, 0);
+    a[2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop, l[2], first ? z : a[2], 0, 0, 0);
+  };
+  // H[t] <- decay H[t] + S[t], S recombined from its three limbs' sums
+  auto update_tile = [&](const v4i (&a)[3], int t, float decay, float post) {
+    v4f sg = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (kPS) sg = *reinterpret_cast<const v4f*>(&sig_s[16 * t + 4 * kg]);
 #pragma unroll
-      for (int t = 0; t < kNt; ++t)
+    for (int i = 0; i < 4; ++i) {
+      const int32_t lo = (a[1][i] << 8) + a[2][i];
+      const float sv = fmaf(float(lo), 1.f / 65536.f, float(a[0][i]));
+      if constexpr (kPS)
+        H[t][i] = fmaf(decay, H[t][i], sv * (post * sg[i]));
+      else
+        H[t][i] = fmaf(decay, H[t][i], sv * post);
+    }
+  };
+  // the state entering chunk c as two INT8 limbs + a power-of-two row scale
+  auto encode = [&](int c) {
+    float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
-      {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    for (int t = 0; t < kNt; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(H[t][i]));
+    {   // the row's four lanes (kg = 0..3) by half-wave swaps
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if (!prow) return;
+    const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
+    const float inv = exp2i(8 - ex);
+    const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
+    const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
+    const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {   // 64-state blocks
+      if (64 * hb >= N) break;
+      v4u Q1, Q2;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = 4 * hb + tt;
+        uint32_t V[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) V[i] = uint32_t(int32_t(fmaf(H[t][i], inv, 128.f)));
+        const uint32_t b1lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0501u), b1hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0501u);
+        const uint32_t b0lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0400u), b0hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0400u);
+        Q1[tt] = __builtin_amdgcn_perm(b1hi, b1lo, 0x05040100u);
+        Q2[tt] = __builtin_amdgcn_perm(b0hi, b0lo, 0x05040100u) ^ 0x80808080u;
       }
-      {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-      }
-      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this chunk's tiles have landed
-      __syncthreads();                      // tiles (and, at a group start, the weights) visible
-
-      v4i acc[kNt][3];
-      kstep(acc, cl, 0, true);
-#pragma unroll 1
-      for (int kb = 64; kb < Q; kb += 64) kstep(acc, cl, kb, false);
-      __builtin_amdgcn_iglp_opt(0);
-      const float decay = gdec[cl];
-      const float post = sxB * exp2i(gexp[cl] + 1);
-      __syncthreads();                      // every wave is done with the tiles and this group's weights
-      dma_chunk(c + 1);                     // the next chunk's tiles, into the same buffers
-
-      // the state entering the chunk as two INT8 limbs + a power-of-two row scale
-      if (prow) {
-        const int ex = min(max(ceil_log2_pos(m * (1.f / 127.f)), -120), 120);
-        const float inv = exp2i(8 - ex);
-        const int64_t blk = (int64_t(b) * nchunks + c) * nheads + h;
-        const Rsrc rh = make_rsrc(hprev + blk * 2 * pn, uint32_t(2 * pn));
-        const uint32_t row = uint32_t(16 * pt + lcol) * uint32_t(N);
+      if (64 * hb + 64 <= N) {
+        __builtin_amdgcn_raw_buffer_store_b128(Q1, rh, row + 64 * hb + 16 * kg, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(Q2, rh, row + 64 * hb + 16 * kg, int(pn), 0);
+      } else {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {   // 64-state blocks
-          if (64 * hb >= N) break;
-          v4u Q1, Q2;
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            const int t = 4 * hb + tt;
-            uint32_t V[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) V[i] = uint32_t(int32_t(fmaf(H[t][i], inv, 128.f)));
-            const uint32_t b1lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0501u), b1hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0501u);
-            const uint32_t b0lo = __builtin_amdgcn_perm(V[1], V[0], 0x0c0c0400u), b0hi = __builtin_amdgcn_perm(V[3], V[2], 0x0c0c0400u);
-            Q1[tt] = __builtin_amdgcn_perm(b1hi, b1lo, 0x05040100u);
-            Q2[tt] = __builtin_amdgcn_perm(b0hi, b0lo, 0x05040100u) ^ 0x80808080u;
-          }
-          if (64 * hb + 64 <= N) {
-            __builtin_amdgcn_raw_buffer_store_b128(Q1, rh, row + 64 * hb + 16 * kg, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(Q2, rh, row + 64 * hb + 16 * kg, int(pn), 0);
-          } else {
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-              if (64 * hb + 16 * tt >= N) break;
-              __builtin_amdgcn_raw_buffer_store_b32(Q1[tt], rh, row + 64 * hb + 16 * tt + 4 * kg, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b32(Q2[tt], rh, row + 64 * hb + 16 * tt + 4 * kg, int(pn), 0);
-            }
-          }
-        }
-        if (kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
-      }
-
-      // H <- exp(Acs_last) H + S_c (the chunk's products recombined from their three limbs)
-#pragma unroll
-      for (int t = 0; t < kNt; ++t) {
-        v4f sg = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (kPS) sg = *reinterpret_cast<const v4f*>(&sig_s[16 * t + 4 * kg]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int32_t lo = (acc[t][1][i] << 8) + acc[t][2][i];
-          const float sv = fmaf(float(lo), 1.f / 65536.f, float(acc[t][0][i]));
-          if constexpr (kPS)
-            H[t][i] = fmaf(decay, H[t][i], sv * (post * sg[i]));
-          else
-            H[t][i] = fmaf(decay, H[t][i], sv * post);
+        for (int tt = 0; tt < 4; ++tt) {
+          if (64 * hb + 16 * tt >= N) break;
+          __builtin_amdgcn_raw_buffer_store_b32(Q1[tt], rh, row + 64 * hb + 16 * tt + 4 * kg, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(Q2[tt], rh, row + 64 * hb + 16 * tt + 4 * kg, int(pn), 0);
         }
       }
     }
+    if (kg == 0) hscale[blk * P + 16 * pt + lcol] = exp2i(ex);
+  };
+
+  load_dt_group(0);
+  dma_unit(0);
+  group_prologue(0, 0);
+  load_dt_group(kGroup4);
+
+  v4i acc[kNt][3];
+  float dec_prev = 1.f, post_prev = 0.f;   // chunk c - 1's decay and products' scale
+  for (int c = 0; c < nchunks; ++c) {
+    const int s = (c / kGroup4) & 1, cl = c % kGroup4;
+#pragma unroll
+    for (int hu = 0; hu < kUnits; ++hu) {
+      const int u = c * kUnits + hu;
+      const int ub = kUnits == 2 ? hu : (c & 1);   // u & 1
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this unit's tiles have landed
+      __syncthreads();                      // tiles visible; every wave is done with unit u - 1
+      float dec_c = 0.f, post_c = 0.f;
+      if (hu == 0) {
+        dec_c = gdec[s][cl];
+        post_c = sxB * exp2i(gexp[s][cl] + 1);
+      }
+      if (hu + 1 < kUnits || c + 1 < nchunks) dma_unit(u + 1);   // into the buffer unit u - 1 used
+      if (hu == 0 && cl == 0) {             // a group start: the next group's weights, other slot
+        group_prologue(c + kGroup4, s ^ 1);
+        load_dt_group(c + 2 * kGroup4);
+      }
+      const uint8_t* xb = xs[ub];
+      const uint8_t* bb = bs[ub];
+      const uint32_t* omu = &om[s][cl][hu * kU];
+      v4i l[kKs][3];
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) limbs(l[ks], xb, omu, 64 * ks);
+      if (hu == 0) {
+        if (c > 0) {
+#pragma unroll
+          for (int t = 0; t < kNt; ++t) {
+            update_tile(acc[t], t, dec_prev, post_prev);
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) mfma_tile(acc[t], l[ks], bb, t, 64 * ks, ks == 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < kNt; ++t)
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) mfma_tile(acc[t], l[ks], bb, t, 64 * ks, ks == 0);
+        }
+        dec_prev = dec_c;
+        post_prev = post_c;
+      } else {
+#pragma unroll
+        for (int t = 0; t < kNt; ++t)
+#pragma unroll
+          for (int ks = 0; ks < kKs; ++ks) mfma_tile(acc[t], l[ks], bb, t, 64 * ks, false);
+      }
+      if (hu == kUnits - 1) encode(c);
+    }
   }
+#pragma unroll
+  for (int t = 0; t < kNt; ++t) update_tile(acc[t], t, dec_prev, post_prev);   // the last chunk's S
 
   if (h_final && prow) {
     const Rsrc rf = make_rsrc(h_final + int64_t(bh) * pn, uint32_t(pn) * 4u);
