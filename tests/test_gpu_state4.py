@@ -61,6 +61,14 @@ def test_chunk_sizes_and_ragged_lengths(chunk, seqlen):
     _check(_make(110 + chunk, chunk=chunk, seqlen=seqlen), f"Q={chunk} L={seqlen}")
 
 
+@pytest.mark.parametrize("chunk,seqlen", [(64, 700), (128, 1100), (256, 1300)])
+def test_many_chunks(chunk, seqlen):
+    # 11, 9 and 6 chunks: the chunk weights go through both LDS slots (prepared one group of four
+    # chunks ahead) and the staged units through both tile buffers more than once; at chunk 256
+    # the last chunk's second 128-token unit lies wholly past the sequence end
+    _check(_make(140 + chunk, chunk=chunk, seqlen=seqlen, h0_std=0.1), f"Q={chunk} L={seqlen}")
+
+
 @pytest.mark.parametrize("P,N,G", [(16, 16, 1), (32, 80, 4), (48, 64, 8)])
 def test_head_and_state_widths(P, N, G):
     _check(_make(120 + P + N, headdim=P, dstate=N, ngroups=G, seqlen=200), f"P={P} N={N} G={G}")
