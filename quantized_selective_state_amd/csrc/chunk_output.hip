@@ -66,17 +66,6 @@ __device__ __forceinline__ int bpos(int j, int byte) {
 constexpr int kHPlane = kMaxP * kMaxN;
 __device__ __forceinline__ int hpos(int p, int byte) { return bpos(p, byte); }
 
-__device__ __forceinline__ void transpose4x4(const uint32_t in[4], uint32_t out[4]) {
-  const uint32_t t01lo = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
-  const uint32_t t01hi = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
-  const uint32_t t23lo = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
-  const uint32_t t23hi = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
-  out[0] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);
-  out[1] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-  out[2] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);
-}
-
 // Four int8 codes (biased by 128, i.e. XORed with 0x80 per byte) -> four exact fp16 values:
 // the fp16 with bits 0x64XX is 1024 + XX, so subtracting 1152 leaves the signed code.
 __device__ __forceinline__ v4h codes_to_f16(uint32_t biased) {
