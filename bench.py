@@ -190,7 +190,7 @@ def kernel_bytes(b, L, H, P, N, G, Q):
     }
 
 
-def survey_bytes_per_token(H, P, N, G, Q):
+def specified_bytes_per_token(H, P, N, G, Q):
     """Per-token compulsory traffic of the four steps of the chunked scan as the scan is specified
     (int8 x, B, C in; fp32 dt, Acs and chunk states; fp16 y out): the unit figures the roofline
     of each step is quoted against.  chunk_scan (the output step) reads x, B, C, dt, Acs and the
@@ -298,7 +298,7 @@ def bench_prefill(name, steps, warmup, torch, ssdq, workloads, dev, keep_inputs=
     scan_ms = sum(per_kernel_ms[n] for n in scan_names)
 
     kb = kernel_bytes(b, L, H, P, N, G, Q)
-    unit = survey_bytes_per_token(H, P, N, G, Q)
+    unit = specified_bytes_per_token(H, P, N, G, Q)
     # the roofline of the dominant kernel, priced by the specified per-token traffic of its step
     # (the output kernel is the chunk_scan step; the others are priced by their own bytes)
     spec_name = {"chunk_output": "chunk_scan", "quantize": "quantize", "chunk_state": "chunk_state"}.get(dominant)
@@ -341,7 +341,7 @@ def bench_prefill(name, steps, warmup, torch, ssdq, workloads, dev, keep_inputs=
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         return 2
 

@@ -67,7 +67,7 @@ def test_traffic_is_reported_only_for_the_current_source(tmp_path, monkeypatch):
 def test_specified_bytes_per_token(shape, quant, scan):
     """The per-token traffic the roofline is priced by, for the three prefill shapes (H, P, N,
     G, Q): x, B, C int8 in, dt and Acs fp32, the fp32 state entering each chunk, y fp16 out."""
-    u = bench.survey_bytes_per_token(*shape)
+    u = bench.specified_bytes_per_token(*shape)
     assert u["quantize"] == quant and u["chunk_scan"] == scan
 
 
