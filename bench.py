@@ -265,10 +265,11 @@ def bench_prefill(name, steps, warmup, torch, ssdq, workloads, dev, keep_inputs=
         step()
     torch.cuda.synchronize()
 
-    # per-kernel breakdown: up to 200 steps with events around every kernel (an event between
-    # two kernels can delay the second, so these steps are not the ones whose wall time gives
-    # the throughput)
-    nprof = max(1, min(steps, 200))
+    # per-kernel breakdown: 200 steps with events around every kernel, whatever the timed step
+    # count, so that the per-kernel figures average the same number of steps in a short run as
+    # in a long one (an event between two kernels can delay the second, so these steps are not
+    # the ones whose wall time gives the throughput)
+    nprof = 200
     prof = [{i: (ev(), ev()) for i in range(len(fns))} for _ in range(nprof)]
     for k in range(nprof):
         step(prof[k])
